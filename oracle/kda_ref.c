@@ -1,0 +1,149 @@
+/*
+ * Plain fp64 CPU oracle for Kimi Delta Attention (KDA): the gated delta rule
+ * with a per-channel diagonal decay, run one token at a time.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or
+ * load this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it. It shares no code with the HIP kernels.
+ *
+ * What it computes (per sequence n and head h, for t in order):
+ *   S <- Diag(exp g_t) S                       decay first, one factor per key channel
+ *   S <- S + beta_t k_t (v_t - S^T k_t)^T      = (I - beta_t k_t k_t^T) S + beta_t k_t v_t^T
+ *   o_t = scale * S^T q_t                       read from the post-update state
+ * This is the gated delta rule of Kimi Delta Attention as the Kimi K3 pages
+ * name it (ISEEKYAN/k3 README, KDA compute path; hysenlabs "kimi-k3-mlx",
+ * section "The A_log shape mismatch ...": the log-decay g has shape
+ * (B,T,96,128), i.e. one value per token, head and key channel).
+ *
+ * Layouts (row-major, the same as the library's):
+ *   q,k,g [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H]; o [B,T,H,Dv]
+ *   states [N,H,Dk,Dv] (Dv contiguous); cu_seqlens [N+1] (B must be 1)
+ * Inputs are float: bf16 and fp32 values are both held exactly in float and
+ * every operation below is carried out in double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One token of the recurrence on one (sequence, head) state S [Dk][Dv]. */
+static void kda_ref_token(double* S, double* x, const float* qt, const float* kt,
+                          const float* vt, const float* gt, double bt,
+                          int64_t Dk, int64_t Dv, double scale, double* ot)
+{
+    for (int64_t i = 0; i < Dk; ++i) {
+        const double a = exp((double)gt[i]);
+        double* row = S + i * Dv;
+        for (int64_t j = 0; j < Dv; ++j) row[j] *= a;
+    }
+    for (int64_t j = 0; j < Dv; ++j) x[j] = 0.0;
+    for (int64_t i = 0; i < Dk; ++i) {
+        const double ki = (double)kt[i];
+        const double* row = S + i * Dv;
+        for (int64_t j = 0; j < Dv; ++j) x[j] += ki * row[j];
+    }
+    for (int64_t j = 0; j < Dv; ++j) x[j] = bt * ((double)vt[j] - x[j]);
+    for (int64_t i = 0; i < Dk; ++i) {
+        const double ki = (double)kt[i];
+        double* row = S + i * Dv;
+        for (int64_t j = 0; j < Dv; ++j) row[j] += ki * x[j];
+    }
+    if (ot) {
+        for (int64_t j = 0; j < Dv; ++j) x[j] = 0.0;
+        for (int64_t i = 0; i < Dk; ++i) {
+            const double qi = (double)qt[i];
+            const double* row = S + i * Dv;
+            for (int64_t j = 0; j < Dv; ++j) x[j] += qi * row[j];
+        }
+        for (int64_t j = 0; j < Dv; ++j) ot[j] = scale * x[j];
+    }
+}
+
+/*
+ * Forward over whole sequences. Returns 0, or -1 on bad arguments / no memory.
+ * o [B,T,H,Dv] (rows outside every sequence are left untouched);
+ * final_state [N,H,Dk,Dv] may be NULL. nthreads <= 0 means the OpenMP default.
+ */
+int kda_ref_forward(const float* q, const float* k, const float* v, const float* g,
+                    const float* beta, const float* initial_state,
+                    const int64_t* cu_seqlens, int64_t N,
+                    int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                    double scale, double* o, double* final_state, int nthreads)
+{
+    if (!q || !k || !v || !g || !beta || !o || B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1)
+        return -1;
+    if (cu_seqlens) {
+        if (B != 1 || N < 1 || cu_seqlens[0] != 0 || cu_seqlens[N] != T) return -1;
+        for (int64_t n = 0; n < N; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+    } else {
+        N = B;
+    }
+    int failed = 0;
+    const int64_t units = N * H;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+#endif
+    for (int64_t u = 0; u < units; ++u) {
+        const int64_t n = u / H, h = u % H;
+        const int64_t b = cu_seqlens ? 0 : n;
+        const int64_t bos = cu_seqlens ? cu_seqlens[n] : 0;
+        const int64_t eos = cu_seqlens ? cu_seqlens[n + 1] : T;
+        double* S = (double*)malloc(sizeof(double) * Dk * Dv);
+        double* x = (double*)malloc(sizeof(double) * Dv);
+        if (!S || !x) { free(S); free(x); failed |= 1; continue; }
+        const int64_t s_off = (n * H + h) * Dk * Dv;
+        for (int64_t e = 0; e < Dk * Dv; ++e)
+            S[e] = initial_state ? (double)initial_state[s_off + e] : 0.0;
+        for (int64_t t = bos; t < eos; ++t) {
+            const int64_t row = (b * T + t) * H + h;
+            kda_ref_token(S, x, q + row * Dk, k + row * Dk, v + row * Dv, g + row * Dk,
+                          (double)beta[row], Dk, Dv, scale, o + row * Dv);
+        }
+        if (final_state) memcpy(final_state + s_off, S, sizeof(double) * Dk * Dv);
+        free(S);
+        free(x);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * One decode step: every row r (one token) updates state_cache[slot(r), h] in
+ * place, where slot(r) = slots ? slots[r] : r. q,k,g [Nb,H,Dk]; v [Nb,H,Dv];
+ * beta [Nb,H]; state_cache [n_slots,H,Dk,Dv] (double, updated); o [Nb,H,Dv].
+ */
+int kda_ref_decode_step(const float* q, const float* k, const float* v, const float* g,
+                        const float* beta, double* state_cache, const int64_t* slots,
+                        int64_t n_slots, int64_t Nb, int64_t H, int64_t Dk, int64_t Dv,
+                        double scale, double* o, int nthreads)
+{
+    if (!q || !k || !v || !g || !beta || !state_cache || !o || Nb < 0 || H < 1 || Dk < 1 || Dv < 1)
+        return -1;
+    for (int64_t r = 0; r < Nb; ++r) {
+        const int64_t s = slots ? slots[r] : r;
+        if (s < 0 || s >= n_slots) return -1;
+        for (int64_t r2 = 0; r2 < r; ++r2)   /* two rows may not share a slot */
+            if ((slots ? slots[r2] : r2) == s) return -1;
+    }
+    int failed = 0;
+    const int64_t units = Nb * H;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads) reduction(| : failed)
+#endif
+    for (int64_t u = 0; u < units; ++u) {
+        const int64_t r = u / H, h = u % H;
+        const int64_t s = slots ? slots[r] : r;
+        double* x = (double*)malloc(sizeof(double) * Dv);
+        if (!x) { failed |= 1; continue; }
+        const int64_t row = r * H + h;
+        kda_ref_token(state_cache + (s * H + h) * Dk * Dv, x, q + row * Dk, k + row * Dk,
+                      v + row * Dv, g + row * Dk, (double)beta[row], Dk, Dv, scale, o + row * Dv);
+        free(x);
+    }
+    return failed ? -1 : 0;
+}

@@ -1,0 +1,190 @@
+"""Plain fp64 CPU oracle for Kimi Delta Attention (KDA).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg of
+the benchmark are the only callers. The product path never imports this module
+and this module imports nothing from the product package.
+
+KDA is the gated delta rule with a per-channel diagonal decay. For one sequence
+and one head, with state S of shape [d_k, d_v], token t does:
+
+    S  <- Diag(exp g_t) S                     (decay, one factor per key channel)
+    S  <- (I - beta_t k_t k_t^T) S + beta_t k_t v_t^T
+    o_t = scale * S^T q_t                      (read after the update)
+
+Sources: the ISEEKYAN/k3 README names KDA as 69 of the 93 K3 layers and its
+"bounded torch recurrence" as the CPU correctness path; the hysenlabs article
+"kimi-k3-mlx: a faithful MLX port ...", section "The A_log shape mismatch is a
+silent-garbage bug the tests assert", fixes the log-decay g as a
+(B,T,96,128) tensor, i.e. per token, head and key channel. The pages print no
+equation; the update above is the gated delta rule in its plainest reading
+(decay, then erase along k_t, then write beta_t k_t v_t^T; the output uses the
+post-update state).
+
+Two implementations, written separately:
+  * ``recurrence`` / ``decode_step`` below: NumPy, vectorised over heads only,
+    one Python-level step per token;
+  * ``c_forward`` / ``c_decode_step``: the plain C loops in kda_ref.c (OpenMP
+    over independent (sequence, head) units), loaded with ctypes.
+Both take inputs as float arrays that hold the GPU's bf16 or fp32 values
+exactly, and compute in float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda_ref.so")
+
+
+# ----------------------------------------------------------------------------
+# NumPy twin
+# ----------------------------------------------------------------------------
+
+def _segments(B, T, cu_seqlens):
+    if cu_seqlens is None:
+        return [(b, 0, T) for b in range(B)]
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    if B != 1 or cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing, end at T, with B == 1")
+    return [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
+
+
+def token_step(S, q_t, k_t, v_t, g_t, beta_t, scale=1.0):
+    """One token for a stack of heads. S [H,Dk,Dv] is updated in place; returns o_t [H,Dv]."""
+    S *= np.exp(g_t)[:, :, None]                               # Diag(exp g_t) S
+    x = np.einsum("hk,hkv->hv", k_t, S)                        # S^T k_t
+    S += (beta_t[:, None, None] * k_t[:, :, None]) * (v_t - x)[:, None, :]
+    return scale * np.einsum("hk,hkv->hv", q_t, S)             # S_t^T q_t
+
+
+def recurrence(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0):
+    """Sequential fp64 forward. Returns (o [B,T,H,Dv], final_state [N,H,Dk,Dv]).
+
+    q,k,g: [B,T,H,Dk]; v: [B,T,H,Dv]; beta: [B,T,H]; initial_state: [N,H,Dk,Dv]
+    or None (zeros); cu_seqlens: [N+1] packed offsets (then B must be 1) or None
+    (then N = B). Rows outside every sequence stay zero in o.
+    """
+    q, k, v, g, beta = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    segs = _segments(B, T, cu_seqlens)
+    o = np.zeros((B, T, H, Dv))
+    final = np.zeros((len(segs), H, Dk, Dv))
+    for n, (b, bos, eos) in enumerate(segs):
+        if initial_state is None:
+            S = np.zeros((H, Dk, Dv))
+        else:
+            S = np.array(initial_state[n], dtype=np.float64)
+        for t in range(bos, eos):
+            o[b, t] = token_step(S, q[b, t], k[b, t], v[b, t], g[b, t], beta[b, t], scale)
+        final[n] = S
+    return o, final
+
+
+def decode_step(q, k, v, g, beta, state_cache, state_slots=None, scale=1.0):
+    """One decode step against a state cache. Returns (o [Nb,H,Dv], new cache copy).
+
+    q,k,g: [Nb,H,Dk]; v: [Nb,H,Dv]; beta: [Nb,H]; state_cache [n_slots,H,Dk,Dv];
+    row r updates slot state_slots[r] (identity when None). Slots must be distinct.
+    """
+    q, k, v, g, beta = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta))
+    cache = np.array(state_cache, dtype=np.float64)
+    Nb = q.shape[0]
+    slots = list(range(Nb)) if state_slots is None else [int(s) for s in np.asarray(state_slots)]
+    if len(set(slots)) != len(slots):
+        raise ValueError("state slots must be distinct")
+    o = np.zeros((Nb,) + v.shape[1:])
+    for r, s in enumerate(slots):
+        S = cache[s]
+        o[r] = token_step(S, q[r], k[r], v[r], g[r], beta[r], scale)
+    return o, cache
+
+
+# ----------------------------------------------------------------------------
+# C implementation (ctypes)
+# ----------------------------------------------------------------------------
+
+_lib = None
+
+
+def load_c():
+    """Load oracle/libkda_ref.so (built by the package build step)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        lib.kda_ref_forward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I,
+                                        ctypes.c_double, P, P, ctypes.c_int]
+        lib.kda_ref_forward.restype = ctypes.c_int
+        lib.kda_ref_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I,
+                                            ctypes.c_double, P, ctypes.c_int]
+        lib.kda_ref_decode_step.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def c_forward(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0,
+              nthreads=0, want_final=True):
+    """The C oracle on float32-held inputs. Same contract as ``recurrence``."""
+    lib = load_c()
+    q, k, v, g, beta = (_f32(a) for a in (q, k, v, g, beta))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    cu = None
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64).reshape(-1))
+        N = cu.size - 1
+    else:
+        N = B
+    s0 = None if initial_state is None else _f32(initial_state)
+    o = np.zeros((B, T, H, Dv))
+    final = np.zeros((N, H, Dk, Dv)) if want_final else None
+    rc = lib.kda_ref_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
+                             _ptr(cu), N, B, T, H, Dk, Dv, float(scale), _ptr(o),
+                             _ptr(final), int(nthreads))
+    if rc != 0:
+        raise ValueError("kda_ref_forward rejected its arguments")
+    return o, final
+
+
+def c_decode_step(q, k, v, g, beta, state_cache, state_slots=None, scale=1.0, nthreads=0):
+    """The C oracle's decode step. ``state_cache`` (float64, C-contiguous) is updated in place."""
+    lib = load_c()
+    if state_cache.dtype != np.float64 or not state_cache.flags["C_CONTIGUOUS"]:
+        raise TypeError("state_cache must be a C-contiguous float64 array")
+    q, k, v, g, beta = (_f32(a) for a in (q, k, v, g, beta))
+    Nb, H, Dk = q.shape
+    Dv = v.shape[-1]
+    slots = None
+    if state_slots is not None:
+        slots = np.ascontiguousarray(np.asarray(state_slots, dtype=np.int64))
+    o = np.zeros((Nb, H, Dv))
+    rc = lib.kda_ref_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(state_cache), _ptr(slots), state_cache.shape[0],
+                                 Nb, H, Dk, Dv, float(scale), _ptr(o), int(nthreads))
+    if rc != 0:
+        raise ValueError("kda_ref_decode_step rejected its arguments")
+    return o
+
+
+def rel_l2(x, ref):
+    """||x - ref||_2 / ||ref||_2 in float64 over whole tensors (absolute L2 when ||ref|| < 1e-30)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = float(np.linalg.norm((x - ref).ravel()))
+    den = float(np.linalg.norm(ref.ravel()))
+    return num if den < 1e-30 else num / den
