@@ -1,0 +1,191 @@
+"""Kimi Delta Attention (KDA) forward on AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libkda.so`` (declared in
+include/kda.h). It only marshals arguments: checks tensor shapes, dtypes,
+devices and contiguity, allocates outputs with torch, and passes raw device
+pointers plus torch's current HIP stream. Every step of the computation runs
+in the library's HIP kernels; there is no fallback path. If the library is
+not built, calls raise ``RuntimeError``.
+
+    o, final_state = chunk_fwd(q, k, v, g, beta, initial_state=None,
+                               cu_seqlens=None, chunk_size=0, scale=1.0,
+                               output_final_state=True)
+    o = recurrent_step(q, k, v, g, beta, state_cache, state_slots=None, scale=1.0)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "kda.h")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
+KDA_F32, KDA_BF16 = 0, 1
+_DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+
+class KDAError(RuntimeError):
+    """A non-OK status returned by libkda.so."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkda.so and declare its entry points (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    P, I32, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F,
+                                  ctypes.c_int, P, P, P]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_recurrent_step.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F,
+                                       ctypes.c_int, P, P]
+    lib.kda_recurrent_step.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error_message.argtypes = []
+    lib.kda_last_error_message.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def declared_symbols(header: str = HEADER_PATH):
+    """Names of the functions include/kda.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def _check(status: int):
+    if status != KDA_OK:
+        lib = load_library()
+        msg = lib.kda_last_error_message().decode()
+        name = lib.kda_status_string(status).decode()
+        raise KDAError(status, f"{name}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk_size=0, scale=1.0,
+              output_final_state=True, out=None, final_state=None):
+    """KDA forward over whole sequences (kda_chunk_fwd).
+
+    q, k, g [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H] (all float32 or all bfloat16,
+    on one GPU); initial_state [N,H,Dk,Dv] float32 or None; cu_seqlens int32
+    [N+1] (B must be 1) or None (N = B). Returns (o [B,T,H,Dv], final_state
+    [N,H,Dk,Dv] float32 or None).
+    """
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,Dk]")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    dt = q.dtype
+    _need(q, "q", (B, T, H, Dk), dt, dev)
+    _need(k, "k", (B, T, H, Dk), dt, dev)
+    _need(g, "g", (B, T, H, Dk), dt, dev)
+    _need(v, "v", (B, T, H, Dv), dt, dev)
+    _need(beta, "beta", (B, T, H), dt, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be 1-D")
+        N = cu_seqlens.numel() - 1
+        _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (N, H, Dk, Dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", (B, T, H, Dv), dt, dev)
+    if output_final_state:
+        if final_state is None:
+            final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+        else:
+            _need(final_state, "final_state", (N, H, Dk, Dv), torch.float32, dev)
+    else:
+        final_state = None
+    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                           _ptr(cu_seqlens), B, T, H, Dk, Dv, N, int(chunk_size), float(scale),
+                           _DTYPES[dt], _ptr(out), _ptr(final_state), _stream(dev))
+    _check(st)
+    return out, final_state
+
+
+def recurrent_step(q, k, v, g, beta, state_cache, state_slots=None, scale=1.0, out=None):
+    """One KDA decode step against ``state_cache`` (updated in place; kda_recurrent_step).
+
+    q, k, g [Nb,H,Dk]; v [Nb,H,Dv]; beta [Nb,H]; state_cache [n_slots,H,Dk,Dv]
+    float32; state_slots int32 [Nb] (distinct) or None (row r -> slot r).
+    Returns o [Nb,H,Dv].
+    """
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError("q must be [Nb,H,Dk]")
+    Nb, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    dt = q.dtype
+    _need(q, "q", (Nb, H, Dk), dt, dev)
+    _need(k, "k", (Nb, H, Dk), dt, dev)
+    _need(g, "g", (Nb, H, Dk), dt, dev)
+    _need(v, "v", (Nb, H, Dv), dt, dev)
+    _need(beta, "beta", (Nb, H), dt, dev)
+    if state_cache.dim() != 4:
+        raise ValueError("state_cache must be [n_slots,H,Dk,Dv]")
+    n_slots = state_cache.shape[0]
+    _need(state_cache, "state_cache", (n_slots, H, Dk, Dv), torch.float32, dev)
+    if state_slots is not None:
+        _need(state_slots, "state_slots", (Nb,), torch.int32, dev)
+    if out is None:
+        out = torch.empty((Nb, H, Dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", (Nb, H, Dv), dt, dev)
+    st = lib.kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_cache),
+                                _ptr(state_slots), n_slots, Nb, H, Dk, Dv, float(scale),
+                                _DTYPES[dt], _ptr(out), _stream(dev))
+    _check(st)
+    return out

@@ -1,0 +1,216 @@
+// Chunkwise KDA forward in float32 on the vector ALUs: the general path for
+// every supported (dtype, Dk, Dv, chunk) combination that the bf16
+// matrix-core kernel does not cover.
+//
+// One workgroup owns one (sequence, head, 16-column slice of d_v) and walks
+// the sequence chunk by chunk, carrying the float32 state slice in LDS.
+// Per chunk of C rows with entry state S (Gamma = in-chunk cumulative
+// log-decay per channel, gamma = exp(Gamma)):
+//   M[r][i] = beta_r * sum_c k_rc k_ic exp(Gamma_rc - Gamma_ic)   (i < r)
+//   P[r][i] =          sum_c q_rc k_ic exp(Gamma_rc - Gamma_ic)   (i <= r)
+//   (I + M) U = Diag(beta) (V - (gamma*K) S)         forward substitution
+//   O = scale * ((gamma*Q) S + P U)
+//   S <- Diag(gamma_C) S + (exp(Gamma_C - Gamma) * K)^T U
+// This is the WY/UT-transform chunk form of the gated delta rule with a
+// per-channel decay; every exponential here is of a non-positive number,
+// so no range precondition on g is needed on this path.
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int kGenThreads = 256;
+constexpr int kGenBV = 16;  // value columns per workgroup
+
+template <int DK, int C, typename Tin>
+__global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a) {
+    constexpr int BV = kGenBV;
+    constexpr int DKP = DK + 1;
+    __shared__ float sK[C][DKP];
+    __shared__ float sQ[C][DKP];
+    __shared__ float sG[C][DKP];
+    __shared__ float sA[C][C + 1];
+    __shared__ float sP[C][C + 1];
+    __shared__ float sV[C][BV];
+    __shared__ float sU[C][BV];
+    __shared__ float sS[DK][BV];
+    __shared__ float sBeta[C];
+    __shared__ float sGn[DK];
+
+    const Tin* q = static_cast<const Tin*>(a.q);
+    const Tin* k = static_cast<const Tin*>(a.k);
+    const Tin* v = static_cast<const Tin*>(a.v);
+    const Tin* g = static_cast<const Tin*>(a.g);
+    const Tin* beta = static_cast<const Tin*>(a.beta);
+    Tin* o = static_cast<Tin*>(a.o);
+
+    const int tid = threadIdx.x;
+    const int nvt = a.Dv / BV;
+    const int unit = blockIdx.x / nvt;
+    const int vt = blockIdx.x % nvt;
+    const int n = unit / a.H;
+    const int h = unit % a.H;
+    const int H = a.H, Dv = a.Dv;
+    int64_t bos, len, b;
+    if (a.cu) {
+        bos = a.cu[n];
+        len = (int64_t)a.cu[n + 1] - bos;
+        b = 0;
+    } else {
+        bos = 0;
+        len = a.T;
+        b = n;
+    }
+    const int c0 = vt * BV;
+    const int64_t state_base = ((int64_t)n * H + h) * DK * (int64_t)Dv;
+
+    for (int idx = tid; idx < DK * BV; idx += kGenThreads) {
+        const int r = idx / BV, c = idx % BV;
+        sS[r][c] = a.s0 ? a.s0[state_base + (int64_t)r * Dv + c0 + c] : 0.f;
+    }
+
+    for (int64_t cs = 0; cs < len; cs += C) {
+        const int rows = (int)((len - cs) < C ? (len - cs) : C);
+        const int64_t tok0 = b * (int64_t)a.T + bos + cs;  // token index of chunk row 0
+        __syncthreads();
+        for (int idx = tid; idx < C * DK; idx += kGenThreads) {
+            const int r = idx / DK, c = idx % DK;
+            float qv = 0.f, kv = 0.f, gv = 0.f;
+            if (r < rows) {
+                const int64_t e = ((tok0 + r) * H + h) * DK + c;
+                qv = load_elem(q, e);
+                kv = load_elem(k, e);
+                gv = load_elem(g, e);
+            }
+            sQ[r][c] = qv;
+            sK[r][c] = kv;
+            sG[r][c] = gv;
+        }
+        for (int idx = tid; idx < C * BV; idx += kGenThreads) {
+            const int r = idx / BV, c = idx % BV;
+            sV[r][c] = r < rows ? load_elem(v, ((tok0 + r) * H + h) * Dv + c0 + c) : 0.f;
+        }
+        for (int r = tid; r < C; r += kGenThreads)
+            sBeta[r] = r < rows ? load_elem(beta, (tok0 + r) * H + h) : 0.f;
+        __syncthreads();
+
+        // in-chunk cumulative log-decay, one channel per thread
+        for (int c = tid; c < DK; c += kGenThreads) {
+            float acc = 0.f;
+            for (int r = 0; r < C; ++r) {
+                acc += sG[r][c];
+                sG[r][c] = acc;
+            }
+            sGn[c] = acc;
+        }
+        __syncthreads();
+
+        // decayed key-key and query-key products
+        for (int idx = tid; idx < C * C; idx += kGenThreads) {
+            const int r = idx / C, i = idx % C;
+            float am = 0.f, pm = 0.f;
+            if (i <= r) {
+                for (int c = 0; c < DK; ++c) {
+                    const float ki = sK[i][c] * expf(sG[r][c] - sG[i][c]);
+                    am += sK[r][c] * ki;
+                    pm += sQ[r][c] * ki;
+                }
+            }
+            sA[r][i] = (i < r) ? sBeta[r] * am : 0.f;
+            sP[r][i] = pm;
+        }
+        __syncthreads();
+
+        // gamma*Q into sQ, gamma*K into sG, exp(Gamma_C - Gamma)*K into sK
+        for (int idx = tid; idx < C * DK; idx += kGenThreads) {
+            const int r = idx / DK, c = idx % DK;
+            const float gv = sG[r][c];
+            const float kv = sK[r][c];
+            const float eg = expf(gv);
+            sQ[r][c] *= eg;
+            sG[r][c] = kv * eg;
+            sK[r][c] = kv * expf(sGn[c] - gv);
+        }
+        __syncthreads();
+
+        // right-hand side Diag(beta)(V - (gamma*K) S)
+        for (int idx = tid; idx < C * BV; idx += kGenThreads) {
+            const int r = idx / BV, j = idx % BV;
+            float y = 0.f;
+            for (int c = 0; c < DK; ++c) y += sG[r][c] * sS[c][j];
+            sU[r][j] = sBeta[r] * (sV[r][j] - y);
+        }
+        __syncthreads();
+
+        // (I + M) U = rhs by forward substitution, one column per thread
+        for (int j = tid; j < BV; j += kGenThreads) {
+            for (int r = 1; r < rows; ++r) {
+                float acc = sU[r][j];
+                for (int i = 0; i < r; ++i) acc -= sA[r][i] * sU[i][j];
+                sU[r][j] = acc;
+            }
+        }
+        __syncthreads();
+
+        for (int idx = tid; idx < C * BV; idx += kGenThreads) {
+            const int r = idx / BV, j = idx % BV;
+            if (r < rows) {
+                float acc = 0.f;
+                for (int c = 0; c < DK; ++c) acc += sQ[r][c] * sS[c][j];
+                for (int i = 0; i <= r; ++i) acc += sP[r][i] * sU[i][j];
+                store_elem(o, ((tok0 + r) * H + h) * Dv + c0 + j, a.scale * acc);
+            }
+        }
+        __syncthreads();
+
+        for (int idx = tid; idx < DK * BV; idx += kGenThreads) {
+            const int c = idx / BV, j = idx % BV;
+            float acc = expf(sGn[c]) * sS[c][j];
+            for (int r = 0; r < rows; ++r) acc += sK[r][c] * sU[r][j];
+            sS[c][j] = acc;
+        }
+    }
+    __syncthreads();
+    if (a.sT) {
+        for (int idx = tid; idx < DK * BV; idx += kGenThreads) {
+            const int r = idx / BV, c = idx % BV;
+            a.sT[state_base + (int64_t)r * Dv + c0 + c] = sS[r][c];
+        }
+    }
+}
+
+template <int DK, int C>
+hipError_t launch_dk_c(const ChunkArgs& a, hipStream_t s) {
+    const int units = a.N * a.H;
+    const dim3 grid((unsigned)(units * (a.Dv / kGenBV)));
+    if (a.bf16)
+        hipLaunchKernelGGL((chunk_generic_kernel<DK, C, __bf16>), grid, dim3(kGenThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((chunk_generic_kernel<DK, C, float>), grid, dim3(kGenThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_dk(const ChunkArgs& a, hipStream_t s) {
+    switch (a.chunk) {
+        case 16: return launch_dk_c<DK, 16>(a, s);
+        case 32: return launch_dk_c<DK, 32>(a, s);
+        case 64: return launch_dk_c<DK, 64>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_generic(const ChunkArgs& a, hipStream_t s) {
+    switch (a.Dk) {
+        case 16: return launch_dk<16>(a, s);
+        case 32: return launch_dk<32>(a, s);
+        case 64: return launch_dk<64>(a, s);
+        case 128: return launch_dk<128>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kda

@@ -1,0 +1,46 @@
+// Internal launch interface between the C ABI (kda_api.hip) and the kernels.
+// Arguments are validated by the caller; these functions only launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const float* s0;          // [N,H,Dk,Dv] or nullptr
+    const int32_t* cu;        // [N+1] or nullptr
+    void* o;
+    float* sT;                // [N,H,Dk,Dv] or nullptr
+    int32_t B, T, H, Dk, Dv, N, chunk;
+    float scale;
+    bool bf16;
+};
+
+struct StepArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    float* cache;
+    const int32_t* slots;
+    void* o;
+    int32_t Nb, H, Dk, Dv;
+    float scale;
+    bool bf16;
+};
+
+// Each returns hipSuccess or the launch error; they never synchronise.
+hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t s);     // bf16, Dk=Dv=128, chunk 64
+hipError_t launch_chunk_generic(const ChunkArgs& a, hipStream_t s);  // any supported dims
+hipError_t launch_recurrent_step(const StepArgs& a, hipStream_t s);
+
+bool chunk_mfma_supported(const ChunkArgs& a);
+
+}  // namespace kda

@@ -1,0 +1,141 @@
+// KDA decode step (one token per row) against a float32 state cache, in place.
+//
+// One workgroup per (row, head) streams that head's d_k x d_v float32 state
+// once from HBM and once back:
+//   S' = Diag(exp g) S;  x = S'^T k;  y = S'^T q;  u = beta (v - x)
+//   o  = scale * (y + (k.q) u)            (= scale * S_new^T q)
+//   S  = S' + k u^T
+// The state is the only large operand (64 KiB per head at d=128), so the
+// kernel is bound by HBM bandwidth: each thread keeps its slice of S' in
+// registers between the two reductions and the write-back, and every state
+// access is a coalesced 16-byte load or store along d_v.
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int kStepThreads = 256;
+
+template <int DK, int DV, typename Tin>
+__global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a) {
+    constexpr int QUADS = DV / 4;                 // float4 columns per row
+    constexpr int RG = kStepThreads / QUADS;      // row groups
+    constexpr int ROWS = (DK + RG - 1) / RG;      // rows per thread
+    __shared__ float sk[DK], sq[DK], seg[DK], sv[DV];
+    __shared__ f32x4 redx[RG][QUADS];
+    __shared__ f32x4 redy[RG][QUADS];
+    __shared__ float skq;
+
+    const Tin* q = static_cast<const Tin*>(a.q);
+    const Tin* k = static_cast<const Tin*>(a.k);
+    const Tin* v = static_cast<const Tin*>(a.v);
+    const Tin* g = static_cast<const Tin*>(a.g);
+    const Tin* beta = static_cast<const Tin*>(a.beta);
+    Tin* o = static_cast<Tin*>(a.o);
+
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x / a.H;
+    const int h = blockIdx.x % a.H;
+    const int slot = a.slots ? a.slots[row] : row;
+    const int64_t tok = (int64_t)row * a.H + h;
+    f32x4* S = reinterpret_cast<f32x4*>(a.cache + ((int64_t)slot * a.H + h) * DK * DV);
+
+    const int quad = tid % QUADS;
+    const int rg = tid / QUADS;
+
+    // issue the state loads first: they are the bulk of the traffic
+    f32x4 s[ROWS];
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int r = rg + RG * i;
+        s[i] = (r < DK) ? S[r * QUADS + quad] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int i = tid; i < DK; i += kStepThreads) {
+        sk[i] = load_elem(k, tok * DK + i);
+        sq[i] = load_elem(q, tok * DK + i);
+        seg[i] = expf(load_elem(g, tok * DK + i));
+    }
+    for (int i = tid; i < DV; i += kStepThreads) sv[i] = load_elem(v, tok * DV + i);
+    if (tid < 64) {
+        float p = 0.f;
+        for (int i = tid; i < DK; i += 64) p += load_elem(k, tok * DK + i) * load_elem(q, tok * DK + i);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+        if (tid == 0) skq = p;
+    }
+    const float bt = load_elem(beta, tok);
+    __syncthreads();
+
+    f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int r = rg + RG * i;
+        if (r < DK) {
+            s[i] *= seg[r];
+            x += sk[r] * s[i];
+            y += sq[r] * s[i];
+        }
+    }
+    redx[rg][quad] = x;
+    redy[rg][quad] = y;
+    __syncthreads();
+    x = redx[0][quad];
+    y = redy[0][quad];
+#pragma unroll
+    for (int j = 1; j < RG; ++j) {
+        x += redx[j][quad];
+        y += redy[j][quad];
+    }
+    f32x4 vv = {sv[4 * quad], sv[4 * quad + 1], sv[4 * quad + 2], sv[4 * quad + 3]};
+    const f32x4 u = bt * (vv - x);
+    if (rg == 0) {
+        const f32x4 ov = a.scale * (y + skq * u);
+        const int64_t ob = tok * DV + 4 * quad;
+        store_elem(o, ob + 0, ov.x);
+        store_elem(o, ob + 1, ov.y);
+        store_elem(o, ob + 2, ov.z);
+        store_elem(o, ob + 3, ov.w);
+    }
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int r = rg + RG * i;
+        if (r < DK) S[r * QUADS + quad] = s[i] + sk[r] * u;
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_dims(const StepArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)(a.Nb * a.H));
+    if (a.bf16)
+        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, __bf16>), grid, dim3(kStepThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, float>), grid, dim3(kStepThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_dk(const StepArgs& a, hipStream_t s) {
+    switch (a.Dv) {
+        case 16: return launch_dims<DK, 16>(a, s);
+        case 32: return launch_dims<DK, 32>(a, s);
+        case 64: return launch_dims<DK, 64>(a, s);
+        case 128: return launch_dims<DK, 128>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_recurrent_step(const StepArgs& a, hipStream_t s) {
+    if (a.Nb == 0) return hipSuccess;
+    switch (a.Dk) {
+        case 16: return launch_dk<16>(a, s);
+        case 32: return launch_dk<32>(a, s);
+        case 64: return launch_dk<64>(a, s);
+        case 128: return launch_dk<128>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kda

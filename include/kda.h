@@ -1,0 +1,113 @@
+/*
+ * kda.h — C ABI of libkda.so: Kimi Delta Attention (KDA) forward on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * KDA is the gated delta rule with a per-channel diagonal decay. For one
+ * sequence and one head, with a state S of d_k x d_v, token t computes
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ * It is 69 of the 93 layers of the Kimi K3 text backbone (ISEEKYAN/k3 README,
+ * package scope; hysenlabs "kimi-k3-mlx", section "Attention is 93 layers
+ * split between KDA and a NoPE gated MLA": 96 heads, head_dim 128). The
+ * log-decay g is per token, head AND key channel, a (B,T,96,128) tensor
+ * (hysenlabs "kimi-k3-mlx", section "The A_log shape mismatch is a
+ * silent-garbage bug the tests assert"), bounded below by gate_lower_bound
+ * = -5.0 (section "Attention is 93 layers ...").
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous, owned
+ *    by the caller. The library never allocates, frees or synchronises; work
+ *    is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *    the call returns before it finishes.
+ *  - Every argument check happens on the host before anything is launched;
+ *    a rejected call touches no memory. Unsupported inputs fail explicitly
+ *    (the K3 README's rule for unsupported inputs); nothing falls back to
+ *    another code path silently.
+ *  - Preconditions that are NOT checked on the device: g in [-5, 0] (the K3
+ *    gate bound; the bf16 chunk kernel relies on it to keep every in-chunk
+ *    exponent below 80), finite inputs, cu_seqlens starting at 0,
+ *    non-decreasing and ending at T, distinct decode state slots in range.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, inconsistent shapes      */
+    KDA_ERR_UNSUPPORTED = 2, /* legal but not built: dims, chunk size, dtype     */
+    KDA_ERR_HIP = 3          /* the HIP runtime reported an error at launch      */
+} kda_status;
+
+typedef enum {
+    KDA_F32 = 0,  /* q,k,v,g,beta and o are float32                             */
+    KDA_BF16 = 1  /* q,k,v,g,beta and o are bfloat16; states are always float32  */
+} kda_dtype;
+
+/*
+ * Chunkwise-parallel KDA forward over whole sequences.
+ *
+ *   q, k, g        [B,T,H,Dk]  dtype; g is the natural-log decay (decay = exp g)
+ *   v              [B,T,H,Dv]  dtype
+ *   beta           [B,T,H]     dtype
+ *   initial_state  [N,H,Dk,Dv] float32 (Dv contiguous), or NULL for zeros
+ *   cu_seqlens     [N+1] int32 offsets of N packed sequences along T (B must be
+ *                  1), or NULL: then N must equal B and row b is sequence b.
+ *                  Zero-length sequences are allowed: their final state equals
+ *                  their initial state. Packed ("THD") batches are how the K3
+ *                  package feeds variable-length sequences (ISEEKYAN/k3 README,
+ *                  packed THD with context parallelism).
+ *   chunk_size     16, 32 or 64; 0 selects 64. It changes only rounding.
+ *   scale          multiplies the output (1.0 reproduces the rule above)
+ *   o              [B,T,H,Dv]  dtype, written for every row of every sequence;
+ *                  must not alias an input. With T = 0, q, k, v, g, beta and
+ *                  o may be NULL (only final states are written).
+ *   final_state    [N,H,Dk,Dv] float32, or NULL (not written); may alias
+ *                  initial_state (each state tile is read before it is written)
+ *
+ * Supported: Dk, Dv in {16, 32, 64, 128}. bf16 with Dk = Dv = 128 and
+ * chunk 64 runs the matrix-core kernel; everything else runs the float32
+ * vector-ALU chunk kernel. Chunks start at each sequence's first token; rows
+ * past a sequence's end inside its last chunk are treated as zero tokens,
+ * which leave the state unchanged.
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* initial_state,
+                         const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H,
+                         int32_t Dk, int32_t Dv, int32_t N, int32_t chunk_size, float scale,
+                         kda_dtype dtype, void* o, float* final_state, void* stream);
+
+/*
+ * One decode step (T = 1 per row) against a state cache, updated in place.
+ *
+ *   q, k, g      [Nb,H,Dk] dtype;  v [Nb,H,Dv] dtype;  beta [Nb,H] dtype
+ *   state_cache  [n_slots,H,Dk,Dv] float32
+ *   state_slots  [Nb] int32 device array: row r reads and writes slot
+ *                state_slots[r]; NULL means slot r. Slots must be distinct
+ *                and < n_slots (not checked on the device).
+ *   o            [Nb,H,Dv] dtype
+ *
+ * Supported: Dk, Dv in {16, 32, 64, 128}. Nb = 0 is a no-op (pointers may
+ * then be NULL).
+ */
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* g,
+                              const void* beta, float* state_cache, const int32_t* state_slots,
+                              int32_t n_slots, int32_t Nb, int32_t H, int32_t Dk, int32_t Dv,
+                              float scale, kda_dtype dtype, void* o, void* stream);
+
+/* Static name of a status code. */
+const char* kda_status_string(kda_status s);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* kda_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,106 @@
+"""Host-only checks of the C ABI: the library loads, exports what include/kda.h
+declares, and rejects bad arguments before touching the GPU (no compute calls)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import gated_delta_rule_chunk_amd as kda
+
+FAKE = ctypes.c_void_p(0x1000)     # never dereferenced: every call below is rejected on the host
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_chunk_amd import _build
+        _build.build()
+    return kda.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = kda.declared_symbols()
+    assert set(names) == {"kda_chunk_fwd", "kda_recurrent_step", "kda_status_string",
+                          "kda_last_error_message"}
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(1) == b"KDA_ERR_INVALID_ARG"
+    assert lib.kda_status_string(2) == b"KDA_ERR_UNSUPPORTED"
+    assert lib.kda_status_string(3) == b"KDA_ERR_HIP"
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, cu=None, B=1, T=64, H=2, Dk=128,
+             Dv=128, N=1, chunk=64, scale=1.0, dtype=kda.KDA_BF16, o=ctypes.c_void_p(0x2000),
+             sT=None, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["B"],
+                             a["T"], a["H"], a["Dk"], a["Dv"], a["N"], a["chunk"], a["scale"],
+                             a["dtype"], a["o"], a["sT"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(T=0, q=None, B=0), kda.KDA_ERR_INVALID_ARG, "B >= 1"),
+    (dict(o=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(B=0), kda.KDA_ERR_INVALID_ARG, "B >= 1"),
+    (dict(T=-1), kda.KDA_ERR_INVALID_ARG, "T >= 0"),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARG, "H >= 1"),
+    (dict(Dk=96), kda.KDA_ERR_UNSUPPORTED, "head dims"),
+    (dict(Dv=256), kda.KDA_ERR_UNSUPPORTED, "head dims"),
+    (dict(chunk=48), kda.KDA_ERR_UNSUPPORTED, "chunk_size"),
+    (dict(dtype=7), kda.KDA_ERR_UNSUPPORTED, "dtype"),
+    (dict(N=2), kda.KDA_ERR_INVALID_ARG, "N must equal B"),
+    (dict(cu=FAKE, B=2, N=2), kda.KDA_ERR_INVALID_ARG, "B == 1"),
+    (dict(cu=FAKE, N=0), kda.KDA_ERR_INVALID_ARG, "N >= 1"),
+    (dict(o=FAKE), kda.KDA_ERR_INVALID_ARG, "alias"),
+])
+def test_chunk_fwd_rejects_before_launch(lib, kw, status, needle):
+    st = _fwd(lib, **kw)
+    assert st == status
+    assert needle in lib.kda_last_error_message().decode()
+
+
+def _step(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cache=FAKE, slots=None, n_slots=4, Nb=4, H=2,
+             Dk=128, Dv=128, scale=1.0, dtype=kda.KDA_BF16, o=ctypes.c_void_p(0x2000), stream=None)
+    a.update(kw)
+    return lib.kda_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cache"], a["slots"],
+                                  a["n_slots"], a["Nb"], a["H"], a["Dk"], a["Dv"], a["scale"],
+                                  a["dtype"], a["o"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(cache=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(Nb=-1), kda.KDA_ERR_INVALID_ARG, "Nb >= 0"),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARG, "H >= 1"),
+    (dict(Dk=8), kda.KDA_ERR_UNSUPPORTED, "head dims"),
+    (dict(dtype=5), kda.KDA_ERR_UNSUPPORTED, "dtype"),
+    (dict(Nb=5), kda.KDA_ERR_INVALID_ARG, "n_slots"),
+    (dict(o=FAKE), kda.KDA_ERR_INVALID_ARG, "alias"),
+])
+def test_recurrent_step_rejects_before_launch(lib, kw, status, needle):
+    st = _step(lib, **kw)
+    assert st == status
+    assert needle in lib.kda_last_error_message().decode()
+
+
+def test_empty_work_is_ok_without_launch(lib):
+    assert _step(lib, Nb=0) == kda.KDA_OK
+    assert lib.kda_last_error_message() == b""
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 4, 2, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        kda.chunk_fwd(x, x, x, x, torch.zeros(1, 4, 2))
