@@ -1,0 +1,235 @@
+"""Benchmark: KDA chunked forward on the K3 layer shape, one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+
+One step = one kda_chunk_fwd call over a K3-shaped batch: B=1, T=4096, H=96,
+d_k=d_v=128, chunk 64, bf16 inputs, zero initial state, output plus final
+state. Inputs are seeded synthetic tensors (synth.WORKLOADS["k3_t4096"]),
+resident in HBM before timing; two input sets alternate so the 256 MB
+Infinity Cache cannot serve a step from the previous one.
+
+Prints one JSON line. ``value`` is tokens/s of the forward (T / seconds per
+step). ``roofline`` is for the chunk kernel: algorithmic HBM bytes per launch
+(q,k,v,g,o at 256 B per token-head each, beta at 2 B, the fp32 final state)
+over its average launch time, measured with HIP events on the launch stream.
+``mfma`` gives the same launches against the bf16 dense matrix-core peak with
+the algorithmic full-tile flop count. ``decode`` times kda_recurrent_step on
+256 rows x 96 heads against an fp32 state cache (HBM-bound). ``cpu_baseline``
+times the fp64 CPU oracle on a bounded sample of the same forward workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gated_delta_rule_chunk_amd as kda  # noqa: E402
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "KDA fwd tokens/s at H=96,d=128 (bf16); MFMA util % and decode HBM GB/s"
+CHUNK_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_chunk_amd", "csrc", "chunk_mfma.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_mfma_k3_t4096_traffic.md")
+
+
+def fwd_bytes(T, H, Dk, Dv, n_states_out, n_states_in=0, elem=2):
+    per_tok_head = elem * (3 * Dk + 2 * Dv) + elem          # q,k,g,v in, o out, beta
+    return T * H * per_tok_head + 4 * Dk * Dv * H * (n_states_out + n_states_in)
+
+
+def fwd_flops(T, H, Dk, Dv, C=64):
+    """Full-tile flop count of the chunk form at chunk C, per launch."""
+    return T * H * (2 * C * (3 * Dk + 2 * Dv) + 6 * Dk * Dv)
+
+
+def kernel_source_hash():
+    return hashlib.sha256(open(CHUNK_KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    text = open(TRAFFIC_SUMMARY).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def time_launches(fn, steps, warmup, stream):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]      # ms
+    return wall, per
+
+
+def bench_forward(steps, warmup):
+    w = synth.WORKLOADS["k3_t4096"]
+    dev = torch.device("cuda:0")
+    sets = []
+    for s in range(2):
+        inp = synth.make_chunk_inputs(w.B, w.T, w.H, w.Dk, w.Dv, seed=w.seed + 1000 * s, dtype=w.dtype)
+        sets.append({k: (None if v is None else v.to(dev)) for k, v in inp.items()})
+    o = torch.empty((w.B, w.T, w.H, w.Dv), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        d = sets[i % 2]
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk_size=w.chunk, out=o,
+                      final_state=fin)
+
+    wall, per = time_launches(step, steps, warmup, stream)
+    if not (torch.isfinite(o.float()).all() and torch.isfinite(fin).all()):
+        raise RuntimeError("non-finite forward output")
+    return w, wall, per
+
+
+def bench_decode(steps, warmup):
+    cfg = synth.DECODE
+    Nb, H, Dk, Dv = cfg["Nb"], cfg["H"], cfg["Dk"], cfg["Dv"]
+    dev = torch.device("cuda:0")
+    cache = synth.make_decode_cache(Nb, H, Dk, Dv, seed=cfg["seed"]).to(dev)
+    ins = [{k: v.to(dev) for k, v in synth.make_decode_step(Nb, H, Dk, Dv, cfg["seed"], s).items()}
+           for s in range(4)]
+    o = torch.empty((Nb, H, Dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        d = ins[i % 4]
+        kda.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], cache, out=o)
+
+    wall, per = time_launches(step, steps, warmup, stream)
+    if not torch.isfinite(cache).all():
+        raise RuntimeError("non-finite decode state")
+    step_bytes = 2 * Nb * H * Dk * Dv * 4 + Nb * H * (2 * (3 * Dk + Dv) + 2 + 2 * Dv)
+    avg_ms = float(np.mean(per))
+    gbs = step_bytes / (avg_ms * 1e-3) / 1e9
+    return {"workload": f"{cfg['name']}: batch {Nb}, H={H}, d_k=d_v={Dk}, bf16 q/k/v/g/beta, fp32 state cache",
+            "ms_per_step": avg_ms, "tokens_per_s": Nb / (avg_ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+            "algorithmic_bytes_per_step": step_bytes}
+
+
+def cpu_baseline(target_core_seconds=20.0):
+    """The fp64 C oracle on a sample of the k3_t4096 workload: the first nh heads, all T tokens."""
+    from oracle import kda_ref
+    w = synth.WORKLOADS["k3_t4096"]
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    inp = synth.make_chunk_inputs(w.B, w.T, w.H, w.Dk, w.Dv, seed=w.seed, dtype=w.dtype)
+    f = {k: inp[k].float().numpy() for k in ("q", "k", "v", "g", "beta")}
+
+    def run(nh, threads):
+        t0 = time.perf_counter()
+        kda_ref.c_forward(f["q"][:, :, :nh], f["k"][:, :, :nh], f["v"][:, :, :nh], f["g"][:, :, :nh],
+                          f["beta"][:, :, :nh], nthreads=threads, want_final=True)
+        return time.perf_counter() - t0
+
+    t1 = run(1, 1)                                   # one head on one core: calibration
+    nh = int(max(1, min(w.H, round(target_core_seconds / max(t1, 1e-3)))))
+    nh = max(min(nh, w.H), min(cores, w.H))
+    used = min(cores, nh)
+    t = run(nh, used)
+    tokens_per_s = w.T * (nh / w.H) / t              # full-layer tokens (all 96 heads) per second
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"k3_t4096 first {nh} of {w.H} heads x T={w.T} tokens, fp64 C oracle "
+                      f"(OpenMP over heads), {t:.2f} s wall; scaled to all {w.H} heads"}
+
+
+def copy_calibration(nbytes=1 << 30):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    dev = torch.device("cuda:0")
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": nbytes, "launches": 3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    kda.load_library()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    w, wall, per = bench_forward(args.steps, args.warmup)
+    ms_per_step = wall / args.steps * 1e3
+    kern_ms = float(np.mean(per))
+    nbytes = fwd_bytes(w.T, w.H, w.Dk, w.Dv, n_states_out=1)
+    nflops = fwd_flops(w.T, w.H, w.Dk, w.Dv)
+    gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    tflops = nflops / (kern_ms * 1e-3) / 1e12
+    traffic = read_traffic()
+    line = {
+        "metric": METRIC,
+        "value": w.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "k3_t4096: KDA chunked forward, B=1, T=4096, H=96, d_k=d_v=128, chunk 64, "
+                               "bf16 q/k/v/g/beta, zero initial state, fp32 final state",
+                   "B": w.B, "T": w.T, "H": w.H, "d_k": w.Dk, "d_v": w.Dv, "chunk": w.chunk},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic},
+        "kernel_ms": kern_ms,
+        "algorithmic_bytes_per_launch": nbytes,
+        "mfma": {"achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tflops / BF16_PEAK_TFLOPS, "flops_per_launch": nflops,
+                 "count": "full 64x64 tiles at chunk 64: T*H*(2*64*(3*d_k+2*d_v)+6*d_k*d_v)"},
+        "published_baseline": "none: the source pages report no KDA throughput on any hardware",
+    }
+    if not args.no_decode:
+        line["decode"] = bench_decode(args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
