@@ -62,7 +62,10 @@ typedef enum {
  *                  their initial state. Packed ("THD") batches are how the K3
  *                  package feeds variable-length sequences (ISEEKYAN/k3 README,
  *                  packed THD with context parallelism).
- *   chunk_size     16, 32 or 64; 0 selects 64. It changes only rounding.
+ *   chunk_size     16, 32 or 64, or 0 for the default. It changes only
+ *                  rounding. It sets the chunk length of the float32 path
+ *                  (default 64); the bf16 matrix-core kernel always works in
+ *                  its native 16-row chunks.
  *   scale          multiplies the output (1.0 reproduces the rule above)
  *   o              [B,T,H,Dv]  dtype, written for every row of every sequence;
  *                  must not alias an input. With T = 0, q, k, v, g, beta and
@@ -70,9 +73,9 @@ typedef enum {
  *   final_state    [N,H,Dk,Dv] float32, or NULL (not written); may alias
  *                  initial_state (each state tile is read before it is written)
  *
- * Supported: Dk, Dv in {16, 32, 64, 128}. bf16 with Dk = Dv = 128 and
- * chunk 64 runs the matrix-core kernel; everything else runs the float32
- * vector-ALU chunk kernel. Chunks start at each sequence's first token; rows
+ * Supported: Dk, Dv in {16, 32, 64, 128}. bf16 with Dk = Dv = 128 runs the
+ * matrix-core kernel; everything else runs the float32 vector-ALU chunk
+ * kernel. Chunks start at each sequence's first token; rows
  * past a sequence's end inside its last chunk are treated as zero tokens,
  * which leave the state unchanged.
  */

@@ -39,7 +39,7 @@ def test_f32_general_dims(Dk, Dv, chunk):
     _check(inp, TOL_F32, chunk=chunk, label=f"f32 Dk={Dk} Dv={Dv}")
 
 
-@pytest.mark.parametrize("B,T,H", [(1, 293, 5), (3, 200, 16), (2, 64, 8), (1, 1, 3)])
+@pytest.mark.parametrize("B,T,H", [(1, 293, 5), (3, 200, 16), (2, 64, 8), (1, 1, 3), (3, 77, 96)])
 def test_bf16_mfma_path(B, T, H):
     inp = synth.make_chunk_inputs(B, T, H, 128, 128, seed=200 + T + H, dtype="bf16", init_state=True)
     _check(inp, TOL_BF16, label=f"bf16 mfma B={B} T={T} H={H}")
