@@ -20,6 +20,8 @@ CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     # no packed-fp32 instructions in any generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep matrix-core accumulators in ordinary VGPRs (avoids AGPR copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -149,32 +149,44 @@ struct ChunkRegs {
     uint32_t beta;        // raw bf16 bits
 };
 
-// Loads of one 16-row chunk in row layout. Every load is unconditional:
-// rows past the sequence end re-read its last row (a valid address) and are
-// zeroed where consumed, so no load waits behind a branch.
-template <int NW>
-__device__ __forceinline__ void load_chunk(ChunkRegs<NW>& R, const ChunkArgs& a, int64_t tok_base,
-                                           int64_t first, int64_t len, int h, int vt, int li, int lg) {
-    // row `first + li` of the sequence, clamped to its last row (len >= 1)
-    const int64_t r = first + li < len ? first + li : len - 1;
-    const int64_t row = (tok_base + r) * a.H + h;
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) + row * kDK + 8 * lg;
-    const uint16_t* k = static_cast<const uint16_t*>(a.k) + row * kDK + 8 * lg;
-    const uint16_t* g = static_cast<const uint16_t*>(a.g) + row * kDK + 8 * lg;
-    const uint16_t* v = static_cast<const uint16_t*>(a.v) + row * kDV + vt * Cfg<NW>::BV + 8 * lg;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        R.q[kk] = *reinterpret_cast<const uint4*>(q + 32 * kk);
-        R.k[kk] = *reinterpret_cast<const uint4*>(k + 32 * kk);
-        R.g[kk] = *reinterpret_cast<const uint4*>(g + 32 * kk);
-    }
-#pragma unroll
-    for (int p = 0; p < NW / 2; ++p) R.v[p] = *reinterpret_cast<const uint4*>(v + 32 * p);
-    R.beta = static_cast<const uint16_t*>(a.beta)[row];
+// Buffer resource over [base, base + nbytes): accesses outside it read 0 and
+// writes outside it are dropped by the hardware. This is how rows past a
+// sequence's end become zero tokens (an exact identity step of the
+// recurrence) and how their outputs are never written, with no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t nbytes) {
+    const int32_t n = nbytes <= 0 ? 0 : (nbytes > 0x7fffffff ? 0x7fffffff : (int32_t)nbytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
-__device__ __forceinline__ uint4 keep_if(bool ok, const uint4& u) {
-    return ok ? u : make_uint4(0, 0, 0, 0);
+// Loads of one 16-row chunk (sequence rows first..first+15) in row layout:
+// lane (li, lg) gets row li, channels 32kk+8lg..+7 and value columns
+// 32p+8lg..+7 of its slice. voff = li*H*256 + 16*lg bytes, voffb = li*H*2.
+template <int NW>
+__device__ __forceinline__ void load_chunk(ChunkRegs<NW>& R, const ChunkArgs& a, int64_t tok_base,
+                                           int64_t first, int64_t len, int h, int vt, int voff, int voffb) {
+    const int64_t row0 = (tok_base + first) * a.H + h;
+    const int64_t span = (len - first) * a.H * (int64_t)(kDK * 2);    // bytes to the sequence end
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(a.q) + row0 * kDK, span);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(a.k) + row0 * kDK, span);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(static_cast<const uint16_t*>(a.g) + row0 * kDK, span);
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(static_cast<const uint16_t*>(a.v) + row0 * kDV + vt * Cfg<NW>::BV, span - vt * Cfg<NW>::BV * 2);
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(static_cast<const uint16_t*>(a.beta) + row0, (len - first) * a.H * 2);
+    // issue order = roughly consumption order, so each use waits only for
+    // the loads it needs (memory operations complete in issue order)
+    R.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, voffb, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        R.g[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, voff + 64 * kk, 0, 0));
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        R.k[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff + 64 * kk, 0, 0));
+        R.q[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + 64 * kk, 0, 0));
+    }
+#pragma unroll
+    for (int p = 0; p < NW / 2; ++p)
+        R.v[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff + 64 * p, 0, 0));
 }
 
 template <int NW>
@@ -257,17 +269,17 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_mfma_kernel(ChunkArgs a) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) eye[hf][s] = (__bf16)((8 * lg + s == 16 * hf + li) ? 1.f : 0.f);
 
+    const int voff = li * a.H * (kDK * 2) + 16 * lg;          // row li, 8 channels at 8lg
+    const int voffb = li * a.H * 2;
+    const int voffo = li * a.H * (kDV * 2) + (cw + 4 * lg) * 2;   // output row li, 4 columns
     ChunkRegs<NW> R;
-    if (ngroups > 0) load_chunk<NW>(R, a, tok_base, (int64_t)w * kC, len, h, vt, li, lg);
+    if (ngroups > 0) load_chunk<NW>(R, a, tok_base, (int64_t)w * kC, len, h, vt, voff, voffb);
 
     uint16_t* const out = static_cast<uint16_t*>(a.o);
     for (int grp = 0; grp < ngroups; ++grp) {
         // ========== phase A: wave w prepares chunk c = grp*NW + w ==========
         {
             const int c = grp * NW + w;
-            const int64_t left = len - (int64_t)c * kC;
-            const int rows = (int)(left < 0 ? 0 : (left < kC ? left : kC));
-            const bool ok = li < rows;
             char* const slot = smem + w * CF::SLOT;
 
             // cumulative log2-decay over the 16 rows (DPP scan along lane%16)
@@ -275,7 +287,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_mfma_kernel(ChunkArgs a) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 float gf[8];
-                unpack8(keep_if(ok, R.g[kk]), gf);
+                unpack8(R.g[kk], gf);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) G[kk][e] = scan16(gf[e] * kLog2e);
             }
@@ -285,8 +297,8 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_mfma_kernel(ChunkArgs a) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 float kf[8], qf[8], ka[8], qa[8], kb[8];
-                unpack8(keep_if(ok, R.k[kk]), kf);
-                unpack8(keep_if(ok, R.q[kk]), qf);
+                unpack8(R.k[kk], kf);
+                unpack8(R.q[kk], qf);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float el = exp2_fast(G[kk][e]);
@@ -321,7 +333,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_mfma_kernel(ChunkArgs a) {
                 Mr = mfma32(KB[kk], KA[kk], Mr);    // lane: M[li][4lg+j]
                 Pr = mfma32(KB[kk], QA[kk], Pr);    // lane: P[li][4lg+j]
             }
-            const float beta_li = ok ? bf16_bits_to_f32(R.beta) : 0.f;
+            const float beta_li = bf16_bits_to_f32(R.beta);
             f32x4 bj;   // beta of rows 4lg+j
 #pragma unroll
             for (int j = 0; j < 4; ++j) bj[j] = __shfl(beta_li, 4 * lg + j);
@@ -360,7 +372,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_mfma_kernel(ChunkArgs a) {
             // V^T
 #pragma unroll
             for (int p = 0; p < NW / 2; ++p) {
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, keep_if(ok, R.v[p]));
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, R.v[p]);
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
                     const f32x4 vT = mfma32(vf, eye[hf], zero4());        // V[4lg+j][32p+16hf+li]
@@ -370,19 +382,22 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_mfma_kernel(ChunkArgs a) {
             // prefetch this wave's chunk of the next group
             if (grp + 1 < ngroups) {
                 const int cn = c + NW;
-                load_chunk<NW>(R, a, tok_base, (int64_t)cn * kC, len, h, vt, li, lg);
+                load_chunk<NW>(R, a, tok_base, (int64_t)cn * kC, len, h, vt, voff, voffb);
             }
         }
         __syncthreads();   // all chunks of the group published
 
         // ========== phase B: the state chain through the group's chunks ==========
-#pragma unroll 1
+        // Unrolled and unconditional: a chunk past the sequence end holds zero
+        // tokens, which leave the state unchanged, and its output stores fall
+        // outside the store buffer's range, so the hardware drops them.
+#pragma unroll
         for (int s = 0; s < NW; ++s) {
             const int c = grp * NW + s;
-            const int64_t left = len - (int64_t)c * kC;
-            if (left <= 0) break;                              // uniform
-            const int rows = (int)(left < kC ? left : kC);
             const char* const slot = smem + s * CF::SLOT;
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(out + ((tok_base + (int64_t)c * kC) * a.H + h) * kDV + vt * BV,
+                          (len - (int64_t)c * kC) * a.H * (kDV * 2) - vt * BV * 2);
 
             bf16x8 sb[4];
 #pragma unroll
@@ -407,12 +422,10 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_mfma_kernel(ChunkArgs a) {
             // take a 16x16x32 result as its accumulator input (the compiler does not
             // insert enough wait states between the two shapes on gfx950).
             OT += mfma16(ub, pp, zero4());
-            if (li < rows) {
-                const int64_t tok = tok_base + (int64_t)c * kC + li;
-                *reinterpret_cast<uint2*>(out + (tok * a.H + h) * kDV + vt * BV + cw + 4 * lg) =
-                    make_uint2(pack2_bf16(a.scale * OT[0], a.scale * OT[1]),
-                               pack2_bf16(a.scale * OT[2], a.scale * OT[3]));
-            }
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            __builtin_amdgcn_raw_buffer_store_b64(
+                u32x2{pack2_bf16(a.scale * OT[0], a.scale * OT[1]), pack2_bf16(a.scale * OT[2], a.scale * OT[3])},
+                ro, voffo, 0, 0);
             // S <- Diag(e^{Gamma_C}) S + Kh^T U
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt) {
