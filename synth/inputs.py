@@ -12,8 +12,12 @@ is bounded below by gate_lower_bound = -5.0 (section "Attention is 93
 layers ..."); packed variable-length batches are concatenated on T with
 cumulative offsets (ISEEKYAN/k3 README, packed THD with context parallelism).
 
-Recipe (all draws from numpy's PCG64 ``default_rng(seed)``, float32):
-  draw order: [sequence lengths] -> q -> k -> v -> g_raw -> beta_raw -> [S0]
+Recipe (numpy PCG64 generators, float32 draws):
+  streams: lengths 0, q 1, k 2, v 3, g_raw 4, beta_raw 5, S0 6. Stream s of a
+  workload with seed S is cut into fixed blocks of BLOCK_ROWS leading-axis
+  rows (tokens; state slots for S0); block b is drawn from
+  ``default_rng([S, s, b])``. Blocks are independent, so large tensors are
+  filled on several threads and the values never depend on the thread count.
   q, k  ~ N(0,1), then L2-normalised over d_k per (token, head), in float32
   v     ~ N(0,1)
   g     = -5 * sigmoid(g_raw), g_raw ~ N(0,1)   (per channel, in [-5, 0))
@@ -24,6 +28,8 @@ even). States stay float32.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -81,6 +87,41 @@ def packed_lengths(rng, n, lo, hi):
     return rng.integers(lo, hi + 1, size=n)
 
 
+BLOCK_ROWS = 1024
+_STREAM = dict(lengths=0, q=1, k=2, v=3, g=4, beta=5, s0=6)
+
+
+def _pool_size():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _blocked(seed, stream, shape, finish):
+    """float32 array of ``shape`` whose leading-axis blocks of BLOCK_ROWS rows
+    are standard normals from default_rng([seed, stream, block]), each block
+    passed through ``finish`` (an elementwise or per-row map) in place."""
+    out = np.empty(shape, dtype=np.float32)
+    rows = shape[0]
+    nblk = (rows + BLOCK_ROWS - 1) // BLOCK_ROWS
+
+    def fill(b):
+        lo, hi = b * BLOCK_ROWS, min(rows, (b + 1) * BLOCK_ROWS)
+        x = np.random.default_rng([seed, stream, b]).standard_normal((hi - lo,) + tuple(shape[1:]),
+                                                                      dtype=np.float32)
+        out[lo:hi] = finish(x)
+
+    if nblk <= 1:
+        for b in range(nblk):
+            fill(b)
+    else:
+        with ThreadPoolExecutor(max_workers=_pool_size()) as ex:
+            list(ex.map(fill, range(nblk)))
+    return out
+
+
 def make_chunk_inputs(B, T, H, Dk, Dv, seed, dtype="bf16", init_state=False, lengths=None,
                       n_seqs=0, len_lo=0, len_hi=0, g_mode="default", beta_mode="default",
                       v_zero=False, s0_std=0.02):
@@ -93,46 +134,37 @@ def make_chunk_inputs(B, T, H, Dk, Dv, seed, dtype="bf16", init_state=False, len
     Variants used by the stress tests: g_mode "weak" (-0.05*sigmoid), "zero",
     "bound" (g == -5 everywhere); beta_mode "one"; v_zero; s0_std.
     """
-    rng = np.random.default_rng(seed)
     cu = None
     if lengths is None and n_seqs > 0:
-        lengths = packed_lengths(rng, n_seqs, len_lo, len_hi)
+        lengths = packed_lengths(np.random.default_rng([seed, _STREAM["lengths"]]), n_seqs, len_lo, len_hi)
     if lengths is not None:
         lengths = np.asarray(lengths, dtype=np.int64)
         cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
         B, T = 1, int(cu[-1])
     N = B if cu is None else len(cu) - 1
-    q = _l2norm(rng.standard_normal((B, T, H, Dk), dtype=np.float32))
-    k = _l2norm(rng.standard_normal((B, T, H, Dk), dtype=np.float32))
-    v = rng.standard_normal((B, T, H, Dv), dtype=np.float32)
-    g_raw = rng.standard_normal((B, T, H, Dk), dtype=np.float32)
-    b_raw = rng.standard_normal((B, T, H), dtype=np.float32)
-    if g_mode == "default":
-        g = np.float32(GATE_LOWER_BOUND) * _sigmoid(g_raw)
-    elif g_mode == "weak":
-        g = np.float32(-0.05) * _sigmoid(g_raw)
-    elif g_mode == "zero":
-        g = np.zeros_like(g_raw)
-    elif g_mode == "bound":
-        g = np.full_like(g_raw, GATE_LOWER_BOUND)
-    else:
+    rows = B * T
+    ident = lambda x: x  # noqa: E731
+    gmap = {"default": lambda x: np.float32(GATE_LOWER_BOUND) * _sigmoid(x),
+            "weak": lambda x: np.float32(-0.05) * _sigmoid(x),
+            "zero": np.zeros_like,
+            "bound": lambda x: np.full_like(x, GATE_LOWER_BOUND)}
+    bmap = {"default": _sigmoid, "one": np.ones_like, "zero": np.zeros_like}
+    if g_mode not in gmap:
         raise ValueError(g_mode)
-    if beta_mode == "default":
-        beta = _sigmoid(b_raw)
-    elif beta_mode == "one":
-        beta = np.ones_like(b_raw)
-    elif beta_mode == "zero":
-        beta = np.zeros_like(b_raw)
-    else:
+    if beta_mode not in bmap:
         raise ValueError(beta_mode)
-    if v_zero:
-        v = np.zeros_like(v)
+    q = _blocked(seed, _STREAM["q"], (rows, H, Dk), _l2norm)
+    k = _blocked(seed, _STREAM["k"], (rows, H, Dk), _l2norm)
+    v = _blocked(seed, _STREAM["v"], (rows, H, Dv), np.zeros_like if v_zero else ident)
+    g = _blocked(seed, _STREAM["g"], (rows, H, Dk), gmap[g_mode])
+    beta = _blocked(seed, _STREAM["beta"], (rows, H), bmap[beta_mode])
     s0 = None
     if init_state:
-        s0 = torch.from_numpy(
-            (np.float32(s0_std) * rng.standard_normal((N, H, Dk, Dv), dtype=np.float32)))
-    return dict(q=_round(q, dtype), k=_round(k, dtype), v=_round(v, dtype), g=_round(g, dtype),
-                beta=_round(beta, dtype), initial_state=s0,
+        s0 = torch.from_numpy(_blocked(seed, _STREAM["s0"], (N, H, Dk, Dv),
+                                       lambda x: np.float32(s0_std) * x))
+    shp = lambda x: x.reshape((B, T) + x.shape[1:])  # noqa: E731
+    return dict(q=_round(shp(q), dtype), k=_round(shp(k), dtype), v=_round(shp(v), dtype),
+                g=_round(shp(g), dtype), beta=_round(shp(beta), dtype), initial_state=s0,
                 cu_seqlens=None if cu is None else torch.from_numpy(cu))
 
 
@@ -145,10 +177,10 @@ def make_workload(w: Workload, **overrides):
 
 
 def make_decode_cache(n_slots, H, Dk, Dv, seed, std=0.02):
-    """Decode state cache [n_slots,H,Dk,Dv] float32 ~ N(0, std), from default_rng(seed)."""
-    rng = np.random.default_rng(seed)
-    return torch.from_numpy(np.float32(std) * rng.standard_normal((n_slots, H, Dk, Dv),
-                                                                  dtype=np.float32))
+    """Decode state cache [n_slots,H,Dk,Dv] float32 ~ N(0, std): stream 6 of
+    ``seed``, blocked over slots like every other tensor here."""
+    return torch.from_numpy(_blocked(seed, _STREAM["s0"], (n_slots, H, Dk, Dv),
+                                     lambda x: np.float32(std) * x))
 
 
 def make_decode_step(Nb, H, Dk, Dv, seed, step, dtype="bf16"):
