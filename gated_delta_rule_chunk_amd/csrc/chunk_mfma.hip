@@ -64,7 +64,8 @@ constexpr int S_PN = 12800;     // [64 lanes] bf16x4        -P, row li, columns 
 constexpr int S_EG = 13312;     // [4 lg][8 t][4 j] f32     e^{Gamma_C} of channel 16t+4lg+j
 constexpr int SLOT = 13824;
 constexpr int S_FS = 2 * kNA * SLOT;            // per preparation wave: [16][16] f32 (row-wise N)
-constexpr int LDS_BYTES = S_FS + kNA * 1024;
+constexpr int S_JUNK = S_FS + kNA * 1024;       // per preparation wave: 1 KiB sink for masked-off stores
+constexpr int LDS_BYTES = S_JUNK + kNA * 1024;
 static_assert(LDS_BYTES <= 163840, "LDS budget");
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -100,8 +101,7 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // value of x in lane N of this lane's 16-lane row
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                 0x150 + N, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, true));
 }
 
 // Forward substitution for T = (I + N)^{-1}, N strictly lower triangular.
@@ -178,7 +178,7 @@ __device__ __forceinline__ u32x2 load_v(const ChunkArgs& a, int64_t tok_base, in
 // ---------------------------------------------------------------------------
 // preparation of one chunk (wave-local; lane = (li, lg))
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void prepare_chunk(const PrepRegs& R, char* slot, char* fs, int li, int lg,
+__device__ __forceinline__ void prepare_chunk(const PrepRegs& R, char* slot, char* fs, char* junk, int li, int lg,
                                               const bf16x8 (&eyeN)[2], const bf16x8 (&eyeP)[2],
                                               const bf16x4& lowT) {
     const int lane = li + 16 * lg;
@@ -209,8 +209,9 @@ __device__ __forceinline__ void prepare_chunk(const PrepRegs& R, char* slot, cha
                 qa[hf][j] = qf[j] * el[j];
                 kb[hf][j] = kf[j] * enl;
             }
-            if (li == 15)   // token 15 carries e^{Gamma_C}
-                *reinterpret_cast<f32x4*>(slot + S_EG + 4 * (32 * lg + 4 * t)) = el;
+            // token 15 carries e^{Gamma_C}; the other lanes store to the sink
+            // (a store under an exec mask would split the schedule)
+            *reinterpret_cast<f32x4*>(li == 15 ? slot + S_EG + 4 * (32 * lg + 4 * t) : junk) = el;
         }
         KA[kk] = pack_pair(ka[0], ka[1]);
         QA[kk] = pack_pair(qa[0], qa[1]);
@@ -328,18 +329,27 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         const int voff = li * a.H * (kDK * 2) + 16 * lg;
         const int voffb = li * a.H * 2;
         char* const fs = smem + S_FS + 1024 * pa;
-        PrepRegs R;
-        if (ngroups > 0) load_prep(R, a, tok_base, (int64_t)pa * kC, len, h, voff, voffb);
-        for (int it = 0; it <= ngroups; ++it) {
-            if (it < ngroups) {
-                char* const slot = smem + ((it & 1) * kNA + pa) * SLOT;
-                const PrepRegs cur = R;
-                if (it + 1 < ngroups)
-                    load_prep(R, a, tok_base, ((int64_t)(it + 1) * kNA + pa) * kC, len, h, voff, voffb);
-                prepare_chunk(cur, slot, fs, li, lg, eyeN, eyeP, lowT);
-            }
+        char* const junk = smem + S_JUNK + 1024 * pa + 16 * lane;
+        // Two register sets alternate (the loop is unrolled by two), so a
+        // prefetch is never copied (a copy would wait for it to land). Every
+        // step issues its prefetch unconditionally: past the sequence end the
+        // buffer range is empty and the loads return zeros without touching
+        // memory, and every path through the loop then has the same number of
+        // loads in flight, which keeps the compiler's waits exact.
+        PrepRegs R0, R1;
+        auto step = [&](int it, const PrepRegs& cur, PrepRegs& nxt) {
+            load_prep(nxt, a, tok_base, ((int64_t)(it + 1) * kNA + pa) * kC, len, h, voff, voffb);
+            prepare_chunk(cur, smem + ((it & 1) * kNA + pa) * SLOT, fs, junk, li, lg, eyeN, eyeP, lowT);
             __syncthreads();
+        };
+        load_prep(R0, a, tok_base, (int64_t)pa * kC, len, h, voff, voffb);
+        int it = 0;
+        for (; it + 1 < ngroups; it += 2) {
+            step(it, R0, R1);
+            step(it + 1, R1, R0);
         }
+        if (it < ngroups) step(it, R0, R1);
+        __syncthreads();   // the state waves' last group
     } else {
         // ========================== state wave ===============================
         const int cw = 16 * w;                       // this wave's columns within the half
@@ -359,60 +369,74 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         uint16_t* const out = static_cast<uint16_t*>(a.o);
         const float neg_scale = -a.scale;
 
-        u32x2 vcur[kNA], vnext[kNA];
-        for (int it = 0; it <= ngroups; ++it) {
-            if (it < ngroups) {
+        // Value tiles of the next group: two register sets alternate and the
+        // loads are unconditional, as in the preparation waves.
+        u32x2 VA[kNA], VB[kNA];
+        auto load_group = [&](int gi, u32x2 (&vt_)[kNA]) {
 #pragma unroll
-                for (int s = 0; s < kNA; ++s)
-                    vnext[s] = load_v(a, tok_base, ((int64_t)it * kNA + s) * kC, len, h, col0, voffv);
-            }
-            if (it >= 1) {
-                const int gi = it - 1;
-                // Unconditional: a chunk past the sequence end holds zero tokens,
-                // which leave the state unchanged, and its output stores fall
-                // outside the store buffer's range, so the hardware drops them.
+            for (int s = 0; s < kNA; ++s)
+                vt_[s] = load_v(a, tok_base, ((int64_t)gi * kNA + s) * kC, len, h, col0, voffv);
+        };
+        // Chunks of group gi from its LDS buffer. Unconditional: a chunk past
+        // the sequence end holds zero tokens, which leave the state unchanged,
+        // and its output stores fall outside the store buffer's range, so the
+        // hardware drops them.
+        auto consume = [&](int gi, const u32x2 (&vcur)[kNA]) {
 #pragma unroll
-                for (int s = 0; s < kNA; ++s) {
-                    const int c = gi * kNA + s;
-                    const char* const slot = smem + ((gi & 1) * kNA + s) * SLOT;
-                    const __amdgpu_buffer_rsrc_t ro =
-                        make_rsrc(out + ((tok_base + (int64_t)c * kC) * a.H + h) * kDV + col0,
-                                  (len - (int64_t)c * kC) * a.H * (kDV * 2) - col0 * 2);
-                    bf16x8 sbn[4];
+            for (int s = 0; s < kNA; ++s) {
+                const int c = gi * kNA + s;
+                const char* const slot = smem + ((gi & 1) * kNA + s) * SLOT;
+                const __amdgpu_buffer_rsrc_t ro =
+                    make_rsrc(out + ((tok_base + (int64_t)c * kC) * a.H + h) * kDV + col0,
+                              (len - (int64_t)c * kC) * a.H * (kDV * 2) - col0 * 2);
+                bf16x8 sbn[4];
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) sbn[kk] = pack_pair_neg(S[2 * kk], S[2 * kk + 1]);
-                    // X = V - Kg S  (rows 4lg+j, column li)
-                    const bf16x8 vop = widen(__builtin_bit_cast(bf16x4, vcur[s]));
-                    f32x4 X = mfma32(vop, eyeV, zero4());
-                    // OT = -(Qh S)^T  (column 4lg+j of row li)
-                    f32x4 OT = zero4();
+                for (int kk = 0; kk < 4; ++kk) sbn[kk] = pack_pair_neg(S[2 * kk], S[2 * kk + 1]);
+                // X = V - Kg S  (rows 4lg+j, column li)
+                const bf16x8 vop = widen(__builtin_bit_cast(bf16x4, vcur[s]));
+                f32x4 X = mfma32(vop, eyeV, zero4());
+                // OT = -(Qh S)^T  (column 4lg+j of row li)
+                f32x4 OT = zero4();
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        const bf16x8 kg = *reinterpret_cast<const bf16x8*>(slot + S_KG + 16 * (64 * kk + lane));
-                        const bf16x8 qh = *reinterpret_cast<const bf16x8*>(slot + S_QH + 16 * (64 * kk + lane));
-                        X = mfma32(kg, sbn[kk], X);
-                        OT = mfma32(sbn[kk], qh, OT);
-                    }
-                    const bf16x4 tt = *reinterpret_cast<const bf16x4*>(slot + S_TT + 8 * lane);
-                    const f32x4 U = mfma16(tt, pack4v(X), zero4());      // U[4lg+j][li]
-                    const bf16x4 ub = pack4v(U);
-                    const bf16x4 pn = *reinterpret_cast<const bf16x4*>(slot + S_PN + 8 * lane);
-                    OT = mfma32(widen(ub), widen(pn), OT);               // -(Qh S + P U)^T
-                    __builtin_amdgcn_raw_buffer_store_b64(
-                        u32x2{pack2_bf16(neg_scale * OT[0], neg_scale * OT[1]),
-                              pack2_bf16(neg_scale * OT[2], neg_scale * OT[3])},
-                        ro, voffo, 0, 0);
-                    // S <- Diag(e^{Gamma_C}) S + Kh^T U
+                for (int kk = 0; kk < 4; ++kk) {
+                    const bf16x8 kg = *reinterpret_cast<const bf16x8*>(slot + S_KG + 16 * (64 * kk + lane));
+                    const bf16x8 qh = *reinterpret_cast<const bf16x8*>(slot + S_QH + 16 * (64 * kk + lane));
+                    X = mfma32(kg, sbn[kk], X);
+                    OT = mfma32(sbn[kk], qh, OT);
+                }
+                const bf16x4 tt = *reinterpret_cast<const bf16x4*>(slot + S_TT + 8 * lane);
+                const f32x4 U = mfma16(tt, pack4v(X), zero4());      // U[4lg+j][li]
+                const bf16x4 ub = pack4v(U);
+                const bf16x4 pn = *reinterpret_cast<const bf16x4*>(slot + S_PN + 8 * lane);
+                OT = mfma32(widen(ub), widen(pn), OT);               // -(Qh S + P U)^T
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    u32x2{pack2_bf16(neg_scale * OT[0], neg_scale * OT[1]),
+                          pack2_bf16(neg_scale * OT[2], neg_scale * OT[3])},
+                    ro, voffo, 0, 0);
+                // S <- Diag(e^{Gamma_C}) S + Kh^T U
 #pragma unroll
-                    for (int rt = 0; rt < 8; ++rt) {
-                        const f32x4 eg = *reinterpret_cast<const f32x4*>(slot + S_EG + 4 * (32 * lg + 4 * rt));
-                        const bf16x4 kh = *reinterpret_cast<const bf16x4*>(slot + S_KH + 8 * (64 * rt + lane));
-                        S[rt] = mfma16(kh, ub, S[rt] * eg);
-                    }
+                for (int rt = 0; rt < 8; ++rt) {
+                    const f32x4 eg = *reinterpret_cast<const f32x4*>(slot + S_EG + 4 * (32 * lg + 4 * rt));
+                    const bf16x4 kh = *reinterpret_cast<const bf16x4*>(slot + S_KH + 8 * (64 * rt + lane));
+                    S[rt] = mfma16(kh, ub, S[rt] * eg);
                 }
             }
-#pragma unroll
-            for (int s = 0; s < kNA; ++s) vcur[s] = vnext[s];
+        };
+        // iteration it loads group it and consumes group it-1
+        load_group(0, VA);
+        __syncthreads();
+        int it = 1;
+        for (; it + 1 <= ngroups; it += 2) {
+            load_group(it, VB);
+            consume(it - 1, VA);
+            __syncthreads();
+            load_group(it + 1, VA);
+            consume(it, VB);
+            __syncthreads();
+        }
+        if (it <= ngroups) {
+            load_group(it, VB);
+            consume(it - 1, VA);
             __syncthreads();
         }
         if (a.sT) {
