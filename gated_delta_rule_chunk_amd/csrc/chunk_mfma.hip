@@ -15,10 +15,13 @@
 // per-channel decay.
 //
 // Structure. A workgroup owns one (sequence, head, 64-column half of d_v) and
-// runs two kinds of wave side by side, one of each per SIMD:
-//   4 preparation waves: for each group of 4 chunks, wave a builds everything
-//     of chunk a that does not depend on the state (Kg, Qh, Kh^T, T Diag(beta),
-//     -P, e^{Gamma_C}) and stores it to its slot of an LDS double buffer;
+// runs two kinds of wave side by side, three per SIMD:
+//   8 preparation waves, two per chunk of a group of 4: the wave for channel
+//     half h of chunk a builds, for channels 64h..64h+63, everything that
+//     does not depend on the state (Kg, Qh and Kh^T fragments, e^{Gamma_C},
+//     its share of M and P) and stores it to chunk a's slot of an LDS double
+//     buffer; the upper half hands its share of M and P to the lower half,
+//     which forms T Diag(beta) and -P;
 //   4 state waves: wave b carries the fp32 state columns 16b..16b+15 of the
 //     half (128 x 16, in registers) through the chunks of the previous group.
 // One barrier per group hands a filled buffer to the state waves and a free
@@ -48,11 +51,12 @@ namespace {
 constexpr int kC = 16;          // rows per chunk
 constexpr int kDK = 128;
 constexpr int kDV = 128;
-constexpr int kNA = 4;          // preparation waves = chunks per group
+constexpr int kNA = 4;          // chunks per group
+constexpr int kNP = 2 * kNA;    // preparation waves: two channel halves per chunk
 constexpr int kNB = 4;          // state waves, 16 value columns each
 constexpr int kBV = 16 * kNB;   // value columns per workgroup
 constexpr int kNVT = kDV / kBV;
-constexpr int kThreads = 64 * (kNA + kNB);
+constexpr int kThreads = 64 * (kNP + kNB);
 
 // One chunk's slot (bytes). Fragments are stored in lane order, so every
 // access is 64 consecutive 8- or 16-byte pieces.
@@ -61,11 +65,14 @@ constexpr int S_QH = 4096;      // [4 kk][64 lanes] bf16x8  (e^G Q)
 constexpr int S_KH = 8192;      // [8 rt][64 lanes] bf16x4  (e^{Gc-G} K)^T, A operand of the state update
 constexpr int S_TT = 12288;     // [64 lanes] bf16x4        T Diag(beta), row li, columns 4lg+j
 constexpr int S_PN = 12800;     // [64 lanes] bf16x4        -P, row li, columns 4lg+j
-constexpr int S_EG = 13312;     // [4 lg][8 t][4 j] f32     e^{Gamma_C} of channel 16t+4lg+j
-constexpr int SLOT = 13824;
-constexpr int S_FS = 2 * kNA * SLOT;            // per preparation wave: [16][16] f32 (row-wise N)
-constexpr int S_JUNK = S_FS + kNA * 1024;       // per preparation wave: 1 KiB sink for masked-off stores
-constexpr int LDS_BYTES = S_JUNK + kNA * 1024;
+constexpr int S_EG = 13312;     // [4 lg][36] f32: entry 4t+j is e^{Gamma_C} of channel 16t+4lg+j
+constexpr int EG_STRIDE = 36;   //   (32 used; the pad keeps the lane groups in different banks)
+constexpr int SLOT = S_EG + 4 * 4 * EG_STRIDE;
+constexpr int S_FS = 2 * kNA * SLOT;            // per chunk: [16][16] f32 (row-wise N)
+constexpr int S_XP = S_FS + kNA * 1024;         // per chunk: upper half's share of M, P (32 B per lane)
+constexpr int S_JUNK = S_XP + kNA * 2048;       // per preparation wave: 1 KiB sink for masked-off stores
+constexpr int S_FLAG = S_JUNK + kNP * 1024;     // per chunk: int, step count + 1 once the share is stored
+constexpr int LDS_BYTES = S_FLAG + 16 * kNA;
 static_assert(LDS_BYTES <= 163840, "LDS budget");
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -98,6 +105,16 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const 
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Workgroup barrier that the instruction scheduler may not move work across:
+// otherwise it pulls register-only work of the next step (which consumes the
+// prefetch just issued) above the barrier and the wave waits for that
+// prefetch to land.
+__device__ __forceinline__ void group_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // value of x in lane N of this lane's 16-lane row
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
@@ -114,6 +131,22 @@ __device__ __forceinline__ void fsub(f32x4& t, const float* nrow) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) t[c] = fmaf(-nrow[J], row_bcast<J>(t[c]), t[c]);
         fsub<J + 1>(t, nrow);
+    }
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// S[rt] <- Diag(e) S[rt] + Kh^T U for tiles RT..7. e2 holds decay entries
+// 2li, 2li+1 of this lane's row group; row 4lg+j of tile RT needs entry
+// 4RT+j, held by lane 2RT + j/2 of the same 16-lane row.
+template <int RT>
+__device__ __forceinline__ void update_state(f32x4 (&S)[8], const f32x2& e2, const char* kh_base, const bf16x4& ub) {
+    if constexpr (RT < 8) {
+        const f32x4 d = {S[RT][0] * row_bcast<2 * RT>(e2[0]), S[RT][1] * row_bcast<2 * RT>(e2[1]),
+                         S[RT][2] * row_bcast<2 * RT + 1>(e2[0]), S[RT][3] * row_bcast<2 * RT + 1>(e2[1])};
+        const bf16x4 kh = *reinterpret_cast<const bf16x4*>(kh_base + 512 * RT);
+        S[RT] = mfma16(kh, ub, d);
+        update_state<RT + 1>(S, e2, kh_base, ub);
     }
 }
 
@@ -138,31 +171,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 struct PrepRegs {
-    uint4 q[4], k[4], g[4];   // row li, channels 32kk+8lg..+7
-    uint32_t beta;            // raw bf16 bits of beta[row li]
+    uint4 q[2], k[2], g[2];   // row li, channels 32(2h+m)+8lg..+7, m = 0, 1
+    uint32_t beta;            // raw bf16 bits of beta[row li] (lower half only)
 };
 
-// Loads of one 16-row chunk (sequence rows first..first+15) for a preparation
-// wave. voff = li*H*256 + 16*lg bytes, voffb = li*H*2.
+// Loads of channel half h of one 16-row chunk (sequence rows first..first+15)
+// for a preparation wave. voff = li*H*256 + 128*h + 16*lg bytes, voffb = li*H*2.
 __device__ __forceinline__ void load_prep(PrepRegs& R, const ChunkArgs& a, int64_t tok_base, int64_t first,
-                                          int64_t len, int h, int voff, int voffb) {
+                                          int64_t len, int h, int voff, int voffb, bool with_beta) {
     const int64_t row0 = (tok_base + first) * a.H + h;
     const int64_t span = (len - first) * a.H * (int64_t)(kDK * 2);    // bytes to the sequence end
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(a.q) + row0 * kDK, span);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(a.k) + row0 * kDK, span);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(static_cast<const uint16_t*>(a.g) + row0 * kDK, span);
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(static_cast<const uint16_t*>(a.beta) + row0, (len - first) * a.H * 2);
     // issue order = consumption order; memory operations complete in order
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        R.g[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, voff + 64 * kk, 0, 0));
+    for (int m = 0; m < 2; ++m)
+        R.g[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, voff + 64 * m, 0, 0));
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        R.k[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff + 64 * kk, 0, 0));
-        R.q[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + 64 * kk, 0, 0));
+    for (int m = 0; m < 2; ++m) {
+        R.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff + 64 * m, 0, 0));
+        R.q[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + 64 * m, 0, 0));
     }
-    R.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, voffb, 0, 0);
+    if (with_beta) {
+        const __amdgpu_buffer_rsrc_t rb =
+            make_rsrc(static_cast<const uint16_t*>(a.beta) + row0, (len - first) * a.H * 2);
+        R.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, voffb, 0, 0);
+    }
 }
 
 // Value tile of one chunk for a state wave: row li, columns 4lg..4lg+3 of
@@ -176,18 +211,21 @@ __device__ __forceinline__ u32x2 load_v(const ChunkArgs& a, int64_t tok_base, in
 }
 
 // ---------------------------------------------------------------------------
-// preparation of one chunk (wave-local; lane = (li, lg))
+// preparation of channel half H of one chunk (wave-local; lane = (li, lg));
+// fragments kk = 2H, 2H+1, tiles t = 4H..4H+3
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void prepare_chunk(const PrepRegs& R, char* slot, char* fs, char* junk, int li, int lg,
-                                              const bf16x8 (&eyeN)[2], const bf16x8 (&eyeP)[2],
-                                              const bf16x4& lowT) {
+template <int H>
+__device__ __forceinline__ void prepare_half(const PrepRegs& R, char* slot, char* fs, char* xp, int* flag, int epoch,
+                                             char* junk, int li, int lg, const bf16x8 (&eyeN)[2],
+                                             const bf16x8 (&eyeP)[2], const bf16x4& lowT) {
     const int lane = li + 16 * lg;
-    bf16x8 KA[4], QA[4], KB[4];
+    bf16x8 KA[2], QA[2], KB[2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 gop = __builtin_bit_cast(bf16x8, R.g[kk]);
-        const bf16x8 kop = __builtin_bit_cast(bf16x8, R.k[kk]);
-        const bf16x8 qop = __builtin_bit_cast(bf16x8, R.q[kk]);
+    for (int m = 0; m < 2; ++m) {
+        const int kk = 2 * H + m;
+        const bf16x8 gop = __builtin_bit_cast(bf16x8, R.g[m]);
+        const bf16x8 kop = __builtin_bit_cast(bf16x8, R.k[m]);
+        const bf16x8 qop = __builtin_bit_cast(bf16x8, R.q[m]);
         f32x4 ka[2], qa[2], kb[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -211,57 +249,75 @@ __device__ __forceinline__ void prepare_chunk(const PrepRegs& R, char* slot, cha
             }
             // token 15 carries e^{Gamma_C}; the other lanes store to the sink
             // (a store under an exec mask would split the schedule)
-            *reinterpret_cast<f32x4*>(li == 15 ? slot + S_EG + 4 * (32 * lg + 4 * t) : junk) = el;
+            *reinterpret_cast<f32x4*>(li == 15 ? slot + S_EG + 4 * (EG_STRIDE * lg + 4 * t) : junk) = el;
         }
-        KA[kk] = pack_pair(ka[0], ka[1]);
-        QA[kk] = pack_pair(qa[0], qa[1]);
-        KB[kk] = pack_pair(kb[0], kb[1]);
-        *reinterpret_cast<bf16x8*>(slot + S_KG + 16 * (64 * kk + lane)) = KA[kk];
-        *reinterpret_cast<bf16x8*>(slot + S_QH + 16 * (64 * kk + lane)) = QA[kk];
+        KA[m] = pack_pair(ka[0], ka[1]);
+        QA[m] = pack_pair(qa[0], qa[1]);
+        KB[m] = pack_pair(kb[0], kb[1]);
+        *reinterpret_cast<bf16x8*>(slot + S_KG + 16 * (64 * kk + lane)) = KA[m];
+        *reinterpret_cast<bf16x8*>(slot + S_QH + 16 * (64 * kk + lane)) = QA[m];
     }
 
-    // M and P, row li, columns 4lg+j: contraction over the 128 channels
+    // this half's share of M and P, row li, columns 4lg+j
     f32x4 Mr = zero4(), Pr = zero4();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        Mr = mfma32(KB[kk], KA[kk], Mr);    // (Kg Kb^T)[li][4lg+j]
-        Pr = mfma32(KB[kk], QA[kk], Pr);    // (Qh Kb^T)[li][4lg+j]
+    for (int m = 0; m < 2; ++m) {
+        Mr = mfma32(KB[m], KA[m], Mr);    // (Kg Kb^T)[li][4lg+j] over these channels
+        Pr = mfma32(KB[m], QA[m], Pr);    // (Qh Kb^T)[li][4lg+j]
     }
-    const float beta_li = bf16_bits_to_f32(R.beta);
-    f32x4 bj;   // beta of rows 4lg+j
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bj[j] = __shfl(beta_li, 4 * lg + j);
-    f32x4 Nr, Pn, Tr;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int col = 4 * lg + j;
-        Nr[j] = (col < li) ? beta_li * Mr[j] : 0.f;
-        Pn[j] = (col <= li) ? -Pr[j] : 0.f;
-        Tr[j] = (col == li) ? 1.f : 0.f;
+    if constexpr (H == 1) {
+        // hand the share to the lower half: data first, then the flag (release)
+        *reinterpret_cast<f32x4*>(xp + 32 * lane) = Mr;
+        *reinterpret_cast<f32x4*>(xp + 32 * lane + 16) = Pr;
+        __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    // T = (I + N)^{-1}: each lane needs its whole row of N
-    *reinterpret_cast<f32x4*>(fs + 4 * (16 * li + 4 * lg)) = Nr;
-    float nrow[16];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(fs + 4 * (16 * li + 4 * p));
-        nrow[4 * p] = x[0]; nrow[4 * p + 1] = x[1]; nrow[4 * p + 2] = x[2]; nrow[4 * p + 3] = x[3];
-    }
-    fsub<0>(Tr, nrow);
-    *reinterpret_cast<bf16x4*>(slot + S_TT + 8 * lane) = pack4v(Tr * bj);
-    *reinterpret_cast<bf16x4*>(slot + S_PN + 8 * lane) = pack4v(Pn);
 
     // (e^{Gamma_C - Gamma} K)^T per state tile: transpose Kb on the matrix
     // cores, then scale channel 16t+li by e^{Gamma_C}
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int m = 0; m < 2; ++m) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            const int t = 2 * kk + hf;
-            const f32x4 kbT = mfma32(KB[kk], eyeP[hf], zero4());   // Kb[token 4lg+j][channel 16t+li]
-            const float egc = *reinterpret_cast<const float*>(slot + S_EG + 4 * (32 * (li >> 2) + 4 * t + (li & 3)));
+            const int t = 4 * H + 2 * m + hf;
+            const f32x4 kbT = mfma32(KB[m], eyeP[hf], zero4());   // Kb[token 4lg+j][channel 16t+li]
+            const float egc = *reinterpret_cast<const float*>(slot + S_EG + 4 * (EG_STRIDE * (li >> 2) + 4 * t + (li & 3)));
             *reinterpret_cast<bf16x4*>(slot + S_KH + 8 * (64 * t + lane)) = pack4v(kbT * egc);
         }
+    }
+
+    if constexpr (H == 0) {
+        // the upper half's share (bounded wait: the upper half stores it every
+        // step before it waits for anything, so the flag always arrives)
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+            if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == epoch) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        Mr += *reinterpret_cast<const f32x4*>(xp + 32 * lane);
+        Pr += *reinterpret_cast<const f32x4*>(xp + 32 * lane + 16);
+
+        const float beta_li = bf16_bits_to_f32(R.beta);
+        f32x4 bj;   // beta of rows 4lg+j
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bj[j] = __shfl(beta_li, 4 * lg + j);
+        f32x4 Nr, Pn, Tr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = 4 * lg + j;
+            Nr[j] = (col < li) ? beta_li * Mr[j] : 0.f;
+            Pn[j] = (col <= li) ? -Pr[j] : 0.f;
+            Tr[j] = (col == li) ? 1.f : 0.f;
+        }
+        // T = (I + N)^{-1}: each lane needs its whole row of N
+        *reinterpret_cast<f32x4*>(fs + 4 * (16 * li + 4 * lg)) = Nr;
+        float nrow[16];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(fs + 4 * (16 * li + 4 * p));
+            nrow[4 * p] = x[0]; nrow[4 * p + 1] = x[1]; nrow[4 * p + 2] = x[2]; nrow[4 * p + 3] = x[3];
+        }
+        fsub<0>(Tr, nrow);
+        *reinterpret_cast<bf16x4*>(slot + S_TT + 8 * lane) = pack4v(Tr * bj);
+        *reinterpret_cast<bf16x4*>(slot + S_PN + 8 * lane) = pack4v(Pn);
     }
 }
 
@@ -311,10 +367,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
     const int nchunks = (int)((len + kC - 1) / kC);
     const int ngroups = (nchunks + kNA - 1) / kNA;
     const int64_t state_base = ((int64_t)n * a.H + h) * kDK * kDV;
+    // hand-over flags start below every step count (LDS holds stale data)
+    if (tid < kNA) reinterpret_cast<int*>(smem + S_FLAG)[4 * tid] = 0;
+    __syncthreads();
 
     if (w >= kNB) {
         // ======================= preparation wave ============================
-        const int pa = w - kNB;
+        const int pa = (w - kNB) & (kNA - 1);        // chunk within the group
+        const int ph = (w - kNB) / kNA;              // channel half (wave-uniform)
         bf16x8 eyeN[2], eyeP[2];   // identity blocks for the natural / packed slot orders
         bf16x4 lowT;               // (L^T)[4lg+s][li] = (4lg+s <= li)
 #pragma unroll
@@ -326,10 +386,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
             }
 #pragma unroll
         for (int s = 0; s < 4; ++s) lowT[s] = (__bf16)((4 * lg + s <= li) ? 1.f : 0.f);
-        const int voff = li * a.H * (kDK * 2) + 16 * lg;
+        const int voff = li * a.H * (kDK * 2) + 128 * ph + 16 * lg;
         const int voffb = li * a.H * 2;
         char* const fs = smem + S_FS + 1024 * pa;
-        char* const junk = smem + S_JUNK + 1024 * pa + 16 * lane;
+        char* const xp = smem + S_XP + 2048 * pa;
+        int* const flag = reinterpret_cast<int*>(smem + S_FLAG) + 4 * pa;
+        char* const junk = smem + S_JUNK + 1024 * (w - kNB) + 16 * lane;
+        const bool lower = ph == 0;
         // Two register sets alternate (the loop is unrolled by two), so a
         // prefetch is never copied (a copy would wait for it to land). Every
         // step issues its prefetch unconditionally: past the sequence end the
@@ -338,18 +401,22 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         // loads in flight, which keeps the compiler's waits exact.
         PrepRegs R0, R1;
         auto step = [&](int it, const PrepRegs& cur, PrepRegs& nxt) {
-            load_prep(nxt, a, tok_base, ((int64_t)(it + 1) * kNA + pa) * kC, len, h, voff, voffb);
-            prepare_chunk(cur, smem + ((it & 1) * kNA + pa) * SLOT, fs, junk, li, lg, eyeN, eyeP, lowT);
-            __syncthreads();
+            load_prep(nxt, a, tok_base, ((int64_t)(it + 1) * kNA + pa) * kC, len, h, voff, voffb, lower);
+            char* const slot = smem + ((it & 1) * kNA + pa) * SLOT;
+            if (lower)
+                prepare_half<0>(cur, slot, fs, xp, flag, it + 1, junk, li, lg, eyeN, eyeP, lowT);
+            else
+                prepare_half<1>(cur, slot, fs, xp, flag, it + 1, junk, li, lg, eyeN, eyeP, lowT);
+            group_barrier();
         };
-        load_prep(R0, a, tok_base, (int64_t)pa * kC, len, h, voff, voffb);
+        load_prep(R0, a, tok_base, (int64_t)pa * kC, len, h, voff, voffb, lower);
         int it = 0;
         for (; it + 1 < ngroups; it += 2) {
             step(it, R0, R1);
             step(it + 1, R1, R0);
         }
         if (it < ngroups) step(it, R0, R1);
-        __syncthreads();   // the state waves' last group
+        group_barrier();   // the state waves' last group
     } else {
         // ========================== state wave ===============================
         const int cw = 16 * w;                       // this wave's columns within the half
@@ -413,31 +480,29 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
                     u32x2{pack2_bf16(neg_scale * OT[0], neg_scale * OT[1]),
                           pack2_bf16(neg_scale * OT[2], neg_scale * OT[3])},
                     ro, voffo, 0, 0);
-                // S <- Diag(e^{Gamma_C}) S + Kh^T U
-#pragma unroll
-                for (int rt = 0; rt < 8; ++rt) {
-                    const f32x4 eg = *reinterpret_cast<const f32x4*>(slot + S_EG + 4 * (32 * lg + 4 * rt));
-                    const bf16x4 kh = *reinterpret_cast<const bf16x4*>(slot + S_KH + 8 * (64 * rt + lane));
-                    S[rt] = mfma16(kh, ub, S[rt] * eg);
-                }
+                // S <- Diag(e^{Gamma_C}) S + Kh^T U. Lane li of row group lg
+                // reads entries 2li, 2li+1 of the group's 32 decay factors;
+                // tile rt row 4lg+j needs entry 4rt+j, which DPP broadcasts.
+                const f32x2 e2 = *reinterpret_cast<const f32x2*>(slot + S_EG + 4 * (EG_STRIDE * lg + 2 * li));
+                update_state<0>(S, e2, slot + S_KH + 8 * lane, ub);
             }
         };
         // iteration it loads group it and consumes group it-1
         load_group(0, VA);
-        __syncthreads();
+        group_barrier();
         int it = 1;
         for (; it + 1 <= ngroups; it += 2) {
             load_group(it, VB);
             consume(it - 1, VA);
-            __syncthreads();
+            group_barrier();
             load_group(it + 1, VA);
             consume(it, VB);
-            __syncthreads();
+            group_barrier();
         }
         if (it <= ngroups) {
             load_group(it, VB);
             consume(it - 1, VA);
-            __syncthreads();
+            group_barrier();
         }
         if (a.sT) {
 #pragma unroll
