@@ -20,10 +20,11 @@
 //     half h of chunk a builds, for channels 64h..64h+63, everything that
 //     does not depend on the state (Kg, Qh and Kh^T fragments, e^{Gamma_C},
 //     its share of M and P) and stores it to chunk a's slot of an LDS double
-//     buffer; the upper half hands its share of M and P to the lower half,
-//     which forms T Diag(beta) and -P;
+//     buffer;
 //   4 state waves: wave b carries the fp32 state columns 16b..16b+15 of the
 //     half (128 x 16, in registers) through the chunks of the previous group.
+//     After that, wave b waits for the two shares of M and P of chunk b of
+//     the group being prepared, and forms its T Diag(beta) and -P.
 // One barrier per group hands a filled buffer to the state waves and a free
 // one to the preparation waves, so preparation of group i+1 overlaps the
 // state chain of group i.
@@ -68,14 +69,15 @@ constexpr int S_PN = 12800;     // [64 lanes] bf16x4        -P, row li, columns 
 constexpr int S_EG = 13312;     // [4 lg][36] f32: entry 4t+j is e^{Gamma_C} of channel 16t+4lg+j
 constexpr int EG_STRIDE = 36;   //   (32 used; the pad keeps the lane groups in different banks)
 constexpr int SLOT = S_EG + 4 * 4 * EG_STRIDE;
-constexpr int S_FS = 2 * kNA * SLOT;            // per chunk: [16][16] f32 (row-wise N)
-constexpr int S_XP = S_FS + kNA * 1024;         // per chunk: upper half's share of M, P (32 B per lane)
-constexpr int S_JUNK = S_XP + kNA * 2048;       // per preparation wave: 1 KiB sink for masked-off stores
-constexpr int S_FLAG = S_JUNK + kNP * 1024;     // per chunk: int, step count + 1 once the share is stored
-constexpr int LDS_BYTES = S_FLAG + 16 * kNA;
+constexpr int S_XP = 2 * kNA * SLOT;            // [buffer][chunk][half]: share of M, P (32 B per lane)
+constexpr int S_FS = S_XP + 2 * kNA * 2 * 2048; // per state wave: [16][16] f32 (row-wise N)
+constexpr int S_JUNK = S_FS + kNB * 1024;       // per preparation wave: 1 KiB sink for masked-off stores
+constexpr int S_FLAG = S_JUNK + kNP * 1024;     // per (chunk, half): int, group + 1 once its share is stored
+constexpr int LDS_BYTES = S_FLAG + 4 * kNP;
 static_assert(LDS_BYTES <= 163840, "LDS budget");
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ bf16x8 pack_pair(const f32x4& lo, const f32x4& hi) {
     const bf16x8 r = {(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
@@ -172,13 +174,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 struct PrepRegs {
     uint4 q[2], k[2], g[2];   // row li, channels 32(2h+m)+8lg..+7, m = 0, 1
-    uint32_t beta;            // raw bf16 bits of beta[row li] (lower half only)
 };
 
 // Loads of channel half h of one 16-row chunk (sequence rows first..first+15)
-// for a preparation wave. voff = li*H*256 + 128*h + 16*lg bytes, voffb = li*H*2.
+// for a preparation wave. voff = li*H*256 + 128*h + 16*lg bytes.
 __device__ __forceinline__ void load_prep(PrepRegs& R, const ChunkArgs& a, int64_t tok_base, int64_t first,
-                                          int64_t len, int h, int voff, int voffb, bool with_beta) {
+                                          int64_t len, int h, int voff) {
     const int64_t row0 = (tok_base + first) * a.H + h;
     const int64_t span = (len - first) * a.H * (int64_t)(kDK * 2);    // bytes to the sequence end
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(a.q) + row0 * kDK, span);
@@ -193,11 +194,14 @@ __device__ __forceinline__ void load_prep(PrepRegs& R, const ChunkArgs& a, int64
         R.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff + 64 * m, 0, 0));
         R.q[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + 64 * m, 0, 0));
     }
-    if (with_beta) {
-        const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(static_cast<const uint16_t*>(a.beta) + row0, (len - first) * a.H * 2);
-        R.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, voffb, 0, 0);
-    }
+}
+
+// beta of row li of one chunk for a state wave (raw bf16 bits). voffb = li*H*2.
+__device__ __forceinline__ uint32_t load_beta(const ChunkArgs& a, int64_t tok_base, int64_t first, int64_t len,
+                                              int h, int voffb) {
+    const int64_t row0 = (tok_base + first) * a.H + h;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(static_cast<const uint16_t*>(a.beta) + row0, (len - first) * a.H * 2);
+    return __builtin_amdgcn_raw_buffer_load_b16(rb, voffb, 0, 0);
 }
 
 // Value tile of one chunk for a state wave: row li, columns 4lg..4lg+3 of
@@ -215,9 +219,9 @@ __device__ __forceinline__ u32x2 load_v(const ChunkArgs& a, int64_t tok_base, in
 // fragments kk = 2H, 2H+1, tiles t = 4H..4H+3
 // ---------------------------------------------------------------------------
 template <int H>
-__device__ __forceinline__ void prepare_half(const PrepRegs& R, char* slot, char* fs, char* xp, int* flag, int epoch,
-                                             char* junk, int li, int lg, const bf16x8 (&eyeN)[2],
-                                             const bf16x8 (&eyeP)[2], const bf16x4& lowT) {
+__device__ __forceinline__ void prepare_half(const PrepRegs& R, char* slot, char* xp, int* flag, int epoch, char* junk,
+                                             int li, int lg,
+                                             const bf16x8 (&eyeN)[2], const bf16x8 (&eyeP)[2], const bf16x4& lowT) {
     const int lane = li + 16 * lg;
     bf16x8 KA[2], QA[2], KB[2];
 #pragma unroll
@@ -265,12 +269,9 @@ __device__ __forceinline__ void prepare_half(const PrepRegs& R, char* slot, char
         Mr = mfma32(KB[m], KA[m], Mr);    // (Kg Kb^T)[li][4lg+j] over these channels
         Pr = mfma32(KB[m], QA[m], Pr);    // (Qh Kb^T)[li][4lg+j]
     }
-    if constexpr (H == 1) {
-        // hand the share to the lower half: data first, then the flag (release)
-        *reinterpret_cast<f32x4*>(xp + 32 * lane) = Mr;
-        *reinterpret_cast<f32x4*>(xp + 32 * lane + 16) = Pr;
-        __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
+    *reinterpret_cast<f32x4*>(xp + 32 * lane) = Mr;
+    *reinterpret_cast<f32x4*>(xp + 32 * lane + 16) = Pr;
+    __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 
     // (e^{Gamma_C - Gamma} K)^T per state tile: transpose Kb on the matrix
     // cores, then scale channel 16t+li by e^{Gamma_C}
@@ -284,41 +285,39 @@ __device__ __forceinline__ void prepare_half(const PrepRegs& R, char* slot, char
             *reinterpret_cast<bf16x4*>(slot + S_KH + 8 * (64 * t + lane)) = pack4v(kbT * egc);
         }
     }
+}
 
-    if constexpr (H == 0) {
-        // the upper half's share (bounded wait: the upper half stores it every
-        // step before it waits for anything, so the flag always arrives)
-        for (int spin = 0; spin < (1 << 22); ++spin) {
-            if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == epoch) break;
-            __builtin_amdgcn_s_sleep(1);
-        }
-        Mr += *reinterpret_cast<const f32x4*>(xp + 32 * lane);
-        Pr += *reinterpret_cast<const f32x4*>(xp + 32 * lane + 16);
-
-        const float beta_li = bf16_bits_to_f32(R.beta);
-        f32x4 bj;   // beta of rows 4lg+j
+// T Diag(beta) and -P of one chunk from the two halves' shares of M and P
+// (wave-local; lane = (li, lg)); fs is this wave's 1 KiB scratch.
+__device__ __forceinline__ void finish_chunk(const char* xp, uint32_t beta_bits, char* slot, char* fs, int li, int lg) {
+    const int lane = li + 16 * lg;
+    const f32x4 Mr = *reinterpret_cast<const f32x4*>(xp + 32 * lane) +
+                     *reinterpret_cast<const f32x4*>(xp + 2048 + 32 * lane);
+    const f32x4 Pr = *reinterpret_cast<const f32x4*>(xp + 32 * lane + 16) +
+                     *reinterpret_cast<const f32x4*>(xp + 2048 + 32 * lane + 16);
+    const float beta_li = bf16_bits_to_f32(beta_bits);
+    f32x4 bj;   // beta of rows 4lg+j
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bj[j] = __shfl(beta_li, 4 * lg + j);
-        f32x4 Nr, Pn, Tr;
+    for (int j = 0; j < 4; ++j) bj[j] = __shfl(beta_li, 4 * lg + j);
+    f32x4 Nr, Pn, Tr;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = 4 * lg + j;
-            Nr[j] = (col < li) ? beta_li * Mr[j] : 0.f;
-            Pn[j] = (col <= li) ? -Pr[j] : 0.f;
-            Tr[j] = (col == li) ? 1.f : 0.f;
-        }
-        // T = (I + N)^{-1}: each lane needs its whole row of N
-        *reinterpret_cast<f32x4*>(fs + 4 * (16 * li + 4 * lg)) = Nr;
-        float nrow[16];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(fs + 4 * (16 * li + 4 * p));
-            nrow[4 * p] = x[0]; nrow[4 * p + 1] = x[1]; nrow[4 * p + 2] = x[2]; nrow[4 * p + 3] = x[3];
-        }
-        fsub<0>(Tr, nrow);
-        *reinterpret_cast<bf16x4*>(slot + S_TT + 8 * lane) = pack4v(Tr * bj);
-        *reinterpret_cast<bf16x4*>(slot + S_PN + 8 * lane) = pack4v(Pn);
+    for (int j = 0; j < 4; ++j) {
+        const int col = 4 * lg + j;
+        Nr[j] = (col < li) ? beta_li * Mr[j] : 0.f;
+        Pn[j] = (col <= li) ? -Pr[j] : 0.f;
+        Tr[j] = (col == li) ? 1.f : 0.f;
     }
+    // T = (I + N)^{-1}: each lane needs its whole row of N
+    *reinterpret_cast<f32x4*>(fs + 4 * (16 * li + 4 * lg)) = Nr;
+    float nrow[16];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(fs + 4 * (16 * li + 4 * p));
+        nrow[4 * p] = x[0]; nrow[4 * p + 1] = x[1]; nrow[4 * p + 2] = x[2]; nrow[4 * p + 3] = x[3];
+    }
+    fsub<0>(Tr, nrow);
+    *reinterpret_cast<bf16x4*>(slot + S_TT + 8 * lane) = pack4v(Tr * bj);
+    *reinterpret_cast<bf16x4*>(slot + S_PN + 8 * lane) = pack4v(Pn);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
@@ -368,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
     const int ngroups = (nchunks + kNA - 1) / kNA;
     const int64_t state_base = ((int64_t)n * a.H + h) * kDK * kDV;
     // hand-over flags start below every step count (LDS holds stale data)
-    if (tid < kNA) reinterpret_cast<int*>(smem + S_FLAG)[4 * tid] = 0;
+    if (tid < kNP) reinterpret_cast<int*>(smem + S_FLAG)[tid] = 0;
     __syncthreads();
 
     if (w >= kNB) {
@@ -387,12 +386,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) lowT[s] = (__bf16)((4 * lg + s <= li) ? 1.f : 0.f);
         const int voff = li * a.H * (kDK * 2) + 128 * ph + 16 * lg;
-        const int voffb = li * a.H * 2;
-        char* const fs = smem + S_FS + 1024 * pa;
-        char* const xp = smem + S_XP + 2048 * pa;
-        int* const flag = reinterpret_cast<int*>(smem + S_FLAG) + 4 * pa;
         char* const junk = smem + S_JUNK + 1024 * (w - kNB) + 16 * lane;
-        const bool lower = ph == 0;
+        int* const flag = reinterpret_cast<int*>(smem + S_FLAG) + 2 * pa + ph;
         // Two register sets alternate (the loop is unrolled by two), so a
         // prefetch is never copied (a copy would wait for it to land). Every
         // step issues its prefetch unconditionally: past the sequence end the
@@ -401,15 +396,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         // loads in flight, which keeps the compiler's waits exact.
         PrepRegs R0, R1;
         auto step = [&](int it, const PrepRegs& cur, PrepRegs& nxt) {
-            load_prep(nxt, a, tok_base, ((int64_t)(it + 1) * kNA + pa) * kC, len, h, voff, voffb, lower);
+            load_prep(nxt, a, tok_base, ((int64_t)(it + 1) * kNA + pa) * kC, len, h, voff);
             char* const slot = smem + ((it & 1) * kNA + pa) * SLOT;
-            if (lower)
-                prepare_half<0>(cur, slot, fs, xp, flag, it + 1, junk, li, lg, eyeN, eyeP, lowT);
+            char* const xp = smem + S_XP + (((it & 1) * kNA + pa) * 2 + ph) * 2048;
+            if (ph == 0)
+                prepare_half<0>(cur, slot, xp, flag, it + 1, junk, li, lg, eyeN, eyeP, lowT);
             else
-                prepare_half<1>(cur, slot, fs, xp, flag, it + 1, junk, li, lg, eyeN, eyeP, lowT);
+                prepare_half<1>(cur, slot, xp, flag, it + 1, junk, li, lg, eyeN, eyeP, lowT);
             group_barrier();
         };
-        load_prep(R0, a, tok_base, (int64_t)pa * kC, len, h, voff, voffb, lower);
+        load_prep(R0, a, tok_base, (int64_t)pa * kC, len, h, voff);
         int it = 0;
         for (; it + 1 < ngroups; it += 2) {
             step(it, R0, R1);
@@ -419,6 +415,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         group_barrier();   // the state waves' last group
     } else {
         // ========================== state wave ===============================
+        // The state chain is the serial critical path: its waves issue first,
+        // and the preparation waves fill the issue slots it leaves idle.
+        __builtin_amdgcn_s_setprio(2);
         const int cw = 16 * w;                       // this wave's columns within the half
         const int col0 = vt * kBV + cw;              // ... within d_v
         f32x4 S[8];                                  // tile rt: [channel 16rt+4lg+j][column col0+li]
@@ -436,19 +435,45 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         uint16_t* const out = static_cast<uint16_t*>(a.o);
         const float neg_scale = -a.scale;
 
-        // Value tiles of the next group: two register sets alternate and the
-        // loads are unconditional, as in the preparation waves.
-        u32x2 VA[kNA], VB[kNA];
-        auto load_group = [&](int gi, u32x2 (&vt_)[kNA]) {
+        // Value tiles of group gi and beta of this wave's chunk of group gi+1
+        // (used one iteration later, like the tiles): two register sets
+        // alternate and the loads are unconditional, as in the preparation
+        // waves.
+        const int voffb = li * a.H * 2;
+        char* const fs = smem + S_FS + 1024 * w;
+        int* const flags = reinterpret_cast<int*>(smem + S_FLAG);
+        // (one vector value per set: an array here would be left in private
+        // memory, and every prefetch would then wait to be stored there)
+        struct StateIn { u32x8 v; uint32_t beta; };   // tile s in v[2s], v[2s+1]
+        StateIn VA, VB;
+        auto load_group = [&](int gi, StateIn& in) {
+            in.beta = load_beta(a, tok_base, ((int64_t)(gi + 1) * kNA + w) * kC, len, h, voffb);
 #pragma unroll
-            for (int s = 0; s < kNA; ++s)
-                vt_[s] = load_v(a, tok_base, ((int64_t)gi * kNA + s) * kC, len, h, col0, voffv);
+            for (int s = 0; s < kNA; ++s) {
+                const u32x2 t = load_v(a, tok_base, ((int64_t)gi * kNA + s) * kC, len, h, col0, voffv);
+                in.v[2 * s] = t[0];
+                in.v[2 * s + 1] = t[1];
+            }
         };
         // Chunks of group gi from its LDS buffer. Unconditional: a chunk past
         // the sequence end holds zero tokens, which leave the state unchanged,
         // and its output stores fall outside the store buffer's range, so the
         // hardware drops them.
-        auto consume = [&](int gi, const u32x2 (&vcur)[kNA]) {
+        // T Diag(beta) and -P of chunk w of group gi, once both preparation
+        // halves have stored their shares (bounded wait: they store them every
+        // step before the barrier, so they always arrive)
+        auto finish = [&](int gi, uint32_t beta_bits) {
+            for (int spin = 0; spin < (1 << 22); ++spin) {
+                if (__hip_atomic_load(flags + 2 * w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == gi + 1 &&
+                    __hip_atomic_load(flags + 2 * w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == gi + 1)
+                    break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            finish_chunk(smem + S_XP + ((gi & 1) * kNA + w) * 4096, beta_bits,
+                         smem + ((gi & 1) * kNA + w) * SLOT, fs, li, lg);
+        };
+        auto consume = [&](int gi, const StateIn& vcur) {
 #pragma unroll
             for (int s = 0; s < kNA; ++s) {
                 const int c = gi * kNA + s;
@@ -460,7 +485,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) sbn[kk] = pack_pair_neg(S[2 * kk], S[2 * kk + 1]);
                 // X = V - Kg S  (rows 4lg+j, column li)
-                const bf16x8 vop = widen(__builtin_bit_cast(bf16x4, vcur[s]));
+                const bf16x8 vop = widen(__builtin_bit_cast(bf16x4, u32x2{vcur.v[2 * s], vcur.v[2 * s + 1]}));
                 f32x4 X = mfma32(vop, eyeV, zero4());
                 // OT = -(Qh S)^T  (column 4lg+j of row li)
                 f32x4 OT = zero4();
@@ -487,21 +512,27 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
                 update_state<0>(S, e2, slot + S_KH + 8 * lane, ub);
             }
         };
-        // iteration it loads group it and consumes group it-1
+        // iteration it loads group it, consumes group it-1 and finishes chunk w
+        // of group it
+        const uint32_t beta0 = load_beta(a, tok_base, (int64_t)w * kC, len, h, voffb);
         load_group(0, VA);
+        if (ngroups > 0) finish(0, beta0);
         group_barrier();
         int it = 1;
         for (; it + 1 <= ngroups; it += 2) {
             load_group(it, VB);
             consume(it - 1, VA);
+            if (it < ngroups) finish(it, VA.beta);
             group_barrier();
             load_group(it + 1, VA);
             consume(it, VB);
+            if (it + 1 < ngroups) finish(it + 1, VB.beta);
             group_barrier();
         }
         if (it <= ngroups) {
             load_group(it, VB);
             consume(it - 1, VA);
+            if (it < ngroups) finish(it, VA.beta);
             group_barrier();
         }
         if (a.sT) {
