@@ -163,28 +163,44 @@ __device__ __forceinline__ int remap_block(int b, int units) {
     return (grp * 8 + (rem & 7)) * kNVT + (rem >> 3);
 }
 
-// Buffer resource over [base, base + nbytes): accesses outside it read 0 and
+// Buffer descriptors: accesses outside [base, base + num_records) read 0 and
 // writes outside it are dropped by the hardware. Rows past a sequence's end
 // therefore read as zero tokens (an exact identity step of the recurrence)
 // and their outputs are never written, with no branch.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t nbytes) {
-    const int32_t n = nbytes <= 0 ? 0 : (nbytes > 0x7fffffff ? 0x7fffffff : (int32_t)nbytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+//
+// A per-(sequence, head) tensor stream walked one group of 64 rows at a time:
+// p is the byte address of the current group's first row (this head's slice),
+// rem the bytes from there to the sequence end. The descriptor of a group is
+// rebuilt from these with a constant stride; rows within the group are
+// addressed through the per-lane offset.
+struct Stream {
+    const char* p;
+    int64_t rem;
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const Stream& st) {
+    // clamp rem to [0, 2^31 - 1] with 32-bit scalar operations
+    const int32_t hi = (int32_t)(st.rem >> 32);
+    const uint32_t lo = (uint32_t)st.rem;
+    const int32_t n = hi < 0 ? 0 : ((hi > 0 || lo > 0x7fffffffu) ? 0x7fffffff : (int32_t)lo);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(st.p), 0, n, 0x00020000);
+}
+__device__ __forceinline__ void stream_advance(Stream& st, int64_t bytes) {
+    st.p += bytes;
+    st.rem -= bytes;
 }
 
 struct PrepRegs {
     uint4 q[2], k[2], g[2];   // row li, channels 32(2h+m)+8lg..+7, m = 0, 1
 };
 
-// Loads of channel half h of one 16-row chunk (sequence rows first..first+15)
-// for a preparation wave. voff = li*H*256 + 128*h + 16*lg bytes.
-__device__ __forceinline__ void load_prep(PrepRegs& R, const ChunkArgs& a, int64_t tok_base, int64_t first,
-                                          int64_t len, int h, int voff) {
-    const int64_t row0 = (tok_base + first) * a.H + h;
-    const int64_t span = (len - first) * a.H * (int64_t)(kDK * 2);    // bytes to the sequence end
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(a.q) + row0 * kDK, span);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(a.k) + row0 * kDK, span);
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(static_cast<const uint16_t*>(a.g) + row0 * kDK, span);
+// Loads of channel half h of one 16-row chunk for a preparation wave from the
+// q, k, g streams positioned at the chunk's group. voff = (16*a + li)*H*256 +
+// 128*h + 16*lg bytes for chunk a of the group.
+__device__ __forceinline__ void load_prep(PrepRegs& R, const Stream& sq, const Stream& sk, const Stream& sg,
+                                          int voff) {
+    const __amdgpu_buffer_rsrc_t rq = stream_rsrc(sq);
+    const __amdgpu_buffer_rsrc_t rk = stream_rsrc(sk);
+    const __amdgpu_buffer_rsrc_t rg = stream_rsrc(sg);
     // issue order = consumption order; memory operations complete in order
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -194,24 +210,6 @@ __device__ __forceinline__ void load_prep(PrepRegs& R, const ChunkArgs& a, int64
         R.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff + 64 * m, 0, 0));
         R.q[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + 64 * m, 0, 0));
     }
-}
-
-// beta of row li of one chunk for a state wave (raw bf16 bits). voffb = li*H*2.
-__device__ __forceinline__ uint32_t load_beta(const ChunkArgs& a, int64_t tok_base, int64_t first, int64_t len,
-                                              int h, int voffb) {
-    const int64_t row0 = (tok_base + first) * a.H + h;
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(static_cast<const uint16_t*>(a.beta) + row0, (len - first) * a.H * 2);
-    return __builtin_amdgcn_raw_buffer_load_b16(rb, voffb, 0, 0);
-}
-
-// Value tile of one chunk for a state wave: row li, columns 4lg..4lg+3 of
-// the wave's 16 (8 bytes).
-__device__ __forceinline__ u32x2 load_v(const ChunkArgs& a, int64_t tok_base, int64_t first, int64_t len,
-                                        int h, int col0, int voffv) {
-    const int64_t row0 = (tok_base + first) * a.H + h;
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(a.v) + row0 * kDV + col0,
-                                                (len - first) * a.H * (int64_t)(kDV * 2) - col0 * 2);
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voffv, 0, 0));
 }
 
 // ---------------------------------------------------------------------------
@@ -385,7 +383,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
             }
 #pragma unroll
         for (int s = 0; s < 4; ++s) lowT[s] = (__bf16)((4 * lg + s <= li) ? 1.f : 0.f);
-        const int voff = li * a.H * (kDK * 2) + 128 * ph + 16 * lg;
+        const int64_t row_bytes = (int64_t)a.H * (kDK * 2);          // one token of q, k or g
+        const int64_t gstride = (int64_t)kNA * kC * row_bytes;        // one group
+        const int64_t head0 = (tok_base * a.H + h) * (int64_t)(kDK * 2);
+        Stream sq{static_cast<const char*>(a.q) + head0, len * row_bytes};
+        Stream sk{static_cast<const char*>(a.k) + head0, len * row_bytes};
+        Stream sg{static_cast<const char*>(a.g) + head0, len * row_bytes};
+        const int voff = (kC * pa + li) * (int)row_bytes + 128 * ph + 16 * lg;
         char* const junk = smem + S_JUNK + 1024 * (w - kNB) + 16 * lane;
         int* const flag = reinterpret_cast<int*>(smem + S_FLAG) + 2 * pa + ph;
         // Two register sets alternate (the loop is unrolled by two), so a
@@ -396,7 +400,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         // loads in flight, which keeps the compiler's waits exact.
         PrepRegs R0, R1;
         auto step = [&](int it, const PrepRegs& cur, PrepRegs& nxt) {
-            load_prep(nxt, a, tok_base, ((int64_t)(it + 1) * kNA + pa) * kC, len, h, voff);
+            load_prep(nxt, sq, sk, sg, voff);            // the streams stand at group it+1
+            stream_advance(sq, gstride);
+            stream_advance(sk, gstride);
+            stream_advance(sg, gstride);
             char* const slot = smem + ((it & 1) * kNA + pa) * SLOT;
             char* const xp = smem + S_XP + (((it & 1) * kNA + pa) * 2 + ph) * 2048;
             if (ph == 0)
@@ -405,7 +412,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
                 prepare_half<1>(cur, slot, xp, flag, it + 1, junk, li, lg, eyeN, eyeP, lowT);
             group_barrier();
         };
-        load_prep(R0, a, tok_base, (int64_t)pa * kC, len, h, voff);
+        load_prep(R0, sq, sk, sg, voff);
+        stream_advance(sq, gstride);
+        stream_advance(sk, gstride);
+        stream_advance(sg, gstride);
         int it = 0;
         for (; it + 1 < ngroups; it += 2) {
             step(it, R0, R1);
@@ -430,30 +440,40 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         bf16x8 eyeV;   // [slot 8lg+s][column li] = (s < 4 && 4lg+s == li)
 #pragma unroll
         for (int s = 0; s < 8; ++s) eyeV[s] = (__bf16)((s < 4 && 4 * lg + s == li) ? 1.f : 0.f);
-        const int voffv = li * a.H * (kDV * 2) + 8 * lg;
-        const int voffo = li * a.H * (kDV * 2) + 8 * lg;
-        uint16_t* const out = static_cast<uint16_t*>(a.o);
         const float neg_scale = -a.scale;
 
         // Value tiles of group gi and beta of this wave's chunk of group gi+1
         // (used one iteration later, like the tiles): two register sets
         // alternate and the loads are unconditional, as in the preparation
         // waves.
-        const int voffb = li * a.H * 2;
+        const int64_t vrow_bytes = (int64_t)a.H * (kDV * 2);          // one token of v or o
+        const int64_t head0 = (tok_base * a.H + h) * (int64_t)(kDV * 2) + col0 * 2;
+        Stream sv{static_cast<const char*>(a.v) + head0, len * vrow_bytes - col0 * 2};
+        Stream so{static_cast<const char*>(a.o) + head0, len * vrow_bytes - col0 * 2};
+        Stream sb{static_cast<const char*>(a.beta) + (tok_base * a.H + h) * 2, len * a.H * 2};
+        const int64_t vstride = (int64_t)kNA * kC * vrow_bytes, bstride = (int64_t)kNA * kC * a.H * 2;
+        int vofs[kNA];                                 // row li of chunk s, columns 4lg..4lg+3
+#pragma unroll
+        for (int s = 0; s < kNA; ++s) vofs[s] = (kC * s + li) * (int)vrow_bytes + 8 * lg;
+        const int voffb = (kC * w + li) * a.H * 2;     // beta of row li of this wave's chunk
         char* const fs = smem + S_FS + 1024 * w;
         int* const flags = reinterpret_cast<int*>(smem + S_FLAG);
         // (one vector value per set: an array here would be left in private
         // memory, and every prefetch would then wait to be stored there)
         struct StateIn { u32x8 v; uint32_t beta; };   // tile s in v[2s], v[2s+1]
         StateIn VA, VB;
-        auto load_group = [&](int gi, StateIn& in) {
-            in.beta = load_beta(a, tok_base, ((int64_t)(gi + 1) * kNA + w) * kC, len, h, voffb);
+        // sv stands at group gi, sb at group gi+1 when group gi is loaded
+        auto load_group = [&](StateIn& in) {
+            in.beta = __builtin_amdgcn_raw_buffer_load_b16(stream_rsrc(sb), voffb, 0, 0);
+            const __amdgpu_buffer_rsrc_t rv = stream_rsrc(sv);
 #pragma unroll
             for (int s = 0; s < kNA; ++s) {
-                const u32x2 t = load_v(a, tok_base, ((int64_t)gi * kNA + s) * kC, len, h, col0, voffv);
+                const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, vofs[s], 0, 0));
                 in.v[2 * s] = t[0];
                 in.v[2 * s + 1] = t[1];
             }
+            stream_advance(sv, vstride);
+            stream_advance(sb, bstride);
         };
         // Chunks of group gi from its LDS buffer. Unconditional: a chunk past
         // the sequence end holds zero tokens, which leave the state unchanged,
@@ -473,14 +493,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
             finish_chunk(smem + S_XP + ((gi & 1) * kNA + w) * 4096, beta_bits,
                          smem + ((gi & 1) * kNA + w) * SLOT, fs, li, lg);
         };
+        // so stands at group gi when group gi is consumed
         auto consume = [&](int gi, const StateIn& vcur) {
+            const __amdgpu_buffer_rsrc_t ro = stream_rsrc(so);
+            stream_advance(so, vstride);
 #pragma unroll
             for (int s = 0; s < kNA; ++s) {
-                const int c = gi * kNA + s;
                 const char* const slot = smem + ((gi & 1) * kNA + s) * SLOT;
-                const __amdgpu_buffer_rsrc_t ro =
-                    make_rsrc(out + ((tok_base + (int64_t)c * kC) * a.H + h) * kDV + col0,
-                              (len - (int64_t)c * kC) * a.H * (kDV * 2) - col0 * 2);
                 bf16x8 sbn[4];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) sbn[kk] = pack_pair_neg(S[2 * kk], S[2 * kk + 1]);
@@ -504,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
                 __builtin_amdgcn_raw_buffer_store_b64(
                     u32x2{pack2_bf16(neg_scale * OT[0], neg_scale * OT[1]),
                           pack2_bf16(neg_scale * OT[2], neg_scale * OT[3])},
-                    ro, voffo, 0, 0);
+                    ro, vofs[s], 0, 0);
                 // S <- Diag(e^{Gamma_C}) S + Kh^T U. Lane li of row group lg
                 // reads entries 2li, 2li+1 of the group's 32 decay factors;
                 // tile rt row 4lg+j needs entry 4rt+j, which DPP broadcasts.
@@ -514,23 +533,24 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         };
         // iteration it loads group it, consumes group it-1 and finishes chunk w
         // of group it
-        const uint32_t beta0 = load_beta(a, tok_base, (int64_t)w * kC, len, h, voffb);
-        load_group(0, VA);
+        const uint32_t beta0 = __builtin_amdgcn_raw_buffer_load_b16(stream_rsrc(sb), voffb, 0, 0);
+        stream_advance(sb, bstride);
+        load_group(VA);
         if (ngroups > 0) finish(0, beta0);
         group_barrier();
         int it = 1;
         for (; it + 1 <= ngroups; it += 2) {
-            load_group(it, VB);
+            load_group(VB);
             consume(it - 1, VA);
             if (it < ngroups) finish(it, VA.beta);
             group_barrier();
-            load_group(it + 1, VA);
+            load_group(VA);
             consume(it, VB);
             if (it + 1 < ngroups) finish(it + 1, VB.beta);
             group_barrier();
         }
         if (it <= ngroups) {
-            load_group(it, VB);
+            load_group(VB);
             consume(it - 1, VA);
             if (it < ngroups) finish(it, VA.beta);
             group_barrier();
