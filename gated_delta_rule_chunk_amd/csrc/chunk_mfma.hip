@@ -89,9 +89,11 @@ __device__ __forceinline__ bf16x8 pack_pair_neg(const f32x4& lo, const f32x4& hi
                       (__bf16)(-hi[0]), (__bf16)(-hi[1]), (__bf16)(-hi[2]), (__bf16)(-hi[3])};
     return r;
 }
+// (two paired conversions; a four-element construction compiles to four
+// single conversions and two permutes)
 __device__ __forceinline__ bf16x4 pack4v(const f32x4& x) {
-    const bf16x4 r = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-    return r;
+    typedef uint32_t u32x2_ __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(bf16x4, u32x2_{pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3])});
 }
 // a 16x16x16 operand widened to a 16x16x32 one: slots 0..3 carry it, 4..7 are zero
 __device__ __forceinline__ bf16x8 widen(const bf16x4& x) {
@@ -138,17 +140,15 @@ __device__ __forceinline__ void fsub(f32x4& t, const float* nrow) {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// S[rt] <- Diag(e) S[rt] + Kh^T U for tiles RT..7. e2 holds decay entries
-// 2li, 2li+1 of this lane's row group; row 4lg+j of tile RT needs entry
-// 4RT+j, held by lane 2RT + j/2 of the same 16-lane row.
+// D[rt] = Diag(e) S[rt] for tiles RT..7. e2 holds decay entries 2li, 2li+1
+// of this lane's row group; row 4lg+j of tile RT needs entry 4RT+j, held by
+// lane 2RT + j/2 of the same 16-lane row.
 template <int RT>
-__device__ __forceinline__ void update_state(f32x4 (&S)[8], const f32x2& e2, const char* kh_base, const bf16x4& ub) {
+__device__ __forceinline__ void decay_state(f32x4 (&D)[8], const f32x4 (&S)[8], const f32x2& e2) {
     if constexpr (RT < 8) {
-        const f32x4 d = {S[RT][0] * row_bcast<2 * RT>(e2[0]), S[RT][1] * row_bcast<2 * RT>(e2[1]),
-                         S[RT][2] * row_bcast<2 * RT + 1>(e2[0]), S[RT][3] * row_bcast<2 * RT + 1>(e2[1])};
-        const bf16x4 kh = *reinterpret_cast<const bf16x4*>(kh_base + 512 * RT);
-        S[RT] = mfma16(kh, ub, d);
-        update_state<RT + 1>(S, e2, kh_base, ub);
+        D[RT] = f32x4{S[RT][0] * row_bcast<2 * RT>(e2[0]), S[RT][1] * row_bcast<2 * RT>(e2[1]),
+                      S[RT][2] * row_bcast<2 * RT + 1>(e2[0]), S[RT][3] * row_bcast<2 * RT + 1>(e2[1])};
+        decay_state<RT + 1>(D, S, e2);
     }
 }
 
@@ -372,6 +372,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         // ======================= preparation wave ============================
         const int pa = (w - kNB) & (kNA - 1);        // chunk within the group
         const int ph = (w - kNB) / kNA;              // channel half (wave-uniform)
+        // the upper half's share of M and P is the last input of the state
+        // waves' T: it issues ahead of the lower half
+        if (ph == 1) __builtin_amdgcn_s_setprio(1);
         bf16x8 eyeN[2], eyeP[2];   // identity blocks for the natural / packed slot orders
         bf16x4 lowT;               // (L^T)[4lg+s][li] = (4lg+s <= li)
 #pragma unroll
@@ -503,6 +506,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
                 bf16x8 sbn[4];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) sbn[kk] = pack_pair_neg(S[2 * kk], S[2 * kk + 1]);
+                // decayed state for the update at the end of the chunk. Lane li of
+                // row group lg reads entries 2li, 2li+1 of the group's 32 decay
+                // factors; DPP broadcasts the one each row needs.
+                const f32x2 e2 = *reinterpret_cast<const f32x2*>(slot + S_EG + 4 * (EG_STRIDE * lg + 2 * li));
+                f32x4 D[8];
+                decay_state<0>(D, S, e2);
                 // X = V - Kg S  (rows 4lg+j, column li)
                 const bf16x8 vop = widen(__builtin_bit_cast(bf16x4, u32x2{vcur.v[2 * s], vcur.v[2 * s + 1]}));
                 f32x4 X = mfma32(vop, eyeV, zero4());
@@ -524,11 +533,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
                     u32x2{pack2_bf16(neg_scale * OT[0], neg_scale * OT[1]),
                           pack2_bf16(neg_scale * OT[2], neg_scale * OT[3])},
                     ro, vofs[s], 0, 0);
-                // S <- Diag(e^{Gamma_C}) S + Kh^T U. Lane li of row group lg
-                // reads entries 2li, 2li+1 of the group's 32 decay factors;
-                // tile rt row 4lg+j needs entry 4rt+j, which DPP broadcasts.
-                const f32x2 e2 = *reinterpret_cast<const f32x2*>(slot + S_EG + 4 * (EG_STRIDE * lg + 2 * li));
-                update_state<0>(S, e2, slot + S_KH + 8 * lane, ub);
+                // S <- Diag(e^{Gamma_C}) S + Kh^T U (the decayed state D was
+                // formed at the top of the chunk, off the critical path)
+#pragma unroll
+                for (int rt = 0; rt < 8; ++rt) {
+                    const bf16x4 kh = *reinterpret_cast<const bf16x4*>(slot + S_KH + 8 * (64 * rt + lane));
+                    S[rt] = mfma16(kh, ub, D[rt]);
+                }
             }
         };
         // iteration it loads group it, consumes group it-1 and finishes chunk w
