@@ -73,20 +73,32 @@ def read_traffic():
 
 
 def time_launches(fn, steps, warmup, stream):
+    """W warm-up calls, then exactly `steps` timed calls back to back, bracketed
+    by device synchronisation; HIP events on the launch stream give the
+    average launch duration. A second, untimed pass with one pair of events
+    per launch gives the per-launch spread (those events add their own
+    overhead to each launch)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    first.record(stream)
+    for i in range(steps):
+        fn(i)
+    last.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_ms = first.elapsed_time(last) / steps
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
         fn(i)
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]      # ms
-    return wall, per
+    return wall, per, avg_ms
 
 
 def bench_forward(steps, warmup):
@@ -105,10 +117,10 @@ def bench_forward(steps, warmup):
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk_size=0, out=o,
                       final_state=fin)
 
-    wall, per = time_launches(step, steps, warmup, stream)
+    wall, per, batch = time_launches(step, steps, warmup, stream)
     if not (torch.isfinite(o.float()).all() and torch.isfinite(fin).all()):
         raise RuntimeError("non-finite forward output")
-    return w, wall, per
+    return w, wall, per, batch
 
 
 def bench_decode(steps, warmup):
@@ -125,11 +137,11 @@ def bench_decode(steps, warmup):
         d = ins[i % 4]
         kda.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], cache, out=o)
 
-    wall, per = time_launches(step, steps, warmup, stream)
+    wall, per, batch = time_launches(step, steps, warmup, stream)
     if not torch.isfinite(cache).all():
         raise RuntimeError("non-finite decode state")
     step_bytes = 2 * Nb * H * Dk * Dv * 4 + Nb * H * (2 * (3 * Dk + Dv) + 2 + 2 * Dv)
-    avg_ms = float(np.mean(per))
+    avg_ms = float(batch)
     gbs = step_bytes / (avg_ms * 1e-3) / 1e9
     return {"workload": f"{cfg['name']}: batch {Nb}, H={H}, d_k=d_v={Dk}, bf16 q/k/v/g/beta, fp32 state cache",
             "ms_per_step": avg_ms, "tokens_per_s": Nb / (avg_ms * 1e-3),
@@ -194,10 +206,10 @@ def main():
         copy_calibration()
         return
 
-    w, wall, per = bench_forward(args.steps, args.warmup)
+    w, wall, per, batch = bench_forward(args.steps, args.warmup)
     ms_per_step = wall / args.steps * 1e3
-    kern_ms = float(np.mean(per))            # average launch time (the profiler's "average")
-    kern_ms_median = float(np.median(per))
+    kern_ms = float(batch)                   # average launch time over the back-to-back timed region
+    kern_ms_median = float(np.median(per))   # untimed per-launch pass (events add their own overhead)
     nbytes = fwd_bytes(w.T, w.H, w.Dk, w.Dv, n_states_out=1)
     nflops = fwd_flops(w.T, w.H, w.Dk, w.Dv)
     gbs = nbytes / (kern_ms * 1e-3) / 1e9
