@@ -8,7 +8,10 @@ workload is specified with 64-row chunks; the bf16 kernel always works in
 16-row chunks (the chunk size changes only the rounding, never the result of
 the recurrence), so the call passes chunk_size=0 (the kernel's own). Inputs are seeded synthetic tensors (synth.WORKLOADS["k3_t4096"]),
 resident in HBM before timing; two input sets alternate so the 256 MB
-Infinity Cache cannot serve a step from the previous one.
+Infinity Cache cannot serve a step from the previous one. Before the W
+warm-up steps the call runs back to back for a fixed 0.25 s (untimed) so that
+the GPU reaches its loaded clocks; an idle MI355X needs about a hundred
+launches for that, and the first launches run up to 20% slower.
 
 Prints one JSON line. ``value`` is tokens/s of the forward (T / seconds per
 step). ``roofline`` is for the chunk kernel: algorithmic HBM bytes per launch
@@ -72,12 +75,30 @@ def read_traffic():
     return float(m_val.group(1))
 
 
+SETTLE_S = 0.25
+
+
+def settle_clocks(fn, seconds=SETTLE_S):
+    """Run the call back to back for `seconds` of wall time, untimed. An idle
+    MI355X runs at low clocks and needs about a hundred back-to-back launches
+    of this kernel (~25 ms) to reach its loaded clocks; launches timed before
+    that measure the ramp, not the kernel."""
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
 def time_launches(fn, steps, warmup, stream):
-    """W warm-up calls, then exactly `steps` timed calls back to back, bracketed
-    by device synchronisation; HIP events on the launch stream give the
-    average launch duration. A second, untimed pass with one pair of events
-    per launch gives the per-launch spread (those events add their own
-    overhead to each launch)."""
+    """Clock settling (settle_clocks), W warm-up calls, then exactly `steps`
+    timed calls back to back, bracketed by device synchronisation; HIP events
+    on the launch stream give the average launch duration. A second, untimed
+    pass with one pair of events per launch gives the per-launch spread (those
+    events add their own overhead to each launch)."""
+    settle_clocks(fn)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -222,6 +243,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle_s": SETTLE_S,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -5,29 +5,45 @@
 // log-decay per channel; with g >= -5, |Gamma| <= 80 < ln(FLT_MAX), so one
 // reference point per chunk suffices):
 //   Kg = e^{Gamma} * K,  Qh = e^{Gamma} * Q,  Kb = e^{-Gamma} * K,
-//   Kh = e^{Gamma_C - Gamma} * K
+//   Kh = e^{Gamma_C - Gamma} * K,  d = e^{Gamma_C}
 //   M = strictly-lower(Diag(beta) Kg Kb^T),  P = lower(Qh Kb^T)
 //   T = (I + M)^{-1}        (forward substitution, fp32)
 //   U = T Diag(beta) (V - Kg S)
 //   O = scale (Qh S + P U)
-//   S <- Diag(e^{Gamma_C}) S + Kh^T U
+//   S <- Diag(d) S + Kh^T U
 // This is the WY/UT-transform chunk form of the gated delta rule with a
 // per-channel decay.
 //
+// The state advances two chunks (1, 2) at a time. Chunk 2 enters with
+// Diag(d1) S + Kh1^T U1, so with Kg2' = Kg2 Diag(d1), Qh2' = Qh2 Diag(d1),
+// A = Kg2 Kh1^T and B = Qh2 Kh1^T (16 x 16, over the channels):
+//   U1 = T1 Diag(beta1) (V1 - Kg1 S)
+//   U2 = T2 Diag(beta2) (V2 - Kg2' S - A U1)
+//   O1 = scale (Qh1 S + P1 U1)
+//   O2 = scale (Qh2' S + B U1 + P2 U2)
+//   S <- Diag(d1 d2) S + [Kh1 Diag(d2) ; Kh2]^T [U1 ; U2]
+// Every factor is a product of in-chunk decays (exponents in [-160, 0]), so
+// nothing overflows, and a pair costs one packing and one decay of the state
+// and one 32-deep update instead of two of each.
+//
 // Structure. A workgroup owns one (sequence, head, 64-column half of d_v) and
-// runs two kinds of wave side by side, three per SIMD:
-//   8 preparation waves, two per chunk of a group of 4: the wave for channel
-//     half h of chunk a builds, for channels 64h..64h+63, everything that
-//     does not depend on the state (Kg, Qh and Kh^T fragments, e^{Gamma_C},
-//     its share of M and P) and stores it to chunk a's slot of an LDS double
-//     buffer;
+// walks the sequence in groups of four chunks (two pairs), with three waves
+// per SIMD:
+//   4 chunk-1 preparation waves, one per (pair p, channel half h): Gamma and
+//     e^{+-Gamma} of chunk 1 for channels 64h..64h+63, d1 published first,
+//     then Kg1 and Qh1 to the pair's slot and the Kb1, Kh1 operands handed
+//     to the chunk-2 wave of the same (p, h), and this half's share of M1,
+//     P1. Half 0 forms T1 Diag(beta1) and -P1; half 1 forms T2 Diag(beta2),
+//     -P2, -A and -B from the chunk-2 waves' shares.
+//   4 chunk-2 preparation waves, one per (p, h): Kg2', Qh2', d2, the update
+//     operand of both chunks, and this half's shares of M2, P2, A and B.
 //   4 state waves: wave b carries the fp32 state columns 16b..16b+15 of the
-//     half (128 x 16, in registers) through the chunks of the previous group.
-//     After that, wave b waits for the two shares of M and P of chunk b of
-//     the group being prepared, and forms its T Diag(beta) and -P.
-// One barrier per group hands a filled buffer to the state waves and a free
-// one to the preparation waves, so preparation of group i+1 overlaps the
-// state chain of group i.
+//     half (128 x 16, in registers) through the pairs of the previous group.
+// One barrier per group hands a filled LDS buffer to the state waves and a
+// free one to the preparation waves, so preparation of group i+1 overlaps the
+// state chain of group i. Within a step the preparation waves pass work to
+// each other through LDS flags with bounded waits; every wave stores its own
+// flags before it waits on another's, so no wait can cycle.
 //
 // Lane layouts. For a 16x16xK matrix-core product an "operand" fragment puts
 // the row (A) or column (B) on lane%16 and the contraction slots on lane/16;
@@ -42,7 +58,10 @@
 // (li, lg) holds token li and channels 16t + 4lg + j. A 16x16x32 operand
 // fragment kk packs tiles 2kk and 2kk+1, so its slot s of lane group lg is
 // channel 32kk + 16(s/4) + 4lg + s%4. State tile rt row r is channel 16rt + r,
-// so the packed state uses the same slot order.
+// so the packed state uses the same slot order. The 32-deep contractions over
+// the rows of a pair (the update and O2's second term) take slot s < 4 of
+// lane group lg as row 4lg+s of chunk 1 and slot s >= 4 as row 4lg+s-4 of
+// chunk 2.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -53,27 +72,48 @@ constexpr int kC = 16;          // rows per chunk
 constexpr int kDK = 128;
 constexpr int kDV = 128;
 constexpr int kNA = 4;          // chunks per group
-constexpr int kNP = 2 * kNA;    // preparation waves: two channel halves per chunk
+constexpr int kNR = kNA / 2;    // pairs per group
+constexpr int kNP = 4 * kNR;    // preparation waves: (chunk of the pair, channel half) per pair
 constexpr int kNB = 4;          // state waves, 16 value columns each
 constexpr int kBV = 16 * kNB;   // value columns per workgroup
 constexpr int kNVT = kDV / kBV;
 constexpr int kThreads = 64 * (kNP + kNB);
 
-// One chunk's slot (bytes). Fragments are stored in lane order, so every
+// One pair's slot (bytes). Fragments are stored in lane order, so every
 // access is 64 consecutive 8- or 16-byte pieces.
-constexpr int S_KG = 0;         // [4 kk][64 lanes] bf16x8  (e^G K) operand fragments
-constexpr int S_QH = 4096;      // [4 kk][64 lanes] bf16x8  (e^G Q)
-constexpr int S_KH = 8192;      // [8 rt][64 lanes] bf16x4  (e^{Gc-G} K)^T, A operand of the state update
-constexpr int S_TT = 12288;     // [64 lanes] bf16x4        T Diag(beta), row li, columns 4lg+j
-constexpr int S_PN = 12800;     // [64 lanes] bf16x4        -P, row li, columns 4lg+j
-constexpr int S_EG = 13312;     // [4 lg][36] f32: entry 4t+j is e^{Gamma_C} of channel 16t+4lg+j
-constexpr int EG_STRIDE = 36;   //   (32 used; the pad keeps the lane groups in different banks)
-constexpr int SLOT = S_EG + 4 * 4 * EG_STRIDE;
-constexpr int S_XP = 2 * kNA * SLOT;            // [buffer][chunk][half]: share of M, P (32 B per lane)
-constexpr int S_FS = S_XP + 2 * kNA * 2 * 2048; // per state wave: [16][16] f32 (row-wise N)
-constexpr int S_JUNK = S_FS + kNB * 1024;       // per preparation wave: 1 KiB sink for masked-off stores
-constexpr int S_FLAG = S_JUNK + kNP * 1024;     // per (chunk, half): int, group + 1 once its share is stored
-constexpr int LDS_BYTES = S_FLAG + 4 * kNP;
+constexpr int S_KG1 = 0;        // [4 kk][64 lanes] bf16x8  Kg1
+constexpr int S_QH1 = 4096;     // [4 kk][64 lanes] bf16x8  Qh1
+constexpr int S_KG2 = 8192;     // [4 kk][64 lanes] bf16x8  Kg2 Diag(d1)
+constexpr int S_QH2 = 12288;    // [4 kk][64 lanes] bf16x8  Qh2 Diag(d1)
+constexpr int S_KH = 16384;     // [8 rt][64 lanes] bf16x8  update operand, row = channel 16rt+li:
+                                //   slots 0..3 (Kh1 Diag(d2))^T, slots 4..7 Kh2^T
+constexpr int S_TT1 = 24576;    // [64 lanes] bf16x4  T1 Diag(beta1), row li, columns 4lg+j
+constexpr int S_TT2 = 25088;    // [64 lanes] bf16x4  T2 Diag(beta2)
+constexpr int S_PN1 = 25600;    // [64 lanes] bf16x4  -P1, row li, columns 4lg+j
+constexpr int S_AN = 26112;     // [64 lanes] bf16x4  -A, row li (chunk 2), columns 4lg+j (chunk 1)
+constexpr int S_BP = 26624;     // [64 lanes] bf16x8  row li of chunk 2: -B (slots 0..3), -P2 (slots 4..7)
+constexpr int EG_STRIDE = 36;   // [4 lg][36] f32 decay tables: entry 4t+j is channel 16t+4lg+j
+                                //   (32 used; the pad keeps the lane groups in different banks)
+constexpr int S_D1 = 27648;     // d1
+constexpr int S_E2 = S_D1 + 4 * 4 * EG_STRIDE;   // d2
+constexpr int S_SJ = S_E2 + 4 * 4 * EG_STRIDE;   // sink for the decay stores of tokens 0..14 (never read)
+constexpr int SLOT = S_SJ + 64 * 16 + 8 * 16;
+// shares of the pair's 16x16 products, [pair][10][64 lanes] f32x4: M1 and P1 of
+// channel half 1; M2, P2, A and B of each channel half (entry + half)
+constexpr int SH_M1 = 0, SH_P1 = 1, SH_M2 = 2, SH_P2 = 4, SH_A = 6, SH_B = 8;
+constexpr int SH_BYTES = 10 * 1024;
+constexpr int S_SH = 2 * kNR * SLOT;
+// hand-over from the chunk-1 wave to the chunk-2 wave of one (pair, half):
+// Kb1 and Kh1 operand fragments [2 m][64 lanes] bf16x8
+constexpr int HO_KB1 = 0, HO_KH1 = 2048;
+constexpr int HO_BYTES = 4096;
+constexpr int S_HO = S_SH + kNR * SH_BYTES;
+constexpr int S_FS = S_HO + 2 * kNR * HO_BYTES; // per finishing wave: [16][16] f32 (row-wise N)
+// ints: d1 stored [4 (pair, half)], hand-over stored [4], chunk-1 shares of half 1 [2 pair],
+// M2/P2 shares [4 (pair, half)], A/B shares [4 (pair, half)]
+constexpr int S_FLAG = S_FS + 2 * kNR * 1024;
+constexpr int F_D1 = 0, F_HO = 4, F_SH1 = 8, F_SH2 = 10, F_SHAB = 14, N_FLAGS = 18;
+constexpr int LDS_BYTES = S_FLAG + 4 * N_FLAGS;
 static_assert(LDS_BYTES <= 163840, "LDS budget");
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -189,22 +229,39 @@ __device__ __forceinline__ void stream_advance(Stream& st, int64_t bytes) {
     st.rem -= bytes;
 }
 
-struct PrepRegs {
-    uint4 q[2], k[2], g[2];   // row li, channels 32(2h+m)+8lg..+7, m = 0, 1
+// Global loads and stores use a row-major lane order, lane = 4*row + piece:
+// four consecutive lanes cover 64 (loads of q, k, g) or 32 (v, o) contiguous
+// bytes of one row, which the load unit merges into one access. The matrix
+// cores take lane = row + 16*piece. A cross-lane gather per 32-bit word moves
+// data between the two; gather address (bytes) = 4 * source lane.
+__device__ __forceinline__ uint32_t gather(uint32_t x, int addr) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)x);
+}
+__device__ __forceinline__ bf16x8 gather8(const uint4& v, int addr) {
+    const uint4 r = {gather(v.x, addr), gather(v.y, addr), gather(v.z, addr), gather(v.w, addr)};
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+struct ChunkRegs {
+    uint4 q[2], k[2], g[2];   // row lane/4, channels 32(2h+m)+8(lane%4)..+7, m = 0, 1
+    // beta of row li, kept as the 16 bits the load returns: a widening here
+    // would sit at the loop head and wait for the prefetch just issued
+    uint16_t beta;
 };
 
 // Loads of channel half h of one 16-row chunk for a preparation wave from the
-// q, k, g streams positioned at the chunk's group. voff = (16*a + li)*H*256 +
-// 128*h + 16*lg bytes for chunk a of the group.
-__device__ __forceinline__ void load_prep(PrepRegs& R, const Stream& sq, const Stream& sk, const Stream& sg,
-                                          int voff) {
-    const __amdgpu_buffer_rsrc_t rq = stream_rsrc(sq);
-    const __amdgpu_buffer_rsrc_t rk = stream_rsrc(sk);
+// streams positioned at the chunk's group. voff = (16*a + lane/4)*H*256 +
+// 128*h + 16*(lane%4) bytes for chunk a of the group. (Issue order =
+// consumption order; memory operations complete in order.)
+__device__ __forceinline__ void load_g(ChunkRegs& R, const Stream& sg, int voff) {
     const __amdgpu_buffer_rsrc_t rg = stream_rsrc(sg);
-    // issue order = consumption order; memory operations complete in order
 #pragma unroll
     for (int m = 0; m < 2; ++m)
         R.g[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, voff + 64 * m, 0, 0));
+}
+__device__ __forceinline__ void load_kq(ChunkRegs& R, const Stream& sq, const Stream& sk, int voff) {
+    const __amdgpu_buffer_rsrc_t rq = stream_rsrc(sq);
+    const __amdgpu_buffer_rsrc_t rk = stream_rsrc(sk);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
         R.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff + 64 * m, 0, 0));
@@ -212,97 +269,51 @@ __device__ __forceinline__ void load_prep(PrepRegs& R, const Stream& sq, const S
     }
 }
 
-// ---------------------------------------------------------------------------
-// preparation of channel half H of one chunk (wave-local; lane = (li, lg));
-// fragments kk = 2H, 2H+1, tiles t = 4H..4H+3
-// ---------------------------------------------------------------------------
-template <int H>
-__device__ __forceinline__ void prepare_half(const PrepRegs& R, char* slot, char* xp, int* flag, int epoch, char* junk,
-                                             int li, int lg,
-                                             const bf16x8 (&eyeN)[2], const bf16x8 (&eyeP)[2], const bf16x4& lowT) {
-    const int lane = li + 16 * lg;
-    bf16x8 KA[2], QA[2], KB[2];
+// Gamma = cumulative log-decay of tiles 2m, 2m+1 of one chunk's channel half
+// and el = e^Gamma, enl = e^-Gamma (lane (li, lg): token li, channels
+// 16t + 4lg + j; index 2m + hf).
+__device__ __forceinline__ void decay_tiles(const ChunkRegs& R, int m, int gaddr, const bf16x8 (&eyeN)[2],
+                                            const bf16x4& lowT, f32x4 (&el)[4], f32x4 (&enl)[4]) {
+    const bf16x8 gop = gather8(R.g[m], gaddr);   // operand order: row li, channels 32kk+8lg+s
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const int kk = 2 * H + m;
-        const bf16x8 gop = __builtin_bit_cast(bf16x8, R.g[m]);
-        const bf16x8 kop = __builtin_bit_cast(bf16x8, R.k[m]);
-        const bf16x8 qop = __builtin_bit_cast(bf16x8, R.q[m]);
-        f32x4 ka[2], qa[2], kb[2];
+    for (int hf = 0; hf < 2; ++hf) {
+        // g^T tile (channel 16t+li, tokens 4lg+j), then Gamma = L * g on the
+        // matrix cores: lane gets Gamma[token li][channel 16t+4lg+j]
+        const f32x4 gT = mfma32(gop, eyeN[hf], zero4());
+        const f32x4 gam = mfma16(pack4v(gT), lowT, zero4());
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int t = 2 * kk + hf;
-            // g^T tile (channel 16t+li, tokens 4lg+j), then Gamma = L * g on
-            // the matrix cores: lane gets Gamma[token li][channel 16t+4lg+j]
-            const f32x4 gT = mfma32(gop, eyeN[hf], zero4());
-            const f32x4 gam = mfma16(pack4v(gT), lowT, zero4());
-            // k, q of the same (token, channel) as fp32, by identity products
-            const f32x4 kf = mfma32(eyeN[hf], kop, zero4());
-            const f32x4 qf = mfma32(eyeN[hf], qop, zero4());
-            f32x4 el;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float x = gam[j] * kLog2e;
-                el[j] = __builtin_amdgcn_exp2f(x);
-                const float enl = __builtin_amdgcn_exp2f(-x);
-                ka[hf][j] = kf[j] * el[j];
-                qa[hf][j] = qf[j] * el[j];
-                kb[hf][j] = kf[j] * enl;
-            }
-            // token 15 carries e^{Gamma_C}; the other lanes store to the sink
-            // (a store under an exec mask would split the schedule)
-            *reinterpret_cast<f32x4*>(li == 15 ? slot + S_EG + 4 * (EG_STRIDE * lg + 4 * t) : junk) = el;
-        }
-        KA[m] = pack_pair(ka[0], ka[1]);
-        QA[m] = pack_pair(qa[0], qa[1]);
-        KB[m] = pack_pair(kb[0], kb[1]);
-        *reinterpret_cast<bf16x8*>(slot + S_KG + 16 * (64 * kk + lane)) = KA[m];
-        *reinterpret_cast<bf16x8*>(slot + S_QH + 16 * (64 * kk + lane)) = QA[m];
-    }
-
-    // this half's share of M and P, row li, columns 4lg+j
-    f32x4 Mr = zero4(), Pr = zero4();
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        Mr = mfma32(KB[m], KA[m], Mr);    // (Kg Kb^T)[li][4lg+j] over these channels
-        Pr = mfma32(KB[m], QA[m], Pr);    // (Qh Kb^T)[li][4lg+j]
-    }
-    *reinterpret_cast<f32x4*>(xp + 32 * lane) = Mr;
-    *reinterpret_cast<f32x4*>(xp + 32 * lane + 16) = Pr;
-    __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-
-    // (e^{Gamma_C - Gamma} K)^T per state tile: transpose Kb on the matrix
-    // cores, then scale channel 16t+li by e^{Gamma_C}
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int t = 4 * H + 2 * m + hf;
-            const f32x4 kbT = mfma32(KB[m], eyeP[hf], zero4());   // Kb[token 4lg+j][channel 16t+li]
-            const float egc = *reinterpret_cast<const float*>(slot + S_EG + 4 * (EG_STRIDE * (li >> 2) + 4 * t + (li & 3)));
-            *reinterpret_cast<bf16x4*>(slot + S_KH + 8 * (64 * t + lane)) = pack4v(kbT * egc);
+        for (int j = 0; j < 4; ++j) {
+            const float x = gam[j] * kLog2e;
+            el[2 * m + hf][j] = __builtin_amdgcn_exp2f(x);
+            enl[2 * m + hf][j] = __builtin_amdgcn_exp2f(-x);
         }
     }
 }
 
-// T Diag(beta) and -P of one chunk from the two halves' shares of M and P
-// (wave-local; lane = (li, lg)); fs is this wave's 1 KiB scratch.
-__device__ __forceinline__ void finish_chunk(const char* xp, uint32_t beta_bits, char* slot, char* fs, int li, int lg) {
-    const int lane = li + 16 * lg;
-    const f32x4 Mr = *reinterpret_cast<const f32x4*>(xp + 32 * lane) +
-                     *reinterpret_cast<const f32x4*>(xp + 2048 + 32 * lane);
-    const f32x4 Pr = *reinterpret_cast<const f32x4*>(xp + 32 * lane + 16) +
-                     *reinterpret_cast<const f32x4*>(xp + 2048 + 32 * lane + 16);
-    const float beta_li = bf16_bits_to_f32(beta_bits);
+// k, q of tiles 2m, 2m+1 (same lane layout) as fp32, by identity products
+__device__ __forceinline__ void kq_tiles(const ChunkRegs& R, int m, int gaddr, const bf16x8 (&eyeN)[2],
+                                         f32x4 (&kf)[2], f32x4 (&qf)[2]) {
+    const bf16x8 kop = gather8(R.k[m], gaddr);
+    const bf16x8 qop = gather8(R.q[m], gaddr);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        kf[hf] = mfma32(eyeN[hf], kop, zero4());
+        qf[hf] = mfma32(eyeN[hf], qop, zero4());
+    }
+}
+
+// T Diag(beta) of one chunk from the summed M (row li, columns 4lg+j);
+// beta_bits holds beta of row lane/4; fs is the wave's 1 KiB scratch.
+__device__ __forceinline__ bf16x4 inverse_times_beta(const f32x4& Mr, uint32_t beta_bits, char* fs, int li, int lg) {
+    const float beta_li = bf16_bits_to_f32(gather(beta_bits, 16 * li));
     f32x4 bj;   // beta of rows 4lg+j
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bj[j] = __shfl(beta_li, 4 * lg + j);
-    f32x4 Nr, Pn, Tr;
+    for (int j = 0; j < 4; ++j) bj[j] = bf16_bits_to_f32(gather(beta_bits, 16 * (4 * lg + j)));
+    f32x4 Nr, Tr;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int col = 4 * lg + j;
         Nr[j] = (col < li) ? beta_li * Mr[j] : 0.f;
-        Pn[j] = (col <= li) ? -Pr[j] : 0.f;
         Tr[j] = (col == li) ? 1.f : 0.f;
     }
     // T = (I + N)^{-1}: each lane needs its whole row of N
@@ -314,9 +325,212 @@ __device__ __forceinline__ void finish_chunk(const char* xp, uint32_t beta_bits,
         nrow[4 * p] = x[0]; nrow[4 * p + 1] = x[1]; nrow[4 * p + 2] = x[2]; nrow[4 * p + 3] = x[3];
     }
     fsub<0>(Tr, nrow);
-    *reinterpret_cast<bf16x4*>(slot + S_TT + 8 * lane) = pack4v(Tr * bj);
-    *reinterpret_cast<bf16x4*>(slot + S_PN + 8 * lane) = pack4v(Pn);
+    return pack4v(Tr * bj);
 }
+
+// -X restricted to the lower triangle (diagonal included), row li, columns 4lg+j
+__device__ __forceinline__ f32x4 neg_lower(const f32x4& X, int li, int lg) {
+    f32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = (4 * lg + j <= li) ? -X[j] : 0.f;
+    return r;
+}
+
+__device__ __forceinline__ f32x4 lds4(const char* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+__device__ __forceinline__ bf16x8 concat(const bf16x4& lo, const bf16x4& hi) {
+    const bf16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return r;
+}
+
+// bounded wait for a hand-over flag: its producer stores it every step
+// before the group barrier, so it always arrives
+__device__ __forceinline__ void wait_flag(const int* flag, int epoch) {
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == epoch) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+__device__ __forceinline__ void set_flag(int* flag, int epoch) {
+    __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+struct PrepCtx {
+    char* slot;        // the pair's slot of the current buffer
+    char* ho;          // hand-over area of this (pair, half)
+    char* sh;          // the pair's share area
+    int* f_d1;         // d1 of this (pair, half) stored
+    int* f_ho;         // hand-over of this (pair, half) stored
+    int* flags;        // the hand-over flags (F_*)
+    int eoff;          // decay-table store offset: the table row for token 15, the slot's sink otherwise
+    char* fs;
+    int epoch, pq, ph, li, lg;
+    int gaddr;         // gather address from the load order: 4 * (lg + 4 li)
+};
+
+// ---------------------------------------------------------------------------
+// Chunk-1 wave of channel half ph of a pair (wave-local; lane = (li, lg));
+// fragments kk = 2ph, 2ph+1, tiles t = 4ph..4ph+3. Publishes d1 first (the
+// chunk-2 wave scales with it), then Kg1, Qh1 to the slot and Kb1, Kh1 to the
+// hand-over. Half 0 sums both halves' M1 and P1 and forms T1 Diag(beta1)
+// and -P1; half 1 stores its share of them, then forms the chunk-2 factors
+// (T2 Diag(beta2), -P2, -A, -B) from the chunk-2 waves' shares.
+// ---------------------------------------------------------------------------
+template <typename Issue>
+__device__ __forceinline__ void prepare_chunk1(const ChunkRegs& R, const PrepCtx& c, const bf16x8 (&eyeN)[2],
+                                               const bf16x4& lowT, Issue&& issue) {
+    const int lane = c.li + 16 * c.lg;
+    issue(0);
+    f32x4 el[4], enl[4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) decay_tiles(R, m, c.gaddr, eyeN, lowT, el, enl);
+    // token 15 carries d1; the other lanes store to the sink (a store under
+    // an exec mask would split the schedule)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        *reinterpret_cast<f32x4*>(c.slot + S_D1 + c.eoff + 16 * (4 * c.ph + u)) = el[u];
+    set_flag(c.f_d1, c.epoch);
+    issue(1);
+    f32x4 Ms = zero4(), Ps = zero4();
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int kk = 2 * c.ph + m;
+        f32x4 kf[2], qf[2], ka[2], qa[2], kb[2], kh[2];
+        kq_tiles(R, m, c.gaddr, eyeN, kf, qf);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int u = 2 * m + hf;
+            f32x4 d1;   // e^Gamma of token 15, from lane 15 of the row
+#pragma unroll
+            for (int j = 0; j < 4; ++j) d1[j] = row_bcast<15>(el[u][j]);
+            ka[hf] = kf[hf] * el[u];
+            qa[hf] = qf[hf] * el[u];
+            kb[hf] = kf[hf] * enl[u];
+            kh[hf] = kb[hf] * d1;
+        }
+        const bf16x8 KA = pack_pair(ka[0], ka[1]);
+        const bf16x8 QA = pack_pair(qa[0], qa[1]);
+        const bf16x8 KB = pack_pair(kb[0], kb[1]);
+        *reinterpret_cast<bf16x8*>(c.slot + S_KG1 + 16 * (64 * kk + lane)) = KA;
+        *reinterpret_cast<bf16x8*>(c.slot + S_QH1 + 16 * (64 * kk + lane)) = QA;
+        *reinterpret_cast<bf16x8*>(c.ho + HO_KB1 + 16 * (64 * m + lane)) = KB;
+        *reinterpret_cast<bf16x8*>(c.ho + HO_KH1 + 16 * (64 * m + lane)) = pack_pair(kh[0], kh[1]);
+        Ms = mfma32(KB, KA, Ms);    // (Kg1 Kb1^T)[li][4lg+j] over these channels
+        Ps = mfma32(KB, QA, Ps);    // (Qh1 Kb1^T)[li][4lg+j]
+    }
+    set_flag(c.f_ho, c.epoch);
+    issue(2);
+    const int pp = c.pq >> 1;
+    if (c.ph == 0) {
+        // T1 Diag(beta1) and -P1 from both halves' shares
+        wait_flag(c.flags + F_SH1 + pp, c.epoch);
+        const f32x4 Mr = Ms + lds4(c.sh + SH_M1 * 1024 + 16 * lane);
+        const f32x4 Pr = Ps + lds4(c.sh + SH_P1 * 1024 + 16 * lane);
+        *reinterpret_cast<bf16x4*>(c.slot + S_TT1 + 8 * lane) = inverse_times_beta(Mr, R.beta, c.fs, c.li, c.lg);
+        *reinterpret_cast<bf16x4*>(c.slot + S_PN1 + 8 * lane) = pack4v(neg_lower(Pr, c.li, c.lg));
+    } else {
+        *reinterpret_cast<f32x4*>(c.sh + SH_M1 * 1024 + 16 * lane) = Ms;
+        *reinterpret_cast<f32x4*>(c.sh + SH_P1 * 1024 + 16 * lane) = Ps;
+        set_flag(c.flags + F_SH1 + pp, c.epoch);
+        // chunk 2 of the pair: T2 Diag(beta2) as soon as both chunk-2 waves
+        // have stored M2 and P2, then -P2, -A and -B (beta here is chunk 2's)
+        wait_flag(c.flags + F_SH2 + 2 * pp, c.epoch);
+        wait_flag(c.flags + F_SH2 + 2 * pp + 1, c.epoch);
+        const f32x4 M2 = lds4(c.sh + SH_M2 * 1024 + 16 * lane) + lds4(c.sh + (SH_M2 + 1) * 1024 + 16 * lane);
+        const f32x4 P2 = lds4(c.sh + SH_P2 * 1024 + 16 * lane) + lds4(c.sh + (SH_P2 + 1) * 1024 + 16 * lane);
+        *reinterpret_cast<bf16x4*>(c.slot + S_TT2 + 8 * lane) = inverse_times_beta(M2, R.beta, c.fs, c.li, c.lg);
+        wait_flag(c.flags + F_SHAB + 2 * pp, c.epoch);
+        wait_flag(c.flags + F_SHAB + 2 * pp + 1, c.epoch);
+        const f32x4 Ar = lds4(c.sh + SH_A * 1024 + 16 * lane) + lds4(c.sh + (SH_A + 1) * 1024 + 16 * lane);
+        const f32x4 Br = lds4(c.sh + SH_B * 1024 + 16 * lane) + lds4(c.sh + (SH_B + 1) * 1024 + 16 * lane);
+        *reinterpret_cast<bf16x4*>(c.slot + S_AN + 8 * lane) = pack4v(-Ar);
+        *reinterpret_cast<bf16x8*>(c.slot + S_BP + 16 * lane) = concat(pack4v(-Br), pack4v(neg_lower(P2, c.li, c.lg)));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk-2 wave of channel half ph of a pair: Kg2', Qh2', d2, the update
+// operand and this half's shares of M2, P2 (stored as soon as they are
+// formed) and of A, B.
+// ---------------------------------------------------------------------------
+template <typename Issue>
+__device__ __forceinline__ void prepare_chunk2(const ChunkRegs& R, const PrepCtx& c, const bf16x8 (&eyeN)[2],
+                                               const bf16x4& lowT, Issue&& issue) {
+    const int lane = c.li + 16 * c.lg;
+    f32x4 el[4], enl[4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) decay_tiles(R, m, c.gaddr, eyeN, lowT, el, enl);
+    issue(0);   // (after the step-start burst of the other waves' loads)
+    wait_flag(c.f_d1, c.epoch);
+    bf16x8 KA[2], QA[2], KB[2];
+    f32x4 Ms = zero4(), Ps = zero4();
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int kk = 2 * c.ph + m;
+        f32x4 kf[2], qf[2], ka[2], qa[2], kb[2], d1[2];
+        kq_tiles(R, m, c.gaddr, eyeN, kf, qf);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int u = 2 * m + hf;
+            const int t = 4 * c.ph + u;
+            d1[hf] = lds4(c.slot + S_D1 + 4 * (EG_STRIDE * c.lg + 4 * t));
+            *reinterpret_cast<f32x4*>(c.slot + S_E2 + c.eoff + 16 * t) = el[u];
+            ka[hf] = kf[hf] * el[u];
+            qa[hf] = qf[hf] * el[u];
+            kb[hf] = kf[hf] * enl[u];
+        }
+        KA[m] = pack_pair(ka[0], ka[1]);
+        QA[m] = pack_pair(qa[0], qa[1]);
+        KB[m] = pack_pair(kb[0], kb[1]);
+        *reinterpret_cast<bf16x8*>(c.slot + S_KG2 + 16 * (64 * kk + lane)) =
+            pack_pair(ka[0] * d1[0], ka[1] * d1[1]);
+        *reinterpret_cast<bf16x8*>(c.slot + S_QH2 + 16 * (64 * kk + lane)) =
+            pack_pair(qa[0] * d1[0], qa[1] * d1[1]);
+        Ms = mfma32(KB[m], KA[m], Ms);    // (Kg2 Kb2^T)[li][4lg+j]
+        Ps = mfma32(KB[m], QA[m], Ps);    // (Qh2 Kb2^T)[li][4lg+j]
+    }
+    *reinterpret_cast<f32x4*>(c.sh + (SH_M2 + c.ph) * 1024 + 16 * lane) = Ms;
+    *reinterpret_cast<f32x4*>(c.sh + (SH_P2 + c.ph) * 1024 + 16 * lane) = Ps;
+    set_flag(c.flags + F_SH2 + c.pq, c.epoch);
+    issue(1);
+    wait_flag(c.f_ho, c.epoch);
+    f32x4 As = zero4(), Bs = zero4();
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const bf16x8 KH1 = *reinterpret_cast<const bf16x8*>(c.ho + HO_KH1 + 16 * (64 * m + lane));
+        As = mfma32(KH1, KA[m], As);      // (Kg2 Kh1^T)[li][4lg+j]
+        Bs = mfma32(KH1, QA[m], Bs);      // (Qh2 Kh1^T)[li][4lg+j]
+    }
+    *reinterpret_cast<f32x4*>(c.sh + (SH_A + c.ph) * 1024 + 16 * lane) = As;
+    *reinterpret_cast<f32x4*>(c.sh + (SH_B + c.ph) * 1024 + 16 * lane) = Bs;
+    set_flag(c.flags + F_SHAB + c.pq, c.epoch);
+    // update operand per state tile: transpose Kb1, Kb2 on the matrix cores,
+    // then scale channel 16t+li by d1 d2 (chunk 1) and d2 (chunk 2)
+    bf16x8 eyeP[2];   // identity block for the packed slot order
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            eyeP[hf][s] = (__bf16)((s / 4 == hf && 4 * c.lg + (s & 3) == c.li) ? 1.f : 0.f);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const bf16x8 KB1 = *reinterpret_cast<const bf16x8*>(c.ho + HO_KB1 + 16 * (64 * m + lane));
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int t = 4 * c.ph + 2 * m + hf;
+            const f32x4 kbT1 = mfma32(KB1, eyeP[hf], zero4());     // Kb1[token 4lg+j][channel 16t+li]
+            const f32x4 kbT2 = mfma32(KB[m], eyeP[hf], zero4());
+            const int e = 4 * (EG_STRIDE * (c.li >> 2) + 4 * t + (c.li & 3));
+            const float f2 = *reinterpret_cast<const float*>(c.slot + S_E2 + e);
+            const float f12 = *reinterpret_cast<const float*>(c.slot + S_D1 + e) * f2;
+            *reinterpret_cast<bf16x8*>(c.slot + S_KH + 16 * (64 * t + lane)) =
+                concat(pack4v(kbT1 * f12), pack4v(kbT2 * f2));
+        }
+    }
+    issue(2);
+}
+
 
 __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
@@ -365,25 +579,22 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
     const int ngroups = (nchunks + kNA - 1) / kNA;
     const int64_t state_base = ((int64_t)n * a.H + h) * kDK * kDV;
     // hand-over flags start below every step count (LDS holds stale data)
-    if (tid < kNP) reinterpret_cast<int*>(smem + S_FLAG)[tid] = 0;
+    if (tid < N_FLAGS) reinterpret_cast<int*>(smem + S_FLAG)[tid] = 0;
     __syncthreads();
 
     if (w >= kNB) {
         // ======================= preparation wave ============================
-        const int pa = (w - kNB) & (kNA - 1);        // chunk within the group
-        const int ph = (w - kNB) / kNA;              // channel half (wave-uniform)
-        // the upper half's share of M and P is the last input of the state
-        // waves' T: it issues ahead of the lower half
-        if (ph == 1) __builtin_amdgcn_s_setprio(1);
-        bf16x8 eyeN[2], eyeP[2];   // identity blocks for the natural / packed slot orders
+        const int pw = w - kNB;
+        const int pc = pw >> 2;                      // chunk within the pair (wave-uniform)
+        const int pq = pw & 3;                       // (pair, half); waves pq, 4+pq share a SIMD
+        const int pp = pq >> 1;                      // pair within the group
+        const int ph = pq & 1;                       // channel half
+        bf16x8 eyeN[2];            // identity blocks for the natural slot order
         bf16x4 lowT;               // (L^T)[4lg+s][li] = (4lg+s <= li)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                eyeN[hf][s] = (__bf16)((8 * lg + s == 16 * hf + li) ? 1.f : 0.f);
-                eyeP[hf][s] = (__bf16)((s / 4 == hf && 4 * lg + (s & 3) == li) ? 1.f : 0.f);
-            }
+            for (int s = 0; s < 8; ++s) eyeN[hf][s] = (__bf16)((8 * lg + s == 16 * hf + li) ? 1.f : 0.f);
 #pragma unroll
         for (int s = 0; s < 4; ++s) lowT[s] = (__bf16)((4 * lg + s <= li) ? 1.f : 0.f);
         const int64_t row_bytes = (int64_t)a.H * (kDK * 2);          // one token of q, k or g
@@ -392,39 +603,79 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         Stream sq{static_cast<const char*>(a.q) + head0, len * row_bytes};
         Stream sk{static_cast<const char*>(a.k) + head0, len * row_bytes};
         Stream sg{static_cast<const char*>(a.g) + head0, len * row_bytes};
-        const int voff = (kC * pa + li) * (int)row_bytes + 128 * ph + 16 * lg;
-        char* const junk = smem + S_JUNK + 1024 * (w - kNB) + 16 * lane;
-        int* const flag = reinterpret_cast<int*>(smem + S_FLAG) + 2 * pa + ph;
-        // Two register sets alternate (the loop is unrolled by two), so a
-        // prefetch is never copied (a copy would wait for it to land). Every
-        // step issues its prefetch unconditionally: past the sequence end the
-        // buffer range is empty and the loads return zeros without touching
-        // memory, and every path through the loop then has the same number of
-        // loads in flight, which keeps the compiler's waits exact.
-        PrepRegs R0, R1;
-        auto step = [&](int it, const PrepRegs& cur, PrepRegs& nxt) {
-            load_prep(nxt, sq, sk, sg, voff);            // the streams stand at group it+1
-            stream_advance(sq, gstride);
-            stream_advance(sk, gstride);
-            stream_advance(sg, gstride);
-            char* const slot = smem + ((it & 1) * kNA + pa) * SLOT;
-            char* const xp = smem + S_XP + (((it & 1) * kNA + pa) * 2 + ph) * 2048;
-            if (ph == 0)
-                prepare_half<0>(cur, slot, xp, flag, it + 1, junk, li, lg, eyeN, eyeP, lowT);
-            else
-                prepare_half<1>(cur, slot, xp, flag, it + 1, junk, li, lg, eyeN, eyeP, lowT);
-            group_barrier();
+        Stream sb{static_cast<const char*>(a.beta) + (tok_base * a.H + h) * 2, len * a.H * 2};
+        const int64_t bstride = (int64_t)kNA * kC * a.H * 2;
+        // load order: row lane/4 of the chunk, 16-byte piece lane%4
+        const int row = kC * (2 * pp + pc) + (lane >> 2);
+        const int voff = row * (int)row_bytes + 128 * ph + 16 * (lane & 3);
+        // beta of the chunk whose factors this wave forms (chunk-1 waves: chunk
+        // 1 for half 0, chunk 2 for half 1; chunk-2 waves load it unused)
+        const int voffb = (kC * (2 * pp + ph) + (lane >> 2)) * a.H * 2;
+        int* const flags = reinterpret_cast<int*>(smem + S_FLAG);
+        PrepCtx ctx;
+        ctx.ho = smem + S_HO + HO_BYTES * pq;
+        ctx.sh = smem + S_SH + SH_BYTES * pp;
+        ctx.f_d1 = flags + F_D1 + pq;
+        ctx.f_ho = flags + F_HO + pq;
+        ctx.flags = flags;
+        // table row of token 15, or this lane's 16 bytes of the slot's sink
+        ctx.eoff = li == 15 ? 4 * EG_STRIDE * lg : (pc == 0 ? S_SJ - S_D1 : S_SJ - S_E2) + 16 * lane;
+        ctx.fs = smem + S_FS + 1024 * pq;
+        ctx.pq = pq;
+        ctx.ph = ph;
+        ctx.gaddr = 4 * (lg + 4 * li);
+        ctx.li = li;
+        ctx.lg = lg;
+        // The next group's loads go out in three parts between the phases of
+        // the current one: issued in one burst, they stall the wave at the
+        // load unit while the other waves issue theirs. Two register sets
+        // alternate (the loop is unrolled by two), so a prefetch is never
+        // copied (a copy would wait for it to land). Every step issues its
+        // prefetch unconditionally: past the sequence end the buffer range is
+        // empty and the loads return zeros without touching memory, and every
+        // path through the loop then has the same number of loads in flight,
+        // which keeps the compiler's waits exact.
+        auto load_part = [&](ChunkRegs& R, int part) {
+            if (part == 0) {
+                load_g(R, sg, voff);
+            } else if (part == 1) {
+                load_kq(R, sq, sk, voff);
+            } else {
+                R.beta = __builtin_amdgcn_raw_buffer_load_b16(stream_rsrc(sb), voffb, 0, 0);
+                stream_advance(sq, gstride);
+                stream_advance(sk, gstride);
+                stream_advance(sg, gstride);
+                stream_advance(sb, bstride);
+            }
         };
-        load_prep(R0, sq, sk, sg, voff);
-        stream_advance(sq, gstride);
-        stream_advance(sk, gstride);
-        stream_advance(sg, gstride);
-        int it = 0;
-        for (; it + 1 < ngroups; it += 2) {
-            step(it, R0, R1);
-            step(it + 1, R1, R0);
-        }
-        if (it < ngroups) step(it, R0, R1);
+        // one loop per role, so that each is register-allocated on its own
+        auto run = [&](auto&& prepare) {
+            ChunkRegs R0, R1;
+            auto step = [&](int it, const ChunkRegs& cur, ChunkRegs& nxt) {
+                // the streams stand at group it+1
+                auto issue = [&](int part) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_part(nxt, part);
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                ctx.slot = smem + ((it & 1) * kNR + pp) * SLOT;
+                ctx.epoch = it + 1;
+                prepare(cur, issue);
+                group_barrier();
+            };
+#pragma unroll
+            for (int part = 0; part < 3; ++part) load_part(R0, part);
+            int it = 0;
+            for (; it + 1 < ngroups; it += 2) {
+                step(it, R0, R1);
+                step(it + 1, R1, R0);
+            }
+            if (it < ngroups) step(it, R0, R1);
+        };
+        if (pc == 0)
+            run([&](const ChunkRegs& cur, auto&& issue) { prepare_chunk1(cur, ctx, eyeN, lowT, issue); });
+        else
+            run([&](const ChunkRegs& cur, auto&& issue) { prepare_chunk2(cur, ctx, eyeN, lowT, issue); });
         group_barrier();   // the state waves' last group
     } else {
         // ========================== state wave ===============================
@@ -445,125 +696,120 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         for (int s = 0; s < 8; ++s) eyeV[s] = (__bf16)((s < 4 && 4 * lg + s == li) ? 1.f : 0.f);
         const float neg_scale = -a.scale;
 
-        // Value tiles of group gi and beta of this wave's chunk of group gi+1
-        // (used one iteration later, like the tiles): two register sets
-        // alternate and the loads are unconditional, as in the preparation
-        // waves.
+        // Value tiles of group gi (used one iteration later): two register
+        // sets alternate and the loads are unconditional, as in the
+        // preparation waves.
         const int64_t vrow_bytes = (int64_t)a.H * (kDV * 2);          // one token of v or o
         const int64_t head0 = (tok_base * a.H + h) * (int64_t)(kDV * 2) + col0 * 2;
         Stream sv{static_cast<const char*>(a.v) + head0, len * vrow_bytes - col0 * 2};
         Stream so{static_cast<const char*>(a.o) + head0, len * vrow_bytes - col0 * 2};
-        Stream sb{static_cast<const char*>(a.beta) + (tok_base * a.H + h) * 2, len * a.H * 2};
-        const int64_t vstride = (int64_t)kNA * kC * vrow_bytes, bstride = (int64_t)kNA * kC * a.H * 2;
-        int vofs[kNA];                                 // row li of chunk s, columns 4lg..4lg+3
+        const int64_t vstride = (int64_t)kNA * kC * vrow_bytes;
+        // load/store order: row lane/4 of chunk s, columns 4(lane%4)..+3 of
+        // this wave's 16; gathers move to and from the operand order
+        int vofs[kNA];
 #pragma unroll
-        for (int s = 0; s < kNA; ++s) vofs[s] = (kC * s + li) * (int)vrow_bytes + 8 * lg;
-        const int voffb = (kC * w + li) * a.H * 2;     // beta of row li of this wave's chunk
-        char* const fs = smem + S_FS + 1024 * w;
-        int* const flags = reinterpret_cast<int*>(smem + S_FLAG);
+        for (int s = 0; s < kNA; ++s) vofs[s] = (kC * s + (lane >> 2)) * (int)vrow_bytes + 8 * (lane & 3);
+        const int gaddr = 4 * (lg + 4 * li);           // operand lane (li, lg) <- load lane 4li + lg
+        const int saddr = 4 * ((lane >> 2) + 16 * (lane & 3));   // store lane <- operand lane
         // (one vector value per set: an array here would be left in private
         // memory, and every prefetch would then wait to be stored there)
-        struct StateIn { u32x8 v; uint32_t beta; };   // tile s in v[2s], v[2s+1]
+        typedef u32x8 StateIn;                         // tile s in [2s], [2s+1]
         StateIn VA, VB;
-        // sv stands at group gi, sb at group gi+1 when group gi is loaded
         auto load_group = [&](StateIn& in) {
-            in.beta = __builtin_amdgcn_raw_buffer_load_b16(stream_rsrc(sb), voffb, 0, 0);
             const __amdgpu_buffer_rsrc_t rv = stream_rsrc(sv);
 #pragma unroll
             for (int s = 0; s < kNA; ++s) {
                 const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, vofs[s], 0, 0));
-                in.v[2 * s] = t[0];
-                in.v[2 * s + 1] = t[1];
+                in[2 * s] = t[0];
+                in[2 * s + 1] = t[1];
             }
             stream_advance(sv, vstride);
-            stream_advance(sb, bstride);
         };
-        // Chunks of group gi from its LDS buffer. Unconditional: a chunk past
+        // Pairs of group gi from its LDS buffer. Unconditional: a chunk past
         // the sequence end holds zero tokens, which leave the state unchanged,
         // and its output stores fall outside the store buffer's range, so the
-        // hardware drops them.
-        // T Diag(beta) and -P of chunk w of group gi, once both preparation
-        // halves have stored their shares (bounded wait: they store them every
-        // step before the barrier, so they always arrive)
-        auto finish = [&](int gi, uint32_t beta_bits) {
-            for (int spin = 0; spin < (1 << 22); ++spin) {
-                if (__hip_atomic_load(flags + 2 * w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == gi + 1 &&
-                    __hip_atomic_load(flags + 2 * w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == gi + 1)
-                    break;
-                __builtin_amdgcn_s_sleep(1);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            finish_chunk(smem + S_XP + ((gi & 1) * kNA + w) * 4096, beta_bits,
-                         smem + ((gi & 1) * kNA + w) * SLOT, fs, li, lg);
-        };
-        // so stands at group gi when group gi is consumed
+        // hardware drops them. so stands at group gi.
         auto consume = [&](int gi, const StateIn& vcur) {
             const __amdgpu_buffer_rsrc_t ro = stream_rsrc(so);
             stream_advance(so, vstride);
 #pragma unroll
-            for (int s = 0; s < kNA; ++s) {
-                const char* const slot = smem + ((gi & 1) * kNA + s) * SLOT;
+            for (int pr = 0; pr < kNR; ++pr) {
+                const char* const slot = smem + ((gi & 1) * kNR + pr) * SLOT;
                 bf16x8 sbn[4];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) sbn[kk] = pack_pair_neg(S[2 * kk], S[2 * kk + 1]);
-                // decayed state for the update at the end of the chunk. Lane li of
-                // row group lg reads entries 2li, 2li+1 of the group's 32 decay
-                // factors; DPP broadcasts the one each row needs.
-                const f32x2 e2 = *reinterpret_cast<const f32x2*>(slot + S_EG + 4 * (EG_STRIDE * lg + 2 * li));
+                // state decayed over the pair, for the update at its end. Lane
+                // li of row group lg reads entries 2li, 2li+1 of the 32 decay
+                // factors of its row group; DPP broadcasts the one each row needs.
+                const f32x2 e2 = *reinterpret_cast<const f32x2*>(slot + S_D1 + 4 * (EG_STRIDE * lg + 2 * li)) *
+                                 *reinterpret_cast<const f32x2*>(slot + S_E2 + 4 * (EG_STRIDE * lg + 2 * li));
                 f32x4 D[8];
                 decay_state<0>(D, S, e2);
-                // X = V - Kg S  (rows 4lg+j, column li)
-                const bf16x8 vop = widen(__builtin_bit_cast(bf16x4, u32x2{vcur.v[2 * s], vcur.v[2 * s + 1]}));
-                f32x4 X = mfma32(vop, eyeV, zero4());
-                // OT = -(Qh S)^T  (column 4lg+j of row li)
-                f32x4 OT = zero4();
+                // X = V - Kg S (rows 4lg+j, column li); OT = -(Qh S)^T (column
+                // 4lg+j of row li), for both chunks
+                const u32x2 v1 = {gather(vcur[4 * pr], gaddr), gather(vcur[4 * pr + 1], gaddr)};
+                const u32x2 v2 = {gather(vcur[4 * pr + 2], gaddr), gather(vcur[4 * pr + 3], gaddr)};
+                f32x4 X1 = mfma32(widen(__builtin_bit_cast(bf16x4, v1)), eyeV, zero4());
+                f32x4 X2 = mfma32(widen(__builtin_bit_cast(bf16x4, v2)), eyeV, zero4());
+                f32x4 OT1 = zero4(), OT2 = zero4();
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const bf16x8 kg = *reinterpret_cast<const bf16x8*>(slot + S_KG + 16 * (64 * kk + lane));
-                    const bf16x8 qh = *reinterpret_cast<const bf16x8*>(slot + S_QH + 16 * (64 * kk + lane));
-                    X = mfma32(kg, sbn[kk], X);
-                    OT = mfma32(sbn[kk], qh, OT);
+                    const bf16x8 kg1 = *reinterpret_cast<const bf16x8*>(slot + S_KG1 + 16 * (64 * kk + lane));
+                    X1 = mfma32(kg1, sbn[kk], X1);
                 }
-                const bf16x4 tt = *reinterpret_cast<const bf16x4*>(slot + S_TT + 8 * lane);
-                const f32x4 U = mfma16(tt, pack4v(X), zero4());      // U[4lg+j][li]
-                const bf16x4 ub = pack4v(U);
-                const bf16x4 pn = *reinterpret_cast<const bf16x4*>(slot + S_PN + 8 * lane);
-                OT = mfma32(widen(ub), widen(pn), OT);               // -(Qh S + P U)^T
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const bf16x8 kg2 = *reinterpret_cast<const bf16x8*>(slot + S_KG2 + 16 * (64 * kk + lane));
+                    const bf16x8 qh1 = *reinterpret_cast<const bf16x8*>(slot + S_QH1 + 16 * (64 * kk + lane));
+                    const bf16x8 qh2 = *reinterpret_cast<const bf16x8*>(slot + S_QH2 + 16 * (64 * kk + lane));
+                    X2 = mfma32(kg2, sbn[kk], X2);
+                    OT1 = mfma32(sbn[kk], qh1, OT1);
+                    OT2 = mfma32(sbn[kk], qh2, OT2);
+                }
+                // chunk 1
+                const bf16x4 tt1 = *reinterpret_cast<const bf16x4*>(slot + S_TT1 + 8 * lane);
+                const bf16x4 ub1 = pack4v(mfma16(tt1, pack4v(X1), zero4()));   // U1[4lg+j][li]
+                const bf16x4 pn1 = *reinterpret_cast<const bf16x4*>(slot + S_PN1 + 8 * lane);
+                OT1 = mfma32(widen(ub1), widen(pn1), OT1);                       // -(Qh1 S + P1 U1)^T
                 __builtin_amdgcn_raw_buffer_store_b64(
-                    u32x2{pack2_bf16(neg_scale * OT[0], neg_scale * OT[1]),
-                          pack2_bf16(neg_scale * OT[2], neg_scale * OT[3])},
-                    ro, vofs[s], 0, 0);
-                // S <- Diag(e^{Gamma_C}) S + Kh^T U (the decayed state D was
-                // formed at the top of the chunk, off the critical path)
+                    u32x2{gather(pack2_bf16(neg_scale * OT1[0], neg_scale * OT1[1]), saddr),
+                          gather(pack2_bf16(neg_scale * OT1[2], neg_scale * OT1[3]), saddr)},
+                    ro, vofs[2 * pr], 0, 0);
+                // chunk 2
+                const bf16x4 an = *reinterpret_cast<const bf16x4*>(slot + S_AN + 8 * lane);
+                X2 = mfma32(widen(an), widen(ub1), X2);                           // - A U1
+                const bf16x4 tt2 = *reinterpret_cast<const bf16x4*>(slot + S_TT2 + 8 * lane);
+                const bf16x4 ub2 = pack4v(mfma16(tt2, pack4v(X2), zero4()));   // U2[4lg+j][li]
+                const bf16x8 ucat = concat(ub1, ub2);
+                const bf16x8 bp = *reinterpret_cast<const bf16x8*>(slot + S_BP + 16 * lane);
+                OT2 = mfma32(ucat, bp, OT2);                                      // -(Qh2' S + B U1 + P2 U2)^T
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    u32x2{gather(pack2_bf16(neg_scale * OT2[0], neg_scale * OT2[1]), saddr),
+                          gather(pack2_bf16(neg_scale * OT2[2], neg_scale * OT2[3]), saddr)},
+                    ro, vofs[2 * pr + 1], 0, 0);
+                // S <- Diag(d1 d2) S + [Kh1 Diag(d2) ; Kh2]^T [U1 ; U2]
 #pragma unroll
                 for (int rt = 0; rt < 8; ++rt) {
-                    const bf16x4 kh = *reinterpret_cast<const bf16x4*>(slot + S_KH + 8 * (64 * rt + lane));
-                    S[rt] = mfma16(kh, ub, D[rt]);
+                    const bf16x8 kh = *reinterpret_cast<const bf16x8*>(slot + S_KH + 16 * (64 * rt + lane));
+                    S[rt] = mfma32(kh, ucat, D[rt]);
                 }
             }
         };
-        // iteration it loads group it, consumes group it-1 and finishes chunk w
-        // of group it
-        const uint32_t beta0 = __builtin_amdgcn_raw_buffer_load_b16(stream_rsrc(sb), voffb, 0, 0);
-        stream_advance(sb, bstride);
+        // iteration it loads group it and consumes group it-1
         load_group(VA);
-        if (ngroups > 0) finish(0, beta0);
         group_barrier();
         int it = 1;
         for (; it + 1 <= ngroups; it += 2) {
             load_group(VB);
             consume(it - 1, VA);
-            if (it < ngroups) finish(it, VA.beta);
             group_barrier();
             load_group(VA);
             consume(it, VB);
-            if (it + 1 < ngroups) finish(it + 1, VB.beta);
             group_barrier();
         }
         if (it <= ngroups) {
             load_group(VB);
             consume(it - 1, VA);
-            if (it < ngroups) finish(it, VA.beta);
             group_barrier();
         }
         if (a.sT) {
