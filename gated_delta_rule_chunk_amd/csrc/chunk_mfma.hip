@@ -108,10 +108,12 @@ constexpr int S_SH = 2 * kNR * SLOT;
 constexpr int HO_KB1 = 0, HO_KH1 = 2048;
 constexpr int HO_BYTES = 4096;
 constexpr int S_HO = S_SH + kNR * SH_BYTES;
-constexpr int S_FS = S_HO + 2 * kNR * HO_BYTES; // per finishing wave: [16][16] f32 (row-wise N)
+constexpr int FS_STRIDE = 20;                  // row stride (floats) of the substitution scratch: rows in different banks
+constexpr int FS_BYTES = 16 * FS_STRIDE * 4;
+constexpr int S_FS = S_HO + 2 * kNR * HO_BYTES; // per finishing wave: [16][FS_STRIDE] f32 (row-wise N)
 // ints: d1 stored [4 (pair, half)], hand-over stored [4], chunk-1 shares of half 1 [2 pair],
 // M2/P2 shares [4 (pair, half)], A/B shares [4 (pair, half)]
-constexpr int S_FLAG = S_FS + 2 * kNR * 1024;
+constexpr int S_FLAG = S_FS + 2 * kNR * FS_BYTES;
 constexpr int F_D1 = 0, F_HO = 4, F_SH1 = 8, F_SH2 = 10, F_SHAB = 14, N_FLAGS = 18;
 constexpr int LDS_BYTES = S_FLAG + 4 * N_FLAGS;
 static_assert(LDS_BYTES <= 163840, "LDS budget");
@@ -269,25 +271,23 @@ __device__ __forceinline__ void load_kq(ChunkRegs& R, const Stream& sq, const St
     }
 }
 
-// Gamma = cumulative log-decay of tiles 2m, 2m+1 of one chunk's channel half
-// and el = e^Gamma, enl = e^-Gamma (lane (li, lg): token li, channels
-// 16t + 4lg + j; index 2m + hf).
-__device__ __forceinline__ void decay_tiles(const ChunkRegs& R, int m, int gaddr, const bf16x8 (&eyeN)[2],
-                                            const bf16x4& lowT, f32x4 (&el)[4], f32x4 (&enl)[4]) {
+// Gamma = cumulative log-decay of tiles 2m, 2m+1 of one chunk's channel half,
+// scaled by log2(e) for the base-2 exponential (lane (li, lg): token li,
+// channels 16t + 4lg + j; index 2m + hf).
+__device__ __forceinline__ void gamma_tiles(const ChunkRegs& R, int m, int gaddr, const bf16x8 (&eyeN)[2],
+                                            const bf16x4& lowT, f32x4 (&x)[4]) {
     const bf16x8 gop = gather8(R.g[m], gaddr);   // operand order: row li, channels 32kk+8lg+s
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
         // g^T tile (channel 16t+li, tokens 4lg+j), then Gamma = L * g on the
         // matrix cores: lane gets Gamma[token li][channel 16t+4lg+j]
         const f32x4 gT = mfma32(gop, eyeN[hf], zero4());
-        const f32x4 gam = mfma16(pack4v(gT), lowT, zero4());
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float x = gam[j] * kLog2e;
-            el[2 * m + hf][j] = __builtin_amdgcn_exp2f(x);
-            enl[2 * m + hf][j] = __builtin_amdgcn_exp2f(-x);
-        }
+        x[2 * m + hf] = mfma16(pack4v(gT), lowT, zero4()) * kLog2e;
     }
+}
+__device__ __forceinline__ f32x4 exp2v(const f32x4& x) {
+    return f32x4{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]), __builtin_amdgcn_exp2f(x[2]),
+                 __builtin_amdgcn_exp2f(x[3])};
 }
 
 // k, q of tiles 2m, 2m+1 (same lane layout) as fp32, by identity products
@@ -317,11 +317,11 @@ __device__ __forceinline__ bf16x4 inverse_times_beta(const f32x4& Mr, uint32_t b
         Tr[j] = (col == li) ? 1.f : 0.f;
     }
     // T = (I + N)^{-1}: each lane needs its whole row of N
-    *reinterpret_cast<f32x4*>(fs + 4 * (16 * li + 4 * lg)) = Nr;
+    *reinterpret_cast<f32x4*>(fs + 4 * (FS_STRIDE * li + 4 * lg)) = Nr;
     float nrow[16];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(fs + 4 * (16 * li + 4 * p));
+        const f32x4 x = *reinterpret_cast<const f32x4*>(fs + 4 * (FS_STRIDE * li + 4 * p));
         nrow[4 * p] = x[0]; nrow[4 * p + 1] = x[1]; nrow[4 * p + 2] = x[2]; nrow[4 * p + 3] = x[3];
     }
     fsub<0>(Tr, nrow);
@@ -382,15 +382,20 @@ __device__ __forceinline__ void prepare_chunk1(const ChunkRegs& R, const PrepCtx
                                                const bf16x4& lowT, Issue&& issue) {
     const int lane = c.li + 16 * c.lg;
     issue(0);
-    f32x4 el[4], enl[4];
+    f32x4 x[4], el[4], enl[4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) decay_tiles(R, m, c.gaddr, eyeN, lowT, el, enl);
-    // token 15 carries d1; the other lanes store to the sink (a store under
-    // an exec mask would split the schedule)
+    for (int m = 0; m < 2; ++m) gamma_tiles(R, m, c.gaddr, eyeN, lowT, x);
+    // d1 first (the chunk-2 wave waits for it): token 15 carries it; the other
+    // lanes store to the sink (a store under an exec mask would split the
+    // schedule)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u) {
+        el[u] = exp2v(x[u]);
         *reinterpret_cast<f32x4*>(c.slot + S_D1 + c.eoff + 16 * (4 * c.ph + u)) = el[u];
+    }
     set_flag(c.f_d1, c.epoch);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) enl[u] = exp2v(-x[u]);
     issue(1);
     f32x4 Ms = zero4(), Ps = zero4();
 #pragma unroll
@@ -458,41 +463,49 @@ template <typename Issue>
 __device__ __forceinline__ void prepare_chunk2(const ChunkRegs& R, const PrepCtx& c, const bf16x8 (&eyeN)[2],
                                                const bf16x4& lowT, Issue&& issue) {
     const int lane = c.li + 16 * c.lg;
-    f32x4 el[4], enl[4];
+    f32x4 x[4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) decay_tiles(R, m, c.gaddr, eyeN, lowT, el, enl);
+    for (int m = 0; m < 2; ++m) gamma_tiles(R, m, c.gaddr, eyeN, lowT, x);
     issue(0);   // (after the step-start burst of the other waves' loads)
-    wait_flag(c.f_d1, c.epoch);
+    // everything that does not need d1 first: Kb2, the unscaled Kg2 and Qh2
+    // (kept in fp32 for the d1 scaling) and this half's M2 and P2 shares
     bf16x8 KA[2], QA[2], KB[2];
+    f32x4 ka[4], qa[4];
     f32x4 Ms = zero4(), Ps = zero4();
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-        const int kk = 2 * c.ph + m;
-        f32x4 kf[2], qf[2], ka[2], qa[2], kb[2], d1[2];
+        f32x4 kf[2], qf[2], kb[2];
         kq_tiles(R, m, c.gaddr, eyeN, kf, qf);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int u = 2 * m + hf;
-            const int t = 4 * c.ph + u;
-            d1[hf] = lds4(c.slot + S_D1 + 4 * (EG_STRIDE * c.lg + 4 * t));
-            *reinterpret_cast<f32x4*>(c.slot + S_E2 + c.eoff + 16 * t) = el[u];
-            ka[hf] = kf[hf] * el[u];
-            qa[hf] = qf[hf] * el[u];
-            kb[hf] = kf[hf] * enl[u];
+            const f32x4 el = exp2v(x[u]);
+            *reinterpret_cast<f32x4*>(c.slot + S_E2 + c.eoff + 16 * (4 * c.ph + u)) = el;
+            ka[u] = kf[hf] * el;
+            qa[u] = qf[hf] * el;
+            kb[hf] = kf[hf] * exp2v(-x[u]);
         }
-        KA[m] = pack_pair(ka[0], ka[1]);
-        QA[m] = pack_pair(qa[0], qa[1]);
+        KA[m] = pack_pair(ka[2 * m], ka[2 * m + 1]);
+        QA[m] = pack_pair(qa[2 * m], qa[2 * m + 1]);
         KB[m] = pack_pair(kb[0], kb[1]);
-        *reinterpret_cast<bf16x8*>(c.slot + S_KG2 + 16 * (64 * kk + lane)) =
-            pack_pair(ka[0] * d1[0], ka[1] * d1[1]);
-        *reinterpret_cast<bf16x8*>(c.slot + S_QH2 + 16 * (64 * kk + lane)) =
-            pack_pair(qa[0] * d1[0], qa[1] * d1[1]);
         Ms = mfma32(KB[m], KA[m], Ms);    // (Kg2 Kb2^T)[li][4lg+j]
         Ps = mfma32(KB[m], QA[m], Ps);    // (Qh2 Kb2^T)[li][4lg+j]
     }
     *reinterpret_cast<f32x4*>(c.sh + (SH_M2 + c.ph) * 1024 + 16 * lane) = Ms;
     *reinterpret_cast<f32x4*>(c.sh + (SH_P2 + c.ph) * 1024 + 16 * lane) = Ps;
     set_flag(c.flags + F_SH2 + c.pq, c.epoch);
+    wait_flag(c.f_d1, c.epoch);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int kk = 2 * c.ph + m;
+        f32x4 d1[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) d1[hf] = lds4(c.slot + S_D1 + 4 * (EG_STRIDE * c.lg + 4 * (4 * c.ph + 2 * m + hf)));
+        *reinterpret_cast<bf16x8*>(c.slot + S_KG2 + 16 * (64 * kk + lane)) =
+            pack_pair(ka[2 * m] * d1[0], ka[2 * m + 1] * d1[1]);
+        *reinterpret_cast<bf16x8*>(c.slot + S_QH2 + 16 * (64 * kk + lane)) =
+            pack_pair(qa[2 * m] * d1[0], qa[2 * m + 1] * d1[1]);
+    }
     issue(1);
     wait_flag(c.f_ho, c.epoch);
     f32x4 As = zero4(), Bs = zero4();
@@ -620,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         ctx.flags = flags;
         // table row of token 15, or this lane's 16 bytes of the slot's sink
         ctx.eoff = li == 15 ? 4 * EG_STRIDE * lg : (pc == 0 ? S_SJ - S_D1 : S_SJ - S_E2) + 16 * lane;
-        ctx.fs = smem + S_FS + 1024 * pq;
+        ctx.fs = smem + S_FS + FS_BYTES * pq;
         ctx.pq = pq;
         ctx.ph = ph;
         ctx.gaddr = 4 * (lg + 4 * li);
