@@ -29,37 +29,62 @@
 #include <omp.h>
 #endif
 
-/* One token of the recurrence on one (sequence, head) state S [Dk][Dv]. */
-static void kda_ref_token(double* S, double* x, const float* qt, const float* kt,
-                          const float* vt, const float* gt, double bt,
+/* One token of the recurrence on one (sequence, head) state S [Dk][Dv]; the
+ * token's rows are given in double. */
+static void kda_ref_token(double* S, double* x, const double* qt, const double* kt,
+                          const double* vt, const double* gt, double bt,
                           int64_t Dk, int64_t Dv, double scale, double* ot)
 {
     for (int64_t i = 0; i < Dk; ++i) {
-        const double a = exp((double)gt[i]);
+        const double a = exp(gt[i]);
         double* row = S + i * Dv;
         for (int64_t j = 0; j < Dv; ++j) row[j] *= a;
     }
     for (int64_t j = 0; j < Dv; ++j) x[j] = 0.0;
     for (int64_t i = 0; i < Dk; ++i) {
-        const double ki = (double)kt[i];
+        const double ki = kt[i];
         const double* row = S + i * Dv;
         for (int64_t j = 0; j < Dv; ++j) x[j] += ki * row[j];
     }
-    for (int64_t j = 0; j < Dv; ++j) x[j] = bt * ((double)vt[j] - x[j]);
+    for (int64_t j = 0; j < Dv; ++j) x[j] = bt * (vt[j] - x[j]);
     for (int64_t i = 0; i < Dk; ++i) {
-        const double ki = (double)kt[i];
+        const double ki = kt[i];
         double* row = S + i * Dv;
         for (int64_t j = 0; j < Dv; ++j) row[j] += ki * x[j];
     }
     if (ot) {
         for (int64_t j = 0; j < Dv; ++j) x[j] = 0.0;
         for (int64_t i = 0; i < Dk; ++i) {
-            const double qi = (double)qt[i];
+            const double qi = qt[i];
             const double* row = S + i * Dv;
             for (int64_t j = 0; j < Dv; ++j) x[j] += qi * row[j];
         }
         for (int64_t j = 0; j < Dv; ++j) ot[j] = scale * x[j];
     }
+}
+
+/* float -> double (exact) */
+static void widen(const float* src, double* dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) dst[i] = (double)src[i];
+}
+
+/* Row buffers of one token in double: q, k, g [Dk] and v [Dv]. */
+typedef struct { double *q, *k, *g, *v, *x; } rows_t;
+
+static int rows_alloc(rows_t* r, int64_t Dk, int64_t Dv)
+{
+    r->q = (double*)malloc(sizeof(double) * Dk);
+    r->k = (double*)malloc(sizeof(double) * Dk);
+    r->g = (double*)malloc(sizeof(double) * Dk);
+    r->v = (double*)malloc(sizeof(double) * Dv);
+    r->x = (double*)malloc(sizeof(double) * Dv);
+    return r->q && r->k && r->g && r->v && r->x;
+}
+
+static void rows_free(rows_t* r)
+{
+    free(r->q); free(r->k); free(r->g); free(r->v); free(r->x);
 }
 
 /*
@@ -94,19 +119,22 @@ int kda_ref_forward(const float* q, const float* k, const float* v, const float*
         const int64_t bos = cu_seqlens ? cu_seqlens[n] : 0;
         const int64_t eos = cu_seqlens ? cu_seqlens[n + 1] : T;
         double* S = (double*)malloc(sizeof(double) * Dk * Dv);
-        double* x = (double*)malloc(sizeof(double) * Dv);
-        if (!S || !x) { free(S); free(x); failed |= 1; continue; }
+        rows_t r = {0};
+        if (!S || !rows_alloc(&r, Dk, Dv)) { free(S); rows_free(&r); failed |= 1; continue; }
         const int64_t s_off = (n * H + h) * Dk * Dv;
         for (int64_t e = 0; e < Dk * Dv; ++e)
             S[e] = initial_state ? (double)initial_state[s_off + e] : 0.0;
         for (int64_t t = bos; t < eos; ++t) {
             const int64_t row = (b * T + t) * H + h;
-            kda_ref_token(S, x, q + row * Dk, k + row * Dk, v + row * Dv, g + row * Dk,
-                          (double)beta[row], Dk, Dv, scale, o + row * Dv);
+            widen(q + row * Dk, r.q, Dk);
+            widen(k + row * Dk, r.k, Dk);
+            widen(g + row * Dk, r.g, Dk);
+            widen(v + row * Dv, r.v, Dv);
+            kda_ref_token(S, r.x, r.q, r.k, r.v, r.g, (double)beta[row], Dk, Dv, scale, o + row * Dv);
         }
         if (final_state) memcpy(final_state + s_off, S, sizeof(double) * Dk * Dv);
         free(S);
-        free(x);
+        rows_free(&r);
     }
     return failed ? -1 : 0;
 }
@@ -138,12 +166,100 @@ int kda_ref_decode_step(const float* q, const float* k, const float* v, const fl
     for (int64_t u = 0; u < units; ++u) {
         const int64_t r = u / H, h = u % H;
         const int64_t s = slots ? slots[r] : r;
-        double* x = (double*)malloc(sizeof(double) * Dv);
-        if (!x) { failed |= 1; continue; }
+        rows_t w = {0};
+        if (!rows_alloc(&w, Dk, Dv)) { rows_free(&w); failed |= 1; continue; }
         const int64_t row = r * H + h;
-        kda_ref_token(state_cache + (s * H + h) * Dk * Dv, x, q + row * Dk, k + row * Dk,
-                      v + row * Dv, g + row * Dk, (double)beta[row], Dk, Dv, scale, o + row * Dv);
-        free(x);
+        widen(q + row * Dk, w.q, Dk);
+        widen(k + row * Dk, w.k, Dk);
+        widen(g + row * Dk, w.g, Dk);
+        widen(v + row * Dv, w.v, Dv);
+        kda_ref_token(state_cache + (s * H + h) * Dk * Dv, w.x, w.q, w.k, w.v, w.g, (double)beta[row],
+                      Dk, Dv, scale, o + row * Dv);
+        rows_free(&w);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * The gate, beta and normalisation prologue of one token-head, in double.
+ * It is the reading of the pages' gate parameters documented with the
+ * library: A_log has one entry per key channel, shared by every head; dt_bias
+ * one per (head, key channel); the gate is bounded below by lb:
+ *   q = q_raw / sqrt(|q_raw|^2 + eps),   k likewise
+ *   g[c] = lb * sigmoid(exp(A_log[c]) * (g_logit[c] + dt_bias[c]))
+ *   beta = sigmoid(beta_logit)
+ * Returns beta; writes q, k, g [Dk].
+ */
+static double kda_ref_prologue_token(const float* qr, const float* kr, const float* gl, double bl,
+                                     const float* A_log, const float* dtb, double lb, double eps,
+                                     int64_t Dk, double* q, double* k, double* g)
+{
+    double sq = 0.0, sk = 0.0;
+    for (int64_t i = 0; i < Dk; ++i) {
+        sq += (double)qr[i] * (double)qr[i];
+        sk += (double)kr[i] * (double)kr[i];
+    }
+    const double nq = sqrt(sq + eps), nk = sqrt(sk + eps);
+    for (int64_t i = 0; i < Dk; ++i) {
+        q[i] = (double)qr[i] / nq;
+        k[i] = (double)kr[i] / nk;
+        const double z = exp((double)A_log[i]) * ((double)gl[i] + (double)dtb[i]);
+        g[i] = lb / (1.0 + exp(-z));
+    }
+    return 1.0 / (1.0 + exp(-bl));
+}
+
+/*
+ * Forward from the raw projections: q_raw, k_raw, g_logit [B,T,H,Dk], v
+ * [B,T,H,Dv], beta_logit [B,T,H], A_log [Dk], dt_bias [H*Dk]; each token goes
+ * through the prologue above, then the recurrence. Other arguments and the
+ * return value as kda_ref_forward.
+ */
+int kda_ref_prologue_forward(const float* q_raw, const float* k_raw, const float* v,
+                             const float* g_logit, const float* beta_logit,
+                             const float* A_log, const float* dt_bias, double lb, double eps,
+                             const float* initial_state, const int64_t* cu_seqlens, int64_t N,
+                             int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                             double scale, double* o, double* final_state, int nthreads)
+{
+    if (!q_raw || !k_raw || !v || !g_logit || !beta_logit || !A_log || !dt_bias || !o ||
+        B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || !(eps >= 0.0))
+        return -1;
+    if (cu_seqlens) {
+        if (B != 1 || N < 1 || cu_seqlens[0] != 0 || cu_seqlens[N] != T) return -1;
+        for (int64_t n = 0; n < N; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+    } else {
+        N = B;
+    }
+    int failed = 0;
+    const int64_t units = N * H;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+#endif
+    for (int64_t u = 0; u < units; ++u) {
+        const int64_t n = u / H, h = u % H;
+        const int64_t b = cu_seqlens ? 0 : n;
+        const int64_t bos = cu_seqlens ? cu_seqlens[n] : 0;
+        const int64_t eos = cu_seqlens ? cu_seqlens[n + 1] : T;
+        double* S = (double*)malloc(sizeof(double) * Dk * Dv);
+        rows_t r = {0};
+        if (!S || !rows_alloc(&r, Dk, Dv)) { free(S); rows_free(&r); failed |= 1; continue; }
+        const int64_t s_off = (n * H + h) * Dk * Dv;
+        for (int64_t e = 0; e < Dk * Dv; ++e)
+            S[e] = initial_state ? (double)initial_state[s_off + e] : 0.0;
+        for (int64_t t = bos; t < eos; ++t) {
+            const int64_t row = (b * T + t) * H + h;
+            const double bt = kda_ref_prologue_token(q_raw + row * Dk, k_raw + row * Dk, g_logit + row * Dk,
+                                                     (double)beta_logit[row], A_log, dt_bias + h * Dk,
+                                                     lb, eps, Dk, r.q, r.k, r.g);
+            widen(v + row * Dv, r.v, Dv);
+            kda_ref_token(S, r.x, r.q, r.k, r.v, r.g, bt, Dk, Dv, scale, o + row * Dv);
+        }
+        if (final_state) memcpy(final_state + s_off, S, sizeof(double) * Dk * Dv);
+        free(S);
+        rows_free(&r);
     }
     return failed ? -1 : 0;
 }

@@ -25,6 +25,10 @@ Two implementations, written separately:
     one Python-level step per token;
   * ``c_forward`` / ``c_decode_step``: the plain C loops in kda_ref.c (OpenMP
     over independent (sequence, head) units), loaded with ctypes.
+The gate, beta and normalisation prologue that turns raw projections into
+(q, k, g, beta) has a NumPy form (``prologue``, then ``recurrence``) and a C
+form (``c_prologue_forward``); the reading of the gate it implements is in
+``prologue``'s docstring.
 Both take inputs as float arrays that hold the GPU's bf16 or fp32 values
 exactly, and compute in float64.
 """
@@ -84,6 +88,35 @@ def recurrence(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0)
     return o, final
 
 
+def prologue(q_raw, k_raw, g_logit, beta_logit, A_log, dt_bias, gate_lower_bound=-5.0, l2_eps=1e-6):
+    """The gate, beta and normalisation prologue (float64), per token and head.
+
+    The pages fix the gate's parameters and bound but not its formula (hysenlabs
+    "kimi-k3-mlx", section "The A_log shape mismatch is a silent-garbage bug the
+    tests assert": A_log has one entry per key channel, shared by every head,
+    dt_bias one per (head, channel); section "Attention is 93 layers ...":
+    gate_lower_bound = -5). The reading implemented, as documented with the
+    library:
+
+        q = q_raw / sqrt(|q_raw|^2 + eps)          (over d_k), k likewise
+        g = lb * sigmoid(exp(A_log) * (g_logit + dt_bias))
+        beta = sigmoid(beta_logit)
+
+    q_raw, k_raw, g_logit [..., H, Dk]; beta_logit [..., H]; A_log [Dk];
+    dt_bias [H*Dk]. Returns (q, k, g, beta) as float64.
+    """
+    q_raw, k_raw, g_logit = (np.asarray(a, dtype=np.float64) for a in (q_raw, k_raw, g_logit))
+    beta_logit = np.asarray(beta_logit, dtype=np.float64)
+    H, Dk = q_raw.shape[-2:]
+    A = np.exp(np.asarray(A_log, dtype=np.float64).reshape(Dk))
+    bias = np.asarray(dt_bias, dtype=np.float64).reshape(H, Dk)
+    q = q_raw / np.sqrt((q_raw * q_raw).sum(-1, keepdims=True) + l2_eps)
+    k = k_raw / np.sqrt((k_raw * k_raw).sum(-1, keepdims=True) + l2_eps)
+    g = gate_lower_bound / (1.0 + np.exp(-(A * (g_logit + bias))))
+    beta = 1.0 / (1.0 + np.exp(-beta_logit))
+    return q, k, g, beta
+
+
 def decode_step(q, k, v, g, beta, state_cache, state_slots=None, scale=1.0):
     """One decode step against a state cache. Returns (o [Nb,H,Dv], new cache copy).
 
@@ -125,6 +158,10 @@ def load_c():
         lib.kda_ref_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I,
                                             ctypes.c_double, P, ctypes.c_int]
         lib.kda_ref_decode_step.restype = ctypes.c_int
+        D = ctypes.c_double
+        lib.kda_ref_prologue_forward.argtypes = [P, P, P, P, P, P, P, D, D, P, P, I, I, I, I, I, I,
+                                                 D, P, P, ctypes.c_int]
+        lib.kda_ref_prologue_forward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -158,6 +195,36 @@ def c_forward(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0,
                              _ptr(final), int(nthreads))
     if rc != 0:
         raise ValueError("kda_ref_forward rejected its arguments")
+    return o, final
+
+
+def c_prologue_forward(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, gate_lower_bound=-5.0,
+                       l2_eps=1e-6, initial_state=None, cu_seqlens=None, scale=1.0, nthreads=0,
+                       want_final=True):
+    """The C oracle from the raw projections: the prologue (see ``prologue``)
+    then the recurrence, all in float64."""
+    lib = load_c()
+    q_raw, k_raw, v, g_logit, beta_logit = (_f32(a) for a in (q_raw, k_raw, v, g_logit, beta_logit))
+    A_log, dt_bias = _f32(A_log).reshape(-1), _f32(dt_bias).reshape(-1)
+    B, T, H, Dk = q_raw.shape
+    Dv = v.shape[-1]
+    if A_log.size != Dk or dt_bias.size != H * Dk:
+        raise ValueError("A_log must have Dk entries and dt_bias H*Dk")
+    cu = None
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64).reshape(-1))
+        N = cu.size - 1
+    else:
+        N = B
+    s0 = None if initial_state is None else _f32(initial_state)
+    o = np.zeros((B, T, H, Dv))
+    final = np.zeros((N, H, Dk, Dv)) if want_final else None
+    rc = lib.kda_ref_prologue_forward(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(g_logit), _ptr(beta_logit),
+                                      _ptr(A_log), _ptr(dt_bias), float(gate_lower_bound), float(l2_eps),
+                                      _ptr(s0), _ptr(cu), N, B, T, H, Dk, Dv, float(scale), _ptr(o),
+                                      _ptr(final), int(nthreads))
+    if rc != 0:
+        raise ValueError("kda_ref_prologue_forward rejected its arguments")
     return o, final
 
 
