@@ -52,6 +52,9 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F,
                                   ctypes.c_int, P, P, P]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_prologue.argtypes = [P, P, P, P, P, P, P, F, F, P, P, I32, I32, I32, I32, I32, I32,
+                                           I32, F, ctypes.c_int, P, P, P]
+    lib.kda_chunk_fwd_prologue.restype = ctypes.c_int
     lib.kda_recurrent_step.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F,
                                        ctypes.c_int, P, P]
     lib.kda_recurrent_step.restype = ctypes.c_int
@@ -99,40 +102,7 @@ def _need(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk_size=0, scale=1.0,
-              output_final_state=True, out=None, final_state=None):
-    """KDA forward over whole sequences (kda_chunk_fwd).
-
-    q, k, g [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H] (all float32 or all bfloat16,
-    on one GPU); initial_state [N,H,Dk,Dv] float32 or None; cu_seqlens int32
-    [N+1] (B must be 1) or None (N = B). Returns (o [B,T,H,Dv], final_state
-    [N,H,Dk,Dv] float32 or None).
-    """
-    lib = load_library()
-    if q.dim() != 4:
-        raise ValueError("q must be [B,T,H,Dk]")
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
-    dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("inputs must be on a GPU")
-    if q.dtype not in _DTYPES:
-        raise TypeError(f"unsupported dtype {q.dtype}")
-    dt = q.dtype
-    _need(q, "q", (B, T, H, Dk), dt, dev)
-    _need(k, "k", (B, T, H, Dk), dt, dev)
-    _need(g, "g", (B, T, H, Dk), dt, dev)
-    _need(v, "v", (B, T, H, Dv), dt, dev)
-    _need(beta, "beta", (B, T, H), dt, dev)
-    if cu_seqlens is not None:
-        if cu_seqlens.dim() != 1:
-            raise ValueError("cu_seqlens must be 1-D")
-        N = cu_seqlens.numel() - 1
-        _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
-    else:
-        N = B
-    if initial_state is not None:
-        _need(initial_state, "initial_state", (N, H, Dk, Dv), torch.float32, dev)
+def _chunk_outputs(B, T, H, Dk, Dv, N, dt, dev, out, final_state, output_final_state):
     if out is None:
         out = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
     else:
@@ -144,9 +114,78 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk_size=
             _need(final_state, "final_state", (N, H, Dk, Dv), torch.float32, dev)
     else:
         final_state = None
+    return out, final_state
+
+
+def _chunk_inputs(q, k, v, g, beta, initial_state, cu_seqlens, names):
+    if q.dim() != 4:
+        raise ValueError(f"{names[0]} must be [B,T,H,Dk]")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    dt = q.dtype
+    _need(q, names[0], (B, T, H, Dk), dt, dev)
+    _need(k, names[1], (B, T, H, Dk), dt, dev)
+    _need(g, names[3], (B, T, H, Dk), dt, dev)
+    _need(v, names[2], (B, T, H, Dv), dt, dev)
+    _need(beta, names[4], (B, T, H), dt, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be 1-D")
+        N = cu_seqlens.numel() - 1
+        _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (N, H, Dk, Dv), torch.float32, dev)
+    return B, T, H, Dk, Dv, N, dt, dev
+
+
+def chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk_size=0, scale=1.0,
+              output_final_state=True, out=None, final_state=None):
+    """KDA forward over whole sequences (kda_chunk_fwd).
+
+    q, k, g [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H] (all float32 or all bfloat16,
+    on one GPU); initial_state [N,H,Dk,Dv] float32 or None; cu_seqlens int32
+    [N+1] (B must be 1) or None (N = B). Returns (o [B,T,H,Dv], final_state
+    [N,H,Dk,Dv] float32 or None).
+    """
+    lib = load_library()
+    B, T, H, Dk, Dv, N, dt, dev = _chunk_inputs(q, k, v, g, beta, initial_state, cu_seqlens,
+                                                ("q", "k", "v", "g", "beta"))
+    out, final_state = _chunk_outputs(B, T, H, Dk, Dv, N, dt, dev, out, final_state, output_final_state)
     st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                            _ptr(cu_seqlens), B, T, H, Dk, Dv, N, int(chunk_size), float(scale),
                            _DTYPES[dt], _ptr(out), _ptr(final_state), _stream(dev))
+    _check(st)
+    return out, final_state
+
+
+def chunk_fwd_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, gate_lower_bound=-5.0,
+                       l2_eps=1e-6, initial_state=None, cu_seqlens=None, chunk_size=0, scale=1.0,
+                       output_final_state=True, out=None, final_state=None):
+    """KDA forward from the raw projections with the gate, beta and L2-norm
+    prologue inside the chunk kernel (kda_chunk_fwd_prologue).
+
+    q_raw, k_raw, g_logit [B,T,H,Dk]; v [B,T,H,Dv]; beta_logit [B,T,H] (one
+    dtype, float32 or bfloat16); A_log [Dk] and dt_bias [H*Dk] float32 on the
+    same GPU. Other arguments and the return value as ``chunk_fwd``.
+    """
+    lib = load_library()
+    B, T, H, Dk, Dv, N, dt, dev = _chunk_inputs(q_raw, k_raw, v, g_logit, beta_logit, initial_state,
+                                                cu_seqlens, ("q_raw", "k_raw", "v", "g_logit", "beta_logit"))
+    _need(A_log, "A_log", (Dk,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H * Dk,), torch.float32, dev)
+    out, final_state = _chunk_outputs(B, T, H, Dk, Dv, N, dt, dev, out, final_state, output_final_state)
+    st = lib.kda_chunk_fwd_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(g_logit), _ptr(beta_logit),
+                                    _ptr(A_log), _ptr(dt_bias), float(gate_lower_bound), float(l2_eps),
+                                    _ptr(initial_state), _ptr(cu_seqlens), B, T, H, Dk, Dv, N,
+                                    int(chunk_size), float(scale), _DTYPES[dt], _ptr(out), _ptr(final_state),
+                                    _stream(dev))
     _check(st)
     return out, final_state
 

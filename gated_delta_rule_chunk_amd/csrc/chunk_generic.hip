@@ -14,6 +14,12 @@
 // This is the WY/UT-transform chunk form of the gated delta rule with a
 // per-channel decay; every exponential here is of a non-positive number,
 // so no range precondition on g is needed on this path.
+//
+// With the prologue (ChunkArgs::prologue), rows are loaded as raw projections
+// and turned into the recurrence's inputs on the way into LDS:
+//   g = lb * sigmoid(exp(A_log[c]) * (logit + dt_bias[h][c])), beta =
+//   sigmoid(logit), q and k scaled to x / sqrt(|x|^2 + eps) per row.
+// Rows past a sequence's end keep g = beta = 0 and zero q, k.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -37,6 +43,8 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
     __shared__ float sS[DK][BV];
     __shared__ float sBeta[C];
     __shared__ float sGn[DK];
+    __shared__ float sAe[DK];     // prologue: exp(A_log)
+    __shared__ float sDb[DK];     // prologue: dt_bias of this head
 
     const Tin* q = static_cast<const Tin*>(a.q);
     const Tin* k = static_cast<const Tin*>(a.k);
@@ -69,6 +77,12 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
         const int r = idx / BV, c = idx % BV;
         sS[r][c] = a.s0 ? a.s0[state_base + (int64_t)r * Dv + c0 + c] : 0.f;
     }
+    if (a.prologue) {
+        for (int c = tid; c < DK; c += kGenThreads) {
+            sAe[c] = expf(a.A_log[c]);
+            sDb[c] = a.dt_bias[h * DK + c];
+        }
+    }
 
     for (int64_t cs = 0; cs < len; cs += C) {
         const int rows = (int)((len - cs) < C ? (len - cs) : C);
@@ -82,6 +96,7 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
                 qv = load_elem(q, e);
                 kv = load_elem(k, e);
                 gv = load_elem(g, e);
+                if (a.prologue) gv = a.gate_lb / (1.f + expf(-sAe[c] * (gv + sDb[c])));
             }
             sQ[r][c] = qv;
             sK[r][c] = kv;
@@ -91,9 +106,23 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
             const int r = idx / BV, c = idx % BV;
             sV[r][c] = r < rows ? load_elem(v, ((tok0 + r) * H + h) * Dv + c0 + c) : 0.f;
         }
-        for (int r = tid; r < C; r += kGenThreads)
-            sBeta[r] = r < rows ? load_elem(beta, (tok0 + r) * H + h) : 0.f;
+        for (int r = tid; r < C; r += kGenThreads) {
+            float bv = r < rows ? load_elem(beta, (tok0 + r) * H + h) : 0.f;
+            if (a.prologue && r < rows) bv = 1.f / (1.f + expf(-bv));
+            sBeta[r] = bv;
+        }
         __syncthreads();
+        if (a.prologue) {
+            // q and k rows to unit length (eps > 0: zero rows stay zero)
+            for (int idx = tid; idx < 2 * C; idx += kGenThreads) {
+                float* row = idx < C ? sQ[idx] : sK[idx - C];
+                float ss = 0.f;
+                for (int c = 0; c < DK; ++c) ss += row[c] * row[c];
+                const float rs = 1.f / sqrtf(ss + a.l2_eps);
+                for (int c = 0; c < DK; ++c) row[c] *= rs;
+            }
+            __syncthreads();
+        }
 
         // in-chunk cumulative log-decay, one channel per thread
         for (int c = tid; c < DK; c += kGenThreads) {

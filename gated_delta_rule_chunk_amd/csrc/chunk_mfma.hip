@@ -838,7 +838,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
 }  // namespace
 
 bool chunk_mfma_supported(const ChunkArgs& a) {
-    return a.bf16 && a.Dk == kDK && a.Dv == kDV;
+    return a.bf16 && a.Dk == kDK && a.Dv == kDV && !a.prologue;
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t s) {

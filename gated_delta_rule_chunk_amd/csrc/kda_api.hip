@@ -37,53 +37,102 @@ const char* kda_status_string(kda_status s) {
 
 const char* kda_last_error_message(void) { return g_last_error; }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two chunk entry points; fills a on success.
+kda_status check_chunk(const char* fn, const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                       int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
+                       int32_t chunk_size, float scale, kda_dtype dtype, void* o, float* final_state,
+                       kda::ChunkArgs& a) {
+    if (T > 0 && (!q || !k || !v || !g || !beta || !o))
+        return fail(KDA_ERR_INVALID_ARG, "%s: every input and o must be non-NULL when T > 0", fn);
+    if (B < 1 || T < 0 || H < 1 || N < 0)
+        return fail(KDA_ERR_INVALID_ARG, "%s: need B >= 1, T >= 0, H >= 1, N >= 0 (got B=%d T=%d H=%d N=%d)",
+                    fn, B, T, H, N);
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dtype %d is not KDA_F32 or KDA_BF16", fn, (int)dtype);
+    if (!dim_ok(Dk) || !dim_ok(Dv))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: Dk=%d, Dv=%d; supported head dims are 16, 32, 64, 128",
+                    fn, Dk, Dv);
+    const int32_t chunk = chunk_size == 0 ? 64 : chunk_size;
+    if (chunk != 16 && chunk != 32 && chunk != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: chunk_size=%d; supported are 16, 32, 64 (0 = 64)", fn, chunk_size);
+    if (cu_seqlens) {
+        if (B != 1)
+            return fail(KDA_ERR_INVALID_ARG, "%s: packed sequences (cu_seqlens) need B == 1, got B=%d", fn, B);
+        if (N < 1)
+            return fail(KDA_ERR_INVALID_ARG, "%s: packed sequences need N >= 1, got N=%d", fn, N);
+    } else if (N != B) {
+        return fail(KDA_ERR_INVALID_ARG, "%s: without cu_seqlens N must equal B (N=%d, B=%d)", fn, N, B);
+    }
+    const int64_t units = (int64_t)N * H;
+    if (units > (int64_t)1 << 26 || (int64_t)B * T * H > ((int64_t)1 << 40))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large (N*H=%lld)", fn, (long long)units);
+    if (T > 0 && (o == q || o == k || o == v || o == g || o == beta))
+        return fail(KDA_ERR_INVALID_ARG, "%s: o must not alias an input", fn);
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.s0 = initial_state; a.cu = cu_seqlens; a.o = o; a.sT = final_state;
+    a.B = B; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.N = N; a.chunk = chunk;
+    a.scale = scale; a.bf16 = dtype == KDA_BF16;
+    return KDA_OK;
+}
+
+kda_status launch_chunk(const char* fn, const kda::ChunkArgs& a, void* stream) {
+    if ((int64_t)a.N * a.H == 0) return KDA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = kda::chunk_mfma_supported(a) ? kda::launch_chunk_mfma(a, s)
+                                                      : kda::launch_chunk_generic(a, s);
+    if (e != hipSuccess)
+        return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, const float* initial_state,
                          const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H,
                          int32_t Dk, int32_t Dv, int32_t N, int32_t chunk_size, float scale,
                          kda_dtype dtype, void* o, float* final_state, void* stream) {
     g_last_error[0] = 0;
-    if (T > 0 && (!q || !k || !v || !g || !beta || !o))
-        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: q, k, v, g, beta and o must be non-NULL when T > 0");
-    if (B < 1 || T < 0 || H < 1 || N < 0)
-        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: need B >= 1, T >= 0, H >= 1, N >= 0 (got B=%d T=%d H=%d N=%d)",
-                    B, T, H, N);
-    if (dtype != KDA_F32 && dtype != KDA_BF16)
-        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: dtype %d is not KDA_F32 or KDA_BF16", (int)dtype);
-    if (!dim_ok(Dk) || !dim_ok(Dv))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: Dk=%d, Dv=%d; supported head dims are 16, 32, 64, 128",
-                    Dk, Dv);
-    const int32_t chunk = chunk_size == 0 ? 64 : chunk_size;
-    if (chunk != 16 && chunk != 32 && chunk != 64)
-        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: chunk_size=%d; supported are 16, 32, 64 (0 = 64)",
-                    chunk_size);
-    if (cu_seqlens) {
-        if (B != 1)
-            return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: packed sequences (cu_seqlens) need B == 1, got B=%d", B);
-        if (N < 1)
-            return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: packed sequences need N >= 1, got N=%d", N);
-    } else if (N != B) {
-        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: without cu_seqlens N must equal B (N=%d, B=%d)", N, B);
-    }
-    const int64_t units = (int64_t)N * H;
-    if (units > (int64_t)1 << 26 || (int64_t)B * T * H > ((int64_t)1 << 40))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: problem too large (N*H=%lld)", (long long)units);
-    if (T > 0 && (o == q || o == k || o == v || o == g || o == beta))
-        return fail(KDA_ERR_INVALID_ARG, "kda_chunk_fwd: o must not alias an input");
-
     kda::ChunkArgs a;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
-    a.s0 = initial_state; a.cu = cu_seqlens; a.o = o; a.sT = final_state;
-    a.B = B; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.N = N; a.chunk = chunk;
-    a.scale = scale; a.bf16 = dtype == KDA_BF16;
-    if (units == 0) return KDA_OK;
+    const kda_status st = check_chunk("kda_chunk_fwd", q, k, v, g, beta, initial_state, cu_seqlens, B, T, H,
+                                      Dk, Dv, N, chunk_size, scale, dtype, o, final_state, a);
+    if (st != KDA_OK) return st;
+    return launch_chunk("kda_chunk_fwd", a, stream);
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = kda::chunk_mfma_supported(a) ? kda::launch_chunk_mfma(a, s)
-                                                      : kda::launch_chunk_generic(a, s);
-    if (e != hipSuccess)
-        return fail(KDA_ERR_HIP, "kda_chunk_fwd: launch failed: %s", hipGetErrorString(e));
-    return KDA_OK;
+kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const void* v,
+                                  const void* g_logit, const void* beta_logit, const float* A_log,
+                                  const float* dt_bias, float gate_lower_bound, float l2_eps,
+                                  const float* initial_state, const int32_t* cu_seqlens, int32_t B,
+                                  int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
+                                  int32_t chunk_size, float scale, kda_dtype dtype, void* o,
+                                  float* final_state, void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_chunk_fwd_prologue";
+    kda::ChunkArgs a;
+    const kda_status st = check_chunk(fn, q_raw, k_raw, v, g_logit, beta_logit, initial_state, cu_seqlens, B,
+                                      T, H, Dk, Dv, N, chunk_size, scale, dtype, o, final_state, a);
+    if (st != KDA_OK) return st;
+    if (T > 0 && (!A_log || !dt_bias))
+        return fail(KDA_ERR_INVALID_ARG, "%s: A_log and dt_bias must be non-NULL when T > 0", fn);
+    if (!(gate_lower_bound < 0.f) || !(gate_lower_bound > -1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: gate_lower_bound must be finite and negative (got %g)", fn,
+                    (double)gate_lower_bound);
+    if (!(l2_eps > 0.f) || !(l2_eps < 1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: l2_eps must be finite and positive (got %g)", fn, (double)l2_eps);
+    a.prologue = true;
+    a.A_log = A_log;
+    a.dt_bias = dt_bias;
+    a.gate_lb = gate_lower_bound;
+    a.l2_eps = l2_eps;
+    return launch_chunk(fn, a, stream);
 }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* g,

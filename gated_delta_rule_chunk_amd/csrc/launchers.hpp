@@ -20,6 +20,14 @@ struct ChunkArgs {
     int32_t B, T, H, Dk, Dv, N, chunk;
     float scale;
     bool bf16;
+    // gate, beta and normalisation prologue: when set, q and k hold the raw
+    // projections (normalised in the kernel), g the gate logits and beta the
+    // beta logits
+    bool prologue = false;
+    const float* A_log = nullptr;     // [Dk]
+    const float* dt_bias = nullptr;   // [H*Dk]
+    float gate_lb = 0.f;
+    float l2_eps = 0.f;
 };
 
 struct StepArgs {

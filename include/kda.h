@@ -86,6 +86,41 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          kda_dtype dtype, void* o, float* final_state, void* stream);
 
 /*
+ * Chunkwise KDA forward from the raw projections, with the gate, beta and
+ * normalisation prologue computed inside the chunk kernel (no separate pass
+ * over HBM). Per token t and head h:
+ *   q = q_raw / sqrt(|q_raw|^2 + l2_eps)          over the Dk channels; k likewise
+ *   g[c] = gate_lower_bound * sigmoid(exp(A_log[c]) * (g_logit[c] + dt_bias[h*Dk + c]))
+ *   beta = sigmoid(beta_logit)
+ * then the recurrence of kda_chunk_fwd. The pages give the gate's parameters
+ * and bound: A_log has one entry per key channel and is shared by every head,
+ * dt_bias one per (head, channel) (hysenlabs "kimi-k3-mlx", section "The A_log
+ * shape mismatch is a silent-garbage bug the tests assert"), and
+ * gate_lower_bound is -5.0 (section "Attention is 93 layers split between KDA
+ * and a NoPE gated MLA"). The formula above is this library's reading of them;
+ * the pages do not print it.
+ *
+ *   q_raw, k_raw, g_logit  [B,T,H,Dk] dtype
+ *   v [B,T,H,Dv], beta_logit [B,T,H]  dtype
+ *   A_log      [Dk] float32, device;  dt_bias [H*Dk] float32, device
+ *   gate_lower_bound  finite and < 0; the gate lies in [gate_lower_bound, 0)
+ *   l2_eps     finite and > 0 (rows of zeros normalise to zeros)
+ * All other arguments, the ownership rules and the errors are those of
+ * kda_chunk_fwd; a bad A_log/dt_bias pointer, bound or eps is
+ * KDA_ERR_INVALID_ARG. bf16 with Dk = Dv = 128 and gate_lower_bound >= -5 runs
+ * the matrix-core kernel (which relies on g >= -5); everything else runs the
+ * float32 chunk kernel. Rows past a sequence's end are zero tokens with g = 0
+ * and beta = 0, as in kda_chunk_fwd.
+ */
+kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const void* v,
+                                  const void* g_logit, const void* beta_logit, const float* A_log,
+                                  const float* dt_bias, float gate_lower_bound, float l2_eps,
+                                  const float* initial_state, const int32_t* cu_seqlens, int32_t B,
+                                  int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
+                                  int32_t chunk_size, float scale, kda_dtype dtype, void* o,
+                                  float* final_state, void* stream);
+
+/*
  * One decode step (T = 1 per row) against a state cache, updated in place.
  *
  *   q, k, g      [Nb,H,Dk] dtype;  v [Nb,H,Dv] dtype;  beta [Nb,H] dtype

@@ -88,7 +88,7 @@ def packed_lengths(rng, n, lo, hi):
 
 
 BLOCK_ROWS = 1024
-_STREAM = dict(lengths=0, q=1, k=2, v=3, g=4, beta=5, s0=6)
+_STREAM = dict(lengths=0, q=1, k=2, v=3, g=4, beta=5, s0=6, A_log=7, dt_bias=8)
 
 
 def _pool_size():
@@ -165,6 +165,45 @@ def make_chunk_inputs(B, T, H, Dk, Dv, seed, dtype="bf16", init_state=False, len
     shp = lambda x: x.reshape((B, T) + x.shape[1:])  # noqa: E731
     return dict(q=_round(shp(q), dtype), k=_round(shp(k), dtype), v=_round(shp(v), dtype),
                 g=_round(shp(g), dtype), beta=_round(shp(beta), dtype), initial_state=s0,
+                cu_seqlens=None if cu is None else torch.from_numpy(cu))
+
+
+def make_prologue_inputs(B, T, H, Dk, Dv, seed, dtype="bf16", init_state=False, lengths=None,
+                         n_seqs=0, len_lo=0, len_hi=0, param_std=0.5, s0_std=0.02):
+    """Raw projections for the fused-prologue forward: the same draws as
+    ``make_chunk_inputs`` (same seeds and streams) before any map, i.e. q_raw,
+    k_raw, g_logit [B,T,H,Dk] and v [B,T,H,Dv], beta_logit [B,T,H] all N(0,1),
+    rounded to ``dtype``; plus the gate parameters A_log [Dk] and dt_bias
+    [H*Dk], float32 N(0, param_std^2) from streams 7 and 8. Returns a dict of
+    CPU tensors with keys q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias,
+    initial_state, cu_seqlens."""
+    cu = None
+    if lengths is None and n_seqs > 0:
+        lengths = packed_lengths(np.random.default_rng([seed, _STREAM["lengths"]]), n_seqs, len_lo, len_hi)
+    if lengths is not None:
+        lengths = np.asarray(lengths, dtype=np.int64)
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        B, T = 1, int(cu[-1])
+    N = B if cu is None else len(cu) - 1
+    rows = B * T
+    ident = lambda x: x  # noqa: E731
+    q = _blocked(seed, _STREAM["q"], (rows, H, Dk), ident)
+    k = _blocked(seed, _STREAM["k"], (rows, H, Dk), ident)
+    v = _blocked(seed, _STREAM["v"], (rows, H, Dv), ident)
+    g = _blocked(seed, _STREAM["g"], (rows, H, Dk), ident)
+    beta = _blocked(seed, _STREAM["beta"], (rows, H), ident)
+    A_log = (np.float32(param_std) * np.random.default_rng([seed, _STREAM["A_log"]]).standard_normal(
+        Dk, dtype=np.float32))
+    dt_bias = (np.float32(param_std) * np.random.default_rng([seed, _STREAM["dt_bias"]]).standard_normal(
+        H * Dk, dtype=np.float32))
+    s0 = None
+    if init_state:
+        s0 = torch.from_numpy(_blocked(seed, _STREAM["s0"], (N, H, Dk, Dv),
+                                       lambda x: np.float32(s0_std) * x))
+    shp = lambda x: x.reshape((B, T) + x.shape[1:])  # noqa: E731
+    return dict(q_raw=_round(shp(q), dtype), k_raw=_round(shp(k), dtype), v=_round(shp(v), dtype),
+                g_logit=_round(shp(g), dtype), beta_logit=_round(shp(beta), dtype),
+                A_log=torch.from_numpy(A_log), dt_bias=torch.from_numpy(dt_bias), initial_state=s0,
                 cu_seqlens=None if cu is None else torch.from_numpy(cu))
 
 

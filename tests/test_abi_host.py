@@ -21,8 +21,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = kda.declared_symbols()
-    assert set(names) == {"kda_chunk_fwd", "kda_recurrent_step", "kda_status_string",
-                          "kda_last_error_message"}
+    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step",
+                          "kda_status_string", "kda_last_error_message"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -68,6 +68,37 @@ def test_chunk_fwd_rejects_before_launch(lib, kw, status, needle):
     st = _fwd(lib, **kw)
     assert st == status
     assert needle in lib.kda_last_error_message().decode()
+
+
+def _pro(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, lb=-5.0, eps=1e-6,
+             s0=None, cu=None, B=1, T=64, H=2, Dk=128, Dv=128, N=1, chunk=0, scale=1.0,
+             dtype=kda.KDA_BF16, o=ctypes.c_void_p(0x2000), sT=None, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_prologue(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"], a["dt_bias"],
+                                      a["lb"], a["eps"], a["s0"], a["cu"], a["B"], a["T"], a["H"], a["Dk"],
+                                      a["Dv"], a["N"], a["chunk"], a["scale"], a["dtype"], a["o"], a["sT"],
+                                      a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(A_log=None), kda.KDA_ERR_INVALID_ARG, "A_log"),
+    (dict(dt_bias=None), kda.KDA_ERR_INVALID_ARG, "dt_bias"),
+    (dict(lb=0.0), kda.KDA_ERR_INVALID_ARG, "gate_lower_bound"),
+    (dict(lb=float("nan")), kda.KDA_ERR_INVALID_ARG, "gate_lower_bound"),
+    (dict(lb=float("-inf")), kda.KDA_ERR_INVALID_ARG, "gate_lower_bound"),
+    (dict(eps=0.0), kda.KDA_ERR_INVALID_ARG, "l2_eps"),
+    (dict(eps=float("nan")), kda.KDA_ERR_INVALID_ARG, "l2_eps"),
+    (dict(q=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(Dk=96), kda.KDA_ERR_UNSUPPORTED, "head dims"),
+    (dict(N=2), kda.KDA_ERR_INVALID_ARG, "N must equal B"),
+    (dict(o=FAKE), kda.KDA_ERR_INVALID_ARG, "alias"),
+])
+def test_chunk_fwd_prologue_rejects_before_launch(lib, kw, status, needle):
+    st = _pro(lib, **kw)
+    assert st == status
+    msg = lib.kda_last_error_message().decode()
+    assert needle in msg and msg.startswith("kda_chunk_fwd_prologue")
 
 
 def _step(lib, **kw):
