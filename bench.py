@@ -17,7 +17,9 @@ Prints one JSON line. ``value`` is tokens/s of the forward (T / seconds per
 step). ``roofline`` is for the chunk kernel: algorithmic HBM bytes per launch
 (q,k,v,g,o at 256 B per token-head each, beta at 2 B, the fp32 final state)
 over its average launch time, measured with HIP events on the launch stream.
-``mfma`` gives the same launches against the bf16 dense matrix-core peak with
+``prologue`` times the same forward from raw projections with the gate, beta
+and L2-normalisation prologue fused into the chunk kernel
+(kda_chunk_fwd_prologue). ``mfma`` gives the same launches against the bf16 dense matrix-core peak with
 the algorithmic flop count of the chunk form at C=64 counted over full tiles,
 a fixed count that does not depend on the chunk size the kernel uses. ``decode`` times kda_recurrent_step on
 256 rows x 96 heads against an fp32 state cache (HBM-bound). ``cpu_baseline``
@@ -62,14 +64,15 @@ def kernel_source_hash():
     return hashlib.sha256(open(CHUNK_KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic():
+def read_traffic(key="traffic_bytes_per_launch"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; otherwise None."""
+    was taken on the current kernel source; otherwise None. ``key`` selects the
+    plain kernel's or the prologue kernel's figure."""
     if not os.path.exists(TRAFFIC_SUMMARY):
         return None
     text = open(TRAFFIC_SUMMARY).read()
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
-    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_val = re.search(r"(?m)^" + key + r":\s*([0-9.eE+]+)", text)
     if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_val.group(1))
@@ -142,6 +145,41 @@ def bench_forward(steps, warmup):
     if not (torch.isfinite(o.float()).all() and torch.isfinite(fin).all()):
         raise RuntimeError("non-finite forward output")
     return w, wall, per, batch
+
+
+def bench_prologue(steps, warmup):
+    """The same forward from raw projections with the gate, beta and L2-norm
+    prologue fused into the chunk kernel (kda_chunk_fwd_prologue)."""
+    w = synth.WORKLOADS["k3_t4096"]
+    dev = torch.device("cuda:0")
+    sets = []
+    for s in range(2):
+        inp = synth.make_prologue_inputs(w.B, w.T, w.H, w.Dk, w.Dv, seed=w.seed + 1000 * s, dtype=w.dtype)
+        sets.append({k: (None if v is None else v.to(dev)) for k, v in inp.items()})
+    o = torch.empty((w.B, w.T, w.H, w.Dv), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        d = sets[i % 2]
+        kda.chunk_fwd_prologue(d["q_raw"], d["k_raw"], d["v"], d["g_logit"], d["beta_logit"], d["A_log"],
+                               d["dt_bias"], gate_lower_bound=synth.GATE_LOWER_BOUND, l2_eps=1e-6,
+                               out=o, final_state=fin)
+
+    wall, per, batch = time_launches(step, steps, warmup, stream)
+    if not (torch.isfinite(o.float()).all() and torch.isfinite(fin).all()):
+        raise RuntimeError("non-finite prologue forward output")
+    kern_ms = float(batch)
+    # the raw projections have the inputs' sizes; A_log and dt_bias add 4 B per channel
+    nbytes = fwd_bytes(w.T, w.H, w.Dk, w.Dv, n_states_out=1) + 4 * w.Dk * (1 + w.H)
+    gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    return {"workload": "k3_t4096 from raw projections: q, k unnormalised, gate and beta logits, "
+                        "A_log [128], dt_bias [96*128]; gate lb*sigmoid(exp(A_log)*(logit+dt_bias)), lb=-5, "
+                        "L2 eps 1e-6",
+            "ms_per_step": wall / steps * 1e3, "tokens_per_s": w.T / (wall / steps), "kernel_ms": kern_ms,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": read_traffic("prologue_traffic_bytes_per_launch")},
+            "algorithmic_bytes_per_launch": nbytes}
 
 
 def bench_decode(steps, warmup):
@@ -266,6 +304,7 @@ def main():
                           "T*H*(2*64*(3*d_k+2*d_v)+6*d_k*d_v), whatever chunk the kernel uses"},
         "published_baseline": "none: the source pages report no KDA throughput on any hardware",
     }
+    line["prologue"] = bench_prologue(args.steps, args.warmup)
     if not args.no_decode:
         line["decode"] = bench_decode(args.steps, args.warmup)
     if not args.no_cpu_baseline:

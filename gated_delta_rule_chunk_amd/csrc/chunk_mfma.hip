@@ -112,9 +112,12 @@ constexpr int FS_STRIDE = 20;                  // row stride (floats) of the sub
 constexpr int FS_BYTES = 16 * FS_STRIDE * 4;
 constexpr int S_FS = S_HO + 2 * kNR * HO_BYTES; // per finishing wave: [16][FS_STRIDE] f32 (row-wise N)
 // ints: d1 stored [4 (pair, half)], hand-over stored [4], chunk-1 shares of half 1 [2 pair],
-// M2/P2 shares [4 (pair, half)], A/B shares [4 (pair, half)]
-constexpr int S_FLAG = S_FS + 2 * kNR * FS_BYTES;
-constexpr int F_D1 = 0, F_HO = 4, F_SH1 = 8, F_SH2 = 10, F_SHAB = 14, N_FLAGS = 18;
+// M2/P2 shares [4 (pair, half)], A/B shares [4 (pair, half)],
+// prologue: per preparation wave, (sum k^2, sum q^2) of its channel half per token: [8][16] f32x2
+constexpr int S_NRM = S_FS + 2 * kNR * FS_BYTES;
+constexpr int S_FLAG = S_NRM + 8 * 16 * 8;
+// (prologue) norm partials [8 preparation waves]
+constexpr int F_D1 = 0, F_HO = 4, F_SH1 = 8, F_SH2 = 10, F_SHAB = 14, F_NRM = 18, N_FLAGS = 26;
 constexpr int LDS_BYTES = S_FLAG + 4 * N_FLAGS;
 static_assert(LDS_BYTES <= 163840, "LDS budget");
 
@@ -273,16 +276,38 @@ __device__ __forceinline__ void load_kq(ChunkRegs& R, const Stream& sq, const St
 
 // Gamma = cumulative log-decay of tiles 2m, 2m+1 of one chunk's channel half,
 // scaled by log2(e) for the base-2 exponential (lane (li, lg): token li,
-// channels 16t + 4lg + j; index 2m + hf).
+// channels 16t + 4lg + j; index 2m + hf). g is the loaded log-decay, or with
+// the prologue the gate lb * sigmoid(A (logit + b)) of the loaded logits, formed
+// on the transposed tile (one channel per lane) and scanned in two bf16 parts
+// (hi + lo) so that Gamma keeps float32 accuracy; rows at or past rows_left
+// (the sequence end) get g = 0.
+template <bool kPro>
 __device__ __forceinline__ void gamma_tiles(const ChunkRegs& R, int m, int gaddr, const bf16x8 (&eyeN)[2],
-                                            const bf16x4& lowT, f32x4 (&x)[4]) {
+                                            const bf16x4& lowT, f32x4 (&x)[4], const f32x4& nA,
+                                            const f32x4& nAb, float lbl2e, int rows_left, int lg) {
     const bf16x8 gop = gather8(R.g[m], gaddr);   // operand order: row li, channels 32kk+8lg+s
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
+        const int u = 2 * m + hf;
         // g^T tile (channel 16t+li, tokens 4lg+j), then Gamma = L * g on the
         // matrix cores: lane gets Gamma[token li][channel 16t+4lg+j]
         const f32x4 gT = mfma32(gop, eyeN[hf], zero4());
-        x[2 * m + hf] = mfma16(pack4v(gT), lowT, zero4()) * kLog2e;
+        if constexpr (!kPro) {
+            x[u] = mfma16(pack4v(gT), lowT, zero4()) * kLog2e;
+        } else {
+            // sigmoid(A (logit + b)) = 1 / (1 + 2^(nA logit + nAb)), nA = -log2(e) A
+            f32x4 sg;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(gT[j], nA[u], nAb[u]));
+                sg[j] = (4 * lg + j < rows_left) ? __builtin_amdgcn_rcpf(1.f + e) : 0.f;
+            }
+            const bf16x4 hi = pack4v(sg);
+            f32x4 lo;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) lo[j] = sg[j] - (float)hi[j];
+            x[u] = mfma16(pack4v(lo), lowT, mfma16(hi, lowT, zero4())) * lbl2e;
+        }
     }
 }
 __device__ __forceinline__ f32x4 exp2v(const f32x4& x) {
@@ -302,13 +327,22 @@ __device__ __forceinline__ void kq_tiles(const ChunkRegs& R, int m, int gaddr, c
     }
 }
 
+// beta from its loaded bits: the value, or with the prologue sigmoid(logit)
+template <bool kPro>
+__device__ __forceinline__ float beta_value(uint32_t bits) {
+    const float b = bf16_bits_to_f32(bits);
+    if constexpr (kPro) return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-b * kLog2e));
+    return b;
+}
+
 // T Diag(beta) of one chunk from the summed M (row li, columns 4lg+j);
-// beta_bits holds beta of row lane/4; fs is the wave's 1 KiB scratch.
+// beta_bits holds beta (or its logit) of row lane/4; fs is the wave's scratch.
+template <bool kPro>
 __device__ __forceinline__ bf16x4 inverse_times_beta(const f32x4& Mr, uint32_t beta_bits, char* fs, int li, int lg) {
-    const float beta_li = bf16_bits_to_f32(gather(beta_bits, 16 * li));
+    const float beta_li = beta_value<kPro>(gather(beta_bits, 16 * li));
     f32x4 bj;   // beta of rows 4lg+j
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bj[j] = bf16_bits_to_f32(gather(beta_bits, 16 * (4 * lg + j)));
+    for (int j = 0; j < 4; ++j) bj[j] = beta_value<kPro>(gather(beta_bits, 16 * (4 * lg + j)));
     f32x4 Nr, Tr;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -367,7 +401,57 @@ struct PrepCtx {
     char* fs;
     int epoch, pq, ph, li, lg;
     int gaddr;         // gather address from the load order: 4 * (lg + 4 li)
+    // prologue
+    f32x4 nA, nAb;     // per tile u of this half (channel 16(4ph+u)+li): -log2(e) exp(A_log), times dt_bias
+    float lbl2e;       // gate_lower_bound * log2(e)
+    float l2_eps;
+    int rows_left;     // rows of this chunk before the sequence end (may be <= 0 or >= 16)
+    char* nrm;         // norm partials of the preparation waves
+    int pw;            // this preparation wave
 };
+
+// k, q of all four tiles as fp32 (lane (li, lg): token li, channels
+// 16t + 4lg + j); with the prologue, scaled to unit length per token: each
+// half sums its 64 channels' squares, the two halves of the same chunk swap
+// their sums through LDS, and both scale by 1 / sqrt(total + eps).
+template <bool kPro>
+__device__ __forceinline__ void kq_all(const ChunkRegs& R, const PrepCtx& c, const bf16x8 (&eyeN)[2],
+                                       f32x4 (&kf)[4], f32x4 (&qf)[4]) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        f32x4 k2[2], q2[2];
+        kq_tiles(R, m, c.gaddr, eyeN, k2, q2);
+        kf[2 * m] = k2[0]; kf[2 * m + 1] = k2[1];
+        qf[2 * m] = q2[0]; qf[2 * m + 1] = q2[1];
+    }
+    if constexpr (kPro) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sk = fmaf(kf[u][j], kf[u][j], sk);
+                sq = fmaf(qf[u][j], qf[u][j], sq);
+            }
+        // over the four lane groups (channel groups) of token li
+        sk += __shfl_xor(sk, 16);
+        sq += __shfl_xor(sq, 16);
+        sk += __shfl_xor(sk, 32);
+        sq += __shfl_xor(sq, 32);
+        // the four lanes of a token store the same pair
+        *reinterpret_cast<f32x2*>(c.nrm + 128 * c.pw + 8 * c.li) = f32x2{sk, sq};
+        set_flag(c.flags + F_NRM + c.pw, c.epoch);
+        wait_flag(c.flags + F_NRM + (c.pw ^ 1), c.epoch);
+        const f32x2 other = *reinterpret_cast<const f32x2*>(c.nrm + 128 * (c.pw ^ 1) + 8 * c.li);
+        const float rk = __builtin_amdgcn_rsqf(sk + other[0] + c.l2_eps);
+        const float rq = __builtin_amdgcn_rsqf(sq + other[1] + c.l2_eps);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            kf[u] = kf[u] * rk;
+            qf[u] = qf[u] * rq;
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Chunk-1 wave of channel half ph of a pair (wave-local; lane = (li, lg));
@@ -377,14 +461,15 @@ struct PrepCtx {
 // and -P1; half 1 stores its share of them, then forms the chunk-2 factors
 // (T2 Diag(beta2), -P2, -A, -B) from the chunk-2 waves' shares.
 // ---------------------------------------------------------------------------
-template <typename Issue>
+template <bool kPro, typename Issue>
 __device__ __forceinline__ void prepare_chunk1(const ChunkRegs& R, const PrepCtx& c, const bf16x8 (&eyeN)[2],
                                                const bf16x4& lowT, Issue&& issue) {
     const int lane = c.li + 16 * c.lg;
     issue(0);
     f32x4 x[4], el[4], enl[4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) gamma_tiles(R, m, c.gaddr, eyeN, lowT, x);
+    for (int m = 0; m < 2; ++m)
+        gamma_tiles<kPro>(R, m, c.gaddr, eyeN, lowT, x, c.nA, c.nAb, c.lbl2e, c.rows_left, c.lg);
     // d1 first (the chunk-2 wave waits for it): token 15 carries it; the other
     // lanes store to the sink (a store under an exec mask would split the
     // schedule)
@@ -397,21 +482,22 @@ __device__ __forceinline__ void prepare_chunk1(const ChunkRegs& R, const PrepCtx
 #pragma unroll
     for (int u = 0; u < 4; ++u) enl[u] = exp2v(-x[u]);
     issue(1);
+    f32x4 kf[4], qf[4];
+    kq_all<kPro>(R, c, eyeN, kf, qf);
     f32x4 Ms = zero4(), Ps = zero4();
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
         const int kk = 2 * c.ph + m;
-        f32x4 kf[2], qf[2], ka[2], qa[2], kb[2], kh[2];
-        kq_tiles(R, m, c.gaddr, eyeN, kf, qf);
+        f32x4 ka[2], qa[2], kb[2], kh[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int u = 2 * m + hf;
             f32x4 d1;   // e^Gamma of token 15, from lane 15 of the row
 #pragma unroll
             for (int j = 0; j < 4; ++j) d1[j] = row_bcast<15>(el[u][j]);
-            ka[hf] = kf[hf] * el[u];
-            qa[hf] = qf[hf] * el[u];
-            kb[hf] = kf[hf] * enl[u];
+            ka[hf] = kf[u] * el[u];
+            qa[hf] = qf[u] * el[u];
+            kb[hf] = kf[u] * enl[u];
             kh[hf] = kb[hf] * d1;
         }
         const bf16x8 KA = pack_pair(ka[0], ka[1]);
@@ -432,7 +518,7 @@ __device__ __forceinline__ void prepare_chunk1(const ChunkRegs& R, const PrepCtx
         wait_flag(c.flags + F_SH1 + pp, c.epoch);
         const f32x4 Mr = Ms + lds4(c.sh + SH_M1 * 1024 + 16 * lane);
         const f32x4 Pr = Ps + lds4(c.sh + SH_P1 * 1024 + 16 * lane);
-        *reinterpret_cast<bf16x4*>(c.slot + S_TT1 + 8 * lane) = inverse_times_beta(Mr, R.beta, c.fs, c.li, c.lg);
+        *reinterpret_cast<bf16x4*>(c.slot + S_TT1 + 8 * lane) = inverse_times_beta<kPro>(Mr, R.beta, c.fs, c.li, c.lg);
         *reinterpret_cast<bf16x4*>(c.slot + S_PN1 + 8 * lane) = pack4v(neg_lower(Pr, c.li, c.lg));
     } else {
         *reinterpret_cast<f32x4*>(c.sh + SH_M1 * 1024 + 16 * lane) = Ms;
@@ -444,7 +530,7 @@ __device__ __forceinline__ void prepare_chunk1(const ChunkRegs& R, const PrepCtx
         wait_flag(c.flags + F_SH2 + 2 * pp + 1, c.epoch);
         const f32x4 M2 = lds4(c.sh + SH_M2 * 1024 + 16 * lane) + lds4(c.sh + (SH_M2 + 1) * 1024 + 16 * lane);
         const f32x4 P2 = lds4(c.sh + SH_P2 * 1024 + 16 * lane) + lds4(c.sh + (SH_P2 + 1) * 1024 + 16 * lane);
-        *reinterpret_cast<bf16x4*>(c.slot + S_TT2 + 8 * lane) = inverse_times_beta(M2, R.beta, c.fs, c.li, c.lg);
+        *reinterpret_cast<bf16x4*>(c.slot + S_TT2 + 8 * lane) = inverse_times_beta<kPro>(M2, R.beta, c.fs, c.li, c.lg);
         wait_flag(c.flags + F_SHAB + 2 * pp, c.epoch);
         wait_flag(c.flags + F_SHAB + 2 * pp + 1, c.epoch);
         const f32x4 Ar = lds4(c.sh + SH_A * 1024 + 16 * lane) + lds4(c.sh + (SH_A + 1) * 1024 + 16 * lane);
@@ -459,31 +545,32 @@ __device__ __forceinline__ void prepare_chunk1(const ChunkRegs& R, const PrepCtx
 // operand and this half's shares of M2, P2 (stored as soon as they are
 // formed) and of A, B.
 // ---------------------------------------------------------------------------
-template <typename Issue>
+template <bool kPro, typename Issue>
 __device__ __forceinline__ void prepare_chunk2(const ChunkRegs& R, const PrepCtx& c, const bf16x8 (&eyeN)[2],
                                                const bf16x4& lowT, Issue&& issue) {
     const int lane = c.li + 16 * c.lg;
     f32x4 x[4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) gamma_tiles(R, m, c.gaddr, eyeN, lowT, x);
+    for (int m = 0; m < 2; ++m)
+        gamma_tiles<kPro>(R, m, c.gaddr, eyeN, lowT, x, c.nA, c.nAb, c.lbl2e, c.rows_left, c.lg);
     issue(0);   // (after the step-start burst of the other waves' loads)
     // everything that does not need d1 first: Kb2, the unscaled Kg2 and Qh2
     // (kept in fp32 for the d1 scaling) and this half's M2 and P2 shares
     bf16x8 KA[2], QA[2], KB[2];
     f32x4 ka[4], qa[4];
+    kq_all<kPro>(R, c, eyeN, ka, qa);   // k, q here; scaled by e^Gamma below
     f32x4 Ms = zero4(), Ps = zero4();
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-        f32x4 kf[2], qf[2], kb[2];
-        kq_tiles(R, m, c.gaddr, eyeN, kf, qf);
+        f32x4 kb[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int u = 2 * m + hf;
             const f32x4 el = exp2v(x[u]);
             *reinterpret_cast<f32x4*>(c.slot + S_E2 + c.eoff + 16 * (4 * c.ph + u)) = el;
-            ka[u] = kf[hf] * el;
-            qa[u] = qf[hf] * el;
-            kb[hf] = kf[hf] * exp2v(-x[u]);
+            kb[hf] = ka[u] * exp2v(-x[u]);
+            ka[u] = ka[u] * el;
+            qa[u] = qa[u] * el;
         }
         KA[m] = pack_pair(ka[2 * m], ka[2 * m + 1]);
         QA[m] = pack_pair(qa[2 * m], qa[2 * m + 1]);
@@ -545,6 +632,7 @@ __device__ __forceinline__ void prepare_chunk2(const ChunkRegs& R, const PrepCtx
 }
 
 
+template <bool kPro>
 __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
 
@@ -637,6 +725,23 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         ctx.pq = pq;
         ctx.ph = ph;
         ctx.gaddr = 4 * (lg + 4 * li);
+        ctx.nrm = smem + S_NRM;
+        ctx.pw = pw;
+        ctx.nA = zero4();
+        ctx.nAb = zero4();
+        ctx.lbl2e = 0.f;
+        ctx.l2_eps = 0.f;
+        if constexpr (kPro) {
+            // this lane's channel of tile u of the half: 64 ph + 16 u + li
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int ch = 64 * ph + 16 * u + li;
+                ctx.nA[u] = -kLog2e * __expf(a.A_log[ch]);
+                ctx.nAb[u] = ctx.nA[u] * a.dt_bias[h * kDK + ch];
+            }
+            ctx.lbl2e = a.gate_lb * kLog2e;
+            ctx.l2_eps = a.l2_eps;
+        }
         ctx.li = li;
         ctx.lg = lg;
         // The next group's loads go out in three parts between the phases of
@@ -673,6 +778,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
                 };
                 ctx.slot = smem + ((it & 1) * kNR + pp) * SLOT;
                 ctx.epoch = it + 1;
+                ctx.rows_left = (int)(len - (int64_t)it * (kNA * kC)) - kC * (2 * pp + pc);
                 prepare(cur, issue);
                 group_barrier();
             };
@@ -686,9 +792,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
             if (it < ngroups) step(it, R0, R1);
         };
         if (pc == 0)
-            run([&](const ChunkRegs& cur, auto&& issue) { prepare_chunk1(cur, ctx, eyeN, lowT, issue); });
+            run([&](const ChunkRegs& cur, auto&& issue) { prepare_chunk1<kPro>(cur, ctx, eyeN, lowT, issue); });
         else
-            run([&](const ChunkRegs& cur, auto&& issue) { prepare_chunk2(cur, ctx, eyeN, lowT, issue); });
+            run([&](const ChunkRegs& cur, auto&& issue) { prepare_chunk2<kPro>(cur, ctx, eyeN, lowT, issue); });
         group_barrier();   // the state waves' last group
     } else {
         // ========================== state wave ===============================
@@ -837,13 +943,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
 
 }  // namespace
 
+// The 16-row chunk needs every g >= -5 (|Gamma| <= 80); with the prologue
+// the gate is bounded below by gate_lb.
 bool chunk_mfma_supported(const ChunkArgs& a) {
-    return a.bf16 && a.Dk == kDK && a.Dv == kDV && !a.prologue;
+    return a.bf16 && a.Dk == kDK && a.Dv == kDV && (!a.prologue || a.gate_lb >= -5.f);
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t s) {
     const int units = a.N * a.H;
-    hipLaunchKernelGGL(chunk_mfma_kernel, dim3((unsigned)(units * kNVT)), dim3(kThreads), 0, s, a);
+    if (a.prologue)
+        hipLaunchKernelGGL(chunk_mfma_kernel<true>, dim3((unsigned)(units * kNVT)), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(chunk_mfma_kernel<false>, dim3((unsigned)(units * kNVT)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
