@@ -263,3 +263,78 @@ int kda_ref_prologue_forward(const float* q_raw, const float* k_raw, const float
     }
     return failed ? -1 : 0;
 }
+
+/*
+ * Short causal depthwise convolution over time (kernel 4), the step before the
+ * KDA projections enter the recurrence (hysenlabs "kimi-k3-mlx", section
+ * "Attention is 93 layers ...": a short convolution with kernel size 4 on the
+ * query, key and value projections). Per sequence n and channel c, with the
+ * window ending at token t:
+ *   y[t][c] = sum_{i=0..3} w[c][i] * x[t - 3 + i][c]
+ * where x before the sequence's first token comes from the conv state
+ * (state[n][j][c] holds x[-3 + j]) or is 0 without one; then, with
+ * activation = 1, y <- y * sigmoid(y). The final conv state holds the last
+ * three inputs of the window (x[L-3 .. L-1], reaching into the initial state
+ * when L < 3). x, y [B,T,C]; w [C][4]; states [N][3][C]. Returns 0, or -1 on
+ * bad arguments.
+ */
+int kda_ref_short_conv(const float* x, const float* w, const float* state_in, const int64_t* cu_seqlens,
+                       int64_t N, int64_t B, int64_t T, int64_t C, int activation, double* y,
+                       double* state_out)
+{
+    if (!x || !w || !y || B < 1 || T < 0 || C < 1 || (activation != 0 && activation != 1)) return -1;
+    if (cu_seqlens) {
+        if (B != 1 || N < 1 || cu_seqlens[0] != 0 || cu_seqlens[N] != T) return -1;
+        for (int64_t n = 0; n < N; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+    } else {
+        N = B;
+    }
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t b = cu_seqlens ? 0 : n;
+        const int64_t bos = cu_seqlens ? cu_seqlens[n] : 0;
+        const int64_t L = (cu_seqlens ? cu_seqlens[n + 1] : T) - bos;
+        for (int64_t c = 0; c < C; ++c) {
+            /* the input sequence extended by the three state values in front */
+            #define XIN(tau) ((tau) >= 0 ? (double)x[((b * T) + bos + (tau)) * C + c] \
+                              : (state_in ? (double)state_in[(n * 3 + (3 + (tau))) * C + c] : 0.0))
+            for (int64_t t = 0; t < L; ++t) {
+                double acc = 0.0;
+                for (int i = 0; i < 4; ++i) acc += (double)w[c * 4 + i] * XIN(t - 3 + i);
+                if (activation) acc = acc / (1.0 + exp(-acc));
+                y[((b * T) + bos + t) * C + c] = acc;
+            }
+            if (state_out)
+                for (int j = 0; j < 3; ++j) state_out[(n * 3 + j) * C + c] = XIN(L - 3 + j);
+            #undef XIN
+        }
+    }
+    return 0;
+}
+
+/*
+ * One decode step of the convolution: row r (one token) reads and updates
+ * cache[slot(r)] ([3][C], the last three inputs), slot(r) = slots ? slots[r] : r.
+ * x, y [Nb][C]; cache [n_slots][3][C] (double, updated in place).
+ */
+int kda_ref_short_conv_step(const float* x, const float* w, double* cache, const int64_t* slots,
+                            int64_t n_slots, int64_t Nb, int64_t C, int activation, double* y)
+{
+    if (!x || !w || !cache || !y || Nb < 0 || C < 1 || (activation != 0 && activation != 1)) return -1;
+    for (int64_t r = 0; r < Nb; ++r) {
+        const int64_t s = slots ? slots[r] : r;
+        if (s < 0 || s >= n_slots) return -1;
+        double* st = cache + s * 3 * C;
+        for (int64_t c = 0; c < C; ++c) {
+            const double win[4] = {st[c], st[C + c], st[2 * C + c], (double)x[r * C + c]};
+            double acc = 0.0;
+            for (int i = 0; i < 4; ++i) acc += (double)w[c * 4 + i] * win[i];
+            if (activation) acc = acc / (1.0 + exp(-acc));
+            y[r * C + c] = acc;
+            st[c] = win[1];
+            st[C + c] = win[2];
+            st[2 * C + c] = win[3];
+        }
+    }
+    return 0;
+}

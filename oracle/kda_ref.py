@@ -117,6 +117,34 @@ def prologue(q_raw, k_raw, g_logit, beta_logit, A_log, dt_bias, gate_lower_bound
     return q, k, g, beta
 
 
+def short_conv(x, w, state=None, cu_seqlens=None, activation=False):
+    """Short causal depthwise convolution (kernel 4) over time, float64.
+
+    The pages say KDA applies a short convolution with kernel size 4 on the
+    query, key and value projections (hysenlabs "kimi-k3-mlx", section
+    "Attention is 93 layers split between KDA and a NoPE gated MLA"); they give
+    no formula, weights layout or activation. The reading implemented:
+    y[t] = sum_i w[:, i] * x[t - 3 + i] per channel, inputs before a sequence's
+    start taken from ``state`` ([N, 3, C]: x[-3], x[-2], x[-1]) or zero, then
+    y * sigmoid(y) if ``activation``. x [B, T, C]; w [C, 4]. Returns (y, final
+    state [N, 3, C]: the last three inputs of each sequence's window).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    B, T, C = x.shape
+    segs = _segments(B, T, cu_seqlens)
+    st0 = None if state is None else np.asarray(state, dtype=np.float64)
+    y = np.zeros_like(x)
+    fin = np.zeros((len(segs), 3, C))
+    for n, (b, bos, eos) in enumerate(segs):
+        ext = np.concatenate([st0[n] if st0 is not None else np.zeros((3, C)), x[b, bos:eos]], axis=0)
+        for t in range(eos - bos):
+            acc = (w * ext[t:t + 4].T).sum(-1)          # window x[t-3 .. t]
+            y[b, bos + t] = acc / (1.0 + np.exp(-acc)) if activation else acc
+        fin[n] = ext[-3:]
+    return y, fin
+
+
 def decode_step(q, k, v, g, beta, state_cache, state_slots=None, scale=1.0):
     """One decode step against a state cache. Returns (o [Nb,H,Dv], new cache copy).
 
@@ -162,6 +190,10 @@ def load_c():
         lib.kda_ref_prologue_forward.argtypes = [P, P, P, P, P, P, P, D, D, P, P, I, I, I, I, I, I,
                                                  D, P, P, ctypes.c_int]
         lib.kda_ref_prologue_forward.restype = ctypes.c_int
+        lib.kda_ref_short_conv.argtypes = [P, P, P, P, I, I, I, I, ctypes.c_int, P, P]
+        lib.kda_ref_short_conv.restype = ctypes.c_int
+        lib.kda_ref_short_conv_step.argtypes = [P, P, P, P, I, I, I, ctypes.c_int, P]
+        lib.kda_ref_short_conv_step.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -226,6 +258,42 @@ def c_prologue_forward(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, gat
     if rc != 0:
         raise ValueError("kda_ref_prologue_forward rejected its arguments")
     return o, final
+
+
+def c_short_conv(x, w, state=None, cu_seqlens=None, activation=False):
+    """The C oracle's short convolution (same contract as ``short_conv``)."""
+    lib = load_c()
+    x, w = _f32(x), _f32(w)
+    B, T, C = x.shape
+    cu = None
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64).reshape(-1))
+        N = cu.size - 1
+    else:
+        N = B
+    st = None if state is None else _f32(state)
+    y = np.zeros((B, T, C))
+    fin = np.zeros((N, 3, C))
+    if lib.kda_ref_short_conv(_ptr(x), _ptr(w), _ptr(st), _ptr(cu), N, B, T, C, int(bool(activation)),
+                              _ptr(y), _ptr(fin)) != 0:
+        raise ValueError("kda_ref_short_conv rejected its arguments")
+    return y, fin
+
+
+def c_short_conv_step(x, w, cache, slots=None, activation=False):
+    """One decode step of the C oracle's convolution; ``cache`` (float64
+    [n_slots, 3, C], C-contiguous) is updated in place. Returns y [Nb, C]."""
+    lib = load_c()
+    if cache.dtype != np.float64 or not cache.flags["C_CONTIGUOUS"]:
+        raise TypeError("cache must be a C-contiguous float64 array")
+    x, w = _f32(x), _f32(w)
+    Nb, C = x.shape
+    sl = None if slots is None else np.ascontiguousarray(np.asarray(slots, dtype=np.int64))
+    y = np.zeros((Nb, C))
+    if lib.kda_ref_short_conv_step(_ptr(x), _ptr(w), _ptr(cache), _ptr(sl), cache.shape[0], Nb, C,
+                                   int(bool(activation)), _ptr(y)) != 0:
+        raise ValueError("kda_ref_short_conv_step rejected its arguments")
+    return y
 
 
 def c_decode_step(q, k, v, g, beta, state_cache, state_slots=None, scale=1.0, nthreads=0):
