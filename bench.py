@@ -19,7 +19,9 @@ step). ``roofline`` is for the chunk kernel: algorithmic HBM bytes per launch
 over its average launch time, measured with HIP events on the launch stream.
 ``prologue`` times the same forward from raw projections with the gate, beta
 and L2-normalisation prologue fused into the chunk kernel
-(kda_chunk_fwd_prologue). ``mfma`` gives the same launches against the bf16 dense matrix-core peak with
+(kda_chunk_fwd_prologue). ``short_conv`` times the kernel-4 convolution of the
+q, k and v projections (kda_short_conv) and the chain convolution ->
+prologue forward. ``mfma`` gives the same launches against the bf16 dense matrix-core peak with
 the algorithmic flop count of the chunk form at C=64 counted over full tiles,
 a fixed count that does not depend on the chunk size the kernel uses. ``decode`` times kda_recurrent_step on
 256 rows x 96 heads against an fp32 state cache (HBM-bound). ``cpu_baseline``
@@ -182,6 +184,53 @@ def bench_prologue(steps, warmup):
             "algorithmic_bytes_per_launch": nbytes}
 
 
+def bench_conv(steps, warmup):
+    """The short causal convolution (kernel 4, SiLU) of the q, k and v
+    projections at k3_t4096 (kda_short_conv, three launches per step), and the
+    chain convolution -> fused-prologue forward."""
+    w = synth.WORKLOADS["k3_t4096"]
+    dev = torch.device("cuda:0")
+    C = w.H * w.Dk
+    sets = []
+    for s in range(2):
+        inp = synth.make_prologue_inputs(w.B, w.T, w.H, w.Dk, w.Dv, seed=w.seed + 1000 * s, dtype=w.dtype)
+        sets.append({k: (None if v is None else v.to(dev)) for k, v in inp.items()})
+    rng = np.random.default_rng(w.seed)
+    weights = [torch.from_numpy((0.5 * rng.standard_normal((C, 4))).astype(np.float32)).to(dev) for _ in range(3)]
+    ys = [torch.empty((w.B, w.T, w.H, w.Dk), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    states = [torch.empty((w.B, 3, C), dtype=torch.float32, device=dev) for _ in range(3)]
+    o = torch.empty((w.B, w.T, w.H, w.Dv), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def conv(i):
+        d = sets[i % 2]
+        for j, name in enumerate(("q_raw", "k_raw", "v")):
+            kda.short_conv(d[name], weights[j], activation=True, out=ys[j], final_state=states[j])
+
+    def chain(i):
+        conv(i)
+        d = sets[i % 2]
+        kda.chunk_fwd_prologue(ys[0], ys[1], ys[2], d["g_logit"], d["beta_logit"], d["A_log"], d["dt_bias"],
+                               gate_lower_bound=synth.GATE_LOWER_BOUND, l2_eps=1e-6, out=o, final_state=fin)
+
+    _, _, conv_ms = time_launches(conv, steps, warmup, stream)
+    wall, _, _ = time_launches(chain, steps, warmup, stream)
+    if not (torch.isfinite(o.float()).all() and torch.isfinite(fin).all()):
+        raise RuntimeError("non-finite conv chain output")
+    # per projection: x read and y written at 2 B per token-channel, the weights and the final state
+    nbytes = 3 * (2 * w.B * w.T * C * 2 + C * 4 * 4 + w.B * 3 * C * 4)
+    gbs = nbytes / (float(conv_ms) * 1e-3) / 1e9
+    return {"workload": "k3_t4096: causal depthwise conv (kernel 4, SiLU) of q, k, v, each [1,4096,96*128] bf16, "
+                        "with the final conv state",
+            "ms_per_step": float(conv_ms),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+            "algorithmic_bytes_per_step": nbytes,
+            "chain": {"steps": "conv of q, k, v then the fused-prologue forward",
+                      "ms_per_step": wall / steps * 1e3, "tokens_per_s": w.T / (wall / steps)}}
+
+
 def bench_decode(steps, warmup):
     cfg = synth.DECODE
     Nb, H, Dk, Dv = cfg["Nb"], cfg["H"], cfg["Dk"], cfg["Dv"]
@@ -305,6 +354,7 @@ def main():
         "published_baseline": "none: the source pages report no KDA throughput on any hardware",
     }
     line["prologue"] = bench_prologue(args.steps, args.warmup)
+    line["short_conv"] = bench_conv(args.steps, args.warmup)
     if not args.no_decode:
         line["decode"] = bench_decode(args.steps, args.warmup)
     if not args.no_cpu_baseline:

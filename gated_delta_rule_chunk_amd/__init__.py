@@ -58,6 +58,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_recurrent_step.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F,
                                        ctypes.c_int, P, P]
     lib.kda_recurrent_step.restype = ctypes.c_int
+    lib.kda_short_conv.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, ctypes.c_int, P, P, P]
+    lib.kda_short_conv.restype = ctypes.c_int
+    lib.kda_short_conv_step.argtypes = [P, P, P, P, I32, I32, I32, I32, ctypes.c_int, P, P]
+    lib.kda_short_conv_step.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error_message.argtypes = []
@@ -188,6 +192,82 @@ def chunk_fwd_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, gat
                                     _stream(dev))
     _check(st)
     return out, final_state
+
+
+def short_conv(x, weight, conv_state=None, cu_seqlens=None, activation=True, output_final_state=True,
+               out=None, final_state=None):
+    """Short causal depthwise convolution (kernel 4) over time (kda_short_conv).
+
+    x [B,T,C] or [B,T,H,D] (float32 or bfloat16; C = H*D); weight [C,4]
+    float32; conv_state [N,3,C] float32 or None (zeros); cu_seqlens int32
+    [N+1] (B must be 1) or None. Returns (y like x, final conv state [N,3,C]
+    float32 or None).
+    """
+    lib = load_library()
+    if x.dim() not in (3, 4):
+        raise ValueError("x must be [B,T,C] or [B,T,H,D]")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    B, T = x.shape[0], x.shape[1]
+    C = x[0, 0].numel() if T > 0 else int(torch.tensor(x.shape[2:]).prod())
+    _need(x, "x", tuple(x.shape), x.dtype, dev)
+    _need(weight, "weight", (C, 4), torch.float32, dev)
+    if cu_seqlens is not None:
+        N = cu_seqlens.numel() - 1
+        _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    else:
+        N = B
+    if conv_state is not None:
+        _need(conv_state, "conv_state", (N, 3, C), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _need(out, "out", tuple(x.shape), x.dtype, dev)
+    if output_final_state:
+        if final_state is None:
+            final_state = torch.empty((N, 3, C), dtype=torch.float32, device=dev)
+        else:
+            _need(final_state, "final_state", (N, 3, C), torch.float32, dev)
+    else:
+        final_state = None
+    st = lib.kda_short_conv(_ptr(x), _ptr(weight), _ptr(conv_state), _ptr(cu_seqlens), B, T, C, N,
+                            int(bool(activation)), _DTYPES[x.dtype], _ptr(out), _ptr(final_state), _stream(dev))
+    _check(st)
+    return out, final_state
+
+
+def short_conv_step(x, weight, conv_cache, cache_slots=None, activation=True, out=None):
+    """One decode step of the short convolution (kda_short_conv_step).
+
+    x [Nb,C] or [Nb,H,D]; weight [C,4] float32; conv_cache [n_slots,3,C]
+    float32 (updated in place); cache_slots int32 [Nb] or None. Returns y like x.
+    """
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    Nb = x.shape[0]
+    C = conv_cache.shape[-1]
+    _need(x, "x", tuple(x.shape), x.dtype, dev)
+    if x[0].numel() != C if Nb > 0 else False:
+        raise ValueError("x's channels must match conv_cache")
+    _need(weight, "weight", (C, 4), torch.float32, dev)
+    _need(conv_cache, "conv_cache", (conv_cache.shape[0], 3, C), torch.float32, dev)
+    if cache_slots is not None:
+        _need(cache_slots, "cache_slots", (Nb,), torch.int32, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _need(out, "out", tuple(x.shape), x.dtype, dev)
+    st = lib.kda_short_conv_step(_ptr(x), _ptr(weight), _ptr(conv_cache), _ptr(cache_slots), conv_cache.shape[0],
+                                 Nb, C, int(bool(activation)), _DTYPES[x.dtype], _ptr(out), _stream(dev))
+    _check(st)
+    return out
 
 
 def recurrent_step(q, k, v, g, beta, state_cache, state_slots=None, scale=1.0, out=None):

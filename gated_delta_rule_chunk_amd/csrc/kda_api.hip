@@ -135,6 +135,74 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
     return launch_chunk(fn, a, stream);
 }
 
+kda_status kda_short_conv(const void* x, const float* weight, const float* conv_state_in,
+                          const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t C, int32_t N,
+                          int32_t activation, kda_dtype dtype, void* y, float* conv_state_out, void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_short_conv";
+    if (T > 0 && (!x || !y || !weight))
+        return fail(KDA_ERR_INVALID_ARG, "%s: x, weight and y must be non-NULL when T > 0", fn);
+    if (B < 1 || T < 0 || C < 1 || N < 0)
+        return fail(KDA_ERR_INVALID_ARG, "%s: need B >= 1, T >= 0, C >= 1, N >= 0 (got B=%d T=%d C=%d N=%d)", fn,
+                    B, T, C, N);
+    if (C % 8 != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: C=%d; the channel count must be a multiple of 8", fn, C);
+    if (activation != 0 && activation != 1)
+        return fail(KDA_ERR_INVALID_ARG, "%s: activation must be 0 (none) or 1 (SiLU), got %d", fn, activation);
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dtype %d is not KDA_F32 or KDA_BF16", fn, (int)dtype);
+    if (cu_seqlens) {
+        if (B != 1)
+            return fail(KDA_ERR_INVALID_ARG, "%s: packed sequences (cu_seqlens) need B == 1, got B=%d", fn, B);
+        if (N < 1)
+            return fail(KDA_ERR_INVALID_ARG, "%s: packed sequences need N >= 1, got N=%d", fn, N);
+    } else if (N != B) {
+        return fail(KDA_ERR_INVALID_ARG, "%s: without cu_seqlens N must equal B (N=%d, B=%d)", fn, N, B);
+    }
+    if ((int64_t)B * T > ((int64_t)1 << 31) * 16 || (int64_t)C > ((int64_t)1 << 24))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", fn);
+    if (T > 0 && y == x)
+        return fail(KDA_ERR_INVALID_ARG, "%s: y must not alias x", fn);
+    kda::ConvArgs a;
+    a.x = x; a.w = weight; a.state_in = conv_state_in; a.cu = cu_seqlens; a.y = y; a.state_out = conv_state_out;
+    a.B = B; a.T = T; a.C = C; a.N = N; a.act = activation == 1; a.bf16 = dtype == KDA_BF16;
+    if ((int64_t)B * T == 0 && !conv_state_out) return KDA_OK;
+    const hipError_t e = kda::launch_short_conv(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
+}
+
+kda_status kda_short_conv_step(const void* x, const float* weight, float* conv_cache, const int32_t* cache_slots,
+                               int32_t n_slots, int32_t Nb, int32_t C, int32_t activation, kda_dtype dtype,
+                               void* y, void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_short_conv_step";
+    if (Nb != 0 && (!x || !weight || !conv_cache || !y))
+        return fail(KDA_ERR_INVALID_ARG, "%s: x, weight, conv_cache and y must be non-NULL", fn);
+    if (Nb < 0 || C < 1 || n_slots < 0)
+        return fail(KDA_ERR_INVALID_ARG, "%s: need Nb >= 0, C >= 1, n_slots >= 0 (got %d, %d, %d)", fn, Nb, C,
+                    n_slots);
+    if (C % 8 != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: C=%d; the channel count must be a multiple of 8", fn, C);
+    if (activation != 0 && activation != 1)
+        return fail(KDA_ERR_INVALID_ARG, "%s: activation must be 0 (none) or 1 (SiLU), got %d", fn, activation);
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dtype %d is not KDA_F32 or KDA_BF16", fn, (int)dtype);
+    if (!cache_slots && Nb > n_slots)
+        return fail(KDA_ERR_INVALID_ARG, "%s: without cache_slots row r uses slot r, so Nb (%d) must be <= n_slots (%d)",
+                    fn, Nb, n_slots);
+    if ((int64_t)C > ((int64_t)1 << 24))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: C too large", fn);
+    if (Nb == 0) return KDA_OK;
+    if (y == x) return fail(KDA_ERR_INVALID_ARG, "%s: y must not alias x", fn);
+    kda::ConvStepArgs a;
+    a.x = x; a.w = weight; a.cache = conv_cache; a.slots = cache_slots; a.y = y;
+    a.Nb = Nb; a.C = C; a.act = activation == 1; a.bf16 = dtype == KDA_BF16;
+    const hipError_t e = kda::launch_short_conv_step(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
+}
+
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* g,
                               const void* beta, float* state_cache, const int32_t* state_slots,
                               int32_t n_slots, int32_t Nb, int32_t H, int32_t Dk, int32_t Dv,

@@ -45,6 +45,30 @@ struct StepArgs {
 };
 
 // Each returns hipSuccess or the launch error; they never synchronise.
+struct ConvArgs {
+    const void* x;             // [B,T,C]
+    const float* w;            // [C][4]
+    const float* state_in;     // [N][3][C] or nullptr
+    const int32_t* cu;         // [N+1] or nullptr
+    void* y;                   // [B,T,C]
+    float* state_out;          // [N][3][C] or nullptr
+    int32_t B, T, C, N;
+    bool act, bf16;
+};
+
+struct ConvStepArgs {
+    const void* x;             // [Nb][C]
+    const float* w;            // [C][4]
+    float* cache;              // [n_slots][3][C]
+    const int32_t* slots;      // [Nb] or nullptr
+    void* y;                   // [Nb][C]
+    int32_t Nb, C;
+    bool act, bf16;
+};
+
+hipError_t launch_short_conv(const ConvArgs& a, hipStream_t s);
+hipError_t launch_short_conv_step(const ConvStepArgs& a, hipStream_t s);
+
 hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t s);     // bf16, Dk=Dv=128, chunk 64
 hipError_t launch_chunk_generic(const ChunkArgs& a, hipStream_t s);  // any supported dims
 hipError_t launch_recurrent_step(const StepArgs& a, hipStream_t s);

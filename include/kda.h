@@ -121,6 +121,47 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
                                   float* final_state, void* stream);
 
 /*
+ * Short causal depthwise convolution over time (kernel size 4), the step that
+ * KDA applies to the query, key and value projections before the recurrence
+ * (hysenlabs "kimi-k3-mlx", section "Attention is 93 layers split between KDA
+ * and a NoPE gated MLA"; the pages give the kernel size only, the formula below
+ * is this library's reading). Per sequence and channel c:
+ *   y[t][c] = sum_{i=0..3} weight[c][i] * x[t - 3 + i][c]
+ * with the three inputs before a sequence's first token taken from
+ * conv_state_in, then y <- y * sigmoid(y) when activation = 1. Call it once per
+ * projection (q, k, v: C = H*Dk or H*Dv channels, the [B,T,H,D] tensor viewed
+ * as [B,T,C]).
+ *
+ *   x               [B,T,C] dtype; y [B,T,C] dtype, must not alias x
+ *   weight          [C][4] float32 (16-byte aligned rows)
+ *   conv_state_in   [N][3][C] float32: x[-3], x[-2], x[-1] of each sequence,
+ *                   or NULL for zeros
+ *   conv_state_out  [N][3][C] float32, or NULL: the last three inputs of each
+ *                   sequence's window (reaching into conv_state_in when a
+ *                   sequence has fewer than 3 tokens); may alias conv_state_in
+ *   cu_seqlens      as for kda_chunk_fwd (packed sequences, B = 1), or NULL
+ *   activation      0 = none, 1 = SiLU
+ * Supported: C a multiple of 8; dtype KDA_F32 or KDA_BF16. Errors as for
+ * kda_chunk_fwd.
+ */
+kda_status kda_short_conv(const void* x, const float* weight, const float* conv_state_in,
+                          const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t C, int32_t N,
+                          int32_t activation, kda_dtype dtype, void* y, float* conv_state_out, void* stream);
+
+/*
+ * One decode step of the short convolution: row r (one token) reads the three
+ * previous inputs from conv_cache[slot(r)] ([3][C] float32), writes
+ * y[r] = sum_i weight[c][i] * window[i] (then SiLU if activation = 1) and
+ * shifts x[r] into the cache. slot(r) = cache_slots[r], or r when cache_slots
+ * is NULL; slots must be distinct and < n_slots (not checked on the device).
+ *   x, y [Nb][C] dtype; conv_cache [n_slots][3][C] float32, updated in place.
+ * Nb = 0 is a no-op. Errors as for kda_recurrent_step.
+ */
+kda_status kda_short_conv_step(const void* x, const float* weight, float* conv_cache, const int32_t* cache_slots,
+                               int32_t n_slots, int32_t Nb, int32_t C, int32_t activation, kda_dtype dtype,
+                               void* y, void* stream);
+
+/*
  * One decode step (T = 1 per row) against a state cache, updated in place.
  *
  *   q, k, g      [Nb,H,Dk] dtype;  v [Nb,H,Dv] dtype;  beta [Nb,H] dtype

@@ -21,8 +21,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = kda.declared_symbols()
-    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step",
-                          "kda_status_string", "kda_last_error_message"}
+    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step", "kda_short_conv",
+                          "kda_short_conv_step", "kda_status_string", "kda_last_error_message"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -135,3 +135,49 @@ def test_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(1, 4, 2, 16)
     with pytest.raises(ValueError, match="GPU"):
         kda.chunk_fwd(x, x, x, x, torch.zeros(1, 4, 2))
+
+
+def _conv(lib, **kw):
+    a = dict(x=FAKE, w=FAKE, s_in=None, cu=None, B=1, T=64, C=1024, N=1, act=1, dtype=kda.KDA_BF16,
+             y=ctypes.c_void_p(0x2000), s_out=None, stream=None)
+    a.update(kw)
+    return lib.kda_short_conv(a["x"], a["w"], a["s_in"], a["cu"], a["B"], a["T"], a["C"], a["N"], a["act"],
+                              a["dtype"], a["y"], a["s_out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(w=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(C=1020), kda.KDA_ERR_UNSUPPORTED, "multiple of 8"),
+    (dict(act=2), kda.KDA_ERR_INVALID_ARG, "activation"),
+    (dict(dtype=9), kda.KDA_ERR_UNSUPPORTED, "dtype"),
+    (dict(N=3), kda.KDA_ERR_INVALID_ARG, "N must equal B"),
+    (dict(cu=FAKE, B=2, N=2), kda.KDA_ERR_INVALID_ARG, "B == 1"),
+    (dict(y=FAKE), kda.KDA_ERR_INVALID_ARG, "alias"),
+    (dict(B=0), kda.KDA_ERR_INVALID_ARG, "B >= 1"),
+])
+def test_short_conv_rejects_before_launch(lib, kw, status, needle):
+    assert _conv(lib, **kw) == status
+    assert needle in lib.kda_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(cache=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(C=12), kda.KDA_ERR_UNSUPPORTED, "multiple of 8"),
+    (dict(Nb=5), kda.KDA_ERR_INVALID_ARG, "n_slots"),
+    (dict(act=-1), kda.KDA_ERR_INVALID_ARG, "activation"),
+    (dict(y=FAKE), kda.KDA_ERR_INVALID_ARG, "alias"),
+])
+def test_short_conv_step_rejects_before_launch(lib, kw, status, needle):
+    a = dict(x=FAKE, w=FAKE, cache=FAKE, slots=None, n_slots=4, Nb=4, C=1024, act=1, dtype=kda.KDA_BF16,
+             y=ctypes.c_void_p(0x2000), stream=None)
+    a.update(kw)
+    st = lib.kda_short_conv_step(a["x"], a["w"], a["cache"], a["slots"], a["n_slots"], a["Nb"], a["C"], a["act"],
+                                 a["dtype"], a["y"], a["stream"])
+    assert st == status
+    assert needle in lib.kda_last_error_message().decode()
+
+
+def test_short_conv_step_empty_is_ok(lib):
+    st = lib.kda_short_conv_step(None, None, None, None, 0, 0, 1024, 1, kda.KDA_BF16, None, None)
+    assert st == kda.KDA_OK
