@@ -17,7 +17,7 @@
 namespace kda {
 namespace {
 
-constexpr int kRows = 16;        // tokens per thread
+constexpr int kRows = 8;         // tokens per thread
 constexpr int kThreadsConv = 256;
 
 template <typename T> struct Vec8;
@@ -103,6 +103,29 @@ __global__ __launch_bounds__(kThreadsConv) void short_conv_kernel(ConvArgs a) {
     int n;
     int64_t bos, eos;
     find_sequence(a, t0, n, bos, eos);
+    if constexpr (sizeof(T) == 2) {
+        if (t0 - bos >= 3 && t0 + kRows <= eos) {
+            // the common case: the whole block and its halo inside one sequence.
+            // All kRows + 3 rows are loaded before any is used, so the loads overlap.
+            uint4 raw[kRows + 3];
+#pragma unroll
+            for (int r = 0; r < kRows + 3; ++r)
+                raw[r] = *reinterpret_cast<const uint4*>(x + (t0 - 3 + r) * a.C + c0);
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) {
+                float f0[8], f1[8], f2[8], f3[8], out[8];
+                unpack8(raw[r], f0);
+                unpack8(raw[r + 1], f1);
+                unpack8(raw[r + 2], f2);
+                unpack8(raw[r + 3], f3);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    out[i] = activate<kAct>(fmaf(w[i][3], f3[i], fmaf(w[i][2], f2[i], fmaf(w[i][1], f1[i], w[i][0] * f0[i]))));
+                Vec8<T>::store(y + (t0 + r) * a.C + c0, out);
+            }
+            return;
+        }
+    }
     float h0[8], h1[8], h2[8];      // x[t-3], x[t-2], x[t-1]
     window_input<T>(a, x, n, bos, t0 - bos - 3, c0, h0);
     window_input<T>(a, x, n, bos, t0 - bos - 2, c0, h1);
