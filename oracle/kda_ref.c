@@ -338,3 +338,147 @@ int kda_ref_short_conv_step(const float* x, const float* w, double* cache, const
     }
     return 0;
 }
+
+/*
+ * Reverse-mode gradient of the recurrence (the forward of kda_ref_forward)
+ * for the loss  L = sum_t <d_o[t], o[t]> + <d_final, S_T>  per sequence and
+ * head, written out step by step from the forward's definition:
+ *   S' = Diag(e^g) S_{t-1};  x = S'^T k;  u = beta (v - x);  S_t = S' + k u^T;
+ *   o = scale S_t^T q.
+ * Going backward with dS (= dL/dS_t, starting from d_final or 0):
+ *   dS += scale q do^T;           dq = scale S_t do
+ *   du = dS^T k;  dk = dS u;      dbeta = du . (v - x);  dv = beta du
+ *   dx = -beta du;  dk += S' dx;  dS' = dS + k dx^T
+ *   dg = rowsum(dS' * S');        dS_{t-1} = Diag(e^g) dS'
+ * The states S_{t-1} come from a forward recomputation: one checkpoint every
+ * 64 tokens, the 64 states of a block re-run from it. Outputs (double):
+ * dq, dk, dg [B,T,H,Dk], dv [B,T,H,Dv], dbeta [B,T,H], d_initial [N,H,Dk,Dv]
+ * (may be NULL). Rows outside every sequence are left untouched. Returns 0,
+ * or -1 on bad arguments / no memory.
+ */
+int kda_ref_backward(const float* q, const float* k, const float* v, const float* g, const float* beta,
+                     const float* initial_state, const int64_t* cu_seqlens, const float* d_o,
+                     const float* d_final, int64_t N, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                     double scale, double* dq, double* dk, double* dv, double* dg, double* dbeta,
+                     double* d_initial, int nthreads)
+{
+    if (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta || B < 1 || T < 0 ||
+        H < 1 || Dk < 1 || Dv < 1)
+        return -1;
+    if (cu_seqlens) {
+        if (B != 1 || N < 1 || cu_seqlens[0] != 0 || cu_seqlens[N] != T) return -1;
+        for (int64_t n = 0; n < N; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+    } else {
+        N = B;
+    }
+    enum { BLK = 64 };
+    int failed = 0;
+    const int64_t units = N * H;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+#endif
+    for (int64_t uidx = 0; uidx < units; ++uidx) {
+        const int64_t n = uidx / H, h = uidx % H;
+        const int64_t b = cu_seqlens ? 0 : n;
+        const int64_t bos = cu_seqlens ? cu_seqlens[n] : 0;
+        const int64_t eos = cu_seqlens ? cu_seqlens[n + 1] : T;
+        const int64_t L = eos - bos, SZ = Dk * Dv;
+        const int64_t nblk = (L + BLK - 1) / BLK;
+        double* ckpt = (double*)malloc(sizeof(double) * SZ * (nblk > 0 ? nblk : 1));
+        double* states = (double*)malloc(sizeof(double) * SZ * BLK);   /* S_{t-1} of one block */
+        double* S = (double*)malloc(sizeof(double) * SZ);
+        double* dS = (double*)malloc(sizeof(double) * SZ);
+        double* Sd = (double*)malloc(sizeof(double) * SZ);
+        double* vec = (double*)malloc(sizeof(double) * (4 * Dv + 2 * Dk));
+        rows_t r = {0};
+        if (!ckpt || !states || !S || !dS || !Sd || !vec || !rows_alloc(&r, Dk, Dv)) {
+            free(ckpt); free(states); free(S); free(dS); free(Sd); free(vec); rows_free(&r);
+            failed |= 1;
+            continue;
+        }
+        double *x = vec, *u = vec + Dv, *du = vec + 2 * Dv, *dx = vec + 3 * Dv;
+        const int64_t s_off = (n * H + h) * SZ;
+        for (int64_t e = 0; e < SZ; ++e) S[e] = initial_state ? (double)initial_state[s_off + e] : 0.0;
+        /* forward: checkpoint at the start of every block */
+        for (int64_t t = 0; t < L; ++t) {
+            if (t % BLK == 0) memcpy(ckpt + (t / BLK) * SZ, S, sizeof(double) * SZ);
+            const int64_t row = (b * T + bos + t) * H + h;
+            widen(q + row * Dk, r.q, Dk); widen(k + row * Dk, r.k, Dk);
+            widen(g + row * Dk, r.g, Dk); widen(v + row * Dv, r.v, Dv);
+            kda_ref_token(S, r.x, r.q, r.k, r.v, r.g, (double)beta[row], Dk, Dv, scale, NULL);
+        }
+        for (int64_t e = 0; e < SZ; ++e) dS[e] = d_final ? (double)d_final[s_off + e] : 0.0;
+        for (int64_t blk = nblk - 1; blk >= 0; --blk) {
+            const int64_t t0 = blk * BLK, t1 = (t0 + BLK < L) ? t0 + BLK : L;
+            memcpy(S, ckpt + blk * SZ, sizeof(double) * SZ);
+            for (int64_t t = t0; t < t1; ++t) {
+                memcpy(states + (t - t0) * SZ, S, sizeof(double) * SZ);
+                const int64_t row = (b * T + bos + t) * H + h;
+                widen(q + row * Dk, r.q, Dk); widen(k + row * Dk, r.k, Dk);
+                widen(g + row * Dk, r.g, Dk); widen(v + row * Dv, r.v, Dv);
+                kda_ref_token(S, r.x, r.q, r.k, r.v, r.g, (double)beta[row], Dk, Dv, scale, NULL);
+            }
+            for (int64_t t = t1 - 1; t >= t0; --t) {
+                const int64_t row = (b * T + bos + t) * H + h;
+                widen(q + row * Dk, r.q, Dk); widen(k + row * Dk, r.k, Dk);
+                widen(g + row * Dk, r.g, Dk); widen(v + row * Dv, r.v, Dv);
+                const double bt = (double)beta[row];
+                const double* Sp = states + (t - t0) * SZ;            /* S_{t-1} */
+                const float* dot = d_o + row * Dv;
+                /* S' = Diag(e^g) S_{t-1}; x = S'^T k; u = beta (v - x) */
+                for (int64_t i = 0; i < Dk; ++i) {
+                    const double a = exp(r.g[i]);
+                    for (int64_t j = 0; j < Dv; ++j) Sd[i * Dv + j] = a * Sp[i * Dv + j];
+                }
+                for (int64_t j = 0; j < Dv; ++j) x[j] = 0.0;
+                for (int64_t i = 0; i < Dk; ++i)
+                    for (int64_t j = 0; j < Dv; ++j) x[j] += r.k[i] * Sd[i * Dv + j];
+                for (int64_t j = 0; j < Dv; ++j) u[j] = bt * (r.v[j] - x[j]);
+                /* o = scale (S' + k u^T)^T q */
+                for (int64_t i = 0; i < Dk; ++i) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < Dv; ++j) {
+                        dS[i * Dv + j] += scale * r.q[i] * (double)dot[j];
+                        acc += (Sd[i * Dv + j] + r.k[i] * u[j]) * (double)dot[j];
+                    }
+                    dq[row * Dk + i] = scale * acc;
+                }
+                /* S_t = S' + k u^T */
+                for (int64_t j = 0; j < Dv; ++j) du[j] = 0.0;
+                for (int64_t i = 0; i < Dk; ++i) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < Dv; ++j) {
+                        du[j] += dS[i * Dv + j] * r.k[i];
+                        acc += dS[i * Dv + j] * u[j];
+                    }
+                    dk[row * Dk + i] = acc;
+                }
+                double dbt = 0.0;
+                for (int64_t j = 0; j < Dv; ++j) {
+                    dbt += du[j] * (r.v[j] - x[j]);
+                    dv[row * Dv + j] = bt * du[j];
+                    dx[j] = -bt * du[j];
+                }
+                dbeta[row] = dbt;
+                /* x = S'^T k;  S' = Diag(e^g) S_{t-1} */
+                for (int64_t i = 0; i < Dk; ++i) {
+                    const double a = exp(r.g[i]);
+                    double acc = 0.0, dgi = 0.0;
+                    for (int64_t j = 0; j < Dv; ++j) {
+                        acc += Sd[i * Dv + j] * dx[j];
+                        const double dsd = dS[i * Dv + j] + r.k[i] * dx[j];
+                        dgi += dsd * Sd[i * Dv + j];
+                        dS[i * Dv + j] = a * dsd;
+                    }
+                    dk[row * Dk + i] += acc;
+                    dg[row * Dk + i] = dgi;
+                }
+            }
+        }
+        if (d_initial) memcpy(d_initial + s_off, dS, sizeof(double) * SZ);
+        free(ckpt); free(states); free(S); free(dS); free(Sd); free(vec); rows_free(&r);
+    }
+    return failed ? -1 : 0;
+}

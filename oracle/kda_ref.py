@@ -25,6 +25,9 @@ Two implementations, written separately:
     one Python-level step per token;
   * ``c_forward`` / ``c_decode_step``: the plain C loops in kda_ref.c (OpenMP
     over independent (sequence, head) units), loaded with ctypes.
+The reverse-mode gradient has the same two forms (``recurrence_backward``,
+``c_backward``); both are pinned against central finite differences of the
+forward, not against each other alone.
 The gate, beta and normalisation prologue that turns raw projections into
 (q, k, g, beta) has a NumPy form (``prologue``, then ``recurrence``) and a C
 form (``c_prologue_forward``); the reading of the gate it implements is in
@@ -88,8 +91,67 @@ def recurrence(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0)
     return o, final
 
 
+def recurrence_backward(q, k, v, g, beta, d_o, initial_state=None, d_final=None, cu_seqlens=None,
+                        scale=1.0):
+    """Reverse-mode gradient of ``recurrence`` (float64), for the scalar loss
+
+        L = sum_t <d_o[t], o[t]> + sum_n <d_final[n], S_final[n]>.
+
+    Walks each sequence backward, differentiating the three steps of
+    ``token_step`` in reverse (write, erase-read, decay) with dS = dL/dS_t:
+
+        dS  += scale q_t d_o_t^T                  (o_t = scale S_t^T q_t)
+        dq_t = scale S_t d_o_t
+        du   = dS^T k_t,   dk_t = dS u            (S_t = S' + k_t u^T)
+        dbeta_t = du . (v_t - x),   dv_t = beta_t du,   dx = -beta_t du
+        dk_t += S' dx,   dS' = dS + k_t dx^T       (x = S'^T k_t)
+        dg_t = rowsum(dS' * S'),   dS = Diag(exp g_t) dS'   (S' = Diag(exp g_t) S_{t-1})
+
+    with u = beta_t (v_t - x). States are kept from a forward pass (small
+    inputs only). Returns (dq, dk, dv, dg, dbeta, d_initial [N,H,Dk,Dv]); rows
+    outside every sequence are zero.
+    """
+    q, k, v, g, beta, d_o = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta, d_o))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    segs = _segments(B, T, cu_seqlens)
+    dq, dk, dg = (np.zeros((B, T, H, Dk)) for _ in range(3))
+    dv = np.zeros((B, T, H, Dv))
+    dbeta = np.zeros((B, T, H))
+    d_init = np.zeros((len(segs), H, Dk, Dv))
+    for n, (b, bos, eos) in enumerate(segs):
+        S = np.zeros((H, Dk, Dv)) if initial_state is None else np.array(initial_state[n], dtype=np.float64)
+        prev = []                                      # S_{t-1} for each t
+        for t in range(bos, eos):
+            prev.append(S.copy())
+            token_step(S, q[b, t], k[b, t], v[b, t], g[b, t], beta[b, t], scale)
+        dS = np.zeros((H, Dk, Dv)) if d_final is None else np.array(d_final[n], dtype=np.float64)
+        for t in range(eos - 1, bos - 1, -1):
+            a = np.exp(g[b, t])[:, :, None]
+            Sd = a * prev[t - bos]
+            x = np.einsum("hk,hkv->hv", k[b, t], Sd)
+            u = beta[b, t][:, None] * (v[b, t] - x)
+            St = Sd + k[b, t][:, :, None] * u[:, None, :]
+            dS += scale * q[b, t][:, :, None] * d_o[b, t][:, None, :]
+            dq[b, t] = scale * np.einsum("hkv,hv->hk", St, d_o[b, t])
+            du = np.einsum("hkv,hk->hv", dS, k[b, t])
+            dkt = np.einsum("hkv,hv->hk", dS, u)
+            dbeta[b, t] = (du * (v[b, t] - x)).sum(-1)
+            dv[b, t] = beta[b, t][:, None] * du
+            dx = -beta[b, t][:, None] * du
+            dk[b, t] = dkt + np.einsum("hkv,hv->hk", Sd, dx)
+            dSd = dS + k[b, t][:, :, None] * dx[:, None, :]
+            dg[b, t] = (dSd * Sd).sum(-1)
+            dS = a * dSd
+        d_init[n] = dS
+    return dq, dk, dv, dg, dbeta, d_init
+
+
 def prologue(q_raw, k_raw, g_logit, beta_logit, A_log, dt_bias, gate_lower_bound=-5.0, l2_eps=1e-6):
-    """The gate, beta and normalisation prologue (float64), per token and head.
+    """The reverse-mode gradient has the same two forms (``recurrence_backward``,
+``c_backward``); both are pinned against central finite differences of the
+forward, not against each other alone.
+The gate, beta and normalisation prologue (float64), per token and head.
 
     The pages fix the gate's parameters and bound but not its formula (hysenlabs
     "kimi-k3-mlx", section "The A_log shape mismatch is a silent-garbage bug the
@@ -194,6 +256,9 @@ def load_c():
         lib.kda_ref_short_conv.restype = ctypes.c_int
         lib.kda_ref_short_conv_step.argtypes = [P, P, P, P, I, I, I, ctypes.c_int, P]
         lib.kda_ref_short_conv_step.restype = ctypes.c_int
+        lib.kda_ref_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, D,
+                                         P, P, P, P, P, P, ctypes.c_int]
+        lib.kda_ref_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -228,6 +293,38 @@ def c_forward(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0,
     if rc != 0:
         raise ValueError("kda_ref_forward rejected its arguments")
     return o, final
+
+
+def c_backward(q, k, v, g, beta, d_o, initial_state=None, d_final=None, cu_seqlens=None, scale=1.0,
+               nthreads=0):
+    """The C oracle's reverse-mode gradient (kda_ref_backward) on float32-held inputs.
+
+    Same contract as ``recurrence_backward``; memory is O(d_k d_v) per token
+    block of 64 (forward states re-run from one checkpoint per block).
+    """
+    lib = load_c()
+    q, k, v, g, beta, d_o = (_f32(a) for a in (q, k, v, g, beta, d_o))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    cu = None
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64).reshape(-1))
+        N = cu.size - 1
+    else:
+        N = B
+    s0 = None if initial_state is None else _f32(initial_state)
+    dfin = None if d_final is None else _f32(d_final)
+    dq, dk, dg = (np.zeros((B, T, H, Dk)) for _ in range(3))
+    dv = np.zeros((B, T, H, Dv))
+    dbeta = np.zeros((B, T, H))
+    d_init = np.zeros((N, H, Dk, Dv))
+    rc = lib.kda_ref_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(cu),
+                              _ptr(d_o), _ptr(dfin), N, B, T, H, Dk, Dv, float(scale),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(d_init),
+                              int(nthreads))
+    if rc != 0:
+        raise ValueError("kda_ref_backward rejected its arguments")
+    return dq, dk, dv, dg, dbeta, d_init
 
 
 def c_prologue_forward(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, gate_lower_bound=-5.0,
