@@ -1,4 +1,4 @@
-"""Kimi Delta Attention (KDA) forward on AMD MI355X (gfx950).
+"""Kimi Delta Attention (KDA) forward and backward on AMD MI355X (gfx950).
 
 A thin ctypes binding over the C ABI of ``libkda.so`` (declared in
 include/kda.h). It only marshals arguments: checks tensor shapes, dtypes,
@@ -10,6 +10,8 @@ not built, calls raise ``RuntimeError``.
     o, final_state = chunk_fwd(q, k, v, g, beta, initial_state=None,
                                cu_seqlens=None, chunk_size=0, scale=1.0,
                                output_final_state=True)
+    dq, dk, dv, dg, dbeta, d_initial = chunk_bwd(q, k, v, g, beta, d_o, initial_state=None,
+                                                 d_final_state=None, cu_seqlens=None, scale=1.0)
     o = recurrent_step(q, k, v, g, beta, state_cache, state_slots=None, scale=1.0)
 """
 from __future__ import annotations
@@ -62,6 +64,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_short_conv.restype = ctypes.c_int
     lib.kda_short_conv_step.argtypes = [P, P, P, P, I32, I32, I32, I32, ctypes.c_int, P, P]
     lib.kda_short_conv_step.restype = ctypes.c_int
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+    lib.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_chunk_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, F, ctypes.c_int,
+                                  P, ctypes.c_size_t, P, P, P, P, P, P, P]
+    lib.kda_chunk_bwd.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error_message.argtypes = []
@@ -167,6 +174,47 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk_size=
                            _DTYPES[dt], _ptr(out), _ptr(final_state), _stream(dev))
     _check(st)
     return out, final_state
+
+
+def chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, N, packed):
+    """Bytes of workspace kda_chunk_bwd needs (kda_chunk_bwd_workspace_bytes)."""
+    return int(load_library().kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, N, int(bool(packed))))
+
+
+def chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, cu_seqlens=None, scale=1.0,
+              workspace=None, want_d_initial=True):
+    """Gradients of <d_o, o> + <d_final_state, final_state> for ``chunk_fwd`` (kda_chunk_bwd).
+
+    Inputs as for ``chunk_fwd``; d_o [B,T,H,Dv] in the inputs' dtype;
+    d_final_state [N,H,Dk,Dv] float32 or None. ``workspace`` is a uint8 device
+    tensor of at least ``chunk_bwd_workspace_bytes`` bytes, or None to
+    allocate one. Returns float32 (dq, dk, dv, dg, dbeta, d_initial_state or
+    None).
+    """
+    lib = load_library()
+    B, T, H, Dk, Dv, N, dt, dev = _chunk_inputs(q, k, v, g, beta, initial_state, cu_seqlens,
+                                                ("q", "k", "v", "g", "beta"))
+    _need(d_o, "d_o", (B, T, H, Dv), dt, dev)
+    if d_final_state is not None:
+        _need(d_final_state, "d_final_state", (N, H, Dk, Dv), torch.float32, dev)
+    need = chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((B, T, H, Dk), **f32)
+    dk = torch.empty((B, T, H, Dk), **f32)
+    dg = torch.empty((B, T, H, Dk), **f32)
+    dv = torch.empty((B, T, H, Dv), **f32)
+    dbeta = torch.empty((B, T, H), **f32)
+    d_init = torch.empty((N, H, Dk, Dv), **f32) if want_d_initial else None
+    st = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                           _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final_state), B, T, H, Dk, Dv, N, float(scale),
+                           _DTYPES[dt], _ptr(workspace), workspace.numel(), _ptr(dq), _ptr(dk), _ptr(dv),
+                           _ptr(dg), _ptr(dbeta), _ptr(d_init), _stream(dev))
+    _check(st)
+    return dq, dk, dv, dg, dbeta, d_init
 
 
 def chunk_fwd_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, gate_lower_bound=-5.0,

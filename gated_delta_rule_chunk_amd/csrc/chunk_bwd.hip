@@ -1,0 +1,525 @@
+// Chunkwise KDA backward in float32 on the vector ALUs.
+//
+// Loss: L = sum_t <dO_t, o_t> + <dS_final, S_final>. The forward's chunk form
+// (16-row chunks, Gamma = in-chunk cumulative log-decay per channel, entry
+// state S):
+//   KK[r][s] = sum_c k_rc k_sc e^(Gamma_rc - Gamma_sc)         (s < r)
+//   P[r][s]  = sum_c q_rc k_sc e^(Gamma_rc - Gamma_sc)         (s <= r)
+//   T = (I + Diag(beta) KK)^-1,  W = V - Kg S,  U = T Diag(beta) W
+//   O = scale (Qh S + P U),  S_next = Diag(e^Gamma_C) S + Kh^T U
+// with Kg = e^Gamma * K, Qh = e^Gamma * Q, Kh = e^(Gamma_C - Gamma) * K.
+// Differentiating it, with dS the gradient at the chunk's end:
+//   dU = scale P^T dO + Kh dS,   dY = T^T dU,   dW = Diag(beta) dY = dV
+//   dP = scale dO U^T (lower),   dM = -dY U^T (strict lower),  dKK = Diag(beta) dM
+//   dbeta_r = dY_r . W_r + sum_s dM[r][s] KK[r][s]
+//   dS_prev = Diag(e^Gamma_C) dS + scale Qh^T dO - Kg^T dW
+// then through the exponentials to dq, dk and dGamma channel by channel,
+// every pair term differentiated with its own e^(Gamma_r - Gamma_s) (only
+// exponentials of differences, as in the forward); dg is the reverse
+// cumulative sum of dGamma over the chunk, Gamma_C's gradient entering at
+// its last row.
+//
+// Two kernels: chunk_states_kernel re-runs the forward and writes each
+// chunk's entry state to a caller-provided workspace; chunk_bwd_kernel walks
+// every sequence backward from its last chunk. Both own one (sequence, head,
+// value slice of up to 64 columns). The slices' partial sums of dq, dk, dg
+// and dbeta meet in float32 atomic adds onto zeroed outputs; with two slices
+// (d_v = 128) the sum does not depend on their order.
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int kBC = 16;  // chunk rows
+constexpr int kBwdThreads = 512;
+constexpr int kWaves = kBwdThreads / 64;
+constexpr int kPairs = kBC * (kBC + 1) / 2;
+
+struct SeqInfo {
+    int64_t bos, len, b, slot0;
+};
+
+__device__ __forceinline__ SeqInfo seq_info(const BwdArgs& a, int n) {
+    SeqInfo s;
+    if (a.cu) {
+        s.bos = a.cu[n];
+        s.len = (int64_t)a.cu[n + 1] - s.bos;
+        s.b = 0;
+        s.slot0 = s.bos / kBC + n;
+    } else {
+        s.bos = 0;
+        s.len = a.T;
+        s.b = n;
+        s.slot0 = (int64_t)n * ((a.T + kBC - 1) / kBC);
+    }
+    return s;
+}
+
+// Pair index p = r(r+1)/2 + s (s <= r) -> (r, s).
+__device__ __forceinline__ void pair_rs(int p, int& r, int& s) {
+    int rr = (int)((__builtin_sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+    if ((rr + 1) * (rr + 2) / 2 <= p) ++rr;
+    if (rr * (rr + 1) / 2 > p) --rr;
+    r = rr;
+    s = p - rr * (rr + 1) / 2;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+__device__ __forceinline__ void add_out(float* p, float v, bool atomic) {
+    if (atomic)
+        unsafeAtomicAdd(p, v);
+    else
+        *p = v;
+}
+
+// One chunk's K (and Q when sQ is given), the log2-scaled gate and beta;
+// rows past the sequence's end are zero tokens.
+template <int DK, typename Tin>
+__device__ __forceinline__ void load_chunk(const BwdArgs& a, const SeqInfo& sq, int h, int64_t t0,
+                                           int rows, float (*sQ)[DK], float (*sK)[DK],
+                                           float (*sG)[DK], float* sBeta) {
+    const Tin* q = static_cast<const Tin*>(a.q);
+    const Tin* k = static_cast<const Tin*>(a.k);
+    const Tin* g = static_cast<const Tin*>(a.g);
+    const Tin* beta = static_cast<const Tin*>(a.beta);
+    for (int idx = threadIdx.x; idx < kBC * DK; idx += kBwdThreads) {
+        const int r = idx / DK, c = idx % DK;
+        const bool in = r < rows;
+        const int64_t e = ((sq.b * a.T + t0 + r) * a.H + h) * DK + c;
+        if (sQ) sQ[r][c] = in ? load_elem(q, e) : 0.f;
+        sK[r][c] = in ? load_elem(k, e) : 0.f;
+        sG[r][c] = in ? load_elem(g, e) * kLog2e : 0.f;
+    }
+    if (threadIdx.x < kBC) {
+        const int r = threadIdx.x;
+        sBeta[r] = r < rows ? load_elem(beta, (sq.b * a.T + t0 + r) * a.H + h) : 0.f;
+    }
+}
+
+// Rows of [C][BV] from a [.., H, Dv] tensor, columns c0 .. c0+BV.
+template <int BV, typename Tin>
+__device__ __forceinline__ void load_rows_v(const Tin* x, const BwdArgs& a, const SeqInfo& sq, int h,
+                                            int64_t t0, int rows, int c0, float (*dst)[BV]) {
+    for (int idx = threadIdx.x; idx < kBC * BV; idx += kBwdThreads) {
+        const int r = idx / BV, j = idx % BV;
+        dst[r][j] = r < rows ? load_elem(x, ((sq.b * a.T + t0 + r) * a.H + h) * a.Dv + c0 + j) : 0.f;
+    }
+}
+
+// In-chunk cumulative sum of the (log2-scaled) gate per channel, and
+// e^Gamma_C; then Kg, Kh (and Qh) for every (row, channel).
+template <int DK>
+__device__ __forceinline__ void gamma_and_scaled(float (*sG)[DK], float* sEC, const float (*sQ)[DK],
+                                                 const float (*sK)[DK], float (*sQh)[DK],
+                                                 float (*sKg)[DK], float (*sKh)[DK]) {
+    if (threadIdx.x < DK) {
+        const int c = threadIdx.x;
+        float run = 0.f;
+#pragma unroll
+        for (int r = 0; r < kBC; ++r) {
+            run += sG[r][c];
+            sG[r][c] = run;
+        }
+        sEC[c] = __builtin_amdgcn_exp2f(run);
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kBC * DK; idx += kBwdThreads) {
+        const int r = idx / DK, c = idx % DK;
+        const float gr = sG[r][c];
+        const float e = __builtin_amdgcn_exp2f(gr);
+        const float k = sK[r][c];
+        if (sQh) sQh[r][c] = e * sQ[r][c];
+        sKg[r][c] = e * k;
+        sKh[r][c] = __builtin_amdgcn_exp2f(sG[kBC - 1][c] - gr) * k;
+    }
+}
+
+// KK (strict lower) and, when sP is given, P (lower with diagonal): one wave
+// per (r, s) pair, lanes across channels.
+template <int DK>
+__device__ __forceinline__ void pair_sums(const float (*sG)[DK], const float (*sK)[DK],
+                                          const float (*sQ)[DK], float (*sKK)[kBC + 1],
+                                          float (*sP)[kBC + 1]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int p = w; p < kPairs; p += kWaves) {
+        int r, s;
+        pair_rs(p, r, s);
+        if (!sP && s == r) continue;
+        float ak = 0.f, ap = 0.f;
+        for (int c = lane; c < DK; c += 64) {
+            const float e = __builtin_amdgcn_exp2f(sG[r][c] - sG[s][c]);
+            const float ks = sK[s][c] * e;
+            ak += sK[r][c] * ks;
+            if (sP) ap += sQ[r][c] * ks;
+        }
+        ak = wave_sum(ak);
+        if (sP) ap = wave_sum(ap);
+        if (lane == 0) {
+            sKK[r][s] = s < r ? ak : 0.f;
+            if (sP) sP[r][s] = ap;
+        }
+    }
+}
+
+// T = (I + Diag(beta) KK)^-1 (unit lower triangular), one thread per column.
+__device__ __forceinline__ void invert_unit_lower(const float (*sKK)[kBC + 1], const float* sBeta,
+                                                  float (*sT)[kBC + 1]) {
+    if (threadIdx.x < kBC) {
+        const int i = threadIdx.x;
+        for (int r = 0; r < kBC; ++r) {
+            float t;
+            if (r < i) {
+                t = 0.f;
+            } else if (r == i) {
+                t = 1.f;
+            } else {
+                float acc = 0.f;
+                for (int s = i; s < r; ++s) acc += sKK[r][s] * sT[s][i];
+                t = -sBeta[r] * acc;
+            }
+            sT[r][i] = t;
+        }
+    }
+}
+
+template <int DK, int BV, typename Tin>
+__global__ __launch_bounds__(kBwdThreads) void chunk_states_kernel(BwdArgs a) {
+    __shared__ float sS[DK][BV + 1];
+    __shared__ float sK[kBC][DK];
+    __shared__ float sG[kBC][DK];
+    __shared__ float sKg[kBC][DK];
+    __shared__ float sKh[kBC][DK];
+    __shared__ float sW[kBC][BV];
+    __shared__ float sU[kBC][BV];
+    __shared__ float sKK[kBC][kBC + 1];
+    __shared__ float sT[kBC][kBC + 1];
+    __shared__ float sBeta[kBC];
+    __shared__ float sEC[DK];
+
+    const int tid = threadIdx.x;
+    const int nvt = a.Dv / BV;
+    const int vt = blockIdx.x % nvt, unit = blockIdx.x / nvt;
+    const int n = unit / a.H, h = unit % a.H;
+    const int Dv = a.Dv, c0 = vt * BV;
+    const SeqInfo sq = seq_info(a, n);
+    const int64_t sbase = ((int64_t)n * a.H + h) * DK * (int64_t)Dv;
+    const int64_t slot_stride = (int64_t)a.H * DK * Dv;
+
+    for (int idx = tid; idx < DK * BV; idx += kBwdThreads) {
+        const int c = idx / BV, j = idx % BV;
+        sS[c][j] = a.s0 ? a.s0[sbase + (int64_t)c * Dv + c0 + j] : 0.f;
+    }
+    __syncthreads();
+    const int64_t nch = (sq.len + kBC - 1) / kBC;
+    for (int64_t ch = 0; ch < nch; ++ch) {
+        const int64_t t0 = sq.bos + ch * kBC;
+        const int rows = (int)min<int64_t>(kBC, sq.len - ch * kBC);
+        float* ws = a.ws + (sq.slot0 + ch) * slot_stride + (int64_t)h * DK * Dv;
+        for (int idx = tid; idx < DK * BV; idx += kBwdThreads) {
+            const int c = idx / BV, j = idx % BV;
+            ws[(int64_t)c * Dv + c0 + j] = sS[c][j];
+        }
+        load_chunk<DK, Tin>(a, sq, h, t0, rows, nullptr, sK, sG, sBeta);
+        load_rows_v<BV>(static_cast<const Tin*>(a.v), a, sq, h, t0, rows, c0, sW);
+        __syncthreads();
+        gamma_and_scaled<DK>(sG, sEC, nullptr, sK, nullptr, sKg, sKh);
+        pair_sums<DK>(sG, sK, nullptr, sKK, nullptr);
+        __syncthreads();
+        invert_unit_lower(sKK, sBeta, sT);
+        // W = V - Kg S (in place)
+        for (int idx = tid; idx < kBC * BV; idx += kBwdThreads) {
+            const int r = idx / BV, j = idx % BV;
+            float acc = 0.f;
+#pragma unroll 8
+            for (int c = 0; c < DK; ++c) acc += sKg[r][c] * sS[c][j];
+            sW[r][j] -= acc;
+        }
+        __syncthreads();
+        // U = T Diag(beta) W
+        for (int idx = tid; idx < kBC * BV; idx += kBwdThreads) {
+            const int r = idx / BV, j = idx % BV;
+            float acc = 0.f;
+            for (int s = 0; s <= r; ++s) acc += sT[r][s] * sBeta[s] * sW[s][j];
+            sU[r][j] = acc;
+        }
+        __syncthreads();
+        // S <- Diag(e^Gamma_C) S + Kh^T U
+        for (int idx = tid; idx < DK * BV; idx += kBwdThreads) {
+            const int c = idx / BV, j = idx % BV;
+            float acc = sEC[c] * sS[c][j];
+#pragma unroll
+            for (int r = 0; r < kBC; ++r) acc += sKh[r][c] * sU[r][j];
+            sS[c][j] = acc;
+        }
+        __syncthreads();
+    }
+}
+
+template <int DK, int BV, typename Tin>
+__global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(BwdArgs a) {
+    constexpr int kGroups = kBwdThreads / DK;  // threads sharing one channel
+    static_assert(kBwdThreads % DK == 0, "each thread keeps one channel");
+    __shared__ float sS[DK][BV + 1];
+    __shared__ float sdS[DK][BV + 1];
+    __shared__ float sQ[kBC][DK];
+    __shared__ float sK[kBC][DK];
+    __shared__ float sG[kBC][DK];
+    __shared__ float sQh[kBC][DK];
+    __shared__ float sKg[kBC][DK];
+    __shared__ float sKh[kBC][DK];
+    __shared__ float sdG[kBC][DK];
+    __shared__ float sW[kBC][BV];
+    __shared__ float sU[kBC][BV];
+    __shared__ float sdO[kBC][BV];
+    __shared__ float sdUW[kBC][BV];  // dU, then dW
+    __shared__ float sdY[kBC][BV];
+    __shared__ float sKK[kBC][kBC + 1];
+    __shared__ float sP[kBC][kBC + 1];
+    __shared__ float sT[kBC][kBC + 1];
+    __shared__ float sdP[kBC][kBC + 1];
+    __shared__ float sdM[kBC][kBC + 1];
+    __shared__ float sBeta[kBC];
+    __shared__ float sEC[DK];
+    __shared__ float sGCp[kGroups][DK];
+    __shared__ float sGC0[DK];
+
+    const Tin* v = static_cast<const Tin*>(a.v);
+    const Tin* d_o = static_cast<const Tin*>(a.d_o);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int nvt = a.Dv / BV;
+    const bool atomic = nvt > 1;
+    const int vt = blockIdx.x % nvt, unit = blockIdx.x / nvt;
+    const int n = unit / a.H, h = unit % a.H;
+    const int H = a.H, Dv = a.Dv, c0 = vt * BV;
+    const float scale = a.scale;
+    const SeqInfo sq = seq_info(a, n);
+    const int64_t sbase = ((int64_t)n * H + h) * DK * (int64_t)Dv;
+    const int64_t slot_stride = (int64_t)H * DK * Dv;
+
+    for (int idx = tid; idx < DK * BV; idx += kBwdThreads) {
+        const int c = idx / BV, j = idx % BV;
+        sdS[c][j] = a.d_final ? a.d_final[sbase + (int64_t)c * Dv + c0 + j] : 0.f;
+    }
+    const int64_t nch = (sq.len + kBC - 1) / kBC;
+    for (int64_t ch = nch - 1; ch >= 0; --ch) {
+        const int64_t t0 = sq.bos + ch * kBC;
+        const int rows = (int)min<int64_t>(kBC, sq.len - ch * kBC);
+        const float* ws = a.ws + (sq.slot0 + ch) * slot_stride + (int64_t)h * DK * Dv;
+        for (int idx = tid; idx < DK * BV; idx += kBwdThreads) {
+            const int c = idx / BV, j = idx % BV;
+            sS[c][j] = ws[(int64_t)c * Dv + c0 + j];
+        }
+        load_chunk<DK, Tin>(a, sq, h, t0, rows, sQ, sK, sG, sBeta);
+        load_rows_v<BV>(v, a, sq, h, t0, rows, c0, sW);
+        load_rows_v<BV>(d_o, a, sq, h, t0, rows, c0, sdO);
+        __syncthreads();
+        gamma_and_scaled<DK>(sG, sEC, sQ, sK, sQh, sKg, sKh);
+        pair_sums<DK>(sG, sK, sQ, sKK, sP);
+        __syncthreads();
+        invert_unit_lower(sKK, sBeta, sT);
+        // W = V - Kg S (in place);  dU = scale P^T dO + Kh dS
+        for (int idx = tid; idx < kBC * BV; idx += kBwdThreads) {
+            const int r = idx / BV, j = idx % BV;
+            float aw = 0.f, au = 0.f;
+#pragma unroll 8
+            for (int c = 0; c < DK; ++c) {
+                aw += sKg[r][c] * sS[c][j];
+                au += sKh[r][c] * sdS[c][j];
+            }
+            float ap = 0.f;
+            for (int s = r; s < kBC; ++s) ap += sP[s][r] * sdO[s][j];
+            sW[r][j] -= aw;
+            sdUW[r][j] = au + scale * ap;
+        }
+        __syncthreads();
+        // U = T Diag(beta) W;  dY = T^T dU
+        for (int idx = tid; idx < kBC * BV; idx += kBwdThreads) {
+            const int r = idx / BV, j = idx % BV;
+            float au = 0.f, ay = 0.f;
+            for (int s = 0; s <= r; ++s) au += sT[r][s] * sBeta[s] * sW[s][j];
+            for (int s = r; s < kBC; ++s) ay += sT[s][r] * sdUW[s][j];
+            sU[r][j] = au;
+            sdY[r][j] = ay;
+        }
+        __syncthreads();
+        // dP = scale dO U^T (s <= r), dM = -dY U^T (s < r): one wave per pair
+        for (int p = w; p < kPairs; p += kWaves) {
+            int r, s;
+            pair_rs(p, r, s);
+            float ap = 0.f, am = 0.f;
+            for (int j = lane; j < BV; j += 64) {
+                const float us = sU[s][j];
+                ap += sdO[r][j] * us;
+                am += sdY[r][j] * us;
+            }
+            ap = wave_sum(ap);
+            am = wave_sum(am);
+            if (lane == 0) {
+                sdP[r][s] = scale * ap;
+                sdM[r][s] = s < r ? -am : 0.f;
+            }
+        }
+        // dW = Diag(beta) dY = dV
+        for (int idx = tid; idx < kBC * BV; idx += kBwdThreads) {
+            const int r = idx / BV, j = idx % BV;
+            const float dw = sBeta[r] * sdY[r][j];
+            sdUW[r][j] = dw;
+            if (r < rows) a.dv[((sq.b * a.T + t0 + r) * H + h) * (int64_t)Dv + c0 + j] = dw;
+        }
+        __syncthreads();
+        // dbeta
+        if (tid < kBC && tid < rows) {
+            const int r = tid;
+            float acc = 0.f;
+            for (int j = 0; j < BV; ++j) acc += sdY[r][j] * sW[r][j];
+            for (int s = 0; s < r; ++s) acc += sdM[r][s] * sKK[r][s];
+            add_out(a.dbeta + (sq.b * a.T + t0 + r) * H + h, acc, atomic);
+        }
+        // dq, dk and dGamma per (row, channel)
+        {
+            const int c = tid % DK;
+            float gc_part = 0.f;
+            for (int idx = tid; idx < kBC * DK; idx += kBwdThreads) {
+                const int r = idx / DK;
+                const float gr = sG[r][c], qr = sQ[r][c], kr = sK[r][c];
+                // pairs with this row as the later one (r, s <= r)
+                float accq = 0.f, acckr = 0.f;
+                for (int s = 0; s <= r; ++s) {
+                    const float ks = sK[s][c] * __builtin_amdgcn_exp2f(gr - sG[s][c]);
+                    accq += sdP[r][s] * ks;
+                    acckr += sBeta[r] * sdM[r][s] * ks;
+                }
+                // pairs with this row as the earlier one (r2 >= r, r)
+                float accks = 0.f;
+                for (int r2 = r; r2 < kBC; ++r2) {
+                    const float e = __builtin_amdgcn_exp2f(sG[r2][c] - gr);
+                    accks += (sdP[r2][r] * sQ[r2][c] + sBeta[r2] * sdM[r2][r] * sK[r2][c]) * e;
+                }
+                // dense terms
+                float ao = 0.f, aw = 0.f, ad = 0.f;
+#pragma unroll 8
+                for (int j = 0; j < BV; ++j) {
+                    const float sv = sS[c][j];
+                    ao += sdO[r][j] * sv;
+                    aw += sdUW[r][j] * sv;
+                    ad += sU[r][j] * sdS[c][j];
+                }
+                const float qh = sQh[r][c], kg = sKg[r][c], kh = sKh[r][c];
+                const float eg = __builtin_amdgcn_exp2f(gr);
+                const float eh = __builtin_amdgcn_exp2f(sG[kBC - 1][c] - gr);
+                const float dqv = accq + eg * scale * ao;
+                const float dkv = acckr + accks - eg * aw + eh * ad;
+                const float dgv = qr * accq + kr * acckr - kr * accks + qh * scale * ao - kg * aw - kh * ad;
+                gc_part += kh * ad;
+                sdG[r][c] = dgv;
+                if (r < rows) {
+                    const int64_t e = ((sq.b * a.T + t0 + r) * H + h) * DK + c;
+                    add_out(a.dq + e, dqv, atomic);
+                    add_out(a.dk + e, dkv, atomic);
+                }
+            }
+            sGCp[tid / DK][c] = gc_part;
+            if (tid < DK) {
+                float acc = 0.f;
+                for (int j = 0; j < BV; ++j) acc += sdS[c][j] * sS[c][j];
+                sGC0[c] = sEC[c] * acc;
+            }
+        }
+        __syncthreads();
+        // dg: reverse cumulative sum of dGamma, Gamma_C's gradient at the last row
+        if (tid < DK) {
+            const int c = tid;
+            float run = sGC0[c];
+            for (int p = 0; p < kGroups; ++p) run += sGCp[p][c];
+            for (int r = kBC - 1; r >= 0; --r) {
+                run += sdG[r][c];
+                if (r < rows) add_out(a.dg + ((sq.b * a.T + t0 + r) * H + h) * DK + c, run, atomic);
+            }
+        }
+        // dS <- Diag(e^Gamma_C) dS + scale Qh^T dO - Kg^T dW
+        for (int idx = tid; idx < DK * BV; idx += kBwdThreads) {
+            const int c = idx / BV, j = idx % BV;
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < kBC; ++r) acc += scale * sQh[r][c] * sdO[r][j] - sKg[r][c] * sdUW[r][j];
+            sdS[c][j] = sEC[c] * sdS[c][j] + acc;
+        }
+        __syncthreads();
+    }
+    if (a.d_s0) {
+        for (int idx = tid; idx < DK * BV; idx += kBwdThreads) {
+            const int c = idx / BV, j = idx % BV;
+            a.d_s0[sbase + (int64_t)c * Dv + c0 + j] = sdS[c][j];
+        }
+    }
+}
+
+__global__ void zero_fill_kernel(float* p, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
+}
+
+hipError_t zero_fill(float* p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    zero_fill_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p, n);
+    return hipGetLastError();
+}
+
+template <int DK, int BV, typename Tin>
+hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
+    const int64_t grid = (int64_t)a.N * a.H * (a.Dv / BV);
+    if (grid == 0) return hipSuccess;
+    chunk_states_kernel<DK, BV, Tin><<<dim3((unsigned)grid), dim3(kBwdThreads), 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    chunk_bwd_kernel<DK, BV, Tin><<<dim3((unsigned)grid), dim3(kBwdThreads), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int DK, typename Tin>
+hipError_t launch_dk(const BwdArgs& a, hipStream_t s) {
+    switch (a.Dv) {
+        case 16: return launch_typed<DK, 16, Tin>(a, s);
+        case 32: return launch_typed<DK, 32, Tin>(a, s);
+        default: return launch_typed<DK, 64, Tin>(a, s);  // 64 and 128
+    }
+}
+
+template <typename Tin>
+hipError_t launch_dtype(const BwdArgs& a, hipStream_t s) {
+    switch (a.Dk) {
+        case 16: return launch_dk<16, Tin>(a, s);
+        case 32: return launch_dk<32, Tin>(a, s);
+        case 64: return launch_dk<64, Tin>(a, s);
+        default: return launch_dk<128, Tin>(a, s);
+    }
+}
+
+}  // namespace
+
+int64_t chunk_bwd_slots(int32_t B, int32_t T, int32_t N, bool packed) {
+    return packed ? (int64_t)T / kBC + N : (int64_t)B * ((T + kBC - 1) / kBC);
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s) {
+    const int nvt = a.Dv / (a.Dv >= 64 ? 64 : a.Dv);
+    if (nvt > 1) {
+        const int64_t rows = (int64_t)a.B * a.T * a.H;
+        hipError_t e;
+        if ((e = zero_fill(a.dq, rows * a.Dk, s)) != hipSuccess) return e;
+        if ((e = zero_fill(a.dk, rows * a.Dk, s)) != hipSuccess) return e;
+        if ((e = zero_fill(a.dg, rows * a.Dk, s)) != hipSuccess) return e;
+        if ((e = zero_fill(a.dbeta, rows, s)) != hipSuccess) return e;
+    }
+    return a.bf16 ? launch_dtype<__bf16>(a, s) : launch_dtype<float>(a, s);
+}
+
+}  // namespace kda

@@ -135,6 +135,64 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
     return launch_chunk(fn, a, stream);
 }
 
+size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
+                                     int32_t packed) {
+    if (B < 1 || T <= 0 || H < 1 || Dk < 1 || Dv < 1 || N < 0) return 0;
+    const int64_t slots = kda::chunk_bwd_slots(B, T, N, packed != 0);
+    return (size_t)slots * (size_t)H * (size_t)Dk * (size_t)Dv * sizeof(float);
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
+                         const float* d_final_state, int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                         int32_t N, float scale, kda_dtype dtype, void* workspace, size_t workspace_bytes,
+                         float* dq, float* dk, float* dv, float* dg, float* dbeta, float* d_initial_state,
+                         void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_chunk_bwd";
+    if (T > 0 && (!q || !k || !v || !g || !beta || !d_o))
+        return fail(KDA_ERR_INVALID_ARG, "%s: q, k, v, g, beta and d_o must be non-NULL when T > 0", fn);
+    if (T > 0 && (!dq || !dk || !dv || !dg || !dbeta))
+        return fail(KDA_ERR_INVALID_ARG, "%s: dq, dk, dv, dg and dbeta must be non-NULL when T > 0", fn);
+    if (B < 1 || T < 0 || H < 1 || N < 0)
+        return fail(KDA_ERR_INVALID_ARG, "%s: need B >= 1, T >= 0, H >= 1, N >= 0 (got B=%d T=%d H=%d N=%d)",
+                    fn, B, T, H, N);
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dtype %d is not KDA_F32 or KDA_BF16", fn, (int)dtype);
+    if (!dim_ok(Dk) || !dim_ok(Dv))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: Dk=%d, Dv=%d; supported head dims are 16, 32, 64, 128", fn, Dk, Dv);
+    if (cu_seqlens) {
+        if (B != 1)
+            return fail(KDA_ERR_INVALID_ARG, "%s: packed sequences (cu_seqlens) need B == 1, got B=%d", fn, B);
+        if (N < 1) return fail(KDA_ERR_INVALID_ARG, "%s: packed sequences need N >= 1, got N=%d", fn, N);
+    } else if (N != B) {
+        return fail(KDA_ERR_INVALID_ARG, "%s: without cu_seqlens N must equal B (N=%d, B=%d)", fn, N, B);
+    }
+    if ((int64_t)N * H > ((int64_t)1 << 26) || (int64_t)B * T * H > ((int64_t)1 << 40))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", fn);
+    const size_t need = kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens != nullptr);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KDA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, got %zu%s", fn, need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    if (T > 0) {
+        const void* ins[] = {q, k, v, g, beta, d_o, workspace};
+        const void* outs[] = {dq, dk, dv, dg, dbeta};
+        for (const void* o : outs)
+            for (const void* i : ins)
+                if (o == i) return fail(KDA_ERR_INVALID_ARG, "%s: gradients must not alias an input", fn);
+    }
+    kda::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.d_o = d_o;
+    a.s0 = initial_state; a.cu = cu_seqlens; a.d_final = d_final_state;
+    a.ws = static_cast<float*>(workspace);
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.d_s0 = d_initial_state;
+    a.B = B; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.N = N; a.scale = scale; a.bf16 = dtype == KDA_BF16;
+    if ((int64_t)N * H == 0) return KDA_OK;
+    const hipError_t e = kda::launch_chunk_bwd(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
+}
+
 kda_status kda_short_conv(const void* x, const float* weight, const float* conv_state_in,
                           const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t C, int32_t N,
                           int32_t activation, kda_dtype dtype, void* y, float* conv_state_out, void* stream) {

@@ -66,6 +66,33 @@ struct ConvStepArgs {
     bool act, bf16;
 };
 
+// Backward of the chunk forward; gradients are float32.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const void* d_o;           // [B,T,H,Dv], input dtype
+    const float* s0;           // [N,H,Dk,Dv] or nullptr
+    const int32_t* cu;         // [N+1] or nullptr
+    const float* d_final;      // [N,H,Dk,Dv] or nullptr
+    float* ws;                 // chunk entry states [slots][H][Dk][Dv]
+    float* dq;                 // [B,T,H,Dk]
+    float* dk;
+    float* dv;                 // [B,T,H,Dv]
+    float* dg;                 // [B,T,H,Dk]
+    float* dbeta;              // [B,T,H]
+    float* d_s0;               // [N,H,Dk,Dv] or nullptr
+    int32_t B, T, H, Dk, Dv, N;
+    float scale;
+    bool bf16;
+};
+
+// Number of chunk-state slots the backward's workspace holds.
+int64_t chunk_bwd_slots(int32_t B, int32_t T, int32_t N, bool packed);
+hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s);
+
 hipError_t launch_short_conv(const ConvArgs& a, hipStream_t s);
 hipError_t launch_short_conv_step(const ConvStepArgs& a, hipStream_t s);
 

@@ -31,6 +31,7 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -119,6 +120,52 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
                                   int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
                                   int32_t chunk_size, float scale, kda_dtype dtype, void* o,
                                   float* final_state, void* stream);
+
+/*
+ * Bytes of device workspace kda_chunk_bwd needs: one float32 state
+ * [H,Dk,Dv] per 16-row chunk slot, T/16 + N slots for packed sequences
+ * (packed != 0), B * ceil(T/16) otherwise. 0 when T = 0 or a size is out of
+ * range.
+ */
+size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
+                                     int32_t packed);
+
+/*
+ * Backward of kda_chunk_fwd: the gradients of
+ *   L = sum_t <d_o[t], o[t]> + sum_n <d_final_state[n], final_state[n]>
+ * with respect to q, k, v, g, beta and initial_state, for the recurrence and
+ * the scale that kda_chunk_fwd computes. The package the method comes from
+ * trains through KDA (ISEEKYAN/k3 README: its single-rank reference path runs
+ * a KDA layer through loss and backward), while the FlashKDA backend it names
+ * is forward-only; this is the training-side counterpart of the forward here.
+ *
+ *   q, k, v, g, beta, initial_state, cu_seqlens, B, T, H, Dk, Dv, N, scale,
+ *   dtype     exactly as passed to kda_chunk_fwd
+ *   d_o       [B,T,H,Dv] dtype: gradient of the loss with respect to o
+ *   d_final_state  [N,H,Dk,Dv] float32, or NULL for zeros
+ *   workspace at least kda_chunk_bwd_workspace_bytes(...) bytes of device
+ *             memory (packed = cu_seqlens != NULL), owned by the caller; its
+ *             contents on entry do not matter and are overwritten (the
+ *             forward's state at the start of every 16-row chunk)
+ *   dq, dk, dg [B,T,H,Dk], dv [B,T,H,Dv], dbeta [B,T,H]: float32 outputs,
+ *             written for every row of every sequence; they must not alias
+ *             an input or the workspace
+ *   d_initial_state [N,H,Dk,Dv] float32, or NULL (not written)
+ *
+ * Everything is computed in float32, in 16-row chunks, on the vector ALUs;
+ * bf16 inputs are widened exactly. For Dv = 128 the two 64-column halves of
+ * the value dimension add their shares of dq, dk, dg and dbeta with float32
+ * atomics, which with two terms is order-independent, so the result is
+ * deterministic. With T = 0 only d_initial_state is written (it then equals
+ * d_final_state, or zeros). Supported dims and errors as for kda_chunk_fwd; a
+ * short or NULL workspace is KDA_ERR_INVALID_ARG.
+ */
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
+                         const float* d_final_state, int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                         int32_t N, float scale, kda_dtype dtype, void* workspace, size_t workspace_bytes,
+                         float* dq, float* dk, float* dv, float* dg, float* dbeta, float* d_initial_state,
+                         void* stream);
 
 /*
  * Short causal depthwise convolution over time (kernel size 4), the step that

@@ -1,4 +1,4 @@
 """Seeded synthetic KDA inputs (no recurrence arithmetic lives here)."""
 from .inputs import (DECODE, GATE_LOWER_BOUND, K3_HEAD_DIM, K3_HEADS, WORKLOADS,  # noqa: F401
-                     Workload, as_f32_numpy, make_chunk_inputs, make_decode_cache, make_prologue_inputs,
+                     Workload, as_f32_numpy, make_chunk_inputs, make_cotangents, make_decode_cache, make_prologue_inputs,
                      make_decode_step, make_workload, packed_lengths)

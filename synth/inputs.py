@@ -23,6 +23,8 @@ Recipe (numpy PCG64 generators, float32 draws):
   g     = -5 * sigmoid(g_raw), g_raw ~ N(0,1)   (per channel, in [-5, 0))
   beta  = sigmoid(beta_raw), beta_raw ~ N(0,1)  (per token and head)
   S0    ~ N(0, 0.02) float32 when requested (0.02 is the standard deviation)
+  d_o   ~ N(0,1) (stream 9), d_final ~ N(0, 0.1) float32 (stream 10): the
+        output and final-state cotangents of the backward workloads
 then, for bf16 workloads, q,k,v,g,beta are rounded to bf16 (round to nearest
 even). States stay float32.
 """
@@ -88,7 +90,7 @@ def packed_lengths(rng, n, lo, hi):
 
 
 BLOCK_ROWS = 1024
-_STREAM = dict(lengths=0, q=1, k=2, v=3, g=4, beta=5, s0=6, A_log=7, dt_bias=8)
+_STREAM = dict(lengths=0, q=1, k=2, v=3, g=4, beta=5, s0=6, A_log=7, dt_bias=8, d_o=9, d_final=10)
 
 
 def _pool_size():
@@ -240,3 +242,19 @@ def make_decode_step(Nb, H, Dk, Dv, seed, step, dtype="bf16"):
 def as_f32_numpy(t):
     """Exact float32 copy of a CPU tensor (bf16 values are exact in float32)."""
     return None if t is None else t.float().numpy()
+
+
+def make_cotangents(inp, seed, d_final=True, d_final_std=0.1):
+    """Cotangents for the backward of the forward workload ``inp`` (a dict from
+    ``make_chunk_inputs``): d_o shaped and typed like the output [B,T,H,Dv] and
+    N(0,1), and d_final [N,H,Dk,Dv] float32 N(0, d_final_std^2) or None."""
+    B, T, H, Dv = inp["v"].shape
+    Dk = inp["q"].shape[-1]
+    dtype = "bf16" if inp["v"].dtype == torch.bfloat16 else "f32"
+    N = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+    d_o = _blocked(seed, _STREAM["d_o"], (B * T, H, Dv), lambda x: x).reshape(B, T, H, Dv)
+    dfin = None
+    if d_final:
+        dfin = torch.from_numpy(_blocked(seed, _STREAM["d_final"], (N, H, Dk, Dv),
+                                         lambda x: np.float32(d_final_std) * x))
+    return _round(d_o, dtype), dfin

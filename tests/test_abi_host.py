@@ -22,7 +22,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = kda.declared_symbols()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step", "kda_short_conv",
-                          "kda_short_conv_step", "kda_status_string", "kda_last_error_message"}
+                          "kda_short_conv_step", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
+                          "kda_status_string", "kda_last_error_message"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -181,3 +182,61 @@ def test_short_conv_step_rejects_before_launch(lib, kw, status, needle):
 def test_short_conv_step_empty_is_ok(lib):
     st = lib.kda_short_conv_step(None, None, None, None, 0, 0, 1024, 1, kda.KDA_BF16, None, None)
     assert st == kda.KDA_OK
+
+
+def test_chunk_bwd_workspace_bytes(lib):
+    # one float32 [H,Dk,Dv] state per 16-row chunk slot
+    assert kda.chunk_bwd_workspace_bytes(1, 4096, 96, 128, 128, 1, False) == 256 * 96 * 128 * 128 * 4
+    assert kda.chunk_bwd_workspace_bytes(2, 17, 3, 64, 32, 2, False) == 2 * 2 * 3 * 64 * 32 * 4
+    assert kda.chunk_bwd_workspace_bytes(1, 100, 2, 16, 16, 5, True) == (100 // 16 + 5) * 2 * 16 * 16 * 4
+    assert kda.chunk_bwd_workspace_bytes(1, 0, 2, 16, 16, 1, False) == 0
+    assert kda.chunk_bwd_workspace_bytes(0, 10, 2, 16, 16, 1, False) == 0
+
+
+def test_chunk_bwd_packed_slots_never_overlap():
+    # Sequence n's chunks use slots [cu[n] // 16 + n, ... + ceil(len / 16)); the
+    # ranges of consecutive sequences must not overlap and must fit the count.
+    import numpy as np
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        lens = rng.integers(0, 70, size=int(rng.integers(1, 9)))
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        T, N = int(cu[-1]), len(lens)
+        total = T // 16 + N
+        used = set()
+        for n in range(N):
+            base = int(cu[n]) // 16 + n
+            for c in range((int(lens[n]) + 15) // 16):
+                assert base + c not in used and base + c < total
+                used.add(base + c)
+
+
+def _bwd(lib, **kw):
+    W = ctypes.c_void_p(0x3000)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, cu=None, do=FAKE, dfin=None, B=1, T=64, H=2,
+             Dk=128, Dv=128, N=1, scale=1.0, dtype=kda.KDA_BF16, ws=W, wsb=1 << 30,
+             dq=ctypes.c_void_p(0x4000), dk=ctypes.c_void_p(0x5000), dv=ctypes.c_void_p(0x6000),
+             dg=ctypes.c_void_p(0x7000), db=ctypes.c_void_p(0x8000), d0=None, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["do"], a["dfin"],
+                             a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["N"], a["scale"], a["dtype"], a["ws"],
+                             a["wsb"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["d0"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(do=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(dg=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(B=0), kda.KDA_ERR_INVALID_ARG, "B >= 1"),
+    (dict(Dk=96), kda.KDA_ERR_UNSUPPORTED, "head dims"),
+    (dict(dtype=7), kda.KDA_ERR_UNSUPPORTED, "dtype"),
+    (dict(cu=FAKE, B=2, N=1), kda.KDA_ERR_INVALID_ARG, "B == 1"),
+    (dict(N=2), kda.KDA_ERR_INVALID_ARG, "N must equal B"),
+    (dict(wsb=64 * 2 * 128 * 128 * 4 // 16 - 1), kda.KDA_ERR_INVALID_ARG, "workspace"),
+    (dict(ws=None), kda.KDA_ERR_INVALID_ARG, "workspace"),
+    (dict(dq=FAKE), kda.KDA_ERR_INVALID_ARG, "alias"),
+    (dict(dv=ctypes.c_void_p(0x3000)), kda.KDA_ERR_INVALID_ARG, "alias"),
+])
+def test_chunk_bwd_rejects_before_launch(lib, kw, status, needle):
+    st = _bwd(lib, **kw)
+    assert st == status
+    assert needle in lib.kda_last_error_message().decode()
