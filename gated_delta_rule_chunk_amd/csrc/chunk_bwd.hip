@@ -503,11 +503,461 @@ hipError_t launch_dtype(const BwdArgs& a, hipStream_t s) {
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Matrix-core variant for d_k = 128 and 64-column value slices.
+//
+// Same chunk algebra as above; every dense product with the state or its
+// gradient (W = V - Kg S, Kh dS, dO S^T, dW S^T, U dS^T, the state and
+// state-gradient updates) and the small 16x16 products (T W, T^T dU, dO U^T,
+// dY U^T, dY W^T) run on v_mfma_f32_16x16x4f32, which takes float32
+// operands, so the arithmetic stays float32. One workgroup of 8 waves owns
+// (sequence, head, slice): it first re-runs the forward over the sequence,
+// writing each chunk's entry state to the workspace, then walks the chunks
+// backward. Wave w keeps rows 16w..16w+15 of the state (forward sweep) and of
+// the state gradient (backward sweep) in registers, in the MFMA result layout
+// (lane l: rows 16w + 4(l/16) + i, column 16t + l%16 of tile t).
+//
+// f32 16x16x4 operand layouts (lane l, l16 = l%16, lg = l/16): A[m][k] with
+// m = l16, k = lg; B[k][n] with k = lg, n = l16; D[m][n] with m = 4lg + i
+// (register i), n = l16.
+namespace mf {
+
+constexpr int C = 16, DK = 128, BV = 64, NT = 512;
+constexpr int SP = BV + 4;   // row stride of the [DK][SP] state tiles
+constexpr int KP = DK + 4;   // row stride of [C][KP] per-channel rows
+constexpr int VP = BV + 4;   // row stride of [C][VP] per-column rows
+constexpr int CP = C + 1;
+
+struct Smem {
+    float S[DK][SP];
+    float dS[DK][SP];
+    float Q[C][KP], K[C][KP], G[C][KP], Qh[C][KP], Kg[C][KP], Kh[C][KP];
+    float W[C][VP], U[C][VP], dO[C][VP], dUW[C][VP], dY[C][VP];
+    float KK[C][CP], P[C][CP], T[C][CP], dP[C][CP], dKK[C][CP];
+    float beta[C], EC[DK];
+};
+
+__device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ void load4(const T* p, int64_t i, float* o);
+template <> __device__ __forceinline__ void load4<float>(const float* p, int64_t i, float* o) {
+    const float4 v = *reinterpret_cast<const float4*>(p + i);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+template <> __device__ __forceinline__ void load4<__bf16>(const __bf16* p, int64_t i, float* o) {
+    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p) + i);
+    o[0] = __uint_as_float(u.x << 16);
+    o[1] = __uint_as_float(u.x & 0xffff0000u);
+    o[2] = __uint_as_float(u.y << 16);
+    o[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+
+// Q (optional), K, log2-scaled gate rows and beta of one chunk; V (and dO)
+// columns c0 .. c0+BV. Rows past the sequence's end are zeros.
+template <typename Tin>
+__device__ __forceinline__ void load_chunk(Smem& sm, const BwdArgs& a, const SeqInfo& sq, int h, int64_t t0,
+                                           int rows, int c0, bool with_q) {
+    const int tid = threadIdx.x;
+    {
+        const int r = tid >> 5, c = (tid & 31) * 4;   // 16 rows x 32 quads
+        const bool in = r < rows;
+        const int64_t e = ((sq.b * a.T + t0 + r) * a.H + h) * DK + c;
+        float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f}, z[4] = {0.f, 0.f, 0.f, 0.f};
+        if (in) {
+            load4(static_cast<const Tin*>(a.k), e, x);
+            load4(static_cast<const Tin*>(a.g), e, y);
+            if (with_q) load4(static_cast<const Tin*>(a.q), e, z);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            sm.K[r][c + u] = x[u];
+            sm.G[r][c + u] = y[u] * kLog2e;
+            if (with_q) sm.Q[r][c + u] = z[u];
+        }
+    }
+    if (tid < 256) {
+        const int r = tid >> 4, j = (tid & 15) * 4;   // 16 rows x 16 quads
+        const int64_t e = ((sq.b * a.T + t0 + r) * a.H + h) * (int64_t)a.Dv + c0 + j;
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        if (r < rows) load4(static_cast<const Tin*>(a.v), e, x);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sm.W[r][j + u] = x[u];
+    } else if (with_q) {
+        const int t2 = tid - 256;
+        const int r = t2 >> 4, j = (t2 & 15) * 4;
+        const int64_t e = ((sq.b * a.T + t0 + r) * a.H + h) * (int64_t)a.Dv + c0 + j;
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        if (r < rows) load4(static_cast<const Tin*>(a.d_o), e, x);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sm.dO[r][j + u] = x[u];
+    }
+    if (tid < C) sm.beta[tid] = tid < rows ? load_elem(static_cast<const Tin*>(a.beta),
+                                                       (sq.b * a.T + t0 + tid) * a.H + h) : 0.f;
+}
+
+// Gamma (in-chunk cumulative log2 decay), e^Gamma_C, then Kg, Kh and (when
+// with_q) Qh; and the pair sums KK (strict lower; zeros elsewhere) and P
+// (lower with diagonal; zeros above), one wave per pair.
+__device__ __forceinline__ void chunk_prep(Smem& sm, bool with_q) {
+    const int tid = threadIdx.x;
+    if (tid < DK) {
+        float run = 0.f;
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            run += sm.G[r][tid];
+            sm.G[r][tid] = run;
+        }
+        sm.EC[tid] = __builtin_amdgcn_exp2f(run);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int idx = tid + NT * u;
+        const int r = idx / DK, c = idx % DK;
+        const float gr = sm.G[r][c];
+        const float e = __builtin_amdgcn_exp2f(gr);
+        const float k = sm.K[r][c];
+        sm.Kg[r][c] = e * k;
+        sm.Kh[r][c] = __builtin_amdgcn_exp2f(sm.G[C - 1][c] - gr) * k;
+        if (with_q) sm.Qh[r][c] = e * sm.Q[r][c];
+    }
+    const int lane = tid & 63, w = tid >> 6;
+    for (int p = w; p < kPairs; p += NT / 64) {
+        int r, s;
+        pair_rs(p, r, s);
+        float ak = 0.f, ap = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int c = lane + 64 * u;
+            const float ks = sm.K[s][c] * __builtin_amdgcn_exp2f(sm.G[r][c] - sm.G[s][c]);
+            ak += sm.K[r][c] * ks;
+            if (with_q) ap += sm.Q[r][c] * ks;
+        }
+        ak = wave_sum(ak);
+        if (with_q) ap = wave_sum(ap);
+        if (lane == 0) {
+            sm.KK[r][s] = s < r ? ak : 0.f;
+            if (s < r) sm.KK[s][r] = 0.f;
+            if (with_q) {
+                sm.P[r][s] = ap;
+                if (s < r) sm.P[s][r] = 0.f;
+            }
+        }
+    }
+}
+
+// T = (I + Diag(beta) KK)^-1 by forward substitution; lane i < 16 of the
+// calling wave owns column i in registers.
+__device__ __forceinline__ void invert_T(Smem& sm, int lane) {
+    if (lane < C) {
+        const int i = lane;
+        float tc[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < r; ++s) acc += sm.KK[r][s] * tc[s];
+            tc[r] = r < i ? 0.f : (r == i ? 1.f : -sm.beta[r] * acc);
+        }
+#pragma unroll
+        for (int r = 0; r < C; ++r) sm.T[r][i] = tc[r];
+    }
+}
+
+// W = V - Kg S for columns 16t..16t+15 (sm.W holds V on entry).
+__device__ __forceinline__ void w_tile(Smem& sm, int t, int l16, int lg) {
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+    for (int ks = 0; ks < DK / 4; ks += 2) {
+        a0 = mfma(sm.Kg[l16][4 * ks + lg], sm.S[4 * ks + lg][16 * t + l16], a0);
+        a1 = mfma(sm.Kg[l16][4 * ks + 4 + lg], sm.S[4 * ks + 4 + lg][16 * t + l16], a1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.W[4 * lg + i][16 * t + l16] -= a0[i] + a1[i];
+}
+
+// U = T Diag(beta) W for columns 16t..16t+15.
+__device__ __forceinline__ void u_tile(Smem& sm, int t, int l16, int lg) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C / 4; ++ks) {
+        const int s = 4 * ks + lg;
+        acc = mfma(sm.T[l16][s], sm.beta[s] * sm.W[s][16 * t + l16], acc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.U[4 * lg + i][16 * t + l16] = acc[i];
+}
+
+template <typename Tin>
+__global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
+    __shared__ Smem sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
+    const int nvt = a.Dv / BV;
+    const bool atomic = nvt > 1;
+    const int vt = blockIdx.x % nvt, unit = blockIdx.x / nvt;
+    const int n = unit / a.H, h = unit % a.H;
+    const int H = a.H, Dv = a.Dv, c0 = vt * BV;
+    const float scale = a.scale;
+    const SeqInfo sq = seq_info(a, n);
+    const int64_t sbase = ((int64_t)n * H + h) * DK * (int64_t)Dv;
+    const int64_t slot_stride = (int64_t)H * DK * Dv;
+    const int64_t nch = (sq.len + C - 1) / C;
+    const int cw = 16 * w;   // this wave's state rows / channel tile
+
+    // ---------------- forward sweep: chunk entry states ----------------
+    f32x4 st[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            st[t][i] = a.s0 ? a.s0[sbase + (int64_t)(cw + 4 * lg + i) * Dv + c0 + 16 * t + l16] : 0.f;
+    for (int64_t ch = 0; ch < nch; ++ch) {
+        const int64_t t0 = sq.bos + ch * C;
+        const int rows = (int)min<int64_t>(C, sq.len - ch * C);
+        float* ws = a.ws + (sq.slot0 + ch) * slot_stride + (int64_t)h * DK * Dv + c0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = cw + 4 * lg + i, j = 16 * t + l16;
+                ws[(int64_t)c * Dv + j] = st[t][i];
+                sm.S[c][j] = st[t][i];
+            }
+        load_chunk<Tin>(sm, a, sq, h, t0, rows, c0, false);
+        __syncthreads();
+        chunk_prep(sm, false);
+        __syncthreads();
+        if (w < 4) w_tile(sm, w, l16, lg);
+        if (w == 4) invert_T(sm, lane);
+        __syncthreads();
+        if (w < 4) u_tile(sm, w, l16, lg);
+        __syncthreads();
+        // S <- Diag(e^Gamma_C) S + Kh^T U
+        {
+            float ak[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) ak[ks] = sm.Kh[4 * ks + lg][cw + l16];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                f32x4 acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = sm.EC[cw + 4 * lg + i] * st[t][i];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) acc = mfma(ak[ks], sm.U[4 * ks + lg][16 * t + l16], acc);
+                st[t] = acc;
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---------------- backward sweep ----------------
+    f32x4 ds[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ds[t][i] = a.d_final ? a.d_final[sbase + (int64_t)(cw + 4 * lg + i) * Dv + c0 + 16 * t + l16] : 0.f;
+    for (int64_t ch = nch - 1; ch >= 0; --ch) {
+        const int64_t t0 = sq.bos + ch * C;
+        const int rows = (int)min<int64_t>(C, sq.len - ch * C);
+        const float* ws = a.ws + (sq.slot0 + ch) * slot_stride + (int64_t)h * DK * Dv + c0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q4 = tid + NT * u;             // 128 rows x 16 quads
+            const int c = q4 >> 4, j = (q4 & 15) * 4;
+            const float4 v = *reinterpret_cast<const float4*>(ws + (int64_t)c * Dv + j);
+            sm.S[c][j] = v.x; sm.S[c][j + 1] = v.y; sm.S[c][j + 2] = v.z; sm.S[c][j + 3] = v.w;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.dS[cw + 4 * lg + i][16 * t + l16] = ds[t][i];
+        load_chunk<Tin>(sm, a, sq, h, t0, rows, c0, true);
+        __syncthreads();
+        chunk_prep(sm, true);
+        __syncthreads();
+        // W = V - Kg S (waves 0-3);  dU = scale P^T dO + Kh dS (waves 4-7);  T (wave 0)
+        if (w < 4) {
+            w_tile(sm, w, l16, lg);
+        } else {
+            const int t = w - 4;
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, ap = a0;
+#pragma unroll
+            for (int ks = 0; ks < DK / 4; ks += 2) {
+                a0 = mfma(sm.Kh[l16][4 * ks + lg], sm.dS[4 * ks + lg][16 * t + l16], a0);
+                a1 = mfma(sm.Kh[l16][4 * ks + 4 + lg], sm.dS[4 * ks + 4 + lg][16 * t + l16], a1);
+            }
+#pragma unroll
+            for (int ks = 0; ks < C / 4; ++ks)
+                ap = mfma(sm.P[4 * ks + lg][l16], sm.dO[4 * ks + lg][16 * t + l16], ap);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.dUW[4 * lg + i][16 * t + l16] = a0[i] + a1[i] + scale * ap[i];
+        }
+        if (w == 0) invert_T(sm, lane);
+        __syncthreads();
+        // U = T Diag(beta) W (waves 0-3);  dY = T^T dU (waves 4-7)
+        if (w < 4) {
+            u_tile(sm, w, l16, lg);
+        } else {
+            const int t = w - 4;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < C / 4; ++ks)
+                acc = mfma(sm.T[4 * ks + lg][l16], sm.dUW[4 * ks + lg][16 * t + l16], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.dY[4 * lg + i][16 * t + l16] = acc[i];
+        }
+        __syncthreads();
+        // dP = scale dO U^T (wave 0);  dM = -dY U^T, dbeta (wave 1);  dW = Diag(beta) dY (all)
+        if (w == 0) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < BV / 4; ++ks)
+                acc = mfma(sm.dO[l16][4 * ks + lg], sm.U[l16][4 * ks + lg], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i;
+                sm.dP[r][l16] = l16 <= r ? scale * acc[i] : 0.f;
+            }
+        } else if (w == 1) {
+            f32x4 am = {0.f, 0.f, 0.f, 0.f}, ax = am;
+#pragma unroll
+            for (int ks = 0; ks < BV / 4; ++ks) {
+                const float dy = sm.dY[l16][4 * ks + lg];
+                am = mfma(dy, sm.U[l16][4 * ks + lg], am);
+                ax = mfma(dy, sm.W[l16][4 * ks + lg], ax);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i, s = l16;
+                const float dm = s < r ? -am[i] : 0.f;
+                sm.dKK[r][s] = sm.beta[r] * dm;
+                float part = dm * sm.KK[r][s] + (s == r ? ax[i] : 0.f);
+#pragma unroll
+                for (int m = 1; m < 16; m <<= 1) part += __shfl_xor(part, m, 64);
+                if (s == 0 && r < rows) add_out(a.dbeta + (sq.b * a.T + t0 + r) * H + h, part, atomic);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int idx = tid + NT * u;
+            const int r = idx / BV, j = idx % BV;
+            const float dw = sm.beta[r] * sm.dY[r][j];
+            sm.dUW[r][j] = dw;
+            if (r < rows) a.dv[((sq.b * a.T + t0 + r) * H + h) * (int64_t)Dv + c0 + j] = dw;
+        }
+        __syncthreads();
+        // Per channel tile cw..cw+15: dense terms, pair terms, dq, dk, dg; then dS.
+        {
+            const int c = cw + l16;
+            f32x4 ao = {0.f, 0.f, 0.f, 0.f}, aw = ao, ad = ao;
+#pragma unroll
+            for (int ks = 0; ks < BV / 4; ++ks) {
+                const int j = 4 * ks + lg;
+                const float sv = sm.S[c][j];
+                ao = mfma(sm.dO[l16][j], sv, ao);
+                aw = mfma(sm.dUW[l16][j], sv, aw);
+                ad = mfma(sm.U[l16][j], sm.dS[c][j], ad);
+            }
+            const float gC = sm.G[C - 1][c];
+            float gr[4], accq[4], acckr[4], accks[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                gr[i] = sm.G[4 * lg + i][c];
+                accq[i] = acckr[i] = accks[i] = 0.f;
+            }
+#pragma unroll 2
+            for (int x = 0; x < C; ++x) {
+                const float gx = sm.G[x][c], kx = sm.K[x][c], qx = sm.Q[x][c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * lg + i;
+                    // later-minus-earlier exponent of the pair {r, x}
+                    const float e = __builtin_amdgcn_exp2f(x <= r ? gr[i] - gx : gx - gr[i]);
+                    const float ke = kx * e;
+                    accq[i] += sm.dP[r][x] * ke;
+                    acckr[i] += sm.dKK[r][x] * ke;
+                    accks[i] += (sm.dP[x][r] * qx + sm.dKK[x][r] * kx) * e;
+                }
+            }
+            float dG[4], kh_ad = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i;
+                const float qr = sm.Q[r][c], kr = sm.K[r][c];
+                const float eg = __builtin_amdgcn_exp2f(gr[i]);
+                const float eh = __builtin_amdgcn_exp2f(gC - gr[i]);
+                const float qh = eg * qr, kg = eg * kr, kh = eh * kr;
+                const float dq = accq[i] + eg * scale * ao[i];
+                const float dk = acckr[i] + accks[i] - eg * aw[i] + eh * ad[i];
+                dG[i] = qr * accq[i] + kr * acckr[i] - kr * accks[i] + qh * scale * ao[i] - kg * aw[i] - kh * ad[i];
+                kh_ad += kh * ad[i];
+                if (r < rows) {
+                    const int64_t e2 = ((sq.b * a.T + t0 + r) * H + h) * DK + c;
+                    add_out(a.dq + e2, dq, atomic);
+                    add_out(a.dk + e2, dk, atomic);
+                }
+            }
+            // Gamma_C's gradient: sum_r Kh*ad (over the 16 rows) + e^Gamma_C sum_j dS S
+            float sds = 0.f;
+#pragma unroll
+            for (int m = 0; m < BV / 4; ++m) sds += sm.dS[c][lg + 4 * m] * sm.S[c][lg + 4 * m];
+            float gsum = kh_ad + sm.EC[c] * sds;
+            gsum += __shfl_xor(gsum, 16, 64);
+            gsum += __shfl_xor(gsum, 32, 64);
+            // dg = reverse cumulative sum of dGamma over the chunk, plus gsum
+            const float s3 = dG[3], s2 = dG[2] + s3, s1 = dG[1] + s2, s0v = dG[0] + s1;
+            const float t1 = __shfl(s0v, l16 + 16, 64), t2 = __shfl(s0v, l16 + 32, 64),
+                        t3 = __shfl(s0v, l16 + 48, 64);
+            const float above = (lg < 1 ? t1 : 0.f) + (lg < 2 ? t2 : 0.f) + (lg < 3 ? t3 : 0.f) + gsum;
+            const float sfx[4] = {s0v, s1, s2, s3};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i;
+                if (r < rows) add_out(a.dg + ((sq.b * a.T + t0 + r) * H + h) * DK + c, sfx[i] + above, atomic);
+            }
+            // dS <- Diag(e^Gamma_C) dS + scale Qh^T dO - Kg^T dW   (rows cw..cw+15)
+            float aq[4], akg[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                aq[ks] = scale * sm.Qh[4 * ks + lg][cw + l16];
+                akg[ks] = -sm.Kg[4 * ks + lg][cw + l16];
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                f32x4 acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = sm.EC[cw + 4 * lg + i] * ds[t][i];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    acc = mfma(aq[ks], sm.dO[4 * ks + lg][16 * t + l16], acc);
+                    acc = mfma(akg[ks], sm.dUW[4 * ks + lg][16 * t + l16], acc);
+                }
+                ds[t] = acc;
+            }
+        }
+        __syncthreads();
+    }
+    if (a.d_s0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a.d_s0[sbase + (int64_t)(cw + 4 * lg + i) * Dv + c0 + 16 * t + l16] = ds[t][i];
+    }
+}
+
+}  // namespace mf
 }  // namespace
 
 int64_t chunk_bwd_slots(int32_t B, int32_t T, int32_t N, bool packed) {
     return packed ? (int64_t)T / kBC + N : (int64_t)B * ((T + kBC - 1) / kBC);
 }
+
+bool chunk_bwd_mfma_supported(const BwdArgs& a);
 
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s) {
     const int nvt = a.Dv / (a.Dv >= 64 ? 64 : a.Dv);
@@ -519,7 +969,18 @@ hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s) {
         if ((e = zero_fill(a.dg, rows * a.Dk, s)) != hipSuccess) return e;
         if ((e = zero_fill(a.dbeta, rows, s)) != hipSuccess) return e;
     }
+    if (chunk_bwd_mfma_supported(a)) {
+        const int64_t grid = (int64_t)a.N * a.H * (a.Dv / mf::BV);
+        if (grid == 0) return hipSuccess;
+        if (a.bf16)
+            mf::chunk_bwd_mfma_kernel<__bf16><<<dim3((unsigned)grid), dim3(mf::NT), 0, s>>>(a);
+        else
+            mf::chunk_bwd_mfma_kernel<float><<<dim3((unsigned)grid), dim3(mf::NT), 0, s>>>(a);
+        return hipGetLastError();
+    }
     return a.bf16 ? launch_dtype<__bf16>(a, s) : launch_dtype<float>(a, s);
 }
+
+bool chunk_bwd_mfma_supported(const BwdArgs& a) { return a.Dk == 128 && (a.Dv == 64 || a.Dv == 128); }
 
 }  // namespace kda

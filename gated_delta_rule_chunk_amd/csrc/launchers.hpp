@@ -92,6 +92,7 @@ struct BwdArgs {
 // Number of chunk-state slots the backward's workspace holds.
 int64_t chunk_bwd_slots(int32_t B, int32_t T, int32_t N, bool packed);
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s);
+bool chunk_bwd_mfma_supported(const BwdArgs& a);   // Dk = 128, Dv in {64, 128}
 
 hipError_t launch_short_conv(const ConvArgs& a, hipStream_t s);
 hipError_t launch_short_conv_step(const ConvStepArgs& a, hipStream_t s);
