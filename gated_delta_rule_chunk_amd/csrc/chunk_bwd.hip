@@ -528,11 +528,14 @@ constexpr int SP = BV + 4;   // row stride of the [DK][SP] state tiles
 constexpr int KP = DK + 4;   // row stride of [C][KP] per-channel rows
 constexpr int VP = BV + 4;   // row stride of [C][VP] per-column rows
 constexpr int CP = C + 1;
+constexpr int kRef = 7;      // reference row of the factored pair exponentials
+constexpr int kMats = 3 * C * C;   // T, P, KK of one chunk, kept for the reverse sweep
 
 struct Smem {
     float S[DK][SP];
     float dS[DK][SP];
-    float Q[C][KP], K[C][KP], G[C][KP], Qh[C][KP], Kg[C][KP], Kh[C][KP];
+    float G[C][KP];
+    float Qh[C][KP], Kg[C][KP], Kh[C][KP], Qp[C][KP], Kp[C][KP], Km[C][KP];
     float W[C][VP], U[C][VP], dO[C][VP], dUW[C][VP], dY[C][VP];
     float KK[C][CP], P[C][CP], T[C][CP], dP[C][CP], dKK[C][CP];
     float beta[C], EC[DK];
@@ -555,27 +558,27 @@ template <> __device__ __forceinline__ void load4<__bf16>(const __bf16* p, int64
     o[3] = __uint_as_float(u.y & 0xffff0000u);
 }
 
-// Q (optional), K, log2-scaled gate rows and beta of one chunk; V (and dO)
-// columns c0 .. c0+BV. Rows past the sequence's end are zeros.
+// Raw q (into Qh), k (into Kg), log2-scaled gate rows and beta of one chunk;
+// V (into W) and, when with_do, dO for columns c0 .. c0+BV. Rows past the
+// sequence's end are zeros.
 template <typename Tin>
 __device__ __forceinline__ void load_chunk(Smem& sm, const BwdArgs& a, const SeqInfo& sq, int h, int64_t t0,
-                                           int rows, int c0, bool with_q) {
+                                           int rows, int c0, bool with_do) {
     const int tid = threadIdx.x;
     {
         const int r = tid >> 5, c = (tid & 31) * 4;   // 16 rows x 32 quads
-        const bool in = r < rows;
         const int64_t e = ((sq.b * a.T + t0 + r) * a.H + h) * DK + c;
         float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f}, z[4] = {0.f, 0.f, 0.f, 0.f};
-        if (in) {
+        if (r < rows) {
             load4(static_cast<const Tin*>(a.k), e, x);
             load4(static_cast<const Tin*>(a.g), e, y);
-            if (with_q) load4(static_cast<const Tin*>(a.q), e, z);
+            load4(static_cast<const Tin*>(a.q), e, z);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            sm.K[r][c + u] = x[u];
+            sm.Kg[r][c + u] = x[u];
             sm.G[r][c + u] = y[u] * kLog2e;
-            if (with_q) sm.Q[r][c + u] = z[u];
+            sm.Qh[r][c + u] = z[u];
         }
     }
     if (tid < 256) {
@@ -585,7 +588,7 @@ __device__ __forceinline__ void load_chunk(Smem& sm, const BwdArgs& a, const Seq
         if (r < rows) load4(static_cast<const Tin*>(a.v), e, x);
 #pragma unroll
         for (int u = 0; u < 4; ++u) sm.W[r][j + u] = x[u];
-    } else if (with_q) {
+    } else if (with_do) {
         const int t2 = tid - 256;
         const int r = t2 >> 4, j = (t2 & 15) * 4;
         const int64_t e = ((sq.b * a.T + t0 + r) * a.H + h) * (int64_t)a.Dv + c0 + j;
@@ -598,10 +601,15 @@ __device__ __forceinline__ void load_chunk(Smem& sm, const BwdArgs& a, const Seq
                                                        (sq.b * a.T + t0 + tid) * a.H + h) : 0.f;
 }
 
-// Gamma (in-chunk cumulative log2 decay), e^Gamma_C, then Kg, Kh and (when
-// with_q) Qh; and the pair sums KK (strict lower; zeros elsewhere) and P
-// (lower with diagonal; zeros above), one wave per pair.
-__device__ __forceinline__ void chunk_prep(Smem& sm, bool with_q) {
+// Gamma (in-chunk cumulative log2 decay) and e^Gamma_C; then, per (row,
+// channel), the scaled rows used by the products:
+//   Qh = e^Gamma q, Kg = e^Gamma k, Kh = e^(Gamma_C - Gamma) k,
+//   Qp = e^(Gamma - Gamma_ref) q, Kp = e^(Gamma - Gamma_ref) k, Km = e^(Gamma_ref - Gamma) k
+// with Gamma_ref the row kRef, so that the pair factor
+// e^(Gamma_r - Gamma_s) = e^(Gamma_r - Gamma_ref) e^(Gamma_ref - Gamma_s) and
+// KK = Kp Km^T, P = Qp Km^T become matrix products. With g >= -5 every
+// exponent here stays within 2^58.
+__device__ __forceinline__ void chunk_scale(Smem& sm) {
     const int tid = threadIdx.x;
     if (tid < DK) {
         float run = 0.f;
@@ -617,35 +625,34 @@ __device__ __forceinline__ void chunk_prep(Smem& sm, bool with_q) {
     for (int u = 0; u < 4; ++u) {
         const int idx = tid + NT * u;
         const int r = idx / DK, c = idx % DK;
-        const float gr = sm.G[r][c];
-        const float e = __builtin_amdgcn_exp2f(gr);
-        const float k = sm.K[r][c];
-        sm.Kg[r][c] = e * k;
+        const float gr = sm.G[r][c], gref = sm.G[kRef][c];
+        const float q = sm.Qh[r][c], k = sm.Kg[r][c];
+        const float eg = __builtin_amdgcn_exp2f(gr);
+        const float ep = __builtin_amdgcn_exp2f(gr - gref);
+        const float em = __builtin_amdgcn_exp2f(gref - gr);
+        sm.Qh[r][c] = eg * q;
+        sm.Kg[r][c] = eg * k;
         sm.Kh[r][c] = __builtin_amdgcn_exp2f(sm.G[C - 1][c] - gr) * k;
-        if (with_q) sm.Qh[r][c] = e * sm.Q[r][c];
+        sm.Qp[r][c] = ep * q;
+        sm.Kp[r][c] = ep * k;
+        sm.Km[r][c] = em * k;
     }
-    const int lane = tid & 63, w = tid >> 6;
-    for (int p = w; p < kPairs; p += NT / 64) {
-        int r, s;
-        pair_rs(p, r, s);
-        float ak = 0.f, ap = 0.f;
+}
+
+// X Km^T over the 128 channels for X = Kp (KK, kept strictly lower) or
+// X = Qp (P, kept lower with the diagonal); zeros elsewhere.
+__device__ __forceinline__ void pair_matrix(Smem& sm, const float (*X)[KP], float (*dst)[CP], bool diag,
+                                            int l16, int lg) {
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int c = lane + 64 * u;
-            const float ks = sm.K[s][c] * __builtin_amdgcn_exp2f(sm.G[r][c] - sm.G[s][c]);
-            ak += sm.K[r][c] * ks;
-            if (with_q) ap += sm.Q[r][c] * ks;
-        }
-        ak = wave_sum(ak);
-        if (with_q) ap = wave_sum(ap);
-        if (lane == 0) {
-            sm.KK[r][s] = s < r ? ak : 0.f;
-            if (s < r) sm.KK[s][r] = 0.f;
-            if (with_q) {
-                sm.P[r][s] = ap;
-                if (s < r) sm.P[s][r] = 0.f;
-            }
-        }
+    for (int ks = 0; ks < DK / 4; ks += 2) {
+        a0 = mfma(X[l16][4 * ks + lg], sm.Km[l16][4 * ks + lg], a0);
+        a1 = mfma(X[l16][4 * ks + 4 + lg], sm.Km[l16][4 * ks + 4 + lg], a1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * lg + i, s = l16;
+        dst[r][s] = (s < r || (diag && s == r)) ? a0[i] + a1[i] : 0.f;
     }
 }
 
@@ -706,8 +713,11 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
     const int64_t slot_stride = (int64_t)H * DK * Dv;
     const int64_t nch = (sq.len + C - 1) / C;
     const int cw = 16 * w;   // this wave's state rows / channel tile
+    // T, P and KK of every chunk, per (slot, head, slice), after the states
+    float* mats = a.ws + chunk_bwd_slots(a.B, a.T, a.N, a.cu != nullptr) * slot_stride;
+    auto mats_of = [&](int64_t ch) { return mats + (((sq.slot0 + ch) * H + h) * nvt + vt) * kMats; };
 
-    // ---------------- forward sweep: chunk entry states ----------------
+    // ---------------- forward sweep: entry states, T, P, KK ----------------
     f32x4 st[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -728,12 +738,24 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
             }
         load_chunk<Tin>(sm, a, sq, h, t0, rows, c0, false);
         __syncthreads();
-        chunk_prep(sm, false);
+        chunk_scale(sm);
         __syncthreads();
-        if (w < 4) w_tile(sm, w, l16, lg);
-        if (w == 4) invert_T(sm, lane);
+        if (w == 0) pair_matrix(sm, sm.Kp, sm.KK, false, l16, lg);
+        else if (w == 1) pair_matrix(sm, sm.Qp, sm.P, true, l16, lg);
+        else if (w < 6) w_tile(sm, w - 2, l16, lg);
+        __syncthreads();
+        if (w == 0) invert_T(sm, lane);
         __syncthreads();
         if (w < 4) u_tile(sm, w, l16, lg);
+        {
+            float* m = mats_of(ch);
+            if (tid < C * C) {
+                const int r = tid / C, s = tid % C;
+                m[tid] = sm.T[r][s];
+                m[C * C + tid] = sm.P[r][s];
+                m[2 * C * C + tid] = sm.KK[r][s];
+            }
+        }
         __syncthreads();
         // S <- Diag(e^Gamma_C) S + Kh^T U
         {
@@ -771,15 +793,22 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
             const float4 v = *reinterpret_cast<const float4*>(ws + (int64_t)c * Dv + j);
             sm.S[c][j] = v.x; sm.S[c][j + 1] = v.y; sm.S[c][j + 2] = v.z; sm.S[c][j + 3] = v.w;
         }
+        if (tid < C * C) {
+            const float* m = mats_of(ch);
+            const int r = tid / C, s = tid % C;
+            sm.T[r][s] = m[tid];
+            sm.P[r][s] = m[C * C + tid];
+            sm.KK[r][s] = m[2 * C * C + tid];
+        }
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) sm.dS[cw + 4 * lg + i][16 * t + l16] = ds[t][i];
         load_chunk<Tin>(sm, a, sq, h, t0, rows, c0, true);
         __syncthreads();
-        chunk_prep(sm, true);
+        chunk_scale(sm);
         __syncthreads();
-        // W = V - Kg S (waves 0-3);  dU = scale P^T dO + Kh dS (waves 4-7);  T (wave 0)
+        // W = V - Kg S (waves 0-3);  dU = scale P^T dO + Kh dS (waves 4-7)
         if (w < 4) {
             w_tile(sm, w, l16, lg);
         } else {
@@ -796,7 +825,6 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) sm.dUW[4 * lg + i][16 * t + l16] = a0[i] + a1[i] + scale * ap[i];
         }
-        if (w == 0) invert_T(sm, lane);
         __syncthreads();
         // U = T Diag(beta) W (waves 0-3);  dY = T^T dU (waves 4-7)
         if (w < 4) {
@@ -811,7 +839,8 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
             for (int i = 0; i < 4; ++i) sm.dY[4 * lg + i][16 * t + l16] = acc[i];
         }
         __syncthreads();
-        // dP = scale dO U^T (wave 0);  dM = -dY U^T, dbeta (wave 1);  dW = Diag(beta) dY (all)
+        // dP = scale dO U^T (wave 0);  dKK = -Diag(beta) dY U^T and dbeta (wave 1);
+        // dW = Diag(beta) dY = dV (all)
         if (w == 0) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -850,7 +879,8 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
             if (r < rows) a.dv[((sq.b * a.T + t0 + r) * H + h) * (int64_t)Dv + c0 + j] = dw;
         }
         __syncthreads();
-        // Per channel tile cw..cw+15: dense terms, pair terms, dq, dk, dg; then dS.
+        // Channel tile cw..cw+15 of this wave: dense terms, pair terms, dq,
+        // dk, dg, then the state gradient's rows cw..cw+15.
         {
             const int c = cw + l16;
             f32x4 ao = {0.f, 0.f, 0.f, 0.f}, aw = ao, ad = ao;
@@ -862,38 +892,33 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
                 aw = mfma(sm.dUW[l16][j], sv, aw);
                 ad = mfma(sm.U[l16][j], sm.dS[c][j], ad);
             }
-            const float gC = sm.G[C - 1][c];
-            float gr[4], accq[4], acckr[4], accks[4];
+            // pair terms, factored through the reference row:
+            //   Aq = dP Km, Akr = dKK Km, Aks = dP^T Qp + dKK^T Kp
+            f32x4 aq = {0.f, 0.f, 0.f, 0.f}, akr = aq, aks = aq;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                gr[i] = sm.G[4 * lg + i][c];
-                accq[i] = acckr[i] = accks[i] = 0.f;
+            for (int ks = 0; ks < C / 4; ++ks) {
+                const int s = 4 * ks + lg;
+                const float km = sm.Km[s][c];
+                aq = mfma(sm.dP[l16][s], km, aq);
+                akr = mfma(sm.dKK[l16][s], km, akr);
+                aks = mfma(sm.dP[s][l16], sm.Qp[s][c], aks);
+                aks = mfma(sm.dKK[s][l16], sm.Kp[s][c], aks);
             }
-#pragma unroll 2
-            for (int x = 0; x < C; ++x) {
-                const float gx = sm.G[x][c], kx = sm.K[x][c], qx = sm.Q[x][c];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * lg + i;
-                    // later-minus-earlier exponent of the pair {r, x}
-                    const float e = __builtin_amdgcn_exp2f(x <= r ? gr[i] - gx : gx - gr[i]);
-                    const float ke = kx * e;
-                    accq[i] += sm.dP[r][x] * ke;
-                    acckr[i] += sm.dKK[r][x] * ke;
-                    accks[i] += (sm.dP[x][r] * qx + sm.dKK[x][r] * kx) * e;
-                }
-            }
+            const float gC = sm.G[C - 1][c], gref = sm.G[kRef][c];
             float dG[4], kh_ad = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * lg + i;
-                const float qr = sm.Q[r][c], kr = sm.K[r][c];
-                const float eg = __builtin_amdgcn_exp2f(gr[i]);
-                const float eh = __builtin_amdgcn_exp2f(gC - gr[i]);
-                const float qh = eg * qr, kg = eg * kr, kh = eh * kr;
-                const float dq = accq[i] + eg * scale * ao[i];
-                const float dk = acckr[i] + accks[i] - eg * aw[i] + eh * ad[i];
-                dG[i] = qr * accq[i] + kr * acckr[i] - kr * accks[i] + qh * scale * ao[i] - kg * aw[i] - kh * ad[i];
+                const float gr = sm.G[r][c];
+                const float eg = __builtin_amdgcn_exp2f(gr);
+                const float eh = __builtin_amdgcn_exp2f(gC - gr);
+                const float ep = __builtin_amdgcn_exp2f(gr - gref);
+                const float em = __builtin_amdgcn_exp2f(gref - gr);
+                const float qh = sm.Qh[r][c], kg = sm.Kg[r][c], kh = sm.Kh[r][c];
+                const float dq = ep * aq[i] + eg * scale * ao[i];
+                const float dk = ep * akr[i] + em * aks[i] - eg * aw[i] + eh * ad[i];
+                dG[i] = sm.Qp[r][c] * aq[i] + sm.Kp[r][c] * akr[i] - sm.Km[r][c] * aks[i] + qh * scale * ao[i] -
+                        kg * aw[i] - kh * ad[i];
                 kh_ad += kh * ad[i];
                 if (r < rows) {
                     const int64_t e2 = ((sq.b * a.T + t0 + r) * H + h) * DK + c;
@@ -901,7 +926,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
                     add_out(a.dk + e2, dk, atomic);
                 }
             }
-            // Gamma_C's gradient: sum_r Kh*ad (over the 16 rows) + e^Gamma_C sum_j dS S
+            // Gamma_C's gradient: sum_r Kh*ad over the 16 rows + e^Gamma_C sum_j dS S
             float sds = 0.f;
 #pragma unroll
             for (int m = 0; m < BV / 4; ++m) sds += sm.dS[c][lg + 4 * m] * sm.S[c][lg + 4 * m];
@@ -920,10 +945,10 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
                 if (r < rows) add_out(a.dg + ((sq.b * a.T + t0 + r) * H + h) * DK + c, sfx[i] + above, atomic);
             }
             // dS <- Diag(e^Gamma_C) dS + scale Qh^T dO - Kg^T dW   (rows cw..cw+15)
-            float aq[4], akg[4];
+            float aqh[4], akg[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                aq[ks] = scale * sm.Qh[4 * ks + lg][cw + l16];
+                aqh[ks] = scale * sm.Qh[4 * ks + lg][cw + l16];
                 akg[ks] = -sm.Kg[4 * ks + lg][cw + l16];
             }
 #pragma unroll
@@ -933,7 +958,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
                 for (int i = 0; i < 4; ++i) acc[i] = sm.EC[cw + 4 * lg + i] * ds[t][i];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    acc = mfma(aq[ks], sm.dO[4 * ks + lg][16 * t + l16], acc);
+                    acc = mfma(aqh[ks], sm.dO[4 * ks + lg][16 * t + l16], acc);
                     acc = mfma(akg[ks], sm.dUW[4 * ks + lg][16 * t + l16], acc);
                 }
                 ds[t] = acc;
@@ -953,9 +978,6 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
 }  // namespace mf
 }  // namespace
 
-int64_t chunk_bwd_slots(int32_t B, int32_t T, int32_t N, bool packed) {
-    return packed ? (int64_t)T / kBC + N : (int64_t)B * ((T + kBC - 1) / kBC);
-}
 
 bool chunk_bwd_mfma_supported(const BwdArgs& a);
 

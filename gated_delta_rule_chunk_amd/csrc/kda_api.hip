@@ -138,8 +138,7 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
 size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
                                      int32_t packed) {
     if (B < 1 || T <= 0 || H < 1 || Dk < 1 || Dv < 1 || N < 0) return 0;
-    const int64_t slots = kda::chunk_bwd_slots(B, T, N, packed != 0);
-    return (size_t)slots * (size_t)H * (size_t)Dk * (size_t)Dv * sizeof(float);
+    return (size_t)kda::chunk_bwd_ws_floats(B, T, H, Dk, Dv, N, packed != 0) * sizeof(float);
 }
 
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,

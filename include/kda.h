@@ -122,10 +122,11 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
                                   float* final_state, void* stream);
 
 /*
- * Bytes of device workspace kda_chunk_bwd needs: one float32 state
- * [H,Dk,Dv] per 16-row chunk slot, T/16 + N slots for packed sequences
- * (packed != 0), B * ceil(T/16) otherwise. 0 when T = 0 or a size is out of
- * range.
+ * Bytes of device workspace kda_chunk_bwd needs: per 16-row chunk slot and
+ * head, one float32 state [Dk,Dv] plus three float32 16x16 matrices per
+ * 64-column value slice (one slice when Dv < 64); T/16 + N slots for packed
+ * sequences (packed != 0), B * ceil(T/16) otherwise. 0 when T = 0 or a size
+ * is out of range.
  */
 size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
                                      int32_t packed);
@@ -152,8 +153,11 @@ size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk
  *             an input or the workspace
  *   d_initial_state [N,H,Dk,Dv] float32, or NULL (not written)
  *
- * Everything is computed in float32, in 16-row chunks, on the vector ALUs;
- * bf16 inputs are widened exactly. For Dv = 128 the two 64-column halves of
+ * Everything is computed in float32, in 16-row chunks; bf16 inputs are
+ * widened exactly. Dk = 128 with Dv = 64 or 128 runs a matrix-core kernel
+ * (float32 MFMA) that factors the in-chunk decay through the chunk's middle
+ * row and so relies on g >= -5 (see the preconditions above); other head
+ * dims run a vector-ALU kernel with no range condition on g. For Dv = 128 the two 64-column halves of
  * the value dimension add their shares of dq, dk, dg and dbeta with float32
  * atomics, which with two terms is order-independent, so the result is
  * deterministic. With T = 0 only d_initial_state is written (it then equals
