@@ -529,7 +529,7 @@ constexpr int KP = DK + 4;   // row stride of [C][KP] per-channel rows
 constexpr int VP = BV + 4;   // row stride of [C][VP] per-column rows
 constexpr int CP = C + 1;
 constexpr int kRef = 7;      // reference row of the factored pair exponentials
-constexpr int kMats = 3 * C * C;   // T, P, KK of one chunk, kept for the reverse sweep
+constexpr int kMats = 3 * C * C;   // T, P, KK of one chunk
 
 struct Smem {
     float S[DK][SP];
@@ -545,71 +545,141 @@ __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <typename T> __device__ __forceinline__ void load4(const T* p, int64_t i, float* o);
-template <> __device__ __forceinline__ void load4<float>(const float* p, int64_t i, float* o) {
-    const float4 v = *reinterpret_cast<const float4*>(p + i);
-    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
-}
-template <> __device__ __forceinline__ void load4<__bf16>(const __bf16* p, int64_t i, float* o) {
-    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p) + i);
-    o[0] = __uint_as_float(u.x << 16);
-    o[1] = __uint_as_float(u.x & 0xffff0000u);
-    o[2] = __uint_as_float(u.y << 16);
-    o[3] = __uint_as_float(u.y & 0xffff0000u);
+// Sum over the 16 lanes of each row of the wave (DPP row shifts); lane 15 of
+// each row ends with the row's total.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+    return v;
 }
 
-// Raw q (into Qh), k (into Kg), log2-scaled gate rows and beta of one chunk;
-// V (into W) and, when with_do, dO for columns c0 .. c0+BV. Rows past the
-// sequence's end are zeros.
+// Four consecutive input elements, raw (float4 or four bf16 in a uint2).
+template <typename T> struct Raw4;
+template <> struct Raw4<float> {
+    float4 v;
+    __device__ __forceinline__ void load(const float* p, int64_t i) { v = *reinterpret_cast<const float4*>(p + i); }
+    __device__ __forceinline__ float get(int u) const { return u == 0 ? v.x : u == 1 ? v.y : u == 2 ? v.z : v.w; }
+};
+template <> struct Raw4<__bf16> {
+    uint2 v;
+    __device__ __forceinline__ void load(const __bf16* p, int64_t i) {
+        v = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p) + i);
+    }
+    __device__ __forceinline__ float get(int u) const {
+        const uint32_t w = u < 2 ? v.x : v.y;
+        return __uint_as_float((u & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+
+// One chunk's global inputs held in registers between issue and commit, so
+// that every load of a chunk is in flight at once. Rows past the sequence's
+// end load row 0 (always in range) and are zeroed at commit.
 template <typename Tin>
-__device__ __forceinline__ void load_chunk(Smem& sm, const BwdArgs& a, const SeqInfo& sq, int h, int64_t t0,
-                                           int rows, int c0, bool with_do) {
+struct Fetch {
+    Raw4<Tin> q, k, g, x;   // x: v for threads < 256, dO for the others
+    float beta;
+    float4 s[4];            // entry state slice (reverse sweep)
+    float m[3];             // T, P, KK entries (threads < 256)
+    bool in_qk, in_x, in_b;
+};
+
+template <typename Tin>
+__device__ __forceinline__ void fetch_chunk(Fetch<Tin>& f, const BwdArgs& a, const SeqInfo& sq, int h, int64_t t0,
+                                            int rows, int c0, bool reverse, const float* ws, const float* mats) {
     const int tid = threadIdx.x;
     {
         const int r = tid >> 5, c = (tid & 31) * 4;   // 16 rows x 32 quads
-        const int64_t e = ((sq.b * a.T + t0 + r) * a.H + h) * DK + c;
-        float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f}, z[4] = {0.f, 0.f, 0.f, 0.f};
-        if (r < rows) {
-            load4(static_cast<const Tin*>(a.k), e, x);
-            load4(static_cast<const Tin*>(a.g), e, y);
-            load4(static_cast<const Tin*>(a.q), e, z);
+        f.in_qk = r < rows;
+        const int64_t e = ((sq.b * a.T + t0 + (f.in_qk ? r : 0)) * a.H + h) * DK + c;
+        f.k.load(static_cast<const Tin*>(a.k), e);
+        f.g.load(static_cast<const Tin*>(a.g), e);
+        if (reverse) f.q.load(static_cast<const Tin*>(a.q), e);
+    }
+    {
+        const int t2 = tid & 255;
+        const int r = t2 >> 4, j = (t2 & 15) * 4;    // 16 rows x 16 quads
+        f.in_x = r < rows;
+        const int64_t e = ((sq.b * a.T + t0 + (f.in_x ? r : 0)) * a.H + h) * (int64_t)a.Dv + c0 + j;
+        if (tid < 256)
+            f.x.load(static_cast<const Tin*>(a.v), e);
+        else if (reverse)
+            f.x.load(static_cast<const Tin*>(a.d_o), e);
+    }
+    {
+        const int r = tid & (C - 1);
+        f.in_b = r < rows;
+        f.beta = load_elem(static_cast<const Tin*>(a.beta), (sq.b * a.T + t0 + (f.in_b ? r : 0)) * a.H + h);
+    }
+    if (tid < C * C) {
+        f.m[0] = mats[tid];
+        if (reverse) {
+            f.m[1] = mats[C * C + tid];
+            f.m[2] = mats[2 * C * C + tid];
         }
+    }
+    if (reverse) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            sm.Kg[r][c + u] = x[u];
-            sm.G[r][c + u] = y[u] * kLog2e;
-            sm.Qh[r][c + u] = z[u];
+            const int q4 = tid + NT * u;             // 128 rows x 16 quads
+            f.s[u] = *reinterpret_cast<const float4*>(ws + (int64_t)(q4 >> 4) * a.Dv + (q4 & 15) * 4);
         }
     }
-    if (tid < 256) {
-        const int r = tid >> 4, j = (tid & 15) * 4;   // 16 rows x 16 quads
-        const int64_t e = ((sq.b * a.T + t0 + r) * a.H + h) * (int64_t)a.Dv + c0 + j;
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-        if (r < rows) load4(static_cast<const Tin*>(a.v), e, x);
+}
+
+template <typename Tin>
+__device__ __forceinline__ void commit_chunk(Smem& sm, const Fetch<Tin>& f, bool reverse) {
+    const int tid = threadIdx.x;
+    {
+        const int r = tid >> 5, c = (tid & 31) * 4;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) sm.W[r][j + u] = x[u];
-    } else if (with_do) {
-        const int t2 = tid - 256;
-        const int r = t2 >> 4, j = (t2 & 15) * 4;
-        const int64_t e = ((sq.b * a.T + t0 + r) * a.H + h) * (int64_t)a.Dv + c0 + j;
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-        if (r < rows) load4(static_cast<const Tin*>(a.d_o), e, x);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) sm.dO[r][j + u] = x[u];
+        for (int u = 0; u < 4; ++u) {
+            sm.Kg[r][c + u] = f.in_qk ? f.k.get(u) : 0.f;
+            sm.G[r][c + u] = f.in_qk ? f.g.get(u) * kLog2e : 0.f;
+            if (reverse) sm.Qh[r][c + u] = f.in_qk ? f.q.get(u) : 0.f;
+        }
     }
-    if (tid < C) sm.beta[tid] = tid < rows ? load_elem(static_cast<const Tin*>(a.beta),
-                                                       (sq.b * a.T + t0 + tid) * a.H + h) : 0.f;
+    {
+        const int t2 = tid & 255;
+        const int r = t2 >> 4, j = (t2 & 15) * 4;
+        if (tid < 256) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sm.W[r][j + u] = f.in_x ? f.x.get(u) : 0.f;
+        } else if (reverse) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sm.dO[r][j + u] = f.in_x ? f.x.get(u) : 0.f;
+        }
+    }
+    if (tid < C) sm.beta[tid] = f.in_b ? f.beta : 0.f;
+    if (tid < C * C) {
+        const int r = tid / C, s = tid % C;
+        sm.T[r][s] = f.m[0];
+        if (reverse) {
+            sm.P[r][s] = f.m[1];
+            sm.KK[r][s] = f.m[2];
+        }
+    }
+    if (reverse) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q4 = tid + NT * u;
+            const int c = q4 >> 4, j = (q4 & 15) * 4;
+            sm.S[c][j] = f.s[u].x; sm.S[c][j + 1] = f.s[u].y; sm.S[c][j + 2] = f.s[u].z; sm.S[c][j + 3] = f.s[u].w;
+        }
+    }
 }
 
 // Gamma (in-chunk cumulative log2 decay) and e^Gamma_C; then, per (row,
-// channel), the scaled rows used by the products:
-//   Qh = e^Gamma q, Kg = e^Gamma k, Kh = e^(Gamma_C - Gamma) k,
-//   Qp = e^(Gamma - Gamma_ref) q, Kp = e^(Gamma - Gamma_ref) k, Km = e^(Gamma_ref - Gamma) k
-// with Gamma_ref the row kRef, so that the pair factor
-// e^(Gamma_r - Gamma_s) = e^(Gamma_r - Gamma_ref) e^(Gamma_ref - Gamma_s) and
-// KK = Kp Km^T, P = Qp Km^T become matrix products. With g >= -5 every
-// exponent here stays within 2^58.
-__device__ __forceinline__ void chunk_scale(Smem& sm) {
+// channel), the scaled rows the products use:
+//   Kg = e^Gamma k, Kh = e^(Gamma_C - Gamma) k, and in the reverse sweep
+//   Qh = e^Gamma q, Qp = e^(Gamma - Gamma_ref) q, Kp = e^(Gamma - Gamma_ref) k,
+//   Km = e^(Gamma_ref - Gamma) k
+// with Gamma_ref the row kRef, so that e^(Gamma_r - Gamma_s) =
+// e^(Gamma_r - Gamma_ref) e^(Gamma_ref - Gamma_s) turns the pair sums and
+// their gradients into matrix products. With g >= -5 every exponent stays
+// within 2^58.
+__device__ __forceinline__ void chunk_scale(Smem& sm, bool reverse) {
     const int tid = threadIdx.x;
     if (tid < DK) {
         float run = 0.f;
@@ -625,52 +695,20 @@ __device__ __forceinline__ void chunk_scale(Smem& sm) {
     for (int u = 0; u < 4; ++u) {
         const int idx = tid + NT * u;
         const int r = idx / DK, c = idx % DK;
-        const float gr = sm.G[r][c], gref = sm.G[kRef][c];
-        const float q = sm.Qh[r][c], k = sm.Kg[r][c];
+        const float gr = sm.G[r][c];
+        const float k = sm.Kg[r][c];
         const float eg = __builtin_amdgcn_exp2f(gr);
-        const float ep = __builtin_amdgcn_exp2f(gr - gref);
-        const float em = __builtin_amdgcn_exp2f(gref - gr);
-        sm.Qh[r][c] = eg * q;
         sm.Kg[r][c] = eg * k;
         sm.Kh[r][c] = __builtin_amdgcn_exp2f(sm.G[C - 1][c] - gr) * k;
-        sm.Qp[r][c] = ep * q;
-        sm.Kp[r][c] = ep * k;
-        sm.Km[r][c] = em * k;
-    }
-}
-
-// X Km^T over the 128 channels for X = Kp (KK, kept strictly lower) or
-// X = Qp (P, kept lower with the diagonal); zeros elsewhere.
-__device__ __forceinline__ void pair_matrix(Smem& sm, const float (*X)[KP], float (*dst)[CP], bool diag,
-                                            int l16, int lg) {
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-#pragma unroll
-    for (int ks = 0; ks < DK / 4; ks += 2) {
-        a0 = mfma(X[l16][4 * ks + lg], sm.Km[l16][4 * ks + lg], a0);
-        a1 = mfma(X[l16][4 * ks + 4 + lg], sm.Km[l16][4 * ks + 4 + lg], a1);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * lg + i, s = l16;
-        dst[r][s] = (s < r || (diag && s == r)) ? a0[i] + a1[i] : 0.f;
-    }
-}
-
-// T = (I + Diag(beta) KK)^-1 by forward substitution; lane i < 16 of the
-// calling wave owns column i in registers.
-__device__ __forceinline__ void invert_T(Smem& sm, int lane) {
-    if (lane < C) {
-        const int i = lane;
-        float tc[C];
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-            float acc = 0.f;
-#pragma unroll
-            for (int s = 0; s < r; ++s) acc += sm.KK[r][s] * tc[s];
-            tc[r] = r < i ? 0.f : (r == i ? 1.f : -sm.beta[r] * acc);
+        if (reverse) {
+            const float gref = sm.G[kRef][c];
+            const float q = sm.Qh[r][c];
+            const float ep = __builtin_amdgcn_exp2f(gr - gref);
+            sm.Qh[r][c] = eg * q;
+            sm.Qp[r][c] = ep * q;
+            sm.Kp[r][c] = ep * k;
+            sm.Km[r][c] = __builtin_amdgcn_exp2f(gref - gr) * k;
         }
-#pragma unroll
-        for (int r = 0; r < C; ++r) sm.T[r][i] = tc[r];
     }
 }
 
@@ -698,6 +736,127 @@ __device__ __forceinline__ void u_tile(Smem& sm, int t, int l16, int lg) {
     for (int i = 0; i < 4; ++i) sm.U[4 * lg + i][16 * t + l16] = acc[i];
 }
 
+// Per (chunk slot, head): T = (I + Diag(beta) KK)^-1, P and KK, which depend
+// on q, k, g and beta only. Every chunk is independent, so this runs over all
+// of them at once ahead of the sequential kernel.
+struct MatsSmem {
+    float G[C][KP], Qp[C][KP], Kp[C][KP], Km[C][KP];
+    float KK[C][CP], beta[C];
+};
+
+template <typename Tin>
+__global__ __launch_bounds__(256) void chunk_mats_kernel(BwdArgs a) {
+    __shared__ MatsSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
+    const int64_t slot = blockIdx.x;
+    const int h = blockIdx.y;
+    int n;
+    int64_t ch;
+    if (a.cu) {   // largest n with cu[n]/16 + n <= slot
+        int lo = 0, hi = a.N - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)a.cu[mid] / C + mid <= slot) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
+        ch = slot - ((int64_t)a.cu[n] / C + n);
+    } else {
+        const int64_t per = (a.T + C - 1) / C;
+        n = (int)(slot / per);
+        ch = slot % per;
+    }
+    const SeqInfo sq = seq_info(a, n);
+    if (ch * C >= sq.len) return;   // a slot no sequence uses (uniform per block)
+    const int64_t t0 = sq.bos + ch * C;
+    const int rows = (int)min<int64_t>(C, sq.len - ch * C);
+    // loads: 16 rows x 32 quads, two quads per thread
+    Raw4<Tin> q[2], k[2], g[2];
+    bool in[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int idx = tid + 256 * u;
+        const int r = idx >> 5, c = (idx & 31) * 4;
+        in[u] = r < rows;
+        const int64_t e = ((sq.b * a.T + t0 + (in[u] ? r : 0)) * a.H + h) * DK + c;
+        q[u].load(static_cast<const Tin*>(a.q), e);
+        k[u].load(static_cast<const Tin*>(a.k), e);
+        g[u].load(static_cast<const Tin*>(a.g), e);
+    }
+    const bool inb = (tid & (C - 1)) < rows;
+    const float bt = load_elem(static_cast<const Tin*>(a.beta), (sq.b * a.T + t0 + (inb ? (tid & (C - 1)) : 0)) * a.H + h);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int idx = tid + 256 * u;
+        const int r = idx >> 5, c = (idx & 31) * 4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            sm.G[r][c + v] = in[u] ? g[u].get(v) * kLog2e : 0.f;
+            sm.Kp[r][c + v] = in[u] ? k[u].get(v) : 0.f;
+            sm.Qp[r][c + v] = in[u] ? q[u].get(v) : 0.f;
+        }
+    }
+    if (tid < C) sm.beta[tid] = inb ? bt : 0.f;
+    __syncthreads();
+    if (tid < DK) {
+        float run = 0.f;
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            run += sm.G[r][tid];
+            sm.G[r][tid] = run;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int idx = tid + 256 * u;
+        const int r = idx / DK, c = idx % DK;
+        const float d = sm.G[r][c] - sm.G[kRef][c];
+        const float k0 = sm.Kp[r][c];
+        const float ep = __builtin_amdgcn_exp2f(d);
+        sm.Kp[r][c] = ep * k0;
+        sm.Qp[r][c] *= ep;
+        sm.Km[r][c] = __builtin_amdgcn_exp2f(-d) * k0;
+    }
+    __syncthreads();
+    float* mats = a.ws + chunk_bwd_slots(a.B, a.T, a.N, a.cu != nullptr) * (int64_t)a.H * DK * a.Dv +
+                  (slot * a.H + h) * kMats;
+    if (w < 2) {   // wave 0: KK = Kp Km^T (strict lower); wave 1: P = Qp Km^T (lower)
+        const float (*X)[KP] = w == 0 ? sm.Kp : sm.Qp;
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+        for (int ks = 0; ks < DK / 4; ks += 2) {
+            a0 = mfma(X[l16][4 * ks + lg], sm.Km[l16][4 * ks + lg], a0);
+            a1 = mfma(X[l16][4 * ks + 4 + lg], sm.Km[l16][4 * ks + 4 + lg], a1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lg + i, s = l16;
+            const float v = a0[i] + a1[i];
+            if (w == 0) {
+                const float kk = s < r ? v : 0.f;
+                sm.KK[r][s] = kk;
+                mats[2 * C * C + r * C + s] = kk;
+            } else {
+                mats[C * C + r * C + s] = s <= r ? v : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < C) {   // T by forward substitution, column tid in registers
+        const int i = tid;
+        float tc[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < r; ++s) acc += sm.KK[r][s] * tc[s];
+            tc[r] = r < i ? 0.f : (r == i ? 1.f : -sm.beta[r] * acc);
+        }
+#pragma unroll
+        for (int r = 0; r < C; ++r) mats[r * C + i] = tc[r];
+    }
+}
+
 template <typename Tin>
 __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
     __shared__ Smem sm;
@@ -713,21 +872,22 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
     const int64_t slot_stride = (int64_t)H * DK * Dv;
     const int64_t nch = (sq.len + C - 1) / C;
     const int cw = 16 * w;   // this wave's state rows / channel tile
-    // T, P and KK of every chunk, per (slot, head, slice), after the states
-    float* mats = a.ws + chunk_bwd_slots(a.B, a.T, a.N, a.cu != nullptr) * slot_stride;
-    auto mats_of = [&](int64_t ch) { return mats + (((sq.slot0 + ch) * H + h) * nvt + vt) * kMats; };
+    const float* mats0 = a.ws + chunk_bwd_slots(a.B, a.T, a.N, a.cu != nullptr) * slot_stride;
+    auto mats_of = [&](int64_t ch) { return mats0 + ((sq.slot0 + ch) * H + h) * kMats; };
+    auto state_of = [&](int64_t ch) { return a.ws + (sq.slot0 + ch) * slot_stride + (int64_t)h * DK * Dv + c0; };
+    Fetch<Tin> f;
 
-    // ---------------- forward sweep: entry states, T, P, KK ----------------
+    // ---------------- forward sweep: chunk entry states ----------------
     f32x4 st[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             st[t][i] = a.s0 ? a.s0[sbase + (int64_t)(cw + 4 * lg + i) * Dv + c0 + 16 * t + l16] : 0.f;
+    auto rows_of = [&](int64_t ch) { return (int)min<int64_t>(C, sq.len - ch * C); };
     for (int64_t ch = 0; ch < nch; ++ch) {
-        const int64_t t0 = sq.bos + ch * C;
-        const int rows = (int)min<int64_t>(C, sq.len - ch * C);
-        float* ws = a.ws + (sq.slot0 + ch) * slot_stride + (int64_t)h * DK * Dv + c0;
+        fetch_chunk<Tin>(f, a, sq, h, sq.bos + ch * C, rows_of(ch), c0, false, nullptr, mats_of(ch));
+        float* ws = state_of(ch);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -736,26 +896,13 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
                 ws[(int64_t)c * Dv + j] = st[t][i];
                 sm.S[c][j] = st[t][i];
             }
-        load_chunk<Tin>(sm, a, sq, h, t0, rows, c0, false);
+        commit_chunk<Tin>(sm, f, false);
         __syncthreads();
-        chunk_scale(sm);
+        chunk_scale(sm, false);
         __syncthreads();
-        if (w == 0) pair_matrix(sm, sm.Kp, sm.KK, false, l16, lg);
-        else if (w == 1) pair_matrix(sm, sm.Qp, sm.P, true, l16, lg);
-        else if (w < 6) w_tile(sm, w - 2, l16, lg);
-        __syncthreads();
-        if (w == 0) invert_T(sm, lane);
+        if (w < 4) w_tile(sm, w, l16, lg);
         __syncthreads();
         if (w < 4) u_tile(sm, w, l16, lg);
-        {
-            float* m = mats_of(ch);
-            if (tid < C * C) {
-                const int r = tid / C, s = tid % C;
-                m[tid] = sm.T[r][s];
-                m[C * C + tid] = sm.P[r][s];
-                m[2 * C * C + tid] = sm.KK[r][s];
-            }
-        }
         __syncthreads();
         // S <- Diag(e^Gamma_C) S + Kh^T U
         {
@@ -784,29 +931,15 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
             ds[t][i] = a.d_final ? a.d_final[sbase + (int64_t)(cw + 4 * lg + i) * Dv + c0 + 16 * t + l16] : 0.f;
     for (int64_t ch = nch - 1; ch >= 0; --ch) {
         const int64_t t0 = sq.bos + ch * C;
-        const int rows = (int)min<int64_t>(C, sq.len - ch * C);
-        const float* ws = a.ws + (sq.slot0 + ch) * slot_stride + (int64_t)h * DK * Dv + c0;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int q4 = tid + NT * u;             // 128 rows x 16 quads
-            const int c = q4 >> 4, j = (q4 & 15) * 4;
-            const float4 v = *reinterpret_cast<const float4*>(ws + (int64_t)c * Dv + j);
-            sm.S[c][j] = v.x; sm.S[c][j + 1] = v.y; sm.S[c][j + 2] = v.z; sm.S[c][j + 3] = v.w;
-        }
-        if (tid < C * C) {
-            const float* m = mats_of(ch);
-            const int r = tid / C, s = tid % C;
-            sm.T[r][s] = m[tid];
-            sm.P[r][s] = m[C * C + tid];
-            sm.KK[r][s] = m[2 * C * C + tid];
-        }
+        const int rows = rows_of(ch);
+        fetch_chunk<Tin>(f, a, sq, h, t0, rows, c0, true, state_of(ch), mats_of(ch));
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) sm.dS[cw + 4 * lg + i][16 * t + l16] = ds[t][i];
-        load_chunk<Tin>(sm, a, sq, h, t0, rows, c0, true);
+        commit_chunk<Tin>(sm, f, true);
         __syncthreads();
-        chunk_scale(sm);
+        chunk_scale(sm, true);
         __syncthreads();
         // W = V - Kg S (waves 0-3);  dU = scale P^T dO + Kh dS (waves 4-7)
         if (w < 4) {
@@ -859,15 +992,21 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
                 am = mfma(dy, sm.U[l16][4 * ks + lg], am);
                 ax = mfma(dy, sm.W[l16][4 * ks + lg], ax);
             }
+            // dbeta_r = dY_r . W_r + sum_s dM[r][s] KK[r][s]
+            float part[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * lg + i, s = l16;
                 const float dm = s < r ? -am[i] : 0.f;
                 sm.dKK[r][s] = sm.beta[r] * dm;
-                float part = dm * sm.KK[r][s] + (s == r ? ax[i] : 0.f);
+                part[i] = row16_sum(dm * sm.KK[r][s] + (s == r ? ax[i] : 0.f));
+            }
+            if (l16 == 15) {
 #pragma unroll
-                for (int m = 1; m < 16; m <<= 1) part += __shfl_xor(part, m, 64);
-                if (s == 0 && r < rows) add_out(a.dbeta + (sq.b * a.T + t0 + r) * H + h, part, atomic);
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * lg + i;
+                    if (r < rows) add_out(a.dbeta + (sq.b * a.T + t0 + r) * H + h, part[i], atomic);
+                }
             }
         }
 #pragma unroll
@@ -993,7 +1132,17 @@ hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s) {
     }
     if (chunk_bwd_mfma_supported(a)) {
         const int64_t grid = (int64_t)a.N * a.H * (a.Dv / mf::BV);
+        const int64_t slots = chunk_bwd_slots(a.B, a.T, a.N, a.cu != nullptr);
         if (grid == 0) return hipSuccess;
+        if (slots > 0) {
+            const dim3 mg((unsigned)slots, (unsigned)a.H);
+            if (a.bf16)
+                mf::chunk_mats_kernel<__bf16><<<mg, dim3(256), 0, s>>>(a);
+            else
+                mf::chunk_mats_kernel<float><<<mg, dim3(256), 0, s>>>(a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         if (a.bf16)
             mf::chunk_bwd_mfma_kernel<__bf16><<<dim3((unsigned)grid), dim3(mf::NT), 0, s>>>(a);
         else

@@ -91,15 +91,14 @@ struct BwdArgs {
 
 // The backward's workspace: a float32 chunk-entry state [H][Dk][Dv] per
 // 16-row chunk slot (sequence n's chunks start at slot cu[n]/16 + n when
-// packed, n*ceil(T/16) otherwise), then per (slot, head, 64-column value
-// slice) the chunk's T, P and KK (3 x 16 x 16 floats).
+// packed, n*ceil(T/16) otherwise), then per (slot, head) the chunk's T, P
+// and KK (3 x 16 x 16 floats).
 __host__ __device__ inline int64_t chunk_bwd_slots(int32_t B, int32_t T, int32_t N, bool packed) {
     return packed ? (int64_t)T / 16 + N : (int64_t)B * ((T + 15) / 16);
 }
 __host__ __device__ inline int64_t chunk_bwd_ws_floats(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
                                                        int32_t N, bool packed) {
-    const int64_t slices = Dv >= 64 ? Dv / 64 : 1;
-    return chunk_bwd_slots(B, T, N, packed) * H * ((int64_t)Dk * Dv + slices * 3 * 16 * 16);
+    return chunk_bwd_slots(B, T, N, packed) * H * ((int64_t)Dk * Dv + 3 * 16 * 16);
 }
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s);
 bool chunk_bwd_mfma_supported(const BwdArgs& a);   // Dk = 128, Dv in {64, 128}

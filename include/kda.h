@@ -123,10 +123,9 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
 
 /*
  * Bytes of device workspace kda_chunk_bwd needs: per 16-row chunk slot and
- * head, one float32 state [Dk,Dv] plus three float32 16x16 matrices per
- * 64-column value slice (one slice when Dv < 64); T/16 + N slots for packed
- * sequences (packed != 0), B * ceil(T/16) otherwise. 0 when T = 0 or a size
- * is out of range.
+ * head, one float32 state [Dk,Dv] plus three float32 16x16 matrices; T/16 + N
+ * slots for packed sequences (packed != 0), B * ceil(T/16) otherwise. 0 when
+ * T = 0 or a size is out of range.
  */
 size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
                                      int32_t packed);

@@ -185,10 +185,10 @@ def test_short_conv_step_empty_is_ok(lib):
 
 
 def test_chunk_bwd_workspace_bytes(lib):
-    # per 16-row chunk slot and head: a float32 [Dk,Dv] state, then T, P and
-    # KK (3 x 16 x 16 floats) per 64-column value slice
+    # per 16-row chunk slot and head: a float32 [Dk,Dv] state, and the chunk's
+    # T, P and KK (3 x 16 x 16 floats)
     def expect(slots, H, Dk, Dv):
-        return slots * H * (Dk * Dv + max(1, Dv // 64) * 768) * 4
+        return slots * H * (Dk * Dv + 768) * 4
     assert kda.chunk_bwd_workspace_bytes(1, 4096, 96, 128, 128, 1, False) == expect(256, 96, 128, 128)
     assert kda.chunk_bwd_workspace_bytes(2, 17, 3, 64, 32, 2, False) == expect(4, 3, 64, 32)
     assert kda.chunk_bwd_workspace_bytes(1, 100, 2, 16, 16, 5, True) == expect(100 // 16 + 5, 2, 16, 16)
@@ -234,7 +234,7 @@ def _bwd(lib, **kw):
     (dict(dtype=7), kda.KDA_ERR_UNSUPPORTED, "dtype"),
     (dict(cu=FAKE, B=2, N=1), kda.KDA_ERR_INVALID_ARG, "B == 1"),
     (dict(N=2), kda.KDA_ERR_INVALID_ARG, "N must equal B"),
-    (dict(wsb=4 * 2 * (128 * 128 + 2 * 768) * 4 - 1), kda.KDA_ERR_INVALID_ARG, "workspace"),
+    (dict(wsb=4 * 2 * (128 * 128 + 768) * 4 - 1), kda.KDA_ERR_INVALID_ARG, "workspace"),
     (dict(ws=None), kda.KDA_ERR_INVALID_ARG, "workspace"),
     (dict(dq=FAKE), kda.KDA_ERR_INVALID_ARG, "alias"),
     (dict(dv=ctypes.c_void_p(0x3000)), kda.KDA_ERR_INVALID_ARG, "alias"),
