@@ -1,6 +1,6 @@
 """Benchmark: KDA chunked forward on the K3 layer shape, one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-backward]
 
 One step = one kda_chunk_fwd call over a K3-shaped batch: B=1, T=4096, H=96,
 d_k=d_v=128, bf16 inputs, zero initial state, output plus final state. The
@@ -23,7 +23,11 @@ and L2-normalisation prologue fused into the chunk kernel
 q, k and v projections (kda_short_conv) and the chain convolution ->
 prologue forward. ``mfma`` gives the same launches against the bf16 dense matrix-core peak with
 the algorithmic flop count of the chunk form at C=64 counted over full tiles,
-a fixed count that does not depend on the chunk size the kernel uses. ``decode`` times kda_recurrent_step on
+a fixed count that does not depend on the chunk size the kernel uses. ``backward`` times kda_chunk_bwd on
+the same workload with output and final-state cotangents, against the fp32
+matrix-core peak (its products run as float32 MFMA) with the algorithmic flop
+count of the chunked backward (recompute included), plus the fp64 oracle's
+backward on the same workload. ``decode`` times kda_recurrent_step on
 256 rows x 96 heads against an fp32 state cache (HBM-bound). ``cpu_baseline``
 times the fp64 CPU oracle (C, OpenMP over heads) on the same forward workload,
 repeated until about ten seconds of wall time have passed.
@@ -50,6 +54,8 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "KDA fwd tokens/s at H=96,d=128 (bf16); MFMA util % and decode HBM GB/s"
 CHUNK_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_chunk_amd", "csrc", "chunk_mfma.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_mfma_k3_t4096_traffic.md")
+BWD_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_chunk_amd", "csrc", "chunk_bwd.hip")
+BWD_SUMMARY = os.path.join(ROOT, "profiles", "chunk_bwd_k3_t4096.md")
 
 
 def fwd_bytes(T, H, Dk, Dv, n_states_out, n_states_in=0, elem=2):
@@ -64,6 +70,23 @@ def fwd_flops(T, H, Dk, Dv, C=64):
 
 def kernel_source_hash():
     return hashlib.sha256(open(CHUNK_KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def bwd_source_hash():
+    return hashlib.sha256(open(BWD_KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_bwd_traffic():
+    """HBM bytes per backward call from the committed counter summary, if it was
+    taken on the current backward source; otherwise None."""
+    if not os.path.exists(BWD_SUMMARY):
+        return None
+    text = open(BWD_SUMMARY).read()
+    m_hash = re.search(r"bwd_source_sha256:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"(?m)^bwd_traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != bwd_source_hash():
+        return None
+    return float(m_val.group(1))
 
 
 def read_traffic(key="traffic_bytes_per_launch"):
@@ -258,6 +281,98 @@ def bench_decode(steps, warmup):
             "algorithmic_bytes_per_step": step_bytes}
 
 
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 MFMA, TFLOP/s
+
+
+def bwd_flops(T, H, Dk, Dv, C=16):
+    """Algorithmic flops of the chunked backward per launch, recompute included:
+    per 16-row chunk and head, 11 state-sized products (2*C*Dk*Dv each: the
+    forward re-run's W and state update, W again, Kh dS, the two state-gradient
+    products, dO S^T, dW S^T, U dS^T) and the 16x16 ones (KK, P and the four
+    pair-gradient products over d_k; T W twice, P^T dO, T^T dU, dO U^T, dY U^T
+    over d_v)."""
+    per_chunk = 22 * C * Dk * Dv + 12 * C * C * Dk + 12 * C * C * Dv
+    return T * H * per_chunk // C
+
+
+def bwd_bytes(T, H, Dk, Dv, elem=2):
+    """Algorithmic HBM bytes of the backward per launch: q, k, g, v, beta and
+    d_o read in the input dtype; dq, dk, dg, dv, dbeta written in float32; the
+    final-state cotangent read and the initial-state gradient written."""
+    per_tok_head = elem * (3 * Dk + 2 * Dv + 1) + 4 * (3 * Dk + Dv + 1)
+    return T * H * per_tok_head + 2 * 4 * H * Dk * Dv
+
+
+def bench_backward(steps, warmup, cpu=True):
+    """kda_chunk_bwd on k3_t4096 with an output cotangent and a final-state
+    cotangent (seeded, standard deviations 1 and 0.1); float32 gradients."""
+    w = synth.WORKLOADS["k3_t4096"]
+    dev = torch.device("cuda:0")
+    sets = []
+    for s in range(2):
+        inp = synth.make_chunk_inputs(w.B, w.T, w.H, w.Dk, w.Dv, seed=w.seed + 1000 * s, dtype=w.dtype)
+        d_o, dfin = synth.make_cotangents(inp, seed=w.seed + 1000 * s + 7)
+        d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+        d["d_o"], d["d_final"] = d_o.to(dev), dfin.to(dev)
+        sets.append(d)
+    ws = torch.empty((kda.chunk_bwd_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, w.B, False),), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+    scale = w.Dk ** -0.5
+    out = {}
+
+    def step(i):
+        d = sets[i % 2]
+        out["g"] = kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["d_o"], d_final_state=d["d_final"],
+                                 scale=scale, workspace=ws)
+
+    wall, per, batch = time_launches(step, steps, warmup, stream)
+    if not all(torch.isfinite(x).all() for x in out["g"]):
+        raise RuntimeError("non-finite backward output")
+    kern_ms = float(batch)
+    nflops = bwd_flops(w.T, w.H, w.Dk, w.Dv)
+    nbytes = bwd_bytes(w.T, w.H, w.Dk, w.Dv)
+    tflops = nflops / (kern_ms * 1e-3) / 1e12
+    res = {"workload": "k3_t4096 backward: B=1, T=4096, H=96, d_k=d_v=128, bf16 q/k/v/g/beta/d_o, "
+                       "fp32 final-state cotangent, fp32 dq/dk/dv/dg/dbeta/d_initial",
+           "ms_per_step": wall / steps * 1e3, "tokens_per_s": w.T / (wall / steps), "kernel_ms": kern_ms,
+           "kernel_ms_median": float(np.median(per)),
+           "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tflops / FP32_MFMA_PEAK_TFLOPS, "traffic": read_bwd_traffic(),
+                        "dtype": "f32 (v_mfma_f32_16x16x4f32)"},
+           "flops_per_launch": nflops,
+           "hbm": {"algorithmic_bytes_per_launch": nbytes,
+                   "achieved_GBs": nbytes / (kern_ms * 1e-3) / 1e9,
+                   "workspace_bytes_each_way": w.T // 16 * w.H * w.Dk * w.Dv * 4},
+           "timed": "one kda_chunk_bwd call: zero fills of the atomically summed gradients, the per-chunk "
+                    "T/P/KK kernel, the sequential kernel"}
+    if cpu:
+        res["cpu_baseline"] = cpu_backward_baseline()
+    return res
+
+
+def cpu_backward_baseline(heads=96):
+    """The fp64 C oracle's backward on k3_t4096: all 4096 tokens of the first
+    `heads` heads (all 96 by default, a few seconds on 16 threads), scaled to
+    the whole workload."""
+    from oracle import kda_ref
+    w = synth.WORKLOADS["k3_t4096"]
+    cores = len(os.sched_getaffinity(0))
+    omp = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    if omp > 0:
+        cores = min(cores, omp)
+    inp = synth.make_chunk_inputs(w.B, w.T, w.H, w.Dk, w.Dv, seed=w.seed, dtype=w.dtype)
+    d_o, dfin = synth.make_cotangents(inp, seed=w.seed + 7)
+    f = {k: inp[k].float().numpy()[:, :, :heads] for k in ("q", "k", "v", "g", "beta")}
+    t0 = time.perf_counter()
+    kda_ref.c_backward(f["q"], f["k"], f["v"], f["g"], f["beta"], d_o.float().numpy()[:, :, :heads],
+                       d_final=dfin.numpy()[:, :heads], scale=w.Dk ** -0.5, nthreads=cores)
+    wall = time.perf_counter() - t0
+    return {"value": w.T * heads / w.H / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"k3_t4096 backward, all {w.T} tokens of {heads} of the {w.H} heads (fp64 C oracle, "
+                      f"OpenMP over heads on {cores} threads), {wall:.1f} s wall, scaled by {heads}/{w.H}"}
+
+
 def cpu_baseline(min_wall_s=10.0, max_runs=200):
     """The fp64 C oracle over the whole k3_t4096 workload (all heads, all
     tokens), run repeatedly until min_wall_s of wall time has passed."""
@@ -300,6 +415,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -355,6 +471,8 @@ def main():
     }
     line["prologue"] = bench_prologue(args.steps, args.warmup)
     line["short_conv"] = bench_conv(args.steps, args.warmup)
+    if not args.no_backward:
+        line["backward"] = bench_backward(args.steps, args.warmup, cpu=not args.no_cpu_baseline)
     if not args.no_decode:
         line["decode"] = bench_decode(args.steps, args.warmup)
     if not args.no_cpu_baseline:
