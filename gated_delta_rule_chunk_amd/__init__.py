@@ -64,6 +64,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_short_conv.restype = ctypes.c_int
     lib.kda_short_conv_step.argtypes = [P, P, P, P, I32, I32, I32, I32, ctypes.c_int, P, P]
     lib.kda_short_conv_step.restype = ctypes.c_int
+    lib.kda_chunk_fwd_split_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.c_int, I32]
+    lib.kda_chunk_fwd_split_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_chunk_fwd_split.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, ctypes.c_int,
+                                        I32, P, ctypes.c_size_t, P, P, P]
+    lib.kda_chunk_fwd_split.restype = ctypes.c_int
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     lib.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_chunk_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, F, ctypes.c_int,
@@ -172,6 +177,34 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk_size=
     st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                            _ptr(cu_seqlens), B, T, H, Dk, Dv, N, int(chunk_size), float(scale),
                            _DTYPES[dt], _ptr(out), _ptr(final_state), _stream(dev))
+    _check(st)
+    return out, final_state
+
+
+def chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, N, dtype, segments):
+    """Bytes of workspace kda_chunk_fwd_split needs (0 when segments <= 1)."""
+    return int(load_library().kda_chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, N, _DTYPES[dtype], segments))
+
+
+def chunk_fwd_split(q, k, v, g, beta, segments, initial_state=None, cu_seqlens=None, chunk_size=0, scale=1.0,
+                    output_final_state=True, out=None, final_state=None, workspace=None):
+    """``chunk_fwd`` with every sequence cut into ``segments`` pieces run in
+    parallel and joined by the affine form of the state map
+    (kda_chunk_fwd_split). ``workspace``: a uint8 device tensor of at least
+    ``chunk_fwd_split_workspace_bytes`` bytes, or None to allocate one."""
+    lib = load_library()
+    B, T, H, Dk, Dv, N, dt, dev = _chunk_inputs(q, k, v, g, beta, initial_state, cu_seqlens,
+                                                ("q", "k", "v", "g", "beta"))
+    out, final_state = _chunk_outputs(B, T, H, Dk, Dv, N, dt, dev, out, final_state, output_final_state)
+    need = chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, N, dt, int(segments))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    st = lib.kda_chunk_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                 _ptr(cu_seqlens), B, T, H, Dk, Dv, N, int(chunk_size), float(scale), _DTYPES[dt],
+                                 int(segments), _ptr(workspace), workspace.numel(), _ptr(out), _ptr(final_state),
+                                 _stream(dev))
     _check(st)
     return out, final_state
 

@@ -21,6 +21,8 @@ kda_status fail(kda_status st, const char* fmt, ...) {
 
 bool dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+constexpr int32_t KDA_MAX_SEGMENTS = 4096;
+
 }  // namespace
 
 extern "C" {
@@ -133,6 +135,50 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
     a.gate_lb = gate_lower_bound;
     a.l2_eps = l2_eps;
     return launch_chunk(fn, a, stream);
+}
+
+size_t kda_chunk_fwd_split_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
+                                           kda_dtype dtype, int32_t segments) {
+    if (B < 1 || T <= 0 || H < 1 || N < 1 || segments <= 1 || segments > KDA_MAX_SEGMENTS || !dim_ok(Dk) ||
+        !dim_ok(Dv) || (dtype != KDA_F32 && dtype != KDA_BF16))
+        return 0;
+    kda::ChunkArgs a;
+    a.B = B; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.N = N; a.bf16 = dtype == KDA_BF16;
+    return (size_t)kda::split_layout(a, segments).bytes;
+}
+
+kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                               const float* initial_state, const int32_t* cu_seqlens, int32_t B, int32_t T,
+                               int32_t H, int32_t Dk, int32_t Dv, int32_t N, int32_t chunk_size, float scale,
+                               kda_dtype dtype, int32_t segments, void* workspace, size_t workspace_bytes, void* o,
+                               float* final_state, void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_chunk_fwd_split";
+    kda::ChunkArgs a;
+    const kda_status st = check_chunk(fn, q, k, v, g, beta, initial_state, cu_seqlens, B, T, H, Dk, Dv, N,
+                                      chunk_size, scale, dtype, o, final_state, a);
+    if (st != KDA_OK) return st;
+    if (segments < 1 || segments > KDA_MAX_SEGMENTS)
+        return fail(KDA_ERR_INVALID_ARG, "%s: segments must be in [1, %d], got %d", fn, KDA_MAX_SEGMENTS, segments);
+    if ((int64_t)B * T > INT32_MAX || (int64_t)N * segments * H > ((int64_t)1 << 26))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: B*T must fit in int32 and N*segments*H below 2^26", fn);
+    if (segments == 1 || T == 0) return launch_chunk(fn, a, stream);
+    const size_t need = kda_chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, N, dtype, segments);
+    if (workspace_bytes < need || !workspace)
+        return fail(KDA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, got %zu%s", fn, need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    {
+        const char* ws = static_cast<const char*>(workspace);
+        const void* ptrs[] = {q, k, v, g, beta, o, initial_state, final_state};
+        for (const void* p : ptrs) {
+            const char* c = static_cast<const char*>(p);
+            if (c && c >= ws && c < ws + need)
+                return fail(KDA_ERR_INVALID_ARG, "%s: the workspace must not overlap an input or output", fn);
+        }
+    }
+    const hipError_t e = kda::launch_chunk_fwd_split(a, segments, workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
 }
 
 size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,

@@ -103,6 +103,13 @@ __host__ __device__ inline int64_t chunk_bwd_ws_floats(int32_t B, int32_t T, int
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s);
 bool chunk_bwd_mfma_supported(const BwdArgs& a);   // Dk = 128, Dv in {64, 128}
 
+// Workspace of the intra-sequence split (byte offsets, 256-aligned).
+struct SplitLayout {
+    int64_t seg_cu, vzero, vzero2, scratch_o, ident, Bst, Sin, bytes;
+};
+SplitLayout split_layout(const ChunkArgs& a, int32_t P);
+hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace, hipStream_t s);
+
 hipError_t launch_short_conv(const ConvArgs& a, hipStream_t s);
 hipError_t launch_short_conv_step(const ConvStepArgs& a, hipStream_t s);
 

@@ -1,0 +1,225 @@
+// Intra-sequence split of the chunk forward: each sequence is cut into P
+// segments that run as independent sequences, and the segments are joined by
+// the affine form of the state map.
+//
+// Over one segment the recurrence maps its entry state linearly plus a
+// constant: S_out = A S_in + B, where B is the segment's final state from a
+// zero entry state and A (d_k x d_k) is its final state from the identity
+// with v = 0. Likewise its outputs split into o(S_in, v) = o(0, v) + o(S_in, 0).
+// So one call runs:
+//   1. the forward over all segments from zero entry states: outputs o(0, v)
+//      straight into o, and the B of every segment;
+//   2. the forward over all segments with v = 0 from identity entry states: A;
+//   3. split_scan_kernel: S_in(0) = the sequence's initial state,
+//      S_in(p) = A(p-1) S_in(p-1) + B(p-1), and the final state
+//      A(P-1) S_in(P-1) + B(P-1);
+//   4. the forward over all segments with v = 0 from S_in: o(S_in, 0);
+//   5. split_add_kernel: o += o(S_in, 0).
+// Passes 1, 2 and 4 are plain packed-sequence forward launches, so each of
+// them puts P times as many workgroups on the chip as the unsplit call.
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int kSegAlign = 64;  // segment lengths are multiples of the largest chunk
+
+// Segment offsets for every sequence: sequence n of length L starts at bos;
+// its segments have length roundup(ceil(L / P), 64) except the last, and
+// trailing segments may be empty.
+__global__ void split_offsets_kernel(const int32_t* cu, int32_t N, int32_t T, int32_t P, int32_t* seg_cu) {
+    const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    const int64_t bos = cu ? cu[n] : (int64_t)n * T;
+    const int64_t len = cu ? (int64_t)cu[n + 1] - cu[n] : T;
+    int64_t seg = (len + P - 1) / P;
+    seg = (seg + kSegAlign - 1) / kSegAlign * kSegAlign;
+    for (int p = 0; p < P; ++p) {
+        const int64_t off = (int64_t)p * seg < len ? (int64_t)p * seg : len;
+        seg_cu[(int64_t)n * P + p] = (int32_t)(bos + off);
+    }
+    if (n == N - 1) seg_cu[(int64_t)N * P] = (int32_t)(bos + len);
+}
+
+__global__ void fill_zero_u32_kernel(uint32_t* p, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+// Identity [Dk][Dk] per (segment, head).
+__global__ void fill_identity_kernel(float* p, int64_t mats, int Dk) {
+    const int64_t n = mats * Dk * Dk;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const int64_t e = i % ((int64_t)Dk * Dk);
+        p[i] = (e / Dk == e % Dk) ? 1.f : 0.f;
+    }
+}
+
+// One workgroup per (sequence, head, 16-column slice of d_v): the chain of
+// entry states S_in(p) over the sequence's P segments, and its final state.
+// A is [N*P][H][Dk][Dk], Bst and Sin are [N*P][H][Dk][Dv].
+template <int DK>
+__global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const float* Bst, const float* s0,
+                                                         float* Sin, float* sT, int32_t N, int32_t H,
+                                                         int32_t Dv, int32_t P) {
+    constexpr int BVs = 16;
+    __shared__ float sS[DK][BVs + 1];
+    const int nvt = Dv / BVs;
+    const int vt = blockIdx.x % nvt, unit = blockIdx.x / nvt;
+    const int n = unit / H, h = unit % H;
+    const int c0 = vt * BVs;
+    for (int idx = threadIdx.x; idx < DK * BVs; idx += blockDim.x) {
+        const int c = idx / BVs, j = idx % BVs;
+        sS[c][j] = s0 ? s0[(((int64_t)n * H + h) * DK + c) * Dv + c0 + j] : 0.f;
+    }
+    __syncthreads();
+    for (int p = 0; p < P; ++p) {
+        const int64_t seg = (int64_t)n * P + p;
+        float* sin = Sin + (seg * H + h) * (int64_t)DK * Dv;
+        for (int idx = threadIdx.x; idx < DK * BVs; idx += blockDim.x) {
+            const int c = idx / BVs, j = idx % BVs;
+            sin[(int64_t)c * Dv + c0 + j] = sS[c][j];
+        }
+        if (p == P - 1 && !sT) break;
+        // S <- A(p) S + B(p)
+        const float* a = A + (seg * H + h) * (int64_t)DK * DK;
+        const float* b = Bst + (seg * H + h) * (int64_t)DK * Dv;
+        float out[DK * BVs / 256 > 0 ? DK * BVs / 256 : 1];
+        int m = 0;
+        for (int idx = threadIdx.x; idx < DK * BVs; idx += blockDim.x, ++m) {
+            const int c = idx / BVs, j = idx % BVs;
+            float acc = b[(int64_t)c * Dv + c0 + j];
+            const float* arow = a + (int64_t)c * DK;
+            for (int i = 0; i < DK; ++i) acc += arow[i] * sS[i][j];
+            out[m] = acc;
+        }
+        __syncthreads();
+        m = 0;
+        for (int idx = threadIdx.x; idx < DK * BVs; idx += blockDim.x, ++m) sS[idx / BVs][idx % BVs] = out[m];
+        __syncthreads();
+    }
+    if (sT) {
+        for (int idx = threadIdx.x; idx < DK * BVs; idx += blockDim.x) {
+            const int c = idx / BVs, j = idx % BVs;
+            sT[(((int64_t)n * H + h) * DK + c) * Dv + c0 + j] = sS[c][j];
+        }
+    }
+}
+
+template <typename T>
+__global__ void split_add_kernel(T* o, const T* corr, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        store_elem(o, i, load_elem(o, i) + load_elem(corr, i));
+}
+
+unsigned grid_for(int64_t n) {
+    const int64_t b = (n + 255) / 256;
+    return (unsigned)(b < 8192 ? (b > 0 ? b : 1) : 8192);
+}
+
+hipError_t chunk_forward(const ChunkArgs& a, hipStream_t s) {
+    return chunk_mfma_supported(a) ? launch_chunk_mfma(a, s) : launch_chunk_generic(a, s);
+}
+
+}  // namespace
+
+SplitLayout split_layout(const ChunkArgs& a, int32_t P) {
+    SplitLayout L;
+    const int64_t segs = (int64_t)a.N * P;
+    const int64_t rows = (int64_t)a.B * a.T * a.H;
+    const int64_t elem = a.bf16 ? 2 : 4;
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    int64_t off = 0;
+    L.seg_cu = off;  off += up((segs + 1) * 4);
+    L.vzero = off;   off += up(rows * a.Dk * elem);           // v = 0 for passes 2 and 4 (d_v = d_k in pass 2)
+    L.vzero2 = off;  off += up(a.Dv == a.Dk ? 0 : rows * a.Dv * elem);
+    L.scratch_o = off; off += up(rows * (a.Dk > a.Dv ? a.Dk : a.Dv) * elem);   // pass 2's and pass 4's outputs
+    L.ident = off;   off += up(segs * a.H * (int64_t)a.Dk * a.Dk * 4);          // identity entry states, then A
+    L.Bst = off;     off += up(segs * a.H * (int64_t)a.Dk * a.Dv * 4);
+    L.Sin = off;     off += up(segs * a.H * (int64_t)a.Dk * a.Dv * 4);
+    L.bytes = off;
+    return L;
+}
+
+hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace, hipStream_t s) {
+    const SplitLayout L = split_layout(a, P);
+    char* ws = static_cast<char*>(workspace);
+    int32_t* seg_cu = reinterpret_cast<int32_t*>(ws + L.seg_cu);
+    void* vzero = ws + L.vzero;
+    void* vzero2 = a.Dv == a.Dk ? vzero : static_cast<void*>(ws + L.vzero2);
+    void* scratch_o = ws + L.scratch_o;
+    float* AI = reinterpret_cast<float*>(ws + L.ident);
+    float* Bst = reinterpret_cast<float*>(ws + L.Bst);
+    float* Sin = reinterpret_cast<float*>(ws + L.Sin);
+    const int64_t segs = (int64_t)a.N * P;
+    const int64_t rows = (int64_t)a.B * a.T * a.H;
+    const int64_t elem = a.bf16 ? 2 : 4;
+    hipError_t e;
+
+    split_offsets_kernel<<<dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, s>>>(a.cu, a.N, a.T, P, seg_cu);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        const int64_t w1 = rows * a.Dk * elem / 4;
+        fill_zero_u32_kernel<<<dim3(grid_for(w1)), dim3(256), 0, s>>>(static_cast<uint32_t*>(vzero), w1);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (vzero2 != vzero) {
+            const int64_t w2 = rows * a.Dv * elem / 4;
+            fill_zero_u32_kernel<<<dim3(grid_for(w2)), dim3(256), 0, s>>>(static_cast<uint32_t*>(vzero2), w2);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        fill_identity_kernel<<<dim3(grid_for(segs * a.H * a.Dk * a.Dk)), dim3(256), 0, s>>>(AI, segs * a.H, a.Dk);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // the packed view of the input: one row of B*T tokens, N*P sequences
+    ChunkArgs seg = a;
+    seg.B = 1;
+    seg.T = a.B * a.T;
+    seg.N = (int32_t)segs;
+    seg.cu = seg_cu;
+    // 1. o(0, v) into o, and B
+    ChunkArgs p1 = seg;
+    p1.s0 = nullptr;
+    p1.sT = Bst;
+    if ((e = chunk_forward(p1, s)) != hipSuccess) return e;
+    // 2. A: identity entry states, v = 0, d_v = d_k (its outputs are not used)
+    ChunkArgs p2 = seg;
+    p2.v = vzero;
+    p2.Dv = a.Dk;
+    p2.s0 = AI;
+    p2.sT = AI;   // each state tile is read before it is written
+    p2.o = scratch_o;
+    if ((e = chunk_forward(p2, s)) != hipSuccess) return e;
+    // 3. entry states of every segment, and the final states
+    switch (a.Dk) {
+        case 16: split_scan_kernel<16><<<dim3((unsigned)(a.N * a.H * (a.Dv / 16))), dim3(256), 0, s>>>(
+                     AI, Bst, a.s0, Sin, a.sT, a.N, a.H, a.Dv, P); break;
+        case 32: split_scan_kernel<32><<<dim3((unsigned)(a.N * a.H * (a.Dv / 16))), dim3(256), 0, s>>>(
+                     AI, Bst, a.s0, Sin, a.sT, a.N, a.H, a.Dv, P); break;
+        case 64: split_scan_kernel<64><<<dim3((unsigned)(a.N * a.H * (a.Dv / 16))), dim3(256), 0, s>>>(
+                     AI, Bst, a.s0, Sin, a.sT, a.N, a.H, a.Dv, P); break;
+        default: split_scan_kernel<128><<<dim3((unsigned)(a.N * a.H * (a.Dv / 16))), dim3(256), 0, s>>>(
+                     AI, Bst, a.s0, Sin, a.sT, a.N, a.H, a.Dv, P); break;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 4. o(S_in, 0)
+    ChunkArgs p4 = seg;
+    p4.v = vzero2;
+    p4.s0 = Sin;
+    p4.sT = nullptr;
+    p4.o = scratch_o;
+    if ((e = chunk_forward(p4, s)) != hipSuccess) return e;
+    // 5. o += o(S_in, 0)
+    const int64_t n_o = rows * a.Dv;
+    if (a.bf16)
+        split_add_kernel<__bf16><<<dim3(grid_for(n_o)), dim3(256), 0, s>>>(
+            static_cast<__bf16*>(a.o), static_cast<const __bf16*>(scratch_o), n_o);
+    else
+        split_add_kernel<float><<<dim3(grid_for(n_o)), dim3(256), 0, s>>>(
+            static_cast<float*>(a.o), static_cast<const float*>(scratch_o), n_o);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -122,6 +122,48 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
                                   float* final_state, void* stream);
 
 /*
+ * Bytes of device workspace kda_chunk_fwd_split needs for these sizes and
+ * segments >= 2 (0 for segments <= 1, T = 0 or out-of-range sizes; the same
+ * for packed and fixed-length batches with the same N).
+ */
+size_t kda_chunk_fwd_split_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
+                                           kda_dtype dtype, int32_t segments);
+
+/*
+ * kda_chunk_fwd with every sequence cut into `segments` pieces that run in
+ * parallel, for batches with too few (sequence, head) pairs to fill the chip
+ * (a long sequence over few heads, as one GPU's share of a head-sharded
+ * layer). The package the method comes from notes that context parallelism is
+ * not available on its first KDA path and feeds long inputs as packed THD with
+ * context parallelism (ISEEKYAN/k3 README); this is the same idea inside one
+ * GPU. Over a segment the recurrence is affine in its entry state,
+ * S_out = A S_in + B, and the outputs are o(S_in, v) = o(0, v) + o(S_in, 0), so
+ * the call runs the forward over all segments from zero states (o(0, v) and
+ * B), again with v = 0 from identity states (A, d_k x d_k), chains the entry
+ * states S_in(p) = A(p-1) S_in(p-1) + B(p-1) per sequence, runs the forward
+ * with v = 0 from S_in, and adds those outputs to o.
+ *
+ * Segments are cut at multiples of 64 rows: sequence n of length L gets
+ * segments of roundup(ceil(L/segments), 64) rows, the last shorter and
+ * trailing ones possibly empty. The results equal kda_chunk_fwd's up to
+ * rounding; bf16 outputs are rounded twice (o(0, v) and the sum).
+ *
+ *   segments   1 .. 4096; 1 (or T = 0) runs kda_chunk_fwd and needs no
+ *              workspace
+ *   workspace  at least kda_chunk_fwd_split_workspace_bytes(...) bytes of
+ *              device memory owned by the caller, not overlapping any input or
+ *              output; its contents on entry do not matter
+ * All other arguments, the supported shapes and the errors are those of
+ * kda_chunk_fwd; B*T must fit in int32. A short or NULL workspace is
+ * KDA_ERR_INVALID_ARG.
+ */
+kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                               const float* initial_state, const int32_t* cu_seqlens, int32_t B, int32_t T,
+                               int32_t H, int32_t Dk, int32_t Dv, int32_t N, int32_t chunk_size, float scale,
+                               kda_dtype dtype, int32_t segments, void* workspace, size_t workspace_bytes, void* o,
+                               float* final_state, void* stream);
+
+/*
  * Bytes of device workspace kda_chunk_bwd needs: per 16-row chunk slot and
  * head, one float32 state [Dk,Dv] plus three float32 16x16 matrices; T/16 + N
  * slots for packed sequences (packed != 0), B * ceil(T/16) otherwise. 0 when

@@ -23,6 +23,7 @@ def test_exports_every_declared_symbol(lib):
     names = kda.declared_symbols()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step", "kda_short_conv",
                           "kda_short_conv_step", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
+                          "kda_chunk_fwd_split", "kda_chunk_fwd_split_workspace_bytes",
                           "kda_status_string", "kda_last_error_message"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -243,3 +244,41 @@ def test_chunk_bwd_rejects_before_launch(lib, kw, status, needle):
     st = _bwd(lib, **kw)
     assert st == status
     assert needle in lib.kda_last_error_message().decode()
+
+
+def _split(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, cu=None, B=1, T=4096, H=12, Dk=128, Dv=128, N=1,
+             chunk=0, scale=1.0, dtype=kda.KDA_BF16, seg=8, ws=ctypes.c_void_p(1 << 40), wsb=1 << 34,
+             o=ctypes.c_void_p(0x2000), sT=None, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_split(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["B"], a["T"],
+                                   a["H"], a["Dk"], a["Dv"], a["N"], a["chunk"], a["scale"], a["dtype"], a["seg"],
+                                   a["ws"], a["wsb"], a["o"], a["sT"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(seg=0), kda.KDA_ERR_INVALID_ARG, "segments"),
+    (dict(seg=5000), kda.KDA_ERR_INVALID_ARG, "segments"),
+    (dict(ws=None), kda.KDA_ERR_INVALID_ARG, "workspace"),
+    (dict(wsb=1000), kda.KDA_ERR_INVALID_ARG, "workspace"),
+    (dict(o=ctypes.c_void_p((1 << 40) + 4096)), kda.KDA_ERR_INVALID_ARG, "overlap"),
+    (dict(Dk=96), kda.KDA_ERR_UNSUPPORTED, "head dims"),
+    (dict(o=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(B=2, N=1), kda.KDA_ERR_INVALID_ARG, "N must equal B"),
+])
+def test_chunk_fwd_split_rejects_before_launch(lib, kw, status, needle):
+    st = _split(lib, **kw)
+    assert st == status
+    assert needle in lib.kda_last_error_message().decode()
+
+
+def test_chunk_fwd_split_workspace_bytes(lib):
+    import torch
+    assert kda.chunk_fwd_split_workspace_bytes(1, 4096, 12, 128, 128, 1, torch.bfloat16, 1) == 0
+    assert kda.chunk_fwd_split_workspace_bytes(1, 0, 12, 128, 128, 1, torch.bfloat16, 8) == 0
+    a = kda.chunk_fwd_split_workspace_bytes(1, 4096, 12, 128, 128, 1, torch.bfloat16, 8)
+    b = kda.chunk_fwd_split_workspace_bytes(1, 4096, 12, 128, 128, 1, torch.float32, 8)
+    # zeros for v and one output-sized buffer in the input dtype, plus 3 fp32 states per segment and head
+    rows = 4096 * 12
+    assert a >= rows * 128 * 2 * 2 + 3 * 8 * 12 * 128 * 128 * 4
+    assert b - a == rows * 128 * 2 * 2

@@ -1,0 +1,98 @@
+"""GPU parity of the intra-sequence split (kda_chunk_fwd_split through the C
+ABI) against the fp64 oracle's forward on the same inputs: the split must give
+the unsplit recurrence's outputs and final states (bf16 <= 2e-2, fp32 <= 1e-4
+relative L2). Cases cover several segment counts, segments longer than the
+sequence (empty segments), packed batches with empty and one-token
+sequences, weak decay (where the carried state matters most), the fp32
+vector-ALU path and the few-head long-sequence shape the split is for.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_chunk_amd as kda
+import synth
+from tests.gpu_helpers import TOL_BF16, TOL_F32, oracle_chunk, rel, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_split(inp, segments, scale=1.0):
+    d = to_dev(inp)
+    o, fin = kda.chunk_fwd_split(d["q"], d["k"], d["v"], d["g"], d["beta"], segments,
+                                 initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"], scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), fin.cpu().numpy()
+
+
+def _check(inp, segments, tol, label="", scale=1.0):
+    say(f"[case] split {label} segments={segments} q={tuple(inp['q'].shape)} {inp['q'].dtype}")
+    o, fin = gpu_split(inp, segments, scale)
+    ro, rfin = oracle_chunk(inp, scale=scale)
+    eo, ef = rel(o, ro), rel(fin, rfin)
+    say(f"        relL2 o={eo:.3e} final={ef:.3e}")
+    assert np.isfinite(o).all() and np.isfinite(fin).all()
+    assert eo <= tol and ef <= tol, (eo, ef)
+
+
+@pytest.mark.parametrize("segments", [2, 3, 8])
+def test_split_bf16_k3_dims(segments):
+    inp = synth.make_chunk_inputs(1, 1000, 3, 128, 128, seed=600 + segments, dtype="bf16", init_state=True)
+    _check(inp, segments, TOL_BF16, label="bf16")
+
+
+@pytest.mark.parametrize("g_mode", ["weak", "zero"])
+def test_split_bf16_weak_decay(g_mode):
+    # little decay: the state carried across segment boundaries dominates the outputs
+    inp = synth.make_chunk_inputs(1, 700, 2, 128, 128, seed=610, dtype="bf16", init_state=True, g_mode=g_mode,
+                                  s0_std=0.5)
+    _check(inp, 5, TOL_BF16, label=f"bf16 g={g_mode}")
+
+
+@pytest.mark.parametrize("Dk,Dv,segments", [(64, 32, 4), (128, 128, 3), (16, 64, 6), (32, 16, 2)])
+def test_split_f32(Dk, Dv, segments):
+    inp = synth.make_chunk_inputs(2, 300, 3, Dk, Dv, seed=620 + Dk + Dv, dtype="f32", init_state=True, s0_std=0.5,
+                                  g_mode="weak")
+    _check(inp, segments, TOL_F32, label=f"f32 Dk={Dk} Dv={Dv}")
+
+
+@pytest.mark.parametrize("dtype,tol", [("bf16", TOL_BF16), ("f32", TOL_F32)])
+def test_split_packed_ragged(dtype, tol):
+    inp = synth.make_chunk_inputs(1, 0, 3, 128, 128, seed=630, dtype=dtype, init_state=True, g_mode="weak",
+                                  lengths=[0, 1, 63, 64, 65, 300, 7, 1000])
+    _check(inp, 4, tol, label=f"packed {dtype}")
+
+
+def test_split_more_segments_than_chunks():
+    inp = synth.make_chunk_inputs(1, 50, 2, 128, 128, seed=640, dtype="bf16", init_state=True, g_mode="weak")
+    _check(inp, 8, TOL_BF16, label="T=50")
+
+
+def test_split_one_segment_is_the_plain_call():
+    inp = synth.make_chunk_inputs(1, 300, 4, 128, 128, seed=650, dtype="bf16", init_state=True)
+    d = to_dev(inp)
+    o1, f1 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["initial_state"])
+    o2, f2 = kda.chunk_fwd_split(d["q"], d["k"], d["v"], d["g"], d["beta"], 1, initial_state=d["initial_state"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_split_is_deterministic():
+    inp = synth.make_chunk_inputs(1, 900, 4, 128, 128, seed=660, dtype="bf16", init_state=True)
+    a = gpu_split(inp, 4)
+    b = gpu_split(inp, 4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.slow
+def test_split_few_heads_long_sequence_sampled_heads():
+    # 12 heads (one GPU's share of 96 under head sharding) at T = 32768, S0 ~ N(0, 0.02),
+    # 8 segments: the oracle checks two heads (a head's outputs depend on that head only).
+    inp = synth.make_chunk_inputs(1, 32768, 12, 128, 128, seed=670, dtype="bf16", init_state=True)
+    say("[case] split H=12 T=32768 segments=8")
+    o, fin = gpu_split(inp, 8)
+    heads = [0, 11]
+    ro, rfin = oracle_chunk(inp, heads=heads)
+    eo, ef = rel(o[:, :, heads], ro), rel(fin[:, heads], rfin)
+    say(f"        relL2 o={eo:.3e} final={ef:.3e}")
+    assert np.isfinite(o).all() and eo <= TOL_BF16 and ef <= TOL_BF16, (eo, ef)
