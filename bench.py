@@ -1,6 +1,7 @@
 """Benchmark: KDA chunked forward on the K3 layer shape, one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-backward]
+                    [--only split|backward]
 
 One step = one kda_chunk_fwd call over a K3-shaped batch: B=1, T=4096, H=96,
 d_k=d_v=128, bf16 inputs, zero initial state, output plus final state. The
@@ -27,7 +28,9 @@ a fixed count that does not depend on the chunk size the kernel uses. ``backward
 the same workload with output and final-state cotangents, against the fp32
 matrix-core peak (its products run as float32 MFMA) with the algorithmic flop
 count of the chunked backward (recompute included), plus the fp64 oracle's
-backward on the same workload. ``decode`` times kda_recurrent_step on
+backward on the same workload. ``split`` times the intra-sequence split
+(kda_chunk_fwd_split, 10 segments) on 12 heads at T=32768 against the unsplit
+call. ``decode`` times kda_recurrent_step on
 256 rows x 96 heads against an fp32 state cache (HBM-bound). ``cpu_baseline``
 times the fp64 CPU oracle (C, OpenMP over heads) on the same forward workload,
 repeated until about ten seconds of wall time have passed.
@@ -351,6 +354,49 @@ def bench_backward(steps, warmup, cpu=True):
     return res
 
 
+def bench_split(steps, warmup, segments=10):
+    """The intra-sequence split (kda_chunk_fwd_split) on the shape it is for:
+    12 heads (one GPU's share of the 96 under 8-way head sharding) at
+    T=32768, bf16, initial state ~ N(0, 0.02); against the unsplit call."""
+    B, T, H, D = 1, 32768, 12, 128
+    dev = torch.device("cuda:0")
+    sets = []
+    for s_ in range(2):
+        inp = synth.make_chunk_inputs(B, T, H, D, D, seed=2 + 1000 * s_, dtype="bf16", init_state=True)
+        sets.append({k: (None if v is None else v.to(dev)) for k, v in inp.items()})
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty((kda.chunk_fwd_split_workspace_bytes(B, T, H, D, D, B, torch.bfloat16, segments),),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def plain(i):
+        d = sets[i % 2]
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["initial_state"], out=o,
+                      final_state=fin)
+
+    def split(i):
+        d = sets[i % 2]
+        kda.chunk_fwd_split(d["q"], d["k"], d["v"], d["g"], d["beta"], segments, initial_state=d["initial_state"],
+                            out=o, final_state=fin, workspace=ws)
+
+    _, _, plain_ms = time_launches(plain, steps, warmup, stream)
+    wall, _, split_ms = time_launches(split, steps, warmup, stream)
+    if not (torch.isfinite(o.float()).all() and torch.isfinite(fin).all()):
+        raise RuntimeError("non-finite split output")
+    nbytes = fwd_bytes(T, H, D, D, n_states_out=1, n_states_in=1)
+    gbs = nbytes / (float(split_ms) * 1e-3) / 1e9
+    return {"workload": f"B=1, T={T}, H={H} (12 of the 96 heads), d_k=d_v=128, bf16, initial state N(0,0.02), "
+                        f"final state; {segments} segments per sequence",
+            "segments": segments, "ms_per_step": float(split_ms), "tokens_per_s": T / (float(split_ms) * 1e-3),
+            "unsplit_ms_per_step": float(plain_ms), "speedup_vs_unsplit": float(plain_ms) / float(split_ms),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+            "algorithmic_bytes_per_step": nbytes,
+            "timed": "one kda_chunk_fwd_split call: offsets, zero and identity fills, three forward launches over "
+                     "the segments, the entry-state scan"}
+
+
 def cpu_backward_baseline(heads=96):
     """The fp64 C oracle's backward on k3_t4096: all 4096 tokens of the first
     `heads` heads (all 96 by default, a few seconds on 16 threads), scaled to
@@ -417,6 +463,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--only", choices=["split", "backward"], default=None,
+                    help="run one secondary leg alone and print its JSON object (for per-kernel profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -428,6 +476,11 @@ def main():
     kda.load_library()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.only:
+        leg = bench_split(args.steps, args.warmup) if args.only == "split" else \
+            bench_backward(args.steps, args.warmup, cpu=False)
+        print(json.dumps({"only": args.only, **leg}), flush=True)
         return
 
     w, wall, per, batch = bench_forward(args.steps, args.warmup)
@@ -471,6 +524,7 @@ def main():
     }
     line["prologue"] = bench_prologue(args.steps, args.warmup)
     line["short_conv"] = bench_conv(args.steps, args.warmup)
+    line["split"] = bench_split(args.steps, args.warmup)
     if not args.no_backward:
         line["backward"] = bench_backward(args.steps, args.warmup, cpu=not args.no_cpu_baseline)
     if not args.no_decode:

@@ -105,7 +105,7 @@ bool chunk_bwd_mfma_supported(const BwdArgs& a);   // Dk = 128, Dv in {64, 128}
 
 // Workspace of the intra-sequence split (byte offsets, 256-aligned).
 struct SplitLayout {
-    int64_t seg_cu, vzero, vzero2, scratch_o, ident, Bst, Sin, bytes;
+    int64_t seg_cu, vzero, scratch_o, ident, Bst, Sin, bytes;
 };
 SplitLayout split_layout(const ChunkArgs& a, int32_t P);
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace, hipStream_t s);

@@ -5,16 +5,14 @@
 // Over one segment the recurrence maps its entry state linearly plus a
 // constant: S_out = A S_in + B, where B is the segment's final state from a
 // zero entry state and A (d_k x d_k) is its final state from the identity
-// with v = 0. Likewise its outputs split into o(S_in, v) = o(0, v) + o(S_in, 0).
-// So one call runs:
-//   1. the forward over all segments from zero entry states: outputs o(0, v)
-//      straight into o, and the B of every segment;
+// with v = 0. So one call runs:
+//   1. the forward over all segments from zero entry states: the B of every
+//      segment (its outputs are not used);
 //   2. the forward over all segments with v = 0 from identity entry states: A;
 //   3. split_scan_kernel: S_in(0) = the sequence's initial state,
 //      S_in(p) = A(p-1) S_in(p-1) + B(p-1), and the final state
 //      A(P-1) S_in(P-1) + B(P-1);
-//   4. the forward over all segments with v = 0 from S_in: o(S_in, 0);
-//   5. split_add_kernel: o += o(S_in, 0).
+//   4. the forward over all segments from S_in: the outputs, into o.
 // Passes 1, 2 and 4 are plain packed-sequence forward launches, so each of
 // them puts P times as many workgroups on the chip as the unsplit call.
 #include "device_common.hpp"
@@ -108,13 +106,6 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
     }
 }
 
-template <typename T>
-__global__ void split_add_kernel(T* o, const T* corr, int64_t n) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-        store_elem(o, i, load_elem(o, i) + load_elem(corr, i));
-}
-
 unsigned grid_for(int64_t n) {
     const int64_t b = (n + 255) / 256;
     return (unsigned)(b < 8192 ? (b > 0 ? b : 1) : 8192);
@@ -134,9 +125,8 @@ SplitLayout split_layout(const ChunkArgs& a, int32_t P) {
     auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
     int64_t off = 0;
     L.seg_cu = off;  off += up((segs + 1) * 4);
-    L.vzero = off;   off += up(rows * a.Dk * elem);           // v = 0 for passes 2 and 4 (d_v = d_k in pass 2)
-    L.vzero2 = off;  off += up(a.Dv == a.Dk ? 0 : rows * a.Dv * elem);
-    L.scratch_o = off; off += up(rows * (a.Dk > a.Dv ? a.Dk : a.Dv) * elem);   // pass 2's and pass 4's outputs
+    L.vzero = off;   off += up(rows * a.Dk * elem);           // v = 0 for pass 2 (d_v = d_k there)
+    L.scratch_o = off; off += up(rows * (a.Dk > a.Dv ? a.Dk : a.Dv) * elem);   // pass 1's and pass 2's outputs
     L.ident = off;   off += up(segs * a.H * (int64_t)a.Dk * a.Dk * 4);          // identity entry states, then A
     L.Bst = off;     off += up(segs * a.H * (int64_t)a.Dk * a.Dv * 4);
     L.Sin = off;     off += up(segs * a.H * (int64_t)a.Dk * a.Dv * 4);
@@ -149,7 +139,6 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
     char* ws = static_cast<char*>(workspace);
     int32_t* seg_cu = reinterpret_cast<int32_t*>(ws + L.seg_cu);
     void* vzero = ws + L.vzero;
-    void* vzero2 = a.Dv == a.Dk ? vzero : static_cast<void*>(ws + L.vzero2);
     void* scratch_o = ws + L.scratch_o;
     float* AI = reinterpret_cast<float*>(ws + L.ident);
     float* Bst = reinterpret_cast<float*>(ws + L.Bst);
@@ -165,11 +154,6 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
         const int64_t w1 = rows * a.Dk * elem / 4;
         fill_zero_u32_kernel<<<dim3(grid_for(w1)), dim3(256), 0, s>>>(static_cast<uint32_t*>(vzero), w1);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (vzero2 != vzero) {
-            const int64_t w2 = rows * a.Dv * elem / 4;
-            fill_zero_u32_kernel<<<dim3(grid_for(w2)), dim3(256), 0, s>>>(static_cast<uint32_t*>(vzero2), w2);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
         fill_identity_kernel<<<dim3(grid_for(segs * a.H * a.Dk * a.Dk)), dim3(256), 0, s>>>(AI, segs * a.H, a.Dk);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -179,10 +163,11 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
     seg.T = a.B * a.T;
     seg.N = (int32_t)segs;
     seg.cu = seg_cu;
-    // 1. o(0, v) into o, and B
+    // 1. B (the outputs go to scratch)
     ChunkArgs p1 = seg;
     p1.s0 = nullptr;
     p1.sT = Bst;
+    p1.o = scratch_o;
     if ((e = chunk_forward(p1, s)) != hipSuccess) return e;
     // 2. A: identity entry states, v = 0, d_v = d_k (its outputs are not used)
     ChunkArgs p2 = seg;
@@ -204,22 +189,11 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
                      AI, Bst, a.s0, Sin, a.sT, a.N, a.H, a.Dv, P); break;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // 4. o(S_in, 0)
+    // 4. the outputs, every segment from its entry state
     ChunkArgs p4 = seg;
-    p4.v = vzero2;
     p4.s0 = Sin;
     p4.sT = nullptr;
-    p4.o = scratch_o;
-    if ((e = chunk_forward(p4, s)) != hipSuccess) return e;
-    // 5. o += o(S_in, 0)
-    const int64_t n_o = rows * a.Dv;
-    if (a.bf16)
-        split_add_kernel<__bf16><<<dim3(grid_for(n_o)), dim3(256), 0, s>>>(
-            static_cast<__bf16*>(a.o), static_cast<const __bf16*>(scratch_o), n_o);
-    else
-        split_add_kernel<float><<<dim3(grid_for(n_o)), dim3(256), 0, s>>>(
-            static_cast<float*>(a.o), static_cast<const float*>(scratch_o), n_o);
-    return hipGetLastError();
+    return chunk_forward(p4, s);
 }
 
 }  // namespace kda

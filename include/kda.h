@@ -137,16 +137,15 @@ size_t kda_chunk_fwd_split_workspace_bytes(int32_t B, int32_t T, int32_t H, int3
  * not available on its first KDA path and feeds long inputs as packed THD with
  * context parallelism (ISEEKYAN/k3 README); this is the same idea inside one
  * GPU. Over a segment the recurrence is affine in its entry state,
- * S_out = A S_in + B, and the outputs are o(S_in, v) = o(0, v) + o(S_in, 0), so
- * the call runs the forward over all segments from zero states (o(0, v) and
- * B), again with v = 0 from identity states (A, d_k x d_k), chains the entry
- * states S_in(p) = A(p-1) S_in(p-1) + B(p-1) per sequence, runs the forward
- * with v = 0 from S_in, and adds those outputs to o.
+ * S_out = A S_in + B, so the call runs the forward over all segments from zero
+ * states (B), again with v = 0 from identity states (A, d_k x d_k), chains the
+ * entry states S_in(p) = A(p-1) S_in(p-1) + B(p-1) per sequence, and runs the
+ * forward over all segments once more from S_in, which writes o.
  *
  * Segments are cut at multiples of 64 rows: sequence n of length L gets
  * segments of roundup(ceil(L/segments), 64) rows, the last shorter and
  * trailing ones possibly empty. The results equal kda_chunk_fwd's up to
- * rounding; bf16 outputs are rounded twice (o(0, v) and the sum).
+ * rounding (the entry states carry the rounding of A and B).
  *
  *   segments   1 .. 4096; 1 (or T = 0) runs kda_chunk_fwd and needs no
  *              workspace
