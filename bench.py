@@ -1,6 +1,6 @@
 """Benchmark: KDA chunked forward on the K3 layer shape, one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-backward]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-backward] [--no-split]
                     [--only split|backward]
 
 One step = one kda_chunk_fwd call over a K3-shaped batch: B=1, T=4096, H=96,
@@ -462,6 +462,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-split", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--only", choices=["split", "backward"], default=None,
                     help="run one secondary leg alone and print its JSON object (for per-kernel profiles)")
@@ -524,7 +525,8 @@ def main():
     }
     line["prologue"] = bench_prologue(args.steps, args.warmup)
     line["short_conv"] = bench_conv(args.steps, args.warmup)
-    line["split"] = bench_split(args.steps, args.warmup)
+    if not args.no_split:
+        line["split"] = bench_split(args.steps, args.warmup)
     if not args.no_backward:
         line["backward"] = bench_backward(args.steps, args.warmup, cpu=not args.no_cpu_baseline)
     if not args.no_decode:

@@ -57,18 +57,25 @@ __global__ void fill_identity_kernel(float* p, int64_t mats, int Dk) {
 
 // One workgroup per (sequence, head, 16-column slice of d_v): the chain of
 // entry states S_in(p) over the sequence's P segments, and its final state.
-// A is [N*P][H][Dk][Dk], Bst and Sin are [N*P][H][Dk][Dv].
+// A is [N*P][H][Dk][Dk], Bst and Sin are [N*P][H][Dk][Dv]. Each step stages
+// A(p) in LDS with coalesced 16-byte loads.
 template <int DK>
 __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const float* Bst, const float* s0,
                                                          float* Sin, float* sT, int32_t N, int32_t H,
                                                          int32_t Dv, int32_t P) {
     constexpr int BVs = 16;
+    constexpr int NT = 256;
+    constexpr int kQuads = DK * DK / 4;                       // float4 pieces of A
+    constexpr int kPer = kQuads / NT > 0 ? kQuads / NT : 1;   // per thread
+    constexpr int kOut = DK * BVs / NT > 0 ? DK * BVs / NT : 1;
+    __shared__ float sA[DK][DK + 4];
     __shared__ float sS[DK][BVs + 1];
+    const int tid = threadIdx.x;
     const int nvt = Dv / BVs;
     const int vt = blockIdx.x % nvt, unit = blockIdx.x / nvt;
     const int n = unit / H, h = unit % H;
     const int c0 = vt * BVs;
-    for (int idx = threadIdx.x; idx < DK * BVs; idx += blockDim.x) {
+    for (int idx = tid; idx < DK * BVs; idx += NT) {
         const int c = idx / BVs, j = idx % BVs;
         sS[c][j] = s0 ? s0[(((int64_t)n * H + h) * DK + c) * Dv + c0 + j] : 0.f;
     }
@@ -76,30 +83,57 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
     for (int p = 0; p < P; ++p) {
         const int64_t seg = (int64_t)n * P + p;
         float* sin = Sin + (seg * H + h) * (int64_t)DK * Dv;
-        for (int idx = threadIdx.x; idx < DK * BVs; idx += blockDim.x) {
+        for (int idx = tid; idx < DK * BVs; idx += NT) {
             const int c = idx / BVs, j = idx % BVs;
             sin[(int64_t)c * Dv + c0 + j] = sS[c][j];
         }
         if (p == P - 1 && !sT) break;
         // S <- A(p) S + B(p)
-        const float* a = A + (seg * H + h) * (int64_t)DK * DK;
+        const float4* a4 = reinterpret_cast<const float4*>(A + (seg * H + h) * (int64_t)DK * DK);
         const float* b = Bst + (seg * H + h) * (int64_t)DK * Dv;
-        float out[DK * BVs / 256 > 0 ? DK * BVs / 256 : 1];
-        int m = 0;
-        for (int idx = threadIdx.x; idx < DK * BVs; idx += blockDim.x, ++m) {
-            const int c = idx / BVs, j = idx % BVs;
-            float acc = b[(int64_t)c * Dv + c0 + j];
-            const float* arow = a + (int64_t)c * DK;
-            for (int i = 0; i < DK; ++i) acc += arow[i] * sS[i][j];
-            out[m] = acc;
+        float4 ra[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int q = tid + NT * u;
+            ra[u] = q < kQuads ? a4[q] : float4{0.f, 0.f, 0.f, 0.f};
+        }
+        float rb[kOut];
+#pragma unroll
+        for (int u = 0; u < kOut; ++u) {
+            const int idx = tid + NT * u;
+            rb[u] = idx < DK * BVs ? b[(int64_t)(idx / BVs) * Dv + c0 + idx % BVs] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int q = tid + NT * u;
+            if (q < kQuads) {
+                const int r = q / (DK / 4), c = (q % (DK / 4)) * 4;
+                sA[r][c] = ra[u].x; sA[r][c + 1] = ra[u].y; sA[r][c + 2] = ra[u].z; sA[r][c + 3] = ra[u].w;
+            }
         }
         __syncthreads();
-        m = 0;
-        for (int idx = threadIdx.x; idx < DK * BVs; idx += blockDim.x, ++m) sS[idx / BVs][idx % BVs] = out[m];
+        float out[kOut];
+#pragma unroll
+        for (int u = 0; u < kOut; ++u) {
+            const int idx = tid + NT * u;
+            const int c = idx / BVs, j = idx % BVs;
+            float acc = rb[u];
+            if (idx < DK * BVs) {
+#pragma unroll 8
+                for (int i = 0; i < DK; ++i) acc += sA[c][i] * sS[i][j];
+            }
+            out[u] = acc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kOut; ++u) {
+            const int idx = tid + NT * u;
+            if (idx < DK * BVs) sS[idx / BVs][idx % BVs] = out[u];
+        }
         __syncthreads();
     }
     if (sT) {
-        for (int idx = threadIdx.x; idx < DK * BVs; idx += blockDim.x) {
+        for (int idx = tid; idx < DK * BVs; idx += NT) {
             const int c = idx / BVs, j = idx % BVs;
             sT[(((int64_t)n * H + h) * DK + c) * Dv + c0 + j] = sS[c][j];
         }
