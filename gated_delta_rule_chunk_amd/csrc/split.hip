@@ -112,23 +112,45 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
             }
         }
         __syncthreads();
-        float out[kOut];
+        if constexpr (DK == 128) {
+            // S_new = A S + B on the matrix cores: 8 row tiles of 16 x 16, two per wave
+            const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
+            f32x4 acc[2];
 #pragma unroll
-        for (int u = 0; u < kOut; ++u) {
-            const int idx = tid + NT * u;
-            const int c = idx / BVs, j = idx % BVs;
-            float acc = rb[u];
-            if (idx < DK * BVs) {
+            for (int t = 0; t < 2; ++t) {
+                const int r0 = 16 * (2 * w + t);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[t][i] = b[(int64_t)(r0 + 4 * lg + i) * Dv + c0 + l16];
 #pragma unroll 8
-                for (int i = 0; i < DK; ++i) acc += sA[c][i] * sS[i][j];
+                for (int ks = 0; ks < DK / 4; ++ks)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[r0 + l16][4 * ks + lg], sS[4 * ks + lg][l16],
+                                                                  acc[t], 0, 0, 0);
             }
-            out[u] = acc;
-        }
-        __syncthreads();
+            __syncthreads();
 #pragma unroll
-        for (int u = 0; u < kOut; ++u) {
-            const int idx = tid + NT * u;
-            if (idx < DK * BVs) sS[idx / BVs][idx % BVs] = out[u];
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sS[16 * (2 * w + t) + 4 * lg + i][l16] = acc[t][i];
+            (void)rb;
+        } else {
+            float out[kOut];
+#pragma unroll
+            for (int u = 0; u < kOut; ++u) {
+                const int idx = tid + NT * u;
+                const int c = idx / BVs, j = idx % BVs;
+                float acc = rb[u];
+                if (idx < DK * BVs) {
+#pragma unroll 8
+                    for (int i = 0; i < DK; ++i) acc += sA[c][i] * sS[i][j];
+                }
+                out[u] = acc;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < kOut; ++u) {
+                const int idx = tid + NT * u;
+                if (idx < DK * BVs) sS[idx / BVs][idx % BVs] = out[u];
+            }
         }
         __syncthreads();
     }
