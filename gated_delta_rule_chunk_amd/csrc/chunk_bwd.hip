@@ -539,6 +539,7 @@ struct Smem {
     float W[C][VP], U[C][VP], dO[C][VP], dUW[C][VP], dY[C][VP];
     float KK[C][CP], P[C][CP], T[C][CP], dP[C][CP], dKK[C][CP];
     float beta[C], EC[DK];
+    float dbp[C], xd[C];   // the two parts of dbeta
 };
 
 __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
@@ -972,8 +973,8 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
             for (int i = 0; i < 4; ++i) sm.dY[4 * lg + i][16 * t + l16] = acc[i];
         }
         __syncthreads();
-        // dP = scale dO U^T (wave 0);  dKK = -Diag(beta) dY U^T and dbeta (wave 1);
-        // dW = Diag(beta) dY = dV (all)
+        // dP = scale dO U^T (wave 0);  dKK = -Diag(beta) dY U^T and its part of
+        // dbeta (wave 1);  dY_r . W_r (wave 2);  dW = Diag(beta) dY = dV (all)
         if (w == 0) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -985,29 +986,30 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
                 sm.dP[r][l16] = l16 <= r ? scale * acc[i] : 0.f;
             }
         } else if (w == 1) {
-            f32x4 am = {0.f, 0.f, 0.f, 0.f}, ax = am;
+            f32x4 am = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < BV / 4; ++ks) {
-                const float dy = sm.dY[l16][4 * ks + lg];
-                am = mfma(dy, sm.U[l16][4 * ks + lg], am);
-                ax = mfma(dy, sm.W[l16][4 * ks + lg], ax);
-            }
-            // dbeta_r = dY_r . W_r + sum_s dM[r][s] KK[r][s]
+            for (int ks = 0; ks < BV / 4; ++ks) am = mfma(sm.dY[l16][4 * ks + lg], sm.U[l16][4 * ks + lg], am);
+            // sum_s dM[r][s] KK[r][s]
             float part[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * lg + i, s = l16;
                 const float dm = s < r ? -am[i] : 0.f;
                 sm.dKK[r][s] = sm.beta[r] * dm;
-                part[i] = row16_sum(dm * sm.KK[r][s] + (s == r ? ax[i] : 0.f));
+                part[i] = row16_sum(dm * sm.KK[r][s]);
             }
             if (l16 == 15) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * lg + i;
-                    if (r < rows) add_out(a.dbeta + (sq.b * a.T + t0 + r) * H + h, part[i], atomic);
-                }
+                for (int i = 0; i < 4; ++i) sm.dbp[4 * lg + i] = part[i];
             }
+        } else if (w == 2) {
+            // dY_r . W_r: the diagonal of dY W^T
+            f32x4 ax = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < BV / 4; ++ks) ax = mfma(sm.dY[l16][4 * ks + lg], sm.W[l16][4 * ks + lg], ax);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (l16 == 4 * lg + i) sm.xd[l16] = ax[i];
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -1018,6 +1020,8 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
             if (r < rows) a.dv[((sq.b * a.T + t0 + r) * H + h) * (int64_t)Dv + c0 + j] = dw;
         }
         __syncthreads();
+        if (tid < C && tid < rows)   // dbeta_r = dY_r . W_r + sum_s dM[r][s] KK[r][s]
+            add_out(a.dbeta + (sq.b * a.T + t0 + tid) * H + h, sm.xd[tid] + sm.dbp[tid], atomic);
         // Channel tile cw..cw+15 of this wave: dense terms, pair terms, dq,
         // dk, dg, then the state gradient's rows cw..cw+15.
         {
