@@ -901,9 +901,33 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
         __syncthreads();
         chunk_scale(sm, false);
         __syncthreads();
-        if (w < 4) w_tile(sm, w, l16, lg);
+        // W = V - Kg S with the channel sum split over two waves per column
+        // tile: waves 4-7 leave their half in sm.dUW (free in this sweep)
+        f32x4 wpart = {0.f, 0.f, 0.f, 0.f};
+        {
+            const int t = w & 3, kb = (w >> 2) * (DK / 8);   // 32 k-steps of 4 channels, half each
+            f32x4 a1 = wpart;
+#pragma unroll 4
+            for (int ks = kb; ks < kb + DK / 8; ks += 2) {
+                wpart = mfma(sm.Kg[l16][4 * ks + lg], sm.S[4 * ks + lg][16 * t + l16], wpart);
+                a1 = mfma(sm.Kg[l16][4 * ks + 4 + lg], sm.S[4 * ks + 4 + lg][16 * t + l16], a1);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wpart[i] += a1[i];
+            if (w >= 4) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.dUW[4 * lg + i][16 * t + l16] = wpart[i];
+            }
+        }
         __syncthreads();
-        if (w < 4) u_tile(sm, w, l16, lg);
+        if (w < 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i, j = 16 * w + l16;
+                sm.W[r][j] -= wpart[i] + sm.dUW[r][j];
+            }
+            u_tile(sm, w, l16, lg);   // reads only this wave's columns of W
+        }
         __syncthreads();
         // S <- Diag(e^Gamma_C) S + Kh^T U
         {
