@@ -134,3 +134,21 @@ def test_bwd_full_k3_shape_sampled_heads():
         e = rel(xs, r)
         say(f"        {name} relL2={e:.2e}")
         assert np.isfinite(x).all() and e <= TOL_F32, (name, e)
+
+
+@pytest.mark.slow
+def test_bwd_full_packed_varlen_sampled_heads():
+    # The packed workload: 16 sequences of U[128, 8192] tokens, H=96, d=128, bf16, with
+    # a final-state cotangent; the oracle checks two heads of every sequence.
+    w = synth.WORKLOADS["k3_varlen16"]
+    inp = synth.make_workload(w)
+    d_o, dfin = synth.make_cotangents(inp, seed=580)
+    say(f"[case] bwd full {w.name} T={inp['q'].shape[1]}")
+    got = gpu_bwd(inp, d_o, dfin, scale=128 ** -0.5)
+    heads = [7, 88]
+    ref = oracle_bwd(inp, d_o, dfin, scale=128 ** -0.5, heads=heads)
+    for name, x, r in zip(NAMES, got, ref):
+        xs = x[:, heads] if name == "d_initial" else x[:, :, heads]
+        e = rel(xs, r)
+        say(f"        {name} relL2={e:.2e}")
+        assert np.isfinite(x).all() and e <= TOL_F32, (name, e)

@@ -96,3 +96,18 @@ def test_split_few_heads_long_sequence_sampled_heads():
     eo, ef = rel(o[:, :, heads], ro), rel(fin[:, heads], rfin)
     say(f"        relL2 o={eo:.3e} final={ef:.3e}")
     assert np.isfinite(o).all() and eo <= TOL_BF16 and ef <= TOL_BF16, (eo, ef)
+
+
+@pytest.mark.slow
+def test_split_full_packed_varlen_sampled_heads():
+    # The packed workload (16 sequences of U[128, 8192] tokens, H=96) with an initial state, cut into
+    # 4 segments per sequence; the oracle checks three heads of every sequence.
+    w = synth.WORKLOADS["k3_varlen16"]
+    inp = synth.make_workload(w, init_state=True)
+    say(f"[case] split full {w.name} T={inp['q'].shape[1]} segments=4")
+    o, fin = gpu_split(inp, 4)
+    heads = [0, 41, 95]
+    ro, rfin = oracle_chunk(inp, heads=heads)
+    eo, ef = rel(o[:, :, heads], ro), rel(fin[:, heads], rfin)
+    say(f"        relL2 o={eo:.3e} final={ef:.3e}")
+    assert np.isfinite(o).all() and eo <= TOL_BF16 and ef <= TOL_BF16, (eo, ef)
