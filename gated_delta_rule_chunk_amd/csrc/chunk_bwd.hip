@@ -1,4 +1,6 @@
-// Chunkwise KDA backward in float32 on the vector ALUs.
+// Chunkwise KDA backward, all arithmetic in float32: a vector-ALU path for
+// every supported head size (this part of the file) and a matrix-core path
+// for d_k = 128 (namespace mf below).
 //
 // Loss: L = sum_t <dO_t, o_t> + <dS_final, S_final>. The forward's chunk form
 // (16-row chunks, Gamma = in-chunk cumulative log-decay per channel, entry
@@ -19,9 +21,9 @@
 // cumulative sum of dGamma over the chunk, Gamma_C's gradient entering at
 // its last row.
 //
-// Two kernels: chunk_states_kernel re-runs the forward and writes each
-// chunk's entry state to a caller-provided workspace; chunk_bwd_kernel walks
-// every sequence backward from its last chunk. Both own one (sequence, head,
+// Vector-ALU path, two kernels: chunk_states_kernel re-runs the forward and
+// writes each chunk's entry state to a caller-provided workspace;
+// chunk_bwd_kernel walks every sequence backward from its last chunk. Both own one (sequence, head,
 // value slice of up to 64 columns). The slices' partial sums of dq, dk, dg
 // and dbeta meet in float32 atomic adds onto zeroed outputs; with two slices
 // (d_v = 128) the sum does not depend on their order.
