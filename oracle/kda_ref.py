@@ -31,7 +31,8 @@ forward, not against each other alone.
 The gate, beta and normalisation prologue that turns raw projections into
 (q, k, g, beta) has a NumPy form (``prologue``, then ``recurrence``) and a C
 form (``c_prologue_forward``); the reading of the gate it implements is in
-``prologue``'s docstring.
+``prologue``'s docstring. ``prologue_backward`` is its reverse-mode gradient,
+pinned by central differences of prologue-then-recurrence.
 Both take inputs as float arrays that hold the GPU's bf16 or fp32 values
 exactly, and compute in float64.
 """
@@ -148,10 +149,7 @@ def recurrence_backward(q, k, v, g, beta, d_o, initial_state=None, d_final=None,
 
 
 def prologue(q_raw, k_raw, g_logit, beta_logit, A_log, dt_bias, gate_lower_bound=-5.0, l2_eps=1e-6):
-    """The reverse-mode gradient has the same two forms (``recurrence_backward``,
-``c_backward``); both are pinned against central finite differences of the
-forward, not against each other alone.
-The gate, beta and normalisation prologue (float64), per token and head.
+    """The gate, beta and normalisation prologue (float64), per token and head.
 
     The pages fix the gate's parameters and bound but not its formula (hysenlabs
     "kimi-k3-mlx", section "The A_log shape mismatch is a silent-garbage bug the
@@ -177,6 +175,42 @@ The gate, beta and normalisation prologue (float64), per token and head.
     g = gate_lower_bound / (1.0 + np.exp(-(A * (g_logit + bias))))
     beta = 1.0 / (1.0 + np.exp(-beta_logit))
     return q, k, g, beta
+
+
+def prologue_backward(q_raw, k_raw, g_logit, beta_logit, A_log, dt_bias, dq, dk, dg, dbeta,
+                      gate_lower_bound=-5.0, l2_eps=1e-6):
+    """Reverse-mode gradient of ``prologue`` (float64): given the gradients with
+    respect to its outputs (q, k, g, beta), those with respect to its inputs.
+    Differentiating each line of the prologue:
+
+        q = x / n, n = sqrt(|x|^2 + eps) (per row):  dx = dq / n - x (x . dq) / n^3
+        g = lb * s, s = sigmoid(z), z = exp(A_log[c]) (x + dt_bias[h, c]):
+            dz = dg lb s (1 - s);  dx = dz exp(A_log[c]);
+            d dt_bias[h, c] = sum over tokens of dz exp(A_log[c]);
+            d A_log[c] = sum over tokens and heads of dz z
+        beta = sigmoid(y):  dy = dbeta beta (1 - beta)
+
+    Shapes as ``prologue``; returns (dq_raw, dk_raw, dg_logit, dbeta_logit,
+    dA_log [Dk], ddt_bias [H*Dk]).
+    """
+    q_raw, k_raw, g_logit, dq, dk, dg = (np.asarray(a, dtype=np.float64)
+                                         for a in (q_raw, k_raw, g_logit, dq, dk, dg))
+    beta_logit, dbeta = np.asarray(beta_logit, dtype=np.float64), np.asarray(dbeta, dtype=np.float64)
+    H, Dk = q_raw.shape[-2:]
+    A = np.exp(np.asarray(A_log, dtype=np.float64).reshape(Dk))
+    bias = np.asarray(dt_bias, dtype=np.float64).reshape(H, Dk)
+
+    def l2_back(x, dy):
+        n = np.sqrt((x * x).sum(-1, keepdims=True) + l2_eps)
+        return dy / n - x * (x * dy).sum(-1, keepdims=True) / n ** 3
+
+    z = A * (g_logit + bias)
+    sg = 1.0 / (1.0 + np.exp(-z))
+    dz = dg * gate_lower_bound * sg * (1.0 - sg)
+    lead = tuple(range(dz.ndim - 2))                       # token axes
+    sb = 1.0 / (1.0 + np.exp(-beta_logit))
+    return (l2_back(q_raw, dq), l2_back(k_raw, dk), dz * A, dbeta * sb * (1.0 - sb),
+            (dz * z).sum(axis=lead + (dz.ndim - 2,)), (dz * A).sum(axis=lead).reshape(H * Dk))
 
 
 def short_conv(x, w, state=None, cu_seqlens=None, activation=False):
