@@ -69,6 +69,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_split.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, ctypes.c_int,
                                         I32, P, ctypes.c_size_t, P, P, P]
     lib.kda_chunk_fwd_split.restype = ctypes.c_int
+    lib.kda_chunk_bwd_prologue_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+    lib.kda_chunk_bwd_prologue_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_chunk_bwd_prologue.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, I32, I32, I32, I32, I32, I32, F,
+                                           ctypes.c_int, P, ctypes.c_size_t, P, P, P, P, P, P, P, P, P]
+    lib.kda_chunk_bwd_prologue.restype = ctypes.c_int
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     lib.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_chunk_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, F, ctypes.c_int,
@@ -248,6 +253,49 @@ def chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, cu_
                            _ptr(dg), _ptr(dbeta), _ptr(d_init), _stream(dev))
     _check(st)
     return dq, dk, dv, dg, dbeta, d_init
+
+
+def chunk_bwd_prologue_workspace_bytes(B, T, H, Dk, Dv, N, packed):
+    """Bytes of workspace kda_chunk_bwd_prologue needs."""
+    return int(load_library().kda_chunk_bwd_prologue_workspace_bytes(B, T, H, Dk, Dv, N, int(bool(packed))))
+
+
+def chunk_bwd_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, d_o, gate_lower_bound=-5.0,
+                       l2_eps=1e-6, initial_state=None, d_final_state=None, cu_seqlens=None, scale=1.0,
+                       workspace=None, want_d_initial=True):
+    """Gradients for ``chunk_fwd_prologue`` (kda_chunk_bwd_prologue): returns
+    float32 (dq_raw, dk_raw, dv, dg_logit, dbeta_logit, dA_log, ddt_bias,
+    d_initial_state or None)."""
+    lib = load_library()
+    B, T, H, Dk, Dv, N, dt, dev = _chunk_inputs(q_raw, k_raw, v, g_logit, beta_logit, initial_state, cu_seqlens,
+                                                ("q_raw", "k_raw", "v", "g_logit", "beta_logit"))
+    _need(A_log, "A_log", (Dk,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H * Dk,), torch.float32, dev)
+    _need(d_o, "d_o", (B, T, H, Dv), dt, dev)
+    if d_final_state is not None:
+        _need(d_final_state, "d_final_state", (N, H, Dk, Dv), torch.float32, dev)
+    need = chunk_bwd_prologue_workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((B, T, H, Dk), **f32)
+    dk = torch.empty((B, T, H, Dk), **f32)
+    dg = torch.empty((B, T, H, Dk), **f32)
+    dv = torch.empty((B, T, H, Dv), **f32)
+    dbeta = torch.empty((B, T, H), **f32)
+    dA = torch.empty((Dk,), **f32)
+    dbias = torch.empty((H * Dk,), **f32)
+    d_init = torch.empty((N, H, Dk, Dv), **f32) if want_d_initial else None
+    st = lib.kda_chunk_bwd_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(g_logit), _ptr(beta_logit), _ptr(A_log),
+                                    _ptr(dt_bias), float(gate_lower_bound), float(l2_eps), _ptr(initial_state),
+                                    _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final_state), B, T, H, Dk, Dv, N,
+                                    float(scale), _DTYPES[dt], _ptr(workspace), workspace.numel(), _ptr(dq),
+                                    _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dA), _ptr(dbias), _ptr(d_init),
+                                    _stream(dev))
+    _check(st)
+    return dq, dk, dv, dg, dbeta, dA, dbias, d_init
 
 
 def chunk_fwd_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, gate_lower_bound=-5.0,

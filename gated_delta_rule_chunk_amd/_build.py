@@ -16,7 +16,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["kda_api.hip", "chunk_mfma.hip", "chunk_generic.hip", "chunk_bwd.hip", "recurrent_step.hip",
-           "short_conv.hip", "split.hip"]
+           "short_conv.hip", "split.hip", "prologue_bwd.hip"]
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     # no packed-fp32 instructions in any generated code

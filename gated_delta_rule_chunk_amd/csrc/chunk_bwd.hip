@@ -1182,6 +1182,8 @@ hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s) {
     return a.bf16 ? launch_dtype<__bf16>(a, s) : launch_dtype<float>(a, s);
 }
 
-bool chunk_bwd_mfma_supported(const BwdArgs& a) { return a.Dk == 128 && (a.Dv == 64 || a.Dv == 128); }
+bool chunk_bwd_mfma_supported(const BwdArgs& a) {
+    return a.Dk == 128 && (a.Dv == 64 || a.Dv == 128) && a.g_ge_m5;
+}
 
 }  // namespace kda

@@ -238,6 +238,88 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     return KDA_OK;
 }
 
+size_t kda_chunk_bwd_prologue_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
+                                              int32_t packed) {
+    if (B < 1 || T <= 0 || H < 1 || Dk < 1 || Dv < 1 || N < 0) return 0;
+    return (size_t)kda::prologue_bwd_layout(B, T, H, Dk, Dv, N, packed != 0).bytes;
+}
+
+kda_status kda_chunk_bwd_prologue(const void* q_raw, const void* k_raw, const void* v, const void* g_logit,
+                                  const void* beta_logit, const float* A_log, const float* dt_bias,
+                                  float gate_lower_bound, float l2_eps, const float* initial_state,
+                                  const int32_t* cu_seqlens, const void* d_o, const float* d_final_state, int32_t B,
+                                  int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N, float scale,
+                                  kda_dtype dtype, void* workspace, size_t workspace_bytes, float* dq_raw,
+                                  float* dk_raw, float* dv, float* dg_logit, float* dbeta_logit, float* dA_log,
+                                  float* ddt_bias, float* d_initial_state, void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_chunk_bwd_prologue";
+    if (!A_log || !dt_bias || !dA_log || !ddt_bias)
+        return fail(KDA_ERR_INVALID_ARG, "%s: A_log, dt_bias, dA_log and ddt_bias must be non-NULL", fn);
+    if (!(gate_lower_bound < 0.f) || !(gate_lower_bound > -1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: gate_lower_bound must be finite and negative (got %g)", fn,
+                    (double)gate_lower_bound);
+    if (!(l2_eps > 0.f) || !(l2_eps < 1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: l2_eps must be finite and positive (got %g)", fn, (double)l2_eps);
+    if (B < 1 || T < 0 || H < 1 || N < 0)
+        return fail(KDA_ERR_INVALID_ARG, "%s: need B >= 1, T >= 0, H >= 1, N >= 0 (got B=%d T=%d H=%d N=%d)",
+                    fn, B, T, H, N);
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dtype %d is not KDA_F32 or KDA_BF16", fn, (int)dtype);
+    if (!dim_ok(Dk) || !dim_ok(Dv))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: Dk=%d, Dv=%d; supported head dims are 16, 32, 64, 128", fn, Dk, Dv);
+    if (cu_seqlens) {
+        if (B != 1)
+            return fail(KDA_ERR_INVALID_ARG, "%s: packed sequences (cu_seqlens) need B == 1, got B=%d", fn, B);
+        if (N < 1) return fail(KDA_ERR_INVALID_ARG, "%s: packed sequences need N >= 1, got N=%d", fn, N);
+    } else if (N != B) {
+        return fail(KDA_ERR_INVALID_ARG, "%s: without cu_seqlens N must equal B (N=%d, B=%d)", fn, N, B);
+    }
+    if ((int64_t)N * H > ((int64_t)1 << 26))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", fn);
+    if (T > 0 && (!q_raw || !k_raw || !v || !g_logit || !beta_logit || !d_o))
+        return fail(KDA_ERR_INVALID_ARG, "%s: every input and d_o must be non-NULL when T > 0", fn);
+    if (T > 0 && (!dq_raw || !dk_raw || !dv || !dg_logit || !dbeta_logit))
+        return fail(KDA_ERR_INVALID_ARG, "%s: the token gradients must be non-NULL when T > 0", fn);
+    if ((int64_t)B * T * H > ((int64_t)1 << 40))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", fn);
+    const bool packed = cu_seqlens != nullptr;
+    const kda::PrologueBwdLayout L = kda::prologue_bwd_layout(B, T, H, Dk, Dv, N, packed);
+    const size_t need = T > 0 ? (size_t)L.bytes : 0;
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KDA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, got %zu%s", fn, need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    if (T > 0) {
+        const void* ins[] = {q_raw, k_raw, v, g_logit, beta_logit, d_o, workspace, A_log, dt_bias};
+        const void* outs[] = {dq_raw, dk_raw, dv, dg_logit, dbeta_logit, dA_log, ddt_bias};
+        for (const void* o : outs)
+            for (const void* i : ins)
+                if (o == i) return fail(KDA_ERR_INVALID_ARG, "%s: gradients must not alias an input", fn);
+    }
+    char* ws = static_cast<char*>(workspace);
+    kda::PrologueBwdArgs p;
+    p.q_raw = q_raw; p.k_raw = k_raw; p.g_logit = g_logit; p.beta_logit = beta_logit; p.v = v; p.d_o = d_o;
+    p.A_log = A_log; p.dt_bias = dt_bias; p.gate_lb = gate_lower_bound; p.l2_eps = l2_eps;
+    p.qf = reinterpret_cast<float*>(ws + L.qf); p.kf = reinterpret_cast<float*>(ws + L.kf);
+    p.gf = reinterpret_cast<float*>(ws + L.gf); p.bf = reinterpret_cast<float*>(ws + L.bf);
+    p.vf = reinterpret_cast<float*>(ws + L.vf); p.dof = reinterpret_cast<float*>(ws + L.dof);
+    p.dq = dq_raw; p.dk = dk_raw; p.dg = dg_logit; p.dbeta = dbeta_logit;
+    p.part_b = reinterpret_cast<float*>(ws + L.part_b); p.part_A = reinterpret_cast<float*>(ws + L.part_A);
+    p.d_A_log = dA_log; p.d_dt_bias = ddt_bias;
+    p.B = B; p.T = T; p.H = H; p.Dk = Dk; p.Dv = Dv; p.bf16 = dtype == KDA_BF16;
+    kda::BwdArgs a;
+    a.q = p.qf; a.k = p.kf; a.v = p.vf; a.g = p.gf; a.beta = p.bf; a.d_o = p.dof;
+    a.s0 = initial_state; a.cu = cu_seqlens; a.d_final = d_final_state;
+    a.ws = reinterpret_cast<float*>(ws + L.core);
+    a.dq = dq_raw; a.dk = dk_raw; a.dv = dv; a.dg = dg_logit; a.dbeta = dbeta_logit; a.d_s0 = d_initial_state;
+    a.B = B; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.N = N; a.scale = scale; a.bf16 = false;
+    a.g_ge_m5 = gate_lower_bound >= -5.f;   // g lies in (gate_lower_bound, 0)
+    if ((int64_t)N * H == 0) return KDA_OK;
+    const hipError_t e = kda::launch_prologue_bwd(p, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
+}
+
 kda_status kda_short_conv(const void* x, const float* weight, const float* conv_state_in,
                           const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t C, int32_t N,
                           int32_t activation, kda_dtype dtype, void* y, float* conv_state_out, void* stream) {

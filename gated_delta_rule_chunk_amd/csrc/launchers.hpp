@@ -87,6 +87,7 @@ struct BwdArgs {
     int32_t B, T, H, Dk, Dv, N;
     float scale;
     bool bf16;
+    bool g_ge_m5 = true;       // g >= -5 holds (the matrix-core kernel relies on it)
 };
 
 // The backward's workspace: a float32 chunk-entry state [H][Dk][Dv] per
@@ -102,6 +103,33 @@ __host__ __device__ inline int64_t chunk_bwd_ws_floats(int32_t B, int32_t T, int
 }
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s);
 bool chunk_bwd_mfma_supported(const BwdArgs& a);   // Dk = 128, Dv in {64, 128}
+
+// Backward from raw projections through the gate, beta and L2-norm prologue.
+struct PrologueBwdArgs {
+    const void* q_raw;
+    const void* k_raw;
+    const void* g_logit;
+    const void* beta_logit;
+    const void* v;
+    const void* d_o;
+    const float* A_log;        // [Dk]
+    const float* dt_bias;      // [H*Dk]
+    float gate_lb, l2_eps;
+    float *qf, *kf, *gf, *bf, *vf, *dof;   // prologue outputs, float32 (workspace)
+    float *dq, *dk, *dg, *dbeta;           // gradient buffers, transformed in place
+    float *part_b, *part_A;                // per (token block, head, channel) partial sums (workspace)
+    float *d_A_log, *d_dt_bias;
+    int32_t B, T, H, Dk, Dv;
+    bool bf16;
+};
+// Byte offsets in its workspace (256-aligned): the recurrence backward's own
+// workspace first, then the float32 prologue outputs and the partial sums.
+struct PrologueBwdLayout {
+    int64_t core, qf, kf, gf, bf, vf, dof, part_b, part_A, bytes;
+};
+PrologueBwdLayout prologue_bwd_layout(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
+                                      bool packed);
+hipError_t launch_prologue_bwd(const PrologueBwdArgs& p, const BwdArgs& core, hipStream_t s);
 
 // Workspace of the intra-sequence split (byte offsets, 256-aligned).
 struct SplitLayout {

@@ -212,6 +212,59 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
                          void* stream);
 
 /*
+ * Bytes of device workspace kda_chunk_bwd_prologue needs: that of
+ * kda_chunk_bwd for the same sizes, plus float32 copies of the prologue's
+ * outputs (q, k, g [B,T,H,Dk], beta [B,T,H]) and of v and d_o [B,T,H,Dv], plus
+ * 2 x ceil(B*T/64) x H x Dk floats of partial sums. 0 when T = 0 or a size is
+ * out of range.
+ */
+size_t kda_chunk_bwd_prologue_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
+                                              int32_t packed);
+
+/*
+ * Backward of kda_chunk_fwd_prologue: the gradients of
+ *   L = sum_t <d_o[t], o[t]> + sum_n <d_final_state[n], final_state[n]>
+ * with respect to the raw projections q_raw, k_raw, g_logit, beta_logit, to v,
+ * to the gate parameters A_log and dt_bias, and to initial_state. The prologue
+ * (the reading documented with kda_chunk_fwd_prologue) is differentiated line
+ * by line:
+ *   q = x / n, n = sqrt(|x|^2 + eps):  dx = dq / n - x (x . dq) / n^3   (k likewise)
+ *   g = lb s, s = sigmoid(z), z = exp(A_log[c]) (g_logit + dt_bias[h,c]):
+ *     dz = dg lb s (1 - s), d g_logit = dz exp(A_log[c]),
+ *     d dt_bias[h,c] = sum over tokens of dz exp(A_log[c]),
+ *     d A_log[c] = sum over tokens and heads of dz z
+ *   beta = sigmoid(y):  dy = dbeta beta (1 - beta)
+ * around kda_chunk_bwd's gradient of the recurrence. The K3 gate's
+ * parameters are trained with the layer (they are checkpoint weights:
+ * hysenlabs "kimi-k3-mlx", section "The A_log shape mismatch is a
+ * silent-garbage bug the tests assert").
+ *
+ *   inputs     as kda_chunk_fwd_prologue (same dtype for the raw projections,
+ *              v and d_o), with d_o and d_final_state as in kda_chunk_bwd
+ *   workspace  at least kda_chunk_bwd_prologue_workspace_bytes(...) bytes,
+ *              owned by the caller; contents on entry do not matter
+ *   dq_raw, dk_raw, dg_logit [B,T,H,Dk], dv [B,T,H,Dv], dbeta_logit [B,T,H],
+ *   dA_log [Dk], ddt_bias [H*Dk], d_initial_state [N,H,Dk,Dv] (or NULL):
+ *              float32 outputs; must not alias an input or the workspace
+ *
+ * The recurrence's part runs on float32 copies of the prologue's outputs, so
+ * every step is float32 (kda_chunk_bwd's matrix-core kernel for Dk = 128 and
+ * gate_lower_bound >= -5, its vector-ALU kernel otherwise).
+ * dA_log and ddt_bias are summed in a fixed order and the call is
+ * deterministic. Errors as for kda_chunk_bwd; a NULL A_log, dt_bias, dA_log
+ * or ddt_bias, a non-negative or non-finite gate_lower_bound or a
+ * non-positive l2_eps is KDA_ERR_INVALID_ARG.
+ */
+kda_status kda_chunk_bwd_prologue(const void* q_raw, const void* k_raw, const void* v, const void* g_logit,
+                                  const void* beta_logit, const float* A_log, const float* dt_bias,
+                                  float gate_lower_bound, float l2_eps, const float* initial_state,
+                                  const int32_t* cu_seqlens, const void* d_o, const float* d_final_state, int32_t B,
+                                  int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N, float scale,
+                                  kda_dtype dtype, void* workspace, size_t workspace_bytes, float* dq_raw,
+                                  float* dk_raw, float* dv, float* dg_logit, float* dbeta_logit, float* dA_log,
+                                  float* ddt_bias, float* d_initial_state, void* stream);
+
+/*
  * Short causal depthwise convolution over time (kernel size 4), the step that
  * KDA applies to the query, key and value projections before the recurrence
  * (hysenlabs "kimi-k3-mlx", section "Attention is 93 layers split between KDA

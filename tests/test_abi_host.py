@@ -24,6 +24,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step", "kda_short_conv",
                           "kda_short_conv_step", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
                           "kda_chunk_fwd_split", "kda_chunk_fwd_split_workspace_bytes",
+                          "kda_chunk_bwd_prologue", "kda_chunk_bwd_prologue_workspace_bytes",
                           "kda_status_string", "kda_last_error_message"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -282,3 +283,44 @@ def test_chunk_fwd_split_workspace_bytes(lib):
     rows = 4096 * 12
     assert a >= rows * 128 * 2 * 2 + 3 * 8 * 12 * 128 * 128 * 4
     assert b - a == rows * 128 * 2 * 2
+
+
+def _bwd_pro(lib, **kw):
+    W = ctypes.c_void_p(0x3000)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A=ctypes.c_void_p(0x9000), b=ctypes.c_void_p(0xA000),
+             lb=-5.0, eps=1e-6, s0=None, cu=None, do=FAKE, dfin=None, B=1, T=64, H=2, Dk=128, Dv=128, N=1,
+             scale=1.0, dtype=kda.KDA_BF16, ws=W, wsb=1 << 34, dq=ctypes.c_void_p(0x4000),
+             dk=ctypes.c_void_p(0x5000), dv=ctypes.c_void_p(0x6000), dg=ctypes.c_void_p(0x7000),
+             db=ctypes.c_void_p(0x8000), dA=ctypes.c_void_p(0xB000), dbias=ctypes.c_void_p(0xC000), d0=None,
+             stream=None)
+    a.update(kw)
+    return lib.kda_chunk_bwd_prologue(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A"], a["b"], a["lb"], a["eps"],
+                                      a["s0"], a["cu"], a["do"], a["dfin"], a["B"], a["T"], a["H"], a["Dk"],
+                                      a["Dv"], a["N"], a["scale"], a["dtype"], a["ws"], a["wsb"], a["dq"], a["dk"],
+                                      a["dv"], a["dg"], a["db"], a["dA"], a["dbias"], a["d0"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(A=None), kda.KDA_ERR_INVALID_ARG, "A_log"),
+    (dict(dbias=None), kda.KDA_ERR_INVALID_ARG, "ddt_bias"),
+    (dict(lb=0.0), kda.KDA_ERR_INVALID_ARG, "gate_lower_bound"),
+    (dict(eps=0.0), kda.KDA_ERR_INVALID_ARG, "l2_eps"),
+    (dict(do=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(Dk=96), kda.KDA_ERR_UNSUPPORTED, "head dims"),
+    (dict(N=2), kda.KDA_ERR_INVALID_ARG, "N must equal B"),
+    (dict(wsb=100), kda.KDA_ERR_INVALID_ARG, "workspace"),
+    (dict(dq=FAKE), kda.KDA_ERR_INVALID_ARG, "alias"),
+    (dict(dA=ctypes.c_void_p(0x9000)), kda.KDA_ERR_INVALID_ARG, "alias"),
+])
+def test_chunk_bwd_prologue_rejects_before_launch(lib, kw, status, needle):
+    st = _bwd_pro(lib, **kw)
+    assert st == status
+    assert needle in lib.kda_last_error_message().decode()
+
+
+def test_chunk_bwd_prologue_workspace_bytes(lib):
+    core = kda.chunk_bwd_workspace_bytes(1, 4096, 96, 128, 128, 1, False)
+    total = kda.chunk_bwd_prologue_workspace_bytes(1, 4096, 96, 128, 128, 1, False)
+    rows = 4096 * 96
+    assert total >= core + rows * (3 * 128 + 1 + 2 * 128) * 4 + 2 * 64 * 96 * 128 * 4
+    assert kda.chunk_bwd_prologue_workspace_bytes(1, 0, 96, 128, 128, 1, False) == 0
