@@ -28,7 +28,8 @@ a fixed count that does not depend on the chunk size the kernel uses. ``backward
 the same workload with output and final-state cotangents, against the fp32
 matrix-core peak (its products run as float32 MFMA) with the algorithmic flop
 count of the chunked backward (recompute included), plus the fp64 oracle's
-backward on the same workload. ``split`` times the intra-sequence split
+backward on the same workload; its ``from_raw_projections`` entry times the
+backward through the gate, beta and L2-norm prologue (kda_chunk_bwd_prologue). ``split`` times the intra-sequence split
 (kda_chunk_fwd_split, 10 segments) on 12 heads at T=32768 against the unsplit
 call. ``decode`` times kda_recurrent_step on
 256 rows x 96 heads against an fp32 state cache (HBM-bound). ``cpu_baseline``
@@ -349,9 +350,45 @@ def bench_backward(steps, warmup, cpu=True):
                    "workspace_bytes_each_way": w.T // 16 * w.H * w.Dk * w.Dv * 4},
            "timed": "one kda_chunk_bwd call: zero fills of the atomically summed gradients, the per-chunk "
                     "T/P/KK kernel, the sequential kernel"}
+    res["from_raw_projections"] = bench_backward_prologue(steps, warmup)
     if cpu:
         res["cpu_baseline"] = cpu_backward_baseline()
     return res
+
+
+def bench_backward_prologue(steps, warmup):
+    """kda_chunk_bwd_prologue on k3_t4096: the same backward from raw
+    projections, through the gate, beta and L2-norm prologue (gradients of the
+    raw inputs, A_log and dt_bias)."""
+    w = synth.WORKLOADS["k3_t4096"]
+    dev = torch.device("cuda:0")
+    sets = []
+    for s_ in range(2):
+        inp = synth.make_prologue_inputs(w.B, w.T, w.H, w.Dk, w.Dv, seed=w.seed + 1000 * s_, dtype=w.dtype)
+        d_o, dfin = synth.make_cotangents({"v": inp["v"], "q": inp["q_raw"], "cu_seqlens": None},
+                                          seed=w.seed + 1000 * s_ + 7)
+        d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+        d["d_o"], d["d_final"] = d_o.to(dev), dfin.to(dev)
+        sets.append(d)
+    ws = torch.empty((kda.chunk_bwd_prologue_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, w.B, False),),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+
+    def step(i):
+        d = sets[i % 2]
+        out["g"] = kda.chunk_bwd_prologue(d["q_raw"], d["k_raw"], d["v"], d["g_logit"], d["beta_logit"], d["A_log"],
+                                          d["dt_bias"], d["d_o"], gate_lower_bound=synth.GATE_LOWER_BOUND,
+                                          l2_eps=1e-6, d_final_state=d["d_final"], scale=w.Dk ** -0.5,
+                                          workspace=ws)
+
+    wall, _, batch = time_launches(step, steps, warmup, stream)
+    if not all(torch.isfinite(x).all() for x in out["g"] if x is not None):
+        raise RuntimeError("non-finite backward output")
+    return {"workload": "k3_t4096 backward from raw projections (gate lb=-5, L2 eps 1e-6): gradients of q_raw, "
+                        "k_raw, v, g_logit, beta_logit, A_log, dt_bias and the initial state",
+            "ms_per_step": wall / steps * 1e3, "kernel_ms": float(batch),
+            "tokens_per_s": w.T / (float(batch) * 1e-3)}
 
 
 def bench_split(steps, warmup, segments=10):

@@ -12,7 +12,8 @@
 //      (k likewise), dz = dg lb s (1 - s), dx_g = dz e^{A_log}, dy = dbeta beta
 //      (1 - beta); and per (token block, head, channel) partial sums of
 //      dz e^{A_log} (for dt_bias) and dz z (for A_log);
-//   4. prologue_reduce_kernel: those partials summed in a fixed order.
+//   4. prologue_reduce_bias_kernel, prologue_reduce_alog_kernel: those partials
+//      summed in a fixed order.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -21,132 +22,200 @@ namespace {
 
 constexpr int kTokBlock = 64;   // tokens per workgroup of the prologue kernels
 
-// Sum over the workgroup's channel threads (blockDim.x = max(DK, 64), one or
-// two waves); every thread gets the totals. `red` holds 2 waves x NV floats.
-template <int NV>
-__device__ __forceinline__ void block_sum(float (&v)[NV], float* red) {
+constexpr int kPThreads = 256;
+
+// Eight consecutive input elements (16 bytes of bf16 or 32 of float32).
+template <typename T> __device__ __forceinline__ void load8(const T* p, int64_t i, float* o);
+template <> __device__ __forceinline__ void load8<float>(const float* p, int64_t i, float* o) {
+    const float4 a = *reinterpret_cast<const float4*>(p + i);
+    const float4 b = *reinterpret_cast<const float4*>(p + i + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+template <> __device__ __forceinline__ void load8<__bf16>(const __bf16* p, int64_t i, float* o) {
+    unpack8(*reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + i), o);
+}
+__device__ __forceinline__ void store8(float* p, int64_t i, const float* v) {
+    *reinterpret_cast<float4*>(p + i) = float4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<float4*>(p + i + 4) = float4{v[4], v[5], v[6], v[7]};
+}
+
+// Sum over the L lanes (a power of two, at most 16) that share a row: every
+// lane of the group gets the total.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) v[i] += __shfl_xor(v[i], m, 64);
-    if (blockDim.x > 64) {
-        const int w = threadIdx.x >> 6;
-        __syncthreads();
-        if ((threadIdx.x & 63) == 0)
-#pragma unroll
-            for (int i = 0; i < NV; ++i) red[w * NV + i] = v[i];
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < NV; ++i) v[i] = red[i] + red[NV + i];
-    }
+    for (int m = 1; m < L; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
 }
 
 __device__ __forceinline__ float sigmoid(float z) { return 1.f / (1.f + __expf(-z)); }
 
+// One workgroup per (block of kTokBlock tokens, head). L = DK/8 lanes hold
+// one (token, head) row, eight channels each, and 256/L rows go at once; row
+// sums are shuffles within the L lanes.
 template <typename Tin, int DK>
-__global__ __launch_bounds__(128) void prologue_apply_kernel(PrologueBwdArgs a) {
-    __shared__ float red[2 * 2];
-    const int c = threadIdx.x;
-    const bool on = c < DK;
+__global__ __launch_bounds__(kPThreads) void prologue_apply_kernel(PrologueBwdArgs a) {
+    constexpr int L = DK / 8, RPI = kPThreads / L;
+    const int tid = threadIdx.x, part = tid % L, rg = tid / L, c0 = 8 * part;
     const int h = blockIdx.y;
     const int64_t rows_total = (int64_t)a.B * a.T;
-    const float eA = on ? __expf(a.A_log[c]) : 0.f;
-    const float bias = on ? a.dt_bias[h * DK + c] : 0.f;
-    const Tin* xq = static_cast<const Tin*>(a.q_raw);
-    const Tin* xk = static_cast<const Tin*>(a.k_raw);
-    const Tin* xg = static_cast<const Tin*>(a.g_logit);
-    const Tin* xb = static_cast<const Tin*>(a.beta_logit);
-    const Tin* v = static_cast<const Tin*>(a.v);
-    const Tin* d_o = static_cast<const Tin*>(a.d_o);
-    const int64_t t_end = min((int64_t)(blockIdx.x + 1) * kTokBlock, rows_total);
-    for (int64_t t = (int64_t)blockIdx.x * kTokBlock; t < t_end; ++t) {
-        const int64_t row = t * a.H + h;
-        const float q = on ? load_elem(xq, row * DK + c) : 0.f;
-        const float k = on ? load_elem(xk, row * DK + c) : 0.f;
-        float s[2] = {q * q, k * k};
-        block_sum(s, red);
-        if (on) {
-            a.qf[row * DK + c] = q / sqrtf(s[0] + a.l2_eps);
-            a.kf[row * DK + c] = k / sqrtf(s[1] + a.l2_eps);
-            a.gf[row * DK + c] = a.gate_lb * sigmoid(eA * (load_elem(xg, row * DK + c) + bias));
+    const int64_t t0 = (int64_t)blockIdx.x * kTokBlock;
+    const int64_t t_end = min(t0 + kTokBlock, rows_total);
+    float eA[8], bias[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        eA[u] = __expf(a.A_log[c0 + u]);
+        bias[u] = a.dt_bias[h * DK + c0 + u];
+    }
+    for (int64_t t = t0 + rg; t < t_end; t += RPI) {
+        const int64_t row = t * a.H + h, e = row * DK + c0;
+        float q[8], k[8], g[8];
+        load8(static_cast<const Tin*>(a.q_raw), e, q);
+        load8(static_cast<const Tin*>(a.k_raw), e, k);
+        load8(static_cast<const Tin*>(a.g_logit), e, g);
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            sq += q[u] * q[u];
+            sk += k[u] * k[u];
         }
-        if (c == 0) a.bf[row] = sigmoid(load_elem(xb, row));
-        for (int j = c; j < a.Dv; j += blockDim.x) {
-            a.vf[row * a.Dv + j] = load_elem(v, row * a.Dv + j);
-            a.dof[row * a.Dv + j] = load_elem(d_o, row * a.Dv + j);
+        sq = group_sum<L>(sq);
+        sk = group_sum<L>(sk);
+        const float rq = 1.f / sqrtf(sq + a.l2_eps), rk = 1.f / sqrtf(sk + a.l2_eps);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            q[u] *= rq;
+            k[u] *= rk;
+            g[u] = a.gate_lb * sigmoid(eA[u] * (g[u] + bias[u]));
+        }
+        store8(a.qf, e, q);
+        store8(a.kf, e, k);
+        store8(a.gf, e, g);
+        if (part == 0) a.bf[row] = sigmoid(load_elem(static_cast<const Tin*>(a.beta_logit), row));
+    }
+    // v and dO widened to float32: Dv/8 lanes per row
+    const int LV = a.Dv / 8, RV = kPThreads / LV;
+    const int pv = tid % LV, rv = tid / LV;
+    if (rv < RV) {
+        for (int64_t t = t0 + rv; t < t_end; t += RV) {
+            const int64_t e = (t * a.H + h) * a.Dv + 8 * pv;
+            float x[8];
+            load8(static_cast<const Tin*>(a.v), e, x);
+            store8(a.vf, e, x);
+            load8(static_cast<const Tin*>(a.d_o), e, x);
+            store8(a.dof, e, x);
         }
     }
 }
 
 template <typename Tin, int DK>
-__global__ __launch_bounds__(128) void prologue_grad_kernel(PrologueBwdArgs a) {
-    __shared__ float red[2 * 4];
-    const int c = threadIdx.x;
-    const bool on = c < DK;
+__global__ __launch_bounds__(kPThreads) void prologue_grad_kernel(PrologueBwdArgs a) {
+    constexpr int L = DK / 8, RPI = kPThreads / L;
+    __shared__ float red[2][RPI][DK + 1];
+    const int tid = threadIdx.x, part = tid % L, rg = tid / L, c0 = 8 * part;
     const int h = blockIdx.y;
     const int64_t rows_total = (int64_t)a.B * a.T;
-    const float eA = on ? __expf(a.A_log[c]) : 0.f;
-    const float bias = on ? a.dt_bias[h * DK + c] : 0.f;
-    const Tin* xq = static_cast<const Tin*>(a.q_raw);
-    const Tin* xk = static_cast<const Tin*>(a.k_raw);
-    const Tin* xg = static_cast<const Tin*>(a.g_logit);
-    const Tin* xb = static_cast<const Tin*>(a.beta_logit);
-    float acc_b = 0.f, acc_A = 0.f;
-    const int64_t t_end = min((int64_t)(blockIdx.x + 1) * kTokBlock, rows_total);
-    for (int64_t t = (int64_t)blockIdx.x * kTokBlock; t < t_end; ++t) {
-        const int64_t row = t * a.H + h;
-        const int64_t e = row * DK + c;
-        const float q = on ? load_elem(xq, e) : 0.f;
-        const float k = on ? load_elem(xk, e) : 0.f;
-        const float dq = on ? a.dq[e] : 0.f;
-        const float dk = on ? a.dk[e] : 0.f;
-        float s[4] = {q * q, q * dq, k * k, k * dk};
-        block_sum(s, red);
-        if (on) {
-            const float nq = sqrtf(s[0] + a.l2_eps), nk = sqrtf(s[2] + a.l2_eps);
-            a.dq[e] = dq / nq - q * s[1] / (nq * nq * nq);
-            a.dk[e] = dk / nk - k * s[3] / (nk * nk * nk);
-            const float z = eA * (load_elem(xg, e) + bias);
-            const float sg = sigmoid(z);
-            const float dz = a.dg[e] * a.gate_lb * sg * (1.f - sg);
-            a.dg[e] = dz * eA;
-            acc_b += dz * eA;
-            acc_A += dz * z;
+    const int64_t t0 = (int64_t)blockIdx.x * kTokBlock;
+    const int64_t t_end = min(t0 + kTokBlock, rows_total);
+    float eA[8], bias[8], acc_b[8], acc_A[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        eA[u] = __expf(a.A_log[c0 + u]);
+        bias[u] = a.dt_bias[h * DK + c0 + u];
+        acc_b[u] = acc_A[u] = 0.f;
+    }
+    for (int64_t t = t0 + rg; t < t_end; t += RPI) {
+        const int64_t row = t * a.H + h, e = row * DK + c0;
+        float q[8], k[8], g[8], dq[8], dk[8], dg[8];
+        load8(static_cast<const Tin*>(a.q_raw), e, q);
+        load8(static_cast<const Tin*>(a.k_raw), e, k);
+        load8(static_cast<const Tin*>(a.g_logit), e, g);
+        load8(a.dq, e, dq);
+        load8(a.dk, e, dk);
+        load8(a.dg, e, dg);
+        float sq = 0.f, pq = 0.f, sk = 0.f, pk = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            sq += q[u] * q[u];
+            pq += q[u] * dq[u];
+            sk += k[u] * k[u];
+            pk += k[u] * dk[u];
         }
-        if (c == 0) {
-            const float sb = sigmoid(load_elem(xb, row));
+        sq = group_sum<L>(sq);
+        pq = group_sum<L>(pq);
+        sk = group_sum<L>(sk);
+        pk = group_sum<L>(pk);
+        const float nq = sqrtf(sq + a.l2_eps), nk = sqrtf(sk + a.l2_eps);
+        const float cq = pq / (nq * nq * nq), ck = pk / (nk * nk * nk);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            dq[u] = dq[u] / nq - q[u] * cq;
+            dk[u] = dk[u] / nk - k[u] * ck;
+            const float z = eA[u] * (g[u] + bias[u]);
+            const float sg = sigmoid(z);
+            const float dz = dg[u] * a.gate_lb * sg * (1.f - sg);
+            dg[u] = dz * eA[u];
+            acc_b[u] += dz * eA[u];
+            acc_A[u] += dz * z;
+        }
+        store8(a.dq, e, dq);
+        store8(a.dk, e, dk);
+        store8(a.dg, e, dg);
+        if (part == 0) {
+            const float sb = sigmoid(load_elem(static_cast<const Tin*>(a.beta_logit), row));
             a.dbeta[row] = a.dbeta[row] * sb * (1.f - sb);
         }
     }
-    if (on) {
+    // per-channel sums over this workgroup's row groups, in a fixed order
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        red[0][rg][c0 + u] = acc_b[u];
+        red[1][rg][c0 + u] = acc_A[u];
+    }
+    __syncthreads();
+    if (tid < 2 * DK) {
+        const int which = tid / DK, c = tid % DK;
+        float acc = 0.f;
+        for (int r = 0; r < RPI; ++r) acc += red[which][r][c];
         const int64_t p = ((int64_t)blockIdx.x * a.H + h) * DK + c;
-        a.part_b[p] = acc_b;
-        a.part_A[p] = acc_A;
+        (which == 0 ? a.part_b : a.part_A)[p] = acc;
     }
 }
 
-// ddt_bias[h][c] = sum over token blocks; dA_log[c] = sum over token blocks and
-// heads; one thread per output, in a fixed order.
-__global__ void prologue_reduce_kernel(PrologueBwdArgs a, int nblk, int DK) {
+// ddt_bias[h][c] = sum over token blocks (one thread per output), and
+// dA_log[c] = sum over token blocks and heads (one workgroup per channel:
+// strided partial sums, then a tree in LDS). Both in a fixed order.
+__global__ void prologue_reduce_bias_kernel(PrologueBwdArgs a, int nblk, int DK) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    const int n_bias = a.H * DK;
-    if (i < n_bias) {
-        const int h = i / DK, c = i % DK;
-        float acc = 0.f;
-        for (int b = 0; b < nblk; ++b) acc += a.part_b[((int64_t)b * a.H + h) * DK + c];
-        a.d_dt_bias[i] = acc;
-    } else if (i < n_bias + DK) {
-        const int c = i - n_bias;
-        float acc = 0.f;
-        for (int b = 0; b < nblk; ++b)
-            for (int h = 0; h < a.H; ++h) acc += a.part_A[((int64_t)b * a.H + h) * DK + c];
-        a.d_A_log[c] = acc;
+    if (i >= a.H * DK) return;
+    const int h = i / DK, c = i % DK;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int b = 0;
+    for (; b + 4 <= nblk; b += 4)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] += a.part_b[((int64_t)(b + u) * a.H + h) * DK + c];
+    for (; b < nblk; ++b) acc[0] += a.part_b[((int64_t)b * a.H + h) * DK + c];
+    a.d_dt_bias[i] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+__global__ __launch_bounds__(256) void prologue_reduce_alog_kernel(PrologueBwdArgs a, int nblk, int DK) {
+    __shared__ float red[256];
+    const int c = blockIdx.x;
+    const int64_t n = (int64_t)nblk * a.H;   // (token block, head) pairs
+    float acc = 0.f;
+    for (int64_t i = threadIdx.x; i < n; i += 256) acc += a.part_A[i * DK + c];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int m = 128; m >= 1; m >>= 1) {
+        if ((int)threadIdx.x < m) red[threadIdx.x] += red[threadIdx.x + m];
+        __syncthreads();
     }
+    if (threadIdx.x == 0) a.d_A_log[c] = red[0];
 }
 
 template <typename Tin>
 hipError_t launch_apply(const PrologueBwdArgs& a, dim3 grid, hipStream_t s, bool grad) {
-    const dim3 block(a.Dk > 64 ? a.Dk : 64);
+    const dim3 block(kPThreads);
     switch (a.Dk) {
         case 16:
             if (grad) prologue_grad_kernel<Tin, 16><<<grid, block, 0, s>>>(a);
@@ -187,13 +256,11 @@ hipError_t launch_prologue_bwd(const PrologueBwdArgs& p, const BwdArgs& core, hi
         const dim3 grid((unsigned)nblk, (unsigned)p.H);
         e = p.bf16 ? launch_apply<__bf16>(p, grid, s, true) : launch_apply<float>(p, grid, s, true);
         if (e != hipSuccess) return e;
-        const int n_out = p.H * p.Dk + p.Dk;
-        prologue_reduce_kernel<<<dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s>>>(p, (int)nblk, p.Dk);
-        return hipGetLastError();
     }
-    // no tokens: the reduction over zero token blocks writes zeros
-    const int n_out = p.H * p.Dk + p.Dk;
-    prologue_reduce_kernel<<<dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s>>>(p, 0, p.Dk);
+    // (with no tokens the reductions over zero token blocks write zeros)
+    prologue_reduce_bias_kernel<<<dim3((unsigned)((p.H * p.Dk + 255) / 256)), dim3(256), 0, s>>>(p, (int)nblk, p.Dk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    prologue_reduce_alog_kernel<<<dim3((unsigned)p.Dk), dim3(256), 0, s>>>(p, (int)nblk, p.Dk);
     return hipGetLastError();
 }
 
