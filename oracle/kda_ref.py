@@ -241,6 +241,50 @@ def short_conv(x, w, state=None, cu_seqlens=None, activation=False):
     return y, fin
 
 
+def short_conv_backward(x, w, dy, state=None, d_final=None, cu_seqlens=None, activation=False):
+    """Reverse-mode gradient of ``short_conv`` (float64) for the loss
+    sum <dy, y> + sum <d_final, final state>. Per sequence, with ext the
+    window [state; x] (ext[e + 3] = x[e], e >= -3) and p[t] = sum_i w[:, i]
+    ext[t + i] the pre-activation:
+
+        dp[t] = dy[t] * (s + p s (1 - s)), s = sigmoid(p[t])   (dy[t] without activation)
+        dext[e] = sum_i w[:, i] dp[e - i]  over 0 <= e - i < len    (the transposed taps)
+        dext[len + j] += d_final[j]  for the last three window entries (j = 0, 1, 2)
+        dw[:, i] = sum over tokens of dp[t] ext[t + i]
+
+    and dext splits into dx (e >= 3) and d_state (e < 3). x, dy [B, T, C];
+    w [C, 4]; state, d_final [N, 3, C] or None. Returns (dx [B, T, C],
+    dw [C, 4], d_state [N, 3, C]).
+    """
+    x, w, dy = (np.asarray(a, dtype=np.float64) for a in (x, w, dy))
+    B, T, C = x.shape
+    segs = _segments(B, T, cu_seqlens)
+    st0 = None if state is None else np.asarray(state, dtype=np.float64)
+    dfin = None if d_final is None else np.asarray(d_final, dtype=np.float64)
+    dx = np.zeros_like(x)
+    dw = np.zeros((C, 4))
+    dst = np.zeros((len(segs), 3, C))
+    for n, (b, bos, eos) in enumerate(segs):
+        L = eos - bos
+        ext = np.concatenate([st0[n] if st0 is not None else np.zeros((3, C)), x[b, bos:eos]], axis=0)
+        dext = np.zeros_like(ext)
+        for t in range(L):
+            p = (w * ext[t:t + 4].T).sum(-1)
+            if activation:
+                sg = 1.0 / (1.0 + np.exp(-p))
+                dp = dy[b, bos + t] * (sg + p * sg * (1.0 - sg))
+            else:
+                dp = dy[b, bos + t]
+            for i in range(4):
+                dext[t + i] += w[:, i] * dp
+                dw[:, i] += dp * ext[t + i]
+        if dfin is not None:
+            dext[L:L + 3] += dfin[n]
+        dx[b, bos:eos] = dext[3:]
+        dst[n] = dext[:3]
+    return dx, dw, dst
+
+
 def decode_step(q, k, v, g, beta, state_cache, state_slots=None, scale=1.0):
     """One decode step against a state cache. Returns (o [Nb,H,Dv], new cache copy).
 
