@@ -241,10 +241,32 @@ def bench_conv(steps, warmup):
         kda.chunk_fwd_prologue(ys[0], ys[1], ys[2], d["g_logit"], d["beta_logit"], d["A_log"], d["dt_bias"],
                                gate_lower_bound=synth.GATE_LOWER_BOUND, l2_eps=1e-6, out=o, final_state=fin)
 
+    # backward of the three convolutions: fp32 cotangents of y, gradients of x, the taps and the initial state
+    gen = torch.Generator(device="cpu").manual_seed(w.seed + 11)
+    dys = [torch.randn((w.B, w.T, C), generator=gen).to(dev) for _ in range(3)]
+    dxs = [torch.empty((w.B, w.T, C), dtype=torch.float32, device=dev) for _ in range(3)]
+    ws_b = torch.empty((kda.short_conv_bwd_workspace_bytes(w.B, w.T, C),), dtype=torch.uint8, device=dev)
+    grads = {}
+
+    def conv_bwd(i):
+        d = sets[i % 2]
+        for j, name in enumerate(("q_raw", "k_raw", "v")):
+            grads[j] = kda.short_conv_bwd(d[name], weights[j], dys[j], activation=True, workspace=ws_b,
+                                          out=dxs[j])
+
     _, _, conv_ms = time_launches(conv, steps, warmup, stream)
     wall, _, _ = time_launches(chain, steps, warmup, stream)
+    _, _, bwd_ms = time_launches(conv_bwd, steps, warmup, stream)
     if not (torch.isfinite(o.float()).all() and torch.isfinite(fin).all()):
         raise RuntimeError("non-finite conv chain output")
+    if not all(torch.isfinite(t).all() for g in grads.values() for t in g if t is not None):
+        raise RuntimeError("non-finite conv backward output")
+    # per projection: x (2 B) and dy (4 B) read, dx (4 B) written per token-channel, the taps and their
+    # gradient, the initial-state gradient; the per-block tap partials (16 B per channel per 64 tokens,
+    # written then read) are counted too
+    nblk = kda.short_conv_bwd_workspace_bytes(w.B, w.T, C) // (16 * C)
+    bwd_bytes = 3 * (w.B * w.T * C * 10 + 2 * C * 4 * 4 + w.B * 3 * C * 4 + 2 * nblk * C * 16)
+    bwd_gbs = bwd_bytes / (float(bwd_ms) * 1e-3) / 1e9
     # per projection: x read and y written at 2 B per token-channel, the weights and the final state
     nbytes = 3 * (2 * w.B * w.T * C * 2 + C * 4 * 4 + w.B * 3 * C * 4)
     gbs = nbytes / (float(conv_ms) * 1e-3) / 1e9
@@ -255,7 +277,12 @@ def bench_conv(steps, warmup):
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None},
             "algorithmic_bytes_per_step": nbytes,
             "chain": {"steps": "conv of q, k, v then the fused-prologue forward",
-                      "ms_per_step": wall / steps * 1e3, "tokens_per_s": w.T / (wall / steps)}}
+                      "ms_per_step": wall / steps * 1e3, "tokens_per_s": w.T / (wall / steps)},
+            "backward": {"steps": "kda_short_conv_bwd of q, k, v (fp32 dy; dx, dweight, d_state)",
+                         "ms_per_step": float(bwd_ms),
+                         "roofline": {"bound": "hbm", "achieved": bwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": bwd_gbs / HBM_PEAK_GBS, "traffic": None},
+                         "algorithmic_bytes_per_step": bwd_bytes}}
 
 
 def bench_decode(steps, warmup):
@@ -501,7 +528,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-split", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["split", "backward"], default=None,
+    ap.add_argument("--only", choices=["split", "backward", "conv"], default=None,
                     help="run one secondary leg alone and print its JSON object (for per-kernel profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -516,8 +543,10 @@ def main():
         copy_calibration()
         return
     if args.only:
-        leg = bench_split(args.steps, args.warmup) if args.only == "split" else \
-            bench_backward(args.steps, args.warmup, cpu=False)
+        legs = {"split": lambda: bench_split(args.steps, args.warmup),
+                "backward": lambda: bench_backward(args.steps, args.warmup, cpu=False),
+                "conv": lambda: bench_conv(args.steps, args.warmup)}
+        leg = legs[args.only]()
         print(json.dumps({"only": args.only, **leg}), flush=True)
         return
 

@@ -62,6 +62,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_recurrent_step.restype = ctypes.c_int
     lib.kda_short_conv.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, ctypes.c_int, P, P, P]
     lib.kda_short_conv.restype = ctypes.c_int
+    lib.kda_short_conv_bwd_workspace_bytes.argtypes = [I32, I32, I32]
+    lib.kda_short_conv_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_short_conv_bwd.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, ctypes.c_int, P, ctypes.c_size_t,
+                                       P, P, P, P]
+    lib.kda_short_conv_bwd.restype = ctypes.c_int
     lib.kda_short_conv_step.argtypes = [P, P, P, P, I32, I32, I32, I32, ctypes.c_int, P, P]
     lib.kda_short_conv_step.restype = ctypes.c_int
     lib.kda_chunk_fwd_split_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.c_int, I32]
@@ -366,6 +371,52 @@ def short_conv(x, weight, conv_state=None, cu_seqlens=None, activation=True, out
                             int(bool(activation)), _DTYPES[x.dtype], _ptr(out), _ptr(final_state), _stream(dev))
     _check(st)
     return out, final_state
+
+
+def short_conv_bwd_workspace_bytes(B, T, C):
+    """Device workspace bytes kda_short_conv_bwd needs (kda_short_conv_bwd_workspace_bytes)."""
+    return int(load_library().kda_short_conv_bwd_workspace_bytes(B, T, C))
+
+
+def short_conv_bwd(x, weight, dy, conv_state=None, d_final_state=None, cu_seqlens=None, activation=True,
+                   want_d_state=True, workspace=None, out=None):
+    """Gradients for ``short_conv`` (kda_short_conv_bwd): dy float32 [B,T,C]
+    (x may be [B,T,C] or [B,T,H,D]); returns float32 (dx [B,T,C],
+    dweight [C,4], d_state [N,3,C] or None). ``out`` may supply dx."""
+    lib = load_library()
+    if x.dim() == 4:
+        x = x.reshape(x.shape[0], x.shape[1], -1)
+    B, T, C = x.shape
+    dev = x.device
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    _need(x, "x", (B, T, C), x.dtype, dev)
+    _need(weight, "weight", (C, 4), torch.float32, dev)
+    dy = dy.reshape(B, T, C)
+    _need(dy, "dy", (B, T, C), torch.float32, dev)
+    if cu_seqlens is not None:
+        N = cu_seqlens.numel() - 1
+        _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    else:
+        N = B
+    if conv_state is not None:
+        _need(conv_state, "conv_state", (N, 3, C), torch.float32, dev)
+    if d_final_state is not None:
+        _need(d_final_state, "d_final_state", (N, 3, C), torch.float32, dev)
+    need = int(lib.kda_short_conv_bwd_workspace_bytes(B, T, C))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.float32, device=dev)
+    _need(out, "out", (B, T, C), torch.float32, dev)
+    dx = out
+    dw = torch.empty((C, 4), dtype=torch.float32, device=dev)
+    dst = torch.empty((N, 3, C), dtype=torch.float32, device=dev) if want_d_state else None
+    st = lib.kda_short_conv_bwd(_ptr(x), _ptr(weight), _ptr(conv_state), _ptr(cu_seqlens), _ptr(dy),
+                                _ptr(d_final_state), B, T, C, N, int(bool(activation)), _DTYPES[x.dtype],
+                                _ptr(workspace), workspace.numel(), _ptr(dx), _ptr(dw), _ptr(dst), _stream(dev))
+    _check(st)
+    return dx, dw, dst
 
 
 def short_conv_step(x, weight, conv_cache, cache_slots=None, activation=True, out=None):

@@ -357,6 +357,63 @@ kda_status kda_short_conv(const void* x, const float* weight, const float* conv_
     return KDA_OK;
 }
 
+size_t kda_short_conv_bwd_workspace_bytes(int32_t B, int32_t T, int32_t C) {
+    if (B < 1 || T < 0 || C < 1) return 0;
+    return (size_t)kda::short_conv_bwd_blocks(B, T) * (size_t)C * 4 * sizeof(float);
+}
+
+kda_status kda_short_conv_bwd(const void* x, const float* weight, const float* conv_state_in,
+                              const int32_t* cu_seqlens, const float* dy, const float* d_final_state, int32_t B,
+                              int32_t T, int32_t C, int32_t N, int32_t activation, kda_dtype dtype, void* workspace,
+                              size_t workspace_bytes, float* dx, float* dweight, float* d_state_in, void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_short_conv_bwd";
+    if (!weight || !dweight)
+        return fail(KDA_ERR_INVALID_ARG, "%s: weight and dweight must be non-NULL", fn);
+    if (T > 0 && (!x || !dy || !dx))
+        return fail(KDA_ERR_INVALID_ARG, "%s: x, dy and dx must be non-NULL when T > 0", fn);
+    if (B < 1 || T < 0 || C < 1 || N < 0)
+        return fail(KDA_ERR_INVALID_ARG, "%s: need B >= 1, T >= 0, C >= 1, N >= 0 (got B=%d T=%d C=%d N=%d)", fn,
+                    B, T, C, N);
+    if (C % 8 != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: C=%d; the channel count must be a multiple of 8", fn, C);
+    if (activation != 0 && activation != 1)
+        return fail(KDA_ERR_INVALID_ARG, "%s: activation must be 0 (none) or 1 (SiLU), got %d", fn, activation);
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dtype %d is not KDA_F32 or KDA_BF16", fn, (int)dtype);
+    if (cu_seqlens) {
+        if (B != 1)
+            return fail(KDA_ERR_INVALID_ARG, "%s: packed sequences (cu_seqlens) need B == 1, got B=%d", fn, B);
+        if (N < 1)
+            return fail(KDA_ERR_INVALID_ARG, "%s: packed sequences need N >= 1, got N=%d", fn, N);
+    } else if (N != B) {
+        return fail(KDA_ERR_INVALID_ARG, "%s: without cu_seqlens N must equal B (N=%d, B=%d)", fn, N, B);
+    }
+    if ((int64_t)B * T > ((int64_t)1 << 31) * 16 || (int64_t)C > ((int64_t)1 << 22))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", fn);
+    const size_t need = kda_short_conv_bwd_workspace_bytes(B, T, C);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KDA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, got %zu%s", fn, need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    {
+        const void* ins[] = {x, weight, conv_state_in, dy, d_final_state, workspace};
+        const void* outs[] = {dx, dweight, d_state_in};
+        for (const void* o : outs)
+            for (const void* i : ins)
+                if (o && o == i) return fail(KDA_ERR_INVALID_ARG, "%s: gradients must not alias an input", fn);
+    }
+    kda::ConvBwdArgs a;
+    a.fwd.x = x; a.fwd.w = weight; a.fwd.state_in = conv_state_in; a.fwd.cu = cu_seqlens; a.fwd.y = nullptr;
+    a.fwd.state_out = nullptr; a.fwd.B = B; a.fwd.T = T; a.fwd.C = C; a.fwd.N = N; a.fwd.act = activation == 1;
+    a.fwd.bf16 = dtype == KDA_BF16;
+    a.dy = dy; a.d_final = d_final_state; a.dx = dx; a.dw = dweight; a.d_state = d_state_in;
+    a.part = static_cast<float*>(workspace);
+    a.B = B; a.T = T; a.C = C; a.N = N;
+    const hipError_t e = kda::launch_short_conv_bwd(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
+}
+
 kda_status kda_short_conv_step(const void* x, const float* weight, float* conv_cache, const int32_t* cache_slots,
                                int32_t n_slots, int32_t Nb, int32_t C, int32_t activation, kda_dtype dtype,
                                void* y, void* stream) {

@@ -138,6 +138,21 @@ struct SplitLayout {
 SplitLayout split_layout(const ChunkArgs& a, int32_t P);
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace, hipStream_t s);
 
+// Backward of the short convolution: fwd holds the forward's arguments (x, w,
+// state_in, cu, sizes, activation, dtype); gradients are float32.
+struct ConvBwdArgs {
+    ConvArgs fwd;
+    const float* dy;           // [B,T,C]
+    const float* d_final;      // [N][3][C] or nullptr
+    float* dx;                 // [B,T,C]
+    float* dw;                 // [C][4]
+    float* d_state;            // [N][3][C] or nullptr
+    float* part;               // [token blocks][C][4] workspace
+    int32_t B, T, C, N;
+};
+int64_t short_conv_bwd_blocks(int32_t B, int32_t T);
+hipError_t launch_short_conv_bwd(const ConvBwdArgs& a, hipStream_t s);
+
 hipError_t launch_short_conv(const ConvArgs& a, hipStream_t s);
 hipError_t launch_short_conv_step(const ConvStepArgs& a, hipStream_t s);
 

@@ -292,6 +292,40 @@ kda_status kda_short_conv(const void* x, const float* weight, const float* conv_
                           const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t C, int32_t N,
                           int32_t activation, kda_dtype dtype, void* y, float* conv_state_out, void* stream);
 
+/* Bytes of device workspace kda_short_conv_bwd needs: ceil(B*T/256) x C x 4 floats. */
+size_t kda_short_conv_bwd_workspace_bytes(int32_t B, int32_t T, int32_t C);
+
+/*
+ * Backward of kda_short_conv: the gradients of
+ *   L = sum <dy, y> + sum_n <d_final_state[n], conv_state_out[n]>
+ * with respect to x, weight and conv_state_in. With p[t] the pre-activation
+ * and dp[t] = dy[t] act'(p[t]) (act' = 1 without activation; for SiLU,
+ * s + p s (1 - s) with s = sigmoid(p)), per sequence and channel c:
+ *   dx[t][c]      = sum_i weight[c][i] dp[t + 3 - i][c]   (terms inside the sequence)
+ *                   + d_final_state for the window's last three inputs
+ *   dweight[c][i] = sum over all tokens t of dp[t][c] x[t - 3 + i][c]
+ *   d_state_in[n][j][c] = sum_{i <= j} weight[c][i] dp[bos + j - i][c]
+ *                   (+ d_final_state where a short sequence's final window
+ *                   still holds state entries)
+ * This is the convolution that sits before the prologue (the reading of the
+ * pages documented with kda_short_conv), so it chains after
+ * kda_chunk_bwd_prologue: its dq_raw, dk_raw and dv are dy for the three
+ * projections.
+ *
+ *   x, weight, conv_state_in, cu_seqlens, B, T, C, N, activation, dtype
+ *              exactly as passed to kda_short_conv
+ *   dy         [B,T,C] float32;  d_final_state [N][3][C] float32 or NULL
+ *   workspace  at least kda_short_conv_bwd_workspace_bytes(B, T, C) bytes
+ *   dx [B,T,C], dweight [C][4] float32 outputs; d_state_in [N][3][C] float32
+ *              or NULL (not written); none may alias an input
+ * dweight is summed over token blocks in a fixed order, so the call is
+ * deterministic. Errors as for kda_short_conv.
+ */
+kda_status kda_short_conv_bwd(const void* x, const float* weight, const float* conv_state_in,
+                              const int32_t* cu_seqlens, const float* dy, const float* d_final_state, int32_t B,
+                              int32_t T, int32_t C, int32_t N, int32_t activation, kda_dtype dtype, void* workspace,
+                              size_t workspace_bytes, float* dx, float* dweight, float* d_state_in, void* stream);
+
 /*
  * One decode step of the short convolution: row r (one token) reads the three
  * previous inputs from conv_cache[slot(r)] ([3][C] float32), writes

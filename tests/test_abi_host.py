@@ -25,6 +25,7 @@ def test_exports_every_declared_symbol(lib):
                           "kda_short_conv_step", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
                           "kda_chunk_fwd_split", "kda_chunk_fwd_split_workspace_bytes",
                           "kda_chunk_bwd_prologue", "kda_chunk_bwd_prologue_workspace_bytes",
+                          "kda_short_conv_bwd", "kda_short_conv_bwd_workspace_bytes",
                           "kda_status_string", "kda_last_error_message"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -324,3 +325,36 @@ def test_chunk_bwd_prologue_workspace_bytes(lib):
     rows = 4096 * 96
     assert total >= core + rows * (3 * 128 + 1 + 2 * 128) * 4 + 2 * 64 * 96 * 128 * 4
     assert kda.chunk_bwd_prologue_workspace_bytes(1, 0, 96, 128, 128, 1, False) == 0
+
+
+def _conv_bwd(lib, **kw):
+    a = dict(x=FAKE, w=ctypes.c_void_p(0x9000), s0=None, cu=None, dy=ctypes.c_void_p(0xA000), dfin=None, B=1, T=64,
+             C=256, N=1, act=1, dtype=kda.KDA_BF16, ws=ctypes.c_void_p(0x3000), wsb=1 << 30,
+             dx=ctypes.c_void_p(0x4000), dw=ctypes.c_void_p(0x5000), dst=None, stream=None)
+    a.update(kw)
+    return lib.kda_short_conv_bwd(a["x"], a["w"], a["s0"], a["cu"], a["dy"], a["dfin"], a["B"], a["T"], a["C"],
+                                  a["N"], a["act"], a["dtype"], a["ws"], a["wsb"], a["dx"], a["dw"], a["dst"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(w=None), kda.KDA_ERR_INVALID_ARG, "weight"),
+    (dict(dy=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(C=12), kda.KDA_ERR_UNSUPPORTED, "multiple of 8"),
+    (dict(act=2), kda.KDA_ERR_INVALID_ARG, "activation"),
+    (dict(N=2), kda.KDA_ERR_INVALID_ARG, "N must equal B"),
+    (dict(wsb=10), kda.KDA_ERR_INVALID_ARG, "workspace"),
+    (dict(dx=FAKE), kda.KDA_ERR_INVALID_ARG, "alias"),
+])
+def test_short_conv_bwd_rejects_before_launch(lib, kw, status, needle):
+    st = _conv_bwd(lib, **kw)
+    assert st == status
+    assert needle in lib.kda_last_error_message().decode()
+
+
+def test_short_conv_bwd_workspace_bytes(lib):
+    # one partial of C x 4 floats per 256 tokens
+    assert lib.kda_short_conv_bwd_workspace_bytes(1, 4096, 12288) == 16 * 12288 * 4 * 4
+    assert lib.kda_short_conv_bwd_workspace_bytes(2, 65, 8) == 1 * 8 * 4 * 4
+    assert lib.kda_short_conv_bwd_workspace_bytes(1, 257, 8) == 2 * 8 * 4 * 4
+    assert lib.kda_short_conv_bwd_workspace_bytes(1, 0, 8) == 0
