@@ -7,17 +7,16 @@
 // state ([N][3][C]: x[-3], x[-2], x[-1]) or are zero; with the activation,
 // y <- y * sigmoid(y). The final state is the window's last three inputs.
 //
-// The kernels are bandwidth-bound: a thread owns 8 consecutive channels (16
-// bytes of bf16) of kRows consecutive tokens and keeps the three previous
-// inputs in registers, so a wave reads and writes 1 KiB contiguous per token
-// and every input is read once (plus a three-token halo per kRows).
+// The kernels are bandwidth-bound: a lane owns a few consecutive channels, a
+// wave walks a run of consecutive tokens keeping the three previous inputs in
+// registers, so every wave access is contiguous across lanes and every input
+// is read once (plus a three-token halo per run).
 #include "device_common.hpp"
 #include "launchers.hpp"
 
 namespace kda {
 namespace {
 
-constexpr int kRows = 8;         // tokens per thread
 constexpr int kThreadsConv = 256;
 
 template <typename T> struct Vec8;
@@ -85,72 +84,134 @@ __device__ __forceinline__ void window_input(const ConvArgs& a, const T* x, int 
     }
 }
 
+// Prefill: a lane owns kFwdCh channels; a wave walks kFwdWaveRows
+// consecutive tokens once, carrying the last three inputs of the window, and
+// goes in groups of up to kFwdGroup tokens with every load of the group
+// issued before any is used. The wave's token range and the sequence bounds
+// are uniform across the wave. The four waves of a workgroup take
+// consecutive token ranges of the same channels.
+// Tiling measured at T=4096, C=12288, bf16: every tiling from 4 or 8
+// channels per lane and 32 or 64 tokens per wave lands within 3% of a
+// device copy's rate for the same bytes; 2-token groups or 128-token runs
+// are slower.
+constexpr int kFwdCh = 4;
+constexpr int kFwdWaveRows = 64;
+constexpr int kFwdBlockRows = 4 * kFwdWaveRows;
+constexpr int kFwdBlockCh = 64 * kFwdCh;
+constexpr int kFwdGroup = 8;
+
+template <typename T, int N> struct LoadN;
+template <typename T> struct LoadN<T, 8> {
+    static __device__ __forceinline__ void load(const T* p, float (&f)[8]) { Vec8<T>::load(p, f); }
+    static __device__ __forceinline__ void store(T* p, const float (&f)[8]) { Vec8<T>::store(p, f); }
+};
+template <> struct LoadN<float, 4> {
+    static __device__ __forceinline__ void load(const float* p, float (&f)[4]) {
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    }
+    static __device__ __forceinline__ void store(float* p, const float (&f)[4]) {
+        *reinterpret_cast<float4*>(p) = float4{f[0], f[1], f[2], f[3]};
+    }
+};
+template <> struct LoadN<__bf16, 4> {
+    static __device__ __forceinline__ void load(const __bf16* p, float (&f)[4]) {
+        const uint2 u = *reinterpret_cast<const uint2*>(p);
+        f[0] = __uint_as_float(u.x << 16); f[1] = __uint_as_float(u.x & 0xffff0000u);
+        f[2] = __uint_as_float(u.y << 16); f[3] = __uint_as_float(u.y & 0xffff0000u);
+    }
+    static __device__ __forceinline__ void store(__bf16* p, const float (&f)[4]) {
+        uint2 u;
+        u.x = pack2_bf16(f[0], f[1]);
+        u.y = pack2_bf16(f[2], f[3]);
+        *reinterpret_cast<uint2*>(p) = u;
+    }
+};
+
+// input x[tau] of sequence n (tau relative to its start, tau >= -3), N channels
+template <typename T, int N>
+__device__ __forceinline__ void window_input_n(const ConvArgs& a, const T* x, int n, int64_t bos, int64_t tau,
+                                               int64_t c0, float (&f)[N]) {
+    if (tau >= 0) {
+        LoadN<T, N>::load(x + (bos + tau) * a.C + c0, f);
+    } else if (a.state_in) {
+        LoadN<float, N>::load(a.state_in + ((int64_t)n * 3 + (3 + tau)) * a.C + c0, f);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) f[i] = 0.f;
+    }
+}
+
+template <typename T, bool kAct, int G>
+__device__ __forceinline__ void conv_fwd_group(const ConvArgs& a, const T* x, T* y, int64_t c0, int64_t u,
+                                               const float (&w)[kFwdCh][4], float (&h0)[kFwdCh],
+                                               float (&h1)[kFwdCh], float (&h2)[kFwdCh]) {
+    float xu[G][kFwdCh];
+#pragma unroll
+    for (int j = 0; j < G; ++j) LoadN<T, kFwdCh>::load(x + (u + j) * a.C + c0, xu[j]);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        float out[kFwdCh];
+#pragma unroll
+        for (int i = 0; i < kFwdCh; ++i) {
+            out[i] = activate<kAct>(fmaf(w[i][3], xu[j][i], fmaf(w[i][2], h2[i], fmaf(w[i][1], h1[i], w[i][0] * h0[i]))));
+            h0[i] = h1[i];
+            h1[i] = h2[i];
+            h2[i] = xu[j][i];
+        }
+        LoadN<T, kFwdCh>::store(y + (u + j) * a.C + c0, out);
+    }
+}
+
 template <typename T, bool kAct>
-__global__ __launch_bounds__(kThreadsConv) void short_conv_kernel(ConvArgs a) {
-    const int64_t c0 = ((int64_t)blockIdx.y * kThreadsConv + threadIdx.x) * 8;
-    if (c0 >= a.C) return;
+__global__ __launch_bounds__(256) void short_conv_kernel(ConvArgs a) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.y * kFwdBlockCh + (int64_t)lane * kFwdCh;
     const int64_t BT = (int64_t)a.B * a.T;
-    const int64_t t0 = (int64_t)blockIdx.x * kRows;
-    if (t0 >= BT) return;
+    const int64_t tb = (int64_t)blockIdx.x * kFwdBlockRows + (int64_t)wv * kFwdWaveRows;
+    if (c0 >= a.C || tb >= BT) return;
+    const int64_t te = tb + kFwdWaveRows < BT ? tb + kFwdWaveRows : BT;
     const T* x = static_cast<const T*>(a.x);
     T* y = static_cast<T*>(a.y);
-    float w[8][4];
+    float w[kFwdCh][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kFwdCh; ++i) {
         const float4 wi = reinterpret_cast<const float4*>(a.w)[c0 + i];
         w[i][0] = wi.x; w[i][1] = wi.y; w[i][2] = wi.z; w[i][3] = wi.w;
     }
     int n;
     int64_t bos, eos;
-    find_sequence(a, t0, n, bos, eos);
-    if constexpr (sizeof(T) == 2) {
-        if (t0 - bos >= 3 && t0 + kRows <= eos) {
-            // the common case: the whole block and its halo inside one sequence.
-            // All kRows + 3 rows are loaded before any is used, so the loads overlap.
-            uint4 raw[kRows + 3];
-#pragma unroll
-            for (int r = 0; r < kRows + 3; ++r)
-                raw[r] = *reinterpret_cast<const uint4*>(x + (t0 - 3 + r) * a.C + c0);
-#pragma unroll
-            for (int r = 0; r < kRows; ++r) {
-                float f0[8], f1[8], f2[8], f3[8], out[8];
-                unpack8(raw[r], f0);
-                unpack8(raw[r + 1], f1);
-                unpack8(raw[r + 2], f2);
-                unpack8(raw[r + 3], f3);
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    out[i] = activate<kAct>(fmaf(w[i][3], f3[i], fmaf(w[i][2], f2[i], fmaf(w[i][1], f1[i], w[i][0] * f0[i]))));
-                Vec8<T>::store(y + (t0 + r) * a.C + c0, out);
-            }
-            return;
-        }
-    }
-    float h0[8], h1[8], h2[8];      // x[t-3], x[t-2], x[t-1]
-    window_input<T>(a, x, n, bos, t0 - bos - 3, c0, h0);
-    window_input<T>(a, x, n, bos, t0 - bos - 2, c0, h1);
-    window_input<T>(a, x, n, bos, t0 - bos - 1, c0, h2);
-    const int rows = (int)((BT - t0) < kRows ? (BT - t0) : kRows);
-    for (int r = 0; r < rows; ++r) {
-        const int64_t t = t0 + r;
-        if (t == eos) {
+    find_sequence(a, tb, n, bos, eos);
+    float h0[kFwdCh], h1[kFwdCh], h2[kFwdCh];      // x[u-3], x[u-2], x[u-1]
+    window_input_n<T, kFwdCh>(a, x, n, bos, tb - bos - 3, c0, h0);
+    window_input_n<T, kFwdCh>(a, x, n, bos, tb - bos - 2, c0, h1);
+    window_input_n<T, kFwdCh>(a, x, n, bos, tb - bos - 1, c0, h2);
+    int64_t u = tb;
+    while (u < te) {
+        if (u == eos) {
             // the next non-empty sequence starts here: its window starts from its state
-            find_sequence(a, t, n, bos, eos);
-            window_input<T>(a, x, n, bos, -3, c0, h0);
-            window_input<T>(a, x, n, bos, -2, c0, h1);
-            window_input<T>(a, x, n, bos, -1, c0, h2);
+            find_sequence(a, u, n, bos, eos);
+            window_input_n<T, kFwdCh>(a, x, n, bos, -3, c0, h0);
+            window_input_n<T, kFwdCh>(a, x, n, bos, -2, c0, h1);
+            window_input_n<T, kFwdCh>(a, x, n, bos, -1, c0, h2);
         }
-        float xt[8], out[8];
-        Vec8<T>::load(x + t * a.C + c0, xt);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float acc = fmaf(w[i][3], xt[i], fmaf(w[i][2], h2[i], fmaf(w[i][1], h1[i], w[i][0] * h0[i])));
-            out[i] = activate<kAct>(acc);
-            h0[i] = h1[i];
-            h1[i] = h2[i];
-            h2[i] = xt[i];
+        const int64_t rem = (eos < te ? eos : te) - u;
+        if (rem >= kFwdGroup) {
+            conv_fwd_group<T, kAct, kFwdGroup>(a, x, y, c0, u, w, h0, h1, h2);
+            u += kFwdGroup;
+        } else if (rem >= 4) {
+            conv_fwd_group<T, kAct, 4>(a, x, y, c0, u, w, h0, h1, h2);
+            u += 4;
+        } else if (rem == 3) {
+            conv_fwd_group<T, kAct, 3>(a, x, y, c0, u, w, h0, h1, h2);
+            u += 3;
+        } else if (rem == 2) {
+            conv_fwd_group<T, kAct, 2>(a, x, y, c0, u, w, h0, h1, h2);
+            u += 2;
+        } else {
+            conv_fwd_group<T, kAct, 1>(a, x, y, c0, u, w, h0, h1, h2);
+            u += 1;
         }
-        Vec8<T>::store(y + t * a.C + c0, out);
     }
 }
 
@@ -563,11 +624,12 @@ hipError_t launch_conv_t(const ConvArgs& a, hipStream_t s) {
     const int64_t BT = (int64_t)a.B * a.T;
     const unsigned cgroups = (unsigned)((a.C / 8 + kThreadsConv - 1) / kThreadsConv);
     if (BT > 0) {
-        const dim3 grid((unsigned)((BT + kRows - 1) / kRows), cgroups);
+        const dim3 grid((unsigned)((BT + kFwdBlockRows - 1) / kFwdBlockRows),
+                        (unsigned)((a.C + kFwdBlockCh - 1) / kFwdBlockCh));
         if (a.act)
-            hipLaunchKernelGGL((short_conv_kernel<T, true>), grid, dim3(kThreadsConv), 0, s, a);
+            hipLaunchKernelGGL((short_conv_kernel<T, true>), grid, dim3(256), 0, s, a);
         else
-            hipLaunchKernelGGL((short_conv_kernel<T, false>), grid, dim3(kThreadsConv), 0, s, a);
+            hipLaunchKernelGGL((short_conv_kernel<T, false>), grid, dim3(256), 0, s, a);
     }
     if (a.state_out && a.N > 0)
         hipLaunchKernelGGL((short_conv_state_kernel<T>), dim3((unsigned)a.N, cgroups), dim3(kThreadsConv), 0, s, a);
