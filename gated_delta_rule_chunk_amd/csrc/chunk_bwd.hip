@@ -888,18 +888,30 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
         for (int i = 0; i < 4; ++i)
             st[t][i] = a.s0 ? a.s0[sbase + (int64_t)(cw + 4 * lg + i) * Dv + c0 + 16 * t + l16] : 0.f;
     auto rows_of = [&](int64_t ch) { return (int)min<int64_t>(C, sq.len - ch * C); };
-    for (int64_t ch = 0; ch < nch; ++ch) {
-        fetch_chunk<Tin>(f, a, sq, h, sq.bos + ch * C, rows_of(ch), c0, false, nullptr, mats_of(ch));
-        float* ws = state_of(ch);
+    // Chunk ch + 1's inputs are fetched while chunk ch is computed, into the
+    // other of two register sets (the loop is unrolled by two, so no set is
+    // copied and every fetch is issued unconditionally). Past the last chunk
+    // the fetch re-reads the last chunk with no rows, and an odd count runs
+    // one extra such chunk: all-zero rows leave the state unchanged exactly,
+    // and its entry state is not stored.
+    auto fetch_fwd = [&](Fetch<Tin>& dst, int64_t ch) {
+        const int64_t cc = ch < nch ? ch : nch - 1;
+        fetch_chunk<Tin>(dst, a, sq, h, sq.bos + cc * C, ch < nch ? rows_of(ch) : 0, c0, false, nullptr,
+                         mats_of(cc));
+    };
+    auto fwd_chunk = [&](int64_t ch, Fetch<Tin>& cur, Fetch<Tin>& nxt) {
+        float* ws = state_of(ch < nch ? ch : nch - 1);
+        const bool real = ch < nch;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int c = cw + 4 * lg + i, j = 16 * t + l16;
-                ws[(int64_t)c * Dv + j] = st[t][i];
+                if (real) ws[(int64_t)c * Dv + j] = st[t][i];
                 sm.S[c][j] = st[t][i];
             }
-        commit_chunk<Tin>(sm, f, false);
+        commit_chunk<Tin>(sm, cur, false);
+        fetch_fwd(nxt, ch + 1);
         __syncthreads();
         chunk_scale(sm, false);
         __syncthreads();
@@ -947,6 +959,14 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
             }
         }
         __syncthreads();
+    };
+    if (nch > 0) {
+        Fetch<Tin> fb;
+        fetch_fwd(f, 0);
+        for (int64_t ch = 0; ch < nch; ch += 2) {
+            fwd_chunk(ch, f, fb);
+            fwd_chunk(ch + 1, fb, f);
+        }
     }
 
     // ---------------- backward sweep ----------------
