@@ -406,6 +406,8 @@ def short_conv_bwd(x, weight, dy, conv_state=None, d_final_state=None, cu_seqlen
     need = int(lib.kda_short_conv_bwd_workspace_bytes(B, T, C))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
     if out is None:
         out = torch.empty((B, T, C), dtype=torch.float32, device=dev)
     _need(out, "out", (B, T, C), torch.float32, dev)
