@@ -527,8 +527,8 @@ namespace mf {
 
 constexpr int C = 16, DK = 128, BV = 64, NT = 512;
 constexpr int SP = BV + 4;   // row stride of the [DK][SP] state tiles
-constexpr int KP = DK + 4;   // row stride of [C][KP] per-channel rows
-constexpr int VP = BV + 4;   // row stride of [C][VP] per-column rows
+constexpr int KP = DK + 2;   // row stride of [C][KP] per-channel rows (= 2 mod 32: operand reads by row hit distinct banks)
+constexpr int VP = BV + 2;   // row stride of [C][VP] per-column rows (likewise)
 constexpr int CP = C + 1;
 constexpr int kRef = 7;      // reference row of the factored pair exponentials
 constexpr int kMats = 3 * C * C;   // T, P, KK of one chunk
