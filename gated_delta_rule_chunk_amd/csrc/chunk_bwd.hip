@@ -579,17 +579,18 @@ template <> struct Raw4<__bf16> {
 // One chunk's global inputs held in registers between issue and commit, so
 // that every load of a chunk is in flight at once. Rows past the sequence's
 // end load row 0 (always in range) and are zeroed at commit.
-template <typename Tin>
+template <typename Tin, typename Tx>
 struct Fetch {
-    Raw4<Tin> q, k, g, x;   // x: v for threads < 256, dO for the others
+    Raw4<Tin> q, k, g;
+    Raw4<Tx> x;             // x: v for threads < 256, dO for the others
     float beta;
     float4 s[4];            // entry state slice (reverse sweep)
     float m[3];             // T, P, KK entries (threads < 256)
     bool in_qk, in_x, in_b;
 };
 
-template <typename Tin>
-__device__ __forceinline__ void fetch_chunk(Fetch<Tin>& f, const BwdArgs& a, const SeqInfo& sq, int h, int64_t t0,
+template <typename Tin, typename Tx>
+__device__ __forceinline__ void fetch_chunk(Fetch<Tin, Tx>& f, const BwdArgs& a, const SeqInfo& sq, int h, int64_t t0,
                                             int rows, int c0, bool reverse, const float* ws, const float* mats) {
     const int tid = threadIdx.x;
     {
@@ -606,9 +607,9 @@ __device__ __forceinline__ void fetch_chunk(Fetch<Tin>& f, const BwdArgs& a, con
         f.in_x = r < rows;
         const int64_t e = ((sq.b * a.T + t0 + (f.in_x ? r : 0)) * a.H + h) * (int64_t)a.Dv + c0 + j;
         if (tid < 256)
-            f.x.load(static_cast<const Tin*>(a.v), e);
+            f.x.load(static_cast<const Tx*>(a.v), e);
         else if (reverse)
-            f.x.load(static_cast<const Tin*>(a.d_o), e);
+            f.x.load(static_cast<const Tx*>(a.d_o), e);
     }
     {
         const int r = tid & (C - 1);
@@ -631,8 +632,8 @@ __device__ __forceinline__ void fetch_chunk(Fetch<Tin>& f, const BwdArgs& a, con
     }
 }
 
-template <typename Tin>
-__device__ __forceinline__ void commit_chunk(Smem& sm, const Fetch<Tin>& f, bool reverse) {
+template <typename Tin, typename Tx>
+__device__ __forceinline__ void commit_chunk(Smem& sm, const Fetch<Tin, Tx>& f, bool reverse) {
     const int tid = threadIdx.x;
     {
         const int r = tid >> 5, c = (tid & 31) * 4;
@@ -860,7 +861,10 @@ __global__ __launch_bounds__(256) void chunk_mats_kernel(BwdArgs a) {
     }
 }
 
-template <typename Tin>
+// Tin: q, k, g and beta; Tx: v and dO (bf16 v and dO with float32 q, k, g
+// and beta come from the backward through the prologue, which widens only
+// what it computes).
+template <typename Tin, typename Tx>
 __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
@@ -878,7 +882,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
     const float* mats0 = a.ws + chunk_bwd_slots(a.B, a.T, a.N, a.cu != nullptr) * slot_stride;
     auto mats_of = [&](int64_t ch) { return mats0 + ((sq.slot0 + ch) * H + h) * kMats; };
     auto state_of = [&](int64_t ch) { return a.ws + (sq.slot0 + ch) * slot_stride + (int64_t)h * DK * Dv + c0; };
-    Fetch<Tin> f;
+    Fetch<Tin, Tx> f;
 
     // ---------------- forward sweep: chunk entry states ----------------
     f32x4 st[4];
@@ -894,12 +898,12 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
     // the fetch re-reads the last chunk with no rows, and an odd count runs
     // one extra such chunk: all-zero rows leave the state unchanged exactly,
     // and its entry state is not stored.
-    auto fetch_fwd = [&](Fetch<Tin>& dst, int64_t ch) {
+    auto fetch_fwd = [&](Fetch<Tin, Tx>& dst, int64_t ch) {
         const int64_t cc = ch < nch ? ch : nch - 1;
-        fetch_chunk<Tin>(dst, a, sq, h, sq.bos + cc * C, ch < nch ? rows_of(ch) : 0, c0, false, nullptr,
+        fetch_chunk<Tin, Tx>(dst, a, sq, h, sq.bos + cc * C, ch < nch ? rows_of(ch) : 0, c0, false, nullptr,
                          mats_of(cc));
     };
-    auto fwd_chunk = [&](int64_t ch, Fetch<Tin>& cur, Fetch<Tin>& nxt) {
+    auto fwd_chunk = [&](int64_t ch, Fetch<Tin, Tx>& cur, Fetch<Tin, Tx>& nxt) {
         float* ws = state_of(ch < nch ? ch : nch - 1);
         const bool real = ch < nch;
 #pragma unroll
@@ -910,7 +914,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
                 if (real) ws[(int64_t)c * Dv + j] = st[t][i];
                 sm.S[c][j] = st[t][i];
             }
-        commit_chunk<Tin>(sm, cur, false);
+        commit_chunk<Tin, Tx>(sm, cur, false);
         fetch_fwd(nxt, ch + 1);
         __syncthreads();
         chunk_scale(sm, false);
@@ -961,7 +965,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
         __syncthreads();
     };
     if (nch > 0) {
-        Fetch<Tin> fb;
+        Fetch<Tin, Tx> fb;
         fetch_fwd(f, 0);
         for (int64_t ch = 0; ch < nch; ch += 2) {
             fwd_chunk(ch, f, fb);
@@ -979,12 +983,12 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
     for (int64_t ch = nch - 1; ch >= 0; --ch) {
         const int64_t t0 = sq.bos + ch * C;
         const int rows = rows_of(ch);
-        fetch_chunk<Tin>(f, a, sq, h, t0, rows, c0, true, state_of(ch), mats_of(ch));
+        fetch_chunk<Tin, Tx>(f, a, sq, h, t0, rows, c0, true, state_of(ch), mats_of(ch));
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) sm.dS[cw + 4 * lg + i][16 * t + l16] = ds[t][i];
-        commit_chunk<Tin>(sm, f, true);
+        commit_chunk<Tin, Tx>(sm, f, true);
         __syncthreads();
         chunk_scale(sm, true);
         __syncthreads();
@@ -1194,11 +1198,14 @@ hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s) {
             if (e != hipSuccess) return e;
         }
         if (a.bf16)
-            mf::chunk_bwd_mfma_kernel<__bf16><<<dim3((unsigned)grid), dim3(mf::NT), 0, s>>>(a);
+            mf::chunk_bwd_mfma_kernel<__bf16, __bf16><<<dim3((unsigned)grid), dim3(mf::NT), 0, s>>>(a);
+        else if (a.x_bf16)
+            mf::chunk_bwd_mfma_kernel<float, __bf16><<<dim3((unsigned)grid), dim3(mf::NT), 0, s>>>(a);
         else
-            mf::chunk_bwd_mfma_kernel<float><<<dim3((unsigned)grid), dim3(mf::NT), 0, s>>>(a);
+            mf::chunk_bwd_mfma_kernel<float, float><<<dim3((unsigned)grid), dim3(mf::NT), 0, s>>>(a);
         return hipGetLastError();
     }
+    if (a.x_bf16) return hipErrorInvalidValue;   // mixed input types: matrix-core path only
     return a.bf16 ? launch_dtype<__bf16>(a, s) : launch_dtype<float>(a, s);
 }
 

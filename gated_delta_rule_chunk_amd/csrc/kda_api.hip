@@ -314,6 +314,15 @@ kda_status kda_chunk_bwd_prologue(const void* q_raw, const void* k_raw, const vo
     a.dq = dq_raw; a.dk = dk_raw; a.dv = dv; a.dg = dg_logit; a.dbeta = dbeta_logit; a.d_s0 = d_initial_state;
     a.B = B; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.N = N; a.scale = scale; a.bf16 = false;
     a.g_ge_m5 = gate_lower_bound >= -5.f;   // g lies in (gate_lower_bound, 0)
+    // v and dO are read as given by the matrix-core backward (bf16 widens exactly) and by
+    // either backward when already float32; only bf16 ones bound for the vector-ALU backward
+    // are widened into the workspace.
+    p.widen_x = dtype == KDA_BF16 && !kda::chunk_bwd_mfma_supported(a);
+    if (!p.widen_x) {
+        a.v = v;
+        a.d_o = d_o;
+        a.x_bf16 = dtype == KDA_BF16;
+    }
     if ((int64_t)N * H == 0) return KDA_OK;
     const hipError_t e = kda::launch_prologue_bwd(p, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));

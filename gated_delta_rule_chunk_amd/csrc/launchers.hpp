@@ -88,6 +88,7 @@ struct BwdArgs {
     float scale;
     bool bf16;
     bool g_ge_m5 = true;       // g >= -5 holds (the matrix-core kernel relies on it)
+    bool x_bf16 = false;       // with bf16 false: v and d_o are bf16 (matrix-core path only)
 };
 
 // The backward's workspace: a float32 chunk-entry state [H][Dk][Dv] per
@@ -116,6 +117,7 @@ struct PrologueBwdArgs {
     const float* dt_bias;      // [H*Dk]
     float gate_lb, l2_eps;
     float *qf, *kf, *gf, *bf, *vf, *dof;   // prologue outputs, float32 (workspace)
+    bool widen_x;                          // write v and dO widened to vf, dof
     float *dq, *dk, *dg, *dbeta;           // gradient buffers, transformed in place
     float *part_b, *part_A;                // per (token block, head, channel) partial sums (workspace)
     float *d_A_log, *d_dt_bias;

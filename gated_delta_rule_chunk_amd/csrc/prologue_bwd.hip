@@ -93,10 +93,10 @@ __global__ __launch_bounds__(kPThreads) void prologue_apply_kernel(PrologueBwdAr
         store8(a.gf, e, g);
         if (part == 0) a.bf[row] = sigmoid(load_elem(static_cast<const Tin*>(a.beta_logit), row));
     }
-    // v and dO widened to float32: Dv/8 lanes per row
+    // v and dO widened to float32 (for the vector-ALU backward): Dv/8 lanes per row
     const int LV = a.Dv / 8, RV = kPThreads / LV;
     const int pv = tid % LV, rv = tid / LV;
-    if (rv < RV) {
+    if (a.widen_x && rv < RV) {
         for (int64_t t = t0 + rv; t < t_end; t += RV) {
             const int64_t e = (t * a.H + h) * a.Dv + 8 * pv;
             float x[8];
