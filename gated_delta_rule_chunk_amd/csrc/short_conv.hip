@@ -70,19 +70,6 @@ __device__ __forceinline__ void find_sequence(const ConvArgs& a, int64_t t, int&
     }
 }
 
-// input x[tau] of sequence n, tau relative to the sequence start (tau >= -3)
-template <typename T>
-__device__ __forceinline__ void window_input(const ConvArgs& a, const T* x, int n, int64_t bos, int64_t tau,
-                                             int64_t c0, float (&f)[8]) {
-    if (tau >= 0) {
-        Vec8<T>::load(x + (bos + tau) * a.C + c0, f);
-    } else if (a.state_in) {
-        load_state8(a.state_in + ((int64_t)n * 3 + (3 + tau)) * a.C + c0, f);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = 0.f;
-    }
-}
 
 // Prefill: a lane owns kFwdCh channels; a wave walks kFwdWaveRows
 // consecutive tokens once, carrying the last three inputs of the window, and
@@ -235,7 +222,7 @@ __global__ __launch_bounds__(kThreadsConv) void short_conv_state_kernel(ConvArgs
     const int64_t L = eos - bos;
     float f[3][8];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) window_input<T>(a, x, n, bos, L - 3 + j, c0, f[j]);
+    for (int j = 0; j < 3; ++j) window_input_n<T, 8>(a, x, n, bos, L - 3 + j, c0, f[j]);
 #pragma unroll
     for (int j = 0; j < 3; ++j) Vec8<float>::store(a.state_out + ((int64_t)n * 3 + j) * a.C + c0, f[j]);
 }
@@ -297,29 +284,6 @@ constexpr int kBwdBlockRows = kBwdWaveRows * kBwdWaves;
 constexpr int kBwdBlockCh = 64 * kBwdCh;            // channels per workgroup
 constexpr int kBwdGroup = 4;                        // tokens whose loads are issued together
 
-template <typename T, int N> struct VecN;
-template <typename T> struct VecN<T, 8> {
-    static __device__ __forceinline__ void load(const T* p, float (&f)[8]) { Vec8<T>::load(p, f); }
-};
-template <> struct VecN<float, 4> {
-    static __device__ __forceinline__ void load(const float* p, float (&f)[4]) {
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    }
-};
-template <> struct VecN<__bf16, 4> {
-    static __device__ __forceinline__ void load(const __bf16* p, float (&f)[4]) {
-        const uint2 u = *reinterpret_cast<const uint2*>(p);
-        f[0] = __uint_as_float(u.x << 16); f[1] = __uint_as_float(u.x & 0xffff0000u);
-        f[2] = __uint_as_float(u.y << 16); f[3] = __uint_as_float(u.y & 0xffff0000u);
-    }
-};
-template <int N>
-__device__ __forceinline__ void store_f32(float* p, const float (&f)[N]) {
-#pragma unroll
-    for (int i = 0; i < N; i += 4) reinterpret_cast<float4*>(p)[i / 4] = float4{f[i], f[i + 1], f[i + 2], f[i + 3]};
-}
-
 template <bool kAct>
 __device__ __forceinline__ float activate_slope(float p) {
     if constexpr (kAct) {
@@ -336,20 +300,6 @@ struct ConvBwdLane {
     float d1[kBwdCh], d2[kBwdCh], d3[kBwdCh];   // dp[u - 1], dp[u - 2], dp[u - 3]
 };
 
-// input x[tau] of sequence n (tau relative to its start, tau >= -3), kBwdCh channels
-template <typename T>
-__device__ __forceinline__ void window_input_bwd(const ConvArgs& a, const T* x, int n, int64_t bos, int64_t tau,
-                                                 int64_t c0, float (&f)[kBwdCh]) {
-    if (tau >= 0) {
-        VecN<T, kBwdCh>::load(x + (bos + tau) * a.C + c0, f);
-    } else if (a.state_in) {
-        VecN<float, kBwdCh>::load(a.state_in + ((int64_t)n * 3 + (3 + tau)) * a.C + c0, f);
-    } else {
-#pragma unroll
-        for (int i = 0; i < kBwdCh; ++i) f[i] = 0.f;
-    }
-}
-
 // G consecutive tokens u .. u + G - 1, all inside [bos, eos): loads first,
 // then dp, dw (tokens below te) and dx[t] for t = u + j - 3 in [lo, te).
 template <typename T, bool kAct, int G>
@@ -358,8 +308,8 @@ __device__ __forceinline__ void conv_bwd_group(const ConvBwdArgs& a, const T* x,
     float xu[G][kBwdCh], dyu[G][kBwdCh];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-        VecN<T, kBwdCh>::load(x + (u + j) * a.C + c0, xu[j]);
-        VecN<float, kBwdCh>::load(a.dy + (u + j) * a.C + c0, dyu[j]);
+        LoadN<T, kBwdCh>::load(x + (u + j) * a.C + c0, xu[j]);
+        LoadN<float, kBwdCh>::load(a.dy + (u + j) * a.C + c0, dyu[j]);
     }
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -385,7 +335,7 @@ __device__ __forceinline__ void conv_bwd_group(const ConvBwdArgs& a, const T* x,
 #pragma unroll
             for (int i = 0; i < kBwdCh; ++i)
                 out[i] = fmaf(s.w[i][0], dp[i], fmaf(s.w[i][1], s.d1[i], fmaf(s.w[i][2], s.d2[i], s.w[i][3] * s.d3[i])));
-            store_f32<kBwdCh>(a.dx + t * a.C + c0, out);
+            LoadN<float, kBwdCh>::store(a.dx + t * a.C + c0, out);
         }
 #pragma unroll
         for (int i = 0; i < kBwdCh; ++i) {
@@ -421,9 +371,9 @@ __global__ __launch_bounds__(64 * kBwdWaves) void short_conv_bwd_kernel(ConvBwdA
         int n;
         int64_t bos, eos;
         find_sequence(f, tb, n, bos, eos);
-        window_input_bwd<T>(f, x, n, bos, tb - bos - 3, c0, s.h0);
-        window_input_bwd<T>(f, x, n, bos, tb - bos - 2, c0, s.h1);
-        window_input_bwd<T>(f, x, n, bos, tb - bos - 1, c0, s.h2);
+        window_input_n<T, kBwdCh>(f, x, n, bos, tb - bos - 3, c0, s.h0);
+        window_input_n<T, kBwdCh>(f, x, n, bos, tb - bos - 2, c0, s.h1);
+        window_input_n<T, kBwdCh>(f, x, n, bos, tb - bos - 1, c0, s.h2);
         int64_t u = tb;
         for (;;) {
             if (u == eos) {
@@ -445,17 +395,17 @@ __global__ __launch_bounds__(64 * kBwdWaves) void short_conv_bwd_kernel(ConvBwdA
                     }
                     if (a.d_final) {
                         float df[kBwdCh];
-                        VecN<float, kBwdCh>::load(a.d_final + ((int64_t)n * 3 + r) * a.C + c0, df);
+                        LoadN<float, kBwdCh>::load(a.d_final + ((int64_t)n * 3 + r) * a.C + c0, df);
 #pragma unroll
                         for (int i = 0; i < kBwdCh; ++i) out[i] += df[i];
                     }
-                    store_f32<kBwdCh>(a.dx + t * a.C + c0, out);
+                    LoadN<float, kBwdCh>::store(a.dx + t * a.C + c0, out);
                 }
                 if (u >= te) break;
                 find_sequence(f, u, n, bos, eos);    // the next non-empty sequence starts at u
-                window_input_bwd<T>(f, x, n, bos, -3, c0, s.h0);
-                window_input_bwd<T>(f, x, n, bos, -2, c0, s.h1);
-                window_input_bwd<T>(f, x, n, bos, -1, c0, s.h2);
+                window_input_n<T, kBwdCh>(f, x, n, bos, -3, c0, s.h0);
+                window_input_n<T, kBwdCh>(f, x, n, bos, -2, c0, s.h1);
+                window_input_n<T, kBwdCh>(f, x, n, bos, -1, c0, s.h2);
 #pragma unroll
                 for (int i = 0; i < kBwdCh; ++i) s.d1[i] = s.d2[i] = s.d3[i] = 0.f;
             }
@@ -494,7 +444,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void short_conv_bwd_kernel(ConvBwdA
         for (int w2 = 1; w2 < kBwdWaves; ++w2)
 #pragma unroll
             for (int k = 0; k < kPer; ++k) acc[k] += red[w2][e + k];
-        store_f32<kPer>(a.part + ((int64_t)blockIdx.x * a.C + cbase) * 4 + e, acc);
+        LoadN<float, kPer>::store(a.part + ((int64_t)blockIdx.x * a.C + cbase) * 4 + e, acc);
     }
 }
 
@@ -535,9 +485,9 @@ __device__ __forceinline__ void conv_bwd_dstate(const ConvBwdArgs& a, int n, int
         w[i][0] = wi.x; w[i][1] = wi.y; w[i][2] = wi.z; w[i][3] = wi.w;
     }
     float h0[8], h1[8], h2[8], dp[3][8];
-    window_input<T>(f, x, n, bos, -3, c0, h0);
-    window_input<T>(f, x, n, bos, -2, c0, h1);
-    window_input<T>(f, x, n, bos, -1, c0, h2);
+    window_input_n<T, 8>(f, x, n, bos, -3, c0, h0);
+    window_input_n<T, 8>(f, x, n, bos, -2, c0, h1);
+    window_input_n<T, 8>(f, x, n, bos, -1, c0, h2);
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
         float xu[8], dyu[8];
