@@ -550,9 +550,11 @@ __device__ __forceinline__ void prepare_chunk2(const ChunkRegs& R, const PrepCtx
                                                const bf16x4& lowT, Issue&& issue) {
     const int lane = c.li + 16 * c.lg;
     f32x4 x[4];
+    if constexpr (kPro) __builtin_amdgcn_s_setprio(3);   // the gate (see the kernel's wave priorities)
 #pragma unroll
     for (int m = 0; m < 2; ++m)
         gamma_tiles<kPro>(R, m, c.gaddr, eyeN, lowT, x, c.nA, c.nAb, c.lbl2e, c.rows_left, c.lg);
+    if constexpr (kPro) __builtin_amdgcn_s_setprio(1);
     issue(0);   // (after the step-start burst of the other waves' loads)
     // everything that does not need d1 first: Kb2, the unscaled Kg2 and Qh2
     // (kept in fp32 for the d1 scaling) and this half's M2 and P2 shares
@@ -791,15 +793,23 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
             }
             if (it < ngroups) step(it, R0, R1);
         };
-        // Wave priorities: the chunk-2 waves and the chunk-1 wave of half 1
-        // (which forms the chunk-2 factors from their shares) are the
-        // preparation's critical path, so they issue ahead of the chunk-1 wave
-        // of half 0 they share a SIMD with; otherwise the older wave wins
-        // every tie. Measured at B=1 T=4096 H=96: -1.3% plain, -5% with the
-        // prologue (whose heavier chunk-1 work otherwise starves the chunk-2
-        // waves' gate).
+        // Wave priorities (state waves 2). The chunk-2 waves (1) and the
+        // chunk-1 wave of half 1, which forms the chunk-2 factors from their
+        // shares, are the preparation's critical path, so they issue ahead of
+        // the chunk-1 wave of half 0 they share a SIMD with; otherwise the
+        // older wave wins every tie. The factor-forming wave goes above the
+        // state waves (3) in the plain kernel; with the prologue it stays at 2
+        // and the chunk-2 waves instead rise to 3 while they form the gate
+        // (whose transcendentals the heavier chunk-1 work otherwise starves).
+        // Measured at B=1 T=4096 H=96 against no priorities: plain 195 -> 186
+        // us, with the prologue 257 -> 243 us.
         if (pc == 0) {
-            if (ph == 1) __builtin_amdgcn_s_setprio(2);
+            if (ph == 1) {
+                if constexpr (kPro)
+                    __builtin_amdgcn_s_setprio(2);
+                else
+                    __builtin_amdgcn_s_setprio(3);
+            }
             run([&](const ChunkRegs& cur, auto&& issue) { prepare_chunk1<kPro>(cur, ctx, eyeN, lowT, issue); });
         } else {
             __builtin_amdgcn_s_setprio(1);
