@@ -375,8 +375,8 @@ def bench_backward(steps, warmup, cpu=True):
            "hbm": {"algorithmic_bytes_per_launch": nbytes,
                    "achieved_GBs": nbytes / (kern_ms * 1e-3) / 1e9,
                    "workspace_bytes_each_way": w.T // 16 * w.H * w.Dk * w.Dv * 4},
-           "timed": "one kda_chunk_bwd call: zero fills of the atomically summed gradients, the per-chunk "
-                    "T/P/KK kernel, the sequential kernel"}
+           "timed": "one kda_chunk_bwd call: the per-chunk T/P/KK kernel (which also zeroes the atomically "
+                    "summed gradients) and the sequential kernel"}
     res["from_raw_projections"] = bench_backward_prologue(steps, warmup)
     if cpu:
         res["cpu_baseline"] = cpu_backward_baseline()

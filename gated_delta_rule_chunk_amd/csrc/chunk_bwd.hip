@@ -773,6 +773,23 @@ __global__ __launch_bounds__(256) void chunk_mats_kernel(BwdArgs a) {
     if (ch * C >= sq.len) return;   // a slot no sequence uses (uniform per block)
     const int64_t t0 = sq.bos + ch * C;
     const int rows = (int)min<int64_t>(C, sq.len - ch * C);
+    if (a.zero_grads) {
+        // this chunk's rows of the atomically summed gradients: every token
+        // row of every head lies in exactly one (slot, head) workgroup
+        const float4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int idx = tid + 256 * u;
+            const int r = idx >> 5, c = (idx & 31) * 4;
+            if (r < rows) {
+                const int64_t e = ((sq.b * a.T + t0 + r) * a.H + h) * DK + c;
+                *reinterpret_cast<float4*>(a.dq + e) = z;
+                *reinterpret_cast<float4*>(a.dk + e) = z;
+                *reinterpret_cast<float4*>(a.dg + e) = z;
+            }
+        }
+        if (tid < rows) a.dbeta[(sq.b * a.T + t0 + tid) * a.H + h] = 0.f;
+    }
     // loads: 16 rows x 32 quads, two quads per thread
     Raw4<Tin> q[2], k[2], g[2];
     bool in[2];
@@ -1174,9 +1191,12 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
 
 bool chunk_bwd_mfma_supported(const BwdArgs& a);
 
-hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t s) {
-    const int nvt = a.Dv / (a.Dv >= 64 ? 64 : a.Dv);
-    if (nvt > 1) {
+hipError_t launch_chunk_bwd(const BwdArgs& args, hipStream_t s) {
+    const int nvt = args.Dv / (args.Dv >= 64 ? 64 : args.Dv);
+    BwdArgs a = args;
+    // the matrix-core path zeroes the atomically summed gradients in its T/P/KK kernel
+    a.zero_grads = nvt > 1 && chunk_bwd_mfma_supported(a);
+    if (nvt > 1 && !a.zero_grads) {
         const int64_t rows = (int64_t)a.B * a.T * a.H;
         hipError_t e;
         if ((e = zero_fill(a.dq, rows * a.Dk, s)) != hipSuccess) return e;

@@ -89,6 +89,7 @@ struct BwdArgs {
     bool bf16;
     bool g_ge_m5 = true;       // g >= -5 holds (the matrix-core kernel relies on it)
     bool x_bf16 = false;       // with bf16 false: v and d_o are bf16 (matrix-core path only)
+    bool zero_grads = false;   // (set by the launcher) the T/P/KK kernel zeroes dq, dk, dg, dbeta
 };
 
 // The backward's workspace: a float32 chunk-entry state [H][Dk][Dv] per
