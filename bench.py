@@ -107,6 +107,26 @@ def read_traffic(key="traffic_bytes_per_launch"):
     return float(m_val.group(1))
 
 
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "chunk_mfma_k3_t4096_mfma_counters.md")
+
+
+def read_mfma_counters():
+    """The counter-measured matrix-core figures of the chunk kernel (rocprofv3's
+    MfmaUtil and MfmaFlopsBF16, per launch) from the committed summary, if it
+    was taken on the current kernel source; otherwise None."""
+    if not os.path.exists(MFMA_SUMMARY):
+        return None
+    text = open(MFMA_SUMMARY).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_util = re.search(r"(?m)^mfma_util_pct:\s*([0-9.eE+]+)", text)
+    m_fl = re.search(r"(?m)^mfma_flops_bf16_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_hash and m_util and m_fl) or m_hash.group(1) != kernel_source_hash():
+        return None
+    return {"mfma_busy_pct": float(m_util.group(1)), "mfma_flops_bf16_per_launch": float(m_fl.group(1)),
+            "what": "rocprofv3 MfmaUtil (matrix-core busy cycles over all SIMDs of the chip) and MfmaFlopsBF16 "
+                    "(executed bf16 MFMA flops, identity and zero-padded tiles included)"}
+
+
 SETTLE_S = 0.25
 
 
@@ -501,10 +521,23 @@ def cpu_baseline(min_wall_s=10.0, max_runs=200):
         wall = time.perf_counter() - t0
         if wall >= min_wall_s or runs >= max_runs:
             break
+    t1 = time.perf_counter()
+    kda_ref.c_forward(f["q"], f["k"], f["v"], f["g"], f["beta"], nthreads=1, want_final=True)
+    single = w.B * w.T / (time.perf_counter() - t1)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": runs * w.B * w.T / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"k3_t4096 whole workload (B=1, T={w.T}, H={w.H}, d=128; all heads and tokens), "
                       f"fp64 C oracle with OpenMP over the {w.H} heads on {cores} threads, {runs} runs "
-                      f"in {wall:.1f} s wall"}
+                      f"in {wall:.1f} s wall",
+            "single_thread_value": single, "cpu_model": model}
 
 
 def copy_calibration(nbytes=1 << 30):
@@ -586,7 +619,8 @@ def main():
         "mfma": {"achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": tflops / BF16_PEAK_TFLOPS, "flops_per_launch": nflops,
                  "count": "algorithmic, fixed: full 64x64 tiles of the chunk form at C=64, "
-                          "T*H*(2*64*(3*d_k+2*d_v)+6*d_k*d_v), whatever chunk the kernel uses"},
+                          "T*H*(2*64*(3*d_k+2*d_v)+6*d_k*d_v), whatever chunk the kernel uses",
+                 "counter_measured": read_mfma_counters()},
         "published_baseline": "none: the source pages report no KDA throughput on any hardware",
     }
     line["prologue"] = bench_prologue(args.steps, args.warmup)
