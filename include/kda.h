@@ -214,9 +214,10 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
 /*
  * Bytes of device workspace kda_chunk_bwd_prologue needs: that of
  * kda_chunk_bwd for the same sizes, plus float32 copies of the prologue's
- * outputs (q, k, g [B,T,H,Dk], beta [B,T,H]) and of v and d_o [B,T,H,Dv], plus
- * 2 x ceil(B*T/64) x H x Dk floats of partial sums. 0 when T = 0 or a size is
- * out of range.
+ * outputs (q, k, g [B,T,H,Dk], beta [B,T,H]) and room for float32 copies of v
+ * and d_o [B,T,H,Dv] (written only when bf16 inputs go to the vector-ALU
+ * backward), plus 2 x ceil(B*T/64) x H x Dk floats of partial sums. 0 when
+ * T = 0 or a size is out of range.
  */
 size_t kda_chunk_bwd_prologue_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
                                               int32_t packed);
