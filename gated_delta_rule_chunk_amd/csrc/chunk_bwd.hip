@@ -730,7 +730,7 @@ __device__ __forceinline__ void chunk_scale(Smem& sm, bool reverse) {
 // W = V - Kg S for columns 16t..16t+15 (sm.W holds V on entry).
 __device__ __forceinline__ void w_tile(Smem& sm, int t, int l16, int lg) {
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-#pragma unroll 4
+#pragma unroll 8
     for (int ks = 0; ks < DK / 4; ks += 2) {
         a0 = mfma(sm.Kg[l16][4 * ks + lg], sm.S[4 * ks + lg][16 * t + l16], a0);
         a1 = mfma(sm.Kg[l16][4 * ks + 4 + lg], sm.S[4 * ks + 4 + lg][16 * t + l16], a1);
@@ -1033,7 +1033,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
         } else {
             const int t = w - 4;
             f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, ap = a0;
-#pragma unroll 4
+#pragma unroll 8
             for (int ks = 0; ks < DK / 4; ks += 2) {
                 a0 = mfma(sm.Kh[l16][4 * ks + lg], sm.dS[4 * ks + lg][16 * t + l16], a0);
                 a1 = mfma(sm.Kh[l16][4 * ks + 4 + lg], sm.dS[4 * ks + 4 + lg][16 * t + l16], a1);
