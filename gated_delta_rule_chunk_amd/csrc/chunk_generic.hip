@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
         }
         for (int idx = tid; idx < C * BV; idx += kGenThreads) {
             const int r = idx / BV, c = idx % BV;
-            sV[r][c] = r < rows ? load_elem(v, ((tok0 + r) * H + h) * Dv + c0 + c) : 0.f;
+            sV[r][c] = r < rows && v ? load_elem(v, ((tok0 + r) * H + h) * Dv + c0 + c) : 0.f;
         }
         for (int r = tid; r < C; r += kGenThreads) {
             float bv = r < rows ? load_elem(beta, (tok0 + r) * H + h) : 0.f;
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
 
         for (int idx = tid; idx < C * BV; idx += kGenThreads) {
             const int r = idx / BV, j = idx % BV;
-            if (r < rows) {
+            if (r < rows && o) {
                 float acc = 0.f;
                 for (int c = 0; c < DK; ++c) acc += sQ[r][c] * sS[c][j];
                 for (int i = 0; i <= r; ++i) acc += sP[r][i] * sU[i][j];

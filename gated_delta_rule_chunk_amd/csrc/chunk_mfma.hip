@@ -840,8 +840,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         // preparation waves.
         const int64_t vrow_bytes = (int64_t)a.H * (kDV * 2);          // one token of v or o
         const int64_t head0 = (tok_base * a.H + h) * (int64_t)(kDV * 2) + col0 * 2;
-        Stream sv{static_cast<const char*>(a.v) + head0, len * vrow_bytes - col0 * 2};
-        Stream so{static_cast<const char*>(a.o) + head0, len * vrow_bytes - col0 * 2};
+        // a null v reads as zeros and a null o drops the outputs (empty buffer ranges)
+        Stream sv{a.v ? static_cast<const char*>(a.v) + head0 : nullptr, a.v ? len * vrow_bytes - col0 * 2 : 0};
+        Stream so{a.o ? static_cast<const char*>(a.o) + head0 : nullptr, a.o ? len * vrow_bytes - col0 * 2 : 0};
         const int64_t vstride = (int64_t)kNA * kC * vrow_bytes;
         // load/store order: row lane/4 of chunk s, columns 4(lane%4)..+3 of
         // this wave's 16; gathers move to and from the operand order

@@ -10,12 +10,12 @@ namespace kda {
 struct ChunkArgs {
     const void* q;
     const void* k;
-    const void* v;
+    const void* v;            // nullptr: v = 0 (internal passes of the split)
     const void* g;
     const void* beta;
     const float* s0;          // [N,H,Dk,Dv] or nullptr
     const int32_t* cu;        // [N+1] or nullptr
-    void* o;
+    void* o;                  // nullptr: outputs not written (internal passes of the split)
     float* sT;                // [N,H,Dk,Dv] or nullptr
     int32_t B, T, H, Dk, Dv, N, chunk;
     float scale;
@@ -136,7 +136,7 @@ hipError_t launch_prologue_bwd(const PrologueBwdArgs& p, const BwdArgs& core, hi
 
 // Workspace of the intra-sequence split (byte offsets, 256-aligned).
 struct SplitLayout {
-    int64_t seg_cu, vzero, scratch_o, ident, Bst, Sin, bytes;
+    int64_t seg_cu, ident, Bst, Sin, bytes;
 };
 SplitLayout split_layout(const ChunkArgs& a, int32_t P);
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace, hipStream_t s);

@@ -40,11 +40,6 @@ __global__ void split_offsets_kernel(const int32_t* cu, int32_t N, int32_t T, in
     if (n == N - 1) seg_cu[(int64_t)N * P] = (int32_t)(bos + len);
 }
 
-__global__ void fill_zero_u32_kernel(uint32_t* p, int64_t n) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
-}
-
 // Identity [Dk][Dk] per (segment, head).
 __global__ void fill_identity_kernel(float* p, int64_t mats, int Dk) {
     const int64_t n = mats * Dk * Dk;
@@ -176,13 +171,9 @@ hipError_t chunk_forward(const ChunkArgs& a, hipStream_t s) {
 SplitLayout split_layout(const ChunkArgs& a, int32_t P) {
     SplitLayout L;
     const int64_t segs = (int64_t)a.N * P;
-    const int64_t rows = (int64_t)a.B * a.T * a.H;
-    const int64_t elem = a.bf16 ? 2 : 4;
     auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
     int64_t off = 0;
     L.seg_cu = off;  off += up((segs + 1) * 4);
-    L.vzero = off;   off += up(rows * a.Dk * elem);           // v = 0 for pass 2 (d_v = d_k there)
-    L.scratch_o = off; off += up(rows * (a.Dk > a.Dv ? a.Dk : a.Dv) * elem);   // pass 1's and pass 2's outputs
     L.ident = off;   off += up(segs * a.H * (int64_t)a.Dk * a.Dk * 4);          // identity entry states, then A
     L.Bst = off;     off += up(segs * a.H * (int64_t)a.Dk * a.Dv * 4);
     L.Sin = off;     off += up(segs * a.H * (int64_t)a.Dk * a.Dv * 4);
@@ -194,44 +185,35 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
     const SplitLayout L = split_layout(a, P);
     char* ws = static_cast<char*>(workspace);
     int32_t* seg_cu = reinterpret_cast<int32_t*>(ws + L.seg_cu);
-    void* vzero = ws + L.vzero;
-    void* scratch_o = ws + L.scratch_o;
     float* AI = reinterpret_cast<float*>(ws + L.ident);
     float* Bst = reinterpret_cast<float*>(ws + L.Bst);
     float* Sin = reinterpret_cast<float*>(ws + L.Sin);
     const int64_t segs = (int64_t)a.N * P;
-    const int64_t rows = (int64_t)a.B * a.T * a.H;
-    const int64_t elem = a.bf16 ? 2 : 4;
     hipError_t e;
 
     split_offsets_kernel<<<dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, s>>>(a.cu, a.N, a.T, P, seg_cu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    {
-        const int64_t w1 = rows * a.Dk * elem / 4;
-        fill_zero_u32_kernel<<<dim3(grid_for(w1)), dim3(256), 0, s>>>(static_cast<uint32_t*>(vzero), w1);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        fill_identity_kernel<<<dim3(grid_for(segs * a.H * a.Dk * a.Dk)), dim3(256), 0, s>>>(AI, segs * a.H, a.Dk);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    fill_identity_kernel<<<dim3(grid_for(segs * a.H * a.Dk * a.Dk)), dim3(256), 0, s>>>(AI, segs * a.H, a.Dk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     // the packed view of the input: one row of B*T tokens, N*P sequences
     ChunkArgs seg = a;
     seg.B = 1;
     seg.T = a.B * a.T;
     seg.N = (int32_t)segs;
     seg.cu = seg_cu;
-    // 1. B (the outputs go to scratch)
+    // 1. B (no outputs written)
     ChunkArgs p1 = seg;
     p1.s0 = nullptr;
     p1.sT = Bst;
-    p1.o = scratch_o;
+    p1.o = nullptr;
     if ((e = chunk_forward(p1, s)) != hipSuccess) return e;
-    // 2. A: identity entry states, v = 0, d_v = d_k (its outputs are not used)
+    // 2. A: identity entry states, v = 0 (read from an empty range), d_v = d_k, no outputs
     ChunkArgs p2 = seg;
-    p2.v = vzero;
+    p2.v = nullptr;
     p2.Dv = a.Dk;
     p2.s0 = AI;
     p2.sT = AI;   // each state tile is read before it is written
-    p2.o = scratch_o;
+    p2.o = nullptr;
     if ((e = chunk_forward(p2, s)) != hipSuccess) return e;
     // 3. entry states of every segment, and the final states
     switch (a.Dk) {
