@@ -75,47 +75,50 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
         sS[c][j] = s0 ? s0[(((int64_t)n * H + h) * DK + c) * Dv + c0 + j] : 0.f;
     }
     __syncthreads();
-    for (int p = 0; p < P; ++p) {
-        const int64_t seg = (int64_t)n * P + p;
-        float* sin = Sin + (seg * H + h) * (int64_t)DK * Dv;
-        for (int idx = tid; idx < DK * BVs; idx += NT) {
-            const int c = idx / BVs, j = idx % BVs;
-            sin[(int64_t)c * Dv + c0 + j] = sS[c][j];
-        }
-        if (p == P - 1 && !sT) break;
-        // S <- A(p) S + B(p)
-        const float4* a4 = reinterpret_cast<const float4*>(A + (seg * H + h) * (int64_t)DK * DK);
-        const float* b = Bst + (seg * H + h) * (int64_t)DK * Dv;
+    if constexpr (DK == 128) {
+        // S_new = A S + B on the matrix cores: 8 row tiles of 16 x 16, two per
+        // wave. Step p + 1's A and B are loaded while step p is computed, into
+        // the registers step p's values left when they went to LDS and to the
+        // accumulators (past the last step the loads repeat it).
+        const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
         float4 ra[kPer];
+        float rbv[2][4];
+        auto issue = [&](int p) {
+            const int64_t seg = (int64_t)n * P + (p < P ? p : P - 1);
+            const float4* a4 = reinterpret_cast<const float4*>(A + (seg * H + h) * (int64_t)DK * DK);
+            const float* b = Bst + (seg * H + h) * (int64_t)DK * Dv;
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-            const int q = tid + NT * u;
-            ra[u] = q < kQuads ? a4[q] : float4{0.f, 0.f, 0.f, 0.f};
-        }
-        float rb[kOut];
+            for (int u = 0; u < kPer; ++u) ra[u] = a4[tid + NT * u];
 #pragma unroll
-        for (int u = 0; u < kOut; ++u) {
-            const int idx = tid + NT * u;
-            rb[u] = idx < DK * BVs ? b[(int64_t)(idx / BVs) * Dv + c0 + idx % BVs] : 0.f;
-        }
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-            const int q = tid + NT * u;
-            if (q < kQuads) {
+                for (int i = 0; i < 4; ++i) rbv[t][i] = b[(int64_t)(16 * (2 * w + t) + 4 * lg + i) * Dv + c0 + l16];
+        };
+        issue(0);
+        for (int p = 0; p < P; ++p) {
+            const int64_t seg = (int64_t)n * P + p;
+            float* sin = Sin + (seg * H + h) * (int64_t)DK * Dv;
+            for (int idx = tid; idx < DK * BVs; idx += NT) {
+                const int c = idx / BVs, j = idx % BVs;
+                sin[(int64_t)c * Dv + c0 + j] = sS[c][j];
+            }
+            if (p == P - 1 && !sT) break;
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const int q = tid + NT * u;
                 const int r = q / (DK / 4), c = (q % (DK / 4)) * 4;
                 sA[r][c] = ra[u].x; sA[r][c + 1] = ra[u].y; sA[r][c + 2] = ra[u].z; sA[r][c + 3] = ra[u].w;
             }
-        }
-        __syncthreads();
-        if constexpr (DK == 128) {
-            // S_new = A S + B on the matrix cores: 8 row tiles of 16 x 16, two per wave
-            const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
             f32x4 acc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[t][i] = rbv[t][i];
+            __syncthreads();
+            issue(p + 1);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int r0 = 16 * (2 * w + t);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[t][i] = b[(int64_t)(r0 + 4 * lg + i) * Dv + c0 + l16];
 #pragma unroll 8
                 for (int ks = 0; ks < DK / 4; ++ks)
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[r0 + l16][4 * ks + lg], sS[4 * ks + lg][l16],
@@ -126,28 +129,63 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sS[16 * (2 * w + t) + 4 * lg + i][l16] = acc[t][i];
-            (void)rb;
-        } else {
-            float out[kOut];
-#pragma unroll
+            __syncthreads();
+        }
+    } else {
+        for (int p = 0; p < P; ++p) {
+            const int64_t seg = (int64_t)n * P + p;
+            float* sin = Sin + (seg * H + h) * (int64_t)DK * Dv;
+            for (int idx = tid; idx < DK * BVs; idx += NT) {
+                const int c = idx / BVs, j = idx % BVs;
+                sin[(int64_t)c * Dv + c0 + j] = sS[c][j];
+            }
+            if (p == P - 1 && !sT) break;
+            // S <- A(p) S + B(p)
+            const float4* a4 = reinterpret_cast<const float4*>(A + (seg * H + h) * (int64_t)DK * DK);
+            const float* b = Bst + (seg * H + h) * (int64_t)DK * Dv;
+            float4 ra[kPer];
+    #pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const int q = tid + NT * u;
+                ra[u] = q < kQuads ? a4[q] : float4{0.f, 0.f, 0.f, 0.f};
+            }
+            float rb[kOut];
+    #pragma unroll
             for (int u = 0; u < kOut; ++u) {
                 const int idx = tid + NT * u;
-                const int c = idx / BVs, j = idx % BVs;
-                float acc = rb[u];
-                if (idx < DK * BVs) {
-#pragma unroll 8
-                    for (int i = 0; i < DK; ++i) acc += sA[c][i] * sS[i][j];
+                rb[u] = idx < DK * BVs ? b[(int64_t)(idx / BVs) * Dv + c0 + idx % BVs] : 0.f;
+            }
+    #pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const int q = tid + NT * u;
+                if (q < kQuads) {
+                    const int r = q / (DK / 4), c = (q % (DK / 4)) * 4;
+                    sA[r][c] = ra[u].x; sA[r][c + 1] = ra[u].y; sA[r][c + 2] = ra[u].z; sA[r][c + 3] = ra[u].w;
                 }
-                out[u] = acc;
             }
             __syncthreads();
-#pragma unroll
-            for (int u = 0; u < kOut; ++u) {
-                const int idx = tid + NT * u;
-                if (idx < DK * BVs) sS[idx / BVs][idx % BVs] = out[u];
+            {
+                float out[kOut];
+    #pragma unroll
+                for (int u = 0; u < kOut; ++u) {
+                    const int idx = tid + NT * u;
+                    const int c = idx / BVs, j = idx % BVs;
+                    float acc = rb[u];
+                    if (idx < DK * BVs) {
+    #pragma unroll 8
+                        for (int i = 0; i < DK; ++i) acc += sA[c][i] * sS[i][j];
+                    }
+                    out[u] = acc;
+                }
+                __syncthreads();
+    #pragma unroll
+                for (int u = 0; u < kOut; ++u) {
+                    const int idx = tid + NT * u;
+                    if (idx < DK * BVs) sS[idx / BVs][idx % BVs] = out[u];
+                }
             }
+            __syncthreads();
         }
-        __syncthreads();
     }
     if (sT) {
         for (int idx = tid; idx < DK * BVs; idx += NT) {
