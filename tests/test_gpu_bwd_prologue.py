@@ -115,3 +115,18 @@ def test_bwd_prologue_gate_bound_below_five():
     inp = synth.make_prologue_inputs(1, 120, 2, 128, 128, seed=760, dtype="bf16", init_state=True)
     d_o, d_fin = _cotangents(inp, 761)
     _check(inp, d_o, d_fin, label="lb=-8", lb=-8.0)
+
+
+def test_bwd_prologue_bf16_inputs_match_their_float32_widening_bitwise():
+    # bf16 raw inputs run the matrix-core backward with float32 q, k, g, beta and bf16 v, dO;
+    # the same values widened to float32 run it with every input float32. The arithmetic is
+    # the same, so the gradients must agree bit for bit.
+    inp = synth.make_prologue_inputs(1, 300, 3, 128, 128, seed=770, dtype="bf16", init_state=True)
+    d_o, d_fin = _cotangents(inp, 771)
+    wide = {k: (None if v is None or v.dtype != torch.bfloat16 else v.float()) for k, v in inp.items()}
+    wide = {k: (wide[k] if wide[k] is not None else inp[k]) for k in inp}
+    say("[case] bwd prologue bf16 vs widened float32, T=300 H=3")
+    a = gpu_grads(inp, d_o, d_fin, 0.5)
+    b = gpu_grads(wide, d_o.float(), d_fin, 0.5)
+    for n, x, y in zip(NAMES, a, b):
+        assert np.array_equal(x, y), n
