@@ -1,11 +1,11 @@
 """GPU parity on tensors larger than 2 GiB, where a 32-bit byte or element
 offset would wrap: the bf16 chunk forward and backward at B=1, T=90000, H=96
 (2.2 GB per q/k/v/g/o tensor, 4.4 GB per fp32 gradient, 35 GB of backward
-workspace, a ragged 16-row tail) and the short convolution at the same T over
-C=12288 channels.
+workspace, a ragged 16-row tail), the short convolution at the same T over
+C=12288 channels, and the decode step on a 2.5 GB state cache.
 
-Heads, and the channels of the convolution, are independent. So only sampled
-heads (channels) hold seeded inputs and the rest stay zero, and the fp64
+Heads, the channels of the convolution and the cache slots are independent.
+So only sampled heads (channels, slots) hold seeded inputs and the rest stay zero, and the fp64
 oracle recomputes exactly those units in full. A unit that read another
 unit's bytes (a wrapped offset) would see zeros or foreign data and miss the
 bar, and the zero units must come out exactly zero. Bars as for the full-size
@@ -122,3 +122,31 @@ def test_short_conv_beyond_2gib():
     e_tail = rel(y_s[:, -100:], ry[:, -100:])
     say(f"        relL2 y={ey:.3e} final={ef:.3e} last100={e_tail:.3e}")
     assert ey <= TOL_BF16 and e_tail <= TOL_BF16 and ef <= 1e-7, (ey, ef, e_tail)
+
+
+def test_decode_step_cache_beyond_2gib():
+    n_slots = 400          # 400 * 96 * 64 KiB = 2.5 GB of fp32 state cache
+    slots = [399, 0, 350, 200]
+    say(f"[case] decode step, cache [{n_slots},{H_BIG},128,128] fp32 ({n_slots * H_BIG * 65536 / 1e9:.2f} GB), "
+        f"slots {slots}")
+    small = synth.make_decode_cache(len(slots), H_BIG, 128, 128, seed=2027)
+    dev = "cuda"
+    cache = torch.zeros((n_slots, H_BIG, 128, 128), dtype=torch.float32, device=dev)
+    cache[slots] = small.to(dev)
+    dslots = torch.tensor(slots, dtype=torch.int32, device=dev)
+    ref_cache = small.double().numpy().copy()
+    for step in range(2):
+        x = synth.make_decode_step(len(slots), H_BIG, 128, 128, seed=2028, step=step, dtype="bf16")
+        d = {n: x[n].to(dev) for n in ("q", "k", "v", "g", "beta")}
+        o = kda.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], cache, state_slots=dslots)
+        torch.cuda.synchronize()
+        ro = kda_ref.c_decode_step(*(_f(x[n]) for n in ("q", "k", "v", "g", "beta")), ref_cache,
+                                   state_slots=np.arange(len(slots), dtype=np.int32))
+        e = rel(o.float().cpu().numpy(), ro)
+        say(f"        step {step} relL2 o={e:.3e}")
+        assert e <= TOL_BF16
+    ec = rel(cache[slots].cpu().numpy(), ref_cache)
+    untouched = [s for s in range(n_slots) if s not in slots]
+    say(f"        cache relL2={ec:.3e}")
+    assert ec <= TOL_BF16
+    assert float(cache[untouched].abs().amax()) == 0.0
