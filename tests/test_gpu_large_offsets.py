@@ -1,5 +1,6 @@
 """GPU parity on tensors larger than 2 GiB, where a 32-bit byte or element
-offset would wrap: the bf16 chunk forward and backward at B=1, T=90000, H=96
+offset would wrap: the bf16 chunk forward (unsplit and split into segments)
+and backward at B=1, T=90000, H=96
 (2.2 GB per q/k/v/g/o tensor, 4.4 GB per fp32 gradient, 35 GB of backward
 workspace, a ragged 16-row tail), the short convolution at the same T over
 C=12288 channels, and the decode step on a 2.5 GB state cache.
@@ -46,11 +47,16 @@ def _spread(small, dev):
     return full
 
 
-def test_forward_beyond_2gib():
-    say(f"[case] forward B=1 T={T_BIG} H={H_BIG} heads {HEADS} (tensors of {T_BIG * H_BIG * 256 / 1e9:.2f} GB)")
+@pytest.mark.parametrize("segments", [1, 4])
+def test_forward_beyond_2gib(segments):
+    say(f"[case] forward B=1 T={T_BIG} H={H_BIG} heads {HEADS} (tensors of {T_BIG * H_BIG * 256 / 1e9:.2f} GB), "
+        f"{'unsplit' if segments == 1 else f'{segments} segments'}")
     small = synth.make_chunk_inputs(1, T_BIG, len(HEADS), 128, 128, seed=2024, dtype="bf16")
     full = _spread(small, "cuda")
-    o, fin = kda.chunk_fwd(full["q"], full["k"], full["v"], full["g"], full["beta"])
+    if segments == 1:
+        o, fin = kda.chunk_fwd(full["q"], full["k"], full["v"], full["g"], full["beta"])
+    else:
+        o, fin = kda.chunk_fwd_split(full["q"], full["k"], full["v"], full["g"], full["beta"], segments)
     torch.cuda.synchronize()
     o_s = o[:, :, HEADS].float().cpu().numpy()
     f_s = fin[:, HEADS].cpu().numpy()
