@@ -146,31 +146,26 @@ def settle_clocks(fn, seconds=SETTLE_S):
 
 def time_launches(fn, steps, warmup, stream):
     """Clock settling (settle_clocks), W warm-up calls, then exactly `steps`
-    timed calls back to back, bracketed by device synchronisation; HIP events
-    on the launch stream give the average launch duration. A second, untimed
-    pass with one pair of events per launch gives the per-launch spread (those
-    events add their own overhead to each launch)."""
+    timed calls back to back, bracketed by device synchronisation. One HIP
+    event on the launch stream before the first call and one after every
+    call: the K intervals between consecutive events are the per-call
+    durations, their mean is the average launch duration over the timed region
+    and their median the median call. Returns (wall seconds, per-call ms list,
+    average ms)."""
     settle_clocks(fn)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    first.record(stream)
+    ev[0].record(stream)
     for i in range(steps):
         fn(i)
-    last.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    avg_ms = first.elapsed_time(last) / steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for i in range(steps):
-        starts[i].record(stream)
-        fn(i)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]      # ms
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]      # ms
+    avg_ms = ev[0].elapsed_time(ev[steps]) / steps
     return wall, per, avg_ms
 
 
@@ -226,6 +221,7 @@ def bench_prologue(steps, warmup):
                         "A_log [128], dt_bias [96*128]; gate lb*sigmoid(exp(A_log)*(logit+dt_bias)), lb=-5, "
                         "L2 eps 1e-6",
             "ms_per_step": wall / steps * 1e3, "tokens_per_s": w.T / (wall / steps), "kernel_ms": kern_ms,
+            "kernel_ms_median": float(np.median(per)),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": read_traffic("prologue_traffic_bytes_per_launch")},
             "algorithmic_bytes_per_launch": nbytes}
@@ -274,9 +270,9 @@ def bench_conv(steps, warmup):
             grads[j] = kda.short_conv_bwd(d[name], weights[j], dys[j], activation=True, workspace=ws_b,
                                           out=dxs[j])
 
-    _, _, conv_ms = time_launches(conv, steps, warmup, stream)
-    wall, _, _ = time_launches(chain, steps, warmup, stream)
-    _, _, bwd_ms = time_launches(conv_bwd, steps, warmup, stream)
+    _, conv_per, conv_ms = time_launches(conv, steps, warmup, stream)
+    wall, chain_per, _ = time_launches(chain, steps, warmup, stream)
+    _, bwd_per, bwd_ms = time_launches(conv_bwd, steps, warmup, stream)
     if not (torch.isfinite(o.float()).all() and torch.isfinite(fin).all()):
         raise RuntimeError("non-finite conv chain output")
     if not all(torch.isfinite(t).all() for g in grads.values() for t in g if t is not None):
@@ -292,14 +288,15 @@ def bench_conv(steps, warmup):
     gbs = nbytes / (float(conv_ms) * 1e-3) / 1e9
     return {"workload": "k3_t4096: causal depthwise conv (kernel 4, SiLU) of q, k, v, each [1,4096,96*128] bf16, "
                         "with the final conv state",
-            "ms_per_step": float(conv_ms),
+            "ms_per_step": float(conv_ms), "ms_median": float(np.median(conv_per)),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None},
             "algorithmic_bytes_per_step": nbytes,
             "chain": {"steps": "conv of q, k, v then the fused-prologue forward",
-                      "ms_per_step": wall / steps * 1e3, "tokens_per_s": w.T / (wall / steps)},
+                      "ms_per_step": wall / steps * 1e3, "ms_median": float(np.median(chain_per)),
+                      "tokens_per_s": w.T / (wall / steps)},
             "backward": {"steps": "kda_short_conv_bwd of q, k, v (fp32 dy; dx, dweight, d_state)",
-                         "ms_per_step": float(bwd_ms),
+                         "ms_per_step": float(bwd_ms), "ms_median": float(np.median(bwd_per)),
                          "roofline": {"bound": "hbm", "achieved": bwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": bwd_gbs / HBM_PEAK_GBS, "traffic": None},
                          "algorithmic_bytes_per_step": bwd_bytes}}
@@ -326,7 +323,7 @@ def bench_decode(steps, warmup):
     avg_ms = float(batch)
     gbs = step_bytes / (avg_ms * 1e-3) / 1e9
     return {"workload": f"{cfg['name']}: batch {Nb}, H={H}, d_k=d_v={Dk}, bf16 q/k/v/g/beta, fp32 state cache",
-            "ms_per_step": avg_ms, "tokens_per_s": Nb / (avg_ms * 1e-3),
+            "ms_per_step": avg_ms, "ms_median": float(np.median(per)), "tokens_per_s": Nb / (avg_ms * 1e-3),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None},
             "algorithmic_bytes_per_step": step_bytes}
@@ -465,14 +462,15 @@ def bench_split(steps, warmup, segments=10):
                             out=o, final_state=fin, workspace=ws)
 
     _, _, plain_ms = time_launches(plain, steps, warmup, stream)
-    wall, _, split_ms = time_launches(split, steps, warmup, stream)
+    wall, split_per, split_ms = time_launches(split, steps, warmup, stream)
     if not (torch.isfinite(o.float()).all() and torch.isfinite(fin).all()):
         raise RuntimeError("non-finite split output")
     nbytes = fwd_bytes(T, H, D, D, n_states_out=1, n_states_in=1)
     gbs = nbytes / (float(split_ms) * 1e-3) / 1e9
     return {"workload": f"B=1, T={T}, H={H} (12 of the 96 heads), d_k=d_v=128, bf16, initial state N(0,0.02), "
                         f"final state; {segments} segments per sequence",
-            "segments": segments, "ms_per_step": float(split_ms), "tokens_per_s": T / (float(split_ms) * 1e-3),
+            "segments": segments, "ms_per_step": float(split_ms), "ms_median": float(np.median(split_per)),
+            "tokens_per_s": T / (float(split_ms) * 1e-3),
             "unsplit_ms_per_step": float(plain_ms), "speedup_vs_unsplit": float(plain_ms) / float(split_ms),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None},
@@ -585,8 +583,8 @@ def main():
 
     w, wall, per, batch = bench_forward(args.steps, args.warmup)
     ms_per_step = wall / args.steps * 1e3
-    kern_ms = float(batch)                   # average launch time over the back-to-back timed region
-    kern_ms_median = float(np.median(per))   # untimed per-launch pass (events add their own overhead)
+    kern_ms = float(batch)                   # average launch duration over the timed region
+    kern_ms_median = float(np.median(per))   # median of the timed calls
     nbytes = fwd_bytes(w.T, w.H, w.Dk, w.Dv, n_states_out=1)
     nflops = fwd_flops(w.T, w.H, w.Dk, w.Dv)
     gbs = nbytes / (kern_ms * 1e-3) / 1e9
@@ -615,6 +613,8 @@ def main():
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic},
         "kernel_ms": kern_ms,
         "kernel_ms_median": kern_ms_median,
+        "kernel_ms_min_max": [float(np.min(per)), float(np.max(per))],
+        "tokens_per_s_at_median": w.T / (kern_ms_median * 1e-3),
         "algorithmic_bytes_per_launch": nbytes,
         "mfma": {"achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": tflops / BF16_PEAK_TFLOPS, "flops_per_launch": nflops,

@@ -13,6 +13,7 @@ not built, calls raise ``RuntimeError``.
     dq, dk, dv, dg, dbeta, d_initial = chunk_bwd(q, k, v, g, beta, d_o, initial_state=None,
                                                  d_final_state=None, cu_seqlens=None, scale=1.0)
     o = recurrent_step(q, k, v, g, beta, state_cache, state_slots=None, scale=1.0)
+    device_check()      # raises KDAError if a kernel's bounded wait gave up since the last check
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "kda.h")
 
-KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP, KDA_ERR_DEVICE = 0, 1, 2, 3, 4
 KDA_F32, KDA_BF16 = 0, 1
 _DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
 
@@ -88,6 +89,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error_message.argtypes = []
     lib.kda_last_error_message.restype = ctypes.c_char_p
+    lib.kda_device_check.argtypes = [P]
+    lib.kda_device_check.restype = ctypes.c_int
+    lib.kda_set_wait_limit.argtypes = [I32]
+    lib.kda_set_wait_limit.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -490,3 +495,18 @@ def recurrent_step(q, k, v, g, beta, state_cache, state_slots=None, scale=1.0, o
                                 _DTYPES[dt], _ptr(out), _stream(dev))
     _check(st)
     return out
+
+
+def device_check(device=None):
+    """Wait for torch's current stream on ``device`` and raise ``KDAError``
+    (status KDA_ERR_DEVICE) if a bounded wait of any library kernel on that
+    device gave up since the previous check."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.kda_device_check(_stream(dev)))
+
+
+def set_wait_limit(polls: int):
+    """Polls of one bounded wait before it gives up, for calls launched from now on."""
+    _check(load_library().kda_set_wait_limit(int(polls)))

@@ -377,11 +377,19 @@ __device__ __forceinline__ bf16x8 concat(const bf16x4& lo, const bf16x4& hi) {
     return r;
 }
 
-// bounded wait for a hand-over flag: its producer stores it every step
-// before the group barrier, so it always arrives
-__device__ __forceinline__ void wait_flag(const int* flag, int epoch) {
-    for (int spin = 0; spin < (1 << 22); ++spin) {
-        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == epoch) break;
+// Bounded wait for a hand-over flag. Its producer stores it every step before
+// the group barrier, so it always arrives; should it not arrive within
+// `limit` polls, the wave gives up, counts the timeout in the device status
+// word (kda_device_check reports it to the host) and goes on, so the
+// workgroup still reaches every barrier and the kernel ends.
+__device__ __forceinline__ void wait_flag(const int* flag, int epoch, int limit, unsigned int* status) {
+    int spin = 0;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != epoch) {
+        if (spin >= limit) {
+            if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        ++spin;
         __builtin_amdgcn_s_sleep(1);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -408,6 +416,8 @@ struct PrepCtx {
     int rows_left;     // rows of this chunk before the sequence end (may be <= 0 or >= 16)
     char* nrm;         // norm partials of the preparation waves
     int pw;            // this preparation wave
+    int spin_limit;    // polls before a flag wait gives up
+    unsigned int* status;   // device status word (timeouts)
 };
 
 // k, q of all four tiles as fp32 (lane (li, lg): token li, channels
@@ -441,7 +451,7 @@ __device__ __forceinline__ void kq_all(const ChunkRegs& R, const PrepCtx& c, con
         // the four lanes of a token store the same pair
         *reinterpret_cast<f32x2*>(c.nrm + 128 * c.pw + 8 * c.li) = f32x2{sk, sq};
         set_flag(c.flags + F_NRM + c.pw, c.epoch);
-        wait_flag(c.flags + F_NRM + (c.pw ^ 1), c.epoch);
+        wait_flag(c.flags + F_NRM + (c.pw ^ 1), c.epoch, c.spin_limit, c.status);
         const f32x2 other = *reinterpret_cast<const f32x2*>(c.nrm + 128 * (c.pw ^ 1) + 8 * c.li);
         const float rk = __builtin_amdgcn_rsqf(sk + other[0] + c.l2_eps);
         const float rq = __builtin_amdgcn_rsqf(sq + other[1] + c.l2_eps);
@@ -515,7 +525,7 @@ __device__ __forceinline__ void prepare_chunk1(const ChunkRegs& R, const PrepCtx
     const int pp = c.pq >> 1;
     if (c.ph == 0) {
         // T1 Diag(beta1) and -P1 from both halves' shares
-        wait_flag(c.flags + F_SH1 + pp, c.epoch);
+        wait_flag(c.flags + F_SH1 + pp, c.epoch, c.spin_limit, c.status);
         const f32x4 Mr = Ms + lds4(c.sh + SH_M1 * 1024 + 16 * lane);
         const f32x4 Pr = Ps + lds4(c.sh + SH_P1 * 1024 + 16 * lane);
         *reinterpret_cast<bf16x4*>(c.slot + S_TT1 + 8 * lane) = inverse_times_beta<kPro>(Mr, R.beta, c.fs, c.li, c.lg);
@@ -526,13 +536,13 @@ __device__ __forceinline__ void prepare_chunk1(const ChunkRegs& R, const PrepCtx
         set_flag(c.flags + F_SH1 + pp, c.epoch);
         // chunk 2 of the pair: T2 Diag(beta2) as soon as both chunk-2 waves
         // have stored M2 and P2, then -P2, -A and -B (beta here is chunk 2's)
-        wait_flag(c.flags + F_SH2 + 2 * pp, c.epoch);
-        wait_flag(c.flags + F_SH2 + 2 * pp + 1, c.epoch);
+        wait_flag(c.flags + F_SH2 + 2 * pp, c.epoch, c.spin_limit, c.status);
+        wait_flag(c.flags + F_SH2 + 2 * pp + 1, c.epoch, c.spin_limit, c.status);
         const f32x4 M2 = lds4(c.sh + SH_M2 * 1024 + 16 * lane) + lds4(c.sh + (SH_M2 + 1) * 1024 + 16 * lane);
         const f32x4 P2 = lds4(c.sh + SH_P2 * 1024 + 16 * lane) + lds4(c.sh + (SH_P2 + 1) * 1024 + 16 * lane);
         *reinterpret_cast<bf16x4*>(c.slot + S_TT2 + 8 * lane) = inverse_times_beta<kPro>(M2, R.beta, c.fs, c.li, c.lg);
-        wait_flag(c.flags + F_SHAB + 2 * pp, c.epoch);
-        wait_flag(c.flags + F_SHAB + 2 * pp + 1, c.epoch);
+        wait_flag(c.flags + F_SHAB + 2 * pp, c.epoch, c.spin_limit, c.status);
+        wait_flag(c.flags + F_SHAB + 2 * pp + 1, c.epoch, c.spin_limit, c.status);
         const f32x4 Ar = lds4(c.sh + SH_A * 1024 + 16 * lane) + lds4(c.sh + (SH_A + 1) * 1024 + 16 * lane);
         const f32x4 Br = lds4(c.sh + SH_B * 1024 + 16 * lane) + lds4(c.sh + (SH_B + 1) * 1024 + 16 * lane);
         *reinterpret_cast<bf16x4*>(c.slot + S_AN + 8 * lane) = pack4v(-Ar);
@@ -583,7 +593,7 @@ __device__ __forceinline__ void prepare_chunk2(const ChunkRegs& R, const PrepCtx
     *reinterpret_cast<f32x4*>(c.sh + (SH_M2 + c.ph) * 1024 + 16 * lane) = Ms;
     *reinterpret_cast<f32x4*>(c.sh + (SH_P2 + c.ph) * 1024 + 16 * lane) = Ps;
     set_flag(c.flags + F_SH2 + c.pq, c.epoch);
-    wait_flag(c.f_d1, c.epoch);
+    wait_flag(c.f_d1, c.epoch, c.spin_limit, c.status);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
         const int kk = 2 * c.ph + m;
@@ -596,7 +606,7 @@ __device__ __forceinline__ void prepare_chunk2(const ChunkRegs& R, const PrepCtx
             pack_pair(qa[2 * m] * d1[0], qa[2 * m + 1] * d1[1]);
     }
     issue(1);
-    wait_flag(c.f_ho, c.epoch);
+    wait_flag(c.f_ho, c.epoch, c.spin_limit, c.status);
     f32x4 As = zero4(), Bs = zero4();
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -729,6 +739,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         ctx.gaddr = 4 * (lg + 4 * li);
         ctx.nrm = smem + S_NRM;
         ctx.pw = pw;
+        ctx.spin_limit = a.spin_limit;
+        ctx.status = a.status;
         ctx.nA = zero4();
         ctx.nAb = zero4();
         ctx.lbl2e = 0.f;

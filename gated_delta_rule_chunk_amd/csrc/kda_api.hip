@@ -4,8 +4,46 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/kda.h"
 #include "launchers.hpp"
+
+// Device status word: the number of bounded waits (in any kernel of this
+// library, on this device) that gave up since the module was loaded. Kernels
+// add to it with a vector atomic from one lane; the host only reads it.
+__device__ __attribute__((aligned(256))) unsigned int kda_wait_timeouts[64];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mutex;
+unsigned int* g_status_ptr[kMaxDevices] = {};
+unsigned int g_status_seen[kMaxDevices] = {};
+std::atomic<int> g_spin_limit{1 << 22};
+
+}  // namespace
+
+namespace kda {
+
+// The status word's device address on the current device, looked up once per
+// device (each device holds its own copy of the module's variables).
+unsigned int* device_status_word() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (!g_status_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(kda_wait_timeouts)) != hipSuccess) return nullptr;
+        g_status_ptr[dev] = static_cast<unsigned int*>(p);
+    }
+    return g_status_ptr[dev];
+}
+
+int wait_spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
+
+}  // namespace kda
 
 namespace {
 
@@ -33,11 +71,44 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
         case KDA_ERR_HIP: return "KDA_ERR_HIP";
+        case KDA_ERR_DEVICE: return "KDA_ERR_DEVICE";
     }
     return "KDA_UNKNOWN_STATUS";
 }
 
 const char* kda_last_error_message(void) { return g_last_error; }
+
+kda_status kda_set_wait_limit(int32_t polls) {
+    g_last_error[0] = 0;
+    if (polls < 0) return fail(KDA_ERR_INVALID_ARG, "kda_set_wait_limit: polls must be >= 0, got %d", polls);
+    g_spin_limit.store(polls, std::memory_order_relaxed);
+    return KDA_OK;
+}
+
+kda_status kda_device_check(void* stream) {
+    g_last_error[0] = 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned int* word = kda::device_status_word();
+    int dev = 0;
+    if (!word || hipGetDevice(&dev) != hipSuccess)
+        return fail(KDA_ERR_HIP, "kda_device_check: the device status word is not accessible");
+    unsigned int now = 0;
+    hipError_t e = hipMemcpyAsync(&now, word, sizeof(now), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_device_check: %s", hipGetErrorString(e));
+    unsigned int seen;
+    {
+        std::lock_guard<std::mutex> lock(g_dev_mutex);
+        seen = g_status_seen[dev];
+        g_status_seen[dev] = now;
+    }
+    if (now != seen)
+        return fail(KDA_ERR_DEVICE,
+                    "kda_device_check: %u bounded wait(s) between waves gave up on device %d since the last check; "
+                    "the outputs of the calls that ran meanwhile are not valid",
+                    now - seen, dev);
+    return KDA_OK;
+}
 
 }  // extern "C"
 
@@ -77,13 +148,35 @@ kda_status check_chunk(const char* fn, const void* q, const void* k, const void*
         return fail(KDA_ERR_INVALID_ARG, "%s: o must not alias an input", fn);
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.s0 = initial_state; a.cu = cu_seqlens; a.o = o; a.sT = final_state;
-    a.B = B; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.N = N; a.chunk = chunk;
+    a.B = B; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.N = N; a.chunk = chunk; a.chunk_req = chunk_size;
     a.scale = scale; a.bf16 = dtype == KDA_BF16;
     return KDA_OK;
 }
 
-kda_status launch_chunk(const char* fn, const kda::ChunkArgs& a, void* stream) {
+// The matrix-core kernel has one chunk length (16 rows); an explicit request
+// for another one is refused rather than ignored.
+kda_status check_kernel_chunk(const char* fn, const kda::ChunkArgs& a) {
+    if (kda::chunk_mfma_supported(a) && a.chunk_req != 0 && a.chunk_req != 16)
+        return fail(KDA_ERR_UNSUPPORTED,
+                    "%s: chunk_size=%d; the bf16 Dk = Dv = 128 kernel runs 16-row chunks (pass 0 or 16)", fn,
+                    a.chunk_req);
+    return KDA_OK;
+}
+
+// Points a's bounded waits at the current device's status word.
+kda_status attach_status(const char* fn, kda::ChunkArgs& a) {
+    a.status = kda::device_status_word();
+    a.spin_limit = kda::wait_spin_limit();
+    if (!a.status) return fail(KDA_ERR_HIP, "%s: the device status word is not accessible", fn);
+    return KDA_OK;
+}
+
+kda_status launch_chunk(const char* fn, kda::ChunkArgs a, void* stream) {
+    const kda_status cs = check_kernel_chunk(fn, a);
+    if (cs != KDA_OK) return cs;
     if ((int64_t)a.N * a.H == 0) return KDA_OK;
+    const kda_status ss = attach_status(fn, a);
+    if (ss != KDA_OK) return ss;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = kda::chunk_mfma_supported(a) ? kda::launch_chunk_mfma(a, s)
                                                       : kda::launch_chunk_generic(a, s);
@@ -163,6 +256,8 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
     if ((int64_t)B * T > INT32_MAX || (int64_t)N * segments * H > ((int64_t)1 << 26))
         return fail(KDA_ERR_UNSUPPORTED, "%s: B*T must fit in int32 and N*segments*H below 2^26", fn);
     if (segments == 1 || T == 0) return launch_chunk(fn, a, stream);
+    const kda_status cs = check_kernel_chunk(fn, a);
+    if (cs != KDA_OK) return cs;
     const size_t need = kda_chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, N, dtype, segments);
     if (workspace_bytes < need || !workspace)
         return fail(KDA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, got %zu%s", fn, need, workspace_bytes,
@@ -176,6 +271,8 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
                 return fail(KDA_ERR_INVALID_ARG, "%s: the workspace must not overlap an input or output", fn);
         }
     }
+    const kda_status ss = attach_status(fn, a);
+    if (ss != KDA_OK) return ss;
     const hipError_t e = kda::launch_chunk_fwd_split(a, segments, workspace, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KDA_OK;
@@ -448,7 +545,7 @@ kda_status kda_short_conv_step(const void* x, const float* weight, float* conv_c
     if (y == x) return fail(KDA_ERR_INVALID_ARG, "%s: y must not alias x", fn);
     kda::ConvStepArgs a;
     a.x = x; a.w = weight; a.cache = conv_cache; a.slots = cache_slots; a.y = y;
-    a.Nb = Nb; a.C = C; a.act = activation == 1; a.bf16 = dtype == KDA_BF16;
+    a.n_slots = n_slots; a.Nb = Nb; a.C = C; a.act = activation == 1; a.bf16 = dtype == KDA_BF16;
     const hipError_t e = kda::launch_short_conv_step(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KDA_OK;
@@ -482,7 +579,7 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
     kda::StepArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.cache = state_cache; a.slots = state_slots; a.o = o;
-    a.Nb = Nb; a.H = H; a.Dk = Dk; a.Dv = Dv; a.scale = scale; a.bf16 = dtype == KDA_BF16;
+    a.n_slots = n_slots; a.Nb = Nb; a.H = H; a.Dk = Dk; a.Dv = Dv; a.scale = scale; a.bf16 = dtype == KDA_BF16;
     const hipError_t e = kda::launch_recurrent_step(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(KDA_ERR_HIP, "kda_recurrent_step: launch failed: %s", hipGetErrorString(e));

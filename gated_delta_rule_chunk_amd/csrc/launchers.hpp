@@ -18,6 +18,7 @@ struct ChunkArgs {
     void* o;                  // nullptr: outputs not written (internal passes of the split)
     float* sT;                // [N,H,Dk,Dv] or nullptr
     int32_t B, T, H, Dk, Dv, N, chunk;
+    int32_t chunk_req = 0;    // chunk_size as the caller passed it (0 = the kernel's own)
     float scale;
     bool bf16;
     // gate, beta and normalisation prologue: when set, q and k hold the raw
@@ -28,7 +29,16 @@ struct ChunkArgs {
     const float* dt_bias = nullptr;   // [H*Dk]
     float gate_lb = 0.f;
     float l2_eps = 0.f;
+    // bounded waits between waves: polls before giving up, and the device
+    // word that counts give-ups (set by the C ABI for every launch)
+    int spin_limit = 1 << 22;
+    unsigned int* status = nullptr;
 };
+
+// The device status word of the current device and the poll limit of every
+// bounded wait (both owned by the C ABI).
+unsigned int* device_status_word();
+int wait_spin_limit();
 
 struct StepArgs {
     const void* q;
@@ -36,9 +46,10 @@ struct StepArgs {
     const void* v;
     const void* g;
     const void* beta;
-    float* cache;
-    const int32_t* slots;
+    float* cache;              // [n_slots][H][Dk][Dv]
+    const int32_t* slots;      // [Nb] or nullptr (row r -> slot r)
     void* o;
+    int32_t n_slots;           // rows whose slot lies outside [0, n_slots) are padding
     int32_t Nb, H, Dk, Dv;
     float scale;
     bool bf16;
@@ -62,6 +73,7 @@ struct ConvStepArgs {
     float* cache;              // [n_slots][3][C]
     const int32_t* slots;      // [Nb] or nullptr
     void* y;                   // [Nb][C]
+    int32_t n_slots;           // rows whose slot lies outside [0, n_slots) are padding
     int32_t Nb, C;
     bool act, bf16;
 };

@@ -9,6 +9,10 @@
 // kernel is bound by HBM bandwidth: each thread keeps its slice of S' in
 // registers between the two reductions and the write-back, and every state
 // access is a coalesced 16-byte load or store along d_v.
+//
+// A row whose slot lies outside [0, n_slots) (e.g. -1 for a padding row of a
+// serving batch) touches no state: its output is zero and the cache is left
+// as it is.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -39,6 +43,10 @@ __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a
     const int h = blockIdx.x % a.H;
     const int slot = a.slots ? a.slots[row] : row;
     const int64_t tok = (int64_t)row * a.H + h;
+    if (slot < 0 || slot >= a.n_slots) {   // padding row (uniform over the workgroup)
+        for (int i = tid; i < DV; i += kStepThreads) store_elem(o, tok * DV + i, 0.f);
+        return;
+    }
     f32x4* S = reinterpret_cast<f32x4*>(a.cache + ((int64_t)slot * a.H + h) * DK * DV);
 
     const int quad = tid % QUADS;

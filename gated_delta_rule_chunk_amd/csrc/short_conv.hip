@@ -227,17 +227,24 @@ __global__ __launch_bounds__(kThreadsConv) void short_conv_state_kernel(ConvArgs
     for (int j = 0; j < 3; ++j) Vec8<float>::store(a.state_out + ((int64_t)n * 3 + j) * a.C + c0, f[j]);
 }
 
-// Decode: row r reads and shifts cache[slot(r)] ([3][C]).
+// Decode: row r reads and shifts cache[slot(r)] ([3][C]); a row whose slot
+// lies outside [0, n_slots) is padding (y = 0, the cache is not touched).
 template <typename T, bool kAct>
 __global__ __launch_bounds__(kThreadsConv) void short_conv_step_kernel(ConvStepArgs a) {
     const int64_t c0 = ((int64_t)blockIdx.y * kThreadsConv + threadIdx.x) * 8;
     const int r = blockIdx.x;
     if (c0 >= a.C) return;
     const int s = a.slots ? a.slots[r] : r;
-    float* st = a.cache + (int64_t)s * 3 * a.C + c0;
     const T* x = static_cast<const T*>(a.x);
     T* y = static_cast<T*>(a.y);
     float h0[8], h1[8], h2[8], xt[8], out[8];
+    if (s < 0 || s >= a.n_slots) {   // padding row: y = 0, no cache access
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = 0.f;
+        Vec8<T>::store(y + (int64_t)r * a.C + c0, out);
+        return;
+    }
+    float* st = a.cache + (int64_t)s * 3 * a.C + c0;
     load_state8(st, h0);
     load_state8(st + a.C, h1);
     load_state8(st + 2 * (int64_t)a.C, h2);

@@ -26,7 +26,7 @@
  *  - Preconditions that are NOT checked on the device: g in [-5, 0] (the K3
  *    gate bound; the bf16 chunk kernel relies on it to keep every in-chunk
  *    exponent below 80), finite inputs, cu_seqlens starting at 0,
- *    non-decreasing and ending at T, distinct decode state slots in range.
+ *    non-decreasing and ending at T, distinct decode state slots.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -42,7 +42,8 @@ typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, inconsistent shapes      */
     KDA_ERR_UNSUPPORTED = 2, /* legal but not built: dims, chunk size, dtype     */
-    KDA_ERR_HIP = 3          /* the HIP runtime reported an error at launch      */
+    KDA_ERR_HIP = 3,         /* the HIP runtime reported an error at launch      */
+    KDA_ERR_DEVICE = 4       /* kda_device_check: a kernel's bounded wait gave up */
 } kda_status;
 
 typedef enum {
@@ -63,10 +64,12 @@ typedef enum {
  *                  their initial state. Packed ("THD") batches are how the K3
  *                  package feeds variable-length sequences (ISEEKYAN/k3 README,
  *                  packed THD with context parallelism).
- *   chunk_size     16, 32 or 64, or 0 for the default. It changes only
- *                  rounding. It sets the chunk length of the float32 path
- *                  (default 64); the bf16 matrix-core kernel always works in
- *                  its native 16-row chunks.
+ *   chunk_size     0 for the kernel's own chunk length, or an explicit
+ *                  length. It changes only rounding. The bf16 matrix-core
+ *                  kernel (Dk = Dv = 128) works in 16-row chunks only: there
+ *                  chunk_size must be 0 or 16, and any other value is
+ *                  KDA_ERR_UNSUPPORTED. The float32 vector-ALU kernel takes
+ *                  16, 32 or 64 (0 = 64).
  *   scale          multiplies the output (1.0 reproduces the rule above)
  *   o              [B,T,H,Dv]  dtype, written for every row of every sequence;
  *                  must not alias an input. With T = 0, q, k, v, g, beta and
@@ -332,7 +335,9 @@ kda_status kda_short_conv_bwd(const void* x, const float* weight, const float* c
  * previous inputs from conv_cache[slot(r)] ([3][C] float32), writes
  * y[r] = sum_i weight[c][i] * window[i] (then SiLU if activation = 1) and
  * shifts x[r] into the cache. slot(r) = cache_slots[r], or r when cache_slots
- * is NULL; slots must be distinct and < n_slots (not checked on the device).
+ * is NULL; slots in range must be distinct. A row whose slot lies outside
+ * [0, n_slots) (for example -1, a padding row) gets y = 0 and leaves the
+ * cache untouched.
  *   x, y [Nb][C] dtype; conv_cache [n_slots][3][C] float32, updated in place.
  * Nb = 0 is a no-op. Errors as for kda_recurrent_step.
  */
@@ -341,13 +346,24 @@ kda_status kda_short_conv_step(const void* x, const float* weight, float* conv_c
                                void* y, void* stream);
 
 /*
- * One decode step (T = 1 per row) against a state cache, updated in place.
+ * One decode step (T = 1 per row) against a state cache, updated in place:
+ * the recurrence above applied to one token per (row, head),
+ *   S' = Diag(exp g) S,  u = beta (v - S'^T k),  S <- S' + k u^T,
+ *   o = scale * S^T q.
+ * This is the step K3 runs for each generated token in its 69 KDA layers
+ * (ISEEKYAN/k3 README, package scope: the recurrent KDA layers of the K3
+ * backbone; hysenlabs "kimi-k3-mlx", section "Attention is 93 layers split
+ * between KDA and a NoPE gated MLA": 96 heads of 128 channels, so 64 KiB of
+ * float32 state per head and sequence). The per-channel decay and its bound
+ * are those of kda_chunk_fwd.
  *
  *   q, k, g      [Nb,H,Dk] dtype;  v [Nb,H,Dv] dtype;  beta [Nb,H] dtype
  *   state_cache  [n_slots,H,Dk,Dv] float32
  *   state_slots  [Nb] int32 device array: row r reads and writes slot
- *                state_slots[r]; NULL means slot r. Slots must be distinct
- *                and < n_slots (not checked on the device).
+ *                state_slots[r]; NULL means slot r. Slots in range must be
+ *                distinct. A row whose slot lies outside [0, n_slots) (for
+ *                example -1, a padding row of a serving batch) is skipped on
+ *                the device: its o is zero and no state is read or written.
  *   o            [Nb,H,Dv] dtype
  *
  * Supported: Dk, Dv in {16, 32, 64, 128}. Nb = 0 is a no-op (pointers may
@@ -357,6 +373,33 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
                               const void* beta, float* state_cache, const int32_t* state_slots,
                               int32_t n_slots, int32_t Nb, int32_t H, int32_t Dk, int32_t Dv,
                               float scale, kda_dtype dtype, void* o, void* stream);
+
+/*
+ * Device-side failures. The bf16 matrix-core forward hands work between the
+ * waves of a workgroup through flags in LDS; every wait for such a flag is
+ * bounded. A producer always stores its flag, so a wait that gives up means a
+ * fault in the library, and the outputs of that call are then not valid.
+ * Instead of hanging or returning silently wrong data, the kernel counts
+ * each give-up in a per-device status word, finishes normally, and
+ * kda_device_check reports it: failures are explicit (ISEEKYAN/k3 README,
+ * package scope: unsupported or failing paths must fail explicitly).
+ *
+ * kda_device_check waits for the work enqueued on `stream`, then returns
+ * KDA_OK if no bounded wait of any call on the current device gave up since
+ * the previous check (or since the library was loaded), and KDA_ERR_DEVICE
+ * otherwise (kda_last_error_message gives the count). The check itself
+ * synchronises, so it belongs outside timed or captured regions.
+ */
+kda_status kda_device_check(void* stream);
+
+/*
+ * Polls of one bounded wait before it gives up (default 4194304, about 0.1 s
+ * of sleeping polls), for every call launched afterwards from any thread.
+ * Negative values are KDA_ERR_INVALID_ARG. A limit of 0 makes a wait give up
+ * whenever its flag is not already set; that is only useful to exercise the
+ * error path of kda_device_check.
+ */
+kda_status kda_set_wait_limit(int32_t polls);
 
 /* Static name of a status code. */
 const char* kda_status_string(kda_status s);

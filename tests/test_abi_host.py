@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol(lib):
                           "kda_chunk_fwd_split", "kda_chunk_fwd_split_workspace_bytes",
                           "kda_chunk_bwd_prologue", "kda_chunk_bwd_prologue_workspace_bytes",
                           "kda_short_conv_bwd", "kda_short_conv_bwd_workspace_bytes",
-                          "kda_status_string", "kda_last_error_message"}
+                          "kda_status_string", "kda_last_error_message", "kda_device_check",
+                          "kda_set_wait_limit"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -40,6 +41,13 @@ def test_status_strings(lib):
     assert lib.kda_status_string(1) == b"KDA_ERR_INVALID_ARG"
     assert lib.kda_status_string(2) == b"KDA_ERR_UNSUPPORTED"
     assert lib.kda_status_string(3) == b"KDA_ERR_HIP"
+    assert lib.kda_status_string(4) == b"KDA_ERR_DEVICE"
+
+
+def test_set_wait_limit_rejects_negative(lib):
+    assert lib.kda_set_wait_limit(-1) == kda.KDA_ERR_INVALID_ARG
+    assert "polls" in lib.kda_last_error_message().decode()
+    assert lib.kda_set_wait_limit(1 << 22) == kda.KDA_OK
 
 
 def _fwd(lib, **kw):
@@ -62,6 +70,9 @@ def _fwd(lib, **kw):
     (dict(Dk=96), kda.KDA_ERR_UNSUPPORTED, "head dims"),
     (dict(Dv=256), kda.KDA_ERR_UNSUPPORTED, "head dims"),
     (dict(chunk=48), kda.KDA_ERR_UNSUPPORTED, "chunk_size"),
+    # the bf16 d=128 matrix-core kernel runs 16-row chunks only: other explicit lengths are refused
+    (dict(chunk=64), kda.KDA_ERR_UNSUPPORTED, "16-row chunks"),
+    (dict(chunk=32), kda.KDA_ERR_UNSUPPORTED, "16-row chunks"),
     (dict(dtype=7), kda.KDA_ERR_UNSUPPORTED, "dtype"),
     (dict(N=2), kda.KDA_ERR_INVALID_ARG, "N must equal B"),
     (dict(cu=FAKE, B=2, N=2), kda.KDA_ERR_INVALID_ARG, "B == 1"),
@@ -97,6 +108,7 @@ def _pro(lib, **kw):
     (dict(Dk=96), kda.KDA_ERR_UNSUPPORTED, "head dims"),
     (dict(N=2), kda.KDA_ERR_INVALID_ARG, "N must equal B"),
     (dict(o=FAKE), kda.KDA_ERR_INVALID_ARG, "alias"),
+    (dict(chunk=64), kda.KDA_ERR_UNSUPPORTED, "16-row chunks"),
 ])
 def test_chunk_fwd_prologue_rejects_before_launch(lib, kw, status, needle):
     st = _pro(lib, **kw)
@@ -267,6 +279,7 @@ def _split(lib, **kw):
     (dict(Dk=96), kda.KDA_ERR_UNSUPPORTED, "head dims"),
     (dict(o=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
     (dict(B=2, N=1), kda.KDA_ERR_INVALID_ARG, "N must equal B"),
+    (dict(chunk=64), kda.KDA_ERR_UNSUPPORTED, "16-row chunks"),
 ])
 def test_chunk_fwd_split_rejects_before_launch(lib, kw, status, needle):
     st = _split(lib, **kw)
