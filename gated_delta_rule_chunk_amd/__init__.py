@@ -75,6 +75,9 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_split.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, ctypes.c_int,
                                         I32, P, ctypes.c_size_t, P, P, P]
     lib.kda_chunk_fwd_split.restype = ctypes.c_int
+    lib.kda_chunk_fwd_split_static.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F,
+                                               ctypes.c_int, I32, P, P, P]
+    lib.kda_chunk_fwd_split_static.restype = ctypes.c_int
     lib.kda_chunk_bwd_prologue_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     lib.kda_chunk_bwd_prologue_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_chunk_bwd_prologue.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, I32, I32, I32, I32, I32, I32, F,
@@ -220,6 +223,27 @@ def chunk_fwd_split(q, k, v, g, beta, segments, initial_state=None, cu_seqlens=N
                                  _ptr(cu_seqlens), B, T, H, Dk, Dv, N, int(chunk_size), float(scale), _DTYPES[dt],
                                  int(segments), _ptr(workspace), workspace.numel(), _ptr(out), _ptr(final_state),
                                  _stream(dev))
+    _check(st)
+    return out, final_state
+
+
+SPLIT_STATIC_SCRATCH_BYTES = 64 << 20   # KDA_SPLIT_STATIC_SCRATCH_BYTES
+
+
+def chunk_fwd_split_static(q, k, v, g, beta, segments, initial_state=None, cu_seqlens=None, chunk_size=0,
+                           scale=1.0, output_final_state=True, out=None, final_state=None):
+    """``chunk_fwd_split`` on the library's static scratch instead of a
+    workspace (kda_chunk_fwd_split_static): with ``out`` (and ``final_state``)
+    passed in, nothing is allocated. Sizes whose workspace exceeds
+    SPLIT_STATIC_SCRATCH_BYTES are refused; overlapping calls on one device
+    race on the scratch."""
+    lib = load_library()
+    B, T, H, Dk, Dv, N, dt, dev = _chunk_inputs(q, k, v, g, beta, initial_state, cu_seqlens,
+                                                ("q", "k", "v", "g", "beta"))
+    out, final_state = _chunk_outputs(B, T, H, Dk, Dv, N, dt, dev, out, final_state, output_final_state)
+    st = lib.kda_chunk_fwd_split_static(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                        _ptr(cu_seqlens), B, T, H, Dk, Dv, N, int(chunk_size), float(scale),
+                                        _DTYPES[dt], int(segments), _ptr(out), _ptr(final_state), _stream(dev))
     _check(st)
     return out, final_state
 

@@ -278,6 +278,39 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
     return KDA_OK;
 }
 
+kda_status kda_chunk_fwd_split_static(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                      const float* initial_state, const int32_t* cu_seqlens, int32_t B, int32_t T,
+                                      int32_t H, int32_t Dk, int32_t Dv, int32_t N, int32_t chunk_size, float scale,
+                                      kda_dtype dtype, int32_t segments, void* o, float* final_state, void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_chunk_fwd_split_static";
+    static_assert(KDA_SPLIT_STATIC_SCRATCH_BYTES == kda::kSplitStaticScratchBytes, "scratch size");
+    kda::ChunkArgs a;
+    const kda_status st = check_chunk(fn, q, k, v, g, beta, initial_state, cu_seqlens, B, T, H, Dk, Dv, N,
+                                      chunk_size, scale, dtype, o, final_state, a);
+    if (st != KDA_OK) return st;
+    if (segments < 1 || segments > KDA_MAX_SEGMENTS)
+        return fail(KDA_ERR_INVALID_ARG, "%s: segments must be in [1, %d], got %d", fn, KDA_MAX_SEGMENTS, segments);
+    if ((int64_t)B * T > INT32_MAX || (int64_t)N * segments * H > ((int64_t)1 << 26))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: B*T must fit in int32 and N*segments*H below 2^26", fn);
+    if (segments == 1 || T == 0) return launch_chunk(fn, a, stream);
+    const kda_status cs = check_kernel_chunk(fn, a);
+    if (cs != KDA_OK) return cs;
+    const size_t need = kda_chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, N, dtype, segments);
+    if (need > kda::kSplitStaticScratchBytes)
+        return fail(KDA_ERR_UNSUPPORTED,
+                    "%s: these sizes need %zu bytes of scratch; the static scratch holds %zu "
+                    "(use kda_chunk_fwd_split with a workspace)",
+                    fn, need, (size_t)kda::kSplitStaticScratchBytes);
+    void* ws = kda::split_static_scratch();
+    if (!ws) return fail(KDA_ERR_HIP, "%s: the static scratch's device address could not be looked up", fn);
+    const kda_status ss = attach_status(fn, a);
+    if (ss != KDA_OK) return ss;
+    const hipError_t e = kda::launch_chunk_fwd_split(a, segments, ws, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
+}
+
 size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
                                      int32_t packed) {
     if (B < 1 || T <= 0 || H < 1 || Dk < 1 || Dv < 1 || N < 0) return 0;

@@ -152,6 +152,10 @@ struct SplitLayout {
 };
 SplitLayout split_layout(const ChunkArgs& a, int32_t P);
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace, hipStream_t s);
+// The split's static scratch (kda_chunk_fwd_split_static): its size, and its
+// device address on the current device (nullptr if it cannot be looked up).
+constexpr size_t kSplitStaticScratchBytes = (size_t)64 << 20;
+void* split_static_scratch();
 
 // Backward of the short convolution: fwd holds the forward's arguments (x, w,
 // state_in, cu, sizes, activation, dtype); gradients are float32.

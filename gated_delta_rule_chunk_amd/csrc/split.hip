@@ -15,6 +15,8 @@
 //   4. the forward over all segments from S_in: the outputs, into o.
 // Passes 1, 2 and 4 are plain packed-sequence forward launches, so each of
 // them puts P times as many workgroups on the chip as the unsplit call.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -270,6 +272,35 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
     p4.s0 = Sin;
     p4.sT = nullptr;
     return chunk_forward(p4, s);
+}
+
+// Static scratch for the split entry point that allocates nothing
+// (kda_chunk_fwd_split_static): the split's workspace (segment offsets, the
+// identity / A states, the B states and the entry states) lives in this
+// file-scope array, of which every device holds its own copy from module load
+// to the end of the process. In host code the array's name is only a
+// host-side stand-in, so its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is ever passed to a kernel. Every
+// call on one device shares the array; calls that overlap in time on one
+// device (other streams, other threads) race on it.
+static __device__ __align__(256) char scratch[kSplitStaticScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+void* split_static_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
 }
 
 }  // namespace kda

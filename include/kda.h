@@ -166,6 +166,29 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
                                float* final_state, void* stream);
 
 /*
+ * kda_chunk_fwd_split for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Identical to kda_chunk_fwd_split (same arguments minus the
+ * workspace, same kernels, same results), except that the workspace is the
+ * library's static scratch: a device array of KDA_SPLIT_STATIC_SCRATCH_BYTES
+ * that every device the library runs on holds from module load until the
+ * process ends. The call allocates and frees nothing.
+ *
+ *   Sizes whose kda_chunk_fwd_split_workspace_bytes exceeds
+ *   KDA_SPLIT_STATIC_SCRATCH_BYTES are KDA_ERR_UNSUPPORTED (before any launch).
+ *   Every call on a device shares that device's scratch and leaves its last
+ *   contents in it (no call needs it to start at zero). Calls that overlap in
+ *   time on one device (from several streams or threads) race on it and give
+ *   undefined results: serialise them, e.g. on one stream.
+ */
+#define KDA_SPLIT_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_chunk_fwd_split_static(const void* q, const void* k, const void* v, const void* g,
+                                      const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                                      int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
+                                      int32_t chunk_size, float scale, kda_dtype dtype, int32_t segments, void* o,
+                                      float* final_state, void* stream);
+
+/*
  * Bytes of device workspace kda_chunk_bwd needs: per 16-row chunk slot and
  * head, one float32 state [Dk,Dv] plus three float32 16x16 matrices; T/16 + N
  * slots for packed sequences (packed != 0), B * ceil(T/16) otherwise. 0 when

@@ -24,6 +24,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step", "kda_short_conv",
                           "kda_short_conv_step", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
                           "kda_chunk_fwd_split", "kda_chunk_fwd_split_workspace_bytes",
+                          "kda_chunk_fwd_split_static",
                           "kda_chunk_bwd_prologue", "kda_chunk_bwd_prologue_workspace_bytes",
                           "kda_short_conv_bwd", "kda_short_conv_bwd_workspace_bytes",
                           "kda_status_string", "kda_last_error_message", "kda_device_check",
@@ -372,3 +373,33 @@ def test_short_conv_bwd_workspace_bytes(lib):
     assert lib.kda_short_conv_bwd_workspace_bytes(2, 65, 8) == 1 * 8 * 4 * 4
     assert lib.kda_short_conv_bwd_workspace_bytes(1, 257, 8) == 2 * 8 * 4 * 4
     assert lib.kda_short_conv_bwd_workspace_bytes(1, 0, 8) == 0
+
+
+def _split_static(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, cu=None, B=1, T=4096, H=12, Dk=128, Dv=128, N=1,
+             chunk=0, scale=1.0, dtype=kda.KDA_BF16, seg=8, o=ctypes.c_void_p(0x2000), sT=None, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_split_static(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["B"],
+                                          a["T"], a["H"], a["Dk"], a["Dv"], a["N"], a["chunk"], a["scale"],
+                                          a["dtype"], a["seg"], a["o"], a["sT"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    # 3 fp32 states of 64 KiB per (segment, head): 96 heads x 8 segments need 151 MB > 64 MiB
+    (dict(H=96), kda.KDA_ERR_UNSUPPORTED, "static scratch holds 67108864"),
+    (dict(seg=0), kda.KDA_ERR_INVALID_ARG, "segments"),
+    (dict(o=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(chunk=64), kda.KDA_ERR_UNSUPPORTED, "16-row chunks"),
+])
+def test_chunk_fwd_split_static_rejects_before_launch(lib, kw, status, needle):
+    st = _split_static(lib, **kw)
+    assert st == status
+    msg = lib.kda_last_error_message().decode()
+    assert needle in msg and msg.startswith("kda_chunk_fwd_split_static")
+
+
+def test_split_static_scratch_size_matches_header():
+    text = open(kda.HEADER_PATH).read()
+    assert "#define KDA_SPLIT_STATIC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert kda.SPLIT_STATIC_SCRATCH_BYTES == 64 << 20
+
