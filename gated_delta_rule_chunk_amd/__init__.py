@@ -70,6 +70,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_short_conv_bwd.restype = ctypes.c_int
     lib.kda_short_conv_step.argtypes = [P, P, P, P, I32, I32, I32, I32, ctypes.c_int, P, P]
     lib.kda_short_conv_step.restype = ctypes.c_int
+    lib.kda_chunk_fwd_conv_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, ctypes.c_int, F]
+    lib.kda_chunk_fwd_conv_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_chunk_fwd_conv.argtypes = [P, P, P, P, P, P, P, P, P, I32, P, P, P, P, F, F, P, P, I32, I32, I32, I32,
+                                       I32, I32, I32, F, ctypes.c_int, P, ctypes.c_size_t, P, P, P, P, P, P]
+    lib.kda_chunk_fwd_conv.restype = ctypes.c_int
     lib.kda_chunk_fwd_split_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.c_int, I32]
     lib.kda_chunk_fwd_split_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_chunk_fwd_split.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, ctypes.c_int,
@@ -197,6 +202,55 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk_size=
                            _DTYPES[dt], _ptr(out), _ptr(final_state), _stream(dev))
     _check(st)
     return out, final_state
+
+
+def chunk_fwd_conv_workspace_bytes(B, T, H, Dk, Dv, dtype, gate_lower_bound=-5.0):
+    """Bytes of workspace kda_chunk_fwd_conv needs."""
+    return int(load_library().kda_chunk_fwd_conv_workspace_bytes(B, T, H, Dk, Dv, _DTYPES[dtype],
+                                                                  float(gate_lower_bound)))
+
+
+def chunk_fwd_conv(xq, xk, xv, wq, wk, wv, g_logit, beta_logit, A_log, dt_bias, conv_states=None, activation=True,
+                   gate_lower_bound=-5.0, l2_eps=1e-6, initial_state=None, cu_seqlens=None, chunk_size=0, scale=1.0,
+                   output_final_state=True, output_conv_states=True, out=None, final_state=None,
+                   conv_states_out=None, workspace=None):
+    """Short convolution of q, k, v then the prologue forward (kda_chunk_fwd_conv).
+
+    xq, xk [B,T,H,Dk], xv [B,T,H,Dv] (projections before the convolution);
+    wq, wk [H*Dk,4], wv [H*Dv,4] float32; conv_states: None or a triple of
+    [N,3,H*D] float32 (None entries = zeros). Returns (o, final_state,
+    (conv_q, conv_k, conv_v) final conv states or None)."""
+    lib = load_library()
+    B, T, H, Dk, Dv, N, dt, dev = _chunk_inputs(xq, xk, xv, g_logit, beta_logit, initial_state, cu_seqlens,
+                                                ("xq", "xk", "xv", "g_logit", "beta_logit"))
+    _need(A_log, "A_log", (Dk,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H * Dk,), torch.float32, dev)
+    for w, d, name in ((wq, Dk, "wq"), (wk, Dk, "wk"), (wv, Dv, "wv")):
+        _need(w, name, (H * d, 4), torch.float32, dev)
+    s0 = [None, None, None] if conv_states is None else list(conv_states)
+    for st, d, name in zip(s0, (Dk, Dk, Dv), ("conv_state_q", "conv_state_k", "conv_state_v")):
+        if st is not None:
+            _need(st, name, (N, 3, H * d), torch.float32, dev)
+    out, final_state = _chunk_outputs(B, T, H, Dk, Dv, N, dt, dev, out, final_state, output_final_state)
+    s1 = [None, None, None]
+    if output_conv_states:
+        s1 = list(conv_states_out) if conv_states_out is not None else [
+            torch.empty((N, 3, H * d), dtype=torch.float32, device=dev) for d in (Dk, Dk, Dv)]
+        for st, d, name in zip(s1, (Dk, Dk, Dv), ("conv_state_q_out", "conv_state_k_out", "conv_state_v_out")):
+            _need(st, name, (N, 3, H * d), torch.float32, dev)
+    need = chunk_fwd_conv_workspace_bytes(B, T, H, Dk, Dv, dt, gate_lower_bound)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    st = lib.kda_chunk_fwd_conv(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(s0[0]),
+                                _ptr(s0[1]), _ptr(s0[2]), int(bool(activation)), _ptr(g_logit), _ptr(beta_logit),
+                                _ptr(A_log), _ptr(dt_bias), float(gate_lower_bound), float(l2_eps),
+                                _ptr(initial_state), _ptr(cu_seqlens), B, T, H, Dk, Dv, N, int(chunk_size),
+                                float(scale), _DTYPES[dt], _ptr(workspace), workspace.numel(), _ptr(out),
+                                _ptr(final_state), _ptr(s1[0]), _ptr(s1[1]), _ptr(s1[2]), _stream(dev))
+    _check(st)
+    return out, final_state, (tuple(s1) if output_conv_states else None)
 
 
 def chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, N, dtype, segments):

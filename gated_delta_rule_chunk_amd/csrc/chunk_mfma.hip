@@ -644,7 +644,65 @@ __device__ __forceinline__ void prepare_chunk2(const ChunkRegs& R, const PrepCtx
 }
 
 
-template <bool kPro>
+// ---------------------------------------------------------------------------
+// The short convolution fused into the state waves (kConv). Per channel,
+// y[t] = w3 x[t] + w2 x[t-1] + w1 x[t-2] + w0 x[t-3], in the same fma order as
+// the standalone convolution kernel, then y sigmoid(y) with the activation,
+// rounded to bf16 as the standalone kernel stores it; rows at or past the
+// sequence end are zero tokens.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float conv_tap4(const f32x4& w, float xm3, float xm2, float xm1, float x0, bool act) {
+    const float y = fmaf(w[3], x0, fmaf(w[2], xm1, fmaf(w[1], xm2, w[0] * xm3)));
+    return act ? y * __builtin_amdgcn_rcpf(1.f + __expf(-y)) : y;
+}
+__device__ __forceinline__ f32x4 unpack4(uint32_t lo, uint32_t hi) {
+    return f32x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u), __uint_as_float(hi << 16),
+                 __uint_as_float(hi & 0xffff0000u)};
+}
+__device__ __forceinline__ float bperm_f(float x, int addr) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
+}
+
+// v of one group in the state waves' load order (lane L: row L/4 of each
+// chunk, columns 4(L%4)..+3 of the wave's 16): raw bf16 words in, convolved
+// bf16 words out. hv holds this lane's row of "chunk -1" (the previous
+// group's chunk 3, or the conv state before the sequence start) as floats and
+// is advanced to this group's chunk 3. Row r - k comes from lane L - 4k of the
+// same chunk when r >= k, else from lane L - 4k + 64 of the chunk before.
+__device__ __forceinline__ u32x8 conv_v_group(const u32x8& raw, f32x4& hv, const f32x4 (&wv)[4], bool act,
+                                              int64_t row0, int64_t len, int lane) {
+    const int row = lane >> 2;
+    u32x8 out;
+#pragma unroll
+    for (int s = 0; s < kNA; ++s) {
+        const f32x4 cur = unpack4(raw[2 * s], raw[2 * s + 1]);
+        f32x4 xm[3];   // rows r-1, r-2, r-3
+#pragma unroll
+        for (int k = 1; k <= 3; ++k) {
+            const int addr = 4 * ((lane - 4 * k) & 63);
+            const f32x4 fc = unpack4(gather(raw[2 * s], addr), gather(raw[2 * s + 1], addr));
+            f32x4 fp;
+            if (s == 0) {
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) fp[cc] = bperm_f(hv[cc], addr);
+            } else {
+                fp = unpack4(gather(raw[2 * s - 2], addr), gather(raw[2 * s - 1], addr));
+            }
+            xm[k - 1] = row >= k ? fc : fp;
+        }
+        f32x4 y;
+        const bool live = row0 + kC * s + row < len;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+            y[cc] = live ? conv_tap4(wv[cc], xm[2][cc], xm[1][cc], xm[0][cc], cur[cc], act) : 0.f;
+        out[2 * s] = pack2_bf16(y[0], y[1]);
+        out[2 * s + 1] = pack2_bf16(y[2], y[3]);
+    }
+    hv = unpack4(raw[6], raw[7]);
+    return out;
+}
+
+template <bool kPro, bool kConv>
 __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
 
@@ -783,6 +841,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         // one loop per role, so that each is register-allocated on its own
         auto run = [&](auto&& prepare) {
             ChunkRegs R0, R1;
+            if constexpr (kConv) group_barrier();   // q, k of groups 0 and 1 convolved
             auto step = [&](int it, const ChunkRegs& cur, ChunkRegs& nxt) {
                 // the streams stand at group it+1
                 auto issue = [&](int part) {
@@ -881,7 +940,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         // the sequence end holds zero tokens, which leave the state unchanged,
         // and its output stores fall outside the store buffer's range, so the
         // hardware drops them. so stands at group gi.
-        auto consume = [&](int gi, const StateIn& vcur) {
+        // fused convolution: the row before each chunk of v (this lane's columns)
+        f32x4 hv = zero4();
+        if constexpr (kConv) {
+            // rows 13..15 of "chunk -1" are x[-3..-1]: the conv state
+            if (a.conv_s0[2] && lane >= 52)
+                hv = *reinterpret_cast<const f32x4*>(a.conv_s0[2] + ((int64_t)n * 3 + ((lane - 52) >> 2)) *
+                                                                    ((int64_t)a.H * kDV) +
+                                                     (int64_t)h * kDV + col0 + 4 * (lane & 3));
+        }
+        auto consume_words = [&](int gi, const StateIn& vcur) {
             const __amdgpu_buffer_rsrc_t ro = stream_rsrc(so);
             stream_advance(so, vstride);
 #pragma unroll
@@ -947,21 +1015,120 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
                 }
             }
         };
+        auto consume = [&](int gi, const StateIn& v) { consume_words(gi, v); };
+        // Fused convolution of q and k: in period it the state waves convolve
+        // group it + 2 into the workspace, which the preparation waves load in
+        // period it + 1 (their prefetch of the group after the one they
+        // prepare). Wave w takes chunk w of the group; lane: channels
+        // 8 (lane % 16)..+7, rows 4 (lane / 16)..+3 of the chunk. Every store
+        // completes before the period's barrier.
+        const int64_t row_bytes = (int64_t)a.H * (kDK * 2);
+        auto conv_qk = [&](int g) {
+            if constexpr (kConv) {
+                // below the preparation waves: this fills the issue slots they leave
+                __builtin_amdgcn_s_setprio(0);
+                const int pc = lane & 15, rb = lane >> 4;
+                const int64_t gbase = (int64_t)g * (kNA * kC);
+                const int lrow = kC * w + 4 * rb;                // this lane's first row in the group
+                if (g < ngroups) {
+                    const int64_t off = (tok_base * a.H + h) * (int64_t)(kDK * 2);
+                    const int64_t ch = (int64_t)h * kDK + 8 * pc;   // first channel of the lane in [H*Dk]
+#pragma unroll 1
+                    for (int t = 0; t < 2; ++t) {
+                        const float* const wtt = t == 0 ? a.conv_w[0] : a.conv_w[1];
+                        const float* const s0t = t == 0 ? a.conv_s0[0] : a.conv_s0[1];
+                        // raw rows from gbase - 4 on (a row before the sequence start is
+                        // read through an out-of-range offset: zero, no access), and
+                        // the convolved rows from gbase to the sequence end
+                        const Stream sx{static_cast<const char*>(t == 0 ? a.conv_xq : a.conv_xk) + off +
+                                            (gbase - 4) * row_bytes,
+                                        (len - gbase + 4) * row_bytes};
+                        const Stream sy{static_cast<const char*>(t == 0 ? a.q : a.k) + off + gbase * row_bytes,
+                                        (len - gbase) * row_bytes};
+                        const __amdgpu_buffer_rsrc_t rx = stream_rsrc(sx);
+                        const __amdgpu_buffer_rsrc_t ry = stream_rsrc(sy);
+#pragma unroll 1
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const int c0 = 16 * pc + 8 * hf;   // byte offset in the row
+                            u32x2 xr[7];                       // rows lrow-3 .. lrow+3 of the group
+#pragma unroll
+                            for (int j = 0; j < 7; ++j) {
+                                const bool before = gbase + lrow - 3 + j < 0;
+                                const int voff = before ? (int)0x80000000u : (lrow + 1 + j) * (int)row_bytes + c0;
+                                xr[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, voff, 0, 0));
+                            }
+                            f32x4 wt[4];
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) wt[c] = reinterpret_cast<const f32x4*>(wtt)[ch + 4 * hf + c];
+                            f32x4 hw[3];   // x[r-3], x[r-2], x[r-1]
+#pragma unroll
+                            for (int j = 0; j < 3; ++j) {
+                                const int64_t rr = gbase + lrow - 3 + j;
+                                hw[j] = (rr < 0 && s0t)
+                                            ? *reinterpret_cast<const f32x4*>(
+                                                  s0t + ((int64_t)n * 3 + (3 + rr)) * ((int64_t)a.H * kDK) + ch + 4 * hf)
+                                            : unpack4(xr[j][0], xr[j][1]);
+                            }
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const f32x4 xi = unpack4(xr[3 + i][0], xr[3 + i][1]);
+                                f32x4 yo;
+#pragma unroll
+                                for (int c = 0; c < 4; ++c) yo[c] = conv_tap4(wt[c], hw[0][c], hw[1][c], hw[2][c], xi[c], a.conv_act);
+                                hw[0] = hw[1];
+                                hw[1] = hw[2];
+                                hw[2] = xi;
+                                // (rows past the sequence end fall outside the store range)
+                                __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2_bf16(yo[0], yo[1]), pack2_bf16(yo[2], yo[3])},
+                                                                      ry, (lrow + i) * (int)row_bytes + c0, 0, 0);
+                            }
+                        }
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the stores are in L2 before the barrier
+                __builtin_amdgcn_s_setprio(2);
+            }
+        };
+        // v is convolved in place at the end of the period that loaded it, off the state chain
+        auto conv_v = [&](int gi, StateIn& V) {
+            if constexpr (kConv) {
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4 wv[4];   // this lane's v taps (reloaded each group: fewer registers held)
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc)
+                    wv[cc] = reinterpret_cast<const f32x4*>(a.conv_w[2])[(int64_t)h * kDV + col0 + 4 * (lane & 3) + cc];
+                V = conv_v_group(V, hv, wv, a.conv_act, (int64_t)gi * (kNA * kC), len, lane);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if constexpr (kConv) {
+            conv_qk(0);
+            conv_qk(1);
+            group_barrier();
+        }
         // iteration it loads group it and consumes group it-1
         load_group(VA);
+        conv_qk(2);
+        conv_v(0, VA);
         group_barrier();
         int it = 1;
         for (; it + 1 <= ngroups; it += 2) {
             load_group(VB);
             consume(it - 1, VA);
+            conv_qk(it + 2);
+            conv_v(it, VB);
             group_barrier();
             load_group(VA);
             consume(it, VB);
+            conv_qk(it + 3);
+            conv_v(it + 1, VA);
             group_barrier();
         }
         if (it <= ngroups) {
             load_group(VB);
             consume(it - 1, VA);
+            conv_qk(it + 2);
+            conv_v(it, VB);
             group_barrier();
         }
         if (a.sT) {
@@ -984,10 +1151,13 @@ bool chunk_mfma_supported(const ChunkArgs& a) {
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t s) {
     const int units = a.N * a.H;
-    if (a.prologue)
-        hipLaunchKernelGGL(chunk_mfma_kernel<true>, dim3((unsigned)(units * kNVT)), dim3(kThreads), 0, s, a);
+    const dim3 grid((unsigned)(units * kNVT));
+    if (a.conv)
+        hipLaunchKernelGGL((chunk_mfma_kernel<true, true>), grid, dim3(kThreads), 0, s, a);
+    else if (a.prologue)
+        hipLaunchKernelGGL((chunk_mfma_kernel<true, false>), grid, dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(chunk_mfma_kernel<false>, dim3((unsigned)(units * kNVT)), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((chunk_mfma_kernel<false, false>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

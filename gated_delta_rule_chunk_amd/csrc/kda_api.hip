@@ -230,6 +230,127 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
     return launch_chunk(fn, a, stream);
 }
 
+size_t kda_chunk_fwd_conv_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, kda_dtype dtype,
+                                          float gate_lower_bound) {
+    if (B < 1 || T <= 0 || H < 1 || !dim_ok(Dk) || !dim_ok(Dv) || (dtype != KDA_F32 && dtype != KDA_BF16)) return 0;
+    const int64_t rows = (int64_t)B * T * H;
+    const bool fused = dtype == KDA_BF16 && Dk == 128 && Dv == 128 && gate_lower_bound >= -5.f;
+    // fused: the convolved q and k (bf16); otherwise the three convolved projections
+    return fused ? (size_t)(2 * rows * Dk * 2) : (size_t)(rows * (2 * Dk + Dv) * (dtype == KDA_BF16 ? 2 : 4));
+}
+
+kda_status kda_chunk_fwd_conv(const void* xq, const void* xk, const void* xv, const float* wq, const float* wk,
+                              const float* wv, const float* conv_state_q, const float* conv_state_k,
+                              const float* conv_state_v, int32_t activation, const void* g_logit,
+                              const void* beta_logit, const float* A_log, const float* dt_bias,
+                              float gate_lower_bound, float l2_eps, const float* initial_state,
+                              const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                              int32_t N, int32_t chunk_size, float scale, kda_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* o, float* final_state, float* conv_state_q_out,
+                              float* conv_state_k_out, float* conv_state_v_out, void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_chunk_fwd_conv";
+    kda::ChunkArgs a;
+    const kda_status st = check_chunk(fn, xq, xk, xv, g_logit, beta_logit, initial_state, cu_seqlens, B, T, H, Dk,
+                                      Dv, N, chunk_size, scale, dtype, o, final_state, a);
+    if (st != KDA_OK) return st;
+    if (T > 0 && (!A_log || !dt_bias))
+        return fail(KDA_ERR_INVALID_ARG, "%s: A_log and dt_bias must be non-NULL when T > 0", fn);
+    if (!wq || !wk || !wv) return fail(KDA_ERR_INVALID_ARG, "%s: the conv taps wq, wk, wv must be non-NULL", fn);
+    if (activation != 0 && activation != 1)
+        return fail(KDA_ERR_INVALID_ARG, "%s: activation must be 0 (none) or 1 (SiLU), got %d", fn, activation);
+    if (!(gate_lower_bound < 0.f) || !(gate_lower_bound > -1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: gate_lower_bound must be finite and negative (got %g)", fn,
+                    (double)gate_lower_bound);
+    if (!(l2_eps > 0.f) || !(l2_eps < 1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: l2_eps must be finite and positive (got %g)", fn, (double)l2_eps);
+    if ((int64_t)B * T > ((int64_t)1 << 31) * 16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", fn);
+    a.prologue = true;
+    a.A_log = A_log;
+    a.dt_bias = dt_bias;
+    a.gate_lb = gate_lower_bound;
+    a.l2_eps = l2_eps;
+    const kda_status cs = check_kernel_chunk(fn, a);
+    if (cs != KDA_OK) return cs;
+    const size_t need = kda_chunk_fwd_conv_workspace_bytes(B, T, H, Dk, Dv, dtype, gate_lower_bound);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KDA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, got %zu%s", fn, need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    if (need > 0) {
+        const char* ws = static_cast<const char*>(workspace);
+        const void* ptrs[] = {xq, xk, xv, g_logit, beta_logit, o, initial_state, final_state, wq, wk, wv,
+                              conv_state_q, conv_state_k, conv_state_v, conv_state_q_out, conv_state_k_out,
+                              conv_state_v_out};
+        for (const void* p : ptrs) {
+            const char* c = static_cast<const char*>(p);
+            if (c && c >= ws && c < ws + need)
+                return fail(KDA_ERR_INVALID_ARG, "%s: the workspace must not overlap an input or output", fn);
+        }
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t rows = (int64_t)B * T * H;
+    const bool fused = kda::chunk_mfma_supported(a);
+    char* ws = static_cast<char*>(workspace);
+    kda::ConvArgs c[3];
+    const void* xs[3] = {xq, xk, xv};
+    const float* wts[3] = {wq, wk, wv};
+    const float* s0s[3] = {conv_state_q, conv_state_k, conv_state_v};
+    float* s1s[3] = {conv_state_q_out, conv_state_k_out, conv_state_v_out};
+    const int64_t elt = dtype == KDA_BF16 ? 2 : 4;
+    for (int t = 0; t < 3; ++t) {
+        c[t].x = xs[t]; c[t].w = wts[t]; c[t].state_in = s0s[t]; c[t].cu = cu_seqlens;
+        c[t].y = fused ? nullptr : ws + (t == 0 ? 0 : t == 1 ? rows * Dk * elt : 2 * rows * Dk * elt);
+        c[t].state_out = s1s[t];
+        c[t].B = B; c[t].T = T; c[t].C = H * (t < 2 ? Dk : Dv); c[t].N = N;
+        c[t].act = activation == 1; c[t].bf16 = dtype == KDA_BF16;
+    }
+    hipError_t e = hipSuccess;
+    if (fused) {
+        // one kernel: the state waves convolve q, k (into the workspace) and v
+        a.conv = true;
+        a.conv_xq = xq;
+        a.conv_xk = xk;
+        a.q = ws;
+        a.k = ws + rows * Dk * 2;
+        a.v = xv;
+        for (int t = 0; t < 3; ++t) {
+            a.conv_w[t] = wts[t];
+            a.conv_s0[t] = s0s[t];
+        }
+        a.conv_act = activation == 1;
+        if ((int64_t)a.N * a.H > 0) {
+            const kda_status ss = attach_status(fn, a);
+            if (ss != KDA_OK) return ss;
+            e = kda::launch_chunk_mfma(a, s);
+        }
+    } else {
+        // every other shape: the three convolutions into the workspace, then the prologue forward
+        for (int t = 0; t < 3 && e == hipSuccess && T > 0; ++t) {
+            kda::ConvArgs ct = c[t];
+            ct.state_out = nullptr;
+            e = kda::launch_short_conv(ct, s);
+        }
+        if (e == hipSuccess) {
+            a.q = c[0].y;
+            a.k = c[1].y;
+            a.v = c[2].y;
+            if (T == 0) a.q = a.k = a.v = nullptr;
+            const kda_status ls = launch_chunk(fn, a, stream);
+            if (ls != KDA_OK) return ls;
+        }
+    }
+    // final conv states (the last three inputs of every window)
+    for (int t = 0; t < 3 && e == hipSuccess; ++t) {
+        if (!s1s[t] || N == 0) continue;
+        kda::ConvArgs ct = c[t];
+        ct.y = nullptr;
+        e = kda::launch_short_conv(ct, s);
+    }
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
+}
+
 size_t kda_chunk_fwd_split_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
                                            kda_dtype dtype, int32_t segments) {
     if (B < 1 || T <= 0 || H < 1 || N < 1 || segments <= 1 || segments > KDA_MAX_SEGMENTS || !dim_ok(Dk) ||

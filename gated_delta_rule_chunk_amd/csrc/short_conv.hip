@@ -580,7 +580,7 @@ template <typename T>
 hipError_t launch_conv_t(const ConvArgs& a, hipStream_t s) {
     const int64_t BT = (int64_t)a.B * a.T;
     const unsigned cgroups = (unsigned)((a.C / 8 + kThreadsConv - 1) / kThreadsConv);
-    if (BT > 0) {
+    if (BT > 0 && a.y) {   // (a null y: only the final states)
         const dim3 grid((unsigned)((BT + kFwdBlockRows - 1) / kFwdBlockRows),
                         (unsigned)((a.C + kFwdBlockCh - 1) / kFwdBlockCh));
         if (a.act)

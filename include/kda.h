@@ -125,6 +125,60 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
                                   float* final_state, void* stream);
 
 /*
+ * Bytes of device workspace kda_chunk_fwd_conv needs (0 for T = 0 or
+ * out-of-range sizes): for bf16 with Dk = Dv = 128 and gate_lower_bound >= -5
+ * (the fused kernel) the convolved q and k, 2 x B*T*H*Dk bf16; otherwise the
+ * three convolved projections, B*T*H*(2 Dk + Dv) elements of dtype.
+ */
+size_t kda_chunk_fwd_conv_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, kda_dtype dtype,
+                                          float gate_lower_bound);
+
+/*
+ * The KDA layer's token mixer from the projections before the short
+ * convolution: for each of q, k and v the kernel-4 causal convolution of
+ * kda_short_conv (with its conv state and optional SiLU; K3 runs a short
+ * convolution of kernel size 4 on the query, key and value projections before
+ * KDA: hysenlabs "kimi-k3-mlx", section "Attention is 93 layers split between
+ * KDA and a NoPE gated MLA"), its output rounded to dtype, then
+ * kda_chunk_fwd_prologue on the convolved q, k and v. The result equals that
+ * sequence of calls (bit for bit on the fused path).
+ *
+ * For bf16 with Dk = Dv = 128 and gate_lower_bound >= -5 this is one kernel:
+ * the state waves of the chunk kernel, idle for part of every group, convolve
+ * v in registers right before using it and convolve q and k two groups ahead
+ * into the workspace, from which the preparation waves load them (the
+ * convolved q and k are written once and read back from L2; nothing else of
+ * the convolution touches HBM). Every other supported shape runs the three
+ * convolutions into the workspace, then the prologue forward.
+ *
+ *   xq, xk [B,T,H,Dk], xv [B,T,H,Dv]  dtype: the projections before the convolution
+ *   wq, wk [H*Dk][4], wv [H*Dv][4]     float32 taps (16-byte aligned rows)
+ *   conv_state_q, _k, _v  [N][3][H*D] float32 (x[-3], x[-2], x[-1] of each
+ *                          sequence), or NULL for zeros
+ *   activation             0 = none, 1 = SiLU after each convolution
+ *   g_logit, beta_logit, A_log, dt_bias, gate_lower_bound, l2_eps, initial_state,
+ *   cu_seqlens, B, T, H, Dk, Dv, N, chunk_size, scale, dtype, o, final_state
+ *                          as for kda_chunk_fwd_prologue
+ *   workspace              at least kda_chunk_fwd_conv_workspace_bytes(...) bytes
+ *                          of device memory, not overlapping any input or output;
+ *                          contents on entry do not matter
+ *   conv_state_q_out, _k_out, _v_out  [N][3][H*D] float32 or NULL: each
+ *                          sequence's last three inputs (as kda_short_conv's
+ *                          conv_state_out; may alias the input states)
+ * Errors as for kda_chunk_fwd_prologue and kda_short_conv; NULL taps, a bad
+ * activation or a short workspace are KDA_ERR_INVALID_ARG.
+ */
+kda_status kda_chunk_fwd_conv(const void* xq, const void* xk, const void* xv, const float* wq, const float* wk,
+                              const float* wv, const float* conv_state_q, const float* conv_state_k,
+                              const float* conv_state_v, int32_t activation, const void* g_logit,
+                              const void* beta_logit, const float* A_log, const float* dt_bias,
+                              float gate_lower_bound, float l2_eps, const float* initial_state,
+                              const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                              int32_t N, int32_t chunk_size, float scale, kda_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* o, float* final_state, float* conv_state_q_out,
+                              float* conv_state_k_out, float* conv_state_v_out, void* stream);
+
+/*
  * Bytes of device workspace kda_chunk_fwd_split needs for these sizes and
  * segments >= 2 (0 for segments <= 1, T = 0 or out-of-range sizes; the same
  * for packed and fixed-length batches with the same N).

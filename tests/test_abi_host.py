@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step", "kda_short_conv",
                           "kda_short_conv_step", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
                           "kda_chunk_fwd_split", "kda_chunk_fwd_split_workspace_bytes",
-                          "kda_chunk_fwd_split_static",
+                          "kda_chunk_fwd_split_static", "kda_chunk_fwd_conv", "kda_chunk_fwd_conv_workspace_bytes",
                           "kda_chunk_bwd_prologue", "kda_chunk_bwd_prologue_workspace_bytes",
                           "kda_short_conv_bwd", "kda_short_conv_bwd_workspace_bytes",
                           "kda_status_string", "kda_last_error_message", "kda_device_check",
@@ -402,4 +402,47 @@ def test_split_static_scratch_size_matches_header():
     text = open(kda.HEADER_PATH).read()
     assert "#define KDA_SPLIT_STATIC_SCRATCH_BYTES ((size_t)64 << 20)" in text
     assert kda.SPLIT_STATIC_SCRATCH_BYTES == 64 << 20
+
+
+def _conv_fwd(lib, **kw):
+    a = dict(xq=FAKE, xk=FAKE, xv=FAKE, wq=FAKE, wk=FAKE, wv=FAKE, sq=None, sk=None, sv=None, act=1, g=FAKE,
+             beta=FAKE, A_log=FAKE, dt_bias=FAKE, lb=-5.0, eps=1e-6, s0=None, cu=None, B=1, T=64, H=2, Dk=128,
+             Dv=128, N=1, chunk=0, scale=1.0, dtype=kda.KDA_BF16, ws=ctypes.c_void_p(1 << 40), wsb=1 << 30,
+             o=ctypes.c_void_p(0x2000), sT=None, oq=None, ok=None, ov=None, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_conv(a["xq"], a["xk"], a["xv"], a["wq"], a["wk"], a["wv"], a["sq"], a["sk"], a["sv"],
+                                  a["act"], a["g"], a["beta"], a["A_log"], a["dt_bias"], a["lb"], a["eps"], a["s0"],
+                                  a["cu"], a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["N"], a["chunk"], a["scale"],
+                                  a["dtype"], a["ws"], a["wsb"], a["o"], a["sT"], a["oq"], a["ok"], a["ov"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(xq=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(wk=None), kda.KDA_ERR_INVALID_ARG, "conv taps"),
+    (dict(act=2), kda.KDA_ERR_INVALID_ARG, "activation"),
+    (dict(A_log=None), kda.KDA_ERR_INVALID_ARG, "A_log"),
+    (dict(lb=0.0), kda.KDA_ERR_INVALID_ARG, "gate_lower_bound"),
+    (dict(eps=0.0), kda.KDA_ERR_INVALID_ARG, "l2_eps"),
+    (dict(ws=None), kda.KDA_ERR_INVALID_ARG, "workspace"),
+    (dict(wsb=100), kda.KDA_ERR_INVALID_ARG, "workspace"),
+    (dict(o=ctypes.c_void_p((1 << 40) + 64)), kda.KDA_ERR_INVALID_ARG, "overlap"),
+    (dict(Dk=96), kda.KDA_ERR_UNSUPPORTED, "head dims"),
+    (dict(chunk=64), kda.KDA_ERR_UNSUPPORTED, "16-row chunks"),
+])
+def test_chunk_fwd_conv_rejects_before_launch(lib, kw, status, needle):
+    st = _conv_fwd(lib, **kw)
+    assert st == status
+    msg = lib.kda_last_error_message().decode()
+    assert needle in msg and msg.startswith("kda_chunk_fwd_conv")
+
+
+def test_chunk_fwd_conv_workspace_bytes():
+    import torch
+    # fused path (bf16, d=128, bound >= -5): convolved q and k in bf16
+    assert kda.chunk_fwd_conv_workspace_bytes(1, 4096, 96, 128, 128, torch.bfloat16, -5.0) == 2 * 4096 * 96 * 128 * 2
+    # other paths: the three convolved projections in the input dtype
+    assert kda.chunk_fwd_conv_workspace_bytes(1, 100, 4, 64, 32, torch.float32, -5.0) == 100 * 4 * (2 * 64 + 32) * 4
+    assert kda.chunk_fwd_conv_workspace_bytes(1, 100, 4, 128, 128, torch.bfloat16, -6.0) == 100 * 4 * 384 * 2
+    assert kda.chunk_fwd_conv_workspace_bytes(1, 0, 4, 128, 128, torch.bfloat16, -5.0) == 0
 
