@@ -62,6 +62,8 @@
 // the rows of a pair (the update and O2's second term) take slot s < 4 of
 // lane group lg as row 4lg+s of chunk 1 and slot s >= 4 as row 4lg+s-4 of
 // chunk 2.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -645,7 +647,7 @@ __device__ __forceinline__ void prepare_chunk2(const ChunkRegs& R, const PrepCtx
 
 
 // ---------------------------------------------------------------------------
-// The short convolution fused into the state waves (kConv). Per channel,
+// The short convolution of v fused into the state waves (kConv). Per channel,
 // y[t] = w3 x[t] + w2 x[t-1] + w1 x[t-2] + w0 x[t-3], in the same fma order as
 // the standalone convolution kernel, then y sigmoid(y) with the activation,
 // rounded to bf16 as the standalone kernel stores it; rows at or past the
@@ -663,42 +665,65 @@ __device__ __forceinline__ float bperm_f(float x, int addr) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
 }
 
-// v of one group in the state waves' load order (lane L: row L/4 of each
-// chunk, columns 4(L%4)..+3 of the wave's 16): raw bf16 words in, convolved
-// bf16 words out. hv holds this lane's row of "chunk -1" (the previous
-// group's chunk 3, or the conv state before the sequence start) as floats and
-// is advanced to this group's chunk 3. Row r - k comes from lane L - 4k of the
-// same chunk when r >= k, else from lane L - 4k + 64 of the chunk before.
+// 32-bit value of lane li - k (row_shr) or li + m (row_shl) of this lane's
+// 16-lane row; lanes whose source lies outside the row get 0
+template <int K>
+__device__ __forceinline__ uint32_t row_shr(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x110 + K, 0xf, 0xf, false);
+}
+template <int M>
+__device__ __forceinline__ uint32_t row_shl(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x100 + M, 0xf, 0xf, false);
+}
+
+// v of one group, convolved on its way to the matrix-core operand order.
+// raw: the state waves' load order (lane L: row L/4 of each chunk, columns
+// 4(L%4)..+3 of the wave's 16); the result is in operand order (lane (li, lg):
+// row li, columns 4lg..+3), where row li - k of a chunk sits k lanes down the
+// same 16-lane row and, for li < k, row 16 + li - k of the chunk before sits
+// 16 - k lanes up: DPP row shifts, no cross-row traffic. hv holds this lane's
+// row of "chunk -1" (the previous group's chunk 3, or the conv state before the
+// sequence start) in operand order as floats, and is advanced to this group's
+// chunk 3.
 __device__ __forceinline__ u32x8 conv_v_group(const u32x8& raw, f32x4& hv, const f32x4 (&wv)[4], bool act,
-                                              int64_t row0, int64_t len, int lane) {
-    const int row = lane >> 2;
+                                              int64_t row0, int64_t len, int li, int gaddr) {
+    u32x8 op;
+#pragma unroll
+    for (int j = 0; j < 2 * kNA; ++j) op[j] = gather(raw[j], gaddr);
     u32x8 out;
 #pragma unroll
     for (int s = 0; s < kNA; ++s) {
-        const f32x4 cur = unpack4(raw[2 * s], raw[2 * s + 1]);
-        f32x4 xm[3];   // rows r-1, r-2, r-3
-#pragma unroll
-        for (int k = 1; k <= 3; ++k) {
-            const int addr = 4 * ((lane - 4 * k) & 63);
-            const f32x4 fc = unpack4(gather(raw[2 * s], addr), gather(raw[2 * s + 1], addr));
+        const f32x4 cur = unpack4(op[2 * s], op[2 * s + 1]);
+        f32x4 xm[3];   // rows li-1, li-2, li-3
+        auto shifted = [&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            const f32x4 fc = unpack4(row_shr<k>(op[2 * s]), row_shr<k>(op[2 * s + 1]));
             f32x4 fp;
             if (s == 0) {
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) fp[cc] = bperm_f(hv[cc], addr);
+                for (int cc = 0; cc < 4; ++cc) {
+                    // (hv[cc] goes through a scalar first: clang's __builtin_bit_cast of a
+                    // vector element reads element 0 whatever the index)
+                    const float h = hv[cc];
+                    fp[cc] = __uint_as_float(row_shl<16 - k>(__float_as_uint(h)));
+                }
             } else {
-                fp = unpack4(gather(raw[2 * s - 2], addr), gather(raw[2 * s - 1], addr));
+                fp = unpack4(row_shl<16 - k>(op[2 * s - 2]), row_shl<16 - k>(op[2 * s - 1]));
             }
-            xm[k - 1] = row >= k ? fc : fp;
-        }
+            xm[k - 1] = li >= k ? fc : fp;
+        };
+        shifted(std::integral_constant<int, 1>{});
+        shifted(std::integral_constant<int, 2>{});
+        shifted(std::integral_constant<int, 3>{});
         f32x4 y;
-        const bool live = row0 + kC * s + row < len;
+        const bool live = row0 + kC * s + li < len;
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
             y[cc] = live ? conv_tap4(wv[cc], xm[2][cc], xm[1][cc], xm[0][cc], cur[cc], act) : 0.f;
         out[2 * s] = pack2_bf16(y[0], y[1]);
         out[2 * s + 1] = pack2_bf16(y[2], y[3]);
     }
-    hv = unpack4(raw[6], raw[7]);
+    hv = unpack4(op[6], op[7]);
     return out;
 }
 
@@ -841,7 +866,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         // one loop per role, so that each is register-allocated on its own
         auto run = [&](auto&& prepare) {
             ChunkRegs R0, R1;
-            if constexpr (kConv) group_barrier();   // q, k of groups 0 and 1 convolved
             auto step = [&](int it, const ChunkRegs& cur, ChunkRegs& nxt) {
                 // the streams stand at group it+1
                 auto issue = [&](int part) {
@@ -943,11 +967,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         // fused convolution: the row before each chunk of v (this lane's columns)
         f32x4 hv = zero4();
         if constexpr (kConv) {
-            // rows 13..15 of "chunk -1" are x[-3..-1]: the conv state
-            if (a.conv_s0[2] && lane >= 52)
-                hv = *reinterpret_cast<const f32x4*>(a.conv_s0[2] + ((int64_t)n * 3 + ((lane - 52) >> 2)) *
-                                                                    ((int64_t)a.H * kDV) +
-                                                     (int64_t)h * kDV + col0 + 4 * (lane & 3));
+            // rows 13..15 of "chunk -1" are x[-3..-1]: the conv state (operand order)
+            if (a.conv_sv && li >= 13)
+                hv = *reinterpret_cast<const f32x4*>(a.conv_sv + ((int64_t)n * 3 + (li - 13)) * ((int64_t)a.H * kDV) +
+                                                     (int64_t)h * kDV + col0 + 4 * lg);
         }
         auto consume_words = [&](int gi, const StateIn& vcur) {
             const __amdgpu_buffer_rsrc_t ro = stream_rsrc(so);
@@ -967,8 +990,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
                 decay_state<0>(D, S, e2);
                 // X = V - Kg S (rows 4lg+j, column li); OT = -(Qh S)^T (column
                 // 4lg+j of row li), for both chunks
-                const u32x2 v1 = {gather(vcur[4 * pr], gaddr), gather(vcur[4 * pr + 1], gaddr)};
-                const u32x2 v2 = {gather(vcur[4 * pr + 2], gaddr), gather(vcur[4 * pr + 3], gaddr)};
+                // (the fused convolution hands v over in operand order already)
+                const u32x2 v1 = kConv ? u32x2{vcur[4 * pr], vcur[4 * pr + 1]}
+                                       : u32x2{gather(vcur[4 * pr], gaddr), gather(vcur[4 * pr + 1], gaddr)};
+                const u32x2 v2 = kConv ? u32x2{vcur[4 * pr + 2], vcur[4 * pr + 3]}
+                                       : u32x2{gather(vcur[4 * pr + 2], gaddr), gather(vcur[4 * pr + 3], gaddr)};
                 f32x4 X1 = mfma32(widen(__builtin_bit_cast(bf16x4, v1)), eyeV, zero4());
                 f32x4 X2 = mfma32(widen(__builtin_bit_cast(bf16x4, v2)), eyeV, zero4());
                 f32x4 OT1 = zero4(), OT2 = zero4();
@@ -1016,118 +1042,38 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
             }
         };
         auto consume = [&](int gi, const StateIn& v) { consume_words(gi, v); };
-        // Fused convolution of q and k: in period it the state waves convolve
-        // group it + 2 into the workspace, which the preparation waves load in
-        // period it + 1 (their prefetch of the group after the one they
-        // prepare). Wave w takes chunk w of the group; lane: channels
-        // 8 (lane % 16)..+7, rows 4 (lane / 16)..+3 of the chunk. Every store
-        // completes before the period's barrier.
-        const int64_t row_bytes = (int64_t)a.H * (kDK * 2);
-        auto conv_qk = [&](int g) {
-            if constexpr (kConv) {
-                // below the preparation waves: this fills the issue slots they leave
-                __builtin_amdgcn_s_setprio(0);
-                const int pc = lane & 15, rb = lane >> 4;
-                const int64_t gbase = (int64_t)g * (kNA * kC);
-                const int lrow = kC * w + 4 * rb;                // this lane's first row in the group
-                if (g < ngroups) {
-                    const int64_t off = (tok_base * a.H + h) * (int64_t)(kDK * 2);
-                    const int64_t ch = (int64_t)h * kDK + 8 * pc;   // first channel of the lane in [H*Dk]
-#pragma unroll 1
-                    for (int t = 0; t < 2; ++t) {
-                        const float* const wtt = t == 0 ? a.conv_w[0] : a.conv_w[1];
-                        const float* const s0t = t == 0 ? a.conv_s0[0] : a.conv_s0[1];
-                        // raw rows from gbase - 4 on (a row before the sequence start is
-                        // read through an out-of-range offset: zero, no access), and
-                        // the convolved rows from gbase to the sequence end
-                        const Stream sx{static_cast<const char*>(t == 0 ? a.conv_xq : a.conv_xk) + off +
-                                            (gbase - 4) * row_bytes,
-                                        (len - gbase + 4) * row_bytes};
-                        const Stream sy{static_cast<const char*>(t == 0 ? a.q : a.k) + off + gbase * row_bytes,
-                                        (len - gbase) * row_bytes};
-                        const __amdgpu_buffer_rsrc_t rx = stream_rsrc(sx);
-                        const __amdgpu_buffer_rsrc_t ry = stream_rsrc(sy);
-#pragma unroll 1
-                        for (int hf = 0; hf < 2; ++hf) {
-                            const int c0 = 16 * pc + 8 * hf;   // byte offset in the row
-                            u32x2 xr[7];                       // rows lrow-3 .. lrow+3 of the group
-#pragma unroll
-                            for (int j = 0; j < 7; ++j) {
-                                const bool before = gbase + lrow - 3 + j < 0;
-                                const int voff = before ? (int)0x80000000u : (lrow + 1 + j) * (int)row_bytes + c0;
-                                xr[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, voff, 0, 0));
-                            }
-                            f32x4 wt[4];
-#pragma unroll
-                            for (int c = 0; c < 4; ++c) wt[c] = reinterpret_cast<const f32x4*>(wtt)[ch + 4 * hf + c];
-                            f32x4 hw[3];   // x[r-3], x[r-2], x[r-1]
-#pragma unroll
-                            for (int j = 0; j < 3; ++j) {
-                                const int64_t rr = gbase + lrow - 3 + j;
-                                hw[j] = (rr < 0 && s0t)
-                                            ? *reinterpret_cast<const f32x4*>(
-                                                  s0t + ((int64_t)n * 3 + (3 + rr)) * ((int64_t)a.H * kDK) + ch + 4 * hf)
-                                            : unpack4(xr[j][0], xr[j][1]);
-                            }
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const f32x4 xi = unpack4(xr[3 + i][0], xr[3 + i][1]);
-                                f32x4 yo;
-#pragma unroll
-                                for (int c = 0; c < 4; ++c) yo[c] = conv_tap4(wt[c], hw[0][c], hw[1][c], hw[2][c], xi[c], a.conv_act);
-                                hw[0] = hw[1];
-                                hw[1] = hw[2];
-                                hw[2] = xi;
-                                // (rows past the sequence end fall outside the store range)
-                                __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2_bf16(yo[0], yo[1]), pack2_bf16(yo[2], yo[3])},
-                                                                      ry, (lrow + i) * (int)row_bytes + c0, 0, 0);
-                            }
-                        }
-                    }
-                }
-                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the stores are in L2 before the barrier
-                __builtin_amdgcn_s_setprio(2);
-            }
-        };
         // v is convolved in place at the end of the period that loaded it, off the state chain
         auto conv_v = [&](int gi, StateIn& V) {
             if constexpr (kConv) {
                 __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(0);   // below the preparation waves: it fills their idle issue slots
                 f32x4 wv[4];   // this lane's v taps (reloaded each group: fewer registers held)
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc)
-                    wv[cc] = reinterpret_cast<const f32x4*>(a.conv_w[2])[(int64_t)h * kDV + col0 + 4 * (lane & 3) + cc];
-                V = conv_v_group(V, hv, wv, a.conv_act, (int64_t)gi * (kNA * kC), len, lane);
+                    wv[cc] = reinterpret_cast<const f32x4*>(a.conv_wv)[(int64_t)h * kDV + col0 + 4 * lg + cc];
+                V = conv_v_group(V, hv, wv, a.conv_act, (int64_t)gi * (kNA * kC), len, li, gaddr);
+                __builtin_amdgcn_s_setprio(2);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        if constexpr (kConv) {
-            conv_qk(0);
-            conv_qk(1);
-            group_barrier();
-        }
         // iteration it loads group it and consumes group it-1
         load_group(VA);
-        conv_qk(2);
         conv_v(0, VA);
         group_barrier();
         int it = 1;
         for (; it + 1 <= ngroups; it += 2) {
             load_group(VB);
             consume(it - 1, VA);
-            conv_qk(it + 2);
             conv_v(it, VB);
             group_barrier();
             load_group(VA);
             consume(it, VB);
-            conv_qk(it + 3);
             conv_v(it + 1, VA);
             group_barrier();
         }
         if (it <= ngroups) {
             load_group(VB);
             consume(it - 1, VA);
-            conv_qk(it + 2);
             conv_v(it, VB);
             group_barrier();
         }

@@ -307,19 +307,22 @@ kda_status kda_chunk_fwd_conv(const void* xq, const void* xk, const void* xv, co
     }
     hipError_t e = hipSuccess;
     if (fused) {
-        // one kernel: the state waves convolve q, k (into the workspace) and v
-        a.conv = true;
-        a.conv_xq = xq;
-        a.conv_xk = xk;
-        a.q = ws;
-        a.k = ws + rows * Dk * 2;
-        a.v = xv;
-        for (int t = 0; t < 3; ++t) {
-            a.conv_w[t] = wts[t];
-            a.conv_s0[t] = s0s[t];
+        // q and k by the streaming convolution into the workspace; v is
+        // convolved inside the chunk kernel by its state waves
+        for (int t = 0; t < 2 && e == hipSuccess && T > 0; ++t) {
+            kda::ConvArgs ct = c[t];
+            ct.y = ws + t * rows * Dk * 2;
+            ct.state_out = nullptr;
+            e = kda::launch_short_conv(ct, s);
         }
+        a.q = T > 0 ? ws : nullptr;
+        a.k = T > 0 ? ws + rows * Dk * 2 : nullptr;
+        a.v = xv;
+        a.conv = true;
+        a.conv_wv = wv;
+        a.conv_sv = conv_state_v;
         a.conv_act = activation == 1;
-        if ((int64_t)a.N * a.H > 0) {
+        if (e == hipSuccess && (int64_t)a.N * a.H > 0) {
             const kda_status ss = attach_status(fn, a);
             if (ss != KDA_OK) return ss;
             e = kda::launch_chunk_mfma(a, s);

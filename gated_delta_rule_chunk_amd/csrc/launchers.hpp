@@ -33,14 +33,11 @@ struct ChunkArgs {
     // word that counts give-ups (set by the C ABI for every launch)
     int spin_limit = 1 << 22;
     unsigned int* status = nullptr;
-    // short convolution of q, k and v fused in (kda_chunk_fwd_conv; bf16,
-    // Dk = Dv = 128, with the prologue): v is the raw projection, q and k point
-    // at the workspace that the kernel fills with the convolved q and k
+    // short convolution of v fused in (kda_chunk_fwd_conv; bf16, Dk = Dv = 128,
+    // with the prologue): v is the raw projection
     bool conv = false;
-    const void* conv_xq = nullptr;   // raw q and k projections [B,T,H,Dk]
-    const void* conv_xk = nullptr;
-    const float* conv_w[3] = {};     // taps of q, k, v: [H*D][4]
-    const float* conv_s0[3] = {};    // conv states of q, k, v: [N][3][H*D], or null (zeros)
+    const float* conv_wv = nullptr;  // taps of v: [H*Dv][4]
+    const float* conv_sv = nullptr;  // conv state of v: [N][3][H*Dv], or null (zeros)
     bool conv_act = false;           // SiLU after the convolution
 };
 

@@ -127,7 +127,7 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
 /*
  * Bytes of device workspace kda_chunk_fwd_conv needs (0 for T = 0 or
  * out-of-range sizes): for bf16 with Dk = Dv = 128 and gate_lower_bound >= -5
- * (the fused kernel) the convolved q and k, 2 x B*T*H*Dk bf16; otherwise the
+ * (v convolved in the chunk kernel) the convolved q and k, 2 x B*T*H*Dk bf16; otherwise the
  * three convolved projections, B*T*H*(2 Dk + Dv) elements of dtype.
  */
 size_t kda_chunk_fwd_conv_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, kda_dtype dtype,
@@ -143,13 +143,12 @@ size_t kda_chunk_fwd_conv_workspace_bytes(int32_t B, int32_t T, int32_t H, int32
  * kda_chunk_fwd_prologue on the convolved q, k and v. The result equals that
  * sequence of calls (bit for bit on the fused path).
  *
- * For bf16 with Dk = Dv = 128 and gate_lower_bound >= -5 this is one kernel:
- * the state waves of the chunk kernel, idle for part of every group, convolve
- * v in registers right before using it and convolve q and k two groups ahead
- * into the workspace, from which the preparation waves load them (the
- * convolved q and k are written once and read back from L2; nothing else of
- * the convolution touches HBM). Every other supported shape runs the three
- * convolutions into the workspace, then the prologue forward.
+ * For bf16 with Dk = Dv = 128 and gate_lower_bound >= -5, the convolution of
+ * v runs inside the chunk kernel: its state waves, idle for part of every
+ * group, convolve each group of v in registers as it arrives (the convolved v
+ * never goes to memory); q and k are convolved into the workspace by the
+ * streaming convolution kernel first. Every other supported shape runs the
+ * three convolutions into the workspace, then the prologue forward.
  *
  *   xq, xk [B,T,H,Dk], xv [B,T,H,Dv]  dtype: the projections before the convolution
  *   wq, wk [H*Dk][4], wv [H*Dv][4]     float32 taps (16-byte aligned rows)
