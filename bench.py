@@ -21,8 +21,8 @@ over its average launch time, measured with HIP events on the launch stream.
 ``prologue`` times the same forward from raw projections with the gate, beta
 and L2-normalisation prologue fused into the chunk kernel
 (kda_chunk_fwd_prologue). ``short_conv`` times the kernel-4 convolution of the
-q, k and v projections (kda_short_conv) and the chain convolution ->
-prologue forward. ``mfma`` gives the same launches against the bf16 dense matrix-core peak with
+q, k and v projections (kda_short_conv), the chain convolution ->
+prologue forward, and the same chain as one call (kda_chunk_fwd_conv, ``fused``). ``mfma`` gives the same launches against the bf16 dense matrix-core peak with
 the algorithmic flop count of the chunk form at C=64 counted over full tiles,
 a fixed count that does not depend on the chunk size the kernel uses. ``backward`` times kda_chunk_bwd on
 the same workload with output and final-state cotangents, against the fp32
@@ -257,6 +257,15 @@ def bench_conv(steps, warmup):
         kda.chunk_fwd_prologue(ys[0], ys[1], ys[2], d["g_logit"], d["beta_logit"], d["A_log"], d["dt_bias"],
                                gate_lower_bound=synth.GATE_LOWER_BOUND, l2_eps=1e-6, out=o, final_state=fin)
 
+    ws_f = torch.empty((kda.chunk_fwd_conv_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, torch.bfloat16,
+                                                           synth.GATE_LOWER_BOUND),), dtype=torch.uint8, device=dev)
+
+    def fused(i):
+        d = sets[i % 2]
+        kda.chunk_fwd_conv(d["q_raw"], d["k_raw"], d["v"], *weights, d["g_logit"], d["beta_logit"], d["A_log"],
+                           d["dt_bias"], activation=True, gate_lower_bound=synth.GATE_LOWER_BOUND, l2_eps=1e-6,
+                           out=o, final_state=fin, conv_states_out=states, workspace=ws_f)
+
     # backward of the three convolutions: fp32 cotangents of y, gradients of x, the taps and the initial state
     gen = torch.Generator(device="cpu").manual_seed(w.seed + 11)
     dys = [torch.randn((w.B, w.T, C), generator=gen).to(dev) for _ in range(3)]
@@ -272,9 +281,12 @@ def bench_conv(steps, warmup):
 
     _, conv_per, conv_ms = time_launches(conv, steps, warmup, stream)
     wall, chain_per, _ = time_launches(chain, steps, warmup, stream)
-    _, bwd_per, bwd_ms = time_launches(conv_bwd, steps, warmup, stream)
     if not (torch.isfinite(o.float()).all() and torch.isfinite(fin).all()):
         raise RuntimeError("non-finite conv chain output")
+    wall_f, fused_per, _ = time_launches(fused, steps, warmup, stream)
+    _, bwd_per, bwd_ms = time_launches(conv_bwd, steps, warmup, stream)
+    if not (torch.isfinite(o.float()).all() and torch.isfinite(fin).all()):
+        raise RuntimeError("non-finite fused conv forward output")
     if not all(torch.isfinite(t).all() for g in grads.values() for t in g if t is not None):
         raise RuntimeError("non-finite conv backward output")
     # per projection: x (2 B) and dy (4 B) read, dx (4 B) written per token-channel, the taps and their
@@ -295,6 +307,10 @@ def bench_conv(steps, warmup):
             "chain": {"steps": "conv of q, k, v then the fused-prologue forward",
                       "ms_per_step": wall / steps * 1e3, "ms_median": float(np.median(chain_per)),
                       "tokens_per_s": w.T / (wall / steps)},
+            "fused": {"steps": "kda_chunk_fwd_conv: the same chain in one call (v convolved inside the chunk "
+                                "kernel, q and k by the streaming convolution), final conv states included",
+                      "ms_per_step": wall_f / steps * 1e3, "ms_median": float(np.median(fused_per)),
+                      "tokens_per_s": w.T / (wall_f / steps)},
             "backward": {"steps": "kda_short_conv_bwd of q, k, v (fp32 dy; dx, dweight, d_state)",
                          "ms_per_step": float(bwd_ms), "ms_median": float(np.median(bwd_per)),
                          "roofline": {"bound": "hbm", "achieved": bwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -661,32 +661,48 @@ __device__ __forceinline__ f32x4 unpack4(uint32_t lo, uint32_t hi) {
     return f32x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u), __uint_as_float(hi << 16),
                  __uint_as_float(hi & 0xffff0000u)};
 }
-__device__ __forceinline__ float bperm_f(float x, int addr) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
-}
 
-// 32-bit value of lane li - k (row_shr) or li + m (row_shl) of this lane's
-// 16-lane row; lanes whose source lies outside the row get 0
+// DPP row shifts of a 32-bit value within this lane's 16-lane row.
+// row_shr_into: lane li takes lane li - K, and lanes li < K keep `old`.
+// row_shl_any: lane li takes lane li + M (lanes past the row end read 0).
 template <int K>
-__device__ __forceinline__ uint32_t row_shr(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x110 + K, 0xf, 0xf, false);
+__device__ __forceinline__ uint32_t row_shr_into(uint32_t old, uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, 0x110 + K, 0xf, 0xf, false);
 }
 template <int M>
-__device__ __forceinline__ uint32_t row_shl(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x100 + M, 0xf, 0xf, false);
+__device__ __forceinline__ uint32_t row_shl_any(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x100 + M, 0xf, 0xf, true);
+}
+// the value of lane C of this lane's quad
+template <int C>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(x), 0x55 * C, 0xf, 0xf, true));
 }
 
 // v of one group, convolved on its way to the matrix-core operand order.
 // raw: the state waves' load order (lane L: row L/4 of each chunk, columns
 // 4(L%4)..+3 of the wave's 16); the result is in operand order (lane (li, lg):
-// row li, columns 4lg..+3), where row li - k of a chunk sits k lanes down the
+// row li, columns 4lg..+3). There row li - k of a chunk sits k lanes down the
 // same 16-lane row and, for li < k, row 16 + li - k of the chunk before sits
-// 16 - k lanes up: DPP row shifts, no cross-row traffic. hv holds this lane's
-// row of "chunk -1" (the previous group's chunk 3, or the conv state before the
-// sequence start) in operand order as floats, and is advanced to this group's
-// chunk 3.
-__device__ __forceinline__ u32x8 conv_v_group(const u32x8& raw, f32x4& hv, const f32x4 (&wv)[4], bool act,
-                                              int64_t row0, int64_t len, int li, int gaddr) {
+// 16 - k lanes up, so two DPP row shifts of a bf16 pair word give the word of
+// row li - k, across the chunk boundary included. hw: this lane's words of
+// "chunk -1" (the previous group's chunk 3), advanced to this group's chunk 3.
+// The first group (kFirst) takes chunk -1 from hf instead: the conv state
+// before the sequence start in float32 (rows 13..15; zero without a state),
+// in operand order.
+template <bool kFirst>
+__device__ __forceinline__ u32x8 conv_v_group(const u32x8& raw, u32x2& hw, const f32x4& hf, const f32x4& tq,
+                                              bool act, int64_t row0, int64_t len, int li, int gaddr) {
+    // taps of channel 4lg + cc: lane cc of the quad holds them
+    f32x4 wv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float t = tq[j];   // (through a scalar: see the note on hf below)
+        wv[0][j] = quad_bcast<0>(t);
+        wv[1][j] = quad_bcast<1>(t);
+        wv[2][j] = quad_bcast<2>(t);
+        wv[3][j] = quad_bcast<3>(t);
+    }
     u32x8 op;
 #pragma unroll
     for (int j = 0; j < 2 * kNA; ++j) op[j] = gather(raw[j], gaddr);
@@ -694,36 +710,39 @@ __device__ __forceinline__ u32x8 conv_v_group(const u32x8& raw, f32x4& hv, const
 #pragma unroll
     for (int s = 0; s < kNA; ++s) {
         const f32x4 cur = unpack4(op[2 * s], op[2 * s + 1]);
+        const uint32_t p0 = s == 0 ? hw[0] : op[2 * s - 2];
+        const uint32_t p1 = s == 0 ? hw[1] : op[2 * s - 1];
         f32x4 xm[3];   // rows li-1, li-2, li-3
         auto shifted = [&](auto kc) {
             constexpr int k = decltype(kc)::value;
-            const f32x4 fc = unpack4(row_shr<k>(op[2 * s]), row_shr<k>(op[2 * s + 1]));
-            f32x4 fp;
-            if (s == 0) {
+            if (kFirst && s == 0) {
+                const f32x4 fc = unpack4(row_shr_into<k>(0u, op[0]), row_shr_into<k>(0u, op[1]));
+                f32x4 fp;
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) {
-                    // (hv[cc] goes through a scalar first: clang's __builtin_bit_cast of a
+                    // (hf[cc] goes through a scalar first: clang's __builtin_bit_cast of a
                     // vector element reads element 0 whatever the index)
-                    const float h = hv[cc];
-                    fp[cc] = __uint_as_float(row_shl<16 - k>(__float_as_uint(h)));
+                    const float h = hf[cc];
+                    fp[cc] = __uint_as_float(row_shl_any<16 - k>(__float_as_uint(h)));
                 }
+                xm[k - 1] = li >= k ? fc : fp;
             } else {
-                fp = unpack4(row_shl<16 - k>(op[2 * s - 2]), row_shl<16 - k>(op[2 * s - 1]));
+                xm[k - 1] = unpack4(row_shr_into<k>(row_shl_any<16 - k>(p0), op[2 * s]),
+                                    row_shr_into<k>(row_shl_any<16 - k>(p1), op[2 * s + 1]));
             }
-            xm[k - 1] = li >= k ? fc : fp;
         };
         shifted(std::integral_constant<int, 1>{});
         shifted(std::integral_constant<int, 2>{});
         shifted(std::integral_constant<int, 3>{});
         f32x4 y;
-        const bool live = row0 + kC * s + li < len;
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-            y[cc] = live ? conv_tap4(wv[cc], xm[2][cc], xm[1][cc], xm[0][cc], cur[cc], act) : 0.f;
-        out[2 * s] = pack2_bf16(y[0], y[1]);
-        out[2 * s + 1] = pack2_bf16(y[2], y[3]);
+        for (int cc = 0; cc < 4; ++cc) y[cc] = conv_tap4(wv[cc], xm[2][cc], xm[1][cc], xm[0][cc], cur[cc], act);
+        // rows at or past the sequence end are zero
+        const uint32_t keep = row0 + kC * s + li < len ? ~0u : 0u;
+        out[2 * s] = pack2_bf16(y[0], y[1]) & keep;
+        out[2 * s + 1] = pack2_bf16(y[2], y[3]) & keep;
     }
-    hv = unpack4(op[6], op[7]);
+    hw = u32x2{op[6], op[7]};
     return out;
 }
 
@@ -964,14 +983,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         // the sequence end holds zero tokens, which leave the state unchanged,
         // and its output stores fall outside the store buffer's range, so the
         // hardware drops them. so stands at group gi.
-        // fused convolution: the row before each chunk of v (this lane's columns)
-        f32x4 hv = zero4();
-        if constexpr (kConv) {
-            // rows 13..15 of "chunk -1" are x[-3..-1]: the conv state (operand order)
-            if (a.conv_sv && li >= 13)
-                hv = *reinterpret_cast<const f32x4*>(a.conv_sv + ((int64_t)n * 3 + (li - 13)) * ((int64_t)a.H * kDV) +
-                                                     (int64_t)h * kDV + col0 + 4 * lg);
-        }
+        // fused convolution: this lane's row of the chunk before the next group of
+        // v, and the four taps of channel col0 + 4lg + li%4 (the other lanes of the
+        // quad hold the rest of the lane's channels)
+        u32x2 hw = {0u, 0u};
+        f32x4 tq = zero4();
+        if constexpr (kConv) tq = reinterpret_cast<const f32x4*>(a.conv_wv)[(int64_t)h * kDV + col0 + 4 * lg + (li & 3)];
         auto consume_words = [&](int gi, const StateIn& vcur) {
             const __amdgpu_buffer_rsrc_t ro = stream_rsrc(so);
             stream_advance(so, vstride);
@@ -1043,38 +1060,45 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         };
         auto consume = [&](int gi, const StateIn& v) { consume_words(gi, v); };
         // v is convolved in place at the end of the period that loaded it, off the state chain
-        auto conv_v = [&](int gi, StateIn& V) {
+        auto conv_v = [&](auto first, int gi, StateIn& V) {
             if constexpr (kConv) {
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_setprio(0);   // below the preparation waves: it fills their idle issue slots
-                f32x4 wv[4];   // this lane's v taps (reloaded each group: fewer registers held)
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc)
-                    wv[cc] = reinterpret_cast<const f32x4*>(a.conv_wv)[(int64_t)h * kDV + col0 + 4 * lg + cc];
-                V = conv_v_group(V, hv, wv, a.conv_act, (int64_t)gi * (kNA * kC), len, li, gaddr);
+                f32x4 hf = zero4();
+                if constexpr (decltype(first)::value) {
+                    // rows 13..15 of "chunk -1" are x[-3..-1]: the conv state (operand order)
+                    if (a.conv_sv && li >= 13)
+                        hf = *reinterpret_cast<const f32x4*>(a.conv_sv +
+                                                             ((int64_t)n * 3 + (li - 13)) * ((int64_t)a.H * kDV) +
+                                                             (int64_t)h * kDV + col0 + 4 * lg);
+                }
+                V = conv_v_group<decltype(first)::value>(V, hw, hf, tq, a.conv_act, (int64_t)gi * (kNA * kC), len, li,
+                                                         gaddr);
                 __builtin_amdgcn_s_setprio(2);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
+        const std::true_type first_group;
+        const std::false_type later_group;
         // iteration it loads group it and consumes group it-1
         load_group(VA);
-        conv_v(0, VA);
+        conv_v(first_group, 0, VA);
         group_barrier();
         int it = 1;
         for (; it + 1 <= ngroups; it += 2) {
             load_group(VB);
             consume(it - 1, VA);
-            conv_v(it, VB);
+            conv_v(later_group, it, VB);
             group_barrier();
             load_group(VA);
             consume(it, VB);
-            conv_v(it + 1, VA);
+            conv_v(later_group, it + 1, VA);
             group_barrier();
         }
         if (it <= ngroups) {
             load_group(VB);
             consume(it - 1, VA);
-            conv_v(it, VB);
+            conv_v(later_group, it, VB);
             group_barrier();
         }
         if (a.sT) {
