@@ -199,15 +199,15 @@ __device__ __forceinline__ void decay_state(f32x4 (&D)[8], const f32x4 (&S)[8], 
     }
 }
 
-// Block index -> work item: the two column halves of one (sequence, head) land
+// Block index -> work item: the ipu column blocks of one (sequence, head) land
 // on the same XCD (blocks are dealt round-robin over the 8 XCDs) and are
 // dispatched together, so that XCD's L2 serves their shared q, k, g once.
-__device__ __forceinline__ int remap_block(int b, int units) {
-    const int per = 8 * kNVT;
+__device__ __forceinline__ int remap_block(int b, int units, int ipu) {
+    const int per = 8 * ipu;
     const int full = (units / 8) * per;
     if (b >= full) return b;
     const int grp = b / per, rem = b % per;
-    return (grp * 8 + (rem & 7)) * kNVT + (rem >> 3);
+    return (grp * 8 + (rem & 7)) * ipu + (rem >> 3);
 }
 
 // Buffer descriptors: accesses outside [base, base + num_records) read 0 and
@@ -756,24 +756,36 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
     const int units = a.N * a.H;
 
     // ---- work item ----------------------------------------------------------
-    const int wi = remap_block(blockIdx.x, units);
-    const int unit = wi / kNVT, vt = wi % kNVT;
+    const int ipu = a.aug ? 2 * kNVT : kNVT;   // column blocks per (sequence, head)
+    const int wi = remap_block(blockIdx.x, units, ipu);
+    const int unit = wi / ipu;
+    // the split's A pass (second column set of an augmented launch): v = 0
+    // from the identity entry states into A
+    const bool apass = wi % ipu >= kNVT;
+    const int vt = wi % ipu - (apass ? kNVT : 0);
+    const void* const vin = apass ? nullptr : a.v;
+    const float* const s0 = apass ? a.aug_s0 : a.s0;
+    float* const sT = apass ? a.aug_sT : a.sT;
     int n = unit / a.H;
     const int h = unit % a.H;
-    if (a.cu && a.N <= 256) {
-        // packed batch: the rank-n longest sequence (ties by index) goes first
+    if (a.cu) {
+        // packed batch: blocks are dispatched in index order, so within each run
+        // of 256 consecutive sequences the longest (ties by index) goes first and
+        // every run ends with its shortest; the work of the ranking stays at 256
+        // comparisons per thread however many sequences there are
+        const int base = n & ~255, r = n & 255, cnt = min(256, a.N - base);
         int* lens = reinterpret_cast<int*>(smem);
         int* pick = lens + 256;
-        if (tid < a.N) lens[tid] = a.cu[tid + 1] - a.cu[tid];
+        if (tid < cnt) lens[tid] = a.cu[base + tid + 1] - a.cu[base + tid];
         __syncthreads();
-        if (tid < a.N) {
+        if (tid < cnt) {
             const int my = lens[tid];
             int rank = 0;
-            for (int s = 0; s < a.N; ++s) {
+            for (int s = 0; s < cnt; ++s) {
                 const int ls = lens[s];
                 rank += (ls > my) || (ls == my && s < tid);
             }
-            if (rank == n) *pick = tid;
+            if (rank == r) *pick = base + tid;
         }
         __syncthreads();
         n = *pick;
@@ -942,7 +954,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                S[rt][j] = a.s0 ? a.s0[state_base + (int64_t)(16 * rt + 4 * lg + j) * kDV + col0 + li] : 0.f;
+                S[rt][j] = s0 ? s0[state_base + (int64_t)(16 * rt + 4 * lg + j) * kDV + col0 + li] : 0.f;
 
         bf16x8 eyeV;   // [slot 8lg+s][column li] = (s < 4 && 4lg+s == li)
 #pragma unroll
@@ -955,7 +967,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         const int64_t vrow_bytes = (int64_t)a.H * (kDV * 2);          // one token of v or o
         const int64_t head0 = (tok_base * a.H + h) * (int64_t)(kDV * 2) + col0 * 2;
         // a null v reads as zeros and a null o drops the outputs (empty buffer ranges)
-        Stream sv{a.v ? static_cast<const char*>(a.v) + head0 : nullptr, a.v ? len * vrow_bytes - col0 * 2 : 0};
+        Stream sv{vin ? static_cast<const char*>(vin) + head0 : nullptr, vin ? len * vrow_bytes - col0 * 2 : 0};
         Stream so{a.o ? static_cast<const char*>(a.o) + head0 : nullptr, a.o ? len * vrow_bytes - col0 * 2 : 0};
         const int64_t vstride = (int64_t)kNA * kC * vrow_bytes;
         // load/store order: row lane/4 of chunk s, columns 4(lane%4)..+3 of
@@ -1101,12 +1113,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
             conv_v(later_group, it, VB);
             group_barrier();
         }
-        if (a.sT) {
+        if (sT) {
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    a.sT[state_base + (int64_t)(16 * rt + 4 * lg + j) * kDV + col0 + li] = S[rt][j];
+                    sT[state_base + (int64_t)(16 * rt + 4 * lg + j) * kDV + col0 + li] = S[rt][j];
         }
     }
 }
@@ -1121,7 +1133,7 @@ bool chunk_mfma_supported(const ChunkArgs& a) {
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t s) {
     const int units = a.N * a.H;
-    const dim3 grid((unsigned)(units * kNVT));
+    const dim3 grid((unsigned)(units * (a.aug ? 2 * kNVT : kNVT)));
     if (a.conv)
         hipLaunchKernelGGL((chunk_mfma_kernel<true, true>), grid, dim3(kThreads), 0, s, a);
     else if (a.prologue)

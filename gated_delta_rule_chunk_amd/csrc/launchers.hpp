@@ -39,6 +39,13 @@ struct ChunkArgs {
     const float* conv_wv = nullptr;  // taps of v: [H*Dv][4]
     const float* conv_sv = nullptr;  // conv state of v: [N][3][H*Dv], or null (zeros)
     bool conv_act = false;           // SiLU after the convolution
+    // the split's A and B passes in one launch (bf16, Dk = Dv = 128): every
+    // (sequence, head) gets twice the column blocks. The first set runs with v
+    // from s0 into sT (B: s0 is null), the second with v = 0 from aug_s0 into
+    // aug_sT (A: identity entry states). No outputs are written (o is null).
+    bool aug = false;
+    const float* aug_s0 = nullptr;
+    float* aug_sT = nullptr;
 };
 
 // The device status word of the current device and the poll limit of every
@@ -181,7 +188,7 @@ hipError_t launch_short_conv_bwd(const ConvBwdArgs& a, hipStream_t s);
 hipError_t launch_short_conv(const ConvArgs& a, hipStream_t s);
 hipError_t launch_short_conv_step(const ConvStepArgs& a, hipStream_t s);
 
-hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t s);     // bf16, Dk=Dv=128, chunk 64
+hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t s);     // bf16, Dk=Dv=128, 16-row chunks
 hipError_t launch_chunk_generic(const ChunkArgs& a, hipStream_t s);  // any supported dims
 hipError_t launch_recurrent_step(const StepArgs& a, hipStream_t s);
 

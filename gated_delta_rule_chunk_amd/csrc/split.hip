@@ -246,15 +246,25 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
     p1.s0 = nullptr;
     p1.sT = Bst;
     p1.o = nullptr;
-    if ((e = chunk_forward(p1, s)) != hipSuccess) return e;
-    // 2. A: identity entry states, v = 0 (read from an empty range), d_v = d_k, no outputs
-    ChunkArgs p2 = seg;
-    p2.v = nullptr;
-    p2.Dv = a.Dk;
-    p2.s0 = AI;
-    p2.sT = AI;   // each state tile is read before it is written
-    p2.o = nullptr;
-    if ((e = chunk_forward(p2, s)) != hipSuccess) return e;
+    if (chunk_mfma_supported(p1)) {
+        // 1 and 2 in one launch over the augmented state [B | A]: the column
+        // blocks of A run beside those of B on the same XCD, so q, k, g and beta
+        // come from HBM once for both
+        p1.aug = true;
+        p1.aug_s0 = AI;
+        p1.aug_sT = AI;   // each state tile is read before it is written
+        if ((e = launch_chunk_mfma(p1, s)) != hipSuccess) return e;
+    } else {
+        if ((e = chunk_forward(p1, s)) != hipSuccess) return e;
+        // 2. A: identity entry states, v = 0 (read from an empty range), d_v = d_k, no outputs
+        ChunkArgs p2 = seg;
+        p2.v = nullptr;
+        p2.Dv = a.Dk;
+        p2.s0 = AI;
+        p2.sT = AI;   // each state tile is read before it is written
+        p2.o = nullptr;
+        if ((e = chunk_forward(p2, s)) != hipSuccess) return e;
+    }
     // 3. entry states of every segment, and the final states
     switch (a.Dk) {
         case 16: split_scan_kernel<16><<<dim3((unsigned)(a.N * a.H * (a.Dv / 16))), dim3(256), 0, s>>>(

@@ -63,7 +63,10 @@ typedef enum {
  *                  Zero-length sequences are allowed: their final state equals
  *                  their initial state. Packed ("THD") batches are how the K3
  *                  package feeds variable-length sequences (ISEEKYAN/k3 README,
- *                  packed THD with context parallelism).
+ *                  packed THD with context parallelism). The bf16 matrix-core
+ *                  kernel starts the longest sequence of each run of 256
+ *                  consecutive sequences first (scheduling only: results do
+ *                  not depend on it).
  *   chunk_size     0 for the kernel's own chunk length, or an explicit
  *                  length. It changes only rounding. The bf16 matrix-core
  *                  kernel (Dk = Dv = 128) works in 16-row chunks only: there

@@ -57,6 +57,22 @@ def test_bf16_packed_ragged(H):
     _check(inp, TOL_BF16, label=f"bf16 packed H={H}")
 
 
+def test_bf16_packed_many_sequences():
+    """More than 256 packed sequences: the matrix-core kernel orders them by
+    length within runs of 256 (the last run partial); every sequence must still
+    be computed exactly once, so each one's final state is checked on its own."""
+    rng = np.random.default_rng(415)
+    lengths = [int(x) for x in rng.integers(0, 41, size=600)]
+    lengths[0], lengths[300], lengths[599] = 0, 97, 0
+    inp = synth.make_chunk_inputs(1, 0, 2, 128, 128, seed=415, dtype="bf16", init_state=True, lengths=lengths)
+    _check(inp, TOL_BF16, label="bf16 packed N=600")
+    o, fin = gpu_chunk(inp)
+    _, rfin = oracle_chunk(inp)
+    worst = max(rel(fin[n], rfin[n]) for n in range(len(lengths)))
+    say(f"        worst per-sequence final-state relL2 {worst:.3e}")
+    assert worst <= TOL_BF16
+
+
 def test_f32_packed_ragged():
     inp = synth.make_chunk_inputs(1, 0, 2, 32, 32, seed=410, dtype="f32", init_state=True,
                                   lengths=[5, 0, 33, 16])
