@@ -107,6 +107,37 @@ def read_traffic(key="traffic_bytes_per_launch"):
     return float(m_val.group(1))
 
 
+CSRC = os.path.join(ROOT, "gated_delta_rule_chunk_amd", "csrc")
+# per-leg counter summaries: (file, the kernel sources the figure depends on)
+LEG_TRAFFIC = {
+    "decode": ("recurrent_step_k3_decode_b256_traffic.md", ("recurrent_step.hip",)),
+    "short_conv": ("short_conv_k3_t4096_traffic.md", ("short_conv.hip",)),
+    "split": ("chunk_fwd_split_h12_t32768_traffic.md", ("split.hip", "chunk_mfma.hip")),
+}
+
+
+def leg_source_hash(leg):
+    h = hashlib.sha256()
+    for name in LEG_TRAFFIC[leg][1]:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_leg_traffic(leg, key="traffic_bytes_per_step"):
+    """HBM bytes per step of a secondary leg (decode, short_conv, split) from its
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the
+    current sources of its kernels; otherwise None."""
+    path = os.path.join(ROOT, "profiles", LEG_TRAFFIC[leg][0])
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"sources_sha256:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"(?m)^" + key + r":\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != leg_source_hash(leg):
+        return None
+    return float(m_val.group(1))
+
+
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "chunk_mfma_k3_t4096_mfma_counters.md")
 
 
@@ -302,7 +333,7 @@ def bench_conv(steps, warmup):
                         "with the final conv state",
             "ms_per_step": float(conv_ms), "ms_median": float(np.median(conv_per)),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": read_leg_traffic("short_conv")},
             "algorithmic_bytes_per_step": nbytes,
             "chain": {"steps": "conv of q, k, v then the fused-prologue forward",
                       "ms_per_step": wall / steps * 1e3, "ms_median": float(np.median(chain_per)),
@@ -314,7 +345,8 @@ def bench_conv(steps, warmup):
             "backward": {"steps": "kda_short_conv_bwd of q, k, v (fp32 dy; dx, dweight, d_state)",
                          "ms_per_step": float(bwd_ms), "ms_median": float(np.median(bwd_per)),
                          "roofline": {"bound": "hbm", "achieved": bwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": bwd_gbs / HBM_PEAK_GBS, "traffic": None},
+                                      "frac": bwd_gbs / HBM_PEAK_GBS,
+                                      "traffic": read_leg_traffic("short_conv", "bwd_traffic_bytes_per_step")},
                          "algorithmic_bytes_per_step": bwd_bytes}}
 
 
@@ -341,7 +373,7 @@ def bench_decode(steps, warmup):
     return {"workload": f"{cfg['name']}: batch {Nb}, H={H}, d_k=d_v={Dk}, bf16 q/k/v/g/beta, fp32 state cache",
             "ms_per_step": avg_ms, "ms_median": float(np.median(per)), "tokens_per_s": Nb / (avg_ms * 1e-3),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": read_leg_traffic("decode")},
             "algorithmic_bytes_per_step": step_bytes}
 
 
@@ -489,10 +521,10 @@ def bench_split(steps, warmup, segments=10):
             "tokens_per_s": T / (float(split_ms) * 1e-3),
             "unsplit_ms_per_step": float(plain_ms), "speedup_vs_unsplit": float(plain_ms) / float(split_ms),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": read_leg_traffic("split")},
             "algorithmic_bytes_per_step": nbytes,
-            "timed": "one kda_chunk_fwd_split call: offsets, zero and identity fills, three forward launches over "
-                     "the segments, the entry-state scan"}
+            "timed": "one kda_chunk_fwd_split call: offsets, identity fill, the A and B passes over the segments "
+                     "(one launch), the entry-state scan, the output pass"}
 
 
 def cpu_backward_baseline(heads=96):
@@ -575,7 +607,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-split", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["split", "backward", "conv"], default=None,
+    ap.add_argument("--only", choices=["split", "backward", "conv", "decode"], default=None,
                     help="run one secondary leg alone and print its JSON object (for per-kernel profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -592,7 +624,8 @@ def main():
     if args.only:
         legs = {"split": lambda: bench_split(args.steps, args.warmup),
                 "backward": lambda: bench_backward(args.steps, args.warmup, cpu=False),
-                "conv": lambda: bench_conv(args.steps, args.warmup)}
+                "conv": lambda: bench_conv(args.steps, args.warmup),
+                "decode": lambda: bench_decode(args.steps, args.warmup)}
         leg = legs[args.only]()
         print(json.dumps({"only": args.only, **leg}), flush=True)
         return

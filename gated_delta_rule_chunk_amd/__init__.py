@@ -281,7 +281,7 @@ def chunk_fwd_split(q, k, v, g, beta, segments, initial_state=None, cu_seqlens=N
     return out, final_state
 
 
-SPLIT_STATIC_SCRATCH_BYTES = 64 << 20   # KDA_SPLIT_STATIC_SCRATCH_BYTES
+SPLIT_STATIC_SCRATCH_BYTES = 128 << 20   # KDA_SPLIT_STATIC_SCRATCH_BYTES
 
 
 def chunk_fwd_split_static(q, k, v, g, beta, segments, initial_state=None, cu_seqlens=None, chunk_size=0,

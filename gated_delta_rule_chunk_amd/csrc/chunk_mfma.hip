@@ -763,9 +763,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
     // from the identity entry states into A
     const bool apass = wi % ipu >= kNVT;
     const int vt = wi % ipu - (apass ? kNVT : 0);
-    const void* const vin = apass ? nullptr : a.v;
-    const float* const s0 = apass ? a.aug_s0 : a.s0;
-    float* const sT = apass ? a.aug_sT : a.sT;
     int n = unit / a.H;
     const int h = unit % a.H;
     if (a.cu) {
@@ -805,6 +802,32 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
     const int nchunks = (int)((len + kC - 1) / kC);
     const int ngroups = (nchunks + kNA - 1) / kNA;
     const int64_t state_base = ((int64_t)n * a.H + h) * kDK * kDV;
+    const void* vin = a.v;
+    const float* s0 = a.s0;
+    int64_t s0_base = state_base;
+    float* sT = a.sT;
+    void* oout = a.o;
+    bool ident = false;   // entry state: the identity (the split's A pass)
+    if (a.aug) {
+        // segment p of sequence n / P. B runs from a zero entry state, except
+        // in a sequence's first segment, which starts from the sequence's
+        // initial state (so its outputs and final state are exact); A (not
+        // needed for p = 0) runs with v = 0 from the identity (formed here)
+        // and writes its outputs Aᵀq, from which the output pass corrects the
+        // others
+        const int p = n % a.aug_P;
+        if (apass && p == 0) return;   // the whole workgroup, before any barrier
+        if (apass) {
+            vin = nullptr;
+            s0 = nullptr;
+            ident = true;
+            sT = a.aug_sT;
+            oout = a.aug_o;
+        } else {
+            s0 = p == 0 ? a.aug_s0_first : nullptr;
+            s0_base = ((int64_t)(n / a.aug_P) * a.H + h) * kDK * kDV;
+        }
+    }
     // hand-over flags start below every step count (LDS holds stale data)
     if (tid < N_FLAGS) reinterpret_cast<int*>(smem + S_FLAG)[tid] = 0;
     __syncthreads();
@@ -954,7 +977,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                S[rt][j] = s0 ? s0[state_base + (int64_t)(16 * rt + 4 * lg + j) * kDV + col0 + li] : 0.f;
+                S[rt][j] = ident ? (16 * rt + 4 * lg + j == col0 + li ? 1.f : 0.f)
+                                 : s0 ? s0[s0_base + (int64_t)(16 * rt + 4 * lg + j) * kDV + col0 + li] : 0.f;
 
         bf16x8 eyeV;   // [slot 8lg+s][column li] = (s < 4 && 4lg+s == li)
 #pragma unroll
@@ -968,7 +992,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         const int64_t head0 = (tok_base * a.H + h) * (int64_t)(kDV * 2) + col0 * 2;
         // a null v reads as zeros and a null o drops the outputs (empty buffer ranges)
         Stream sv{vin ? static_cast<const char*>(vin) + head0 : nullptr, vin ? len * vrow_bytes - col0 * 2 : 0};
-        Stream so{a.o ? static_cast<const char*>(a.o) + head0 : nullptr, a.o ? len * vrow_bytes - col0 * 2 : 0};
+        Stream so{oout ? static_cast<char*>(oout) + head0 : nullptr, oout ? len * vrow_bytes - col0 * 2 : 0};
         const int64_t vstride = (int64_t)kNA * kC * vrow_bytes;
         // load/store order: row lane/4 of chunk s, columns 4(lane%4)..+3 of
         // this wave's 16; gathers move to and from the operand order

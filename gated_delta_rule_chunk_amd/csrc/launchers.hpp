@@ -39,13 +39,17 @@ struct ChunkArgs {
     const float* conv_wv = nullptr;  // taps of v: [H*Dv][4]
     const float* conv_sv = nullptr;  // conv state of v: [N][3][H*Dv], or null (zeros)
     bool conv_act = false;           // SiLU after the convolution
-    // the split's A and B passes in one launch (bf16, Dk = Dv = 128): every
-    // (sequence, head) gets twice the column blocks. The first set runs with v
-    // from s0 into sT (B: s0 is null), the second with v = 0 from aug_s0 into
-    // aug_sT (A: identity entry states). No outputs are written (o is null).
+    // the split's A and B passes in one launch (bf16, Dk = Dv = 128): the
+    // sequences are the segments, aug_P per original sequence, and every
+    // (segment, head) gets twice the column blocks. The first set runs with v
+    // from a zero entry state (aug_s0_first of the sequence in its first
+    // segment) into sT and o (B); the second, skipped in first segments, with
+    // v = 0 from the identity into aug_sT and aug_o (A).
     bool aug = false;
-    const float* aug_s0 = nullptr;
+    int32_t aug_P = 1;
+    const float* aug_s0_first = nullptr;   // [N / aug_P, H, Dk, Dv] or nullptr
     float* aug_sT = nullptr;
+    void* aug_o = nullptr;                 // like o, with Dk columns
 };
 
 // The device status word of the current device and the poll limit of every
@@ -161,13 +165,13 @@ hipError_t launch_prologue_bwd(const PrologueBwdArgs& p, const BwdArgs& core, hi
 
 // Workspace of the intra-sequence split (byte offsets, 256-aligned).
 struct SplitLayout {
-    int64_t seg_cu, ident, Bst, Sin, bytes;
+    int64_t seg_cu, ident, Bst, Sin, oA, bytes;
 };
 SplitLayout split_layout(const ChunkArgs& a, int32_t P);
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace, hipStream_t s);
 // The split's static scratch (kda_chunk_fwd_split_static): its size, and its
 // device address on the current device (nullptr if it cannot be looked up).
-constexpr size_t kSplitStaticScratchBytes = (size_t)64 << 20;
+constexpr size_t kSplitStaticScratchBytes = (size_t)128 << 20;
 void* split_static_scratch();
 
 // Backward of the short convolution: fwd holds the forward's arguments (x, w,

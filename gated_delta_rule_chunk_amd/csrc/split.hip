@@ -5,16 +5,25 @@
 // Over one segment the recurrence maps its entry state linearly plus a
 // constant: S_out = A S_in + B, where B is the segment's final state from a
 // zero entry state and A (d_k x d_k) is its final state from the identity
-// with v = 0. So one call runs:
-//   1. the forward over all segments from zero entry states: the B of every
-//      segment (its outputs are not used);
-//   2. the forward over all segments with v = 0 from identity entry states: A;
-//   3. split_scan_kernel: S_in(0) = the sequence's initial state,
-//      S_in(p) = A(p-1) S_in(p-1) + B(p-1), and the final state
-//      A(P-1) S_in(P-1) + B(P-1);
-//   4. the forward over all segments from S_in: the outputs, into o.
-// Passes 1, 2 and 4 are plain packed-sequence forward launches, so each of
-// them puts P times as many workgroups on the chip as the unsplit call.
+// with v = 0. The same holds row by row: the state after row t is
+// A_t S_in + B_t, so the output of row t is o_B(t) + S_inᵀ (scale A_tᵀ q_t),
+// and scale A_tᵀ q_t is the output of the A pass.
+//
+// bf16, d_k = d_v = 128 (the matrix-core kernel), one call runs:
+//   1. one launch over all segments with twice the column blocks: B from a
+//      zero entry state (the sequence's initial state in its first segment),
+//      writing its outputs into o, and A (segments p >= 1) from the identity
+//      with v = 0, writing its outputs scale A_tᵀ q_t into the workspace;
+//   2. split_scan_kernel: S_in(1) = B(0), S_in(p) = A(p-1) S_in(p-1) + B(p-1),
+//      and the final state A(P-1) S_in(P-1) + B(P-1);
+//   3. split_correct_kernel: o += S_in(p)ᵀ (scale A_tᵀ q_t) on the rows of
+//      segments p >= 1.
+// Every other shape runs three forward passes: B from zero entry states
+// (outputs discarded), A from the identity, the scan from the initial state,
+// then the forward over all segments from S_in, which writes o.
+// Each forward pass puts P times as many workgroups on the chip as the
+// unsplit call.
+#include <algorithm>
 #include <mutex>
 
 #include "device_common.hpp"
@@ -118,13 +127,17 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
                 for (int i = 0; i < 4; ++i) acc[t][i] = rbv[t][i];
             __syncthreads();
             issue(p + 1);
+            // from a zero initial state, S_in(1) = B(0): A(0) is not read (the
+            // bf16 split does not compute it)
+            if (p > 0 || s0) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int r0 = 16 * (2 * w + t);
+                for (int t = 0; t < 2; ++t) {
+                    const int r0 = 16 * (2 * w + t);
 #pragma unroll 8
-                for (int ks = 0; ks < DK / 4; ++ks)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[r0 + l16][4 * ks + lg], sS[4 * ks + lg][l16],
-                                                                  acc[t], 0, 0, 0);
+                    for (int ks = 0; ks < DK / 4; ++ks)
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[r0 + l16][4 * ks + lg],
+                                                                      sS[4 * ks + lg][l16], acc[t], 0, 0, 0);
+                }
             }
             __syncthreads();
 #pragma unroll
@@ -197,6 +210,127 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
     }
 }
 
+// The output pass of the bf16 d=128 split. Over segment p the state at row t
+// is S_t = A_t S_in(p) + B_t (A_t, B_t: the maps of the segment's rows up to
+// t), so its output is o_t = o_B(t) + S_in(p)ᵀ oA(t), where o_B is the output
+// from a zero entry state and oA(t) = scale A_tᵀ q_t the output of the A pass
+// (v = 0 from the identity, Dk columns). o holds o_B for every segment (exact
+// already in a sequence's first segment); this adds the second term to the
+// rows of segments p >= 1 and rounds once more to bf16.
+//
+// One workgroup of four waves per (segment, head, slice r of R): the 64-row
+// blocks r, r + R, ... of the segment; wave w takes output columns
+// 32w..32w+31 (two 16-column tiles). The products run on the matrix cores as
+// D = S_inᵀ oAᵀ (16x16x32 bf16): S_in split into bf16 hi + lo parts (float32
+// accuracy for the state) held in registers, oA exact (it is stored in bf16).
+// A block's oA rows (16 KB) go straight from global memory to LDS, once for
+// the four waves, in two buffers: block b+1 (and its o rows, into registers)
+// is loaded while block b is computed. In LDS, 16-byte piece c of row i sits
+// at position c ^ (i % 16) of the row, so the 16 rows that one operand read
+// touches fall in different banks.
+constexpr int kCorrBlockBytes = 64 * 256;
+__global__ __launch_bounds__(256, 2) void split_correct_kernel(const int32_t* seg_cu, int32_t P, int32_t H, int32_t R,
+                                                            const float* Sin, const __bf16* oA, __bf16* o) {
+    __shared__ __attribute__((aligned(16))) char buf[2][kCorrBlockBytes];
+    const int r = blockIdx.x % R;
+    const int unit = blockIdx.x / R;
+    const int seg = unit / H, h = unit % H;
+    if (seg % P == 0) return;                       // the whole workgroup
+    const int64_t bos = seg_cu[seg], eos = seg_cu[seg + 1];
+    if ((int64_t)r * 64 >= eos - bos) return;       // the whole workgroup
+    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
+    const int64_t rstride = (int64_t)H * 128;       // elements between consecutive rows of oA and o
+    // Issue block r0's loads: its oA rows into LDS buffer `bi` (wave w: rows
+    // 16w..16w+15, four rows per instruction; rows past the segment end read
+    // its last row) and this wave's o rows (row li of tile rt, columns
+    // 32w + 16t + 4lg..+3) into ob.
+    auto issue = [&](int64_t r0, int bi, uint2 (&ob)[4][2]) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = 16 * w + 4 * k + (lane >> 4);                  // row in the block
+            const int64_t row = r0 + i < eos ? r0 + i : eos - 1;
+            const int c = (lane & 15) ^ (i & 15);                          // piece this lane stores
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(oA + row * rstride + (int64_t)h * 128 + 8 * c),
+                (__attribute__((address_space(3))) void*)(buf[bi] + (16 * w + 4 * k) * 256), 16, 0, 0);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int64_t row = r0 + 16 * rt + li < eos ? r0 + 16 * rt + li : eos - 1;
+            const __bf16* o_row = o + row * rstride + (int64_t)h * 128 + 32 * w + 4 * lg;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) ob[rt][t] = *reinterpret_cast<const uint2*>(o_row + 16 * t);
+        }
+    };
+    // A operands: lane (li, lg) of column tile t, k-step ks holds
+    // S_in[32ks + 8lg + j][32w + 16t + li], j = 0..7
+    const float* S = Sin + ((int64_t)seg * H + h) * 128 * 128;
+    bf16x8 shi[2][4], slo[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = S[(int64_t)(32 * ks + 8 * lg + j) * 128 + 32 * w + 16 * t + li];
+                const __bf16 hi = (__bf16)x;
+                shi[t][ks][j] = hi;
+                slo[t][ks][j] = (__bf16)(x - (float)hi);
+            }
+    uint2 obA[4][2], obB[4][2];
+    auto compute = [&](int64_t r0, int bi, const uint2 (&ob)[4][2]) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            // B operand: row 16rt + li, channels 32ks + 8lg..+7 (piece 4ks + lg)
+            const int i = 16 * rt + li;
+            f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 b = *reinterpret_cast<const bf16x8*>(buf[bi] + i * 256 + 16 * ((4 * ks + lg) ^ li));
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(shi[t][ks], b, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(slo[t][ks], b, acc[t], 0, 0, 0);
+                }
+            }
+            // D: lane (li, lg) holds row li of the tile, columns 32w + 16t + 4lg + i
+            const int64_t row = r0 + i;
+            if (row < eos) {
+                __bf16* orow = o + row * rstride + (int64_t)h * 128 + 32 * w + 4 * lg;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const float y0 = __uint_as_float(ob[rt][t].x << 16) + acc[t][0];
+                    const float y1 = __uint_as_float(ob[rt][t].x & 0xffff0000u) + acc[t][1];
+                    const float y2 = __uint_as_float(ob[rt][t].y << 16) + acc[t][2];
+                    const float y3 = __uint_as_float(ob[rt][t].y & 0xffff0000u) + acc[t][3];
+                    *reinterpret_cast<uint2*>(orow + 16 * t) = uint2{pack2_bf16(y0, y1), pack2_bf16(y2, y3)};
+                }
+            }
+        }
+    };
+    // every wave runs the same block sequence, so the barriers match
+    const int64_t step = (int64_t)R * 64;
+    int64_t r0 = bos + (int64_t)r * 64;
+    issue(r0, 0, obA);
+    for (;;) {
+        // block r0 (buffer 0, obA) landed for every wave; buffer 1 is free
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __syncthreads();
+        const int64_t r1 = r0 + step;
+        if (r1 < eos) issue(r1, 1, obB);
+        compute(r0, 0, obA);
+        if (r1 >= eos) break;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        const int64_t r2 = r1 + step;
+        if (r2 < eos) issue(r2, 0, obA);
+        compute(r1, 1, obB);
+        if (r2 >= eos) break;
+        r0 = r2;
+    }
+}
+
 unsigned grid_for(int64_t n) {
     const int64_t b = (n + 255) / 256;
     return (unsigned)(b < 8192 ? (b > 0 ? b : 1) : 8192);
@@ -217,6 +351,8 @@ SplitLayout split_layout(const ChunkArgs& a, int32_t P) {
     L.ident = off;   off += up(segs * a.H * (int64_t)a.Dk * a.Dk * 4);          // identity entry states, then A
     L.Bst = off;     off += up(segs * a.H * (int64_t)a.Dk * a.Dv * 4);
     L.Sin = off;     off += up(segs * a.H * (int64_t)a.Dk * a.Dv * 4);
+    L.oA = off;
+    if (chunk_mfma_supported(a)) off += up((int64_t)a.B * a.T * a.H * a.Dk * 2);   // the A pass's outputs
     L.bytes = off;
     return L;
 }
@@ -233,8 +369,6 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
 
     split_offsets_kernel<<<dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, s>>>(a.cu, a.N, a.T, P, seg_cu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    fill_identity_kernel<<<dim3(grid_for(segs * a.H * a.Dk * a.Dk)), dim3(256), 0, s>>>(AI, segs * a.H, a.Dk);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     // the packed view of the input: one row of B*T tokens, N*P sequences
     ChunkArgs seg = a;
     seg.B = 1;
@@ -247,14 +381,33 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
     p1.sT = Bst;
     p1.o = nullptr;
     if (chunk_mfma_supported(p1)) {
-        // 1 and 2 in one launch over the augmented state [B | A]: the column
-        // blocks of A run beside those of B on the same XCD, so q, k, g and beta
-        // come from HBM once for both
+        // bf16, d = 128: the A and B passes in one launch, the column blocks of A
+        // beside those of B on the same XCD (q, k, g and beta come from HBM once
+        // for both). B writes o (exact in first segments, which start from the
+        // initial state, so their B is already S_in(1)); A writes A_tᵀ q_t. The
+        // scan from a zero state then gives S_in(p), and the output pass adds
+        // S_in(p)ᵀ A_tᵀ q_t to the other segments' rows.
+        __bf16* oA = reinterpret_cast<__bf16*>(ws + L.oA);
+        p1.o = a.o;
         p1.aug = true;
-        p1.aug_s0 = AI;
-        p1.aug_sT = AI;   // each state tile is read before it is written
+        p1.aug_P = P;
+        p1.aug_s0_first = a.s0;
+        p1.aug_sT = AI;
+        p1.aug_o = oA;
         if ((e = launch_chunk_mfma(p1, s)) != hipSuccess) return e;
+        split_scan_kernel<128><<<dim3((unsigned)(a.N * a.H * (a.Dv / 16))), dim3(256), 0, s>>>(
+            AI, Bst, nullptr, Sin, a.sT, a.N, a.H, a.Dv, P);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (!a.o) return hipSuccess;
+        const int64_t units = segs * a.H;
+        // a grid resident at once (2 workgroups per CU at this kernel's registers)
+        const int R = (int)std::max<int64_t>(1, std::min<int64_t>(16, 512 / units));
+        split_correct_kernel<<<dim3((unsigned)(units * R)), dim3(256), 0, s>>>(seg_cu, P, a.H, R, Sin, oA,
+                                                                               static_cast<__bf16*>(a.o));
+        return hipGetLastError();
     } else {
+        fill_identity_kernel<<<dim3(grid_for(segs * a.H * a.Dk * a.Dk)), dim3(256), 0, s>>>(AI, segs * a.H, a.Dk);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = chunk_forward(p1, s)) != hipSuccess) return e;
         // 2. A: identity entry states, v = 0 (read from an empty range), d_v = d_k, no outputs
         ChunkArgs p2 = seg;

@@ -237,7 +237,7 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
  *   time on one device (from several streams or threads) race on it and give
  *   undefined results: serialise them, e.g. on one stream.
  */
-#define KDA_SPLIT_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+#define KDA_SPLIT_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
 kda_status kda_chunk_fwd_split_static(const void* q, const void* k, const void* v, const void* g,
                                       const void* beta, const float* initial_state, const int32_t* cu_seqlens,
                                       int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,

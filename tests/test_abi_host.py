@@ -295,10 +295,12 @@ def test_chunk_fwd_split_workspace_bytes(lib):
     a = kda.chunk_fwd_split_workspace_bytes(1, 4096, 12, 128, 128, 1, torch.bfloat16, 8)
     b = kda.chunk_fwd_split_workspace_bytes(1, 4096, 12, 128, 128, 1, torch.float32, 8)
     # three fp32 states per segment and head (identity then A, B, entry states) and the segment
-    # offsets, whatever the input dtype
+    # offsets; the bf16 d=128 path adds the A pass's bf16 outputs, one row of Dk per token and head
     states = 3 * 8 * 12 * 128 * 128 * 4
-    assert states <= a < states + 4096
-    assert a == b
+    assert states <= b < states + 4096
+    assert a == b + 4096 * 12 * 128 * 2
+    c = kda.chunk_fwd_split_workspace_bytes(1, 4096, 12, 64, 64, 1, torch.bfloat16, 8)
+    assert 3 * 8 * 12 * 64 * 64 * 4 <= c < 3 * 8 * 12 * 64 * 64 * 4 + 4096
 
 
 def _bwd_pro(lib, **kw):
@@ -385,8 +387,9 @@ def _split_static(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status,needle", [
-    # 3 fp32 states of 64 KiB per (segment, head): 96 heads x 8 segments need 151 MB > 64 MiB
-    (dict(H=96), kda.KDA_ERR_UNSUPPORTED, "static scratch holds 67108864"),
+    # 3 fp32 states of 64 KiB per (segment, head), plus the A pass's bf16 outputs:
+    # 96 heads x 8 segments at T=4096 need 252 MB > 128 MiB
+    (dict(H=96), kda.KDA_ERR_UNSUPPORTED, "static scratch holds 134217728"),
     (dict(seg=0), kda.KDA_ERR_INVALID_ARG, "segments"),
     (dict(o=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
     (dict(chunk=64), kda.KDA_ERR_UNSUPPORTED, "16-row chunks"),
@@ -400,8 +403,8 @@ def test_chunk_fwd_split_static_rejects_before_launch(lib, kw, status, needle):
 
 def test_split_static_scratch_size_matches_header():
     text = open(kda.HEADER_PATH).read()
-    assert "#define KDA_SPLIT_STATIC_SCRATCH_BYTES ((size_t)64 << 20)" in text
-    assert kda.SPLIT_STATIC_SCRATCH_BYTES == 64 << 20
+    assert "#define KDA_SPLIT_STATIC_SCRATCH_BYTES ((size_t)128 << 20)" in text
+    assert kda.SPLIT_STATIC_SCRATCH_BYTES == 128 << 20
 
 
 def _conv_fwd(lib, **kw):

@@ -34,7 +34,7 @@ def _both(inp, segments):
 
 
 def test_static_scratch_matches_workspace_call_twice():
-    # call 1: 12 heads at T=8192, 8 segments (19 MB of the 64 MiB scratch)
+    # call 1: 12 heads at T=8192, 8 segments (44 MB of the 128 MiB scratch)
     inp1 = synth.make_chunk_inputs(1, 8192, 12, 128, 128, seed=950, dtype="bf16", init_state=True)
     need1 = kda.chunk_fwd_split_workspace_bytes(1, 8192, 12, 128, 128, 1, torch.bfloat16, 8)
     say(f"[case] static-scratch split, call 1: B=1 T=8192 H=12 bf16, 8 segments, {need1} bytes of scratch")
