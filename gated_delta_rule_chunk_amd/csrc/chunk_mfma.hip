@@ -765,7 +765,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
     const int vt = wi % ipu - (apass ? kNVT : 0);
     int n = unit / a.H;
     const int h = unit % a.H;
-    if (a.cu) {
+    // length of packed sequence m (a segment of the split in aug mode)
+    auto seq_len = [&](int m) -> int {
+        if (a.aug) {
+            int64_t b0, l0;
+            split_segment(a.cu, a.aug_T, a.aug_P, m, b0, l0);
+            return (int)l0;
+        }
+        return a.cu[m + 1] - a.cu[m];
+    };
+    if (a.cu || a.aug) {
         // packed batch: blocks are dispatched in index order, so within each run
         // of 256 consecutive sequences the longest (ties by index) goes first and
         // every run ends with its shortest; the work of the ranking stays at 256
@@ -773,7 +782,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         const int base = n & ~255, r = n & 255, cnt = min(256, a.N - base);
         int* lens = reinterpret_cast<int*>(smem);
         int* pick = lens + 256;
-        if (tid < cnt) lens[tid] = a.cu[base + tid + 1] - a.cu[base + tid];
+        if (tid < cnt) lens[tid] = seq_len(base + tid);
         __syncthreads();
         if (tid < cnt) {
             const int my = lens[tid];
@@ -789,7 +798,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         __syncthreads();
     }
     int64_t bos, len, b;
-    if (a.cu) {
+    if (a.aug) {
+        split_segment(a.cu, a.aug_T, a.aug_P, n, bos, len);
+        b = 0;
+    } else if (a.cu) {
         bos = a.cu[n];
         len = (int64_t)a.cu[n + 1] - bos;
         b = 0;

@@ -48,6 +48,24 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// The intra-sequence split's cut: sequence m / P (offsets cu, or rows of T0
+// tokens when cu is null) of length L is cut into P segments of
+// roundup(ceil(L / P), 64) rows, the last ones shorter or empty; segment m's
+// first token and length.
+constexpr int kSplitSegAlign = 64;
+__device__ __forceinline__ void split_segment(const int32_t* cu, int32_t T0, int32_t P, int64_t m, int64_t& bos,
+                                              int64_t& len) {
+    const int64_t sq = m / P, p = m % P;
+    const int64_t b0 = cu ? cu[sq] : sq * T0;
+    const int64_t L = cu ? (int64_t)cu[sq + 1] - cu[sq] : T0;
+    int64_t seg = (L + P - 1) / P;
+    seg = (seg + kSplitSegAlign - 1) / kSplitSegAlign * kSplitSegAlign;
+    const int64_t start = p * seg < L ? p * seg : L;
+    const int64_t end = (p + 1) * seg < L ? (p + 1) * seg : L;
+    bos = b0 + start;
+    len = end - start;
+}
+
 // Load element i of an input that is either float or bf16.
 template <typename T> __device__ __forceinline__ float load_elem(const T* p, int64_t i);
 template <> __device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) {

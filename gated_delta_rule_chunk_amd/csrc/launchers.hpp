@@ -40,13 +40,15 @@ struct ChunkArgs {
     const float* conv_sv = nullptr;  // conv state of v: [N][3][H*Dv], or null (zeros)
     bool conv_act = false;           // SiLU after the convolution
     // the split's A and B passes in one launch (bf16, Dk = Dv = 128): the
-    // sequences are the segments, aug_P per original sequence, and every
+    // sequences are the segments, aug_P per original sequence (bounds by
+    // split_segment from the original cu and aug_T; N counts segments), and every
     // (segment, head) gets twice the column blocks. The first set runs with v
     // from a zero entry state (aug_s0_first of the sequence in its first
     // segment) into sT and o (B); the second, skipped in first segments, with
     // v = 0 from the identity into aug_sT and aug_o (A).
     bool aug = false;
     int32_t aug_P = 1;
+    int32_t aug_T = 0;                     // T of the original call (its cu in cu, or null)
     const float* aug_s0_first = nullptr;   // [N / aug_P, H, Dk, Dv] or nullptr
     float* aug_sT = nullptr;
     void* aug_o = nullptr;                 // like o, with Dk columns

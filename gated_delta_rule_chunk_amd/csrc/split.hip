@@ -32,21 +32,15 @@
 namespace kda {
 namespace {
 
-constexpr int kSegAlign = 64;  // segment lengths are multiples of the largest chunk
-
-// Segment offsets for every sequence: sequence n of length L starts at bos;
-// its segments have length roundup(ceil(L / P), 64) except the last, and
-// trailing segments may be empty.
+// Segment offsets for every sequence (split_segment's cut) as packed
+// cu_seqlens of the N * P segments.
 __global__ void split_offsets_kernel(const int32_t* cu, int32_t N, int32_t T, int32_t P, int32_t* seg_cu) {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
     if (n >= N) return;
-    const int64_t bos = cu ? cu[n] : (int64_t)n * T;
-    const int64_t len = cu ? (int64_t)cu[n + 1] - cu[n] : T;
-    int64_t seg = (len + P - 1) / P;
-    seg = (seg + kSegAlign - 1) / kSegAlign * kSegAlign;
+    int64_t bos = 0, len = 0;
     for (int p = 0; p < P; ++p) {
-        const int64_t off = (int64_t)p * seg < len ? (int64_t)p * seg : len;
-        seg_cu[(int64_t)n * P + p] = (int32_t)(bos + off);
+        split_segment(cu, T, P, (int64_t)n * P + p, bos, len);
+        seg_cu[(int64_t)n * P + p] = (int32_t)bos;
     }
     if (n == N - 1) seg_cu[(int64_t)N * P] = (int32_t)(bos + len);
 }
@@ -88,45 +82,48 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
     __syncthreads();
     if constexpr (DK == 128) {
         // S_new = A S + B on the matrix cores: 8 row tiles of 16 x 16, two per
-        // wave. Step p + 1's A and B are loaded while step p is computed, into
-        // the registers step p's values left when they went to LDS and to the
-        // accumulators (past the last step the loads repeat it).
+        // wave. A and B go through two register sets: step p stages its set
+        // into LDS and the accumulators and then loads step p + 2's into it, so
+        // every load has two steps to land (past the last step the loads repeat
+        // it).
         const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
-        float4 ra[kPer];
-        float rbv[2][4];
-        auto issue = [&](int p) {
+        struct Regs {
+            float4 a[kPer];
+            float b[2][4];
+        };
+        auto issue = [&](int p, Regs& R) {
             const int64_t seg = (int64_t)n * P + (p < P ? p : P - 1);
             const float4* a4 = reinterpret_cast<const float4*>(A + (seg * H + h) * (int64_t)DK * DK);
             const float* b = Bst + (seg * H + h) * (int64_t)DK * Dv;
 #pragma unroll
-            for (int u = 0; u < kPer; ++u) ra[u] = a4[tid + NT * u];
+            for (int u = 0; u < kPer; ++u) R.a[u] = a4[tid + NT * u];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) rbv[t][i] = b[(int64_t)(16 * (2 * w + t) + 4 * lg + i) * Dv + c0 + l16];
+                for (int i = 0; i < 4; ++i) R.b[t][i] = b[(int64_t)(16 * (2 * w + t) + 4 * lg + i) * Dv + c0 + l16];
         };
-        issue(0);
-        for (int p = 0; p < P; ++p) {
+        // one step; false once the chain is done
+        auto step = [&](int p, Regs& R) -> bool {
             const int64_t seg = (int64_t)n * P + p;
             float* sin = Sin + (seg * H + h) * (int64_t)DK * Dv;
             for (int idx = tid; idx < DK * BVs; idx += NT) {
                 const int c = idx / BVs, j = idx % BVs;
                 sin[(int64_t)c * Dv + c0 + j] = sS[c][j];
             }
-            if (p == P - 1 && !sT) break;
+            if (p == P - 1 && !sT) return false;
 #pragma unroll
             for (int u = 0; u < kPer; ++u) {
                 const int q = tid + NT * u;
                 const int r = q / (DK / 4), c = (q % (DK / 4)) * 4;
-                sA[r][c] = ra[u].x; sA[r][c + 1] = ra[u].y; sA[r][c + 2] = ra[u].z; sA[r][c + 3] = ra[u].w;
+                sA[r][c] = R.a[u].x; sA[r][c + 1] = R.a[u].y; sA[r][c + 2] = R.a[u].z; sA[r][c + 3] = R.a[u].w;
             }
             f32x4 acc[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[t][i] = rbv[t][i];
+                for (int i = 0; i < 4; ++i) acc[t][i] = R.b[t][i];
             __syncthreads();
-            issue(p + 1);
+            issue(p + 2, R);
             // from a zero initial state, S_in(1) = B(0): A(0) is not read (the
             // bf16 split does not compute it)
             if (p > 0 || s0) {
@@ -145,6 +142,14 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sS[16 * (2 * w + t) + 4 * lg + i][l16] = acc[t][i];
             __syncthreads();
+            return p + 1 < P;
+        };
+        Regs R0, R1;
+        issue(0, R0);
+        issue(1, R1);
+        for (int p = 0;; p += 2) {
+            if (!step(p, R0)) break;
+            if (!step(p + 1, R1)) break;
         }
     } else {
         for (int p = 0; p < P; ++p) {
@@ -229,14 +234,17 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
 // at position c ^ (i % 16) of the row, so the 16 rows that one operand read
 // touches fall in different banks.
 constexpr int kCorrBlockBytes = 64 * 256;
-__global__ __launch_bounds__(256, 2) void split_correct_kernel(const int32_t* seg_cu, int32_t P, int32_t H, int32_t R,
-                                                            const float* Sin, const __bf16* oA, __bf16* o) {
+__global__ __launch_bounds__(256, 2) void split_correct_kernel(const int32_t* cu, int32_t T0, int32_t P, int32_t H,
+                                                               int32_t R, const float* Sin, const __bf16* oA,
+                                                               __bf16* o) {
     __shared__ __attribute__((aligned(16))) char buf[2][kCorrBlockBytes];
     const int r = blockIdx.x % R;
     const int unit = blockIdx.x / R;
     const int seg = unit / H, h = unit % H;
     if (seg % P == 0) return;                       // the whole workgroup
-    const int64_t bos = seg_cu[seg], eos = seg_cu[seg + 1];
+    int64_t bos, len;
+    split_segment(cu, T0, P, seg, bos, len);
+    const int64_t eos = bos + len;
     if ((int64_t)r * 64 >= eos - bos) return;       // the whole workgroup
     const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
@@ -367,8 +375,7 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
     const int64_t segs = (int64_t)a.N * P;
     hipError_t e;
 
-    split_offsets_kernel<<<dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, s>>>(a.cu, a.N, a.T, P, seg_cu);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+
     // the packed view of the input: one row of B*T tokens, N*P sequences
     ChunkArgs seg = a;
     seg.B = 1;
@@ -388,8 +395,10 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
         // scan from a zero state then gives S_in(p), and the output pass adds
         // S_in(p)ᵀ A_tᵀ q_t to the other segments' rows.
         __bf16* oA = reinterpret_cast<__bf16*>(ws + L.oA);
+        p1.cu = a.cu;     // the segments' bounds are computed in the kernels (split_segment)
         p1.o = a.o;
         p1.aug = true;
+        p1.aug_T = a.T;
         p1.aug_P = P;
         p1.aug_s0_first = a.s0;
         p1.aug_sT = AI;
@@ -402,10 +411,12 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
         const int64_t units = segs * a.H;
         // a grid resident at once (2 workgroups per CU at this kernel's registers)
         const int R = (int)std::max<int64_t>(1, std::min<int64_t>(16, 512 / units));
-        split_correct_kernel<<<dim3((unsigned)(units * R)), dim3(256), 0, s>>>(seg_cu, P, a.H, R, Sin, oA,
+        split_correct_kernel<<<dim3((unsigned)(units * R)), dim3(256), 0, s>>>(a.cu, a.T, P, a.H, R, Sin, oA,
                                                                                static_cast<__bf16*>(a.o));
         return hipGetLastError();
     } else {
+        split_offsets_kernel<<<dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, s>>>(a.cu, a.N, a.T, P, seg_cu);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
         fill_identity_kernel<<<dim3(grid_for(segs * a.H * a.Dk * a.Dk)), dim3(256), 0, s>>>(AI, segs * a.H, a.Dk);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = chunk_forward(p1, s)) != hipSuccess) return e;
