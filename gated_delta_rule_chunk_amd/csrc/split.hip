@@ -72,7 +72,15 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
     __shared__ float sS[DK][BVs + 1];
     const int tid = threadIdx.x;
     const int nvt = Dv / BVs;
-    const int vt = blockIdx.x % nvt, unit = blockIdx.x / nvt;
+    // blocks are dealt round-robin over the 8 XCDs: the column slices of one
+    // (sequence, head), which all read its A(p), go to one XCD so that its L2
+    // serves the repeats (the last units, below a multiple of 8, stay spread)
+    int b = blockIdx.x;
+    {
+        const int units = N * H, per = 8 * nvt, full = (units / 8) * per;
+        if (b < full) b = (b / per * 8 + b % 8) * nvt + (b % per) / 8;
+    }
+    const int vt = b % nvt, unit = b / nvt;
     const int n = unit / H, h = unit % H;
     const int c0 = vt * BVs;
     for (int idx = tid; idx < DK * BVs; idx += NT) {
