@@ -82,11 +82,14 @@ CASES = [
     dict(B=2, T=300, H=4, lengths=None, act=False, states=True),
     dict(B=1, T=0, H=3, lengths=[0, 1, 2, 3, 17, 64, 65, 130, 257], act=True, states=True),
     dict(B=1, T=77, H=96, lengths=None, act=True, states=False),
+    # more than 256 packed sequences (the kernel orders them by length within runs of 256)
+    dict(B=1, T=0, H=2, lengths=[int(x) for x in np.random.default_rng(77).integers(0, 41, size=300)], act=True,
+         states=True),
 ]
 
 
-@pytest.mark.parametrize("c", CASES, ids=lambda c: f"B{c['B']}T{c['T']}H{c['H']}L{c['lengths'] is not None}"
-                         f"act{int(c['act'])}s{int(c['states'])}")
+@pytest.mark.parametrize("c", CASES, ids=lambda c: f"B{c['B']}T{c['T']}H{c['H']}"
+                         f"L{0 if c['lengths'] is None else len(c['lengths'])}act{int(c['act'])}s{int(c['states'])}")
 def test_fused_matches_unfused_bitwise_and_oracle(c):
     inp, ws, s0 = _inputs(c["B"], c["T"], c["H"], 128, "bf16", seed=500 + c["H"] + c["T"], lengths=c["lengths"],
                           conv_states=c["states"])
