@@ -816,6 +816,20 @@ __global__ __launch_bounds__(256) void chunk_mats_kernel(BwdArgs a) {
     }
     const bool inb = (tid & (C - 1)) < rows;
     const float bt = load_elem(static_cast<const Tin*>(a.beta), (sq.b * a.T + t0 + (inb ? (tid & (C - 1)) : 0)) * a.H + h);
+    if (a.status) {
+        // the factored exponentials below need g in [-5, 0] (NaN fails too):
+        // a wave that meets one outside counts it in status word 1
+        bool bad = false;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x = g[u].get(e);
+                bad |= in[u] && !(x >= -5.f && x <= 0.f);
+            }
+        if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0)
+            __hip_atomic_fetch_add(a.status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int idx = tid + 256 * u;

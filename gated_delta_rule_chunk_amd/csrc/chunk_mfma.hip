@@ -79,6 +79,10 @@ constexpr int kNP = 4 * kNR;    // preparation waves: (chunk of the pair, channe
 constexpr int kNB = 4;          // state waves, 16 value columns each
 constexpr int kBV = 16 * kNB;   // value columns per workgroup
 constexpr int kNVT = kDV / kBV;
+// e^-84: g in [-5, 0] keeps a 16-row chunk's total log-decay at or above -80,
+// and the margin covers its rounding; below it the in-chunk exponents near
+// the float32 range
+constexpr float kMinChunkDecay = 3.3057e-37f;
 constexpr int kThreads = 64 * (kNP + kNB);
 
 // One pair's slot (bytes). Fragments are stored in lane order, so every
@@ -1037,6 +1041,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
         u32x2 hw = {0u, 0u};
         f32x4 tq = zero4();
         if constexpr (kConv) tq = reinterpret_cast<const f32x4*>(a.conv_wv)[(int64_t)h * kDV + col0 + 4 * lg + (li & 3)];
+        // chunks whose total decay was out of range, as a float in a VGPR (a
+        // loop-carried bool would hold scalar registers); reported at the end
+        float gate_bad = 0.f;
         auto consume_words = [&](int gi, const StateIn& vcur) {
             const __amdgpu_buffer_rsrc_t ro = stream_rsrc(so);
             stream_advance(so, vstride);
@@ -1049,8 +1056,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
                 // state decayed over the pair, for the update at its end. Lane
                 // li of row group lg reads entries 2li, 2li+1 of the 32 decay
                 // factors of its row group; DPP broadcasts the one each row needs.
-                const f32x2 e2 = *reinterpret_cast<const f32x2*>(slot + S_D1 + 4 * (EG_STRIDE * lg + 2 * li)) *
-                                 *reinterpret_cast<const f32x2*>(slot + S_E2 + 4 * (EG_STRIDE * lg + 2 * li));
+                const f32x2 d1v = *reinterpret_cast<const f32x2*>(slot + S_D1 + 4 * (EG_STRIDE * lg + 2 * li));
+                const f32x2 d2v = *reinterpret_cast<const f32x2*>(slot + S_E2 + 4 * (EG_STRIDE * lg + 2 * li));
+                const f32x2 e2 = d1v * d2v;
+                // each chunk's total decay per channel, e^Gamma_C, must lie in
+                // [e^-80, 1] (NaN fails): what the 16-row chunk's exponents need
+                const bool ok = (d1v[0] >= kMinChunkDecay && d1v[0] <= 1.f) & (d1v[1] >= kMinChunkDecay && d1v[1] <= 1.f) &
+                                (d2v[0] >= kMinChunkDecay && d2v[0] <= 1.f) & (d2v[1] >= kMinChunkDecay && d2v[1] <= 1.f);
+                gate_bad += ok ? 0.f : 1.f;
                 f32x4 D[8];
                 decay_state<0>(D, S, e2);
                 // X = V - Kg S (rows 4lg+j, column li); OT = -(Qh S)^T (column
@@ -1156,13 +1169,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
                 for (int j = 0; j < 4; ++j)
                     sT[state_base + (int64_t)(16 * rt + 4 * lg + j) * kDV + col0 + li] = S[rt][j];
         }
+        // a chunk whose total decay left its range: counted once per wave in the
+        // device's second status word (kda_device_check reports it)
+        if (__builtin_amdgcn_ballot_w64(gate_bad != 0.f) != 0 && lane == 0 && a.status)
+            __hip_atomic_fetch_add(a.status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 }  // namespace
 
 // The 16-row chunk needs every g >= -5 (|Gamma| <= 80); with the prologue
-// the gate is bounded below by gate_lb.
+// the gate is bounded below by gate_lb. The state waves check each chunk's
+// total decay per channel against [kMinChunkDecay, 1].
 bool chunk_mfma_supported(const ChunkArgs& a) {
     return a.bf16 && a.Dk == kDK && a.Dv == kDV && (!a.prologue || a.gate_lb >= -5.f);
 }

@@ -10,17 +10,19 @@
 #include "../../include/kda.h"
 #include "launchers.hpp"
 
-// Device status word: the number of bounded waits (in any kernel of this
-// library, on this device) that gave up since the module was loaded. Kernels
-// add to it with a vector atomic from one lane; the host only reads it.
-__device__ __attribute__((aligned(256))) unsigned int kda_wait_timeouts[64];
+// Device status words, counted since the module was loaded on this device:
+// [0] bounded waits between waves (in any kernel of this library) that gave
+// up; [1] waves of the matrix-core forward or backward that met log-decays out
+// of the range they need. Kernels add to them with a vector atomic from one lane; the host
+// only reads them (kda_device_check). The rest of the array is padding.
+__device__ __attribute__((aligned(256))) unsigned int kda_device_status[64];
 
 namespace {
 
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mutex;
 unsigned int* g_status_ptr[kMaxDevices] = {};
-unsigned int g_status_seen[kMaxDevices] = {};
+unsigned int g_status_seen[kMaxDevices][2] = {};   // [0] wait give-ups, [1] gates out of range
 std::atomic<int> g_spin_limit{1 << 22};
 
 }  // namespace
@@ -35,7 +37,7 @@ unsigned int* device_status_word() {
     std::lock_guard<std::mutex> lock(g_dev_mutex);
     if (!g_status_ptr[dev]) {
         void* p = nullptr;
-        if (hipGetSymbolAddress(&p, HIP_SYMBOL(kda_wait_timeouts)) != hipSuccess) return nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(kda_device_status)) != hipSuccess) return nullptr;
         g_status_ptr[dev] = static_cast<unsigned int*>(p);
     }
     return g_status_ptr[dev];
@@ -92,21 +94,29 @@ kda_status kda_device_check(void* stream) {
     int dev = 0;
     if (!word || hipGetDevice(&dev) != hipSuccess)
         return fail(KDA_ERR_HIP, "kda_device_check: the device status word is not accessible");
-    unsigned int now = 0;
-    hipError_t e = hipMemcpyAsync(&now, word, sizeof(now), hipMemcpyDeviceToHost, s);
+    unsigned int now[2] = {0, 0};
+    hipError_t e = hipMemcpyAsync(now, word, sizeof(now), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_device_check: %s", hipGetErrorString(e));
-    unsigned int seen;
+    unsigned int seen[2];
     {
         std::lock_guard<std::mutex> lock(g_dev_mutex);
-        seen = g_status_seen[dev];
-        g_status_seen[dev] = now;
+        seen[0] = g_status_seen[dev][0];
+        seen[1] = g_status_seen[dev][1];
+        g_status_seen[dev][0] = now[0];
+        g_status_seen[dev][1] = now[1];
     }
-    if (now != seen)
+    if (now[0] != seen[0])
         return fail(KDA_ERR_DEVICE,
                     "kda_device_check: %u bounded wait(s) between waves gave up on device %d since the last check; "
                     "the outputs of the calls that ran meanwhile are not valid",
-                    now - seen, dev);
+                    now[0] - seen[0], dev);
+    if (now[1] != seen[1])
+        return fail(KDA_ERR_DEVICE,
+                    "kda_device_check: a matrix-core kernel met log-decays g out of its range (forward: a 16-row "
+                    "chunk's total outside [-84, 0]; backward: a g outside [-5, 0]; NaN included) in %u wave(s) on "
+                    "device %d since the last check; the outputs of the calls that ran meanwhile are not valid",
+                    now[1] - seen[1], dev);
     return KDA_OK;
 }
 
@@ -487,6 +497,8 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.d_s0 = d_initial_state;
     a.B = B; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.N = N; a.scale = scale; a.bf16 = dtype == KDA_BF16;
     if ((int64_t)N * H == 0) return KDA_OK;
+    a.status = kda::device_status_word();
+    if (!a.status) return fail(KDA_ERR_HIP, "%s: the device status word is not accessible", fn);
     const hipError_t e = kda::launch_chunk_bwd(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KDA_OK;

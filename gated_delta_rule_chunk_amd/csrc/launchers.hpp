@@ -121,6 +121,9 @@ struct BwdArgs {
     bool g_ge_m5 = true;       // g >= -5 holds (the matrix-core kernel relies on it)
     bool x_bf16 = false;       // with bf16 false: v and d_o are bf16 (matrix-core path only)
     bool zero_grads = false;   // (set by the launcher) the T/P/KK kernel zeroes dq, dk, dg, dbeta
+    // the device's status words (the matrix-core T/P/KK kernel counts log-decays
+    // outside [-5, 0] in word 1), or nullptr
+    unsigned int* status = nullptr;
 };
 
 // The backward's workspace: a float32 chunk-entry state [H][Dk][Dv] per

@@ -16,17 +16,25 @@
  *
  * Conventions for every call:
  *  - All tensor pointers are DEVICE pointers, row-major and contiguous, owned
- *    by the caller. The library never allocates, frees or synchronises; work
- *    is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
- *    the call returns before it finishes.
+ *    by the caller. The library never allocates or frees, and no call but
+ *    kda_device_check synchronises; work is enqueued on `stream` (a
+ *    hipStream_t; NULL = the default stream) and the call returns before it
+ *    finishes.
  *  - Every argument check happens on the host before anything is launched;
  *    a rejected call touches no memory. Unsupported inputs fail explicitly
  *    (the K3 README's rule for unsupported inputs); nothing falls back to
  *    another code path silently.
- *  - Preconditions that are NOT checked on the device: g in [-5, 0] (the K3
- *    gate bound; the bf16 chunk kernel relies on it to keep every in-chunk
- *    exponent below 80), finite inputs, cu_seqlens starting at 0,
- *    non-decreasing and ending at T, distinct decode state slots.
+ *  - g in [-5, 0] (the K3 gate bound). The bf16 matrix-core forward needs
+ *    every 16-row chunk's total log-decay per channel, the sum of its 16 g,
+ *    in [-84, 0] (g in [-5, 0] keeps it at or above -80) to keep its
+ *    in-chunk exponents within float32, and checks that on the device. The
+ *    matrix-core backward needs g in [-5, 0] element by element and checks
+ *    that. A call that fails either check (a NaN g included) makes the next
+ *    kda_device_check return KDA_ERR_DEVICE, and its outputs are not valid.
+ *    The other kernels take any finite g.
+ *  - Preconditions that are NOT checked on the device: finite inputs,
+ *    cu_seqlens starting at 0, non-decreasing and ending at T, distinct
+ *    decode state slots.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -278,7 +286,8 @@ size_t kda_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk
  * Everything is computed in float32, in 16-row chunks; bf16 inputs are
  * widened exactly. Dk = 128 with Dv = 64 or 128 runs a matrix-core kernel
  * (float32 MFMA) that factors the in-chunk decay through the chunk's middle
- * row and so relies on g >= -5 (see the preconditions above); other head
+ * row and so relies on g in [-5, 0], which it checks on the device like the
+ * forward (kda_device_check reports a g outside it); other head
  * dims run a vector-ALU kernel with no range condition on g. For Dv = 128 the two 64-column halves of
  * the value dimension add their shares of dq, dk, dg and dbeta with float32
  * atomics, which with two terms is order-independent, so the result is
@@ -461,13 +470,15 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
  * Instead of hanging or returning silently wrong data, the kernel counts
  * each give-up in a per-device status word, finishes normally, and
  * kda_device_check reports it: failures are explicit (ISEEKYAN/k3 README,
- * package scope: unsupported or failing paths must fail explicitly).
+ * package scope). A second status word counts log-decays out of the range
+ * the matrix-core kernels need (see the conventions above).
  *
  * kda_device_check waits for the work enqueued on `stream`, then returns
- * KDA_OK if no bounded wait of any call on the current device gave up since
- * the previous check (or since the library was loaded), and KDA_ERR_DEVICE
- * otherwise (kda_last_error_message gives the count). The check itself
- * synchronises, so it belongs outside timed or captured regions.
+ * KDA_OK if, since the previous check (or since the library was loaded), no
+ * bounded wait of any call on the current device gave up and no gate fell
+ * outside its range, and KDA_ERR_DEVICE otherwise (kda_last_error_message
+ * says which, with the count). The check itself synchronises, so it belongs
+ * outside timed or captured regions.
  */
 kda_status kda_device_check(void* stream);
 

@@ -100,6 +100,22 @@ def test_bwd_gate_and_beta_extremes(g_mode, beta_mode):
     _check(inp, d_o, dfin, label=f"g={g_mode} beta={beta_mode}")
 
 
+def test_bwd_gate_out_of_range_is_reported():
+    """The matrix-core backward (d_k = 128) factors the in-chunk decay and needs
+    g in [-5, 0]; a g outside it must be reported by kda_device_check."""
+    kda.device_check()
+    inp = synth.make_chunk_inputs(1, 200, 2, 128, 128, seed=733, dtype="bf16", init_state=True)
+    inp["g"][0, 99, 1, 3] = -6.0
+    d_o = torch.randn((1, 200, 2, 128), generator=torch.Generator().manual_seed(733)).to(torch.bfloat16)
+    say("[case] bwd d=128 with one g = -6 (token 99, head 1, channel 3)")
+    gpu_bwd(inp, d_o, None)
+    with pytest.raises(kda.KDAError) as err:
+        kda.device_check()
+    say(f"        reported: {err.value}")
+    assert err.value.status == kda.KDA_ERR_DEVICE and "out of its range" in str(err.value)
+    kda.device_check()
+
+
 def test_bwd_empty_sequence_passes_final_cotangent_through():
     inp = synth.make_chunk_inputs(2, 0, 3, 32, 32, seed=550, dtype="f32", init_state=True)
     d_o, dfin = synth.make_cotangents(inp, seed=551)

@@ -7,6 +7,10 @@
   every kernel still runs to its end; kda_device_check must then report
   KDA_ERR_DEVICE, and a following call with the default limit must be clean
   and match the oracle.
+* Gate range: the bf16 matrix-core forward needs each 16-row chunk's total
+  log-decay in [-84, 0]; a chunk outside it (or a NaN) must be reported by
+  kda_device_check, while in-range inputs, the bound itself and the other
+  kernels' inputs pass.
 * Decode padding: a row whose cache slot is outside [0, n_slots) (-1 here)
   must write a zero output and leave every cache slot it does not own bit for
   bit unchanged; the other rows must equal the oracle run on them alone.
@@ -50,6 +54,45 @@ def test_wait_give_up_is_reported():
     eo, ef = rel(o[:, :, [0, 95]], ro), rel(fin[:, [0, 95]], rf)
     say(f"        default limit: relL2 o={eo:.3e} final={ef:.3e}")
     assert eo <= TOL_BF16 and ef <= TOL_BF16
+
+
+@pytest.mark.parametrize("case", ["deep", "positive", "nan"])
+def test_gate_out_of_range_is_reported(case):
+    """The bf16 matrix-core forward needs each 16-row chunk's total log-decay
+    per channel in [-84, 0]: one g of -90, a chunk whose sum is positive, or a
+    NaN must be reported by kda_device_check."""
+    kda.device_check()
+    inp = synth.make_chunk_inputs(1, 300, 4, 128, 128, seed=905, dtype="bf16", init_state=True, g_mode="weak")
+    inp["g"][0, 157, 2, 77] = {"deep": -90.0, "positive": 1.0, "nan": float("nan")}[case]
+    d = to_dev(inp)
+    say(f"[case] bf16 d=128 forward with one g out of range ({case}; token 157, head 2, channel 77)")
+    kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["initial_state"])
+    with pytest.raises(kda.KDAError) as err:
+        kda.device_check()
+    say(f"        reported: {err.value}")
+    assert err.value.status == kda.KDA_ERR_DEVICE and "out of its range" in str(err.value)
+    kda.device_check()   # consumed
+
+
+def test_gate_in_range_passes():
+    kda.device_check()
+    # g exactly -5 on 64 rows (chunk totals of -80) and 0 on 16 rows
+    inp = synth.make_chunk_inputs(1, 300, 4, 128, 128, seed=906, dtype="bf16", init_state=True)
+    inp["g"][0, :64] = -5.0
+    inp["g"][0, 64:80] = 0.0
+    # one g below -5 whose chunk total stays far from -84: computed exactly, not reported
+    inp["g"][0, 200, 1, 9] = -5.25
+    o, fin = gpu_chunk(inp)
+    kda.device_check()
+    ro, rf = oracle_chunk(inp)
+    eo, ef = rel(o, ro), rel(fin, rf)
+    say(f"        in-range gates: relL2 o={eo:.3e} final={ef:.3e}")
+    assert eo <= TOL_BF16 and ef <= TOL_BF16
+    # the float32 kernel takes any finite g
+    inp32 = synth.make_chunk_inputs(1, 100, 2, 64, 64, seed=907, dtype="f32", init_state=True)
+    inp32["g"][0, 10, 1, 5] = -90.0
+    gpu_chunk(inp32, chunk=16)
+    kda.device_check()
 
 
 @pytest.mark.wait_timeout_path
