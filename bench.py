@@ -611,7 +611,7 @@ def main():
                     help="run one secondary leg alone and print its JSON object (for per-kernel profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
