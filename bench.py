@@ -523,8 +523,8 @@ def bench_split(steps, warmup, segments=10):
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": read_leg_traffic("split")},
             "algorithmic_bytes_per_step": nbytes,
-            "timed": "one kda_chunk_fwd_split call: offsets, identity fill, the A and B passes over the segments "
-                     "(one launch), the entry-state scan, the output pass"}
+            "timed": "one kda_chunk_fwd_split call: the A and B passes over the segments (one launch), the "
+                     "entry-state scan, the correction of the outputs of segments after the first"}
 
 
 def cpu_backward_baseline(heads=96):

@@ -206,12 +206,18 @@ __device__ __forceinline__ void decay_state(f32x4 (&D)[8], const f32x4 (&S)[8], 
 // Block index -> work item: the ipu column blocks of one (sequence, head) land
 // on the same XCD (blocks are dealt round-robin over the 8 XCDs) and are
 // dispatched together, so that XCD's L2 serves their shared q, k, g once.
+// Within an XCD, consecutive blocks go round-robin to its four shader engines
+// (8 CUs each), whatever their load, so block j of a unit would always land on
+// engine j: with four column blocks (the split's B, B, A, A) the roles rotate
+// by two engines from one group of units to the next, which spreads the
+// longer B blocks of first segments and the A blocks that first segments skip
+// over all four engines.
 __device__ __forceinline__ int remap_block(int b, int units, int ipu) {
     const int per = 8 * ipu;
     const int full = (units / 8) * per;
     if (b >= full) return b;
     const int grp = b / per, rem = b % per;
-    return (grp * 8 + (rem & 7)) * ipu + (rem >> 3);
+    return (grp * 8 + (rem & 7)) * ipu + ((rem >> 3) + 2 * grp) % ipu;
 }
 
 // Buffer descriptors: accesses outside [base, base + num_records) read 0 and
@@ -773,7 +779,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
     auto seq_len = [&](int m) -> int {
         if (a.aug) {
             int64_t b0, l0;
-            split_segment(a.cu, a.aug_T, a.aug_P, m, b0, l0);
+            split_segment(a.cu, a.aug_T, a.aug_P, 2, m, b0, l0);
             return (int)l0;
         }
         return a.cu[m + 1] - a.cu[m];
@@ -803,7 +809,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(ChunkArgs a) {
     }
     int64_t bos, len, b;
     if (a.aug) {
-        split_segment(a.cu, a.aug_T, a.aug_P, n, bos, len);
+        split_segment(a.cu, a.aug_T, a.aug_P, 2, n, bos, len);
         b = 0;
     } else if (a.cu) {
         bos = a.cu[n];

@@ -49,19 +49,24 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
 }
 
 // The intra-sequence split's cut: sequence m / P (offsets cu, or rows of T0
-// tokens when cu is null) of length L is cut into P segments of
-// roundup(ceil(L / P), 64) rows, the last ones shorter or empty; segment m's
-// first token and length.
+// tokens when cu is null) of length L is cut into P segments, the first of
+// w0 shares and the others of one share each, a share being
+// roundup(ceil(L / (P - 1 + w0)), 64) rows; the last segments are shorter or
+// empty. Returns segment m's first token and length. (Where the first segment
+// runs half the passes of the others, w0 = 2 gives every segment the same
+// work.)
 constexpr int kSplitSegAlign = 64;
-__device__ __forceinline__ void split_segment(const int32_t* cu, int32_t T0, int32_t P, int64_t m, int64_t& bos,
-                                              int64_t& len) {
+__device__ __forceinline__ void split_segment(const int32_t* cu, int32_t T0, int32_t P, int32_t w0, int64_t m,
+                                              int64_t& bos, int64_t& len) {
     const int64_t sq = m / P, p = m % P;
     const int64_t b0 = cu ? cu[sq] : sq * T0;
     const int64_t L = cu ? (int64_t)cu[sq + 1] - cu[sq] : T0;
-    int64_t seg = (L + P - 1) / P;
+    const int64_t shares = P - 1 + w0;
+    int64_t seg = (L + shares - 1) / shares;
     seg = (seg + kSplitSegAlign - 1) / kSplitSegAlign * kSplitSegAlign;
-    const int64_t start = p * seg < L ? p * seg : L;
-    const int64_t end = (p + 1) * seg < L ? (p + 1) * seg : L;
+    const int64_t s0 = p == 0 ? 0 : (w0 + p - 1) * seg, s1 = (w0 + p) * seg;
+    const int64_t start = s0 < L ? s0 : L;
+    const int64_t end = s1 < L ? s1 : L;
     bos = b0 + start;
     len = end - start;
 }

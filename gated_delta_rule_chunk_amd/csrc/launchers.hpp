@@ -41,7 +41,8 @@ struct ChunkArgs {
     bool conv_act = false;           // SiLU after the convolution
     // the split's A and B passes in one launch (bf16, Dk = Dv = 128): the
     // sequences are the segments, aug_P per original sequence (bounds by
-    // split_segment from the original cu and aug_T; N counts segments), and every
+    // split_segment, first-segment weight 2, from the original cu and aug_T;
+    // N counts segments), and every
     // (segment, head) gets twice the column blocks. The first set runs with v
     // from a zero entry state (aug_s0_first of the sequence in its first
     // segment) into sT and o (B); the second, skipped in first segments, with

@@ -18,6 +18,8 @@
 //      and the final state A(P-1) S_in(P-1) + B(P-1);
 //   3. split_correct_kernel: o += S_in(p)ᵀ (scale A_tᵀ q_t) on the rows of
 //      segments p >= 1.
+// A first segment runs only B, so it takes two shares of rows and every
+// later segment one: each segment then carries the same work.
 // Every other shape runs three forward passes: B from zero entry states
 // (outputs discarded), A from the identity, the scan from the initial state,
 // then the forward over all segments from S_in, which writes o.
@@ -39,7 +41,7 @@ __global__ void split_offsets_kernel(const int32_t* cu, int32_t N, int32_t T, in
     if (n >= N) return;
     int64_t bos = 0, len = 0;
     for (int p = 0; p < P; ++p) {
-        split_segment(cu, T, P, (int64_t)n * P + p, bos, len);
+        split_segment(cu, T, P, 1, (int64_t)n * P + p, bos, len);
         seg_cu[(int64_t)n * P + p] = (int32_t)bos;
     }
     if (n == N - 1) seg_cu[(int64_t)N * P] = (int32_t)(bos + len);
@@ -60,11 +62,13 @@ __global__ void fill_identity_kernel(float* p, int64_t mats, int Dk) {
 // A is [N*P][H][Dk][Dk], Bst and Sin are [N*P][H][Dk][Dv]. Each step stages
 // A(p) in LDS with coalesced 16-byte loads.
 template <int DK>
-__global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const float* Bst, const float* s0,
-                                                         float* Sin, float* sT, int32_t N, int32_t H,
-                                                         int32_t Dv, int32_t P) {
+constexpr int scan_threads() { return DK == 128 ? 512 : 256; }
+template <int DK>
+__global__ __launch_bounds__(scan_threads<DK>()) void split_scan_kernel(const float* A, const float* Bst,
+                                                                        const float* s0, float* Sin, float* sT,
+                                                                        int32_t N, int32_t H, int32_t Dv, int32_t P) {
     constexpr int BVs = 16;
-    constexpr int NT = 256;
+    constexpr int NT = scan_threads<DK>();
     constexpr int kQuads = DK * DK / 4;                       // float4 pieces of A
     constexpr int kPer = kQuads / NT > 0 ? kQuads / NT : 1;   // per thread
     constexpr int kOut = DK * BVs / NT > 0 ? DK * BVs / NT : 1;
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
     }
     __syncthreads();
     if constexpr (DK == 128) {
-        // S_new = A S + B on the matrix cores: 8 row tiles of 16 x 16, two per
+        // S_new = A S + B on the matrix cores: 8 row tiles of 16 x 16, one per
         // wave. A and B go through two register sets: step p stages its set
         // into LDS and the accumulators and then loads step p + 2's into it, so
         // every load has two steps to land (past the last step the loads repeat
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
         const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
         struct Regs {
             float4 a[kPer];
-            float b[2][4];
+            float b[4];
         };
         auto issue = [&](int p, Regs& R) {
             const int64_t seg = (int64_t)n * P + (p < P ? p : P - 1);
@@ -106,9 +110,7 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
 #pragma unroll
             for (int u = 0; u < kPer; ++u) R.a[u] = a4[tid + NT * u];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) R.b[t][i] = b[(int64_t)(16 * (2 * w + t) + 4 * lg + i) * Dv + c0 + l16];
+            for (int i = 0; i < 4; ++i) R.b[i] = b[(int64_t)(16 * w + 4 * lg + i) * Dv + c0 + l16];
         };
         // one step; false once the chain is done
         auto step = [&](int p, Regs& R) -> bool {
@@ -125,30 +127,33 @@ __global__ __launch_bounds__(256) void split_scan_kernel(const float* A, const f
                 const int r = q / (DK / 4), c = (q % (DK / 4)) * 4;
                 sA[r][c] = R.a[u].x; sA[r][c + 1] = R.a[u].y; sA[r][c + 2] = R.a[u].z; sA[r][c + 3] = R.a[u].w;
             }
-            f32x4 acc[2];
+            f32x4 acc;
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[t][i] = R.b[t][i];
+            for (int i = 0; i < 4; ++i) acc[i] = R.b[i];
             __syncthreads();
             issue(p + 2, R);
             // from a zero initial state, S_in(1) = B(0): A(0) is not read (the
             // bf16 split does not compute it)
             if (p > 0 || s0) {
+                // every operand is read from LDS before the products start (one
+                // LDS round trip per product would set the pace), and the tile
+                // accumulates in four independent chains
+                constexpr int KS = DK / 4;   // k-steps of 4 channels
+                float bs[KS], as[KS];
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int r0 = 16 * (2 * w + t);
-#pragma unroll 8
-                    for (int ks = 0; ks < DK / 4; ++ks)
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[r0 + l16][4 * ks + lg],
-                                                                      sS[4 * ks + lg][l16], acc[t], 0, 0, 0);
+                for (int ks = 0; ks < KS; ++ks) {
+                    bs[ks] = sS[4 * ks + lg][l16];
+                    as[ks] = sA[16 * w + l16][4 * ks + lg];
                 }
+                f32x4 part[4] = {acc, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    part[ks & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(as[ks], bs[ks], part[ks & 3], 0, 0, 0);
+                acc = (part[0] + part[1]) + (part[2] + part[3]);
             }
             __syncthreads();
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sS[16 * (2 * w + t) + 4 * lg + i][l16] = acc[t][i];
+            for (int i = 0; i < 4; ++i) sS[16 * w + 4 * lg + i][l16] = acc[i];
             __syncthreads();
             return p + 1 < P;
         };
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void split_correct_kernel(const int32_t* cu
     const int seg = unit / H, h = unit % H;
     if (seg % P == 0) return;                       // the whole workgroup
     int64_t bos, len;
-    split_segment(cu, T0, P, seg, bos, len);
+    split_segment(cu, T0, P, 2, seg, bos, len);
     const int64_t eos = bos + len;
     if ((int64_t)r * 64 >= eos - bos) return;       // the whole workgroup
     const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
@@ -412,7 +417,7 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
         p1.aug_sT = AI;
         p1.aug_o = oA;
         if ((e = launch_chunk_mfma(p1, s)) != hipSuccess) return e;
-        split_scan_kernel<128><<<dim3((unsigned)(a.N * a.H * (a.Dv / 16))), dim3(256), 0, s>>>(
+        split_scan_kernel<128><<<dim3((unsigned)(a.N * a.H * (a.Dv / 16))), dim3(scan_threads<128>()), 0, s>>>(
             AI, Bst, nullptr, Sin, a.sT, a.N, a.H, a.Dv, P);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (!a.o) return hipSuccess;
@@ -445,7 +450,7 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a, int32_t P, void* workspace
                      AI, Bst, a.s0, Sin, a.sT, a.N, a.H, a.Dv, P); break;
         case 64: split_scan_kernel<64><<<dim3((unsigned)(a.N * a.H * (a.Dv / 16))), dim3(256), 0, s>>>(
                      AI, Bst, a.s0, Sin, a.sT, a.N, a.H, a.Dv, P); break;
-        default: split_scan_kernel<128><<<dim3((unsigned)(a.N * a.H * (a.Dv / 16))), dim3(256), 0, s>>>(
+        default: split_scan_kernel<128><<<dim3((unsigned)(a.N * a.H * (a.Dv / 16))), dim3(scan_threads<128>()), 0, s>>>(
                      AI, Bst, a.s0, Sin, a.sT, a.N, a.H, a.Dv, P); break;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;

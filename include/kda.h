@@ -204,14 +204,23 @@ size_t kda_chunk_fwd_split_workspace_bytes(int32_t B, int32_t T, int32_t H, int3
  * not available on its first KDA path and feeds long inputs as packed THD with
  * context parallelism (ISEEKYAN/k3 README); this is the same idea inside one
  * GPU. Over a segment the recurrence is affine in its entry state,
- * S_out = A S_in + B, so the call runs the forward over all segments from zero
- * states (B), again with v = 0 from identity states (A, d_k x d_k), chains the
- * entry states S_in(p) = A(p-1) S_in(p-1) + B(p-1) per sequence, and runs the
- * forward over all segments once more from S_in, which writes o.
+ * S_out = A S_in + B (B: the final state from a zero entry state; A, d_k x d_k:
+ * from the identity with v = 0), and so is every row's state, so a row's
+ * output is its output from a zero entry state plus S_inᵀ (scale A_tᵀ q_t).
+ *   bf16, d_k = d_v = 128: one launch runs B over every segment (a sequence's
+ *   first segment from its initial state, so its outputs are final) and A
+ *   over the others, keeping A's outputs; a scan chains the entry states
+ *   S_in(p) = A(p-1) S_in(p-1) + B(p-1) per sequence; a last kernel adds the
+ *   correction to the rows of segments after the first.
+ *   Other shapes: the forward over all segments from zero states (B), again
+ *   with v = 0 from identity states (A), the scan, and the forward over all
+ *   segments once more from S_in, which writes o.
  *
- * Segments are cut at multiples of 64 rows: sequence n of length L gets
- * segments of roundup(ceil(L/segments), 64) rows, the last shorter and
- * trailing ones possibly empty. The results equal kda_chunk_fwd's up to
+ * Segments are cut at multiples of 64 rows. With s = roundup(ceil(L/(segments
+ * + w - 1)), 64) for a sequence of length L, the first segment takes w * s
+ * rows and each later one s rows, the last shorter and trailing ones possibly
+ * empty; w = 2 on the bf16 d_k = d_v = 128 path (its first segments run one
+ * pass, the others two), 1 otherwise. The results equal kda_chunk_fwd's up to
  * rounding (the entry states carry the rounding of A and B).
  *
  *   segments   1 .. 4096; 1 (or T = 0) runs kda_chunk_fwd and needs no

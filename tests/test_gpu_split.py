@@ -86,8 +86,8 @@ def test_split_first_segment_rows_equal_the_plain_call():
     o1, _ = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["initial_state"])
     o2, _ = kda.chunk_fwd_split(d["q"], d["k"], d["v"], d["g"], d["beta"], P, initial_state=d["initial_state"])
     torch.cuda.synchronize()
-    seg = -(-T // P)
-    seg = -(-seg // 64) * 64            # segment length: ceil(T / P) rounded up to 64 rows
+    seg = -(-T // (P + 1))
+    seg = 2 * (-(-seg // 64) * 64)      # first segment: two shares of ceil(T / (P + 1)) rounded up to 64 rows
     say(f"[case] split first segment ({seg} rows of {T}) against the plain call, bitwise")
     assert torch.equal(o1[:, :seg], o2[:, :seg])
 
