@@ -242,15 +242,43 @@ __global__ __launch_bounds__(scan_threads<DK>()) void split_scan_kernel(const fl
 // D = S_inᵀ oAᵀ (16x16x32 bf16): S_in split into bf16 hi + lo parts (float32
 // accuracy for the state) held in registers, oA exact (it is stored in bf16).
 // A block's oA rows (16 KB) go straight from global memory to LDS, once for
-// the four waves, in two buffers: block b+1 (and its o rows, into registers)
-// is loaded while block b is computed. In LDS, 16-byte piece c of row i sits
+// the four waves, in a ring of three buffers: blocks b+1 and b+2 (and their o
+// rows, into registers) are in flight while block b is computed, and the wait
+// before block b counts only its own loads, not the stores of the blocks
+// before it. In LDS, 16-byte piece c of row i sits
 // at position c ^ (i % 16) of the row, so the 16 rows that one operand read
 // touches fall in different banks.
 constexpr int kCorrBlockBytes = 64 * 256;
+// s_waitcnt operand that waits until at most n vector-memory operations are
+// outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima)
+constexpr int vmcnt_wait(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+// The workgroup barrier of the correction loop, with no memory fence. A fence
+// (that of __syncthreads(), or one on LDS alone) waits for every global access
+// of the wave, the global-to-LDS loads of later blocks included. Here each
+// wave has waited, with an exact count, for its own loads of the block it is
+// about to read, and has consumed its reads of the buffer that the next loads
+// overwrite, so the barrier only has to align the waves; the empty asm keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// A buffer descriptor over [base, base + bytes), built from wave-uniform
+// values (the stores through it then need no per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), 0, n, 0x00020000);
+}
 __global__ __launch_bounds__(256, 2) void split_correct_kernel(const int32_t* cu, int32_t T0, int32_t P, int32_t H,
                                                                int32_t R, const float* Sin, const __bf16* oA,
                                                                __bf16* o) {
-    __shared__ __attribute__((aligned(16))) char buf[2][kCorrBlockBytes];
+    __shared__ __attribute__((aligned(16))) char buf[3][kCorrBlockBytes];
     const int r = blockIdx.x % R;
     const int unit = blockIdx.x / R;
     const int seg = unit / H, h = unit % H;
@@ -299,8 +327,11 @@ __global__ __launch_bounds__(256, 2) void split_correct_kernel(const int32_t* cu
                 shi[t][ks][j] = hi;
                 slo[t][ks][j] = (__bf16)(x - (float)hi);
             }
-    uint2 obA[4][2], obB[4][2];
+    uint2 ob0[4][2], ob1[4][2], ob2[4][2];
     auto compute = [&](int64_t r0, int bi, const uint2 (&ob)[4][2]) {
+        // o from row r0 to the block's end or the segment's, whichever comes first
+        const int64_t nrows = eos - r0 < 64 ? eos - r0 : 64;
+        const __amdgpu_buffer_rsrc_t ro = uniform_rsrc(o + r0 * rstride, nrows * rstride * 2);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             // B operand: row 16rt + li, channels 32ks + 8lg..+7 (piece 4ks + lg)
@@ -315,41 +346,60 @@ __global__ __launch_bounds__(256, 2) void split_correct_kernel(const int32_t* cu
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(slo[t][ks], b, acc[t], 0, 0, 0);
                 }
             }
-            // D: lane (li, lg) holds row li of the tile, columns 32w + 16t + 4lg + i
-            const int64_t row = r0 + i;
-            if (row < eos) {
-                __bf16* orow = o + row * rstride + (int64_t)h * 128 + 32 * w + 4 * lg;
+            // D: lane (li, lg) holds row li of the tile, columns 32w + 16t + 4lg + i;
+            // every store is issued, and those of rows past the segment end fall
+            // outside the descriptor's range, where the hardware drops them
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const float y0 = __uint_as_float(ob[rt][t].x << 16) + acc[t][0];
-                    const float y1 = __uint_as_float(ob[rt][t].x & 0xffff0000u) + acc[t][1];
-                    const float y2 = __uint_as_float(ob[rt][t].y << 16) + acc[t][2];
-                    const float y3 = __uint_as_float(ob[rt][t].y & 0xffff0000u) + acc[t][3];
-                    *reinterpret_cast<uint2*>(orow + 16 * t) = uint2{pack2_bf16(y0, y1), pack2_bf16(y2, y3)};
-                }
+            for (int t = 0; t < 2; ++t) {
+                const float y0 = __uint_as_float(ob[rt][t].x << 16) + acc[t][0];
+                const float y1 = __uint_as_float(ob[rt][t].x & 0xffff0000u) + acc[t][1];
+                const float y2 = __uint_as_float(ob[rt][t].y << 16) + acc[t][2];
+                const float y3 = __uint_as_float(ob[rt][t].y & 0xffff0000u) + acc[t][3];
+                const int off = 2 * (i * (int)rstride + 128 * h + 32 * w + 16 * t + 4 * lg);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack2_bf16(y0, y1), pack2_bf16(y2, y3)}, ro, off, 0, 0);
             }
         }
     };
+    // Every block issues the same vector-memory operations per wave, past the
+    // segment end too (its loads then repeat the last row): issue() makes 12
+    // loads (4 into LDS, 8 into registers), compute() 8 stores. Before block k
+    // the operations issued after its loads are block k+1's loads (block 0),
+    // then block k-1's stores and block k+2's loads (block 1), then block k-2's
+    // stores as well, so the wait leaves 12, 20 or 28 outstanding, and the
+    // compiler, which sees the same operations on every path, needs no wait of
+    // its own.
+    constexpr int kLoads = 12, kStores = 8;
+    auto wait_block = [](int k) {
+        if (k == 0) __builtin_amdgcn_s_waitcnt(vmcnt_wait(kLoads));
+        else if (k == 1) __builtin_amdgcn_s_waitcnt(vmcnt_wait(kLoads + kStores));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_wait(kLoads + 2 * kStores));
+    };
     // every wave runs the same block sequence, so the barriers match
     const int64_t step = (int64_t)R * 64;
-    int64_t r0 = bos + (int64_t)r * 64;
-    issue(r0, 0, obA);
+    int64_t rk = bos + (int64_t)r * 64;
+    issue(rk, 0, ob0);
+    issue(rk + step, 1, ob1);
+    int k = 0;
+    // one block: its loads landed for every wave, the buffer of block k-1 is
+    // free for block k+2
+    auto stage = [&](int bi, const uint2 (&ob)[4][2], int bn, uint2 (&obn)[4][2]) -> bool {
+        wait_block(k);
+        lds_barrier();
+        issue(rk + 2 * step, bn, obn);
+        compute(rk, bi, ob);
+        if (rk + step >= eos) return false;
+        rk += step;
+        ++k;
+        return true;
+    };
     for (;;) {
-        // block r0 (buffer 0, obA) landed for every wave; buffer 1 is free
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        __syncthreads();
-        const int64_t r1 = r0 + step;
-        if (r1 < eos) issue(r1, 1, obB);
-        compute(r0, 0, obA);
-        if (r1 >= eos) break;
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-        const int64_t r2 = r1 + step;
-        if (r2 < eos) issue(r2, 0, obA);
-        compute(r1, 1, obB);
-        if (r2 >= eos) break;
-        r0 = r2;
+        if (!stage(0, ob0, 2, ob2)) break;
+        if (!stage(1, ob1, 0, ob0)) break;
+        if (!stage(2, ob2, 1, ob1)) break;
     }
+    // the loads issued past the end still write LDS: they land before the
+    // workgroup ends and its LDS goes to another
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
 }
 
 unsigned grid_for(int64_t n) {
