@@ -86,7 +86,14 @@ constexpr int kFwdWaveRows = 64;
 constexpr int kFwdBlockRows = 4 * kFwdWaveRows;
 constexpr int kFwdBlockCh = 64 * kFwdCh;
 constexpr int kFwdGroup = 8;
+typedef uint32_t ntu2 __attribute__((ext_vector_type(2)));
+typedef float ntf4 __attribute__((ext_vector_type(4)));
 
+// Four-channel accesses (the streaming kernels' unit). Loads are
+// non-temporal: every input element is read once (the halo rows a second time
+// by the neighbouring wave). Stores keep the default policy, since the
+// forward's outputs are read right after by the chunk kernel, except
+// store_nt, for outputs that nothing reads soon (the backward's dx).
 template <typename T, int N> struct LoadN;
 template <typename T> struct LoadN<T, 8> {
     static __device__ __forceinline__ void load(const T* p, float (&f)[8]) { Vec8<T>::load(p, f); }
@@ -94,16 +101,19 @@ template <typename T> struct LoadN<T, 8> {
 };
 template <> struct LoadN<float, 4> {
     static __device__ __forceinline__ void load(const float* p, float (&f)[4]) {
-        const float4 a = *reinterpret_cast<const float4*>(p);
+        const ntf4 a = __builtin_nontemporal_load(reinterpret_cast<const ntf4*>(p));
         f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
     }
     static __device__ __forceinline__ void store(float* p, const float (&f)[4]) {
         *reinterpret_cast<float4*>(p) = float4{f[0], f[1], f[2], f[3]};
     }
+    static __device__ __forceinline__ void store_nt(float* p, const float (&f)[4]) {
+        __builtin_nontemporal_store(ntf4{f[0], f[1], f[2], f[3]}, reinterpret_cast<ntf4*>(p));
+    }
 };
 template <> struct LoadN<__bf16, 4> {
     static __device__ __forceinline__ void load(const __bf16* p, float (&f)[4]) {
-        const uint2 u = *reinterpret_cast<const uint2*>(p);
+        const ntu2 u = __builtin_nontemporal_load(reinterpret_cast<const ntu2*>(p));
         f[0] = __uint_as_float(u.x << 16); f[1] = __uint_as_float(u.x & 0xffff0000u);
         f[2] = __uint_as_float(u.y << 16); f[3] = __uint_as_float(u.y & 0xffff0000u);
     }
@@ -342,7 +352,7 @@ __device__ __forceinline__ void conv_bwd_group(const ConvBwdArgs& a, const T* x,
 #pragma unroll
             for (int i = 0; i < kBwdCh; ++i)
                 out[i] = fmaf(s.w[i][0], dp[i], fmaf(s.w[i][1], s.d1[i], fmaf(s.w[i][2], s.d2[i], s.w[i][3] * s.d3[i])));
-            LoadN<float, kBwdCh>::store(a.dx + t * a.C + c0, out);
+            LoadN<float, kBwdCh>::store_nt(a.dx + t * a.C + c0, out);
         }
 #pragma unroll
         for (int i = 0; i < kBwdCh; ++i) {
@@ -406,7 +416,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void short_conv_bwd_kernel(ConvBwdA
 #pragma unroll
                         for (int i = 0; i < kBwdCh; ++i) out[i] += df[i];
                     }
-                    LoadN<float, kBwdCh>::store(a.dx + t * a.C + c0, out);
+                    LoadN<float, kBwdCh>::store_nt(a.dx + t * a.C + c0, out);
                 }
                 if (u >= te) break;
                 find_sequence(f, u, n, bos, eos);    // the next non-empty sequence starts at u
