@@ -317,13 +317,15 @@ kda_status kda_chunk_fwd_conv(const void* xq, const void* xk, const void* xv, co
     }
     hipError_t e = hipSuccess;
     if (fused) {
-        // q and k by the streaming convolution into the workspace; v is
-        // convolved inside the chunk kernel by its state waves
-        for (int t = 0; t < 2 && e == hipSuccess && T > 0; ++t) {
-            kda::ConvArgs ct = c[t];
-            ct.y = ws + t * rows * Dk * 2;
-            ct.state_out = nullptr;
-            e = kda::launch_short_conv(ct, s);
+        // q and k by the streaming convolution into the workspace (one
+        // launch); v is convolved inside the chunk kernel by its state waves
+        if (T > 0) {
+            kda::ConvArgs ct[2] = {c[0], c[1]};
+            for (int t = 0; t < 2; ++t) {
+                ct[t].y = ws + t * rows * Dk * 2;
+                ct[t].state_out = nullptr;
+            }
+            e = kda::launch_short_conv_set(ct, 2, s);
         }
         a.q = T > 0 ? ws : nullptr;
         a.k = T > 0 ? ws + rows * Dk * 2 : nullptr;
@@ -338,11 +340,12 @@ kda_status kda_chunk_fwd_conv(const void* xq, const void* xk, const void* xv, co
             e = kda::launch_chunk_mfma(a, s);
         }
     } else {
-        // every other shape: the three convolutions into the workspace, then the prologue forward
-        for (int t = 0; t < 3 && e == hipSuccess && T > 0; ++t) {
-            kda::ConvArgs ct = c[t];
-            ct.state_out = nullptr;
-            e = kda::launch_short_conv(ct, s);
+        // every other shape: the three convolutions into the workspace (one
+        // launch), then the prologue forward
+        if (T > 0) {
+            kda::ConvArgs ct[3] = {c[0], c[1], c[2]};
+            for (int t = 0; t < 3; ++t) ct[t].state_out = nullptr;
+            e = kda::launch_short_conv_set(ct, 3, s);
         }
         if (e == hipSuccess) {
             a.q = c[0].y;
@@ -353,12 +356,12 @@ kda_status kda_chunk_fwd_conv(const void* xq, const void* xk, const void* xv, co
             if (ls != KDA_OK) return ls;
         }
     }
-    // final conv states (the last three inputs of every window)
-    for (int t = 0; t < 3 && e == hipSuccess; ++t) {
-        if (!s1s[t] || N == 0) continue;
-        kda::ConvArgs ct = c[t];
-        ct.y = nullptr;
-        e = kda::launch_short_conv(ct, s);
+    // final conv states (the last three inputs of every window), after
+    // everything that reads the initial ones, which they may alias; one launch
+    if (e == hipSuccess && N > 0 && (s1s[0] || s1s[1] || s1s[2])) {
+        kda::ConvArgs ct[3] = {c[0], c[1], c[2]};
+        for (int t = 0; t < 3; ++t) ct[t].y = nullptr;
+        e = kda::launch_short_conv_set(ct, 3, s);
     }
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KDA_OK;

@@ -196,6 +196,12 @@ int64_t short_conv_bwd_blocks(int32_t B, int32_t T);
 hipError_t launch_short_conv_bwd(const ConvBwdArgs& a, hipStream_t s);
 
 hipError_t launch_short_conv(const ConvArgs& a, hipStream_t s);
+// Several convolutions of one layer's projections in one launch of each
+// kernel (same dtype, activation, B, T and N; C may differ): the convolution
+// of every one whose y is set, then the final state of every one whose
+// state_out is set.
+constexpr int kMaxConvSet = 3;
+hipError_t launch_short_conv_set(const ConvArgs* a, int count, hipStream_t s);
 hipError_t launch_short_conv_step(const ConvStepArgs& a, hipStream_t s);
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t s);     // bf16, Dk=Dv=128, 16-row chunks

@@ -11,6 +11,8 @@
 // wave walks a run of consecutive tokens keeping the three previous inputs in
 // registers, so every wave access is contiguous across lanes and every input
 // is read once (plus a three-token halo per run).
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -18,6 +20,13 @@ namespace kda {
 namespace {
 
 constexpr int kThreadsConv = 256;
+
+// Up to kMaxConvSet convolutions of one layer's projections (same dtype,
+// activation, B, T and N; C may differ) in one launch: blockIdx.z picks the
+// projection.
+struct ConvSet {
+    ConvArgs p[kMaxConvSet];
+};
 
 template <typename T> struct Vec8;
 template <> struct Vec8<__bf16> {
@@ -161,7 +170,9 @@ __device__ __forceinline__ void conv_fwd_group(const ConvArgs& a, const T* x, T*
 }
 
 template <typename T, bool kAct>
-__global__ __launch_bounds__(256) void short_conv_kernel(ConvArgs a) {
+__global__ __launch_bounds__(256) void short_conv_kernel(ConvSet set) {
+    const ConvArgs& a = set.p[blockIdx.z];   // the projection
+    if (!a.y) return;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t c0 = (int64_t)blockIdx.y * kFwdBlockCh + (int64_t)lane * kFwdCh;
     const int64_t BT = (int64_t)a.B * a.T;
@@ -216,10 +227,11 @@ __global__ __launch_bounds__(256) void short_conv_kernel(ConvArgs a) {
 // thread per (sequence, 8 channels) reads all three before writing, so the
 // output may alias the input state.
 template <typename T>
-__global__ __launch_bounds__(kThreadsConv) void short_conv_state_kernel(ConvArgs a) {
+__global__ __launch_bounds__(kThreadsConv) void short_conv_state_kernel(ConvSet set) {
+    const ConvArgs& a = set.p[blockIdx.z];   // the projection
     const int64_t c0 = ((int64_t)blockIdx.y * kThreadsConv + threadIdx.x) * 8;
     const int n = blockIdx.x;
-    if (c0 >= a.C) return;
+    if (!a.state_out || c0 >= a.C) return;
     int64_t bos, eos;
     if (a.cu) {
         bos = a.cu[n];
@@ -587,19 +599,30 @@ hipError_t launch_conv_bwd_t(const ConvBwdArgs& a, hipStream_t s) {
 }
 
 template <typename T>
-hipError_t launch_conv_t(const ConvArgs& a, hipStream_t s) {
-    const int64_t BT = (int64_t)a.B * a.T;
-    const unsigned cgroups = (unsigned)((a.C / 8 + kThreadsConv - 1) / kThreadsConv);
-    if (BT > 0 && a.y) {   // (a null y: only the final states)
-        const dim3 grid((unsigned)((BT + kFwdBlockRows - 1) / kFwdBlockRows),
-                        (unsigned)((a.C + kFwdBlockCh - 1) / kFwdBlockCh));
-        if (a.act)
-            hipLaunchKernelGGL((short_conv_kernel<T, true>), grid, dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((short_conv_kernel<T, false>), grid, dim3(256), 0, s, a);
+hipError_t launch_conv_t(const ConvArgs* a, int count, hipStream_t s) {
+    ConvSet set;
+    int64_t cmax = 0;
+    bool any_y = false, any_state = false;
+    for (int i = 0; i < count; ++i) {
+        set.p[i] = a[i];
+        cmax = std::max<int64_t>(cmax, a[i].C);
+        any_y |= a[i].y != nullptr;            // (a null y: only the final state)
+        any_state |= a[i].state_out != nullptr;
     }
-    if (a.state_out && a.N > 0)
-        hipLaunchKernelGGL((short_conv_state_kernel<T>), dim3((unsigned)a.N, cgroups), dim3(kThreadsConv), 0, s, a);
+    const int64_t BT = (int64_t)a[0].B * a[0].T;
+    if (BT > 0 && any_y) {
+        const dim3 grid((unsigned)((BT + kFwdBlockRows - 1) / kFwdBlockRows),
+                        (unsigned)((cmax + kFwdBlockCh - 1) / kFwdBlockCh), (unsigned)count);
+        if (a[0].act)
+            hipLaunchKernelGGL((short_conv_kernel<T, true>), grid, dim3(256), 0, s, set);
+        else
+            hipLaunchKernelGGL((short_conv_kernel<T, false>), grid, dim3(256), 0, s, set);
+    }
+    if (any_state && a[0].N > 0) {
+        const unsigned cgroups = (unsigned)((cmax / 8 + kThreadsConv - 1) / kThreadsConv);
+        hipLaunchKernelGGL((short_conv_state_kernel<T>), dim3((unsigned)a[0].N, cgroups, (unsigned)count),
+                           dim3(kThreadsConv), 0, s, set);
+    }
     return hipGetLastError();
 }
 
@@ -616,7 +639,12 @@ hipError_t launch_conv_step_t(const ConvStepArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_short_conv(const ConvArgs& a, hipStream_t s) {
-    return a.bf16 ? launch_conv_t<__bf16>(a, s) : launch_conv_t<float>(a, s);
+    return launch_short_conv_set(&a, 1, s);
+}
+
+hipError_t launch_short_conv_set(const ConvArgs* a, int count, hipStream_t s) {
+    if (count < 1 || count > kMaxConvSet) return hipErrorInvalidValue;
+    return a[0].bf16 ? launch_conv_t<__bf16>(a, count, s) : launch_conv_t<float>(a, count, s);
 }
 
 hipError_t launch_short_conv_step(const ConvStepArgs& a, hipStream_t s) {
