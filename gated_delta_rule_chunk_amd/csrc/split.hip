@@ -72,8 +72,13 @@ __global__ __launch_bounds__(scan_threads<DK>()) void split_scan_kernel(const fl
     constexpr int kQuads = DK * DK / 4;                       // float4 pieces of A
     constexpr int kPer = kQuads / NT > 0 ? kQuads / NT : 1;   // per thread
     constexpr int kOut = DK * BVs / NT > 0 ? DK * BVs / NT : 1;
-    __shared__ float sA[DK][DK + 4];
+    __shared__ __attribute__((aligned(16))) float sA[DK][DK + 4];
     __shared__ float sS[DK][BVs + 1];
+    // DK = 128: S again as bf16 hi and lo parts, transposed ([column][channel]),
+    // the B operands of the products
+    constexpr int kSplitRows = DK == 128 ? BVs : 1;
+    __shared__ __attribute__((aligned(16))) __bf16 sSh[kSplitRows][DK + 8];
+    __shared__ __attribute__((aligned(16))) __bf16 sSl[kSplitRows][DK + 8];
     const int tid = threadIdx.x;
     const int nvt = Dv / BVs;
     // blocks are dealt round-robin over the 8 XCDs: the column slices of one
@@ -89,12 +94,21 @@ __global__ __launch_bounds__(scan_threads<DK>()) void split_scan_kernel(const fl
     const int c0 = vt * BVs;
     for (int idx = tid; idx < DK * BVs; idx += NT) {
         const int c = idx / BVs, j = idx % BVs;
-        sS[c][j] = s0 ? s0[(((int64_t)n * H + h) * DK + c) * Dv + c0 + j] : 0.f;
+        const float x = s0 ? s0[(((int64_t)n * H + h) * DK + c) * Dv + c0 + j] : 0.f;
+        sS[c][j] = x;
+        if constexpr (DK == 128) {
+            const __bf16 hi = (__bf16)x;
+            sSh[j][c] = hi;
+            sSl[j][c] = (__bf16)(x - (float)hi);
+        }
     }
     __syncthreads();
     if constexpr (DK == 128) {
         // S_new = A S + B on the matrix cores: 8 row tiles of 16 x 16, one per
-        // wave. A and B go through two register sets: step p stages its set
+        // wave, each product as three bf16 products of hi and lo parts
+        // (A_hi S_hi + A_hi S_lo + A_lo S_hi, float32 accumulation; the lo lo
+        // term is below 2^-17 of the product). A and B go through two
+        // register sets: step p stages its set
         // into LDS and the accumulators and then loads step p + 2's into it, so
         // every load has two steps to land (past the last step the loads repeat
         // it).
@@ -136,24 +150,46 @@ __global__ __launch_bounds__(scan_threads<DK>()) void split_scan_kernel(const fl
             // bf16 split does not compute it)
             if (p > 0 || s0) {
                 // every operand is read from LDS before the products start (one
-                // LDS round trip per product would set the pace), and the tile
-                // accumulates in four independent chains
-                constexpr int KS = DK / 4;   // k-steps of 4 channels
-                float bs[KS], as[KS];
+                // LDS round trip per product would set the pace); lane (l16, lg)
+                // of k-block kb holds A[16w + l16][32kb + 8lg + s] and
+                // S[32kb + 8lg + s][l16], s = 0..7, and the three parts
+                // accumulate in separate chains
+                constexpr int KB = DK / 32;
+                bf16x8 ah[KB], al[KB], bh[KB], bl[KB];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    bs[ks] = sS[4 * ks + lg][l16];
-                    as[ks] = sA[16 * w + l16][4 * ks + lg];
+                for (int kb = 0; kb < KB; ++kb) {
+                    const float4 x0 = *reinterpret_cast<const float4*>(&sA[16 * w + l16][32 * kb + 8 * lg]);
+                    const float4 x1 = *reinterpret_cast<const float4*>(&sA[16 * w + l16][32 * kb + 8 * lg + 4]);
+                    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const __bf16 hi = (__bf16)xs[e];
+                        ah[kb][e] = hi;
+                        al[kb][e] = (__bf16)(xs[e] - (float)hi);
+                    }
+                    bh[kb] = *reinterpret_cast<const bf16x8*>(&sSh[l16][32 * kb + 8 * lg]);
+                    bl[kb] = *reinterpret_cast<const bf16x8*>(&sSl[l16][32 * kb + 8 * lg]);
                 }
-                f32x4 part[4] = {acc, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                f32x4 phh = acc, phl = {0.f, 0.f, 0.f, 0.f}, plh = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    part[ks & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(as[ks], bs[ks], part[ks & 3], 0, 0, 0);
-                acc = (part[0] + part[1]) + (part[2] + part[3]);
+                for (int kb = 0; kb < KB; ++kb) {
+                    phh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[kb], bh[kb], phh, 0, 0, 0);
+                    phl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[kb], bl[kb], phl, 0, 0, 0);
+                    plh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[kb], bh[kb], plh, 0, 0, 0);
+                }
+                acc = phh + (phl + plh);
             }
             __syncthreads();
+            bf16x4 hi4, lo4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sS[16 * w + 4 * lg + i][l16] = acc[i];
+            for (int i = 0; i < 4; ++i) {
+                sS[16 * w + 4 * lg + i][l16] = acc[i];
+                const __bf16 hb = (__bf16)acc[i];   // (through a scalar)
+                hi4[i] = hb;
+                lo4[i] = (__bf16)(acc[i] - (float)hb);
+            }
+            *reinterpret_cast<bf16x4*>(&sSh[l16][16 * w + 4 * lg]) = hi4;
+            *reinterpret_cast<bf16x4*>(&sSl[l16][16 * w + 4 * lg]) = lo4;
             __syncthreads();
             return p + 1 < P;
         };
