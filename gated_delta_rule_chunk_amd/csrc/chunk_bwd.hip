@@ -565,6 +565,20 @@ template <> struct Raw4<float> {
     __device__ __forceinline__ void load(const float* p, int64_t i) { v = *reinterpret_cast<const float4*>(p + i); }
     __device__ __forceinline__ float get(int u) const { return u == 0 ? v.x : u == 1 ? v.y : u == 2 ? v.z : v.w; }
 };
+// One element, raw: converted when it is used, not when it is loaded (a
+// conversion right after the load would wait for the data there and hold up
+// every load issued after it).
+template <typename T> struct Raw1;
+template <> struct Raw1<float> {
+    float v;
+    __device__ __forceinline__ void load(const float* p, int64_t i) { v = p[i]; }
+    __device__ __forceinline__ float get() const { return v; }
+};
+template <> struct Raw1<__bf16> {
+    uint16_t v;
+    __device__ __forceinline__ void load(const __bf16* p, int64_t i) { v = reinterpret_cast<const uint16_t*>(p)[i]; }
+    __device__ __forceinline__ float get() const { return __uint_as_float((uint32_t)v << 16); }
+};
 template <> struct Raw4<__bf16> {
     uint2 v;
     __device__ __forceinline__ void load(const __bf16* p, int64_t i) {
@@ -587,7 +601,7 @@ template <typename Tin, typename Tx>
 struct Fetch {
     Raw4<Tin> q, k, g;
     Raw4<Tx> x;             // x: v for threads < 256, dO for the others
-    float beta;
+    Raw1<Tin> beta;
     float4 s[4];            // entry state slice (reverse sweep)
     float m[3];             // T, P, KK entries (threads < 256)
     bool in_qk, in_x, in_b;
@@ -608,7 +622,7 @@ __device__ __forceinline__ void fetch_chunk(Fetch<Tin, Tx>& f, const BwdArgs& a,
     {
         const int r = tid & (C - 1);
         f.in_b = r < rows;
-        f.beta = load_elem(static_cast<const Tin*>(a.beta), (sq.b * a.T + t0 + (f.in_b ? r : 0)) * a.H + h);
+        f.beta.load(static_cast<const Tin*>(a.beta), (sq.b * a.T + t0 + (f.in_b ? r : 0)) * a.H + h);
     }
     {
         const int t2 = tid & 255;
@@ -649,7 +663,7 @@ __device__ __forceinline__ void commit_qkg(Smem& sm, const Fetch<Tin, Tx>& f, bo
             if (reverse) sm.Qh[r][c + u] = f.in_qk ? f.q.get(u) : 0.f;
         }
     }
-    if (tid < C) sm.beta[tid] = f.in_b ? f.beta : 0.f;
+    if (tid < C) sm.beta[tid] = f.in_b ? f.beta.get() : 0.f;
 }
 
 // v or dO, T/P/KK and (reverse sweep) the entry state
@@ -903,12 +917,109 @@ __global__ __launch_bounds__(256) void chunk_mats_kernel(BwdArgs a) {
     }
 }
 
+// ---- forward sweep: one chunk's operands, prepared by waves 4-7 ----------
+// An operand set of the forward sweep: the scaled rows Kg and Kh, V, T,
+// beta and e^Gamma_C of one chunk.
+struct FwdSet {
+    float (*Kg)[KP];
+    float (*Kh)[KP];
+    float (*V)[VP];
+    float (*T)[CP];
+    float* beta;
+    float* EC;
+};
+
+// One chunk's inputs for the forward sweep, in the registers of the 256
+// prep threads (p = 0..255): k and g quads p and p + 256 of the 16 x 32, the
+// v quad p of the 16 x 16, T entry p and beta of row p % 16.
+template <typename Tin, typename Tx>
+struct FwdFetch {
+    Raw4<Tin> k[2], g[2];
+    Raw4<Tx> v;
+    Raw1<Tin> beta;
+    float t;
+    bool in_qk[2], in_v, in_b;
+};
+
+template <typename Tin, typename Tx>
+__device__ __forceinline__ void fwd_fetch(FwdFetch<Tin, Tx>& f, const BwdArgs& a, const SeqInfo& sq, int h,
+                                          int64_t t0, int rows, int c0, const float* mats, int p) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int q = p + 256 * u, r = q >> 5, c = (q & 31) * 4;
+        f.in_qk[u] = r < rows;
+        const int64_t e = ((sq.b * a.T + t0 + (f.in_qk[u] ? r : 0)) * a.H + h) * DK + c;
+        f.k[u].load(static_cast<const Tin*>(a.k), e);
+        f.g[u].load(static_cast<const Tin*>(a.g), e);
+    }
+    {
+        const int r = p >> 4, j = (p & 15) * 4;
+        f.in_v = r < rows;
+        const int64_t e = ((sq.b * a.T + t0 + (f.in_v ? r : 0)) * a.H + h) * (int64_t)a.Dv + c0 + j;
+        f.v.load(static_cast<const Tx*>(a.v), e);
+    }
+    {
+        const int r = p & (C - 1);
+        f.in_b = r < rows;
+        f.beta.load(static_cast<const Tin*>(a.beta), (sq.b * a.T + t0 + (f.in_b ? r : 0)) * a.H + h);
+    }
+    f.t = mats[p];   // T[p / C][p % C]
+}
+
+// raw k into Kg, the log2-scaled gate into G, v, T and beta (rows past the
+// sequence end are zero tokens)
+template <typename Tin, typename Tx>
+__device__ __forceinline__ void fwd_commit(Smem& sm, const FwdFetch<Tin, Tx>& f, const FwdSet& s, int p) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int q = p + 256 * u, r = q >> 5, c = (q & 31) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s.Kg[r][c + e] = f.in_qk[u] ? f.k[u].get(e) : 0.f;
+            sm.G[r][c + e] = f.in_qk[u] ? f.g[u].get(e) * kLog2e : 0.f;
+        }
+    }
+    {
+        const int r = p >> 4, j = (p & 15) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s.V[r][j + e] = f.in_v ? f.v.get(e) : 0.f;
+    }
+    s.T[p / C][p % C] = f.t;
+    if (p < C) s.beta[p] = f.in_b ? f.beta.get() : 0.f;
+}
+
+// Gamma (the in-chunk cumulative log2 decay) per channel and e^Gamma_C
+__device__ __forceinline__ void fwd_gamma(Smem& sm, const FwdSet& s, int p) {
+    if (p < DK) {
+        float run = 0.f;
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            run += sm.G[r][p];
+            sm.G[r][p] = run;
+        }
+        s.EC[p] = __builtin_amdgcn_exp2f(run);
+    }
+}
+
+// Kg = e^Gamma k and Kh = e^(Gamma_C - Gamma) k
+__device__ __forceinline__ void fwd_scale(Smem& sm, const FwdSet& s, int p) {
+#pragma unroll
+    for (int u = 0; u < C * DK / 256; ++u) {
+        const int idx = p + 256 * u;
+        const int r = idx / DK, c = idx % DK;
+        const float gr = sm.G[r][c];
+        const float k = s.Kg[r][c];
+        s.Kg[r][c] = __builtin_amdgcn_exp2f(gr) * k;
+        s.Kh[r][c] = __builtin_amdgcn_exp2f(sm.G[C - 1][c] - gr) * k;
+    }
+}
+
 // Tin: q, k, g and beta; Tx: v and dO (bf16 v and dO with float32 q, k, g
 // and beta come from the backward through the prologue, which widens only
 // what it computes).
 template <typename Tin, typename Tx>
 __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
-    __shared__ Smem sm;
+    __shared__ __attribute__((aligned(16))) Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
     const int nvt = a.Dv / BV;
     const bool atomic = nvt > 1;
@@ -927,94 +1038,136 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
     Fetch<Tin, Tx> f;
 
     // ---------------- forward sweep: chunk entry states ----------------
-    f32x4 st[4];
+    // Waves 0-3 carry the state (wave w: rows 32w..32w+31, MFMA result
+    // layout) through the chunks and store each chunk's entry state; waves
+    // 4-7 meanwhile load, commit and scale the next chunk into the other of
+    // two operand sets (the second set lives in arrays only the reverse
+    // sweep uses). Three barriers per chunk, each the end of a phase of both
+    // roles:
+    //   1. state rows to LDS                   | commit chunk c+1, fetch c+3
+    //   2. W = V - Kg S and U = T Diag(beta) W, one 16-column tile per wave
+    //                                         | Gamma of chunk c+1, e^Gamma_C
+    //   3. S <- Diag(e^Gamma_C) S + Kh^T U, then the entry state from LDS to
+    //      the workspace                      | Kg, Kh of chunk c+1
+    const bool chain = w < 4;
+    const int ptid = tid - 256;   // prep threads: 0..255
+    FwdSet set0{sm.Kg, sm.Kh, sm.dUW, sm.T, sm.beta, sm.EC};
+    FwdSet set1{sm.Qp, sm.Kp, sm.dO, sm.P, sm.dbp, &sm.dS[0][0]};
+    f32x4 st[2][4];
+    if (chain) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            st[t][i] = a.s0 ? a.s0[sbase + (int64_t)(cw + 4 * lg + i) * Dv + c0 + 16 * t + l16] : 0.f;
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st[rt][t][i] = a.s0 ? a.s0[sbase + (int64_t)(32 * w + 16 * rt + 4 * lg + i) * Dv + c0 + 16 * t + l16]
+                                        : 0.f;
+    }
     auto rows_of = [&](int64_t ch) { return (int)min<int64_t>(C, sq.len - ch * C); };
-    // Chunk ch + 1's inputs are fetched while chunk ch is computed, into the
-    // other of two register sets (the loop is unrolled by two, so no set is
-    // copied and every fetch is issued unconditionally). Past the last chunk
-    // the fetch re-reads the last chunk with no rows, and an odd count runs
-    // one extra such chunk: all-zero rows leave the state unchanged exactly,
-    // and its entry state is not stored.
-    auto fetch_fwd = [&](Fetch<Tin, Tx>& dst, int64_t ch) {
+    // Chunk ch's inputs into a prep register set. Past the last chunk the
+    // fetch re-reads the last chunk with no rows: such a chunk is all zero
+    // tokens, an exact identity step of the state.
+    auto fetch_fwd = [&](FwdFetch<Tin, Tx>& dst, int64_t ch) {
         const int64_t cc = ch < nch ? ch : nch - 1;
-        fetch_chunk<Tin, Tx>(dst, a, sq, h, sq.bos + cc * C, ch < nch ? rows_of(ch) : 0, c0, false, nullptr,
-                         mats_of(cc));
+        fwd_fetch<Tin, Tx>(dst, a, sq, h, sq.bos + cc * C, ch < nch ? rows_of(ch) : 0, c0, mats_of(cc), ptid);
     };
-    auto fwd_chunk = [&](int64_t ch, Fetch<Tin, Tx>& cur, Fetch<Tin, Tx>& nxt) {
-        float* ws = state_of(ch < nch ? ch : nch - 1);
-        const bool real = ch < nch;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = cw + 4 * lg + i, j = 16 * t + l16;
-                if (real) ws[(int64_t)c * Dv + j] = st[t][i];
-                sm.S[c][j] = st[t][i];
-            }
-        commit_qkg<Tin, Tx>(sm, cur, false);
-        commit_rest<Tin, Tx>(sm, cur, false);
-        fetch_fwd(nxt, ch + 1);
-        __syncthreads();
-        chunk_scale(sm, false);
-        __syncthreads();
-        // W = V - Kg S with the channel sum split over two waves per column
-        // tile: waves 4-7 leave their half in sm.dUW (free in this sweep)
-        f32x4 wpart = {0.f, 0.f, 0.f, 0.f};
-        {
-            const int t = w & 3, kb = (w >> 2) * (DK / 8);   // 32 k-steps of 4 channels, half each
-            f32x4 a1 = wpart;
-#pragma unroll 4
-            for (int ks = kb; ks < kb + DK / 8; ks += 2) {
-                wpart = mfma(sm.Kg[l16][4 * ks + lg], sm.S[4 * ks + lg][16 * t + l16], wpart);
-                a1 = mfma(sm.Kg[l16][4 * ks + 4 + lg], sm.S[4 * ks + 4 + lg][16 * t + l16], a1);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wpart[i] += a1[i];
-            if (w >= 4) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.dUW[4 * lg + i][16 * t + l16] = wpart[i];
-            }
+    FwdFetch<Tin, Tx> fa, fb;
+    if (nch > 0) {
+        // chunk 0 prepared before the loop; chunks 1 and 2 in flight
+        if (!chain) {
+            fetch_fwd(fa, 0);
+            fetch_fwd(fb, 1);
+            fwd_commit(sm, fa, set0, ptid);
+            fetch_fwd(fa, 2);
         }
         __syncthreads();
-        if (w < 4) {
+        if (!chain) fwd_gamma(sm, set0, ptid);
+        __syncthreads();
+        if (!chain) fwd_scale(sm, set0, ptid);
+        __syncthreads();
+    }
+    // chunk ch with its operands in `cur`; the prep waves commit chunk ch+1
+    // from `fn` into `nxt` and refill `fn` with chunk ch+3
+    auto fwd_chunk = [&](int64_t ch, const FwdSet& cur, const FwdSet& nxt, FwdFetch<Tin, Tx>& fn) {
+        if (chain) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sm.S[32 * w + 16 * rt + 4 * lg + i][16 * t + l16] = st[rt][t][i];
+        } else {
+            fwd_commit(sm, fn, nxt, ptid);
+            fetch_fwd(fn, ch + 3);
+        }
+        __syncthreads();
+        if (chain) {
+            // W = V - Kg S, columns 16w..16w+15, then U for the same columns
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll 8
+            for (int ks = 0; ks < DK / 4; ks += 2) {
+                a0 = mfma(cur.Kg[l16][4 * ks + lg], sm.S[4 * ks + lg][16 * w + l16], a0);
+                a1 = mfma(cur.Kg[l16][4 * ks + 4 + lg], sm.S[4 * ks + 4 + lg][16 * w + l16], a1);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * lg + i, j = 16 * w + l16;
-                sm.W[r][j] -= wpart[i] + sm.dUW[r][j];
+                sm.W[r][j] = cur.V[r][j] - (a0[i] + a1[i]);
             }
-            u_tile(sm, w, l16, lg);   // reads only this wave's columns of W
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < C / 4; ++ks) {
+                const int r = 4 * ks + lg;
+                u = mfma(cur.T[l16][r], cur.beta[r] * sm.W[r][16 * w + l16], u);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.U[4 * lg + i][16 * w + l16] = u[i];
+        } else {
+            fwd_gamma(sm, nxt, ptid);
         }
         __syncthreads();
-        // S <- Diag(e^Gamma_C) S + Kh^T U
-        {
-            float ak[4];
+        if (chain) {
+            // S <- Diag(e^Gamma_C) S + Kh^T U, rows 32w..32w+31
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) ak[ks] = sm.Kh[4 * ks + lg][cw + l16];
+            for (int rt = 0; rt < 2; ++rt) {
+                const int cw2 = 32 * w + 16 * rt;
+                float ak[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                f32x4 acc;
+                for (int ks = 0; ks < 4; ++ks) ak[ks] = cur.Kh[4 * ks + lg][cw2 + l16];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = sm.EC[cw + 4 * lg + i] * st[t][i];
+                for (int t = 0; t < 4; ++t) {
+                    f32x4 acc;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mfma(ak[ks], sm.U[4 * ks + lg][16 * t + l16], acc);
-                st[t] = acc;
+                    for (int i = 0; i < 4; ++i) acc[i] = cur.EC[cw2 + 4 * lg + i] * st[rt][t][i];
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) acc = mfma(ak[ks], sm.U[4 * ks + lg][16 * t + l16], acc);
+                    st[rt][t] = acc;
+                }
             }
+            // the entry state (still in sm.S) to the workspace, in 16-byte
+            // pieces of this wave's rows: here, after the products, they neither
+            // delay the products' LDS reads nor queue ahead of the prep waves'
+            // loads in phase 1
+            if (ch < nch) {
+                float* ws = state_of(ch);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int q = lane + 64 * u, c = 32 * w + (q >> 4), j = (q & 15) * 4;
+                    *reinterpret_cast<float4*>(ws + (int64_t)c * Dv + j) = *reinterpret_cast<const float4*>(&sm.S[c][j]);
+                }
+            }
+        } else {
+            fwd_scale(sm, nxt, ptid);
         }
         __syncthreads();
     };
-    if (nch > 0) {
-        Fetch<Tin, Tx> fb;
-        fetch_fwd(f, 0);
-        for (int64_t ch = 0; ch < nch; ch += 2) {
-            fwd_chunk(ch, f, fb);
-            fwd_chunk(ch + 1, fb, f);
-        }
+    for (int64_t ch = 0; ch < nch; ch += 2) {
+        fwd_chunk(ch, set0, set1, fb);
+        fwd_chunk(ch + 1, set1, set0, fa);
     }
+    // the entry states stored above are read below by other waves
+    __syncthreads();
 
     // ---------------- backward sweep ----------------
     f32x4 ds[4];
