@@ -74,6 +74,15 @@ def test_bwd_bf16_k3_dims(B, T, H):
     _check(inp, d_o, dfin, scale=128 ** -0.5, label=f"bf16 B={B} T={T} H={H}")
 
 
+@pytest.mark.parametrize("dtype,T", [("bf16", 99), ("f32", 50)])
+def test_bwd_dv64_one_value_slice(dtype, T):
+    # d_k = 128, d_v = 64: the matrix-core backward with one workgroup per
+    # (sequence, head) over all value columns (no atomic sums); 7 and 4 chunks
+    inp = synth.make_chunk_inputs(2, T, 3, 128, 64, seed=515 + T, dtype=dtype, init_state=True)
+    d_o, dfin = synth.make_cotangents(inp, seed=516 + T)
+    _check(inp, d_o, dfin, scale=0.5, label=f"{dtype} Dk=128 Dv=64 T={T}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_bwd_packed_ragged(dtype):
     inp = synth.make_chunk_inputs(1, 0, 3, 128, 128, seed=520, dtype=dtype, init_state=True,
