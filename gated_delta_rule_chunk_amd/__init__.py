@@ -61,6 +61,12 @@ def load_library(path: str = LIB_PATH):
     lib.kda_recurrent_step.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F,
                                        ctypes.c_int, P, P]
     lib.kda_recurrent_step.restype = ctypes.c_int
+    lib.kda_recurrent_step_prologue.argtypes = [P, P, P, P, P, P, P, F, F, P, P, I32, I32, I32, I32, I32, F,
+                                                ctypes.c_int, P, P]
+    lib.kda_recurrent_step_prologue.restype = ctypes.c_int
+    lib.kda_recurrent_step_conv.argtypes = [P, P, P, P, P, P, P, P, P, I32, P, P, P, P, F, F, P, P, I32, I32, I32,
+                                            I32, I32, F, ctypes.c_int, P, P]
+    lib.kda_recurrent_step_conv.restype = ctypes.c_int
     lib.kda_short_conv.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, ctypes.c_int, P, P, P]
     lib.kda_short_conv.restype = ctypes.c_int
     lib.kda_short_conv_bwd_workspace_bytes.argtypes = [I32, I32, I32]
@@ -571,6 +577,96 @@ def recurrent_step(q, k, v, g, beta, state_cache, state_slots=None, scale=1.0, o
     st = lib.kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_cache),
                                 _ptr(state_slots), n_slots, Nb, H, Dk, Dv, float(scale),
                                 _DTYPES[dt], _ptr(out), _stream(dev))
+    _check(st)
+    return out
+
+
+def _step_shapes(q, v, state_cache, state_slots):
+    if q.dim() != 3:
+        raise ValueError("q must be [Nb,H,Dk]")
+    Nb, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if state_cache.dim() != 4:
+        raise ValueError("state_cache must be [n_slots,H,Dk,Dv]")
+    n_slots = state_cache.shape[0]
+    _need(state_cache, "state_cache", (n_slots, H, Dk, Dv), torch.float32, dev)
+    if state_slots is not None:
+        _need(state_slots, "state_slots", (Nb,), torch.int32, dev)
+    return Nb, H, Dk, Dv, n_slots, dev
+
+
+def _step_raw_inputs(q, k, v, g_logit, beta_logit, A_log, dt_bias, names):
+    Nb, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for t, n, shp in ((q, names[0], (Nb, H, Dk)), (k, names[1], (Nb, H, Dk)), (v, names[2], (Nb, H, Dv)),
+                      (g_logit, "g_logit", (Nb, H, Dk)), (beta_logit, "beta_logit", (Nb, H))):
+        _need(t, n, shp, dt, dev)
+    _need(A_log, "A_log", (Dk,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H * Dk,), torch.float32, dev)
+
+
+def recurrent_step_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, state_cache, state_slots=None,
+                            gate_lower_bound=-5.0, l2_eps=1e-6, scale=1.0, out=None):
+    """One decode step from raw projections (kda_recurrent_step_prologue): the
+    gate, beta and normalisation prologue, then the step against
+    ``state_cache`` (updated in place).
+
+    q_raw, k_raw, g_logit [Nb,H,Dk]; v [Nb,H,Dv]; beta_logit [Nb,H]; A_log [Dk]
+    and dt_bias [H*Dk] float32; state_cache [n_slots,H,Dk,Dv] float32;
+    state_slots int32 [Nb] or None. Returns o [Nb,H,Dv].
+    """
+    lib = load_library()
+    Nb, H, Dk, Dv, n_slots, dev = _step_shapes(q_raw, v, state_cache, state_slots)
+    _step_raw_inputs(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, ("q_raw", "k_raw", "v"))
+    dt = q_raw.dtype
+    if out is None:
+        out = torch.empty((Nb, H, Dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", (Nb, H, Dv), dt, dev)
+    st = lib.kda_recurrent_step_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(g_logit), _ptr(beta_logit),
+                                         _ptr(A_log), _ptr(dt_bias), float(gate_lower_bound), float(l2_eps),
+                                         _ptr(state_cache), _ptr(state_slots), n_slots, Nb, H, Dk, Dv, float(scale),
+                                         _DTYPES[dt], _ptr(out), _stream(dev))
+    _check(st)
+    return out
+
+
+def recurrent_step_conv(xq, xk, xv, wq, wk, wv, conv_caches, g_logit, beta_logit, A_log, dt_bias, state_cache,
+                        state_slots=None, activation=True, gate_lower_bound=-5.0, l2_eps=1e-6, scale=1.0, out=None):
+    """One generated token from the projections before the short convolution
+    (kda_recurrent_step_conv): the convolution step of q, k and v over
+    ``conv_caches``, the prologue and the decode step, all caches updated in
+    place.
+
+    xq, xk, g_logit [Nb,H,Dk]; xv [Nb,H,Dv]; beta_logit [Nb,H]; wq, wk [H*Dk,4]
+    and wv [H*Dv,4] float32; conv_caches (q, k, v) [n_slots,3,H*D] float32,
+    indexed by the state slots; the rest as for ``recurrent_step_prologue``.
+    Returns o [Nb,H,Dv].
+    """
+    lib = load_library()
+    Nb, H, Dk, Dv, n_slots, dev = _step_shapes(xq, xv, state_cache, state_slots)
+    _step_raw_inputs(xq, xk, xv, g_logit, beta_logit, A_log, dt_bias, ("xq", "xk", "xv"))
+    cq, ck, cv = conv_caches
+    for t, n, C in ((wq, "wq", H * Dk), (wk, "wk", H * Dk), (wv, "wv", H * Dv)):
+        _need(t, n, (C, 4), torch.float32, dev)
+    for t, n, C in ((cq, "conv_cache_q", H * Dk), (ck, "conv_cache_k", H * Dk), (cv, "conv_cache_v", H * Dv)):
+        _need(t, n, (n_slots, 3, C), torch.float32, dev)
+    dt = xq.dtype
+    if out is None:
+        out = torch.empty((Nb, H, Dv), dtype=dt, device=dev)
+    else:
+        _need(out, "out", (Nb, H, Dv), dt, dev)
+    st = lib.kda_recurrent_step_conv(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(cq),
+                                     _ptr(ck), _ptr(cv), int(bool(activation)), _ptr(g_logit), _ptr(beta_logit),
+                                     _ptr(A_log), _ptr(dt_bias), float(gate_lower_bound), float(l2_eps),
+                                     _ptr(state_cache), _ptr(state_slots), n_slots, Nb, H, Dk, Dv, float(scale),
+                                     _DTYPES[dt], _ptr(out), _stream(dev))
     _check(st)
     return out
 

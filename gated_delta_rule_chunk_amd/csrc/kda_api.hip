@@ -197,6 +197,60 @@ kda_status launch_chunk(const char* fn, kda::ChunkArgs a, void* stream) {
 
 }  // namespace
 
+namespace {
+
+// Checks shared by the decode entry points; fills a on success.
+kda_status check_step(const char* fn, const void* q, const void* k, const void* v, const void* g, const void* beta,
+                      float* state_cache, const int32_t* state_slots, int32_t n_slots, int32_t Nb, int32_t H,
+                      int32_t Dk, int32_t Dv, float scale, kda_dtype dtype, void* o, kda::StepArgs& a) {
+    if (Nb != 0 && (!q || !k || !v || !g || !beta || !state_cache || !o))
+        return fail(KDA_ERR_INVALID_ARG, "%s: q, k, v, g, beta, state_cache and o must be non-NULL", fn);
+    if (Nb < 0 || H < 1 || n_slots < 0)
+        return fail(KDA_ERR_INVALID_ARG, "%s: need Nb >= 0, H >= 1, n_slots >= 0 (got %d, %d, %d)", fn, Nb, H,
+                    n_slots);
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dtype %d is not KDA_F32 or KDA_BF16", fn, (int)dtype);
+    if (!dim_ok(Dk) || !dim_ok(Dv))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: Dk=%d, Dv=%d; supported head dims are 16, 32, 64, 128", fn, Dk, Dv);
+    if (!state_slots && Nb > n_slots)
+        return fail(KDA_ERR_INVALID_ARG,
+                    "%s: without state_slots row r uses slot r, so Nb (%d) must be <= n_slots (%d)", fn, Nb,
+                    n_slots);
+    if ((int64_t)Nb * H > ((int64_t)1 << 30)) return fail(KDA_ERR_UNSUPPORTED, "%s: Nb*H too large", fn);
+    if (Nb != 0 && (o == q || o == k || o == v || o == g || o == beta || o == state_cache))
+        return fail(KDA_ERR_INVALID_ARG, "%s: o must not alias an input", fn);
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.cache = state_cache; a.slots = state_slots; a.o = o;
+    a.n_slots = n_slots; a.Nb = Nb; a.H = H; a.Dk = Dk; a.Dv = Dv; a.scale = scale; a.bf16 = dtype == KDA_BF16;
+    return KDA_OK;
+}
+
+// The prologue's parameters of a decode entry point.
+kda_status check_step_prologue(const char* fn, const float* A_log, const float* dt_bias, float gate_lower_bound,
+                               float l2_eps, int32_t Nb, kda::StepArgs& a) {
+    if (Nb != 0 && (!A_log || !dt_bias))
+        return fail(KDA_ERR_INVALID_ARG, "%s: A_log and dt_bias must be non-NULL when Nb > 0", fn);
+    if (!(gate_lower_bound < 0.f) || !(gate_lower_bound > -1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: gate_lower_bound must be finite and negative (got %g)", fn,
+                    (double)gate_lower_bound);
+    if (!(l2_eps > 0.f) || !(l2_eps < 1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: l2_eps must be finite and positive (got %g)", fn, (double)l2_eps);
+    a.prologue = true;
+    a.A_log = A_log;
+    a.dt_bias = dt_bias;
+    a.gate_lb = gate_lower_bound;
+    a.l2_eps = l2_eps;
+    return KDA_OK;
+}
+
+kda_status launch_step(const char* fn, const kda::StepArgs& a, void* stream) {
+    const hipError_t e = kda::launch_recurrent_step(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
@@ -728,34 +782,67 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
                               int32_t n_slots, int32_t Nb, int32_t H, int32_t Dk, int32_t Dv,
                               float scale, kda_dtype dtype, void* o, void* stream) {
     g_last_error[0] = 0;
-    if (Nb != 0 && (!q || !k || !v || !g || !beta || !state_cache || !o))
-        return fail(KDA_ERR_INVALID_ARG,
-                    "kda_recurrent_step: q, k, v, g, beta, state_cache and o must be non-NULL");
-    if (Nb < 0 || H < 1 || n_slots < 0)
-        return fail(KDA_ERR_INVALID_ARG, "kda_recurrent_step: need Nb >= 0, H >= 1, n_slots >= 0 (got %d, %d, %d)",
-                    Nb, H, n_slots);
-    if (dtype != KDA_F32 && dtype != KDA_BF16)
-        return fail(KDA_ERR_UNSUPPORTED, "kda_recurrent_step: dtype %d is not KDA_F32 or KDA_BF16", (int)dtype);
-    if (!dim_ok(Dk) || !dim_ok(Dv))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_recurrent_step: Dk=%d, Dv=%d; supported head dims are 16, 32, 64, 128",
-                    Dk, Dv);
-    if (!state_slots && Nb > n_slots)
-        return fail(KDA_ERR_INVALID_ARG, "kda_recurrent_step: without state_slots row r uses slot r, so Nb (%d) must be <= n_slots (%d)",
-                    Nb, n_slots);
-    if ((int64_t)Nb * H > ((int64_t)1 << 30))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_recurrent_step: Nb*H too large");
-    if (Nb == 0) return KDA_OK;
-    if (o == q || o == k || o == v || o == g || o == beta || o == state_cache)
-        return fail(KDA_ERR_INVALID_ARG, "kda_recurrent_step: o must not alias an input");
-
+    const char* fn = "kda_recurrent_step";
     kda::StepArgs a;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
-    a.cache = state_cache; a.slots = state_slots; a.o = o;
-    a.n_slots = n_slots; a.Nb = Nb; a.H = H; a.Dk = Dk; a.Dv = Dv; a.scale = scale; a.bf16 = dtype == KDA_BF16;
-    const hipError_t e = kda::launch_recurrent_step(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(KDA_ERR_HIP, "kda_recurrent_step: launch failed: %s", hipGetErrorString(e));
-    return KDA_OK;
+    const kda_status st = check_step(fn, q, k, v, g, beta, state_cache, state_slots, n_slots, Nb, H, Dk, Dv, scale,
+                                     dtype, o, a);
+    if (st != KDA_OK || Nb == 0) return st;
+    return launch_step(fn, a, stream);
+}
+
+kda_status kda_recurrent_step_prologue(const void* q_raw, const void* k_raw, const void* v, const void* g_logit,
+                                       const void* beta_logit, const float* A_log, const float* dt_bias,
+                                       float gate_lower_bound, float l2_eps, float* state_cache,
+                                       const int32_t* state_slots, int32_t n_slots, int32_t Nb, int32_t H,
+                                       int32_t Dk, int32_t Dv, float scale, kda_dtype dtype, void* o,
+                                       void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_recurrent_step_prologue";
+    kda::StepArgs a;
+    kda_status st = check_step(fn, q_raw, k_raw, v, g_logit, beta_logit, state_cache, state_slots, n_slots, Nb, H,
+                               Dk, Dv, scale, dtype, o, a);
+    if (st == KDA_OK) st = check_step_prologue(fn, A_log, dt_bias, gate_lower_bound, l2_eps, Nb, a);
+    if (st != KDA_OK || Nb == 0) return st;
+    return launch_step(fn, a, stream);
+}
+
+kda_status kda_recurrent_step_conv(const void* xq, const void* xk, const void* xv, const float* wq,
+                                   const float* wk, const float* wv, float* conv_cache_q, float* conv_cache_k,
+                                   float* conv_cache_v, int32_t activation, const void* g_logit,
+                                   const void* beta_logit, const float* A_log, const float* dt_bias,
+                                   float gate_lower_bound, float l2_eps, float* state_cache,
+                                   const int32_t* state_slots, int32_t n_slots, int32_t Nb, int32_t H, int32_t Dk,
+                                   int32_t Dv, float scale, kda_dtype dtype, void* o, void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_recurrent_step_conv";
+    kda::StepArgs a;
+    kda_status st = check_step(fn, xq, xk, xv, g_logit, beta_logit, state_cache, state_slots, n_slots, Nb, H, Dk,
+                               Dv, scale, dtype, o, a);
+    if (st == KDA_OK) st = check_step_prologue(fn, A_log, dt_bias, gate_lower_bound, l2_eps, Nb, a);
+    if (st != KDA_OK) return st;
+    if (activation != 0 && activation != 1)
+        return fail(KDA_ERR_INVALID_ARG, "%s: activation must be 0 (none) or 1 (SiLU), got %d", fn, activation);
+    if (Nb == 0) return KDA_OK;
+    const float* w[3] = {wq, wk, wv};
+    float* cache[3] = {conv_cache_q, conv_cache_k, conv_cache_v};
+    for (int j = 0; j < 3; ++j) {
+        if (!w[j] || !cache[j])
+            return fail(KDA_ERR_INVALID_ARG, "%s: the taps and convolution caches must be non-NULL", fn);
+        if (reinterpret_cast<uintptr_t>(w[j]) % 16 != 0)
+            return fail(KDA_ERR_INVALID_ARG, "%s: the taps must be 16-byte aligned", fn);
+    }
+    if (cache[0] == cache[1] || cache[0] == cache[2] || cache[1] == cache[2] || cache[0] == state_cache ||
+        cache[1] == state_cache || cache[2] == state_cache)
+        return fail(KDA_ERR_INVALID_ARG, "%s: the convolution caches and the state cache must be distinct", fn);
+    for (int j = 0; j < 3; ++j) {
+        if (cache[j] == o)
+            return fail(KDA_ERR_INVALID_ARG, "%s: o must not alias an input", fn);
+        a.conv_w[j] = w[j];
+        a.conv_cache[j] = cache[j];
+    }
+    a.conv = true;
+    a.conv_act = activation == 1;
+    return launch_step(fn, a, stream);
 }
 
 }  // extern "C"

@@ -73,6 +73,21 @@ struct StepArgs {
     int32_t Nb, H, Dk, Dv;
     float scale;
     bool bf16;
+    // decode from raw projections: q and k hold the raw projections
+    // (normalised in the kernel), g the gate logits and beta the beta logits
+    bool prologue = false;
+    const float* A_log = nullptr;     // [Dk]
+    const float* dt_bias = nullptr;   // [H*Dk]
+    float gate_lb = 0.f;
+    float l2_eps = 0.f;
+    // with the prologue, the short-convolution step of q, k and v before it:
+    // q, k and v hold the convolution inputs; per projection j (q, k, v) taps
+    // [H*D][4] and a cache [n_slots][3][H*D] (D = Dk for q and k, Dv for v)
+    // indexed by the row's slot and shifted in place
+    bool conv = false;
+    bool conv_act = false;            // SiLU after the convolution
+    const float* conv_w[3] = {nullptr, nullptr, nullptr};
+    float* conv_cache[3] = {nullptr, nullptr, nullptr};
 };
 
 // Each returns hipSuccess or the launch error; they never synchronise.

@@ -13,9 +13,20 @@
 // the hint keeps the stream from displacing other lines in the caches (7%
 // faster than plain accesses at 256 rows x 96 heads).
 //
+// From raw projections (kIn >= 1) the same workgroup first forms the token's
+// inputs while its state loads are in flight, as the chunk forward's prologue
+// does: q and k scaled to unit length, g = lb sigmoid(exp(A_log) (logit +
+// dt_bias)), beta = sigmoid(logit); with kIn = 2 the short-convolution step of
+// q, k and v comes before that, in the same fma order and with the same
+// rounding of its output to the input type as the standalone convolution
+// step, its cache shifted in place. Wave 0 takes q and k (two channels per
+// lane, and the three sums |q|^2, |k|^2, k.q by a butterfly), wave 1 the
+// gate, waves 2 and 3 v; the state update after the first barrier is the
+// plain step's.
+//
 // A row whose slot lies outside [0, n_slots) (e.g. -1 for a padding row of a
-// serving batch) touches no state: its output is zero and the cache is left
-// as it is.
+// serving batch) touches no state and no convolution cache: its output is
+// zero.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -24,8 +35,38 @@ namespace {
 
 constexpr int kStepThreads = 256;
 
-template <int DK, int DV, typename Tin>
-__global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a) {
+template <typename T> __device__ __forceinline__ float round_to(float x);
+template <> __device__ __forceinline__ float round_to<float>(float x) { return x; }
+template <> __device__ __forceinline__ float round_to<__bf16>(float x) { return bf16_bits_to_f32(f32_to_bf16_bits(x)); }
+
+// Channel c of projection j (0 q, 1 k, 2 v; D channels per head) for token
+// tok: the loaded value, or with kConv the convolution step over the cache of
+// the row's slot (window h0, h1, h2, x oldest first), which it shifts.
+template <typename Tin, bool kConv>
+__device__ __forceinline__ float raw_input(const StepArgs& a, int j, const Tin* x, int64_t tok, int D, int h,
+                                           int slot, int c) {
+    const float xv = load_elem(x, tok * D + c);
+    if constexpr (!kConv) {
+        return xv;
+    } else {
+        const int64_t C = (int64_t)a.H * D;
+        float* st = a.conv_cache[j] + (int64_t)slot * 3 * C + (int64_t)h * D + c;
+        const float h0 = st[0], h1 = st[C], h2 = st[2 * C];
+        const float4 w = reinterpret_cast<const float4*>(a.conv_w[j])[(int64_t)h * D + c];
+        float y = fmaf(w.w, xv, fmaf(w.z, h2, fmaf(w.y, h1, w.x * h0)));
+        if (a.conv_act) y = y * __builtin_amdgcn_rcpf(1.f + __expf(-y));
+        st[0] = h1;
+        st[C] = h2;
+        st[2 * C] = xv;
+        return round_to<Tin>(y);
+    }
+}
+
+// kIn: 0 prepared inputs, 1 raw projections, 2 convolution inputs. At most
+// 128 VGPRs, so that four workgroups stay resident per CU in every variant.
+template <int DK, int DV, typename Tin, int kIn>
+__global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4))) void recurrent_step_kernel(
+    StepArgs a) {
     constexpr int QUADS = DV / 4;                 // float4 columns per row
     constexpr int RG = kStepThreads / QUADS;      // row groups
     constexpr int ROWS = (DK + RG - 1) / RG;      // rows per thread
@@ -62,20 +103,64 @@ __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a
         const int r = rg + RG * i;
         s[i] = (r < DK) ? __builtin_nontemporal_load(&S[r * QUADS + quad]) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    for (int i = tid; i < DK; i += kStepThreads) {
-        sk[i] = load_elem(k, tok * DK + i);
-        sq[i] = load_elem(q, tok * DK + i);
-        seg[i] = expf(load_elem(g, tok * DK + i));
-    }
-    for (int i = tid; i < DV; i += kStepThreads) sv[i] = load_elem(v, tok * DV + i);
-    if (tid < 64) {
-        float p = 0.f;
-        for (int i = tid; i < DK; i += 64) p += load_elem(k, tok * DK + i) * load_elem(q, tok * DK + i);
+    float bt;
+    if constexpr (kIn == 0) {
+        for (int i = tid; i < DK; i += kStepThreads) {
+            sk[i] = load_elem(k, tok * DK + i);
+            sq[i] = load_elem(q, tok * DK + i);
+            seg[i] = expf(load_elem(g, tok * DK + i));
+        }
+        for (int i = tid; i < DV; i += kStepThreads) sv[i] = load_elem(v, tok * DV + i);
+        if (tid < 64) {
+            float p = 0.f;
+            for (int i = tid; i < DK; i += 64) p += load_elem(k, tok * DK + i) * load_elem(q, tok * DK + i);
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
-        if (tid == 0) skq = p;
+            for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+            if (tid == 0) skq = p;
+        }
+        bt = load_elem(beta, tok);
+    } else {
+        constexpr bool kConv = kIn == 2;
+        if (tid < 64) {
+            float qv[2], kv[2];
+            float qq = 0.f, kk = 0.f, kq = 0.f;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int c = tid + 64 * i;
+                qv[i] = c < DK ? raw_input<Tin, kConv>(a, 0, q, tok, DK, h, slot, c) : 0.f;
+                kv[i] = c < DK ? raw_input<Tin, kConv>(a, 1, k, tok, DK, h, slot, c) : 0.f;
+                qq += qv[i] * qv[i];
+                kk += kv[i] * kv[i];
+                kq += kv[i] * qv[i];
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                qq += __shfl_xor(qq, off);
+                kk += __shfl_xor(kk, off);
+                kq += __shfl_xor(kq, off);
+            }
+            // eps > 0: a row of zeros normalises to zeros
+            const float rq = 1.f / sqrtf(qq + a.l2_eps), rk = 1.f / sqrtf(kk + a.l2_eps);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int c = tid + 64 * i;
+                if (c < DK) {
+                    sq[c] = qv[i] * rq;
+                    sk[c] = kv[i] * rk;
+                }
+            }
+            if (tid == 0) skq = kq * rq * rk;
+        } else if (tid < 128) {
+            for (int c = tid - 64; c < DK; c += 64) {
+                const float gl = load_elem(g, tok * DK + c);
+                const float gv = a.gate_lb / (1.f + expf(-expf(a.A_log[c]) * (gl + a.dt_bias[h * DK + c])));
+                seg[c] = expf(gv);
+            }
+        } else {
+            for (int c = tid - 128; c < DV; c += 128) sv[c] = raw_input<Tin, kConv>(a, 2, v, tok, DV, h, slot, c);
+        }
+        bt = 1.f / (1.f + expf(-load_elem(beta, tok)));
     }
-    const float bt = load_elem(beta, tok);
     __syncthreads();
 
     f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
@@ -115,14 +200,21 @@ __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a
     }
 }
 
+template <int DK, int DV, typename Tin>
+hipError_t launch_in(const StepArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)(a.Nb * a.H));
+    if (a.conv)
+        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, Tin, 2>), grid, dim3(kStepThreads), 0, s, a);
+    else if (a.prologue)
+        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, Tin, 1>), grid, dim3(kStepThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, Tin, 0>), grid, dim3(kStepThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int DK, int DV>
 hipError_t launch_dims(const StepArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)(a.Nb * a.H));
-    if (a.bf16)
-        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, __bf16>), grid, dim3(kStepThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, float>), grid, dim3(kStepThreads), 0, s, a);
-    return hipGetLastError();
+    return a.bf16 ? launch_in<DK, DV, __bf16>(a, s) : launch_in<DK, DV, float>(a, s);
 }
 
 template <int DK>
@@ -140,6 +232,7 @@ hipError_t launch_dk(const StepArgs& a, hipStream_t s) {
 
 hipError_t launch_recurrent_step(const StepArgs& a, hipStream_t s) {
     if (a.Nb == 0) return hipSuccess;
+    if (a.conv && !a.prologue) return hipErrorInvalidValue;
     switch (a.Dk) {
         case 16: return launch_dk<16>(a, s);
         case 32: return launch_dk<32>(a, s);

@@ -472,6 +472,58 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
                               float scale, kda_dtype dtype, void* o, void* stream);
 
 /*
+ * kda_recurrent_step from raw projections: per (row, head) the gate, beta and
+ * normalisation prologue of kda_chunk_fwd_prologue (q and k scaled to unit
+ * length, g = gate_lower_bound * sigmoid(exp(A_log) * (g_logit + dt_bias)),
+ * beta = sigmoid(beta_logit)), then the decode step, in one kernel. This is
+ * the per-token form of the prologue forward, for a generation loop that
+ * keeps the recurrent state between tokens; the pages' parameters and bound
+ * are those cited at kda_chunk_fwd_prologue.
+ *
+ *   q_raw, k_raw, g_logit  [Nb,H,Dk] dtype;  v [Nb,H,Dv];  beta_logit [Nb,H]
+ *   A_log [Dk], dt_bias [H*Dk] float32; gate_lower_bound finite and < 0;
+ *   l2_eps finite and > 0
+ *   state_cache, state_slots, n_slots, Nb, H, Dk, Dv, scale, dtype, o
+ *                as for kda_recurrent_step (padding rows included)
+ * The decay factor exp(g) lies in [exp(gate_lower_bound), 1) for any logits,
+ * so there is no range precondition. Errors as for kda_recurrent_step; a NULL
+ * A_log or dt_bias, a bad bound or eps is KDA_ERR_INVALID_ARG.
+ */
+kda_status kda_recurrent_step_prologue(const void* q_raw, const void* k_raw, const void* v, const void* g_logit,
+                                       const void* beta_logit, const float* A_log, const float* dt_bias,
+                                       float gate_lower_bound, float l2_eps, float* state_cache,
+                                       const int32_t* state_slots, int32_t n_slots, int32_t Nb, int32_t H,
+                                       int32_t Dk, int32_t Dv, float scale, kda_dtype dtype, void* o,
+                                       void* stream);
+
+/*
+ * One generated token of the KDA layer from the projections before the short
+ * convolution (the decode form of kda_chunk_fwd_conv): for each of q, k and v
+ * the convolution step of kda_short_conv_step over its cache, its output
+ * rounded to dtype, then kda_recurrent_step_prologue on the convolved q, k
+ * and v, all in one kernel. The result, the state cache and the three
+ * convolution caches equal those of that sequence of calls bit for bit.
+ *
+ *   xq, xk [Nb,H,Dk], xv [Nb,H,Dv]  dtype: the projections before the convolution
+ *   wq, wk [H*Dk][4], wv [H*Dv][4]   float32 taps, 16-byte aligned
+ *   conv_cache_q, _k [n_slots][3][H*Dk], conv_cache_v [n_slots][3][H*Dv]
+ *                float32, updated in place, indexed by the same slot as the
+ *                state cache (a padding row touches none of them)
+ *   activation   0 = none, 1 = SiLU after each convolution
+ *   the rest     as for kda_recurrent_step_prologue
+ * Errors as for kda_recurrent_step_prologue and kda_short_conv_step; NULL or
+ * misaligned taps, a NULL cache or a bad activation are KDA_ERR_INVALID_ARG,
+ * as is a convolution cache that is the state cache or another's.
+ */
+kda_status kda_recurrent_step_conv(const void* xq, const void* xk, const void* xv, const float* wq,
+                                   const float* wk, const float* wv, float* conv_cache_q, float* conv_cache_k,
+                                   float* conv_cache_v, int32_t activation, const void* g_logit,
+                                   const void* beta_logit, const float* A_log, const float* dt_bias,
+                                   float gate_lower_bound, float l2_eps, float* state_cache,
+                                   const int32_t* state_slots, int32_t n_slots, int32_t Nb, int32_t H, int32_t Dk,
+                                   int32_t Dv, float scale, kda_dtype dtype, void* o, void* stream);
+
+/*
  * Device-side failures. The bf16 matrix-core forward hands work between the
  * waves of a workgroup through flags in LDS; every wait for such a flag is
  * bounded. A producer always stores its flag, so a wait that gives up means a

@@ -25,6 +25,10 @@ Recipe (numpy PCG64 generators, float32 draws):
   S0    ~ N(0, 0.02) float32 when requested (0.02 is the standard deviation)
   d_o   ~ N(0,1) (stream 9), d_final ~ N(0, 0.1) float32 (stream 10): the
         output and final-state cotangents of the backward workloads
+  decode from raw projections: q_raw, k_raw, v, g_logit, beta_logit ~ N(0,1)
+        per step (stream 13); gate parameters A_log, dt_bias ~ N(0, 0.5)
+        (streams 7, 8); convolution taps ~ N(0, 0.5) (stream 11) and caches
+        ~ N(0,1) (stream 12), per projection
 then, for bf16 workloads, q,k,v,g,beta are rounded to bf16 (round to nearest
 even). States stay float32.
 """
@@ -90,7 +94,8 @@ def packed_lengths(rng, n, lo, hi):
 
 
 BLOCK_ROWS = 1024
-_STREAM = dict(lengths=0, q=1, k=2, v=3, g=4, beta=5, s0=6, A_log=7, dt_bias=8, d_o=9, d_final=10)
+_STREAM = dict(lengths=0, q=1, k=2, v=3, g=4, beta=5, s0=6, A_log=7, dt_bias=8, d_o=9, d_final=10, conv_w=11,
+               conv_cache=12, decode_raw=13)
 
 
 def _pool_size():
@@ -237,6 +242,43 @@ def make_decode_step(Nb, H, Dk, Dv, seed, step, dtype="bf16"):
     beta = _sigmoid(rng.standard_normal((Nb, H), dtype=np.float32))
     return dict(q=_round(q, dtype), k=_round(k, dtype), v=_round(v, dtype), g=_round(g, dtype),
                 beta=_round(beta, dtype))
+
+
+def make_decode_raw_step(Nb, H, Dk, Dv, seed, step, dtype="bf16"):
+    """Raw projections of one decode step, drawn from
+    default_rng([seed, 13, step]): q_raw, k_raw, g_logit [Nb,H,Dk], v
+    [Nb,H,Dv] and beta_logit [Nb,H], all N(0,1), rounded to ``dtype``. They
+    are the inputs of the prologue, or of the short convolution before it."""
+    rng = np.random.default_rng([seed, _STREAM["decode_raw"], step])
+    f = lambda *shape: rng.standard_normal(shape, dtype=np.float32)  # noqa: E731
+    q, k, g = f(Nb, H, Dk), f(Nb, H, Dk), f(Nb, H, Dk)
+    v, beta = f(Nb, H, Dv), f(Nb, H)
+    return dict(q_raw=_round(q, dtype), k_raw=_round(k, dtype), v=_round(v, dtype), g_logit=_round(g, dtype),
+                beta_logit=_round(beta, dtype))
+
+
+def make_gate_params(H, Dk, seed, std=0.5):
+    """The gate's parameters A_log [Dk] and dt_bias [H*Dk], float32
+    N(0, std^2), from streams 7 and 8 of ``seed`` (the draws of
+    make_prologue_inputs)."""
+    A_log = np.float32(std) * np.random.default_rng([seed, _STREAM["A_log"]]).standard_normal(Dk, dtype=np.float32)
+    dt_bias = np.float32(std) * np.random.default_rng([seed, _STREAM["dt_bias"]]).standard_normal(
+        H * Dk, dtype=np.float32)
+    return torch.from_numpy(A_log), torch.from_numpy(dt_bias)
+
+
+def make_conv_taps(C, seed, which, std=0.5):
+    """Short-convolution taps [C,4] float32 N(0, std^2) of projection
+    ``which`` (0 q, 1 k, 2 v): default_rng([seed, 11, which])."""
+    rng = np.random.default_rng([seed, _STREAM["conv_w"], which])
+    return torch.from_numpy(np.float32(std) * rng.standard_normal((C, 4), dtype=np.float32))
+
+
+def make_conv_cache(n_slots, C, seed, which):
+    """Short-convolution cache [n_slots,3,C] float32 N(0,1) of projection
+    ``which``: default_rng([seed, 12, which])."""
+    rng = np.random.default_rng([seed, _STREAM["conv_cache"], which])
+    return torch.from_numpy(rng.standard_normal((n_slots, 3, C), dtype=np.float32))
 
 
 def as_f32_numpy(t):

@@ -22,6 +22,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = kda.declared_symbols()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step", "kda_short_conv",
+                          "kda_recurrent_step_prologue", "kda_recurrent_step_conv",
                           "kda_short_conv_step", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
                           "kda_chunk_fwd_split", "kda_chunk_fwd_split_workspace_bytes",
                           "kda_chunk_fwd_split_static", "kda_chunk_fwd_conv", "kda_chunk_fwd_conv_workspace_bytes",
@@ -142,7 +143,68 @@ def test_recurrent_step_rejects_before_launch(lib, kw, status, needle):
     assert needle in lib.kda_last_error_message().decode()
 
 
+def _step_prologue(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, lb=-5.0, eps=1e-6, cache=FAKE,
+             slots=None, n_slots=4, Nb=4, H=2, Dk=128, Dv=128, scale=1.0, dtype=kda.KDA_BF16,
+             o=ctypes.c_void_p(0x2000), stream=None)
+    a.update(kw)
+    return lib.kda_recurrent_step_prologue(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"], a["dt_bias"],
+                                           a["lb"], a["eps"], a["cache"], a["slots"], a["n_slots"], a["Nb"],
+                                           a["H"], a["Dk"], a["Dv"], a["scale"], a["dtype"], a["o"], a["stream"])
+
+
+def _step_conv(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, wq=ctypes.c_void_p(0x3000), wk=ctypes.c_void_p(0x4000),
+             wv=ctypes.c_void_p(0x5000), cq=ctypes.c_void_p(0x6000), ck=ctypes.c_void_p(0x7000),
+             cv=ctypes.c_void_p(0x8000), act=1, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, lb=-5.0, eps=1e-6,
+             cache=FAKE, slots=None, n_slots=4, Nb=4, H=2, Dk=128, Dv=128, scale=1.0, dtype=kda.KDA_BF16,
+             o=ctypes.c_void_p(0x2000), stream=None)
+    a.update(kw)
+    return lib.kda_recurrent_step_conv(a["q"], a["k"], a["v"], a["wq"], a["wk"], a["wv"], a["cq"], a["ck"], a["cv"],
+                                       a["act"], a["g"], a["beta"], a["A_log"], a["dt_bias"], a["lb"], a["eps"],
+                                       a["cache"], a["slots"], a["n_slots"], a["Nb"], a["H"], a["Dk"], a["Dv"],
+                                       a["scale"], a["dtype"], a["o"], a["stream"])
+
+
+STEP_RAW_CASES = [
+    (dict(cache=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(Nb=5), kda.KDA_ERR_INVALID_ARG, "n_slots"),
+    (dict(Dv=48), kda.KDA_ERR_UNSUPPORTED, "head dims"),
+    (dict(o=FAKE), kda.KDA_ERR_INVALID_ARG, "alias"),
+    (dict(A_log=None), kda.KDA_ERR_INVALID_ARG, "A_log"),
+    (dict(dt_bias=None), kda.KDA_ERR_INVALID_ARG, "dt_bias"),
+    (dict(lb=0.0), kda.KDA_ERR_INVALID_ARG, "gate_lower_bound"),
+    (dict(lb=float("-inf")), kda.KDA_ERR_INVALID_ARG, "gate_lower_bound"),
+    (dict(eps=0.0), kda.KDA_ERR_INVALID_ARG, "l2_eps"),
+    (dict(eps=float("nan")), kda.KDA_ERR_INVALID_ARG, "l2_eps"),
+]
+
+
+@pytest.mark.parametrize("kw,status,needle", STEP_RAW_CASES)
+def test_recurrent_step_prologue_rejects_before_launch(lib, kw, status, needle):
+    assert _step_prologue(lib, **kw) == status
+    msg = lib.kda_last_error_message().decode()
+    assert needle in msg and msg.startswith("kda_recurrent_step_prologue")
+
+
+@pytest.mark.parametrize("kw,status,needle", STEP_RAW_CASES + [
+    (dict(act=2), kda.KDA_ERR_INVALID_ARG, "activation"),
+    (dict(wk=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(cv=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(wv=ctypes.c_void_p(0x5004)), kda.KDA_ERR_INVALID_ARG, "aligned"),
+    (dict(ck=ctypes.c_void_p(0x6000)), kda.KDA_ERR_INVALID_ARG, "distinct"),
+    (dict(cq=FAKE), kda.KDA_ERR_INVALID_ARG, "distinct"),
+    (dict(cv=ctypes.c_void_p(0x2000)), kda.KDA_ERR_INVALID_ARG, "alias"),
+])
+def test_recurrent_step_conv_rejects_before_launch(lib, kw, status, needle):
+    assert _step_conv(lib, **kw) == status
+    msg = lib.kda_last_error_message().decode()
+    assert needle in msg and msg.startswith("kda_recurrent_step_conv")
+
+
 def test_empty_work_is_ok_without_launch(lib):
+    assert _step_prologue(lib, Nb=0, q=None, A_log=None) == kda.KDA_OK
+    assert _step_conv(lib, Nb=0, wq=None, cq=None) == kda.KDA_OK
     assert _step(lib, Nb=0) == kda.KDA_OK
     assert lib.kda_last_error_message() == b""
 
