@@ -32,7 +32,10 @@ backward on the same workload; its ``from_raw_projections`` entry times the
 backward through the gate, beta and L2-norm prologue (kda_chunk_bwd_prologue). ``split`` times the intra-sequence split
 (kda_chunk_fwd_split, 10 segments) on 12 heads at T=32768 against the unsplit
 call. ``decode`` times kda_recurrent_step on
-256 rows x 96 heads against an fp32 state cache (HBM-bound). ``cpu_baseline``
+256 rows x 96 heads against an fp32 state cache (HBM-bound); its
+``from_conv`` entry times one token from the projections before the short
+convolution (kda_recurrent_step_conv: convolution step, prologue and state
+update in one kernel) beside the same work as four calls. ``cpu_baseline``
 times the fp64 CPU oracle (C, OpenMP over heads) on the same forward workload,
 repeated until about ten seconds of wall time have passed.
 """
@@ -370,11 +373,56 @@ def bench_decode(steps, warmup):
     step_bytes = 2 * Nb * H * Dk * Dv * 4 + Nb * H * (2 * (3 * Dk + Dv) + 2 + 2 * Dv)
     avg_ms = float(batch)
     gbs = step_bytes / (avg_ms * 1e-3) / 1e9
+
+    # one generated token from the projections before the short convolution: the convolution step of q, k and
+    # v over their caches, the gate/beta/normalisation prologue and the state update in one kernel, against the
+    # same work as three convolution steps and the prologue step
+    raw = [{k: v.to(dev) for k, v in synth.make_decode_raw_step(Nb, H, Dk, Dv, cfg["seed"], s).items()}
+           for s in range(4)]
+    A_log, dt_bias = (t.to(dev) for t in synth.make_gate_params(H, Dk, cfg["seed"]))
+    Cs = (H * Dk, H * Dk, H * Dv)
+    taps = [synth.make_conv_taps(C, cfg["seed"], j).to(dev) for j, C in enumerate(Cs)]
+    conv = [synth.make_conv_cache(Nb, C, cfg["seed"], j).to(dev) for j, C in enumerate(Cs)]
+    ys = [torch.empty((Nb, H, D), dtype=torch.bfloat16, device=dev) for D in (Dk, Dk, Dv)]
+
+    def fused(i):
+        d = raw[i % 4]
+        kda.recurrent_step_conv(d["q_raw"], d["k_raw"], d["v"], *taps, conv, d["g_logit"], d["beta_logit"], A_log,
+                                dt_bias, cache, activation=True, gate_lower_bound=synth.GATE_LOWER_BOUND,
+                                l2_eps=1e-6, out=o)
+
+    def chain(i):
+        d = raw[i % 4]
+        for j, name in enumerate(("q_raw", "k_raw", "v")):
+            kda.short_conv_step(d[name], taps[j], conv[j], activation=True, out=ys[j])
+        kda.recurrent_step_prologue(ys[0], ys[1], ys[2], d["g_logit"], d["beta_logit"], A_log, dt_bias, cache,
+                                    gate_lower_bound=synth.GATE_LOWER_BOUND, l2_eps=1e-6, out=o)
+
+    _, fper, fms = time_launches(fused, steps, warmup, stream)
+    _, cper, cms = time_launches(chain, steps, warmup, stream)
+    if not (torch.isfinite(cache).all() and torch.isfinite(o.float()).all()):
+        raise RuntimeError("non-finite decode state from the convolution inputs")
+    # the state read and written, the convolution caches read and written, the inputs, o, the taps and the gate
+    # parameters
+    conv_bytes = (2 * Nb * H * Dk * Dv * 4 + 2 * Nb * sum(Cs) * 3 * 4 + Nb * H * (2 * (3 * Dk + Dv) + 2 + 2 * Dv)
+                  + sum(Cs) * 16 + (Dk + H * Dk) * 4)
+    fgbs = conv_bytes / (float(fms) * 1e-3) / 1e9
     return {"workload": f"{cfg['name']}: batch {Nb}, H={H}, d_k=d_v={Dk}, bf16 q/k/v/g/beta, fp32 state cache",
             "ms_per_step": avg_ms, "ms_median": float(np.median(per)), "tokens_per_s": Nb / (avg_ms * 1e-3),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": read_leg_traffic("decode")},
-            "algorithmic_bytes_per_step": step_bytes}
+            "algorithmic_bytes_per_step": step_bytes,
+            "from_conv": {"steps": "kda_recurrent_step_conv: the short-convolution step of q, k, v (SiLU, fp32 "
+                                   "caches [256,3,96*128]), the gate/beta/normalisation prologue and the state "
+                                   "update in one kernel",
+                          "ms_per_step": float(fms), "ms_median": float(np.median(fper)),
+                          "tokens_per_s": Nb / (float(fms) * 1e-3),
+                          "roofline": {"bound": "hbm", "achieved": fgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": fgbs / HBM_PEAK_GBS,
+                                       "traffic": read_leg_traffic("decode", "conv_traffic_bytes_per_step")},
+                          "algorithmic_bytes_per_step": conv_bytes,
+                          "chain": {"steps": "kda_short_conv_step x 3, then kda_recurrent_step_prologue",
+                                    "ms_per_step": float(cms), "ms_median": float(np.median(cper))}}}
 
 
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 MFMA, TFLOP/s
