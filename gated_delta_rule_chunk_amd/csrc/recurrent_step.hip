@@ -33,7 +33,35 @@
 namespace kda {
 namespace {
 
-constexpr int kStepThreads = 256;
+// Threads per workgroup: four float4 state elements per thread for the large
+// heads. At 128 x 128 (1024 threads) the step runs at the rate of a plain
+// in-place read-modify-write stream of the same bytes; 256 threads with 16
+// float4 each were 6% slower, 512 with 8 each 3%.
+template <int DK, int DV> constexpr int step_threads() {
+    return DK * DV >= 16384 ? 1024 : DK * DV >= 8192 ? 512 : 256;
+}
+
+// Sum of v over lanes l and l ^ M of the wave (the same value on both lanes).
+template <int M> __device__ __forceinline__ float fold_lane(float v) {
+    if constexpr (M == 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    } else if constexpr (M == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    } else {
+        return v + __shfl_xor(v, M);
+    }
+}
+// Sum of v over the lanes of the wave that share lane % M0 (fold_rows<M0>).
+template <int M> __device__ __forceinline__ f32x4 fold_rows(f32x4 v) {
+    if constexpr (M >= 64) {
+        return v;
+    } else {
+        v = f32x4{fold_lane<M>(v.x), fold_lane<M>(v.y), fold_lane<M>(v.z), fold_lane<M>(v.w)};
+        return fold_rows<M * 2>(v);
+    }
+}
 
 template <typename T> __device__ __forceinline__ float round_to(float x);
 template <> __device__ __forceinline__ float round_to<float>(float x) { return x; }
@@ -63,17 +91,20 @@ __device__ __forceinline__ float raw_input(const StepArgs& a, int j, const Tin* 
 }
 
 // kIn: 0 prepared inputs, 1 raw projections, 2 convolution inputs. At most
-// 128 VGPRs, so that four workgroups stay resident per CU in every variant.
+// 128 VGPRs (four waves per SIMD) in every variant.
 template <int DK, int DV, typename Tin, int kIn>
-__global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4))) void recurrent_step_kernel(
-    StepArgs a) {
+__global__ __launch_bounds__((step_threads<DK, DV>())) __attribute__((amdgpu_waves_per_eu(4))) void
+recurrent_step_kernel(StepArgs a) {
+    constexpr int kStepThreads = step_threads<DK, DV>();
     constexpr int QUADS = DV / 4;                 // float4 columns per row
     constexpr int RG = kStepThreads / QUADS;      // row groups
     constexpr int ROWS = (DK + RG - 1) / RG;      // rows per thread
+    constexpr int W = kStepThreads / 64;          // waves
     __shared__ float sk[DK], sq[DK], seg[DK], sv[DV];
-    __shared__ f32x4 redx[RG][QUADS];
-    __shared__ f32x4 redy[RG][QUADS];
+    __shared__ f32x4 redx[W][QUADS];
+    __shared__ f32x4 redy[W][QUADS];
     __shared__ float skq;
+    __shared__ f32x4 su[QUADS];
 
     const Tin* q = static_cast<const Tin*>(a.q);
     const Tin* k = static_cast<const Tin*>(a.k);
@@ -173,26 +204,38 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
             y += sq[r] * s[i];
         }
     }
-    redx[rg][quad] = x;
-    redy[rg][quad] = y;
-    __syncthreads();
-    x = redx[0][quad];
-    y = redy[0][quad];
-#pragma unroll
-    for (int j = 1; j < RG; ++j) {
-        x += redx[j][quad];
-        y += redy[j][quad];
+    // x and y over all rows: the row groups of each wave fold by lane swaps
+    // (lanes l and l ^ m for m = QUADS .. 32 share a column quad), the waves'
+    // partials meet in LDS, wave 0 sums them in wave order, forms u and o, and
+    // hands u back through LDS.
+    x = fold_rows<QUADS>(x);
+    y = fold_rows<QUADS>(y);
+    const int w = tid / 64, lane = tid % 64;
+    if (lane < QUADS) {
+        redx[w][lane] = x;
+        redy[w][lane] = y;
     }
-    f32x4 vv = {sv[4 * quad], sv[4 * quad + 1], sv[4 * quad + 2], sv[4 * quad + 3]};
-    const f32x4 u = bt * (vv - x);
-    if (rg == 0) {
-        const f32x4 ov = a.scale * (y + skq * u);
-        const int64_t ob = tok * DV + 4 * quad;
+    __syncthreads();
+    if (tid < QUADS) {
+        x = redx[0][tid];
+        y = redy[0][tid];
+#pragma unroll
+        for (int j = 1; j < W; ++j) {
+            x += redx[j][tid];
+            y += redy[j][tid];
+        }
+        const f32x4 vv = {sv[4 * tid], sv[4 * tid + 1], sv[4 * tid + 2], sv[4 * tid + 3]};
+        const f32x4 uq = bt * (vv - x);
+        const f32x4 ov = a.scale * (y + skq * uq);
+        const int64_t ob = tok * DV + 4 * tid;
         store_elem(o, ob + 0, ov.x);
         store_elem(o, ob + 1, ov.y);
         store_elem(o, ob + 2, ov.z);
         store_elem(o, ob + 3, ov.w);
+        su[tid] = uq;
     }
+    __syncthreads();
+    const f32x4 u = su[quad];
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) {
         const int r = rg + RG * i;
@@ -202,13 +245,13 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
 
 template <int DK, int DV, typename Tin>
 hipError_t launch_in(const StepArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)(a.Nb * a.H));
+    const dim3 grid((unsigned)(a.Nb * a.H)), block(step_threads<DK, DV>());
     if (a.conv)
-        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, Tin, 2>), grid, dim3(kStepThreads), 0, s, a);
+        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, Tin, 2>), grid, block, 0, s, a);
     else if (a.prologue)
-        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, Tin, 1>), grid, dim3(kStepThreads), 0, s, a);
+        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, Tin, 1>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, Tin, 0>), grid, dim3(kStepThreads), 0, s, a);
+        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, Tin, 0>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
