@@ -86,15 +86,17 @@ __device__ __forceinline__ void find_sequence(const ConvArgs& a, int64_t t, int&
 // issued before any is used. The wave's token range and the sequence bounds
 // are uniform across the wave. The four waves of a workgroup take
 // consecutive token ranges of the same channels.
-// Tiling measured at T=4096, C=12288, bf16: every tiling from 4 or 8
-// channels per lane and 32 or 64 tokens per wave lands within 3% of a
-// device copy's rate for the same bytes; 2-token groups or 128-token runs
-// are slower.
+// Tiling measured at T=4096, C=12288, bf16: 4 channels per lane and 64
+// tokens per wave, in groups of 16 tokens (4% faster than groups of 8, as
+// fast as 32; 8 channels per lane, 32- or 128-token runs and 2-token groups
+// are slower). The group's loads are what is in flight: 8 KiB per wave at
+// four waves per SIMD. Capping the registers for more waves spills and
+// halves the rate.
 constexpr int kFwdCh = 4;
 constexpr int kFwdWaveRows = 64;
 constexpr int kFwdBlockRows = 4 * kFwdWaveRows;
 constexpr int kFwdBlockCh = 64 * kFwdCh;
-constexpr int kFwdGroup = 8;
+constexpr int kFwdGroup = 16;
 typedef uint32_t ntu2 __attribute__((ext_vector_type(2)));
 typedef float ntf4 __attribute__((ext_vector_type(4)));
 
