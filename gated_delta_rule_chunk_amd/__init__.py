@@ -94,6 +94,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_bwd_prologue.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, I32, I32, I32, I32, I32, I32, F,
                                            ctypes.c_int, P, ctypes.c_size_t, P, P, P, P, P, P, P, P, P]
     lib.kda_chunk_bwd_prologue.restype = ctypes.c_int
+    lib.kda_chunk_bwd_conv_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32, ctypes.c_int]
+    lib.kda_chunk_bwd_conv_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_chunk_bwd_conv.argtypes = ([P] * 9 + [I32] + [P] * 4 + [F, F] + [P] * 7 + [I32] * 6 + [F, ctypes.c_int, P,
+                                       ctypes.c_size_t] + [P] * 14 + [P])
+    lib.kda_chunk_bwd_conv.restype = ctypes.c_int
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     lib.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_chunk_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, F, ctypes.c_int,
@@ -390,6 +395,69 @@ def chunk_bwd_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, d_o
                                     _stream(dev))
     _check(st)
     return dq, dk, dv, dg, dbeta, dA, dbias, d_init
+
+
+def chunk_bwd_conv_workspace_bytes(B, T, H, Dk, Dv, N, packed, dtype):
+    """Bytes of workspace kda_chunk_bwd_conv needs."""
+    return int(load_library().kda_chunk_bwd_conv_workspace_bytes(B, T, H, Dk, Dv, N, int(bool(packed)),
+                                                                  _DTYPES[dtype]))
+
+
+def chunk_bwd_conv(xq, xk, xv, wq, wk, wv, g_logit, beta_logit, A_log, dt_bias, d_o, conv_states=None,
+                   d_conv_final=None, activation=True, gate_lower_bound=-5.0, l2_eps=1e-6, initial_state=None,
+                   d_final_state=None, cu_seqlens=None, scale=1.0, workspace=None, want_d_initial=True,
+                   want_d_conv_states=True):
+    """Gradients for ``chunk_fwd_conv`` (kda_chunk_bwd_conv). conv_states and
+    d_conv_final: None or a triple (q, k, v) of [N,3,H*D] float32 (None
+    entries = zeros). Returns a dict of float32 gradients keyed xq, xk, xv
+    ([B,T,H,D]), wq, wk, wv ([H*D,4]), conv_state_q, conv_state_k,
+    conv_state_v ([N,3,H*D] or None), g_logit, beta_logit, A_log, dt_bias,
+    initial_state (or None)."""
+    lib = load_library()
+    B, T, H, Dk, Dv, N, dt, dev = _chunk_inputs(xq, xk, xv, g_logit, beta_logit, initial_state, cu_seqlens,
+                                                ("xq", "xk", "xv", "g_logit", "beta_logit"))
+    _need(A_log, "A_log", (Dk,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H * Dk,), torch.float32, dev)
+    _need(d_o, "d_o", (B, T, H, Dv), dt, dev)
+    if d_final_state is not None:
+        _need(d_final_state, "d_final_state", (N, H, Dk, Dv), torch.float32, dev)
+    Ds = (Dk, Dk, Dv)
+    for w, d, name in zip((wq, wk, wv), Ds, ("wq", "wk", "wv")):
+        _need(w, name, (H * d, 4), torch.float32, dev)
+    s0 = [None, None, None] if conv_states is None else list(conv_states)
+    dfin = [None, None, None] if d_conv_final is None else list(d_conv_final)
+    for lst, what in ((s0, "conv_state"), (dfin, "d_conv_final")):
+        for st_, d, j in zip(lst, Ds, "qkv"):
+            if st_ is not None:
+                _need(st_, f"{what}_{j}", (N, 3, H * d), torch.float32, dev)
+    need = chunk_bwd_conv_workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None, dt)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"xq": torch.empty((B, T, H, Dk), **f32), "xk": torch.empty((B, T, H, Dk), **f32),
+         "xv": torch.empty((B, T, H, Dv), **f32)}
+    for j, d in zip("qkv", Ds):
+        g["w" + j] = torch.empty((H * d, 4), **f32)
+        g["conv_state_" + j] = torch.empty((N, 3, H * d), **f32) if want_d_conv_states else None
+    g["g_logit"] = torch.empty((B, T, H, Dk), **f32)
+    g["beta_logit"] = torch.empty((B, T, H), **f32)
+    g["A_log"] = torch.empty((Dk,), **f32)
+    g["dt_bias"] = torch.empty((H * Dk,), **f32)
+    g["initial_state"] = torch.empty((N, H, Dk, Dv), **f32) if want_d_initial else None
+    st = lib.kda_chunk_bwd_conv(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(s0[0]),
+                                _ptr(s0[1]), _ptr(s0[2]), int(bool(activation)), _ptr(g_logit), _ptr(beta_logit),
+                                _ptr(A_log), _ptr(dt_bias), float(gate_lower_bound), float(l2_eps),
+                                _ptr(initial_state), _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final_state),
+                                _ptr(dfin[0]), _ptr(dfin[1]), _ptr(dfin[2]), B, T, H, Dk, Dv, N, float(scale),
+                                _DTYPES[dt], _ptr(workspace), workspace.numel(), _ptr(g["xq"]), _ptr(g["xk"]),
+                                _ptr(g["xv"]), _ptr(g["wq"]), _ptr(g["wk"]), _ptr(g["wv"]), _ptr(g["conv_state_q"]),
+                                _ptr(g["conv_state_k"]), _ptr(g["conv_state_v"]), _ptr(g["g_logit"]),
+                                _ptr(g["beta_logit"]), _ptr(g["A_log"]), _ptr(g["dt_bias"]),
+                                _ptr(g["initial_state"]), _stream(dev))
+    _check(st)
+    return g
 
 
 def chunk_fwd_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, gate_lower_bound=-5.0,

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -649,6 +650,162 @@ kda_status kda_chunk_bwd_prologue(const void* q_raw, const void* k_raw, const vo
     if ((int64_t)N * H == 0) return KDA_OK;
     const hipError_t e = kda::launch_prologue_bwd(p, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The backward-from-convolution-inputs workspace: the recomputed convolution
+// outputs (dtype), the gradients of them (float32), then one region that the
+// prologue backward and, after it, each convolution backward use in turn.
+struct BwdConvLayout {
+    int64_t y[3], dy[3], rest, bytes;
+};
+BwdConvLayout bwd_conv_layout(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N, bool packed,
+                              kda_dtype dtype) {
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t rows = (int64_t)B * T * H;
+    const int64_t elem = dtype == KDA_BF16 ? 2 : 4;
+    const int64_t D[3] = {Dk, Dk, Dv};
+    BwdConvLayout L;
+    int64_t off = 0;
+    for (int j = 0; j < 3; ++j) { L.y[j] = off; off += up(rows * D[j] * elem); }
+    for (int j = 0; j < 3; ++j) { L.dy[j] = off; off += up(rows * D[j] * 4); }
+    L.rest = off;
+    int64_t rest = kda::prologue_bwd_layout(B, T, H, Dk, Dv, N, packed).bytes;
+    for (int j = 0; j < 3; ++j)
+        rest = std::max<int64_t>(rest, kda::short_conv_bwd_blocks(B, T) * (int64_t)H * D[j] * 4 * 4);
+    L.bytes = off + up(rest);
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_chunk_bwd_conv_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
+                                          int32_t packed, kda_dtype dtype) {
+    if (B < 1 || T <= 0 || H < 1 || !dim_ok(Dk) || !dim_ok(Dv) || N < 0 || (dtype != KDA_F32 && dtype != KDA_BF16))
+        return 0;
+    return (size_t)bwd_conv_layout(B, T, H, Dk, Dv, N, packed != 0, dtype).bytes;
+}
+
+kda_status kda_chunk_bwd_conv(const void* xq, const void* xk, const void* xv, const float* wq, const float* wk,
+                              const float* wv, const float* conv_state_q, const float* conv_state_k,
+                              const float* conv_state_v, int32_t activation, const void* g_logit,
+                              const void* beta_logit, const float* A_log, const float* dt_bias,
+                              float gate_lower_bound, float l2_eps, const float* initial_state,
+                              const int32_t* cu_seqlens, const void* d_o, const float* d_final_state,
+                              const float* d_conv_final_q, const float* d_conv_final_k,
+                              const float* d_conv_final_v, int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                              int32_t N, float scale, kda_dtype dtype, void* workspace, size_t workspace_bytes,
+                              float* dxq, float* dxk, float* dxv, float* dwq, float* dwk, float* dwv,
+                              float* d_conv_state_q, float* d_conv_state_k, float* d_conv_state_v,
+                              float* dg_logit, float* dbeta_logit, float* dA_log, float* ddt_bias,
+                              float* d_initial_state, void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_chunk_bwd_conv";
+    const void* x[3] = {xq, xk, xv};
+    const float* w[3] = {wq, wk, wv};
+    const float* s0[3] = {conv_state_q, conv_state_k, conv_state_v};
+    const float* dfin[3] = {d_conv_final_q, d_conv_final_k, d_conv_final_v};
+    float* dx[3] = {dxq, dxk, dxv};
+    float* dw[3] = {dwq, dwk, dwv};
+    float* ds0[3] = {d_conv_state_q, d_conv_state_k, d_conv_state_v};
+    if (activation != 0 && activation != 1)
+        return fail(KDA_ERR_INVALID_ARG, "%s: activation must be 0 (none) or 1 (SiLU), got %d", fn, activation);
+    for (int j = 0; j < 3; ++j) {
+        if (!w[j] || !dw[j])
+            return fail(KDA_ERR_INVALID_ARG, "%s: the taps and their gradients must be non-NULL", fn);
+        if (reinterpret_cast<uintptr_t>(w[j]) % 16 != 0)
+            return fail(KDA_ERR_INVALID_ARG, "%s: the taps must be 16-byte aligned", fn);
+        if (T > 0 && (!x[j] || !dx[j]))
+            return fail(KDA_ERR_INVALID_ARG, "%s: xq, xk, xv and their gradients must be non-NULL when T > 0", fn);
+    }
+    if (!A_log || !dt_bias || !dA_log || !ddt_bias)
+        return fail(KDA_ERR_INVALID_ARG, "%s: A_log, dt_bias, dA_log and ddt_bias must be non-NULL", fn);
+    if (!(gate_lower_bound < 0.f) || !(gate_lower_bound > -1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: gate_lower_bound must be finite and negative (got %g)", fn,
+                    (double)gate_lower_bound);
+    if (!(l2_eps > 0.f) || !(l2_eps < 1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: l2_eps must be finite and positive (got %g)", fn, (double)l2_eps);
+    if (B < 1 || T < 0 || H < 1 || N < 0)
+        return fail(KDA_ERR_INVALID_ARG, "%s: need B >= 1, T >= 0, H >= 1, N >= 0 (got B=%d T=%d H=%d N=%d)",
+                    fn, B, T, H, N);
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dtype %d is not KDA_F32 or KDA_BF16", fn, (int)dtype);
+    if (!dim_ok(Dk) || !dim_ok(Dv))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: Dk=%d, Dv=%d; supported head dims are 16, 32, 64, 128", fn, Dk, Dv);
+    if (cu_seqlens) {
+        if (B != 1)
+            return fail(KDA_ERR_INVALID_ARG, "%s: packed sequences (cu_seqlens) need B == 1, got B=%d", fn, B);
+        if (N < 1) return fail(KDA_ERR_INVALID_ARG, "%s: packed sequences need N >= 1, got N=%d", fn, N);
+    } else if (N != B) {
+        return fail(KDA_ERR_INVALID_ARG, "%s: without cu_seqlens N must equal B (N=%d, B=%d)", fn, N, B);
+    }
+    if ((int64_t)N * H > ((int64_t)1 << 26) || (int64_t)B * T * H > ((int64_t)1 << 40) ||
+        (int64_t)B * T > ((int64_t)1 << 31) * 16 || (int64_t)H * 128 > ((int64_t)1 << 22))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", fn);
+    if (T > 0 && (!g_logit || !beta_logit || !d_o || !dg_logit || !dbeta_logit))
+        return fail(KDA_ERR_INVALID_ARG, "%s: every input, d_o and the token gradients must be non-NULL when T > 0",
+                    fn);
+    const bool packed = cu_seqlens != nullptr;
+    const BwdConvLayout L = bwd_conv_layout(B, T, H, Dk, Dv, N, packed, dtype);
+    const size_t need = T > 0 ? (size_t)L.bytes : 0;
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KDA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, got %zu%s", fn, need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    {
+        const void* ins[] = {xq, xk, xv, wq, wk, wv, conv_state_q, conv_state_k, conv_state_v, g_logit, beta_logit,
+                             A_log, dt_bias, initial_state, d_o, d_final_state, d_conv_final_q, d_conv_final_k,
+                             d_conv_final_v, workspace};
+        const void* outs[] = {dxq, dxk, dxv, dwq, dwk, dwv, d_conv_state_q, d_conv_state_k, d_conv_state_v,
+                              dg_logit, dbeta_logit, dA_log, ddt_bias, d_initial_state};
+        for (const void* o : outs)
+            for (const void* i : ins)
+                if (o && o == i) return fail(KDA_ERR_INVALID_ARG, "%s: gradients must not alias an input", fn);
+    }
+    char* ws = static_cast<char*>(workspace);
+    void* y[3] = {nullptr, nullptr, nullptr};
+    float* dy[3] = {nullptr, nullptr, nullptr};
+    if (T > 0) {
+        for (int j = 0; j < 3; ++j) {
+            y[j] = ws + L.y[j];
+            dy[j] = reinterpret_cast<float*>(ws + L.dy[j]);
+        }
+        // the forward's convolutions again, into the workspace
+        kda::ConvArgs c[3];
+        const int32_t D[3] = {Dk, Dk, Dv};
+        for (int j = 0; j < 3; ++j) {
+            c[j].x = x[j]; c[j].w = w[j]; c[j].state_in = s0[j]; c[j].cu = cu_seqlens; c[j].y = y[j];
+            c[j].state_out = nullptr; c[j].B = B; c[j].T = T; c[j].C = H * D[j]; c[j].N = N;
+            c[j].act = activation == 1; c[j].bf16 = dtype == KDA_BF16;
+        }
+        const hipError_t e = kda::launch_short_conv_set(c, 3, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    }
+    void* rest = T > 0 ? ws + L.rest : nullptr;
+    const size_t rest_bytes = T > 0 ? (size_t)(L.bytes - L.rest) : 0;
+    char inner[sizeof(g_last_error)];
+    kda_status st = kda_chunk_bwd_prologue(y[0], y[1], y[2], g_logit, beta_logit, A_log, dt_bias, gate_lower_bound,
+                                           l2_eps, initial_state, cu_seqlens, d_o, d_final_state, B, T, H, Dk, Dv, N,
+                                           scale, dtype, rest, rest_bytes, dy[0], dy[1], dy[2], dg_logit, dbeta_logit,
+                                           dA_log, ddt_bias, d_initial_state, stream);
+    if (st != KDA_OK) {
+        snprintf(inner, sizeof(inner), "%s", g_last_error);
+        return fail(st, "%s: %s", fn, inner);
+    }
+    const int32_t D[3] = {Dk, Dk, Dv};
+    for (int j = 0; j < 3; ++j) {
+        st = kda_short_conv_bwd(x[j], w[j], s0[j], cu_seqlens, dy[j], dfin[j], B, T, H * D[j], N, activation, dtype,
+                                rest, rest_bytes, dx[j], dw[j], ds0[j], stream);
+        if (st != KDA_OK) {
+            snprintf(inner, sizeof(inner), "%s", g_last_error);
+            return fail(st, "%s: %s", fn, inner);
+        }
+    }
     return KDA_OK;
 }
 

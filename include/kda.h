@@ -366,6 +366,63 @@ kda_status kda_chunk_bwd_prologue(const void* q_raw, const void* k_raw, const vo
                                   float* ddt_bias, float* d_initial_state, void* stream);
 
 /*
+ * Bytes of device workspace kda_chunk_bwd_conv needs: the three recomputed
+ * convolution outputs (dtype) and their float32 gradients, B*T*H*(2 Dk + Dv)
+ * elements each, plus the larger of kda_chunk_bwd_prologue_workspace_bytes
+ * and kda_short_conv_bwd_workspace_bytes for the same sizes (each 256-byte
+ * aligned). 0 when T = 0 or a size is out of range.
+ */
+size_t kda_chunk_bwd_conv_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
+                                          int32_t packed, kda_dtype dtype);
+
+/*
+ * Backward of kda_chunk_fwd_conv: the gradients of
+ *   L = sum_t <d_o[t], o[t]> + sum_n <d_final_state[n], final_state[n]>
+ *       + sum_n sum_j <d_conv_final_j[n], conv_state_j_out[n]>   (j = q, k, v)
+ * with respect to the projections before the short convolution, the taps,
+ * the initial conv states, the gate logits and parameters and the initial
+ * state. It recomputes the three convolutions into the workspace, runs
+ * kda_chunk_bwd_prologue on them, then kda_short_conv_bwd for each projection
+ * (the convolution before the prologue: hysenlabs "kimi-k3-mlx", section
+ * "Attention is 93 layers split between KDA and a NoPE gated MLA"), and
+ * equals that sequence of calls bit for bit. This is the layer's backward for
+ * training from the pre-convolution projections (ISEEKYAN/k3 README, the
+ * single-rank reference path that runs loss and backward).
+ *
+ *   xq, xk, xv, wq, wk, wv, conv_state_q, _k, _v, activation, g_logit, beta_logit,
+ *   A_log, dt_bias, gate_lower_bound, l2_eps, initial_state, cu_seqlens,
+ *   B, T, H, Dk, Dv, N, scale, dtype
+ *                 exactly as passed to kda_chunk_fwd_conv
+ *   d_o, d_final_state
+ *                 as for kda_chunk_bwd
+ *   d_conv_final_q, _k, _v  [N][3][H*D] float32 or NULL (zeros): cotangents
+ *                 of the final conv states
+ *   workspace     at least kda_chunk_bwd_conv_workspace_bytes(...) bytes,
+ *                 owned by the caller; contents on entry do not matter
+ *   dxq, dxk [B,T,H,Dk], dxv [B,T,H,Dv]; dwq, dwk [H*Dk][4], dwv [H*Dv][4];
+ *   d_conv_state_q, _k, _v [N][3][H*D] (or NULL, not written); dg_logit,
+ *   dbeta_logit, dA_log, ddt_bias, d_initial_state (or NULL) as for
+ *   kda_chunk_bwd_prologue: float32 outputs that must not alias an input
+ *
+ * Errors as for kda_chunk_bwd_prologue and kda_short_conv_bwd (their messages
+ * are prefixed with this call's name); NULL or misaligned taps, a NULL tap
+ * gradient or a bad activation are KDA_ERR_INVALID_ARG.
+ */
+kda_status kda_chunk_bwd_conv(const void* xq, const void* xk, const void* xv, const float* wq, const float* wk,
+                              const float* wv, const float* conv_state_q, const float* conv_state_k,
+                              const float* conv_state_v, int32_t activation, const void* g_logit,
+                              const void* beta_logit, const float* A_log, const float* dt_bias,
+                              float gate_lower_bound, float l2_eps, const float* initial_state,
+                              const int32_t* cu_seqlens, const void* d_o, const float* d_final_state,
+                              const float* d_conv_final_q, const float* d_conv_final_k,
+                              const float* d_conv_final_v, int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv,
+                              int32_t N, float scale, kda_dtype dtype, void* workspace, size_t workspace_bytes,
+                              float* dxq, float* dxk, float* dxv, float* dwq, float* dwk, float* dwv,
+                              float* d_conv_state_q, float* d_conv_state_k, float* d_conv_state_v,
+                              float* dg_logit, float* dbeta_logit, float* dA_log, float* ddt_bias,
+                              float* d_initial_state, void* stream);
+
+/*
  * Short causal depthwise convolution over time (kernel size 4), the step that
  * KDA applies to the query, key and value projections before the recurrence
  * (hysenlabs "kimi-k3-mlx", section "Attention is 93 layers split between KDA

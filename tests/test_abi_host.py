@@ -22,7 +22,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = kda.declared_symbols()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step", "kda_short_conv",
-                          "kda_recurrent_step_prologue", "kda_recurrent_step_conv",
+                          "kda_recurrent_step_prologue", "kda_recurrent_step_conv", "kda_chunk_bwd_conv",
+                          "kda_chunk_bwd_conv_workspace_bytes",
                           "kda_short_conv_step", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
                           "kda_chunk_fwd_split", "kda_chunk_fwd_split_workspace_bytes",
                           "kda_chunk_fwd_split_static", "kda_chunk_fwd_conv", "kda_chunk_fwd_conv_workspace_bytes",
@@ -511,3 +512,45 @@ def test_chunk_fwd_conv_workspace_bytes():
     assert kda.chunk_fwd_conv_workspace_bytes(1, 100, 4, 128, 128, torch.bfloat16, -6.0) == 100 * 4 * 384 * 2
     assert kda.chunk_fwd_conv_workspace_bytes(1, 0, 4, 128, 128, torch.bfloat16, -5.0) == 0
 
+
+
+def _bwd_conv(lib, **kw):
+    P = ctypes.c_void_p
+    a = dict(xq=FAKE, xk=FAKE, xv=FAKE, wq=P(0x3000), wk=P(0x4000), wv=P(0x5000), sq=None, sk=None, sv=None, act=1,
+             g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, lb=-5.0, eps=1e-6, s0=None, cu=None, d_o=FAKE,
+             dfin=None, dcq=None, dck=None, dcv=None, B=1, T=64, H=2, Dk=128, Dv=128, N=1, scale=1.0,
+             dtype=kda.KDA_BF16, ws=P(0x100000), wsb=1 << 40, dxq=P(0x6000), dxk=P(0x7000), dxv=P(0x8000),
+             dwq=P(0x9000), dwk=P(0xa000), dwv=P(0xb000), dsq=None, dsk=None, dsv=None, dg=P(0xc000),
+             db=P(0xd000), dA=P(0xe000), ddt=P(0xf000), ds0=None, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_bwd_conv(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(act=2), kda.KDA_ERR_INVALID_ARG, "activation"),
+    (dict(wk=None), kda.KDA_ERR_INVALID_ARG, "taps"),
+    (dict(dwv=None), kda.KDA_ERR_INVALID_ARG, "taps"),
+    (dict(wq=ctypes.c_void_p(0x3008)), kda.KDA_ERR_INVALID_ARG, "aligned"),
+    (dict(xv=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(dA=None), kda.KDA_ERR_INVALID_ARG, "dA_log"),
+    (dict(lb=0.0), kda.KDA_ERR_INVALID_ARG, "gate_lower_bound"),
+    (dict(eps=-1.0), kda.KDA_ERR_INVALID_ARG, "l2_eps"),
+    (dict(Dk=8), kda.KDA_ERR_UNSUPPORTED, "head dims"),
+    (dict(N=2), kda.KDA_ERR_INVALID_ARG, "N must equal B"),
+    (dict(wsb=16), kda.KDA_ERR_INVALID_ARG, "workspace"),
+    (dict(dg=FAKE), kda.KDA_ERR_INVALID_ARG, "alias"),
+    (dict(dxq=ctypes.c_void_p(0x100000)), kda.KDA_ERR_INVALID_ARG, "alias"),
+])
+def test_chunk_bwd_conv_rejects_before_launch(lib, kw, status, needle):
+    assert _bwd_conv(lib, **kw) == status
+    msg = lib.kda_last_error_message().decode()
+    assert needle in msg and msg.startswith("kda_chunk_bwd_conv")
+
+
+def test_chunk_bwd_conv_workspace_covers_its_parts(lib):
+    B, T, H, D, N = 1, 4096, 96, 128, 1
+    need = lib.kda_chunk_bwd_conv_workspace_bytes(B, T, H, D, D, N, 0, kda.KDA_BF16)
+    parts = 3 * B * T * H * D * (2 + 4) + max(lib.kda_chunk_bwd_prologue_workspace_bytes(B, T, H, D, D, N, 0),
+                                              lib.kda_short_conv_bwd_workspace_bytes(B, T, H * D))
+    assert parts <= need <= parts + 8 * 256
+    assert lib.kda_chunk_bwd_conv_workspace_bytes(B, 0, H, D, D, N, 0, kda.KDA_BF16) == 0

@@ -42,7 +42,7 @@ def _oracle_step(raw, conv_out, A_log, dt_bias, ref_cache, slots, scale):
 
 
 @pytest.mark.parametrize("dtype,Dk,Dv", [("bf16", 128, 128), ("f32", 128, 128), ("f32", 64, 32),
-                                         ("bf16", 16, 128), ("f32", 128, 16)])
+                                         ("bf16", 16, 128), ("f32", 128, 16), ("bf16", 128, 64)])
 def test_step_prologue_against_oracle(dtype, Dk, Dv):
     say(f"[case] decode prologue {dtype} Dk={Dk} Dv={Dv}")
     Nb, H, steps, scale = len(SLOTS), 3, 4, 0.7

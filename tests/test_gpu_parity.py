@@ -118,7 +118,8 @@ def test_delta_rule_invariant_on_gpu_final_state():
 
 # --- decode step ---------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,Dk,Dv", [("bf16", 128, 128), ("f32", 128, 128), ("f32", 64, 32)])
+@pytest.mark.parametrize("dtype,Dk,Dv", [("bf16", 128, 128), ("f32", 128, 128), ("f32", 64, 32), ("bf16", 128, 64),
+                                         ("f32", 64, 64)])
 def test_recurrent_step_against_oracle(dtype, Dk, Dv):
     say(f"[case] decode {dtype} Dk={Dk} Dv={Dv}")
     Nb, H, n_slots, steps = 6, 3, 9, 5
