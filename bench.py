@@ -29,7 +29,8 @@ the same workload with output and final-state cotangents, against the fp32
 matrix-core peak (its products run as float32 MFMA) with the algorithmic flop
 count of the chunked backward (recompute included), plus the fp64 oracle's
 backward on the same workload; its ``from_raw_projections`` entry times the
-backward through the gate, beta and L2-norm prologue (kda_chunk_bwd_prologue). ``split`` times the intra-sequence split
+backward through the gate, beta and L2-norm prologue (kda_chunk_bwd_prologue), and its ``from_conv`` entry
+the backward from the pre-convolution projections (kda_chunk_bwd_conv). ``split`` times the intra-sequence split
 (kda_chunk_fwd_split, 10 segments) on 12 heads at T=32768 against the unsplit
 call. ``decode`` times kda_recurrent_step on
 256 rows x 96 heads against an fp32 state cache (HBM-bound); its
@@ -491,6 +492,7 @@ def bench_backward(steps, warmup, cpu=True):
            "timed": "one kda_chunk_bwd call: the per-chunk T/P/KK kernel (which also zeroes the atomically "
                     "summed gradients) and the sequential kernel"}
     res["from_raw_projections"] = bench_backward_prologue(steps, warmup)
+    res["from_conv"] = bench_backward_conv(steps, warmup)
     if cpu:
         res["cpu_baseline"] = cpu_backward_baseline()
     return res
@@ -528,6 +530,45 @@ def bench_backward_prologue(steps, warmup):
     return {"workload": "k3_t4096 backward from raw projections (gate lb=-5, L2 eps 1e-6): gradients of q_raw, "
                         "k_raw, v, g_logit, beta_logit, A_log, dt_bias and the initial state",
             "ms_per_step": wall / steps * 1e3, "kernel_ms": float(batch),
+            "tokens_per_s": w.T / (float(batch) * 1e-3)}
+
+
+def bench_backward_conv(steps, warmup):
+    """kda_chunk_bwd_conv on k3_t4096: the backward from the projections
+    before the short convolution (SiLU, zero initial conv states), with the
+    convolutions recomputed, the prologue backward and the convolution
+    backward of q, k and v in one call."""
+    w = synth.WORKLOADS["k3_t4096"]
+    dev = torch.device("cuda:0")
+    C = w.H * w.Dk
+    taps = [synth.make_conv_taps(C, w.seed, j).to(dev) for j in range(3)]
+    sets = []
+    for s_ in range(2):
+        inp = synth.make_prologue_inputs(w.B, w.T, w.H, w.Dk, w.Dv, seed=w.seed + 1000 * s_, dtype=w.dtype)
+        d_o, dfin = synth.make_cotangents({"v": inp["v"], "q": inp["q_raw"], "cu_seqlens": None},
+                                          seed=w.seed + 1000 * s_ + 7)
+        d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+        d["d_o"], d["d_final"] = d_o.to(dev), dfin.to(dev)
+        sets.append(d)
+    ws = torch.empty((kda.chunk_bwd_conv_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, w.B, False, torch.bfloat16),),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+
+    def step(i):
+        d = sets[i % 2]
+        out["g"] = kda.chunk_bwd_conv(d["q_raw"], d["k_raw"], d["v"], *taps, d["g_logit"], d["beta_logit"],
+                                      d["A_log"], d["dt_bias"], d["d_o"], activation=True,
+                                      gate_lower_bound=synth.GATE_LOWER_BOUND, l2_eps=1e-6,
+                                      d_final_state=d["d_final"], scale=w.Dk ** -0.5, workspace=ws)
+
+    wall, per, batch = time_launches(step, steps, warmup, stream)
+    if not all(torch.isfinite(x).all() for x in out["g"].values() if x is not None):
+        raise RuntimeError("non-finite backward output")
+    return {"workload": "k3_t4096 backward from the pre-convolution projections (kernel-4 conv with SiLU, gate "
+                        "lb=-5, L2 eps 1e-6): gradients of xq, xk, xv, the taps, the conv states, g_logit, "
+                        "beta_logit, A_log, dt_bias and the initial state",
+            "ms_per_step": wall / steps * 1e3, "kernel_ms": float(batch), "kernel_ms_median": float(np.median(per)),
             "tokens_per_s": w.T / (float(batch) * 1e-3)}
 
 
