@@ -186,3 +186,50 @@ def test_decode_conv_steps_reproduce_the_chunk_forward():
     ef = rel(cache.cpu().numpy(), fin_ref.cpu().numpy())
     say(f"        relL2 o={eo:.3e} final={ef:.3e}")
     assert eo <= TOL_BF16 and ef <= TOL_BF16
+
+
+def test_prefill_then_decode_hands_over_every_state():
+    """A serving flow: kda_chunk_fwd_conv over a prompt, its final state and
+    final conv states written into cache slots, then kda_recurrent_step_conv
+    for the following tokens, against kda_chunk_fwd_conv over prompt and
+    continuation together. Checks that the prefill's state and conv-state
+    layouts are the decode caches' layouts."""
+    B, T0, T1, H, D = 3, 50, 6, 4, 128
+    say(f"[case] prefill {T0} tokens with kda_chunk_fwd_conv, then {T1} decode steps, B={B}")
+    inp = synth.make_prologue_inputs(B, T0 + T1, H, D, D, seed=740, dtype="bf16", init_state=True)
+    Cs, taps, _ = _conv_setup(H, D, D, seed=741)
+    d = {n: (t.cuda() if t is not None else None) for n, t in inp.items()}
+    taps = [t.cuda() for t in taps]
+    rng = np.random.default_rng(742)
+    s0 = [torch.from_numpy(rng.standard_normal((B, 3, C)).astype(np.float32)).cuda() for C in Cs]
+    kw = dict(gate_lower_bound=LB, l2_eps=EPS)
+    o_all, fin_all, _ = kda.chunk_fwd_conv(d["q_raw"], d["k_raw"], d["v"], *taps, d["g_logit"], d["beta_logit"],
+                                           d["A_log"], d["dt_bias"], conv_states=s0,
+                                           initial_state=d["initial_state"], **kw)
+    head = {n: d[n][:, :T0].contiguous() for n in ("q_raw", "k_raw", "v", "g_logit", "beta_logit")}
+    o_pre, fin_pre, conv_fin = kda.chunk_fwd_conv(head["q_raw"], head["k_raw"], head["v"], *taps, head["g_logit"],
+                                                  head["beta_logit"], d["A_log"], d["dt_bias"], conv_states=s0,
+                                                  initial_state=d["initial_state"], **kw)
+    slots = torch.tensor([5, 0, 2], dtype=torch.int32).cuda()
+    n_slots = 7
+    cache = torch.zeros((n_slots, H, D, D), dtype=torch.float32, device="cuda")
+    cache[slots.long()] = fin_pre
+    conv = []
+    for j, C in enumerate(Cs):
+        c = torch.zeros((n_slots, 3, C), dtype=torch.float32, device="cuda")
+        c[slots.long()] = conv_fin[j]
+        conv.append(c)
+    outs = []
+    for t in range(T0, T0 + T1):
+        step = lambda n: d[n][:, t].contiguous()  # noqa: E731
+        outs.append(kda.recurrent_step_conv(step("q_raw"), step("k_raw"), step("v"), *taps, conv, step("g_logit"),
+                                            step("beta_logit"), d["A_log"], d["dt_bias"], cache, state_slots=slots,
+                                            **kw))
+    torch.cuda.synchronize()
+    o = torch.cat([o_pre, torch.stack(outs, 1)], 1)
+    eo = rel(o.float().cpu().numpy(), o_all.float().cpu().numpy())
+    ef = rel(cache[slots.long()].cpu().numpy(), fin_all.cpu().numpy())
+    say(f"        relL2 o={eo:.3e} final={ef:.3e}")
+    assert eo <= TOL_BF16 and ef <= TOL_BF16
+    # the prompt's outputs are the same call's prefix: equal bit for bit
+    assert torch.equal(o_pre, o_all[:, :T0])
