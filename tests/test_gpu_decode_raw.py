@@ -233,3 +233,46 @@ def test_prefill_then_decode_hands_over_every_state():
     assert eo <= TOL_BF16 and ef <= TOL_BF16
     # the prompt's outputs are the same call's prefix: equal bit for bit
     assert torch.equal(o_pre, o_all[:, :T0])
+
+
+def test_decode_step_replays_from_a_captured_graph():
+    """A serving loop captures its per-token work in a HIP graph: one
+    kda_recurrent_step_conv captured once and replayed for several tokens
+    (inputs copied into the captured buffers between replays), against the
+    same steps run eagerly on copies of the caches."""
+    Nb, H, Dk, Dv, steps = 4, 3, 128, 128, 5
+    say(f"[case] decode conv step in a captured graph, {steps} replays")
+    cache = synth.make_decode_cache(N_SLOTS, H, Dk, Dv, seed=750).cuda()
+    A_log, dt_bias = (t.cuda() for t in synth.make_gate_params(H, Dk, seed=751))
+    Cs, taps, caches = _conv_setup(H, Dk, Dv, seed=752)
+    taps = [t.cuda() for t in taps]
+    slots = torch.tensor([6, -1, 1, 3], dtype=torch.int32).cuda()
+    conv_g = [c.cuda() for c in caches]
+    conv_e = [c.cuda() for c in caches]
+    cache_g, cache_e = cache.clone(), cache.clone()
+    raws = [{n: t.cuda() for n, t in synth.make_decode_raw_step(Nb, H, Dk, Dv, seed=753, step=s).items()}
+            for s in range(steps)]
+    buf = {n: torch.empty_like(t) for n, t in raws[0].items()}
+    o_g = torch.empty((Nb, H, Dv), dtype=torch.bfloat16, device="cuda")
+
+    def step(ins, conv, c, out=None):
+        return kda.recurrent_step_conv(ins["q_raw"], ins["k_raw"], ins["v"], *taps, conv, ins["g_logit"],
+                                       ins["beta_logit"], A_log, dt_bias, c, state_slots=slots, out=out)
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step(buf, conv_g, cache_g, out=o_g)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        for n in buf:
+            buf[n].copy_(raws[s][n])
+        graph.replay()
+        o_e = step(raws[s], conv_e, cache_e)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e), s
+    assert torch.equal(cache_g, cache_e)
+    for a, b in zip(conv_g, conv_e):
+        assert torch.equal(a, b)
