@@ -28,6 +28,8 @@
 #include <algorithm>
 #include <mutex>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -277,6 +279,11 @@ __global__ __launch_bounds__(scan_threads<DK>()) void split_scan_kernel(const fl
 // 32w..32w+31 (two 16-column tiles). The products run on the matrix cores as
 // D = S_inᵀ oAᵀ (16x16x32 bf16): S_in split into bf16 hi + lo parts (float32
 // accuracy for the state) held in registers, oA exact (it is stored in bf16).
+// Tile t's operand row a stands for output column 8(a/4) + 4t + a%4 of the
+// wave's 32, so that lane group lg ends up with the 8 consecutive columns
+// 8lg..8lg+7 of its row from the two tiles, and o is read and written in
+// 16-byte pieces, 64 contiguous bytes per row and instruction (8-byte pieces,
+// 32 bytes per row, cost 42 of the kernel's 68 us at 12 heads x 32768).
 // A block's oA rows (16 KB) go straight from global memory to LDS, once for
 // the four waves, in a ring of three buffers: blocks b+1 and b+2 (and their o
 // rows, into registers) are in flight while block b is computed, and the wait
@@ -289,7 +296,7 @@ constexpr int kCorrBlockBytes = 64 * 256;
 // outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt
 // left at their maxima)
 constexpr int vmcnt_wait(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // The workgroup barrier of the correction loop, with no memory fence. A fence
 // (that of __syncthreads(), or one on LDS alone) waits for every global access
 // of the wave, the global-to-LDS loads of later blocks included. Here each
@@ -329,8 +336,8 @@ __global__ __launch_bounds__(256, 2) void split_correct_kernel(const int32_t* cu
     // Issue block r0's loads: its oA rows into LDS buffer `bi` (wave w: rows
     // 16w..16w+15, four rows per instruction; rows past the segment end read
     // its last row) and this wave's o rows (row li of tile rt, columns
-    // 32w + 16t + 4lg..+3) into ob.
-    auto issue = [&](int64_t r0, int bi, uint2 (&ob)[4][2]) {
+    // 32w + 8lg..+7) into ob.
+    auto issue = [&](int64_t r0, int bi, uint4 (&ob)[4]) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int i = 16 * w + 4 * k + (lane >> 4);                  // row in the block
@@ -343,13 +350,11 @@ __global__ __launch_bounds__(256, 2) void split_correct_kernel(const int32_t* cu
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             const int64_t row = r0 + 16 * rt + li < eos ? r0 + 16 * rt + li : eos - 1;
-            const __bf16* o_row = o + row * rstride + (int64_t)h * 128 + 32 * w + 4 * lg;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) ob[rt][t] = *reinterpret_cast<const uint2*>(o_row + 16 * t);
+            ob[rt] = *reinterpret_cast<const uint4*>(o + row * rstride + (int64_t)h * 128 + 32 * w + 8 * lg);
         }
     };
     // A operands: lane (li, lg) of column tile t, k-step ks holds
-    // S_in[32ks + 8lg + j][32w + 16t + li], j = 0..7
+    // S_in[32ks + 8lg + j][32w + 8(li/4) + 4t + li%4], j = 0..7
     const float* S = Sin + ((int64_t)seg * H + h) * 128 * 128;
     bf16x8 shi[2][4], slo[2][4];
 #pragma unroll
@@ -358,13 +363,14 @@ __global__ __launch_bounds__(256, 2) void split_correct_kernel(const int32_t* cu
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float x = S[(int64_t)(32 * ks + 8 * lg + j) * 128 + 32 * w + 16 * t + li];
+                const int col = 32 * w + 8 * (li >> 2) + 4 * t + (li & 3);
+                const float x = S[(int64_t)(32 * ks + 8 * lg + j) * 128 + col];
                 const __bf16 hi = (__bf16)x;
                 shi[t][ks][j] = hi;
                 slo[t][ks][j] = (__bf16)(x - (float)hi);
             }
-    uint2 ob0[4][2], ob1[4][2], ob2[4][2];
-    auto compute = [&](int64_t r0, int bi, const uint2 (&ob)[4][2]) {
+    uint4 ob0[4], ob1[4], ob2[4];
+    auto compute = [&](int64_t r0, int bi, const uint4 (&ob)[4]) {
         // o from row r0 to the block's end or the segment's, whichever comes first
         const int64_t nrows = eos - r0 < 64 ? eos - r0 : 64;
         const __amdgpu_buffer_rsrc_t ro = uniform_rsrc(o + r0 * rstride, nrows * rstride * 2);
@@ -382,56 +388,61 @@ __global__ __launch_bounds__(256, 2) void split_correct_kernel(const int32_t* cu
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(slo[t][ks], b, acc[t], 0, 0, 0);
                 }
             }
-            // D: lane (li, lg) holds row li of the tile, columns 32w + 16t + 4lg + i;
+            // D: lane (li, lg) holds row li of the tile, columns 32w + 8lg + 4t + i;
             // every store is issued, and those of rows past the segment end fall
             // outside the descriptor's range, where the hardware drops them
+            const uint32_t in[4] = {ob[rt].x, ob[rt].y, ob[rt].z, ob[rt].w};
+            uint32_t out[4];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const float y0 = __uint_as_float(ob[rt][t].x << 16) + acc[t][0];
-                const float y1 = __uint_as_float(ob[rt][t].x & 0xffff0000u) + acc[t][1];
-                const float y2 = __uint_as_float(ob[rt][t].y << 16) + acc[t][2];
-                const float y3 = __uint_as_float(ob[rt][t].y & 0xffff0000u) + acc[t][3];
-                const int off = 2 * (i * (int)rstride + 128 * h + 32 * w + 16 * t + 4 * lg);
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack2_bf16(y0, y1), pack2_bf16(y2, y3)}, ro, off, 0, 0);
+                const float y0 = __uint_as_float(in[2 * t] << 16) + acc[t][0];
+                const float y1 = __uint_as_float(in[2 * t] & 0xffff0000u) + acc[t][1];
+                const float y2 = __uint_as_float(in[2 * t + 1] << 16) + acc[t][2];
+                const float y3 = __uint_as_float(in[2 * t + 1] & 0xffff0000u) + acc[t][3];
+                out[2 * t] = pack2_bf16(y0, y1);
+                out[2 * t + 1] = pack2_bf16(y2, y3);
             }
+            const int off = 2 * (i * (int)rstride + 128 * h + 32 * w + 8 * lg);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{out[0], out[1], out[2], out[3]}, ro, off, 0, 0);
         }
     };
     // Every block issues the same vector-memory operations per wave, past the
-    // segment end too (its loads then repeat the last row): issue() makes 12
-    // loads (4 into LDS, 8 into registers), compute() 8 stores. Before block k
+    // segment end too (its loads then repeat the last row): issue() makes 8
+    // loads (4 into LDS, 4 into registers), compute() 4 stores. Before block k
     // the operations issued after its loads are block k+1's loads (block 0),
     // then block k-1's stores and block k+2's loads (block 1), then block k-2's
-    // stores as well, so the wait leaves 12, 20 or 28 outstanding, and the
+    // stores as well, so the wait leaves 8, 12 or 16 outstanding, and the
     // compiler, which sees the same operations on every path, needs no wait of
     // its own.
-    constexpr int kLoads = 12, kStores = 8;
-    auto wait_block = [](int k) {
-        if (k == 0) __builtin_amdgcn_s_waitcnt(vmcnt_wait(kLoads));
-        else if (k == 1) __builtin_amdgcn_s_waitcnt(vmcnt_wait(kLoads + kStores));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_wait(kLoads + 2 * kStores));
-    };
+    constexpr int kLoads = 8, kStores = 4;
+    using Wait0 = std::integral_constant<int, kLoads>;
+    using Wait1 = std::integral_constant<int, kLoads + kStores>;
+    using Wait2 = std::integral_constant<int, kLoads + 2 * kStores>;
     // every wave runs the same block sequence, so the barriers match
     const int64_t step = (int64_t)R * 64;
     int64_t rk = bos + (int64_t)r * 64;
     issue(rk, 0, ob0);
     issue(rk + step, 1, ob1);
-    int k = 0;
     // one block: its loads landed for every wave, the buffer of block k-1 is
-    // free for block k+2
-    auto stage = [&](int bi, const uint2 (&ob)[4][2], int bn, uint2 (&obn)[4][2]) -> bool {
-        wait_block(k);
+    // free for block k+2. Blocks 0 and 1 run before the loop, so that every
+    // stage in it waits with the same count: with the count chosen at run
+    // time the compiler lost track of the register loads and waited for all
+    // of them before the first use in one stage of three.
+    auto stage = [&](auto wait_n, int bi, const uint4 (&ob)[4], int bn, uint4 (&obn)[4]) -> bool {
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(decltype(wait_n)::value));
         lds_barrier();
         issue(rk + 2 * step, bn, obn);
         compute(rk, bi, ob);
         if (rk + step >= eos) return false;
         rk += step;
-        ++k;
         return true;
     };
-    for (;;) {
-        if (!stage(0, ob0, 2, ob2)) break;
-        if (!stage(1, ob1, 0, ob0)) break;
-        if (!stage(2, ob2, 1, ob1)) break;
+    if (stage(Wait0{}, 0, ob0, 2, ob2) && stage(Wait1{}, 1, ob1, 0, ob0)) {
+        for (;;) {
+            if (!stage(Wait2{}, 2, ob2, 1, ob1)) break;
+            if (!stage(Wait2{}, 0, ob0, 2, ob2)) break;
+            if (!stage(Wait2{}, 1, ob1, 0, ob0)) break;
+        }
     }
     // the loads issued past the end still write LDS: they land before the
     // workgroup ends and its LDS goes to another
