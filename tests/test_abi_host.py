@@ -554,3 +554,9 @@ def test_chunk_bwd_conv_workspace_covers_its_parts(lib):
                                               lib.kda_short_conv_bwd_workspace_bytes(B, T, H * D))
     assert parts <= need <= parts + 8 * 256
     assert lib.kda_chunk_bwd_conv_workspace_bytes(B, 0, H, D, D, N, 0, kda.KDA_BF16) == 0
+
+
+def test_autograd_entry_points_import_without_a_gpu():
+    from gated_delta_rule_chunk_amd import autograd as kag
+    for name in ("chunk_kda", "chunk_kda_prologue", "chunk_kda_conv"):
+        assert callable(getattr(kag, name))
