@@ -44,11 +44,13 @@ def _gpu_fused(inp, taps, s0, dfin, d_o, d_fin, scale):
                               d_final_state=d_fin.to(dev), cu_seqlens=d["cu_seqlens"], scale=scale)
 
 
-@pytest.mark.parametrize("dtype,packed", [("bf16", False), ("f32", False), ("bf16", True), ("f32", True)])
-def test_bwd_conv_equals_the_sequence_of_calls_bitwise(dtype, packed):
-    H, D, scale = 2, 128, 128 ** -0.5
+@pytest.mark.parametrize("dtype,packed,Dk,Dv", [("bf16", False, 128, 128), ("f32", False, 128, 128),
+                                                ("bf16", True, 128, 128), ("f32", True, 128, 128),
+                                                ("f32", False, 64, 32), ("bf16", True, 32, 64)])
+def test_bwd_conv_equals_the_sequence_of_calls_bitwise(dtype, packed, Dk, Dv):
+    H, scale = 2, Dk ** -0.5
     lengths = [37, 0, 64, 100] if packed else None
-    inp, taps, s0, dfin, d_o, d_fin, Cs = _case(2, 77, H, D, D, seed=1400, dtype=dtype, lengths=lengths)
+    inp, taps, s0, dfin, d_o, d_fin, Cs = _case(2, 77, H, Dk, Dv, seed=1400, dtype=dtype, lengths=lengths)
     B, T = inp["q_raw"].shape[:2]
     say(f"[case] bwd conv == chain, {dtype} B={B} T={T} packed={packed}")
     got = _gpu_fused(inp, taps, s0, dfin, d_o, d_fin, scale)

@@ -126,3 +126,56 @@ def test_full_size_decode_128_steps():
     say(f"        decode: whole relL2 o(all steps)={rel(outs, refs):.3e} cache={rel(got, ref):.3e}")
     say(f"        worst (row, head) o over the steps: relL2={worst_o[0]:.3e} at {worst_o[1]}; "
         f"cache: relL2={worst_c[0]:.3e} at {worst_c[1]}")
+
+
+def test_full_size_decode_from_conv_inputs():
+    """kda_recurrent_step_conv on the decode workload's shape (256 rows x 96
+    heads, d = 128, bf16), 16 steps, every row and head against the oracle's
+    chain: the convolution step (float64 caches), the prologue (float64), and
+    the C oracle's decode step (which takes the prologue's outputs as float32,
+    a 1e-7 relative rounding far below the bar)."""
+    cfg = synth.DECODE
+    Nb, H, Dk, Dv, seed, steps = cfg["Nb"], cfg["H"], cfg["Dk"], cfg["Dv"], cfg["seed"], 16
+    lb, eps = synth.GATE_LOWER_BOUND, 1e-6
+    say(f"[case] full size decode from conv inputs: Nb={Nb} H={H} d={Dk} steps={steps}, every row and head")
+    cache = synth.make_decode_cache(Nb, H, Dk, Dv, seed=seed)
+    ref = cache.double().numpy()
+    dcache = cache.cuda()
+    del cache
+    A_log, dt_bias = synth.make_gate_params(H, Dk, seed)
+    Cs = (H * Dk, H * Dk, H * Dv)
+    taps = [synth.make_conv_taps(C, seed, j) for j, C in enumerate(Cs)]
+    conv0 = [synth.make_conv_cache(Nb, C, seed, j) for j, C in enumerate(Cs)]
+    dconv = [c.cuda() for c in conv0]
+    rconv = [c.double().numpy().copy() for c in conv0]
+    dtaps = [t.cuda() for t in taps]
+    dA, db = A_log.cuda(), dt_bias.cuda()
+    outs = np.zeros((steps, Nb, H, Dv), dtype=np.float32)
+    refs = np.zeros((steps, Nb, H, Dv))
+    for step in range(steps):
+        x = synth.make_decode_raw_step(Nb, H, Dk, Dv, seed, step)
+        d = {k: v.cuda() for k, v in x.items()}
+        o = kda.recurrent_step_conv(d["q_raw"], d["k_raw"], d["v"], *dtaps, dconv, d["g_logit"], d["beta_logit"],
+                                    dA, db, dcache, gate_lower_bound=lb, l2_eps=eps)
+        outs[step] = o.float().cpu().numpy()
+        y = [kda_ref.c_short_conv_step(x[n].float().numpy().reshape(Nb, Cs[j]), taps[j].numpy(), rconv[j],
+                                       activation=True).reshape(x[n].shape)
+             for j, n in enumerate(("q_raw", "k_raw", "v"))]
+        q, k, g, beta = kda_ref.prologue(y[0], y[1], x["g_logit"].float().numpy(), x["beta_logit"].float().numpy(),
+                                         A_log.numpy(), dt_bias.numpy(), lb, eps)
+        refs[step] = kda_ref.c_decode_step(q, k, y[2], g, beta, ref)
+    torch.cuda.synchronize()
+    kda.device_check()
+    got = dcache.cpu().numpy()
+    for j in range(3):
+        np.testing.assert_array_equal(dconv[j].cpu().numpy().astype(np.float64), rconv[j])
+    worst_o, worst_c = (0.0, None), (0.0, None)
+    for r in range(Nb):
+        for h in range(H):
+            eo = rel(outs[:, r, h], refs[:, r, h])
+            ec = rel(got[r, h], ref[r, h])
+            assert eo <= TOL_BF16 and ec <= TOL_BF16, (r, h, eo, ec)
+            worst_o = max(worst_o, (eo, (r, h)), key=lambda t: t[0])
+            worst_c = max(worst_c, (ec, (r, h)), key=lambda t: t[0])
+    say(f"        decode from conv inputs: whole relL2 o={rel(outs, refs):.3e} cache={rel(got, ref):.3e}")
+    say(f"        worst (row, head) o: relL2={worst_o[0]:.3e} at {worst_o[1]}; cache: {worst_c[0]:.3e} at {worst_c[1]}")
