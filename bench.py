@@ -598,7 +598,19 @@ def bench_split(steps, warmup, segments=10):
         kda.chunk_fwd_split(d["q"], d["k"], d["v"], d["g"], d["beta"], segments, initial_state=d["initial_state"],
                             out=o, final_state=fin, workspace=ws)
 
+    # the same from raw projections (gate, beta and normalisation prologue in every pass)
+    A_log, dt_bias = (t.to(dev) for t in synth.make_gate_params(H, D, 2))
+
+    def split_raw(i):
+        d = sets[i % 2]
+        kda.chunk_fwd_split_prologue(d["q"], d["k"], d["v"], d["g"], d["beta"], A_log, dt_bias, segments,
+                                     gate_lower_bound=synth.GATE_LOWER_BOUND, l2_eps=1e-6,
+                                     initial_state=d["initial_state"], out=o, final_state=fin, workspace=ws)
+
     _, _, plain_ms = time_launches(plain, steps, warmup, stream)
+    _, raw_per, raw_ms = time_launches(split_raw, steps, warmup, stream)
+    if not (torch.isfinite(o.float()).all() and torch.isfinite(fin).all()):
+        raise RuntimeError("non-finite split output from raw projections")
     wall, split_per, split_ms = time_launches(split, steps, warmup, stream)
     if not (torch.isfinite(o.float()).all() and torch.isfinite(fin).all()):
         raise RuntimeError("non-finite split output")
@@ -613,7 +625,10 @@ def bench_split(steps, warmup, segments=10):
                          "frac": gbs / HBM_PEAK_GBS, "traffic": read_leg_traffic("split")},
             "algorithmic_bytes_per_step": nbytes,
             "timed": "one kda_chunk_fwd_split call: the A and B passes over the segments (one launch), the "
-                     "entry-state scan, the correction of the outputs of segments after the first"}
+                     "entry-state scan, the correction of the outputs of segments after the first",
+            "from_raw_projections": {"steps": "kda_chunk_fwd_split_prologue on the same tensors read as raw "
+                                              "projections (q, k unnormalised, gate and beta logits)",
+                                     "ms_per_step": float(raw_ms), "ms_median": float(np.median(raw_per))}}
 
 
 def cpu_backward_baseline(heads=96):

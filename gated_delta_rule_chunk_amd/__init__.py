@@ -86,6 +86,9 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_split.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, ctypes.c_int,
                                         I32, P, ctypes.c_size_t, P, P, P]
     lib.kda_chunk_fwd_split.restype = ctypes.c_int
+    lib.kda_chunk_fwd_split_prologue.argtypes = [P, P, P, P, P, P, P, F, F, P, P, I32, I32, I32, I32, I32, I32, I32,
+                                                 F, ctypes.c_int, I32, P, ctypes.c_size_t, P, P, P]
+    lib.kda_chunk_fwd_split_prologue.restype = ctypes.c_int
     lib.kda_chunk_fwd_split_static.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F,
                                                ctypes.c_int, I32, P, P, P]
     lib.kda_chunk_fwd_split_static.restype = ctypes.c_int
@@ -293,6 +296,32 @@ def chunk_fwd_split(q, k, v, g, beta, segments, initial_state=None, cu_seqlens=N
 
 
 SPLIT_STATIC_SCRATCH_BYTES = 128 << 20   # KDA_SPLIT_STATIC_SCRATCH_BYTES
+
+
+def chunk_fwd_split_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, segments, gate_lower_bound=-5.0,
+                             l2_eps=1e-6, initial_state=None, cu_seqlens=None, chunk_size=0, scale=1.0,
+                             output_final_state=True, out=None, final_state=None, workspace=None):
+    """``chunk_fwd_split`` from raw projections (kda_chunk_fwd_split_prologue):
+    inputs as ``chunk_fwd_prologue``, ``segments`` and ``workspace`` as
+    ``chunk_fwd_split``. Returns (o, final_state or None)."""
+    lib = load_library()
+    B, T, H, Dk, Dv, N, dt, dev = _chunk_inputs(q_raw, k_raw, v, g_logit, beta_logit, initial_state, cu_seqlens,
+                                                ("q_raw", "k_raw", "v", "g_logit", "beta_logit"))
+    _need(A_log, "A_log", (Dk,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H * Dk,), torch.float32, dev)
+    out, final_state = _chunk_outputs(B, T, H, Dk, Dv, N, dt, dev, out, final_state, output_final_state)
+    need = chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, N, dt, segments)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    st = lib.kda_chunk_fwd_split_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(g_logit), _ptr(beta_logit),
+                                          _ptr(A_log), _ptr(dt_bias), float(gate_lower_bound), float(l2_eps),
+                                          _ptr(initial_state), _ptr(cu_seqlens), B, T, H, Dk, Dv, N, int(chunk_size),
+                                          float(scale), _DTYPES[dt], int(segments), _ptr(workspace),
+                                          workspace.numel(), _ptr(out), _ptr(final_state), _stream(dev))
+    _check(st)
+    return out, final_state
 
 
 def chunk_fwd_split_static(q, k, v, g, beta, segments, initial_state=None, cu_seqlens=None, chunk_size=0,

@@ -432,17 +432,15 @@ size_t kda_chunk_fwd_split_workspace_bytes(int32_t B, int32_t T, int32_t H, int3
     return (size_t)kda::split_layout(a, segments).bytes;
 }
 
-kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                               const float* initial_state, const int32_t* cu_seqlens, int32_t B, int32_t T,
-                               int32_t H, int32_t Dk, int32_t Dv, int32_t N, int32_t chunk_size, float scale,
-                               kda_dtype dtype, int32_t segments, void* workspace, size_t workspace_bytes, void* o,
-                               float* final_state, void* stream) {
-    g_last_error[0] = 0;
-    const char* fn = "kda_chunk_fwd_split";
-    kda::ChunkArgs a;
-    const kda_status st = check_chunk(fn, q, k, v, g, beta, initial_state, cu_seqlens, B, T, H, Dk, Dv, N,
-                                      chunk_size, scale, dtype, o, final_state, a);
-    if (st != KDA_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// The split's checks after the inputs', and its launch (shared by the plain
+// and the raw-projection entry points).
+kda_status run_split(const char* fn, kda::ChunkArgs& a, int32_t segments, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    const int32_t B = a.B, T = a.T, H = a.H, N = a.N;
     if (segments < 1 || segments > KDA_MAX_SEGMENTS)
         return fail(KDA_ERR_INVALID_ARG, "%s: segments must be in [1, %d], got %d", fn, KDA_MAX_SEGMENTS, segments);
     if ((int64_t)B * T > INT32_MAX || (int64_t)N * segments * H > ((int64_t)1 << 26))
@@ -450,13 +448,14 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
     if (segments == 1 || T == 0) return launch_chunk(fn, a, stream);
     const kda_status cs = check_kernel_chunk(fn, a);
     if (cs != KDA_OK) return cs;
-    const size_t need = kda_chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, N, dtype, segments);
+    const size_t need = kda_chunk_fwd_split_workspace_bytes(B, T, H, a.Dk, a.Dv, N, a.bf16 ? KDA_BF16 : KDA_F32,
+                                                            segments);
     if (workspace_bytes < need || !workspace)
         return fail(KDA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, got %zu%s", fn, need, workspace_bytes,
                     workspace ? "" : " (NULL)");
     {
         const char* ws = static_cast<const char*>(workspace);
-        const void* ptrs[] = {q, k, v, g, beta, o, initial_state, final_state};
+        const void* ptrs[] = {a.q, a.k, a.v, a.g, a.beta, a.o, a.s0, a.sT, a.A_log, a.dt_bias};
         for (const void* p : ptrs) {
             const char* c = static_cast<const char*>(p);
             if (c && c >= ws && c < ws + need)
@@ -468,6 +467,52 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
     const hipError_t e = kda::launch_chunk_fwd_split(a, segments, workspace, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                               const float* initial_state, const int32_t* cu_seqlens, int32_t B, int32_t T,
+                               int32_t H, int32_t Dk, int32_t Dv, int32_t N, int32_t chunk_size, float scale,
+                               kda_dtype dtype, int32_t segments, void* workspace, size_t workspace_bytes, void* o,
+                               float* final_state, void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_chunk_fwd_split";
+    kda::ChunkArgs a;
+    const kda_status st = check_chunk(fn, q, k, v, g, beta, initial_state, cu_seqlens, B, T, H, Dk, Dv, N,
+                                      chunk_size, scale, dtype, o, final_state, a);
+    if (st != KDA_OK) return st;
+    return run_split(fn, a, segments, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_split_prologue(const void* q_raw, const void* k_raw, const void* v, const void* g_logit,
+                                        const void* beta_logit, const float* A_log, const float* dt_bias,
+                                        float gate_lower_bound, float l2_eps, const float* initial_state,
+                                        const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H, int32_t Dk,
+                                        int32_t Dv, int32_t N, int32_t chunk_size, float scale, kda_dtype dtype,
+                                        int32_t segments, void* workspace, size_t workspace_bytes, void* o,
+                                        float* final_state, void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_chunk_fwd_split_prologue";
+    kda::ChunkArgs a;
+    const kda_status st = check_chunk(fn, q_raw, k_raw, v, g_logit, beta_logit, initial_state, cu_seqlens, B, T, H,
+                                      Dk, Dv, N, chunk_size, scale, dtype, o, final_state, a);
+    if (st != KDA_OK) return st;
+    if (T > 0 && (!A_log || !dt_bias))
+        return fail(KDA_ERR_INVALID_ARG, "%s: A_log and dt_bias must be non-NULL when T > 0", fn);
+    if (!(gate_lower_bound < 0.f) || !(gate_lower_bound > -1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: gate_lower_bound must be finite and negative (got %g)", fn,
+                    (double)gate_lower_bound);
+    if (!(l2_eps > 0.f) || !(l2_eps < 1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: l2_eps must be finite and positive (got %g)", fn, (double)l2_eps);
+    a.prologue = true;
+    a.A_log = A_log;
+    a.dt_bias = dt_bias;
+    a.gate_lb = gate_lower_bound;
+    a.l2_eps = l2_eps;
+    return run_split(fn, a, segments, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_chunk_fwd_split_static(const void* q, const void* k, const void* v, const void* g, const void* beta,

@@ -239,6 +239,26 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, cons
                                float* final_state, void* stream);
 
 /*
+ * kda_chunk_fwd_split from raw projections: the gate, beta and normalisation
+ * prologue of kda_chunk_fwd_prologue inside every pass of the split, for long
+ * sequences of a layer whose inputs are the projections (the K3 layer's
+ * parameters as cited at kda_chunk_fwd_prologue). q_raw, k_raw, v, g_logit,
+ * beta_logit, A_log, dt_bias, gate_lower_bound and l2_eps as for
+ * kda_chunk_fwd_prologue; segments, workspace (at least
+ * kda_chunk_fwd_split_workspace_bytes for the same sizes) and the rest as for
+ * kda_chunk_fwd_split. bf16 with Dk = Dv = 128 and gate_lower_bound >= -5 runs
+ * the matrix-core form, everything else the float32 passes. Errors as for
+ * both.
+ */
+kda_status kda_chunk_fwd_split_prologue(const void* q_raw, const void* k_raw, const void* v, const void* g_logit,
+                                        const void* beta_logit, const float* A_log, const float* dt_bias,
+                                        float gate_lower_bound, float l2_eps, const float* initial_state,
+                                        const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t H, int32_t Dk,
+                                        int32_t Dv, int32_t N, int32_t chunk_size, float scale, kda_dtype dtype,
+                                        int32_t segments, void* workspace, size_t workspace_bytes, void* o,
+                                        float* final_state, void* stream);
+
+/*
  * kda_chunk_fwd_split for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation. Identical to kda_chunk_fwd_split (same arguments minus the

@@ -23,6 +23,7 @@ def test_exports_every_declared_symbol(lib):
     names = kda.declared_symbols()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step", "kda_short_conv",
                           "kda_recurrent_step_prologue", "kda_recurrent_step_conv", "kda_chunk_bwd_conv",
+                          "kda_chunk_fwd_split_prologue",
                           "kda_chunk_bwd_conv_workspace_bytes",
                           "kda_short_conv_step", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
                           "kda_chunk_fwd_split", "kda_chunk_fwd_split_workspace_bytes",

@@ -148,3 +148,34 @@ def test_split_full_packed_varlen_every_head():
     ws = max(rel(fin[n], rfin[n]) for n in range(fin.shape[0]))
     say(f"        worst head o={wo:.3e} final={wf:.3e}; worst sequence final={ws:.3e}")
     assert np.isfinite(o).all() and wo <= TOL_BF16 and wf <= TOL_BF16 and ws <= TOL_BF16, (wo, wf, ws)
+
+
+# --- from raw projections (kda_chunk_fwd_split_prologue) -----------------------
+
+@pytest.mark.parametrize("dtype,Dk,Dv,segments,lengths", [
+    ("bf16", 128, 128, 4, None), ("bf16", 128, 128, 3, [300, 0, 1, 517]), ("f32", 64, 32, 3, None),
+    ("f32", 128, 128, 5, [200, 333])])
+def test_split_prologue_against_oracle(dtype, Dk, Dv, segments, lengths):
+    from tests.test_gpu_prologue import oracle_prologue
+    inp = synth.make_prologue_inputs(1 if lengths else 2, 0 if lengths else 400, 2, Dk, Dv, seed=630 + segments,
+                                     dtype=dtype, init_state=True, lengths=lengths)
+    say(f"[case] split from raw projections {dtype} Dk={Dk} Dv={Dv} segments={segments} lengths={lengths}")
+    d = to_dev(inp)
+    o, fin = kda.chunk_fwd_split_prologue(d["q_raw"], d["k_raw"], d["v"], d["g_logit"], d["beta_logit"], d["A_log"],
+                                          d["dt_bias"], segments, initial_state=d["initial_state"],
+                                          cu_seqlens=d["cu_seqlens"], scale=0.5)
+    o1, fin1 = kda.chunk_fwd_prologue(d["q_raw"], d["k_raw"], d["v"], d["g_logit"], d["beta_logit"], d["A_log"],
+                                      d["dt_bias"], initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
+                                      scale=0.5)
+    torch.cuda.synchronize()
+    ro, rfin = oracle_prologue(inp, scale=0.5)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    eo, ef = rel(o.float().cpu().numpy(), ro), rel(fin.cpu().numpy(), rfin)
+    say(f"        relL2 o={eo:.3e} final={ef:.3e} (unsplit: o={rel(o1.float().cpu().numpy(), ro):.3e})")
+    assert eo <= tol and ef <= tol, (eo, ef)
+    # one segment is the plain prologue forward
+    o2, fin2 = kda.chunk_fwd_split_prologue(d["q_raw"], d["k_raw"], d["v"], d["g_logit"], d["beta_logit"],
+                                            d["A_log"], d["dt_bias"], 1, initial_state=d["initial_state"],
+                                            cu_seqlens=d["cu_seqlens"], scale=0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o1) and torch.equal(fin2, fin1)
