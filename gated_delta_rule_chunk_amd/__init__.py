@@ -58,6 +58,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_prologue.argtypes = [P, P, P, P, P, P, P, F, F, P, P, I32, I32, I32, I32, I32, I32,
                                            I32, F, ctypes.c_int, P, P, P]
     lib.kda_chunk_fwd_prologue.restype = ctypes.c_int
+    lib.kda_prologue.argtypes = [P, P, P, P, P, P, F, F, I32, I32, I32, I32, ctypes.c_int, P, P, P, P, P]
+    lib.kda_prologue.restype = ctypes.c_int
     lib.kda_recurrent_step.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F,
                                        ctypes.c_int, P, P]
     lib.kda_recurrent_step.restype = ctypes.c_int
@@ -512,6 +514,37 @@ def chunk_fwd_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, gat
                                     _stream(dev))
     _check(st)
     return out, final_state
+
+
+def prologue(q_raw, k_raw, g_logit, beta_logit, A_log, dt_bias, gate_lower_bound=-5.0, l2_eps=1e-6, out=None):
+    """The gate, beta and normalisation prologue alone (kda_prologue): q_raw,
+    k_raw, g_logit [B,T,H,Dk] and beta_logit [B,T,H] (one dtype); A_log [Dk],
+    dt_bias [H*Dk] float32. Returns (q, k, g, beta) in the input dtype; ``out``
+    may give the four output tensors (each may be its own input)."""
+    lib = load_library()
+    if q_raw.dim() != 4:
+        raise ValueError("q_raw must be [B,T,H,Dk]")
+    B, T, H, Dk = q_raw.shape
+    dev, dt = q_raw.device, q_raw.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    for t, n, shp in ((q_raw, "q_raw", (B, T, H, Dk)), (k_raw, "k_raw", (B, T, H, Dk)),
+                      (g_logit, "g_logit", (B, T, H, Dk)), (beta_logit, "beta_logit", (B, T, H))):
+        _need(t, n, shp, dt, dev)
+    _need(A_log, "A_log", (Dk,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H * Dk,), torch.float32, dev)
+    if out is None:
+        out = (torch.empty_like(q_raw), torch.empty_like(k_raw), torch.empty_like(g_logit),
+               torch.empty_like(beta_logit))
+    for t, n, shp in zip(out, ("q", "k", "g", "beta"), ((B, T, H, Dk),) * 3 + ((B, T, H),)):
+        _need(t, n, shp, dt, dev)
+    st = lib.kda_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(g_logit), _ptr(beta_logit), _ptr(A_log), _ptr(dt_bias),
+                          float(gate_lower_bound), float(l2_eps), B, T, H, Dk, _DTYPES[dt], *(_ptr(t) for t in out),
+                          _stream(dev))
+    _check(st)
+    return tuple(out)
 
 
 def short_conv(x, weight, conv_state=None, cu_seqlens=None, activation=True, output_final_state=True,

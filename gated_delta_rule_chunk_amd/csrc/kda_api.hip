@@ -854,6 +854,54 @@ kda_status kda_chunk_bwd_conv(const void* xq, const void* xk, const void* xv, co
     return KDA_OK;
 }
 
+kda_status kda_prologue(const void* q_raw, const void* k_raw, const void* g_logit, const void* beta_logit,
+                        const float* A_log, const float* dt_bias, float gate_lower_bound, float l2_eps, int32_t B,
+                        int32_t T, int32_t H, int32_t Dk, kda_dtype dtype, void* q, void* k, void* g, void* beta,
+                        void* stream) {
+    g_last_error[0] = 0;
+    const char* fn = "kda_prologue";
+    if (B < 1 || T < 0 || H < 1)
+        return fail(KDA_ERR_INVALID_ARG, "%s: need B >= 1, T >= 0, H >= 1 (got B=%d T=%d H=%d)", fn, B, T, H);
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dtype %d is not KDA_F32 or KDA_BF16", fn, (int)dtype);
+    if (!dim_ok(Dk)) return fail(KDA_ERR_UNSUPPORTED, "%s: Dk=%d; supported head dims are 16, 32, 64, 128", fn, Dk);
+    if ((int64_t)B * T * H > ((int64_t)1 << 40)) return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", fn);
+    if (T > 0 && (!q_raw || !k_raw || !g_logit || !beta_logit || !q || !k || !g || !beta || !A_log || !dt_bias))
+        return fail(KDA_ERR_INVALID_ARG, "%s: every input and output must be non-NULL when T > 0", fn);
+    if (!(gate_lower_bound < 0.f) || !(gate_lower_bound > -1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: gate_lower_bound must be finite and negative (got %g)", fn,
+                    (double)gate_lower_bound);
+    if (!(l2_eps > 0.f) || !(l2_eps < 1e30f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: l2_eps must be finite and positive (got %g)", fn, (double)l2_eps);
+    if (T == 0) return KDA_OK;
+    {
+        // an output may be its own input (in place), and nothing else
+        const void* ins[] = {q_raw, k_raw, g_logit, beta_logit};
+        void* outs[] = {q, k, g, beta};
+        for (int j = 0; j < 4; ++j) {
+            for (int i = 0; i < 4; ++i)
+                if (i != j && outs[j] == ins[i])
+                    return fail(KDA_ERR_INVALID_ARG, "%s: an output may alias only its own input", fn);
+            for (int i = 0; i < 4; ++i)
+                if (i != j && outs[j] == outs[i])
+                    return fail(KDA_ERR_INVALID_ARG, "%s: the outputs must be distinct", fn);
+            if (outs[j] == A_log || outs[j] == dt_bias)
+                return fail(KDA_ERR_INVALID_ARG, "%s: an output may alias only its own input", fn);
+        }
+    }
+    kda::PrologueBwdArgs p{};
+    p.q_raw = q_raw; p.k_raw = k_raw; p.g_logit = g_logit; p.beta_logit = beta_logit;
+    p.A_log = A_log; p.dt_bias = dt_bias; p.gate_lb = gate_lower_bound; p.l2_eps = l2_eps;
+    // the apply pass writes its outputs in the input dtype here
+    p.qf = static_cast<float*>(q); p.kf = static_cast<float*>(k); p.gf = static_cast<float*>(g);
+    p.bf = static_cast<float*>(beta);
+    p.widen_x = false;
+    p.B = B; p.T = T; p.H = H; p.Dk = Dk; p.Dv = Dk; p.bf16 = dtype == KDA_BF16;
+    const hipError_t e = kda::launch_prologue(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
+}
+
 kda_status kda_short_conv(const void* x, const float* weight, const float* conv_state_in,
                           const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t C, int32_t N,
                           int32_t activation, kda_dtype dtype, void* y, float* conv_state_out, void* stream) {

@@ -183,6 +183,10 @@ struct PrologueBwdLayout {
 PrologueBwdLayout prologue_bwd_layout(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
                                       bool packed);
 hipError_t launch_prologue_bwd(const PrologueBwdArgs& p, const BwdArgs& core, hipStream_t s);
+// The prologue alone (kda_prologue): q_raw, k_raw, g_logit, beta_logit, A_log,
+// dt_bias, gate_lb, l2_eps, B, T, H, Dk and bf16 set, and qf, kf, gf, bf
+// pointing at outputs in the input dtype (widen_x false).
+hipError_t launch_prologue(const PrologueBwdArgs& p, hipStream_t s);
 
 // Workspace of the intra-sequence split (byte offsets, 256-aligned).
 struct SplitLayout {

@@ -14,6 +14,8 @@
 //      dz e^{A_log} (for dt_bias) and dz z (for A_log);
 //   4. prologue_reduce_bias_kernel, prologue_reduce_alog_kernel: those partials
 //      summed in a fixed order.
+// Step 1 alone, with outputs in the input dtype, is the standalone prologue
+// (kda_prologue).
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -38,6 +40,10 @@ __device__ __forceinline__ void store8(float* p, int64_t i, const float* v) {
     *reinterpret_cast<float4*>(p + i) = float4{v[0], v[1], v[2], v[3]};
     *reinterpret_cast<float4*>(p + i + 4) = float4{v[4], v[5], v[6], v[7]};
 }
+__device__ __forceinline__ void store8(__bf16* p, int64_t i, const float* v) {
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p) + i) =
+        uint4{pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]), pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7])};
+}
 
 // Sum over the L lanes (a power of two, at most 16) that share a row: every
 // lane of the group gets the total.
@@ -52,8 +58,10 @@ __device__ __forceinline__ float sigmoid(float z) { return 1.f / (1.f + __expf(-
 
 // One workgroup per (block of kTokBlock tokens, head). L = DK/8 lanes hold
 // one (token, head) row, eight channels each, and 256/L rows go at once; row
-// sums are shuffles within the L lanes.
-template <typename Tin, int DK>
+// sums are shuffles within the L lanes. q, k, g and beta are written as Tout
+// (float32 for the backward, the input dtype for kda_prologue); each lane
+// writes only the elements it has read, so an output may be its own input.
+template <typename Tin, typename Tout, int DK>
 __global__ __launch_bounds__(kPThreads) void prologue_apply_kernel(PrologueBwdArgs a) {
     constexpr int L = DK / 8, RPI = kPThreads / L;
     const int tid = threadIdx.x, part = tid % L, rg = tid / L, c0 = 8 * part;
@@ -88,15 +96,18 @@ __global__ __launch_bounds__(kPThreads) void prologue_apply_kernel(PrologueBwdAr
             k[u] *= rk;
             g[u] = a.gate_lb * sigmoid(eA[u] * (g[u] + bias[u]));
         }
-        store8(a.qf, e, q);
-        store8(a.kf, e, k);
-        store8(a.gf, e, g);
-        if (part == 0) a.bf[row] = sigmoid(load_elem(static_cast<const Tin*>(a.beta_logit), row));
+        store8(reinterpret_cast<Tout*>(a.qf), e, q);
+        store8(reinterpret_cast<Tout*>(a.kf), e, k);
+        store8(reinterpret_cast<Tout*>(a.gf), e, g);
+        if (part == 0)
+            store_elem(reinterpret_cast<Tout*>(a.bf), row,
+                       sigmoid(load_elem(static_cast<const Tin*>(a.beta_logit), row)));
     }
     // v and dO widened to float32 (for the vector-ALU backward): Dv/8 lanes per row
+    if (!a.widen_x) return;
     const int LV = a.Dv / 8, RV = kPThreads / LV;
     const int pv = tid % LV, rv = tid / LV;
-    if (a.widen_x && rv < RV) {
+    if (rv < RV) {
         for (int64_t t = t0 + rv; t < t_end; t += RV) {
             const int64_t e = (t * a.H + h) * a.Dv + 8 * pv;
             float x[8];
@@ -213,25 +224,31 @@ __global__ __launch_bounds__(256) void prologue_reduce_alog_kernel(PrologueBwdAr
     if (threadIdx.x == 0) a.d_A_log[c] = red[0];
 }
 
+// grad: the chain-rule pass; otherwise the apply pass, with outputs in float32
+// or (same) in the input dtype
 template <typename Tin>
-hipError_t launch_apply(const PrologueBwdArgs& a, dim3 grid, hipStream_t s, bool grad) {
+hipError_t launch_apply(const PrologueBwdArgs& a, dim3 grid, hipStream_t s, bool grad, bool same = false) {
     const dim3 block(kPThreads);
     switch (a.Dk) {
         case 16:
             if (grad) prologue_grad_kernel<Tin, 16><<<grid, block, 0, s>>>(a);
-            else prologue_apply_kernel<Tin, 16><<<grid, block, 0, s>>>(a);
+            else if (same) prologue_apply_kernel<Tin, Tin, 16><<<grid, block, 0, s>>>(a);
+            else prologue_apply_kernel<Tin, float, 16><<<grid, block, 0, s>>>(a);
             break;
         case 32:
             if (grad) prologue_grad_kernel<Tin, 32><<<grid, block, 0, s>>>(a);
-            else prologue_apply_kernel<Tin, 32><<<grid, block, 0, s>>>(a);
+            else if (same) prologue_apply_kernel<Tin, Tin, 32><<<grid, block, 0, s>>>(a);
+            else prologue_apply_kernel<Tin, float, 32><<<grid, block, 0, s>>>(a);
             break;
         case 64:
             if (grad) prologue_grad_kernel<Tin, 64><<<grid, block, 0, s>>>(a);
-            else prologue_apply_kernel<Tin, 64><<<grid, block, 0, s>>>(a);
+            else if (same) prologue_apply_kernel<Tin, Tin, 64><<<grid, block, 0, s>>>(a);
+            else prologue_apply_kernel<Tin, float, 64><<<grid, block, 0, s>>>(a);
             break;
         default:
             if (grad) prologue_grad_kernel<Tin, 128><<<grid, block, 0, s>>>(a);
-            else prologue_apply_kernel<Tin, 128><<<grid, block, 0, s>>>(a);
+            else if (same) prologue_apply_kernel<Tin, Tin, 128><<<grid, block, 0, s>>>(a);
+            else prologue_apply_kernel<Tin, float, 128><<<grid, block, 0, s>>>(a);
             break;
     }
     return hipGetLastError();
@@ -262,6 +279,13 @@ hipError_t launch_prologue_bwd(const PrologueBwdArgs& p, const BwdArgs& core, hi
     if ((e = hipGetLastError()) != hipSuccess) return e;
     prologue_reduce_alog_kernel<<<dim3((unsigned)p.Dk), dim3(256), 0, s>>>(p, (int)nblk, p.Dk);
     return hipGetLastError();
+}
+
+hipError_t launch_prologue(const PrologueBwdArgs& p, hipStream_t s) {
+    const int64_t nblk = prologue_bwd_token_blocks(p.B, p.T);
+    if (nblk == 0) return hipSuccess;
+    const dim3 grid((unsigned)nblk, (unsigned)p.H);
+    return p.bf16 ? launch_apply<__bf16>(p, grid, s, false, true) : launch_apply<float>(p, grid, s, false, true);
 }
 
 PrologueBwdLayout prologue_bwd_layout(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,

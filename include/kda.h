@@ -136,6 +136,33 @@ kda_status kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const vo
                                   float* final_state, void* stream);
 
 /*
+ * The gate, beta and normalisation prologue of kda_chunk_fwd_prologue on its
+ * own: per token and head,
+ *   q = q_raw / sqrt(|q_raw|^2 + l2_eps), k likewise,
+ *   g = gate_lower_bound * sigmoid(exp(A_log) * (g_logit + dt_bias)),
+ *   beta = sigmoid(beta_logit),
+ * written in dtype (the parameters and their shapes as cited at
+ * kda_chunk_fwd_prologue). It prepares inputs for the calls that take them
+ * ready (kda_chunk_fwd, kda_chunk_fwd_split, kda_recurrent_step), for
+ * callers that keep them or feed them elsewhere; the fused calls compute the
+ * same values inside their kernels (in float32, without rounding them to
+ * dtype in between).
+ *
+ *   q_raw, k_raw, g_logit [B,T,H,Dk], beta_logit [B,T,H]  dtype
+ *   A_log [Dk], dt_bias [H*Dk] float32; gate_lower_bound finite and < 0;
+ *   l2_eps finite and > 0
+ *   q, k, g [B,T,H,Dk], beta [B,T,H]  dtype outputs; each may be its own
+ *   input (in place, e.g. q == q_raw) and must not alias anything else
+ * T = 0 is a no-op. Errors: KDA_ERR_INVALID_ARG for NULL pointers, bad sizes,
+ * bound, eps or aliasing; KDA_ERR_UNSUPPORTED for dims outside
+ * {16, 32, 64, 128} or another dtype.
+ */
+kda_status kda_prologue(const void* q_raw, const void* k_raw, const void* g_logit, const void* beta_logit,
+                        const float* A_log, const float* dt_bias, float gate_lower_bound, float l2_eps, int32_t B,
+                        int32_t T, int32_t H, int32_t Dk, kda_dtype dtype, void* q, void* k, void* g, void* beta,
+                        void* stream);
+
+/*
  * Bytes of device workspace kda_chunk_fwd_conv needs (0 for T = 0 or
  * out-of-range sizes): for bf16 with Dk = Dv = 128 and gate_lower_bound >= -5
  * (v convolved in the chunk kernel) the convolved q and k, 2 x B*T*H*Dk bf16; otherwise the

@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol(lib):
     names = kda.declared_symbols()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_prologue", "kda_recurrent_step", "kda_short_conv",
                           "kda_recurrent_step_prologue", "kda_recurrent_step_conv", "kda_chunk_bwd_conv",
-                          "kda_chunk_fwd_split_prologue",
+                          "kda_chunk_fwd_split_prologue", "kda_prologue",
                           "kda_chunk_bwd_conv_workspace_bytes",
                           "kda_short_conv_step", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
                           "kda_chunk_fwd_split", "kda_chunk_fwd_split_workspace_bytes",
@@ -561,3 +561,37 @@ def test_autograd_entry_points_import_without_a_gpu():
     from gated_delta_rule_chunk_amd import autograd as kag
     for name in ("chunk_kda", "chunk_kda_prologue", "chunk_kda_conv"):
         assert callable(getattr(kag, name))
+
+
+
+def _prologue(lib, **kw):
+    P = ctypes.c_void_p
+    a = dict(q=FAKE, k=FAKE, g=FAKE, beta=FAKE, A_log=P(0x3000), dt_bias=P(0x4000), lb=-5.0, eps=1e-6, B=1, T=8,
+             H=2, Dk=128, dtype=kda.KDA_BF16, qo=P(0x5000), ko=P(0x6000), go=P(0x7000), bo=P(0x8000), stream=None)
+    a["q"], a["k"], a["g"], a["beta"] = P(0x1000), P(0x1100), P(0x1200), P(0x1300)
+    a.update(kw)
+    return lib.kda_prologue(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(A_log=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(ko=None), kda.KDA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(lb=0.5), kda.KDA_ERR_INVALID_ARG, "gate_lower_bound"),
+    (dict(eps=0.0), kda.KDA_ERR_INVALID_ARG, "l2_eps"),
+    (dict(Dk=48), kda.KDA_ERR_UNSUPPORTED, "head dims"),
+    (dict(dtype=3), kda.KDA_ERR_UNSUPPORTED, "dtype"),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARG, "H >= 1"),
+    (dict(ko=ctypes.c_void_p(0x1000)), kda.KDA_ERR_INVALID_ARG, "its own input"),
+    (dict(go=ctypes.c_void_p(0x5000)), kda.KDA_ERR_INVALID_ARG, "distinct"),
+    (dict(bo=ctypes.c_void_p(0x3000)), kda.KDA_ERR_INVALID_ARG, "its own input"),
+])
+def test_prologue_rejects_before_launch(lib, kw, status, needle):
+    assert _prologue(lib, **kw) == status
+    msg = lib.kda_last_error_message().decode()
+    assert needle in msg and msg.startswith("kda_prologue")
+
+
+def test_prologue_in_place_and_empty_are_accepted_without_launch(lib):
+    # T = 0: nothing to launch, so no GPU is needed even for an in-place call
+    P = ctypes.c_void_p
+    assert _prologue(lib, T=0, qo=P(0x1000), ko=P(0x1100), go=P(0x1200), bo=P(0x1300)) == kda.KDA_OK

@@ -121,3 +121,44 @@ def test_full_size_k3_t4096_sampled_heads():
     say(f"        heads {heads}: relL2 o={eo:.3e} final={ef:.3e}")
     assert np.isfinite(o).all() and np.isfinite(fin).all()
     assert eo <= TOL_BF16 and ef <= TOL_BF16, (eo, ef)
+
+
+# --- the prologue on its own (kda_prologue) ------------------------------------
+
+@pytest.mark.parametrize("dtype,Dk", [("bf16", 128), ("f32", 128), ("f32", 32), ("bf16", 16)])
+def test_standalone_prologue_against_oracle(dtype, Dk):
+    inp = synth.make_prologue_inputs(2, 70, 3, Dk, Dk, seed=560 + Dk, dtype=dtype)
+    say(f"[case] kda_prologue {dtype} Dk={Dk}")
+    d = to_dev(inp)
+    q, k, g, b = kda.prologue(d["q_raw"], d["k_raw"], d["g_logit"], d["beta_logit"], d["A_log"], d["dt_bias"],
+                              gate_lower_bound=LB, l2_eps=EPS)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().numpy()  # noqa: E731
+    ref = kda_ref.prologue(f(inp["q_raw"]), f(inp["k_raw"]), f(inp["g_logit"]), f(inp["beta_logit"]),
+                           f(inp["A_log"]), f(inp["dt_bias"]), LB, EPS)
+    # float32: rounding only; bf16: one rounding of each output to bf16 (2^-8 relative at most)
+    tol = 4e-3 if dtype == "bf16" else 1e-6
+    for name, got, r in zip("qkgb", (q, k, g, b), ref):
+        e = rel(got.float().cpu().numpy(), r)
+        say(f"        {name}: relL2 {e:.2e}")
+        assert e <= tol, (name, e)
+    # in place: each output over its own input gives the same values
+    q2, k2, g2, b2 = (t.clone() for t in (d["q_raw"], d["k_raw"], d["g_logit"], d["beta_logit"]))
+    kda.prologue(q2, k2, g2, b2, d["A_log"], d["dt_bias"], gate_lower_bound=LB, l2_eps=EPS, out=(q2, k2, g2, b2))
+    torch.cuda.synchronize()
+    for a_, b_ in ((q2, q), (k2, k), (g2, g), (b2, b)):
+        assert torch.equal(a_, b_)
+
+
+def test_standalone_prologue_then_chunk_forward_matches_the_fused_call():
+    """float32: kda_prologue then kda_chunk_fwd against kda_chunk_fwd_prologue
+    (the same function; the gate's rounding differs between the two kernels)."""
+    inp = synth.make_prologue_inputs(1, 150, 2, 64, 64, seed=570, dtype="f32", init_state=True)
+    d = to_dev(inp)
+    q, k, g, b = kda.prologue(d["q_raw"], d["k_raw"], d["g_logit"], d["beta_logit"], d["A_log"], d["dt_bias"],
+                              gate_lower_bound=LB, l2_eps=EPS)
+    o1, f1 = kda.chunk_fwd(q, k, d["v"], g, b, initial_state=d["initial_state"])
+    o2, f2 = gpu_prologue(inp)
+    eo, ef = rel(o1.cpu().numpy(), o2), rel(f1.cpu().numpy(), f2)
+    say(f"[case] kda_prologue -> kda_chunk_fwd vs fused: relL2 o={eo:.2e} final={ef:.2e}")
+    assert eo <= 1e-5 and ef <= 1e-5
