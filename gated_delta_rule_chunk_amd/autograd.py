@@ -5,13 +5,17 @@ Each pairs one of the library's forward calls with its backward call:
 (kda_chunk_fwd_prologue / kda_chunk_bwd_prologue) and ``chunk_kda_conv``
 (kda_chunk_fwd_conv / kda_chunk_bwd_conv). The name follows the compute path
 the ISEEKYAN/k3 README names for the KDA layer (its compute-path paragraph);
-the arguments are this library's. Every step runs in the library's kernels:
-this module saves the inputs, routes the incoming gradients to the backward
-call and casts the float32 gradients to each input's dtype.
+the arguments are this library's. With ``segments`` > 1 the forward runs the
+intra-sequence split (kda_chunk_fwd_split, _split_prologue), which computes the
+same function, so its gradient is the same backward call's. Every step runs in
+the library's kernels: this module saves the inputs, routes the incoming
+gradients to the backward call and casts the float32 gradients to each input's
+dtype.
 """
 import torch
 
-from . import chunk_bwd, chunk_bwd_conv, chunk_bwd_prologue, chunk_fwd, chunk_fwd_conv, chunk_fwd_prologue
+from . import (chunk_bwd, chunk_bwd_conv, chunk_bwd_prologue, chunk_fwd, chunk_fwd_conv, chunk_fwd_prologue,
+               chunk_fwd_split, chunk_fwd_split_prologue)
 
 
 def _contig(t):
@@ -24,9 +28,13 @@ def _cast(grad, like):
 
 class _Chunk(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, initial_state, cu_seqlens, scale, chunk_size):
-        o, fin = chunk_fwd(q, k, v, g, beta, initial_state=initial_state, cu_seqlens=cu_seqlens,
-                           chunk_size=chunk_size, scale=scale)
+    def forward(ctx, q, k, v, g, beta, initial_state, cu_seqlens, scale, chunk_size, segments):
+        if segments > 1:
+            o, fin = chunk_fwd_split(q, k, v, g, beta, segments, initial_state=initial_state, cu_seqlens=cu_seqlens,
+                                     chunk_size=chunk_size, scale=scale)
+        else:
+            o, fin = chunk_fwd(q, k, v, g, beta, initial_state=initial_state, cu_seqlens=cu_seqlens,
+                               chunk_size=chunk_size, scale=scale)
         ctx.save_for_backward(q, k, v, g, beta, initial_state, cu_seqlens)
         ctx.scale = scale
         return o, fin
@@ -37,16 +45,21 @@ class _Chunk(torch.autograd.Function):
         dq, dk, dv, dg, db, d0 = chunk_bwd(q, k, v, g, beta, _contig(d_o), initial_state=s0,
                                            d_final_state=_contig(d_fin), cu_seqlens=cu, scale=ctx.scale,
                                            want_d_initial=s0 is not None)
-        return (_cast(dq, q), _cast(dk, k), _cast(dv, v), _cast(dg, g), _cast(db, beta), d0, None, None, None)
+        return (_cast(dq, q), _cast(dk, k), _cast(dv, v), _cast(dg, g), _cast(db, beta), d0, None, None, None, None)
 
 
 class _ChunkPrologue(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, initial_state, cu_seqlens, scale, lb,
-                eps, chunk_size):
-        o, fin = chunk_fwd_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, gate_lower_bound=lb,
-                                    l2_eps=eps, initial_state=initial_state, cu_seqlens=cu_seqlens,
-                                    chunk_size=chunk_size, scale=scale)
+                eps, chunk_size, segments):
+        if segments > 1:
+            o, fin = chunk_fwd_split_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, segments,
+                                              gate_lower_bound=lb, l2_eps=eps, initial_state=initial_state,
+                                              cu_seqlens=cu_seqlens, chunk_size=chunk_size, scale=scale)
+        else:
+            o, fin = chunk_fwd_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, gate_lower_bound=lb,
+                                        l2_eps=eps, initial_state=initial_state, cu_seqlens=cu_seqlens,
+                                        chunk_size=chunk_size, scale=scale)
         ctx.save_for_backward(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, initial_state, cu_seqlens)
         ctx.args = (scale, lb, eps)
         return o, fin
@@ -59,7 +72,7 @@ class _ChunkPrologue(torch.autograd.Function):
             q, k, v, gl, bl, A_log, dt_bias, _contig(d_o), gate_lower_bound=lb, l2_eps=eps, initial_state=s0,
             d_final_state=_contig(d_fin), cu_seqlens=cu, scale=scale, want_d_initial=s0 is not None)
         return (_cast(dq, q), _cast(dk, k), _cast(dv, v), _cast(dg, gl), _cast(db, bl), dA, dbias, d0,
-                None, None, None, None, None)
+                None, None, None, None, None, None)
 
 
 class _ChunkConv(torch.autograd.Function):
@@ -89,19 +102,20 @@ class _ChunkConv(torch.autograd.Function):
                 gr["conv_state_v"] if cs_v is not None else None, None, None, None, None, None, None)
 
 
-def chunk_kda(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0, chunk_size=0):
-    """Differentiable ``chunk_fwd``: returns (o, final_state). Gradients reach
-    q, k, v, g, beta and initial_state (kda_chunk_bwd)."""
-    return _Chunk.apply(q, k, v, g, beta, initial_state, cu_seqlens, float(scale), int(chunk_size))
+def chunk_kda(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0, chunk_size=0, segments=1):
+    """Differentiable ``chunk_fwd`` (``chunk_fwd_split`` with ``segments`` >
+    1): returns (o, final_state). Gradients reach q, k, v, g, beta and
+    initial_state (kda_chunk_bwd)."""
+    return _Chunk.apply(q, k, v, g, beta, initial_state, cu_seqlens, float(scale), int(chunk_size), int(segments))
 
 
 def chunk_kda_prologue(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, initial_state=None, cu_seqlens=None,
-                       scale=1.0, gate_lower_bound=-5.0, l2_eps=1e-6, chunk_size=0):
-    """Differentiable ``chunk_fwd_prologue``: returns (o, final_state).
-    Gradients reach the raw projections, v, A_log, dt_bias and initial_state
-    (kda_chunk_bwd_prologue)."""
+                       scale=1.0, gate_lower_bound=-5.0, l2_eps=1e-6, chunk_size=0, segments=1):
+    """Differentiable ``chunk_fwd_prologue`` (``chunk_fwd_split_prologue``
+    with ``segments`` > 1): returns (o, final_state). Gradients reach the raw
+    projections, v, A_log, dt_bias and initial_state (kda_chunk_bwd_prologue)."""
     return _ChunkPrologue.apply(q_raw, k_raw, v, g_logit, beta_logit, A_log, dt_bias, initial_state, cu_seqlens,
-                                float(scale), float(gate_lower_bound), float(l2_eps), int(chunk_size))
+                                float(scale), float(gate_lower_bound), float(l2_eps), int(chunk_size), int(segments))
 
 
 def chunk_kda_conv(xq, xk, xv, wq, wk, wv, g_logit, beta_logit, A_log, dt_bias, conv_states=None, initial_state=None,

@@ -91,3 +91,33 @@ def test_chunk_kda_conv_gradients_equal_the_backward_call():
              (x["dt_bias"], "dt_bias"), (x["initial_state"], "initial_state")]
     for t, n in pairs:
         assert torch.equal(t.grad, ref[n].to(t.dtype)), n
+
+
+@pytest.mark.parametrize("raw", [False, True])
+def test_split_forward_takes_the_same_backward(raw):
+    """chunk_kda / chunk_kda_prologue with segments > 1: the split's outputs are
+    the unsplit call's within the bf16 bar, and the gradients, which come from
+    the saved inputs, equal the unsplit call's bit for bit."""
+    from tests.gpu_helpers import TOL_BF16, rel
+    say(f"[case] autograd with the split forward, raw={raw}")
+    if raw:
+        inp = synth.make_prologue_inputs(1, 600, 2, 128, 128, seed=1530, dtype="bf16", init_state=True)
+        names = ("q_raw", "k_raw", "v", "g_logit", "beta_logit", "A_log", "dt_bias", "initial_state")
+        fn = lambda x, P: kag.chunk_kda_prologue(*(x[n] for n in names[:7]), initial_state=x["initial_state"],  # noqa
+                                                 segments=P)
+    else:
+        inp = synth.make_chunk_inputs(1, 600, 2, 128, 128, seed=1531, dtype="bf16", init_state=True)
+        names = ("q", "k", "v", "g", "beta", "initial_state")
+        fn = lambda x, P: kag.chunk_kda(*(x[n] for n in names[:5]), initial_state=x["initial_state"], segments=P)  # noqa
+    grads, outs = [], []
+    for P in (1, 4):
+        x = {n: _leaf(inp[n]) for n in names}
+        o, fin = fn(x, P)
+        Wo, Wf = _weights(o.shape, 1532, o.dtype), _weights(fin.shape, 1533)
+        ((o * Wo).float().sum() + (fin * Wf).sum()).backward()
+        outs.append((o.detach().float().cpu().numpy(), fin.detach().cpu().numpy()))
+        grads.append({n: x[n].grad for n in names})
+    torch.cuda.synchronize()
+    assert rel(outs[1][0], outs[0][0]) <= TOL_BF16 and rel(outs[1][1], outs[0][1]) <= TOL_BF16
+    for n in names:
+        assert torch.equal(grads[0][n], grads[1][n]), n
