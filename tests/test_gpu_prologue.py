@@ -110,17 +110,19 @@ def test_other_gate_bounds(lb):
     _check(inp, TOL_BF16, lb=lb, label=f"bf16 d128 lb={lb}")
 
 
-def test_full_size_k3_t4096_sampled_heads():
+def test_full_size_k3_t4096_every_head():
     w = synth.WORKLOADS["k3_t4096"]
     inp = synth.make_prologue_inputs(w.B, w.T, w.H, w.Dk, w.Dv, seed=w.seed, dtype="bf16")
-    say(f"[case] prologue full size k3_t4096")
+    say(f"[case] prologue full size k3_t4096, every head")
     o, fin = gpu_prologue(inp)
-    heads = [0, 41, 95]
-    ro, rf = oracle_prologue(inp, heads=heads)
-    eo, ef = rel(o[:, :, heads], ro), rel(fin[:, heads], rf)
-    say(f"        heads {heads}: relL2 o={eo:.3e} final={ef:.3e}")
+    ro, rf = oracle_prologue(inp)
     assert np.isfinite(o).all() and np.isfinite(fin).all()
-    assert eo <= TOL_BF16 and ef <= TOL_BF16, (eo, ef)
+    worst = (0.0, None)
+    for h in range(w.H):
+        eo, ef = rel(o[:, :, h], ro[:, :, h]), rel(fin[:, h], rf[:, h])
+        assert eo <= TOL_BF16 and ef <= TOL_BF16, (h, eo, ef)
+        worst = max(worst, (max(eo, ef), h), key=lambda t: t[0])
+    say(f"        whole relL2 o={rel(o, ro):.3e} final={rel(fin, rf):.3e}; worst head {worst[1]} at {worst[0]:.3e}")
 
 
 # --- the prologue on its own (kda_prologue) ------------------------------------
