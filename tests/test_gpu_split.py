@@ -179,3 +179,19 @@ def test_split_prologue_against_oracle(dtype, Dk, Dv, segments, lengths):
                                             cu_seqlens=d["cu_seqlens"], scale=0.5)
     torch.cuda.synchronize()
     assert torch.equal(o2, o1) and torch.equal(fin2, fin1)
+
+
+def test_split_prologue_gate_bound_below_five_runs_the_float32_passes():
+    """bf16, d = 128 with gate_lower_bound = -8: the gate can fall below -5, so
+    the split runs its float32 passes (chunk_generic with the prologue)."""
+    from tests.test_gpu_prologue import oracle_prologue
+    inp = synth.make_prologue_inputs(1, 300, 2, 128, 128, seed=640, dtype="bf16", init_state=True)
+    say("[case] split from raw projections, bf16 d=128, gate bound -8")
+    d = to_dev(inp)
+    o, fin = kda.chunk_fwd_split_prologue(d["q_raw"], d["k_raw"], d["v"], d["g_logit"], d["beta_logit"], d["A_log"],
+                                          d["dt_bias"], 3, gate_lower_bound=-8.0, initial_state=d["initial_state"])
+    torch.cuda.synchronize()
+    ro, rfin = oracle_prologue(inp, lb=-8.0)
+    eo, ef = rel(o.float().cpu().numpy(), ro), rel(fin.cpu().numpy(), rfin)
+    say(f"        relL2 o={eo:.3e} final={ef:.3e}")
+    assert eo <= TOL_BF16 and ef <= TOL_BF16, (eo, ef)
