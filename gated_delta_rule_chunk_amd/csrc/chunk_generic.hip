@@ -2,8 +2,8 @@
 // every supported (dtype, Dk, Dv, chunk) combination that the bf16
 // matrix-core kernel does not cover.
 //
-// One workgroup owns one (sequence, head, 16-column slice of d_v) and walks
-// the sequence chunk by chunk, carrying the float32 state slice in LDS.
+// One workgroup owns one (sequence, head, slice of BV columns of d_v) and
+// walks the sequence chunk by chunk, carrying the float32 state slice in LDS.
 // Per chunk of C rows with entry state S (Gamma = in-chunk cumulative
 // log-decay per channel, gamma = exp(Gamma)):
 //   M[r][i] = beta_r * sum_c k_rc k_ic exp(Gamma_rc - Gamma_ic)   (i < r)
@@ -12,8 +12,17 @@
 //   O = scale * ((gamma*Q) S + P U)
 //   S <- Diag(gamma_C) S + (exp(Gamma_C - Gamma) * K)^T U
 // This is the WY/UT-transform chunk form of the gated delta rule with a
-// per-channel decay; every exponential here is of a non-positive number,
-// so no range precondition on g is needed on this path.
+// per-channel decay. The grams take the factored form (gamma*K)(K/gamma)^T,
+// (gamma*Q)(K/gamma)^T when every channel's cumulative decay in the chunk
+// stays within [-80, 80] (so gamma and 1/gamma are finite); a chunk with
+// stronger decay takes every pair's exponential of its own difference instead
+// (non-positive for g <= 0), so no range precondition on g is needed on this
+// path.
+//
+// The three products with the state and the state update run on register
+// tiles (4 output columns per thread, 4 x 8 for the update) that read each
+// LDS operand once per 4 to 32 multiply-adds, and the next chunk's inputs are
+// loaded into registers while the current one is computed.
 //
 // With the prologue (ChunkArgs::prologue), rows are loaded as raw projections
 // and turned into the recurrence's inputs on the way into LDS:
@@ -27,32 +36,71 @@ namespace kda {
 namespace {
 
 constexpr int kGenThreads = 256;
-constexpr int kGenBV = 16;  // value columns per workgroup
+constexpr float kMaxChunkDecay = 80.f;   // factored grams while every -Gamma_C <= this
 
-template <int DK, int C, typename Tin>
+// Value columns per workgroup: 64 (or all of d_v) for 16- and 32-row chunks;
+// 16 for 64-row chunks, whose K, Q and Gamma tiles fill most of the LDS.
+constexpr int gen_bv(int C, int DV) { return C == 64 ? 16 : (DV < 64 ? DV : 64); }
+
+// The inputs of one chunk in registers, loaded ahead (element e of thread
+// tid: row/channel index tid + NT e of the C x DK tiles, and of C x BV for v).
+template <int DK, int C, int BV, typename Tin>
+struct GenRegs {
+    static constexpr int kNK = (C * DK + kGenThreads - 1) / kGenThreads;
+    static constexpr int kNV = (C * BV + kGenThreads - 1) / kGenThreads;
+    float q[kNK], k[kNK], g[kNK], v[kNV];
+    float beta;
+};
+
+template <int DK, int C, int BV, typename Tin>
+__device__ __forceinline__ void gen_load(GenRegs<DK, C, BV, Tin>& R, const ChunkArgs& a, int64_t tok0, int rows,
+                                         int h, int c0) {
+    const Tin* q = static_cast<const Tin*>(a.q);
+    const Tin* k = static_cast<const Tin*>(a.k);
+    const Tin* g = static_cast<const Tin*>(a.g);
+    const Tin* v = static_cast<const Tin*>(a.v);
+    const Tin* beta = static_cast<const Tin*>(a.beta);
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < R.kNK; ++e) {
+        const int idx = tid + kGenThreads * e;
+        const int r = idx / DK, c = idx % DK;
+        const bool in = idx < C * DK && r < rows;
+        const int64_t off = ((tok0 + r) * a.H + h) * DK + c;
+        R.q[e] = in ? load_elem(q, off) : 0.f;
+        R.k[e] = in ? load_elem(k, off) : 0.f;
+        R.g[e] = in ? load_elem(g, off) : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < R.kNV; ++e) {
+        const int idx = tid + kGenThreads * e;
+        const int r = idx / BV, j = idx % BV;
+        const bool in = idx < C * BV && r < rows && v;
+        R.v[e] = in ? load_elem(v, ((tok0 + r) * a.H + h) * a.Dv + c0 + j) : 0.f;
+    }
+    R.beta = tid < rows ? load_elem(beta, (tok0 + tid) * a.H + h) : 0.f;
+}
+
+template <int DK, int C, int BV, typename Tin>
 __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a) {
-    constexpr int BV = kGenBV;
-    constexpr int DKP = DK + 1;
+    constexpr int NT = kGenThreads;
+    constexpr int DKP = DK + 1;     // row stride of the C x DK tiles (odd: column reads spread over banks)
+    constexpr int BVP = BV + 4;     // row stride of the C x BV and DK x BV tiles (16-byte rows)
+    static_assert(C <= NT && DK <= NT, "one thread per row / channel");
     __shared__ float sK[C][DKP];
     __shared__ float sQ[C][DKP];
     __shared__ float sG[C][DKP];
     __shared__ float sA[C][C + 1];
     __shared__ float sP[C][C + 1];
-    __shared__ float sV[C][BV];
-    __shared__ float sU[C][BV];
-    __shared__ float sS[DK][BV];
+    __shared__ __attribute__((aligned(16))) float sV[C][BVP];
+    __shared__ __attribute__((aligned(16))) float sU[C][BVP];
+    __shared__ __attribute__((aligned(16))) float sS[DK][BVP];
     __shared__ float sBeta[C];
     __shared__ float sGn[DK];
     __shared__ float sAe[DK];     // prologue: exp(A_log)
     __shared__ float sDb[DK];     // prologue: dt_bias of this head
 
-    const Tin* q = static_cast<const Tin*>(a.q);
-    const Tin* k = static_cast<const Tin*>(a.k);
-    const Tin* v = static_cast<const Tin*>(a.v);
-    const Tin* g = static_cast<const Tin*>(a.g);
-    const Tin* beta = static_cast<const Tin*>(a.beta);
     Tin* o = static_cast<Tin*>(a.o);
-
     const int tid = threadIdx.x;
     const int nvt = a.Dv / BV;
     const int unit = blockIdx.x / nvt;
@@ -73,48 +121,53 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
     const int c0 = vt * BV;
     const int64_t state_base = ((int64_t)n * H + h) * DK * (int64_t)Dv;
 
-    for (int idx = tid; idx < DK * BV; idx += kGenThreads) {
+    for (int idx = tid; idx < DK * BV; idx += NT) {
         const int r = idx / BV, c = idx % BV;
         sS[r][c] = a.s0 ? a.s0[state_base + (int64_t)r * Dv + c0 + c] : 0.f;
     }
     if (a.prologue) {
-        for (int c = tid; c < DK; c += kGenThreads) {
+        for (int c = tid; c < DK; c += NT) {
             sAe[c] = expf(a.A_log[c]);
             sDb[c] = a.dt_bias[h * DK + c];
         }
     }
+    __syncthreads();
+
+    GenRegs<DK, C, BV, Tin> R;
+    if (len > 0) gen_load(R, a, b * (int64_t)a.T + bos, (int)(len < C ? len : C), h, c0);
 
     for (int64_t cs = 0; cs < len; cs += C) {
         const int rows = (int)((len - cs) < C ? (len - cs) : C);
         const int64_t tok0 = b * (int64_t)a.T + bos + cs;  // token index of chunk row 0
-        __syncthreads();
-        for (int idx = tid; idx < C * DK; idx += kGenThreads) {
-            const int r = idx / DK, c = idx % DK;
-            float qv = 0.f, kv = 0.f, gv = 0.f;
-            if (r < rows) {
-                const int64_t e = ((tok0 + r) * H + h) * DK + c;
-                qv = load_elem(q, e);
-                kv = load_elem(k, e);
-                gv = load_elem(g, e);
-                if (a.prologue) gv = a.gate_lb / (1.f + expf(-sAe[c] * (gv + sDb[c])));
+        // commit this chunk's inputs (the previous chunk's last reads of these
+        // tiles are behind the barrier that ended it)
+#pragma unroll
+        for (int e = 0; e < R.kNK; ++e) {
+            const int idx = tid + NT * e;
+            if (idx < C * DK) {
+                const int r = idx / DK, c = idx % DK;
+                float gv = R.g[e];
+                if (a.prologue && r < rows) gv = a.gate_lb / (1.f + expf(-sAe[c] * (gv + sDb[c])));
+                sQ[r][c] = R.q[e];
+                sK[r][c] = R.k[e];
+                sG[r][c] = gv;
             }
-            sQ[r][c] = qv;
-            sK[r][c] = kv;
-            sG[r][c] = gv;
         }
-        for (int idx = tid; idx < C * BV; idx += kGenThreads) {
-            const int r = idx / BV, c = idx % BV;
-            sV[r][c] = r < rows && v ? load_elem(v, ((tok0 + r) * H + h) * Dv + c0 + c) : 0.f;
+#pragma unroll
+        for (int e = 0; e < R.kNV; ++e) {
+            const int idx = tid + NT * e;
+            if (idx < C * BV) sV[idx / BV][idx % BV] = R.v[e];
         }
-        for (int r = tid; r < C; r += kGenThreads) {
-            float bv = r < rows ? load_elem(beta, (tok0 + r) * H + h) : 0.f;
-            if (a.prologue && r < rows) bv = 1.f / (1.f + expf(-bv));
-            sBeta[r] = bv;
+        if (tid < C) sBeta[tid] = a.prologue && tid < rows ? 1.f / (1.f + expf(-R.beta)) : R.beta;
+        // the next chunk's loads, in flight while this one is computed
+        if (cs + C < len) {
+            const int64_t rem = len - cs - C;
+            gen_load(R, a, tok0 + C, (int)(rem < C ? rem : C), h, c0);
         }
         __syncthreads();
         if (a.prologue) {
             // q and k rows to unit length (eps > 0: zero rows stay zero)
-            for (int idx = tid; idx < 2 * C; idx += kGenThreads) {
+            for (int idx = tid; idx < 2 * C; idx += NT) {
                 float* row = idx < C ? sQ[idx] : sK[idx - C];
                 float ss = 0.f;
                 for (int c = 0; c < DK; ++c) ss += row[c] * row[c];
@@ -124,56 +177,95 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
             __syncthreads();
         }
 
-        // in-chunk cumulative log-decay, one channel per thread
-        for (int c = tid; c < DK; c += kGenThreads) {
-            float acc = 0.f;
+        // in-chunk cumulative log-decay, one channel per thread; a chunk whose
+        // cumulative decay leaves [-80, 80] on some channel (or is not finite)
+        // takes the pairwise grams
+        bool steep = false;
+        if (tid < DK) {
+            float acc = 0.f, lo = 0.f, hi = 0.f;
             for (int r = 0; r < C; ++r) {
-                acc += sG[r][c];
-                sG[r][c] = acc;
+                acc += sG[r][tid];
+                sG[r][tid] = acc;
+                lo = fminf(lo, acc);
+                hi = fmaxf(hi, acc);
             }
-            sGn[c] = acc;
+            sGn[tid] = acc;
+            steep = !(lo >= -kMaxChunkDecay && hi <= kMaxChunkDecay && acc == acc);
         }
-        __syncthreads();
+        steep = __syncthreads_or(steep);
 
-        // decayed key-key and query-key products
-        for (int idx = tid; idx < C * C; idx += kGenThreads) {
-            const int r = idx / C, i = idx % C;
-            float am = 0.f, pm = 0.f;
-            if (i <= r) {
-                for (int c = 0; c < DK; ++c) {
-                    const float ki = sK[i][c] * expf(sG[r][c] - sG[i][c]);
-                    am += sK[r][c] * ki;
-                    pm += sQ[r][c] * ki;
+        if (steep) {
+            // pairwise: every exponential of a non-positive difference
+            for (int idx = tid; idx < C * C; idx += NT) {
+                const int r = idx / C, i = idx % C;
+                float am = 0.f, pm = 0.f;
+                if (i <= r) {
+                    for (int c = 0; c < DK; ++c) {
+                        const float ki = sK[i][c] * expf(sG[r][c] - sG[i][c]);
+                        am += sK[r][c] * ki;
+                        pm += sQ[r][c] * ki;
+                    }
                 }
+                sA[r][i] = (i < r) ? sBeta[r] * am : 0.f;
+                sP[r][i] = pm;
             }
-            sA[r][i] = (i < r) ? sBeta[r] * am : 0.f;
-            sP[r][i] = pm;
+            __syncthreads();
+            // gamma*Q into sQ, gamma*K into sG, exp(Gamma_C - Gamma)*K into sK
+            for (int idx = tid; idx < C * DK; idx += NT) {
+                const int r = idx / DK, c = idx % DK;
+                const float gv = sG[r][c];
+                const float kv = sK[r][c];
+                const float eg = expf(gv);
+                sQ[r][c] *= eg;
+                sG[r][c] = kv * eg;
+                sK[r][c] = kv * expf(sGn[c] - gv);
+            }
+            __syncthreads();
+        } else {
+            // gamma*Q into sQ, gamma*K into sG, K/gamma into sK
+            for (int idx = tid; idx < C * DK; idx += NT) {
+                const int r = idx / DK, c = idx % DK;
+                const float eg = expf(sG[r][c]);
+                const float kv = sK[r][c];
+                sQ[r][c] *= eg;
+                sG[r][c] = kv * eg;
+                sK[r][c] = kv * __builtin_amdgcn_rcpf(eg);
+            }
+            __syncthreads();
+            for (int idx = tid; idx < C * C; idx += NT) {
+                const int r = idx / C, i = idx % C;
+                float am = 0.f, pm = 0.f;
+                if (i <= r) {
+                    for (int c = 0; c < DK; ++c) {
+                        const float kb = sK[i][c];
+                        am += sG[r][c] * kb;
+                        pm += sQ[r][c] * kb;
+                    }
+                }
+                sA[r][i] = (i < r) ? sBeta[r] * am : 0.f;
+                sP[r][i] = pm;
+            }
+            __syncthreads();
+            // K/gamma to exp(Gamma_C - Gamma)*K for the state update
+            for (int idx = tid; idx < C * DK; idx += NT) {
+                const int r = idx / DK, c = idx % DK;
+                sK[r][c] *= expf(sGn[c]);
+            }
         }
-        __syncthreads();
 
-        // gamma*Q into sQ, gamma*K into sG, exp(Gamma_C - Gamma)*K into sK
-        for (int idx = tid; idx < C * DK; idx += kGenThreads) {
-            const int r = idx / DK, c = idx % DK;
-            const float gv = sG[r][c];
-            const float kv = sK[r][c];
-            const float eg = expf(gv);
-            sQ[r][c] *= eg;
-            sG[r][c] = kv * eg;
-            sK[r][c] = kv * expf(sGn[c] - gv);
-        }
-        __syncthreads();
-
-        // right-hand side Diag(beta)(V - (gamma*K) S)
-        for (int idx = tid; idx < C * BV; idx += kGenThreads) {
-            const int r = idx / BV, j = idx % BV;
-            float y = 0.f;
-            for (int c = 0; c < DK; ++c) y += sG[r][c] * sS[c][j];
-            sU[r][j] = sBeta[r] * (sV[r][j] - y);
+        // right-hand side Diag(beta)(V - (gamma*K) S): 4 columns per thread
+        for (int idx = tid; idx < C * (BV / 4); idx += NT) {
+            const int r = idx / (BV / 4), j = 4 * (idx % (BV / 4));
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+            for (int c = 0; c < DK; ++c) y += sG[r][c] * *reinterpret_cast<const f32x4*>(&sS[c][j]);
+            const f32x4 vv = *reinterpret_cast<const f32x4*>(&sV[r][j]);
+            *reinterpret_cast<f32x4*>(&sU[r][j]) = sBeta[r] * (vv - y);
         }
         __syncthreads();
 
         // (I + M) U = rhs by forward substitution, one column per thread
-        for (int j = tid; j < BV; j += kGenThreads) {
+        for (int j = tid; j < BV; j += NT) {
             for (int r = 1; r < rows; ++r) {
                 float acc = sU[r][j];
                 for (int i = 0; i < r; ++i) acc -= sA[r][i] * sU[i][j];
@@ -182,42 +274,77 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
         }
         __syncthreads();
 
-        for (int idx = tid; idx < C * BV; idx += kGenThreads) {
-            const int r = idx / BV, j = idx % BV;
+        // O = scale ((gamma*Q) S + P U): 4 columns per thread
+        for (int idx = tid; idx < C * (BV / 4); idx += NT) {
+            const int r = idx / (BV / 4), j = 4 * (idx % (BV / 4));
             if (r < rows && o) {
-                float acc = 0.f;
-                for (int c = 0; c < DK; ++c) acc += sQ[r][c] * sS[c][j];
-                for (int i = 0; i <= r; ++i) acc += sP[r][i] * sU[i][j];
-                store_elem(o, ((tok0 + r) * H + h) * Dv + c0 + j, a.scale * acc);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+                for (int c = 0; c < DK; ++c) acc += sQ[r][c] * *reinterpret_cast<const f32x4*>(&sS[c][j]);
+                for (int i = 0; i <= r; ++i) acc += sP[r][i] * *reinterpret_cast<const f32x4*>(&sU[i][j]);
+                const int64_t ob = ((tok0 + r) * H + h) * Dv + c0 + j;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) store_elem(o, ob + u, a.scale * acc[u]);
             }
         }
         __syncthreads();
 
-        for (int idx = tid; idx < DK * BV; idx += kGenThreads) {
-            const int c = idx / BV, j = idx % BV;
-            float acc = expf(sGn[c]) * sS[c][j];
-            for (int r = 0; r < rows; ++r) acc += sK[r][c] * sU[r][j];
-            sS[c][j] = acc;
+        // S <- Diag(gamma_C) S + (exp(Gamma_C - Gamma) K)^T U: 4 x 8 tiles (4 x 4 for BV = 16)
+        constexpr int TJ = BV >= 32 ? 8 : 4;
+        for (int idx = tid; idx < (DK / 4) * (BV / TJ); idx += NT) {
+            const int c = 4 * (idx / (BV / TJ)), j = TJ * (idx % (BV / TJ));
+            f32x4 acc[4][TJ / 4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float d = expf(sGn[c + u]);
+#pragma unroll
+                for (int w = 0; w < TJ / 4; ++w) acc[u][w] = d * *reinterpret_cast<const f32x4*>(&sS[c + u][j + 4 * w]);
+            }
+            for (int r = 0; r < rows; ++r) {
+                f32x4 ur[TJ / 4];
+#pragma unroll
+                for (int w = 0; w < TJ / 4; ++w) ur[w] = *reinterpret_cast<const f32x4*>(&sU[r][j + 4 * w]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float kr = sK[r][c + u];
+#pragma unroll
+                    for (int w = 0; w < TJ / 4; ++w) acc[u][w] += kr * ur[w];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int w = 0; w < TJ / 4; ++w) *reinterpret_cast<f32x4*>(&sS[c + u][j + 4 * w]) = acc[u][w];
         }
+        __syncthreads();
     }
-    __syncthreads();
     if (a.sT) {
-        for (int idx = tid; idx < DK * BV; idx += kGenThreads) {
+        for (int idx = tid; idx < DK * BV; idx += NT) {
             const int r = idx / BV, c = idx % BV;
             a.sT[state_base + (int64_t)r * Dv + c0 + c] = sS[r][c];
         }
     }
 }
 
+template <int DK, int C, int DV>
+hipError_t launch_dk_c_dv(const ChunkArgs& a, hipStream_t s) {
+    constexpr int BV = gen_bv(C, DV);
+    const int units = a.N * a.H;
+    const dim3 grid((unsigned)(units * (a.Dv / BV)));
+    if (a.bf16)
+        hipLaunchKernelGGL((chunk_generic_kernel<DK, C, BV, __bf16>), grid, dim3(kGenThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((chunk_generic_kernel<DK, C, BV, float>), grid, dim3(kGenThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int DK, int C>
 hipError_t launch_dk_c(const ChunkArgs& a, hipStream_t s) {
-    const int units = a.N * a.H;
-    const dim3 grid((unsigned)(units * (a.Dv / kGenBV)));
-    if (a.bf16)
-        hipLaunchKernelGGL((chunk_generic_kernel<DK, C, __bf16>), grid, dim3(kGenThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((chunk_generic_kernel<DK, C, float>), grid, dim3(kGenThreads), 0, s, a);
-    return hipGetLastError();
+    switch (a.Dv) {
+        case 16: return launch_dk_c_dv<DK, C, 16>(a, s);
+        case 32: return launch_dk_c_dv<DK, C, 32>(a, s);
+        default: return launch_dk_c_dv<DK, C, 64>(a, s);   // 64 and 128: slices of gen_bv(C, 64)
+    }
 }
 
 template <int DK>

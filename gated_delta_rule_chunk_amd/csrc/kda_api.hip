@@ -141,9 +141,9 @@ kda_status check_chunk(const char* fn, const void* q, const void* k, const void*
     if (!dim_ok(Dk) || !dim_ok(Dv))
         return fail(KDA_ERR_UNSUPPORTED, "%s: Dk=%d, Dv=%d; supported head dims are 16, 32, 64, 128",
                     fn, Dk, Dv);
-    const int32_t chunk = chunk_size == 0 ? 64 : chunk_size;
+    const int32_t chunk = chunk_size == 0 ? 16 : chunk_size;
     if (chunk != 16 && chunk != 32 && chunk != 64)
-        return fail(KDA_ERR_UNSUPPORTED, "%s: chunk_size=%d; supported are 16, 32, 64 (0 = 64)", fn, chunk_size);
+        return fail(KDA_ERR_UNSUPPORTED, "%s: chunk_size=%d; supported are 16, 32, 64 (0 = 16)", fn, chunk_size);
     if (cu_seqlens) {
         if (B != 1)
             return fail(KDA_ERR_INVALID_ARG, "%s: packed sequences (cu_seqlens) need B == 1, got B=%d", fn, B);

@@ -80,7 +80,7 @@ typedef enum {
  *                  kernel (Dk = Dv = 128) works in 16-row chunks only: there
  *                  chunk_size must be 0 or 16, and any other value is
  *                  KDA_ERR_UNSUPPORTED. The float32 vector-ALU kernel takes
- *                  16, 32 or 64 (0 = 64).
+ *                  16, 32 or 64 (0 = 16, its fastest).
  *   scale          multiplies the output (1.0 reproduces the rule above)
  *   o              [B,T,H,Dv]  dtype, written for every row of every sequence;
  *                  must not alias an input. With T = 0, q, k, v, g, beta and
