@@ -253,34 +253,65 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
             }
         }
 
-        // right-hand side Diag(beta)(V - (gamma*K) S): 4 columns per thread
-        for (int idx = tid; idx < C * (BV / 4); idx += NT) {
-            const int r = idx / (BV / 4), j = 4 * (idx % (BV / 4));
-            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        // right-hand side Diag(beta)(V - (gamma*K) S), and the output's
+        // (gamma*Q) S kept in registers: 4 columns per thread, one pass over S
+        constexpr int kRT = (C * (BV / 4) + NT - 1) / NT;
+        f32x4 qs[kRT];
+#pragma unroll
+        for (int e = 0; e < kRT; ++e) {
+            const int idx = tid + NT * e;
+            if (idx < C * (BV / 4)) {
+                const int r = idx / (BV / 4), j = 4 * (idx % (BV / 4));
+                f32x4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-            for (int c = 0; c < DK; ++c) y += sG[r][c] * *reinterpret_cast<const f32x4*>(&sS[c][j]);
-            const f32x4 vv = *reinterpret_cast<const f32x4*>(&sV[r][j]);
-            *reinterpret_cast<f32x4*>(&sU[r][j]) = sBeta[r] * (vv - y);
+                for (int c = 0; c < DK; ++c) {
+                    const f32x4 sv = *reinterpret_cast<const f32x4*>(&sS[c][j]);
+                    y += sG[r][c] * sv;
+                    z += sQ[r][c] * sv;
+                }
+                qs[e] = z;
+                const f32x4 vv = *reinterpret_cast<const f32x4*>(&sV[r][j]);
+                *reinterpret_cast<f32x4*>(&sU[r][j]) = sBeta[r] * (vv - y);
+            }
         }
         __syncthreads();
 
-        // (I + M) U = rhs by forward substitution, one column per thread
-        for (int j = tid; j < BV; j += NT) {
-            for (int r = 1; r < rows; ++r) {
-                float acc = sU[r][j];
-                for (int i = 0; i < r; ++i) acc -= sA[r][i] * sU[i][j];
-                sU[r][j] = acc;
+        // (I + M) U = rhs by forward substitution, one column per thread; for
+        // 16- and 32-row chunks the column stays in registers (rows past the
+        // sequence's end have zero rhs and zero M rows, so they stay zero)
+        if constexpr (C <= 32) {
+            for (int j = tid; j < BV; j += NT) {
+                float u[C];
+#pragma unroll
+                for (int r = 0; r < C; ++r) u[r] = sU[r][j];
+#pragma unroll
+                for (int r = 1; r < C; ++r) {
+                    float acc = u[r];
+#pragma unroll
+                    for (int i = 0; i < r; ++i) acc -= sA[r][i] * u[i];
+                    u[r] = acc;
+                }
+#pragma unroll
+                for (int r = 1; r < C; ++r) sU[r][j] = u[r];
+            }
+        } else {
+            for (int j = tid; j < BV; j += NT) {
+                for (int r = 1; r < rows; ++r) {
+                    float acc = sU[r][j];
+                    for (int i = 0; i < r; ++i) acc -= sA[r][i] * sU[i][j];
+                    sU[r][j] = acc;
+                }
             }
         }
         __syncthreads();
 
         // O = scale ((gamma*Q) S + P U): 4 columns per thread
-        for (int idx = tid; idx < C * (BV / 4); idx += NT) {
+#pragma unroll
+        for (int e = 0; e < kRT; ++e) {
+            const int idx = tid + NT * e;
             const int r = idx / (BV / 4), j = 4 * (idx % (BV / 4));
-            if (r < rows && o) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-                for (int c = 0; c < DK; ++c) acc += sQ[r][c] * *reinterpret_cast<const f32x4*>(&sS[c][j]);
+            if (idx < C * (BV / 4) && r < rows && o) {
+                f32x4 acc = qs[e];
                 for (int i = 0; i <= r; ++i) acc += sP[r][i] * *reinterpret_cast<const f32x4*>(&sU[i][j]);
                 const int64_t ob = ((tok0 + r) * H + h) * Dv + c0 + j;
 #pragma unroll

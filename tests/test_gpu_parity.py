@@ -39,6 +39,24 @@ def test_f32_general_dims(Dk, Dv, chunk):
     _check(inp, TOL_F32, chunk=chunk, label=f"f32 Dk={Dk} Dv={Dv}")
 
 
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_f32_factored_and_pairwise_grams_mixed(chunk):
+    """The float32 kernel forms a chunk's grams from gamma*K and K/gamma while
+    every channel's in-chunk cumulative decay stays within e^(+-80), and from
+    each pair's own exponential otherwise, chunk by chunk. Here one sequence
+    mixes both: mild gates on head 0, gates down to -30 per step on part of
+    head 1 followed by no decay at all, single-step drops of -60 on a few
+    channels of head 2, the default gates on head 3."""
+    inp = synth.make_chunk_inputs(1, 200, 4, 128, 64, seed=510, dtype="f32", init_state=True, s0_std=0.5)
+    g = inp["g"].clone()
+    g[:, :, 0] *= 0.002
+    g[:, 50:120, 1] *= 6.0
+    g[:, 120:, 1] = 0.0
+    g[:, ::7, 2, :5] = -60.0
+    inp["g"] = g
+    _check(inp, TOL_F32, chunk=chunk, label="f32 factored and pairwise grams")
+
+
 @pytest.mark.parametrize("B,T,H", [(1, 293, 5), (3, 200, 16), (2, 64, 8), (1, 1, 3), (3, 77, 96)])
 def test_bf16_mfma_path(B, T, H):
     inp = synth.make_chunk_inputs(B, T, H, 128, 128, seed=200 + T + H, dtype="bf16", init_state=True)
