@@ -81,15 +81,17 @@ __device__ __forceinline__ void gen_load(GenRegs<DK, C, BV, Tin>& R, const Chunk
     R.beta = tid < rows ? load_elem(beta, (tok0 + tid) * a.H + h) : 0.f;
 }
 
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
 template <int DK, int C, int BV, typename Tin>
 __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a) {
     constexpr int NT = kGenThreads;
-    constexpr int DKP = DK + 1;     // row stride of the C x DK tiles (odd: column reads spread over banks)
+    constexpr int DKP = DK + 4;     // row stride of the C x DK tiles (16-byte rows; row r starts at bank 4r)
     constexpr int BVP = BV + 4;     // row stride of the C x BV and DK x BV tiles (16-byte rows)
     static_assert(C <= NT && DK <= NT, "one thread per row / channel");
-    __shared__ float sK[C][DKP];
-    __shared__ float sQ[C][DKP];
-    __shared__ float sG[C][DKP];
+    __shared__ __attribute__((aligned(16))) float sK[C][DKP];
+    __shared__ __attribute__((aligned(16))) float sQ[C][DKP];
+    __shared__ __attribute__((aligned(16))) float sG[C][DKP];
     __shared__ float sA[C][C + 1];
     __shared__ float sP[C][C + 1];
     __shared__ __attribute__((aligned(16))) float sV[C][BVP];
@@ -168,11 +170,15 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
         if (a.prologue) {
             // q and k rows to unit length (eps > 0: zero rows stay zero)
             for (int idx = tid; idx < 2 * C; idx += NT) {
-                float* row = idx < C ? sQ[idx] : sK[idx - C];
+                f32x4* row = reinterpret_cast<f32x4*>(idx < C ? sQ[idx] : sK[idx - C]);
                 float ss = 0.f;
-                for (int c = 0; c < DK; ++c) ss += row[c] * row[c];
+                for (int c4 = 0; c4 < DK / 4; ++c4) {
+                    const f32x4 x = row[c4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) ss += x[u] * x[u];
+                }
                 const float rs = 1.f / sqrtf(ss + a.l2_eps);
-                for (int c = 0; c < DK; ++c) row[c] *= rs;
+                for (int c4 = 0; c4 < DK / 4; ++c4) row[c4] *= rs;
             }
             __syncthreads();
         }
@@ -200,10 +206,15 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
                 const int r = idx / C, i = idx % C;
                 float am = 0.f, pm = 0.f;
                 if (i <= r) {
-                    for (int c = 0; c < DK; ++c) {
-                        const float ki = sK[i][c] * expf(sG[r][c] - sG[i][c]);
-                        am += sK[r][c] * ki;
-                        pm += sQ[r][c] * ki;
+                    for (int c = 0; c < DK; c += 4) {
+                        const f32x4 kb = ld4(&sK[i][c]), gi = ld4(&sG[i][c]), gr = ld4(&sG[r][c]);
+                        const f32x4 kr = ld4(&sK[r][c]), qr = ld4(&sQ[r][c]);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const float ki = kb[u] * expf(gr[u] - gi[u]);
+                            am += kr[u] * ki;
+                            pm += qr[u] * ki;
+                        }
                     }
                 }
                 sA[r][i] = (i < r) ? sBeta[r] * am : 0.f;
@@ -236,10 +247,14 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
                 const int r = idx / C, i = idx % C;
                 float am = 0.f, pm = 0.f;
                 if (i <= r) {
-                    for (int c = 0; c < DK; ++c) {
-                        const float kb = sK[i][c];
-                        am += sG[r][c] * kb;
-                        pm += sQ[r][c] * kb;
+#pragma unroll 4
+                    for (int c = 0; c < DK; c += 4) {
+                        const f32x4 kb = ld4(&sK[i][c]), gr = ld4(&sG[r][c]), qr = ld4(&sQ[r][c]);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            am += gr[u] * kb[u];
+                            pm += qr[u] * kb[u];
+                        }
                     }
                 }
                 sA[r][i] = (i < r) ? sBeta[r] * am : 0.f;
@@ -263,11 +278,15 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
             if (idx < C * (BV / 4)) {
                 const int r = idx / (BV / 4), j = 4 * (idx % (BV / 4));
                 f32x4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-                for (int c = 0; c < DK; ++c) {
-                    const f32x4 sv = *reinterpret_cast<const f32x4*>(&sS[c][j]);
-                    y += sG[r][c] * sv;
-                    z += sQ[r][c] * sv;
+#pragma unroll 2
+                for (int c = 0; c < DK; c += 4) {
+                    const f32x4 gr = ld4(&sG[r][c]), qr = ld4(&sQ[r][c]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const f32x4 sv = ld4(&sS[c + u][j]);
+                        y += gr[u] * sv;
+                        z += qr[u] * sv;
+                    }
                 }
                 qs[e] = z;
                 const f32x4 vv = *reinterpret_cast<const f32x4*>(&sV[r][j]);
@@ -335,12 +354,11 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
                 f32x4 ur[TJ / 4];
 #pragma unroll
                 for (int w = 0; w < TJ / 4; ++w) ur[w] = *reinterpret_cast<const f32x4*>(&sU[r][j + 4 * w]);
+                const f32x4 kr = ld4(&sK[r][c]);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float kr = sK[r][c + u];
+                for (int u = 0; u < 4; ++u)
 #pragma unroll
-                    for (int w = 0; w < TJ / 4; ++w) acc[u][w] += kr * ur[w];
-                }
+                    for (int w = 0; w < TJ / 4; ++w) acc[u][w] += kr[u] * ur[w];
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
