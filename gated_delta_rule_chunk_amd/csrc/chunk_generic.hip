@@ -295,34 +295,40 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
         }
         __syncthreads();
 
-        // (I + M) U = rhs by forward substitution, one column per thread; for
-        // 16- and 32-row chunks the column stays in registers (rows past the
-        // sequence's end have zero rhs and zero M rows, so they stay zero)
-        if constexpr (C <= 32) {
+        // (I + M) U = rhs by blocked forward substitution over 16-row blocks:
+        // each diagonal block is solved with its columns in registers (one
+        // column per thread), then the rows below subtract that block's terms
+        // in parallel. Every row still subtracts its terms in ascending order,
+        // as the plain substitution does. Rows past the sequence's end have
+        // zero rhs and zero M rows, so they stay zero.
+#pragma unroll
+        for (int b0 = 0; b0 < C; b0 += 16) {
             for (int j = tid; j < BV; j += NT) {
-                float u[C];
+                float u[16];
 #pragma unroll
-                for (int r = 0; r < C; ++r) u[r] = sU[r][j];
+                for (int r = 0; r < 16; ++r) u[r] = sU[b0 + r][j];
 #pragma unroll
-                for (int r = 1; r < C; ++r) {
+                for (int r = 1; r < 16; ++r) {
                     float acc = u[r];
 #pragma unroll
-                    for (int i = 0; i < r; ++i) acc -= sA[r][i] * u[i];
+                    for (int i = 0; i < r; ++i) acc -= sA[b0 + r][b0 + i] * u[i];
                     u[r] = acc;
                 }
 #pragma unroll
-                for (int r = 1; r < C; ++r) sU[r][j] = u[r];
+                for (int r = 1; r < 16; ++r) sU[b0 + r][j] = u[r];
             }
-        } else {
-            for (int j = tid; j < BV; j += NT) {
-                for (int r = 1; r < rows; ++r) {
+            __syncthreads();
+            if (b0 + 16 < C) {
+                for (int idx = tid; idx < (C - b0 - 16) * BV; idx += NT) {
+                    const int r = b0 + 16 + idx / BV, j = idx % BV;
                     float acc = sU[r][j];
-                    for (int i = 0; i < r; ++i) acc -= sA[r][i] * sU[i][j];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc -= sA[r][b0 + i] * sU[b0 + i][j];
                     sU[r][j] = acc;
                 }
+                __syncthreads();
             }
         }
-        __syncthreads();
 
         // O = scale ((gamma*Q) S + P U): 4 columns per thread
 #pragma unroll
