@@ -1,7 +1,7 @@
 """Benchmark: KDA chunked forward on the K3 layer shape, one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-backward] [--no-split]
-                    [--only split|backward]
+                    [--only split|backward|conv|decode|f32]
 
 One step = one kda_chunk_fwd call over a K3-shaped batch: B=1, T=4096, H=96,
 d_k=d_v=128, bf16 inputs, zero initial state, output plus final state. The
@@ -18,6 +18,8 @@ Prints one JSON line. ``value`` is tokens/s of the forward (T / seconds per
 step). ``roofline`` is for the chunk kernel: algorithmic HBM bytes per launch
 (q,k,v,g,o at 256 B per token-head each, beta at 2 B, the fp32 final state)
 over its average launch time, measured with HIP events on the launch stream.
+``f32`` times the same forward with float32 inputs and output (the vector-ALU
+chunk kernel, 16-row chunks) against the fp32 vector-ALU peak.
 ``prologue`` times the same forward from raw projections with the gate, beta
 and L2-normalisation prologue fused into the chunk kernel
 (kda_chunk_fwd_prologue). ``short_conv`` times the kernel-4 convolution of the
@@ -59,6 +61,7 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector ALU, TFLOP/s
 METRIC = "KDA fwd tokens/s at H=96,d=128 (bf16); MFMA util % and decode HBM GB/s"
 CHUNK_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_chunk_amd", "csrc", "chunk_mfma.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_mfma_k3_t4096_traffic.md")
@@ -259,6 +262,43 @@ def bench_prologue(steps, warmup):
             "kernel_ms_median": float(np.median(per)),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": read_traffic("prologue_traffic_bytes_per_launch")},
+            "algorithmic_bytes_per_launch": nbytes}
+
+
+def bench_f32(steps, warmup):
+    """The same forward with float32 inputs (q, k, v, g, beta, o all fp32):
+    the vector-ALU chunk kernel at its default 16-row chunks. It is bound by
+    its fp32 arithmetic and LDS reads, so the roofline is the fp32 vector-ALU
+    peak with the full-tile flop count of the chunk form at C=16; the HBM rate
+    of the same launches is given beside it."""
+    w = synth.WORKLOADS["k3_t4096"]
+    dev = torch.device("cuda:0")
+    sets = []
+    for s in range(2):
+        inp = synth.make_chunk_inputs(w.B, w.T, w.H, w.Dk, w.Dv, seed=w.seed + 1000 * s, dtype="f32")
+        sets.append({k: (None if v is None else v.to(dev)) for k, v in inp.items()})
+    o = torch.empty((w.B, w.T, w.H, w.Dv), dtype=torch.float32, device=dev)
+    fin = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        d = sets[i % 2]
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk_size=0, out=o, final_state=fin)
+
+    wall, per, batch = time_launches(step, steps, warmup, stream)
+    if not (torch.isfinite(o).all() and torch.isfinite(fin).all()):
+        raise RuntimeError("non-finite float32 forward output")
+    kern_ms = float(batch)
+    nflops = fwd_flops(w.T, w.H, w.Dk, w.Dv, C=16)
+    nbytes = fwd_bytes(w.T, w.H, w.Dk, w.Dv, n_states_out=1, elem=4)
+    tflops = nflops / (kern_ms * 1e-3) / 1e12
+    gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    return {"workload": "k3_t4096 with float32 q, k, v, g, beta and o (vector-ALU chunk kernel, 16-row chunks)",
+            "ms_per_step": wall / steps * 1e3, "tokens_per_s": w.T / (wall / steps), "kernel_ms": kern_ms,
+            "kernel_ms_median": float(np.median(per)),
+            "roofline": {"bound": "alu", "achieved": tflops, "peak": F32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tflops / F32_VALU_PEAK_TFLOPS, "traffic": None},
+            "flops_per_launch": nflops, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "algorithmic_bytes_per_launch": nbytes}
 
 
@@ -711,7 +751,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-split", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["split", "backward", "conv", "decode"], default=None,
+    ap.add_argument("--only", choices=["split", "backward", "conv", "decode", "f32"], default=None,
                     help="run one secondary leg alone and print its JSON object (for per-kernel profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -729,7 +769,8 @@ def main():
         legs = {"split": lambda: bench_split(args.steps, args.warmup),
                 "backward": lambda: bench_backward(args.steps, args.warmup, cpu=False),
                 "conv": lambda: bench_conv(args.steps, args.warmup),
-                "decode": lambda: bench_decode(args.steps, args.warmup)}
+                "decode": lambda: bench_decode(args.steps, args.warmup),
+                "f32": lambda: bench_f32(args.steps, args.warmup)}
         leg = legs[args.only]()
         print(json.dumps({"only": args.only, **leg}), flush=True)
         return
@@ -778,6 +819,7 @@ def main():
     }
     line["prologue"] = bench_prologue(args.steps, args.warmup)
     line["short_conv"] = bench_conv(args.steps, args.warmup)
+    line["f32"] = bench_f32(args.steps, args.warmup)
     if not args.no_split:
         line["split"] = bench_split(args.steps, args.warmup)
     if not args.no_backward:
