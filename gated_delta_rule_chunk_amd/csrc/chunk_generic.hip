@@ -20,8 +20,8 @@
 // path.
 //
 // The three products with the state and the state update run on register
-// tiles (4 output columns per thread, 4 x 8 for the update) that read each
-// LDS operand once per 4 to 32 multiply-adds, and the next chunk's inputs are
+// tiles (4 output columns per thread, 4 x 4 for the update) that read each
+// LDS operand once per 4 to 16 multiply-adds, and the next chunk's inputs are
 // loaded into registers while the current one is computed.
 //
 // With the prologue (ChunkArgs::prologue), rows are loaded as raw projections
@@ -35,7 +35,7 @@
 namespace kda {
 namespace {
 
-constexpr int kGenThreads = 256;
+constexpr int kGenThreads = 512;
 constexpr float kMaxChunkDecay = 80.f;   // factored grams while every -Gamma_C <= this
 
 // Value columns per workgroup: 64 (or all of d_v) for 16- and 32-row chunks;
@@ -345,8 +345,8 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
         }
         __syncthreads();
 
-        // S <- Diag(gamma_C) S + (exp(Gamma_C - Gamma) K)^T U: 4 x 8 tiles (4 x 4 for BV = 16)
-        constexpr int TJ = BV >= 32 ? 8 : 4;
+        // S <- Diag(gamma_C) S + (exp(Gamma_C - Gamma) K)^T U: 4 x 4 tiles
+        constexpr int TJ = 4;
         for (int idx = tid; idx < (DK / 4) * (BV / TJ); idx += NT) {
             const int c = 4 * (idx / (BV / TJ)), j = TJ * (idx % (BV / TJ));
             f32x4 acc[4][TJ / 4];
