@@ -120,6 +120,7 @@ LEG_TRAFFIC = {
     "decode": ("recurrent_step_k3_decode_b256_traffic.md", ("recurrent_step.hip",)),
     "short_conv": ("short_conv_k3_t4096_traffic.md", ("short_conv.hip",)),
     "split": ("chunk_fwd_split_h12_t32768_traffic.md", ("split.hip", "chunk_mfma.hip")),
+    "f32": ("chunk_generic_k3_t4096_f32.md", ("chunk_generic.hip",)),
 }
 
 
@@ -131,7 +132,7 @@ def leg_source_hash(leg):
 
 
 def read_leg_traffic(leg, key="traffic_bytes_per_step"):
-    """HBM bytes per step of a secondary leg (decode, short_conv, split) from its
+    """HBM bytes per step of a secondary leg (decode, short_conv, split, f32) from its
     committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the
     current sources of its kernels; otherwise None."""
     path = os.path.join(ROOT, "profiles", LEG_TRAFFIC[leg][0])
@@ -297,7 +298,7 @@ def bench_f32(steps, warmup):
             "ms_per_step": wall / steps * 1e3, "tokens_per_s": w.T / (wall / steps), "kernel_ms": kern_ms,
             "kernel_ms_median": float(np.median(per)),
             "roofline": {"bound": "alu", "achieved": tflops, "peak": F32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tflops / F32_VALU_PEAK_TFLOPS, "traffic": None},
+                         "frac": tflops / F32_VALU_PEAK_TFLOPS, "traffic": read_leg_traffic("f32")},
             "flops_per_launch": nflops, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "algorithmic_bytes_per_launch": nbytes}
 
