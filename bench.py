@@ -18,8 +18,8 @@ Prints one JSON line. ``value`` is tokens/s of the forward (T / seconds per
 step). ``roofline`` is for the chunk kernel: algorithmic HBM bytes per launch
 (q,k,v,g,o at 256 B per token-head each, beta at 2 B, the fp32 final state)
 over its average launch time, measured with HIP events on the launch stream.
-``f32`` times the same forward with float32 inputs and output (the vector-ALU
-chunk kernel, 16-row chunks) against the fp32 vector-ALU peak.
+``f32`` times the same forward with float32 inputs and output (the float32
+chunk kernel, 16-row chunks, products as f32 MFMA) against the fp32 matrix peak.
 ``prologue`` times the same forward from raw projections with the gate, beta
 and L2-normalisation prologue fused into the chunk kernel
 (kda_chunk_fwd_prologue). ``short_conv`` times the kernel-4 convolution of the
@@ -61,7 +61,7 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
-F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector ALU, TFLOP/s
+F32_PEAK_TFLOPS = 157.3        # MI355X fp32, dense MFMA and vector ALU alike, TFLOP/s
 METRIC = "KDA fwd tokens/s at H=96,d=128 (bf16); MFMA util % and decode HBM GB/s"
 CHUNK_KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_chunk_amd", "csrc", "chunk_mfma.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_mfma_k3_t4096_traffic.md")
@@ -268,10 +268,10 @@ def bench_prologue(steps, warmup):
 
 def bench_f32(steps, warmup):
     """The same forward with float32 inputs (q, k, v, g, beta, o all fp32):
-    the vector-ALU chunk kernel at its default 16-row chunks. It is bound by
-    its fp32 arithmetic and LDS reads, so the roofline is the fp32 vector-ALU
-    peak with the full-tile flop count of the chunk form at C=16; the HBM rate
-    of the same launches is given beside it."""
+    the float32 chunk kernel at its default 16-row chunks, whose dense
+    products run as f32 MFMA. The roofline is the fp32 matrix peak with the
+    full-tile flop count of the chunk form at C=16; the HBM rate of the same
+    launches is given beside it."""
     w = synth.WORKLOADS["k3_t4096"]
     dev = torch.device("cuda:0")
     sets = []
@@ -294,11 +294,11 @@ def bench_f32(steps, warmup):
     nbytes = fwd_bytes(w.T, w.H, w.Dk, w.Dv, n_states_out=1, elem=4)
     tflops = nflops / (kern_ms * 1e-3) / 1e12
     gbs = nbytes / (kern_ms * 1e-3) / 1e9
-    return {"workload": "k3_t4096 with float32 q, k, v, g, beta and o (vector-ALU chunk kernel, 16-row chunks)",
+    return {"workload": "k3_t4096 with float32 q, k, v, g, beta and o (float32 chunk kernel, 16-row chunks)",
             "ms_per_step": wall / steps * 1e3, "tokens_per_s": w.T / (wall / steps), "kernel_ms": kern_ms,
             "kernel_ms_median": float(np.median(per)),
-            "roofline": {"bound": "alu", "achieved": tflops, "peak": F32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tflops / F32_VALU_PEAK_TFLOPS, "traffic": read_leg_traffic("f32")},
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tflops / F32_PEAK_TFLOPS, "traffic": read_leg_traffic("f32")},
             "flops_per_launch": nflops, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "algorithmic_bytes_per_launch": nbytes}
 

@@ -1,4 +1,4 @@
-// Chunkwise KDA forward in float32 on the vector ALUs: the general path for
+// Chunkwise KDA forward in float32 arithmetic: the general path for
 // every supported (dtype, Dk, Dv, chunk) combination that the bf16
 // matrix-core kernel does not cover.
 //
@@ -19,10 +19,11 @@
 // (non-positive for g <= 0), so no range precondition on g is needed on this
 // path.
 //
-// The three products with the state and the state update run on register
-// tiles (4 output columns per thread, 4 x 4 for the update) that read each
-// LDS operand once per 4 to 16 multiply-adds, and the next chunk's inputs are
-// loaded into registers while the current one is computed.
+// With 16-row chunks the grams (factored form), the two products with the
+// state, P U and the state update run on the matrix cores as float32 16x16x4
+// products; longer chunks run them on the vector ALUs as register tiles (4
+// output columns per thread, 4 x 4 for the update). The next chunk's inputs
+// are loaded into registers while the current one is computed.
 //
 // With the prologue (ChunkArgs::prologue), rows are loaded as raw projections
 // and turned into the recurrence's inputs on the way into LDS:
@@ -99,11 +100,20 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
     __shared__ __attribute__((aligned(16))) float sS[DK][BVP];
     __shared__ float sBeta[C];
     __shared__ float sGn[DK];
+    __shared__ float sEd[DK];     // exp(Gamma_C): the chunk's decay of each state row
     __shared__ float sAe[DK];     // prologue: exp(A_log)
     __shared__ float sDb[DK];     // prologue: dt_bias of this head
 
     Tin* o = static_cast<Tin*>(a.o);
     const int tid = threadIdx.x;
+    // 16-row chunks run their dense products on the matrix cores (f32
+    // 16x16x4: float32 operands, float32 sums). Operand layouts, lane l with
+    // l16 = l % 16, lg = l / 16: A[m][k] at m = l16, k = lg; B[k][n] at k = lg,
+    // n = l16; result register i holds D[4 lg + i][l16].
+    constexpr bool kMfma = C == 16;
+    constexpr int NTL = BV / 16;    // 16-column tiles of the slice
+    const int wave = tid / 64, l16 = tid % 16, lg = (tid % 64) / 16;
+    const int mp = wave / NTL, mt = wave % NTL;   // rhs/output: product (0: K, 1: Q) and column tile of this wave
     const int nvt = a.Dv / BV;
     const int unit = blockIdx.x / nvt;
     const int vt = blockIdx.x % nvt;
@@ -196,6 +206,7 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
                 hi = fmaxf(hi, acc);
             }
             sGn[tid] = acc;
+            sEd[tid] = expf(acc);
             steep = !(lo >= -kMaxChunkDecay && hi <= kMaxChunkDecay && acc == acc);
         }
         steep = __syncthreads_or(steep);
@@ -243,54 +254,95 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
                 sK[r][c] = kv * __builtin_amdgcn_rcpf(eg);
             }
             __syncthreads();
-            for (int idx = tid; idx < C * C; idx += NT) {
-                const int r = idx / C, i = idx % C;
-                float am = 0.f, pm = 0.f;
-                if (i <= r) {
-#pragma unroll 4
-                    for (int c = 0; c < DK; c += 4) {
-                        const f32x4 kb = ld4(&sK[i][c]), gr = ld4(&sG[r][c]), qr = ld4(&sQ[r][c]);
+            if constexpr (kMfma) {
+                // waves 0 and 1: (gamma*K)(K/gamma)^T and (gamma*Q)(K/gamma)^T
+                if (wave < 2) {
+                    const float(*X)[DKP] = wave ? sQ : sG;
+                    f32x4 gm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+                    for (int s4 = 0; s4 < DK; s4 += 4)
+                        gm = __builtin_amdgcn_mfma_f32_16x16x4f32(X[l16][s4 + lg], sK[l16][s4 + lg], gm, 0, 0, 0);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            am += gr[u] * kb[u];
-                            pm += qr[u] * kb[u];
-                        }
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = 4 * lg + i;
+                        if (wave == 0)
+                            sA[m][l16] = l16 < m ? sBeta[m] * gm[i] : 0.f;
+                        else
+                            sP[m][l16] = l16 <= m ? gm[i] : 0.f;
                     }
                 }
-                sA[r][i] = (i < r) ? sBeta[r] * am : 0.f;
-                sP[r][i] = pm;
+            } else {
+                for (int idx = tid; idx < C * C; idx += NT) {
+                    const int r = idx / C, i = idx % C;
+                    float am = 0.f, pm = 0.f;
+                    if (i <= r) {
+#pragma unroll 4
+                        for (int c = 0; c < DK; c += 4) {
+                            const f32x4 kb = ld4(&sK[i][c]), gr = ld4(&sG[r][c]), qr = ld4(&sQ[r][c]);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                am += gr[u] * kb[u];
+                                pm += qr[u] * kb[u];
+                            }
+                        }
+                    }
+                    sA[r][i] = (i < r) ? sBeta[r] * am : 0.f;
+                    sP[r][i] = pm;
+                }
             }
             __syncthreads();
+
             // K/gamma to exp(Gamma_C - Gamma)*K for the state update
             for (int idx = tid; idx < C * DK; idx += NT) {
                 const int r = idx / DK, c = idx % DK;
-                sK[r][c] *= expf(sGn[c]);
+                sK[r][c] *= sEd[c];
             }
         }
 
         // right-hand side Diag(beta)(V - (gamma*K) S), and the output's
-        // (gamma*Q) S kept in registers: 4 columns per thread, one pass over S
-        constexpr int kRT = (C * (BV / 4) + NT - 1) / NT;
+        // (gamma*Q) S kept in registers. 16-row chunks: on the matrix cores
+        // (f32 16x16x4, float32 operands and sums), wave w < 2 BV/16 owning one
+        // 16 x 16 tile of one of the two products; longer chunks: 4 columns
+        // per thread on the vector ALUs, one pass over S.
+        f32x4 macc = {0.f, 0.f, 0.f, 0.f};
+        constexpr int kRT = kMfma ? 1 : (C * (BV / 4) + NT - 1) / NT;
         f32x4 qs[kRT];
+        if constexpr (kMfma) {
+            if (wave < 2 * NTL) {
+                const float(*A)[DKP] = mp ? sQ : sG;
+#pragma unroll 8
+                for (int s4 = 0; s4 < DK; s4 += 4)
+                    macc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[l16][s4 + lg], sS[s4 + lg][16 * mt + l16], macc, 0,
+                                                                0, 0);
+                if (mp == 0) {
 #pragma unroll
-        for (int e = 0; e < kRT; ++e) {
-            const int idx = tid + NT * e;
-            if (idx < C * (BV / 4)) {
-                const int r = idx / (BV / 4), j = 4 * (idx % (BV / 4));
-                f32x4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-                for (int c = 0; c < DK; c += 4) {
-                    const f32x4 gr = ld4(&sG[r][c]), qr = ld4(&sQ[r][c]);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const f32x4 sv = ld4(&sS[c + u][j]);
-                        y += gr[u] * sv;
-                        z += qr[u] * sv;
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = 4 * lg + i, n = 16 * mt + l16;
+                        sU[m][n] = sBeta[m] * (sV[m][n] - macc[i]);
                     }
                 }
-                qs[e] = z;
-                const f32x4 vv = *reinterpret_cast<const f32x4*>(&sV[r][j]);
-                *reinterpret_cast<f32x4*>(&sU[r][j]) = sBeta[r] * (vv - y);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < kRT; ++e) {
+                const int idx = tid + NT * e;
+                if (idx < C * (BV / 4)) {
+                    const int r = idx / (BV / 4), j = 4 * (idx % (BV / 4));
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+                    for (int c = 0; c < DK; c += 4) {
+                        const f32x4 gr = ld4(&sG[r][c]), qr = ld4(&sQ[r][c]);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const f32x4 sv = ld4(&sS[c + u][j]);
+                            y += gr[u] * sv;
+                            z += qr[u] * sv;
+                        }
+                    }
+                    qs[e] = z;
+                    const f32x4 vv = *reinterpret_cast<const f32x4*>(&sV[r][j]);
+                    *reinterpret_cast<f32x4*>(&sU[r][j]) = sBeta[r] * (vv - y);
+                }
             }
         }
         __syncthreads();
@@ -330,46 +382,80 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
             }
         }
 
-        // O = scale ((gamma*Q) S + P U): 4 columns per thread
+        // O = scale ((gamma*Q) S + P U): P U added on the matrix cores by the
+        // waves that hold (gamma*Q) S (16-row chunks), else 4 columns per thread
+        if constexpr (kMfma) {
+            if (wave >= NTL && wave < 2 * NTL) {
 #pragma unroll
-        for (int e = 0; e < kRT; ++e) {
-            const int idx = tid + NT * e;
-            const int r = idx / (BV / 4), j = 4 * (idx % (BV / 4));
-            if (idx < C * (BV / 4) && r < rows && o) {
-                f32x4 acc = qs[e];
-                for (int i = 0; i <= r; ++i) acc += sP[r][i] * *reinterpret_cast<const f32x4*>(&sU[i][j]);
-                const int64_t ob = ((tok0 + r) * H + h) * Dv + c0 + j;
+                for (int s4 = 0; s4 < C; s4 += 4)
+                    macc = __builtin_amdgcn_mfma_f32_16x16x4f32(sP[l16][s4 + lg], sU[s4 + lg][16 * mt + l16], macc, 0,
+                                                                0, 0);
+                if (o) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) store_elem(o, ob + u, a.scale * acc[u]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = 4 * lg + i;
+                        if (m < rows) store_elem(o, ((tok0 + m) * H + h) * Dv + c0 + 16 * mt + l16, a.scale * macc[i]);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < kRT; ++e) {
+                const int idx = tid + NT * e;
+                const int r = idx / (BV / 4), j = 4 * (idx % (BV / 4));
+                if (idx < C * (BV / 4) && r < rows && o) {
+                    f32x4 acc = qs[e];
+                    for (int i = 0; i <= r; ++i) acc += sP[r][i] * *reinterpret_cast<const f32x4*>(&sU[i][j]);
+                    const int64_t ob = ((tok0 + r) * H + h) * Dv + c0 + j;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) store_elem(o, ob + u, a.scale * acc[u]);
+                }
             }
         }
         __syncthreads();
 
-        // S <- Diag(gamma_C) S + (exp(Gamma_C - Gamma) K)^T U: 4 x 4 tiles
-        constexpr int TJ = 4;
-        for (int idx = tid; idx < (DK / 4) * (BV / TJ); idx += NT) {
-            const int c = 4 * (idx / (BV / TJ)), j = TJ * (idx % (BV / TJ));
-            f32x4 acc[4][TJ / 4];
+        // S <- Diag(gamma_C) S + (exp(Gamma_C - Gamma) K)^T U: 16 x 16 tiles on
+        // the matrix cores for 16-row chunks (K^T as the A operand), else 4 x 4
+        // tiles per thread
+        if constexpr (kMfma) {
+            for (int tile = wave; tile < (DK / 16) * NTL; tile += NT / 64) {
+                const int tm = 16 * (tile / NTL), tn = 16 * (tile % NTL);
+                f32x4 acc;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float d = expf(sGn[c + u]);
+                for (int i = 0; i < 4; ++i) acc[i] = sEd[tm + 4 * lg + i] * sS[tm + 4 * lg + i][tn + l16];
 #pragma unroll
-                for (int w = 0; w < TJ / 4; ++w) acc[u][w] = d * *reinterpret_cast<const f32x4*>(&sS[c + u][j + 4 * w]);
+                for (int s4 = 0; s4 < C; s4 += 4)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sK[s4 + lg][tm + l16], sU[s4 + lg][tn + l16], acc, 0, 0,
+                                                               0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sS[tm + 4 * lg + i][tn + l16] = acc[i];
             }
-            for (int r = 0; r < rows; ++r) {
-                f32x4 ur[TJ / 4];
+        } else {
+            constexpr int TJ = 4;
+            for (int idx = tid; idx < (DK / 4) * (BV / TJ); idx += NT) {
+                const int c = 4 * (idx / (BV / TJ)), j = TJ * (idx % (BV / TJ));
+                f32x4 acc[4][TJ / 4];
 #pragma unroll
-                for (int w = 0; w < TJ / 4; ++w) ur[w] = *reinterpret_cast<const f32x4*>(&sU[r][j + 4 * w]);
-                const f32x4 kr = ld4(&sK[r][c]);
+                for (int u = 0; u < 4; ++u) {
+                    const float d = sEd[c + u];
+#pragma unroll
+                    for (int w = 0; w < TJ / 4; ++w) acc[u][w] = d * *reinterpret_cast<const f32x4*>(&sS[c + u][j + 4 * w]);
+                }
+                for (int r = 0; r < rows; ++r) {
+                    f32x4 ur[TJ / 4];
+#pragma unroll
+                    for (int w = 0; w < TJ / 4; ++w) ur[w] = *reinterpret_cast<const f32x4*>(&sU[r][j + 4 * w]);
+                    const f32x4 kr = ld4(&sK[r][c]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+#pragma unroll
+                        for (int w = 0; w < TJ / 4; ++w) acc[u][w] += kr[u] * ur[w];
+                }
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
 #pragma unroll
-                    for (int w = 0; w < TJ / 4; ++w) acc[u][w] += kr[u] * ur[w];
+                    for (int w = 0; w < TJ / 4; ++w) *reinterpret_cast<f32x4*>(&sS[c + u][j + 4 * w]) = acc[u][w];
             }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int w = 0; w < TJ / 4; ++w) *reinterpret_cast<f32x4*>(&sS[c + u][j + 4 * w]) = acc[u][w];
         }
         __syncthreads();
     }

@@ -79,7 +79,7 @@ typedef enum {
  *                  length. It changes only rounding. The bf16 matrix-core
  *                  kernel (Dk = Dv = 128) works in 16-row chunks only: there
  *                  chunk_size must be 0 or 16, and any other value is
- *                  KDA_ERR_UNSUPPORTED. The float32 vector-ALU kernel takes
+ *                  KDA_ERR_UNSUPPORTED. The float32 kernel takes
  *                  16, 32 or 64 (0 = 16, its fastest).
  *   scale          multiplies the output (1.0 reproduces the rule above)
  *   o              [B,T,H,Dv]  dtype, written for every row of every sequence;
@@ -89,7 +89,7 @@ typedef enum {
  *                  initial_state (each state tile is read before it is written)
  *
  * Supported: Dk, Dv in {16, 32, 64, 128}. bf16 with Dk = Dv = 128 runs the
- * matrix-core kernel; everything else runs the float32 vector-ALU chunk
+ * matrix-core kernel; everything else runs the float32 chunk
  * kernel. Chunks start at each sequence's first token; rows
  * past a sequence's end inside its last chunk are treated as zero tokens,
  * which leave the state unchanged.
