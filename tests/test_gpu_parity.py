@@ -39,6 +39,17 @@ def test_f32_general_dims(Dk, Dv, chunk):
     _check(inp, TOL_F32, chunk=chunk, label=f"f32 Dk={Dk} Dv={Dv}")
 
 
+@pytest.mark.parametrize("Dk,Dv", [(16, 16), (128, 16), (16, 128), (64, 32), (128, 64), (32, 128)])
+def test_f32_matrix_core_tiles_packed(Dk, Dv):
+    """16-row chunks run the float32 products as 16x16 matrix-core tiles: one
+    to four column tiles per slice (d_v 16 to 128) and one to eight row tiles
+    of the state (d_k 16 to 128), over packed sequences with empty, one-token
+    and ragged members and a nonzero initial state."""
+    inp = synth.make_chunk_inputs(1, 0, 3, Dk, Dv, seed=520 + Dk + Dv, dtype="f32", init_state=True, s0_std=0.5,
+                                  lengths=[1, 0, 47, 16, 33, 80])
+    _check(inp, TOL_F32, chunk=16, label=f"f32 tiles Dk={Dk} Dv={Dv}")
+
+
 @pytest.mark.parametrize("chunk", [16, 32, 64])
 def test_f32_factored_and_pairwise_grams_mixed(chunk):
     """The float32 kernel forms a chunk's grams from gamma*K and K/gamma while
