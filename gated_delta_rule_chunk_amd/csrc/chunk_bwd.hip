@@ -486,12 +486,19 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Value columns per workgroup: d_v = 64 in two 32-column slices (twice the
+// workgroups of one 64-column slice; with two slices each atomically summed
+// gradient gets exactly two addends, so the sums do not depend on their
+// order), 64-column slices for d_v = 128, all of d_v below 64.
+constexpr int vbwd_bv(int Dv) { return Dv == 64 ? 32 : (Dv > 64 ? 64 : Dv); }
+
 template <int DK, typename Tin>
 hipError_t launch_dk(const BwdArgs& a, hipStream_t s) {
     switch (a.Dv) {
         case 16: return launch_typed<DK, 16, Tin>(a, s);
-        case 32: return launch_typed<DK, 32, Tin>(a, s);
-        default: return launch_typed<DK, 64, Tin>(a, s);  // 64 and 128
+        case 32:
+        case 64: return launch_typed<DK, 32, Tin>(a, s);
+        default: return launch_typed<DK, 64, Tin>(a, s);  // 128
     }
 }
 
@@ -1377,7 +1384,7 @@ __global__ __launch_bounds__(NT) void chunk_bwd_mfma_kernel(BwdArgs a) {
 bool chunk_bwd_mfma_supported(const BwdArgs& a);
 
 hipError_t launch_chunk_bwd(const BwdArgs& args, hipStream_t s) {
-    const int nvt = args.Dv / (args.Dv >= 64 ? 64 : args.Dv);
+    const int nvt = args.Dv / (chunk_bwd_mfma_supported(args) ? mf::BV : vbwd_bv(args.Dv));
     BwdArgs a = args;
     // the matrix-core path zeroes the atomically summed gradients in its T/P/KK kernel
     a.zero_grads = nvt > 1 && chunk_bwd_mfma_supported(a);
