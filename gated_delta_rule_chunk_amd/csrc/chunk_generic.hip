@@ -467,9 +467,8 @@ __global__ __launch_bounds__(kGenThreads) void chunk_generic_kernel(ChunkArgs a)
     }
 }
 
-template <int DK, int C, int DV>
-hipError_t launch_dk_c_dv(const ChunkArgs& a, hipStream_t s) {
-    constexpr int BV = gen_bv(C, DV);
+template <int DK, int C, int BV>
+hipError_t launch_bv(const ChunkArgs& a, hipStream_t s) {
     const int units = a.N * a.H;
     const dim3 grid((unsigned)(units * (a.Dv / BV)));
     if (a.bf16)
@@ -477,6 +476,31 @@ hipError_t launch_dk_c_dv(const ChunkArgs& a, hipStream_t s) {
     else
         hipLaunchKernelGGL((chunk_generic_kernel<DK, C, BV, float>), grid, dim3(kGenThreads), 0, s, a);
     return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <int DK, int C, int DV>
+hipError_t launch_dk_c_dv(const ChunkArgs& a, hipStream_t s) {
+    constexpr int BV = gen_bv(C, DV);
+    if constexpr (C == 16 && BV == 64) {
+        // 32-column slices when even they leave no more workgroups than compute
+        // units: twice the workgroups, each on a compute unit of its own (the
+        // per-element sums are the same, so is the result)
+        if ((int64_t)a.N * a.H * (a.Dv / 32) <= cu_count()) return launch_bv<DK, C, 32>(a, s);
+    }
+    return launch_bv<DK, C, BV>(a, s);
 }
 
 template <int DK, int C>
